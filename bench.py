@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Throughput of the decoder's forward pass on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic request: reset the session,
+prefill the 2,048-token prompt of the Qwen3-4B-shape BF16 decoder (MFMA GEMM path, paged KV
+with a shuffled 32-position block table), then 64 greedy decode steps whose token ids come
+from the previous step's device-resident argmax. Inputs (weights, ids, block table) are
+resident in HBM before timing starts. Prints one JSON line.
+
+value = (prompt + decode tokens) per step / wall time per step. Prefill tok/s, decode tok/s,
+their fractions of the MFMA / HBM peaks, the dominant kernel's roofline (HIP events around its
+launches) and the CPU oracle on a bounded sample are reported beside it.
+"""
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15    # dense FP16/BF16 MFMA, MI355X
+PEAK_HBM = 8.0e12           # bytes/s, MI355X HBM3E
+
+METRIC = "prefill tok/s @2048 + decode tok/s, Qwen3-4B-shape BF16, 1 MI355X (% roofline)"
+
+
+def algorithmic(shape, prompt, decode):
+    """Algorithmic FLOP of the prefill and bytes per decode token (weights + KV, no scratch)."""
+    H, F, V, L, QD = shape.hidden, shape.ffn, shape.vocab, shape.n_layers, shape.q_dim
+    KVD = shape.kv_dim
+    P = H * QD + 2 * H * KVD + QD * H + 3 * H * F                     # projection weights per layer
+    flops = 2 * L * P * prompt + L * shape.n_q_heads * 4 * 128 * prompt * (prompt + 1) // 2 + 2 * V * H
+    w_bytes = 2 * (L * P + V * H + (2 * L + 1) * H + 2 * L * 128) + 2 * H
+    kv_pos = 2 * L * KVD * 2                                            # K and V bytes per cached position
+    ctx_mean = prompt + (decode + 1) / 2.0
+    dec_bytes = w_bytes + kv_pos * ctx_mean + kv_pos
+    return flops, dec_bytes, w_bytes
+
+
+def cpu_baseline(wl, n_prompt=256, n_decode=8):
+    """The oracle on a bounded sample of the same workload: n_prompt prompt tokens then n_decode
+    greedy steps of the same model, timed after weight generation."""
+    import numpy as np
+    import oracle
+    import synth
+    from oracle import model as om
+    cores = len(os.sched_getaffinity(0))
+    m = oracle.OracleModel(wl.shape, wl.weight_seed)
+    for l in range(wl.shape.n_layers):
+        m.layer(l)
+    ids = synth.token_ids(wl.ids_seed, n_prompt)
+    s = oracle.OracleSession(m, oracle.ContiguousKV.for_shape(wl.shape, n_prompt + n_decode + 1))
+    t0 = time.perf_counter()
+    lg = s.prefill(ids)
+    t1 = time.perf_counter()
+    for _ in range(n_decode):
+        lg = s.decode(om.argmax(lg))
+    t2 = time.perf_counter()
+    return {"value": round((n_prompt + n_decode) / (t2 - t0), 3), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "prefill_tok_s": round(n_prompt / (t1 - t0), 3), "decode_tok_s": round(n_decode / (t2 - t1), 3),
+            "sample": f"{wl.shape.name} BF16 oracle (NumPy FP32, OpenBLAS on {cores} cores): {n_prompt}-token prompt "
+                      f"+ {n_decode} greedy decode steps, weight generation untimed"}
+
+
+def git_rev():
+    try:
+        r = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True, text=True)
+        d = subprocess.run(["git", "status", "--porcelain"], cwd=ROOT, capture_output=True, text=True)
+        return r.stdout.strip() or None, bool(d.stdout.strip())
+    except Exception:
+        return None, None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="4b", choices=["4b", "0.6b", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-prompt", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: the decoder is evaluated unsharded on one MI355X "
+              f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dense_gqa_decoder_amd as g
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    g.load()
+    wl = synth.WORKLOADS[args.workload]
+    shape = wl.shape
+    nb = synth.blocks_for(wl.prompt + wl.decode)
+    pool = 4 * nb
+    table = synth.shuffled_blocks(wl.shuffle_seed, pool)[:nb]
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, scheme=wl.scheme, kv_pool_blocks=pool, max_positions=nb * 32)
+    s = g.Session(m, nb * 32, block_ids=table)
+    ids = synth.token_ids(wl.ids_seed, wl.prompt)
+    lg = torch.empty(shape.vocab, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        s.reset()
+        if evs:
+            evs[0].record(stream)
+        s.prefill(ids, lg, am, stream)
+        if evs:
+            evs[1].record(stream)
+        for _ in range(wl.decode):
+            s.decode(am, lg, am, stream)
+        if evs:
+            evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    m.check_device_error(stream)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    pre_ms = sorted(e[0].elapsed_time(e[1]) for e in events)[args.steps // 2]
+    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in events)[args.steps // 2]
+    tokens = wl.prompt + wl.decode
+    flops, dec_bytes, w_bytes = algorithmic(shape, wl.prompt, wl.decode)
+
+    # dominant kernel (decode gate/up matvec): HIP events around each of its launches in one
+    # more step identical to the timed ones
+    kernels = {}
+    for cls in ("decode_gateup", "prefill_gateup", "prefill_attn"):
+        m.profile(cls)
+        step()
+        n, tot_ms, dropped = m.profile_read()
+        m.profile("none")
+        kernels[cls] = (n, tot_ms / max(n, 1))
+    H, F = shape.hidden, shape.ffn
+    gu_bytes = 2 * F * H * 2 + H * 4 + F * 4                     # weights + x hi/lo + m hi/lo, one row
+    gu_ms = kernels["decode_gateup"][1]
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    pgu_flop = 2.0 * wl.prompt * 2 * F * H
+    pgu_ms = kernels["prefill_gateup"][1]
+
+    rev, dirty = git_rev()
+    out = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_step * 1e-3), 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights ~N(0,0.02), uniform random token ids)",
+        "config": {"workload": f"{shape.name} {wl.scheme}: {wl.prompt}-token prefill + {wl.decode} greedy decode "
+                               f"steps, paged KV (shuffled 32-position blocks)",
+                   "layers": shape.n_layers, "hidden": shape.hidden, "q_heads": shape.n_q_heads, "kv_heads": 8,
+                   "ffn": shape.ffn, "vocab": shape.vocab, "prompt": wl.prompt, "decode_steps": wl.decode,
+                   "round_tokens": m.info().round_tokens},
+        "prefill_tok_s": round(wl.prompt / (pre_ms * 1e-3), 1),
+        "decode_tok_s": round(wl.decode / (dec_ms * 1e-3), 2),
+        "prefill_ms": round(pre_ms, 3),
+        "decode_ms_per_token": round(dec_ms / wl.decode, 4),
+        "prefill_frac_mfma_peak": round(flops / (pre_ms * 1e-3) / PEAK_BF16_FLOPS, 4),
+        "decode_frac_hbm_peak": round(dec_bytes / (dec_ms / wl.decode * 1e-3) / PEAK_HBM, 4),
+        "algorithmic": {"prefill_flop": flops, "decode_bytes_per_token": int(dec_bytes), "weight_bytes": w_bytes},
+        "roofline": {"kernel": "gemv_kernel<EPI_SWIGLU> decode gate/up matvec with SwiGLU",
+                     "bound": "hbm", "achieved": round(gu_gbs, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": round(gu_gbs * 1e9 / PEAK_HBM, 4), "traffic": None,
+                     "launch_us": round(gu_ms * 1e3, 2), "bytes_per_launch": gu_bytes,
+                     "launches": kernels["decode_gateup"][0]},
+        "prefill_roofline": {"kernel": "gemm_kernel<EPI_SWIGLU> prefill gate/up GEMM with SwiGLU",
+                             "bound": "mfma", "achieved": round(pgu_flop / (pgu_ms * 1e-3) / 1e12, 1),
+                             "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                             "frac": round(pgu_flop / (pgu_ms * 1e-3) / PEAK_BF16_FLOPS, 4),
+                             "launch_us": round(pgu_ms * 1e3, 1),
+                             "attn_launch_us": round(kernels["prefill_attn"][1] * 1e3, 1)},
+        "commit": rev, "dirty": dirty, "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, n_prompt=args.cpu_prompt)
+    s.close()
+    m.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+"""Thin object wrappers over the C ABI for torch callers (device buffers are torch tensors)."""
+from __future__ import annotations
+
+import atexit
+import ctypes
+import sys
+import weakref
+
+import numpy as np
+
+from . import _lib as L
+
+# Objects still alive at interpreter exit are released before the HIP runtime shuts down
+# (sessions before their models); __del__ does nothing once the interpreter is finalising.
+_live_sessions = weakref.WeakSet()
+_live_models = weakref.WeakSet()
+
+
+@atexit.register
+def _release_all():
+    for s in list(_live_sessions):
+        s.close()
+    for m in list(_live_models):
+        m.close()
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+class Model:
+    """A model on the current HIP device with seeded synthetic weights."""
+
+    def __init__(self, *, n_layers, hidden, n_q_heads, ffn, vocab=151936, tied=True, rope_theta=1e6, rms_eps=1e-6,
+                 scheme="bf16", kv_pool_blocks, max_positions, max_round_tokens=0, seed=0):
+        self.desc = L.ModelDesc(n_layers, hidden, n_q_heads, 8, 128, ffn, vocab, 1 if tied else 0, rope_theta,
+                                rms_eps, L.GQA_SCHEME_Q8_0 if scheme == "q8_0" else L.GQA_SCHEME_BF16,
+                                kv_pool_blocks, max_positions, max_round_tokens)
+        self.vocab, self.hidden, self.n_layers = vocab, hidden, n_layers
+        self.handle = None
+        self.handle = L.gqa_model_create(self.desc, seed)
+        _live_models.add(self)
+
+    @classmethod
+    def from_shape(cls, shape, *, seed, scheme="bf16", kv_pool_blocks, max_positions, max_round_tokens=0):
+        return cls(n_layers=shape.n_layers, hidden=shape.hidden, n_q_heads=shape.n_q_heads, ffn=shape.ffn,
+                   vocab=shape.vocab, tied=shape.tied, rope_theta=shape.rope_theta, rms_eps=shape.rms_eps,
+                   scheme=scheme, kv_pool_blocks=kv_pool_blocks, max_positions=max_positions,
+                   max_round_tokens=max_round_tokens, seed=seed)
+
+    def info(self):
+        return L.gqa_model_get_info(self.handle)
+
+    def close(self):
+        if self.handle:
+            for s in list(_live_sessions):
+                if s.model is self:
+                    s.close()
+            L.gqa_model_destroy(self.handle)
+            self.handle = None
+
+    def read_weight(self, kind, layer, row0, rows, cols):
+        out = np.empty((rows, cols), dtype=np.uint16)
+        L.gqa_debug_read_weight(self.handle, L.GQA_T[kind], layer, row0, rows, out.ctypes.data)
+        return out
+
+    def read_q8(self, kind, layer, row0, rows, cols):
+        q = np.empty((rows, cols), dtype=np.int8)
+        s = np.empty((rows, cols // 32), dtype=np.uint16)
+        L.gqa_debug_read_q8(self.handle, L.GQA_T[kind], layer, row0, rows, q.ctypes.data, s.ctypes.data)
+        return q, s
+
+    def read_rope(self, n):
+        c = np.empty((n, 64), dtype=np.float32)
+        s = np.empty((n, 64), dtype=np.float32)
+        L.gqa_debug_read_rope(self.handle, n, c.ctypes.data, s.ctypes.data)
+        return c, s
+
+    def profile(self, kernel_class: str):
+        L.gqa_model_profile(self.handle, L.GQA_PROF[kernel_class])
+
+    def profile_read(self):
+        return L.gqa_model_profile_read(self.handle)
+
+    def check_device_error(self, stream=None):
+        L.gqa_model_check_device_error(self.handle, _stream(stream))
+
+    def eval_batch(self, sessions, ids, logits, argmax=None, stream=None):
+        """ids: host sequence of ints, or an int32 device tensor (ids_on_device)."""
+        B = len(sessions)
+        arr = (ctypes.c_void_p * B)(*[s.handle for s in sessions])
+        if hasattr(ids, "data_ptr"):
+            L.gqa_session_eval_batch(ctypes.addressof(arr), B, ids.data_ptr(), 1, _ptr(logits), _ptr(argmax),
+                                     _stream(stream))
+        else:
+            h = np.ascontiguousarray(ids, dtype=np.int32)
+            L.gqa_session_eval_batch(ctypes.addressof(arr), B, h.ctypes.data, 0, _ptr(logits), _ptr(argmax),
+                                     _stream(stream))
+
+    def __del__(self):
+        if sys.is_finalizing():
+            return
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Session:
+    def __init__(self, model: Model, max_positions: int, block_ids=None):
+        self.model = model
+        self._ids = None
+        ptr = None
+        if block_ids is not None:
+            self._ids = np.ascontiguousarray(block_ids, dtype=np.int32)
+            ptr = self._ids.ctypes.data
+        self.handle = None
+        self.handle = L.gqa_session_create(model.handle, max_positions, ptr)
+        _live_sessions.add(self)
+
+    @property
+    def position(self):
+        return L.gqa_session_position(self.handle)
+
+    def reset(self):
+        L.gqa_session_reset(self.handle)
+
+    def prefill(self, ids, logits, argmax=None, stream=None):
+        h = np.ascontiguousarray(ids, dtype=np.int32)
+        L.gqa_session_eval_prefill(self.handle, h.ctypes.data, len(h), _ptr(logits), _ptr(argmax), _stream(stream))
+
+    def decode(self, token, logits, argmax=None, stream=None):
+        """token: a host int, or an int32 device tensor holding the id."""
+        if hasattr(token, "data_ptr"):
+            L.gqa_session_eval_decode(self.handle, token.data_ptr(), 1, _ptr(logits), _ptr(argmax), _stream(stream))
+        else:
+            h = np.asarray([token], dtype=np.int32)
+            L.gqa_session_eval_decode(self.handle, h.ctypes.data, 0, _ptr(logits), _ptr(argmax), _stream(stream))
+
+    def read_kv(self, layer, pos0, n):
+        k = np.empty((n, 8, 128), dtype=np.uint16)
+        v = np.empty((n, 8, 128), dtype=np.uint16)
+        L.gqa_debug_read_kv(self.handle, layer, pos0, n, k.ctypes.data, v.ctypes.data)
+        return k, v
+
+    def close(self):
+        if self.handle:
+            L.gqa_session_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        if sys.is_finalizing():
+            return
+        try:
+            self.close()
+        except Exception:
+            pass

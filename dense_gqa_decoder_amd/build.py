@@ -1,0 +1,51 @@
+"""Build libgqa355.so (all HIP kernels + the host runtime) for gfx950 with hipcc, in-tree."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libgqa355.so")
+SOURCES = ["k_weights.hip", "k_elementwise.hip", "k_gemm.hip", "k_gemv.hip", "k_attn.hip", "runtime.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # no packed FP32 instructions (v_pk_*_f32) anywhere in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def _obj(src: str) -> str:
+    return os.path.join(CSRC, "_build", os.path.splitext(src)[0] + ".o")
+
+
+def build(verbose: bool = False, jobs: int = 6) -> str:
+    os.makedirs(os.path.join(CSRC, "_build"), exist_ok=True)
+    procs = []
+    for src in SOURCES:
+        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", _obj(src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        if len([p for _, p in procs if p.poll() is None]) >= jobs:
+            procs[-jobs][1].wait()
+    for src, p in procs:
+        out, _ = p.communicate()
+        text = "\n".join(l for l in out.decode().splitlines() if "packed-fp32-ops' is not a recognized" not in l)
+        if p.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{text}")
+        if verbose and text.strip():
+            print(text)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[_obj(s) for s in SOURCES]]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

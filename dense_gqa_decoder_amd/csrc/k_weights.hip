@@ -1,0 +1,91 @@
+// Seeded synthetic weights generated on the device, and the Q8_0 quantiser.
+//
+// Generator: element i of the logical row-major [rows][cols] tensor with key `key` takes
+// u = SplitMix64 finaliser of (key + (i+1) * 0x9E3779B97F4A7C15) (Steele, Lea and Flood,
+// OOPSLA 2014), S = sum of the four 16-bit fields of u, z = S - 131070, and
+// w = bf16_rne(fp32(z) * scale) with one FP32 multiply. The value lands at the physical row
+// given by the layout mode (plain with a row offset, or the 16-row gate/up interleave).
+//
+// Q8_0 (Kipp Model Support, "Quantization (Q8_0)"): 32-weight blocks along a row, an fp16
+// scale and 32 int8 quants. d = amax / 127 (FP32 division), scale = fp16_rne(d),
+// q = clamp(round_half_away(w / d), -127, 127), and q = 0 when d = 0.
+#include "gqa_common.h"
+
+namespace gqa {
+
+__device__ __forceinline__ uint64_t splitmix_at(uint64_t key, uint64_t i) {
+  uint64_t z = key + (i + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// mode 0: physical row = row_off + r. mode 1: gate rows of the interleave (32*(r/16) + r%16);
+// mode 2: up rows (32*(r/16) + 16 + r%16).
+__global__ void gen_weights_kernel(uint16_t* __restrict__ dst, uint64_t key, int64_t rows, int64_t cols,
+                                   int mode, int64_t row_off, float scale) {
+  int64_t n = rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    uint64_t u = splitmix_at(key, (uint64_t)i);
+    int64_t s = (int64_t)(u & 0xFFFF) + (int64_t)((u >> 16) & 0xFFFF) + (int64_t)((u >> 32) & 0xFFFF) +
+                (int64_t)(u >> 48);
+    float z = (float)(int32_t)(s - 131070);
+    float w = __fmul_rn(z, scale);
+    int64_t r = i / cols, c = i - r * cols;
+    int64_t pr = mode == 0 ? row_off + r : (mode == 1 ? 32 * (r / 16) + (r % 16) : 32 * (r / 16) + 16 + (r % 16));
+    dst[pr * cols + c] = f32_to_bf16_rne(w);
+  }
+}
+
+__global__ void fill_u16_kernel(uint16_t* __restrict__ dst, int64_t n, uint16_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = v;
+}
+
+// One thread per 32-weight block of a BF16 matrix [rows][cols] -> q int8 [rows][cols], d fp16 [rows][cols/32].
+__global__ void quantize_q8_0_kernel(const uint16_t* __restrict__ w, int8_t* __restrict__ q, f16* __restrict__ d,
+                                     int64_t rows, int64_t cols) {
+  int64_t nb = rows * (cols / 32);
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += (int64_t)gridDim.x * blockDim.x) {
+    const uint16_t* src = w + b * 32;
+    float v[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      v[i] = bf16_bits_to_f32(src[i]);
+      amax = fmaxf(amax, fabsf(v[i]));
+    }
+    float dd = __fdiv_rn(amax, 127.0f);
+    d[b] = (f16)dd;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float r = dd == 0.f ? 0.f : __fdiv_rn(v[i], dd);
+      float qi = roundf(r);                      // half away from zero
+      qi = fminf(fmaxf(qi, -127.f), 127.f);
+      q[b * 32 + i] = (int8_t)(int)qi;
+    }
+  }
+}
+
+hipError_t launch_gen_weights(uint16_t* dst, uint64_t key, int64_t rows, int64_t cols, int mode, int64_t row_off,
+                              float scale, hipStream_t st) {
+  int64_t n = rows * cols;
+  int grid = (int)std::min<int64_t>((n + 255) / 256, 65536);
+  hipLaunchKernelGGL(gen_weights_kernel, dim3(grid), dim3(256), 0, st, dst, key, rows, cols, mode, row_off, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t st) {
+  int grid = (int)std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_u16_kernel, dim3(grid), dim3(256), 0, st, dst, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_q8_0(const uint16_t* w, int8_t* q, f16* d, int64_t rows, int64_t cols, hipStream_t st) {
+  int64_t nb = rows * (cols / 32);
+  int grid = (int)std::min<int64_t>((nb + 255) / 256, 65536);
+  hipLaunchKernelGGL(quantize_q8_0_kernel, dim3(grid), dim3(256), 0, st, w, q, d, rows, cols);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

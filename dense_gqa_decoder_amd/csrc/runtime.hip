@@ -1,0 +1,814 @@
+// Host runtime and C ABI of the decoder library: model (weights, KV block pool, per-model
+// scratch), sessions (block table, position), and the launch sequences of prefill rounds,
+// single-row decode and batched decode. Declared in include/gqa.h.
+//
+// Kipp Roadmap, status v0.0.4: prefill runs in device-derived rounds, activation scratch is
+// one per model and the split-K partial count is its own constant. Status v0.0.3: sessions
+// take their KV blocks from one model-owned pool. Kipp Reproducing, "Build": failures are
+// fatal errors, never a fallback.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/gqa.h"
+#include "gqa_common.h"
+
+namespace gqa {
+hipError_t launch_gen_weights(uint16_t* dst, uint64_t key, int64_t rows, int64_t cols, int mode, int64_t row_off,
+                              float scale, hipStream_t st);
+hipError_t launch_fill_u16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t st);
+hipError_t launch_quantize_q8_0(const uint16_t* w, int8_t* q, f16* d, int64_t rows, int64_t cols, hipStream_t st);
+hipError_t launch_embed(const uint16_t* E, const int32_t* ids, int T, int H, int vocab, float* x, int32_t* err,
+                        hipStream_t st);
+hipError_t launch_rmsnorm(float* x, int ldx, const float* part, int nsplit, int part_stride_split, int part_ld,
+                          float part_scale, const uint16_t* w, int H, float eps, float out_scale, f16* yhi, f16* ylo,
+                          int ldy, int rows, hipStream_t st);
+hipError_t launch_qk_rope_kv(bool decode, const float* qkv, int nsplit, int part_stride, int ldqkv, int nq,
+                             const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
+                             const float* rsin, int pos0, const int32_t* table0, const Rows& rows, uint16_t* kpool,
+                             uint16_t* vpool, float* qout, int nrows, hipStream_t st);
+hipError_t launch_argmax(const float* logits, int64_t ld, int V, int B, int32_t* out, hipStream_t st);
+hipError_t launch_gemm(int epi, const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
+                       const f16* Xlo, int ldx, int T, float* C, int ldc, float out_scale, f16* Mhi, f16* Mlo,
+                       int ldm, float m_scale, hipStream_t st);
+hipError_t launch_gemv(int epi, const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
+                       const f16* Xlo, int ldx, int B, int nsplit, float* P, int64_t part_stride, int ldp, f16* Mhi,
+                       f16* Mlo, int ldm, float m_scale, hipStream_t st);
+hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const int32_t* table, const uint16_t* kpool,
+                               const uint16_t* vpool, float out_scale, f16* ohi, f16* olo, int ldo, hipStream_t st);
+hipError_t launch_attn_decode(const float* q, int nq, const Rows& rows, int B, int max_ctx, const uint16_t* kpool,
+                              const uint16_t* vpool, float* part, int max_chunks, float out_scale, f16* ohi,
+                              f16* olo, int ldo, hipStream_t st);
+}  // namespace gqa
+
+using namespace gqa;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                         \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess) return fail(GQA_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+uint64_t splitmix(uint64_t key, uint64_t i) {
+  uint64_t z = key + (i + 1ull) * kGamma;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Scale of the generator: 0.02 / std of the sum of four uniform 16-bit integers.
+float weight_scale() { return (float)(0.02 / sqrt(4.0 * (65536.0 * 65536.0 - 1.0) / 12.0)); }
+
+// Attention output enters the o projection multiplied by this power of two (and the
+// projection result is divided by it), keeping the FP16 lo half of small outputs normal.
+constexpr float kAttnOutScale = 16.0f;
+
+struct LayerW {
+  uint16_t *attn_norm = nullptr, *ffn_norm = nullptr, *q_norm = nullptr, *k_norm = nullptr;
+  uint16_t *wqkv = nullptr, *wo = nullptr, *wgu = nullptr, *wd = nullptr;                  // BF16
+  int8_t *qqkv = nullptr, *qo = nullptr, *qgu = nullptr, *qd = nullptr;                    // Q8_0 quants
+  f16 *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sd = nullptr;                       // Q8_0 scales
+  uint16_t *kpool = nullptr, *vpool = nullptr;
+};
+
+}  // namespace
+
+struct gqa_model {
+  gqa_model_desc d{};
+  int dev = 0, cu = 0, R = 0;
+  int QKV = 0, QD = 0;          // fused q|k|v rows, attention width
+  int max_chunks = 0;
+  int s_qkv = 1, s_o = 1, s_d = 1;  // decode split-K counts
+  std::vector<LayerW> L;
+  uint16_t *embed = nullptr, *lm_head = nullptr, *final_norm = nullptr;
+  float *rcos = nullptr, *rsin = nullptr;
+  float *x = nullptr, *qkv = nullptr, *q = nullptr, *part = nullptr, *apart = nullptr;
+  f16 *xh = nullptr, *xl = nullptr, *oh = nullptr, *ol = nullptr, *mh = nullptr, *ml = nullptr;
+  int32_t *ids_dev = nullptr, *err = nullptr;
+  int32_t* ids_host = nullptr;  // pinned staging
+  hipEvent_t ids_evt = nullptr;
+  int64_t part_floats = 0;
+  std::vector<void*> allocs;
+  std::vector<char> block_used;
+  int free_blocks = 0, sessions = 0;
+  int64_t weight_bytes = 0, kv_bytes = 0, scratch_bytes = 0;
+  std::mutex mu;
+  // kernel timing (gqa_model_profile)
+  int prof_cls = GQA_PROF_NONE;
+  std::vector<hipEvent_t> prof_ev;
+  int64_t prof_used = 0, prof_dropped = 0;
+};
+
+struct gqa_session {
+  gqa_model* m = nullptr;
+  int max_pos = 0, pos = 0;
+  std::vector<int32_t> blocks;
+  int32_t* d_table = nullptr;
+};
+
+namespace {
+
+void free_model(gqa_model* m) {
+  if (!m) return;
+  for (hipEvent_t e : m->prof_ev) (void)hipEventDestroy(e);
+  for (void* p : m->allocs) (void)hipFree(p);
+  if (m->ids_host) (void)hipHostFree(m->ids_host);
+  if (m->ids_evt) (void)hipEventDestroy(m->ids_evt);
+  delete m;
+}
+
+template <class T>
+int dalloc(gqa_model* m, T** p, int64_t count, int64_t* counter) {
+  void* v = nullptr;
+  size_t bytes = (size_t)std::max<int64_t>(count, 1) * sizeof(T);
+  hipError_t e = hipMalloc(&v, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(GQA_E_OOM, "hipMalloc of %zu bytes failed: %s", bytes, hipGetErrorString(e));
+  }
+  m->allocs.push_back(v);
+  *p = (T*)v;
+  if (counter) *counter += (int64_t)bytes;
+  return GQA_OK;
+}
+
+int check_desc(const gqa_model_desc* d) {
+  if (!d) return fail(GQA_E_INVALID, "null descriptor");
+  if (d->n_kv_heads != kKvHeads || d->head_dim != kHeadDim)
+    return fail(GQA_E_INVALID, "n_kv_heads must be 8 and head_dim 128");
+  if (d->n_q_heads != 16 && d->n_q_heads != 32) return fail(GQA_E_INVALID, "n_q_heads must be 16 or 32");
+  if (d->n_layers < 1 || d->hidden < 256 || d->hidden > 4096 || d->hidden % 256 || d->ffn < 128 ||
+      (2 * d->ffn) % 256 || d->vocab < 16 || d->vocab % 16)
+    return fail(GQA_E_INVALID, "unsupported shape (hidden %% 256, hidden <= 4096, 2*ffn %% 256, vocab %% 16)");
+  if (d->scheme != GQA_SCHEME_BF16 && d->scheme != GQA_SCHEME_Q8_0) return fail(GQA_E_INVALID, "unknown scheme");
+  if (d->kv_pool_blocks < 1 || d->max_positions < 1 || d->max_round_tokens < 0)
+    return fail(GQA_E_INVALID, "kv_pool_blocks and max_positions must be positive");
+  if (!(d->rope_theta > 1.0f) || !(d->rms_eps > 0.0f)) return fail(GQA_E_INVALID, "bad rope_theta or rms_eps");
+  return GQA_OK;
+}
+
+// Largest split count <= want with K % (32 * s) == 0.
+int pick_split(int K, int want) {
+  for (int s = std::min(want, 8); s > 1; --s)
+    if (K % (32 * s) == 0) return s;
+  return 1;
+}
+
+// Generator tensor ids: embedding 0; layer l, kind j (attn_norm, q, k, v, q_norm, k_norm, o,
+// ffn_norm, gate, up, down) -> 1 + 11 l + j; final norm 1 + 11 L; lm_head 2 + 11 L.
+uint64_t tensor_key(uint64_t seed, int L, int kind, int layer) {
+  int tid;
+  if (kind == GQA_T_EMBED)
+    tid = 0;
+  else if (kind == GQA_T_FINAL_NORM)
+    tid = 1 + 11 * L;
+  else if (kind == GQA_T_LM_HEAD)
+    tid = 2 + 11 * L;
+  else
+    tid = 1 + 11 * layer + (kind - GQA_T_ATTN_NORM);
+  return splitmix(seed, (uint64_t)tid);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_last_error(void) { return g_err.c_str(); }
+
+int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out) {
+  g_err.clear();
+  if (!out) return fail(GQA_E_INVALID, "null out pointer");
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, dev));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(GQA_E_DEVICE, "device %d is %s, this library is built for gfx950 only", dev, prop.gcnArchName);
+
+  gqa_model* m = new gqa_model();
+  m->d = *desc;
+  m->dev = dev;
+  m->cu = prop.multiProcessorCount;
+  const gqa_model_desc& d = m->d;
+  const int H = d.hidden, F = d.ffn, V = d.vocab, NQ = d.n_q_heads;
+  m->QD = NQ * kHeadDim;
+  m->QKV = m->QD + 2 * kKvHeads * kHeadDim;
+  m->R = d.max_round_tokens > 0 ? d.max_round_tokens : std::max(64, m->cu * 8);
+  m->max_chunks = (d.max_positions + 63) / 64;
+  m->s_qkv = pick_split(H, std::max(1, 2048 / (m->QKV / 16)));
+  m->s_o = pick_split(m->QD, std::max(1, 2048 / (H / 16)));
+  m->s_d = pick_split(F, std::max(1, 2048 / (H / 16)));
+  const bool q8 = d.scheme == GQA_SCHEME_Q8_0;
+  int64_t* wb = &m->weight_bytes;
+
+#define ALLOC(p, n, ctr)                      \
+  do {                                        \
+    int r_ = dalloc(m, &(p), (int64_t)(n), ctr); \
+    if (r_) {                                 \
+      free_model(m);                          \
+      return r_;                              \
+    }                                         \
+  } while (0)
+
+  ALLOC(m->embed, (int64_t)V * H, wb);
+  ALLOC(m->final_norm, H, wb);
+  if (!d.tied)
+    ALLOC(m->lm_head, (int64_t)V * H, wb);
+  else
+    m->lm_head = m->embed;
+  m->L.resize(d.n_layers);
+  const int64_t pool_elems = (int64_t)d.kv_pool_blocks * kKvHeads * kBlock * kHeadDim;
+  for (int l = 0; l < d.n_layers; ++l) {
+    LayerW& w = m->L[l];
+    ALLOC(w.attn_norm, H, wb);
+    ALLOC(w.ffn_norm, H, wb);
+    ALLOC(w.q_norm, kHeadDim, wb);
+    ALLOC(w.k_norm, kHeadDim, wb);
+    if (q8) {
+      ALLOC(w.qqkv, (int64_t)m->QKV * H, wb);
+      ALLOC(w.sqkv, (int64_t)m->QKV * H / 32, wb);
+      ALLOC(w.qo, (int64_t)H * m->QD, wb);
+      ALLOC(w.so, (int64_t)H * m->QD / 32, wb);
+      ALLOC(w.qgu, (int64_t)2 * F * H, wb);
+      ALLOC(w.sgu, (int64_t)2 * F * H / 32, wb);
+      ALLOC(w.qd, (int64_t)H * F, wb);
+      ALLOC(w.sd, (int64_t)H * F / 32, wb);
+    } else {
+      ALLOC(w.wqkv, (int64_t)m->QKV * H, wb);
+      ALLOC(w.wo, (int64_t)H * m->QD, wb);
+      ALLOC(w.wgu, (int64_t)2 * F * H, wb);
+      ALLOC(w.wd, (int64_t)H * F, wb);
+    }
+    ALLOC(w.kpool, pool_elems, &m->kv_bytes);
+    ALLOC(w.vpool, pool_elems, &m->kv_bytes);
+  }
+  const int rows = std::max(m->R, kMaxBatch);
+  int64_t* sb = &m->scratch_bytes;
+  ALLOC(m->x, (int64_t)rows * H, sb);
+  ALLOC(m->xh, (int64_t)rows * H, sb);
+  ALLOC(m->xl, (int64_t)rows * H, sb);
+  ALLOC(m->qkv, (int64_t)m->R * m->QKV, sb);
+  ALLOC(m->q, (int64_t)rows * m->QD, sb);
+  ALLOC(m->oh, (int64_t)rows * m->QD, sb);
+  ALLOC(m->ol, (int64_t)rows * m->QD, sb);
+  ALLOC(m->mh, (int64_t)rows * F, sb);
+  ALLOC(m->ml, (int64_t)rows * F, sb);
+  m->part_floats = (int64_t)8 * kMaxBatch * std::max(m->QKV, H);
+  ALLOC(m->part, m->part_floats, sb);
+  ALLOC(m->apart, (int64_t)kMaxBatch * NQ * m->max_chunks * 132, sb);
+  ALLOC(m->ids_dev, std::max(d.max_positions, kMaxBatch), sb);
+  ALLOC(m->err, 1, sb);
+  ALLOC(m->rcos, (int64_t)d.max_positions * 64, sb);
+  ALLOC(m->rsin, (int64_t)d.max_positions * 64, sb);
+#undef ALLOC
+  hipError_t e = hipHostMalloc((void**)&m->ids_host, sizeof(int32_t) * std::max(d.max_positions, kMaxBatch),
+                               hipHostMallocDefault);
+  if (e != hipSuccess) {
+    free_model(m);
+    return fail(GQA_E_OOM, "pinned staging allocation failed: %s", hipGetErrorString(e));
+  }
+  if ((e = hipEventCreateWithFlags(&m->ids_evt, hipEventDisableTiming)) != hipSuccess) {
+    free_model(m);
+    return fail(GQA_E_HIP, "hipEventCreate failed: %s", hipGetErrorString(e));
+  }
+
+  // weights
+  hipStream_t st = nullptr;
+  const float sc = weight_scale();
+  uint16_t* tmp = nullptr;
+  if (q8) {
+    int64_t biggest = std::max<int64_t>(std::max<int64_t>((int64_t)2 * F * H, (int64_t)m->QKV * H),
+                                        std::max<int64_t>((int64_t)H * m->QD, (int64_t)H * F));
+    void* v = nullptr;
+    if (hipMalloc(&v, biggest * 2) != hipSuccess) {
+      (void)hipGetLastError();
+      free_model(m);
+      return fail(GQA_E_OOM, "temporary BF16 buffer for quantisation does not fit");
+    }
+    tmp = (uint16_t*)v;
+  }
+  auto gen = [&](uint16_t* dst, int kind, int layer, int64_t r, int64_t c, int mode, int64_t off) {
+    return launch_gen_weights(dst, tensor_key(seed, d.n_layers, kind, layer), r, c, mode, off, sc, st);
+  };
+  hipError_t ge = hipSuccess;
+  auto chk = [&](hipError_t x) {
+    if (x != hipSuccess && ge == hipSuccess) ge = x;
+  };
+  chk(gen(m->embed, GQA_T_EMBED, -1, V, H, 0, 0));
+  if (!d.tied) chk(gen(m->lm_head, GQA_T_LM_HEAD, -1, V, H, 0, 0));
+  chk(launch_fill_u16(m->final_norm, H, 0x3F80, st));
+  const int KVD = kKvHeads * kHeadDim;
+  for (int l = 0; l < d.n_layers && ge == hipSuccess; ++l) {
+    LayerW& w = m->L[l];
+    chk(launch_fill_u16(w.attn_norm, H, 0x3F80, st));
+    chk(launch_fill_u16(w.ffn_norm, H, 0x3F80, st));
+    chk(launch_fill_u16(w.q_norm, kHeadDim, 0x3F80, st));
+    chk(launch_fill_u16(w.k_norm, kHeadDim, 0x3F80, st));
+    uint16_t* dqkv = q8 ? tmp : w.wqkv;
+    chk(gen(dqkv, GQA_T_Q, l, m->QD, H, 0, 0));
+    chk(gen(dqkv, GQA_T_K, l, KVD, H, 0, m->QD));
+    chk(gen(dqkv, GQA_T_V, l, KVD, H, 0, m->QD + KVD));
+    if (q8) chk(launch_quantize_q8_0(tmp, w.qqkv, w.sqkv, m->QKV, H, st));
+    uint16_t* dO = q8 ? tmp : w.wo;
+    chk(gen(dO, GQA_T_O, l, H, m->QD, 0, 0));
+    if (q8) chk(launch_quantize_q8_0(tmp, w.qo, w.so, H, m->QD, st));
+    uint16_t* dgu = q8 ? tmp : w.wgu;
+    chk(gen(dgu, GQA_T_GATE, l, F, H, 1, 0));
+    chk(gen(dgu, GQA_T_UP, l, F, H, 2, 0));
+    if (q8) chk(launch_quantize_q8_0(tmp, w.qgu, w.sgu, 2 * F, H, st));
+    uint16_t* dD = q8 ? tmp : w.wd;
+    chk(gen(dD, GQA_T_DOWN, l, H, F, 0, 0));
+    if (q8) chk(launch_quantize_q8_0(tmp, w.qd, w.sd, H, F, st));
+    if (q8) chk(hipStreamSynchronize(st));
+    chk(hipMemsetAsync(w.kpool, 0, pool_elems * 2, st));
+    chk(hipMemsetAsync(w.vpool, 0, pool_elems * 2, st));
+  }
+  chk(hipMemsetAsync(m->err, 0, 4, st));
+  chk(hipDeviceSynchronize());
+  if (tmp) (void)hipFree(tmp);
+  if (ge != hipSuccess) {
+    free_model(m);
+    return fail(GQA_E_HIP, "weight generation failed: %s", hipGetErrorString(ge));
+  }
+
+  // RoPE: angle p * theta^(-2i/128) in double, cos/sin rounded to FP32.
+  {
+    std::vector<float> c((size_t)d.max_positions * 64), s((size_t)d.max_positions * 64);
+    for (int p = 0; p < d.max_positions; ++p)
+      for (int i = 0; i < 64; ++i) {
+        double inv = pow((double)d.rope_theta, -2.0 * i / 128.0);
+        double a = (double)p * inv;
+        c[(size_t)p * 64 + i] = (float)cos(a);
+        s[(size_t)p * 64 + i] = (float)sin(a);
+      }
+    e = hipMemcpy(m->rcos, c.data(), c.size() * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(m->rsin, s.data(), s.size() * 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      free_model(m);
+      return fail(GQA_E_HIP, "RoPE table upload failed: %s", hipGetErrorString(e));
+    }
+  }
+  m->block_used.assign(d.kv_pool_blocks, 0);
+  m->free_blocks = d.kv_pool_blocks;
+  *out = m;
+  return GQA_OK;
+}
+
+void gqa_model_destroy(gqa_model* model) {
+  if (!model) return;
+  (void)hipDeviceSynchronize();
+  free_model(model);
+}
+
+int gqa_model_get_info(const gqa_model* m, gqa_model_info* info) {
+  if (!m || !info) return fail(GQA_E_INVALID, "null argument");
+  info->round_tokens = m->R;
+  info->cu_count = m->cu;
+  info->weight_bytes = m->weight_bytes;
+  info->kv_pool_bytes = m->kv_bytes;
+  info->scratch_bytes = m->scratch_bytes;
+  info->free_blocks = m->free_blocks;
+  return GQA_OK;
+}
+
+int gqa_session_create(gqa_model* m, int32_t max_positions, const int32_t* block_ids, gqa_session** out) {
+  g_err.clear();
+  if (!m || !out) return fail(GQA_E_INVALID, "null argument");
+  if (max_positions < 1 || max_positions > m->d.max_positions)
+    return fail(GQA_E_INVALID, "max_positions %d outside [1, %d]", max_positions, m->d.max_positions);
+  int nb = (max_positions + kBlock - 1) / kBlock;
+  std::lock_guard<std::mutex> lk(m->mu);
+  std::vector<int32_t> blocks(nb);
+  if (block_ids) {
+    std::vector<char> seen(m->d.kv_pool_blocks, 0);
+    for (int i = 0; i < nb; ++i) {
+      int b = block_ids[i];
+      if (b < 0 || b >= m->d.kv_pool_blocks) return fail(GQA_E_INVALID, "block id %d outside the pool", b);
+      if (seen[b]) return fail(GQA_E_INVALID, "block id %d repeated", b);
+      if (m->block_used[b]) return fail(GQA_E_INVALID, "block id %d already owned by a session", b);
+      seen[b] = 1;
+      blocks[i] = b;
+    }
+  } else {
+    if (m->free_blocks < nb) return fail(GQA_E_OOM, "KV pool has %d free blocks, %d needed", m->free_blocks, nb);
+    int k = 0;
+    for (int b = 0; b < m->d.kv_pool_blocks && k < nb; ++b)
+      if (!m->block_used[b]) blocks[k++] = b;
+  }
+  gqa_session* s = new gqa_session();
+  s->m = m;
+  s->max_pos = max_positions;
+  s->blocks = blocks;
+  void* v = nullptr;
+  hipError_t e = hipMalloc(&v, sizeof(int32_t) * nb);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    delete s;
+    return fail(GQA_E_OOM, "block table allocation failed");
+  }
+  s->d_table = (int32_t*)v;
+  e = hipMemcpy(s->d_table, blocks.data(), sizeof(int32_t) * nb, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(v);
+    delete s;
+    return fail(GQA_E_HIP, "block table upload failed: %s", hipGetErrorString(e));
+  }
+  for (int b : blocks) m->block_used[b] = 1;
+  m->free_blocks -= nb;
+  m->sessions++;
+  *out = s;
+  return GQA_OK;
+}
+
+void gqa_session_destroy(gqa_session* s) {
+  if (!s) return;
+  gqa_model* m = s->m;
+  (void)hipDeviceSynchronize();
+  {
+    std::lock_guard<std::mutex> lk(m->mu);
+    for (int b : s->blocks) m->block_used[b] = 0;
+    m->free_blocks += (int)s->blocks.size();
+    m->sessions--;
+  }
+  (void)hipFree(s->d_table);
+  delete s;
+}
+
+int gqa_session_reset(gqa_session* s) {
+  if (!s) return fail(GQA_E_INVALID, "null session");
+  s->pos = 0;
+  return GQA_OK;
+}
+
+int32_t gqa_session_position(const gqa_session* s) { return s ? s->pos : -1; }
+
+}  // extern "C"
+
+namespace {
+
+// Stage host ids into pinned memory and copy them to the device on `st`. The staging buffer is
+// reused, so wait for the previous copy first.
+int upload_ids(gqa_model* m, const int32_t* ids, int n, hipStream_t st) {
+  HIP_TRY(hipEventSynchronize(m->ids_evt));
+  memcpy(m->ids_host, ids, sizeof(int32_t) * n);
+  HIP_TRY(hipMemcpyAsync(m->ids_dev, m->ids_host, sizeof(int32_t) * n, hipMemcpyHostToDevice, st));
+  HIP_TRY(hipEventRecord(m->ids_evt, st));
+  return GQA_OK;
+}
+
+constexpr int64_t kProfMax = 65536;
+
+// Bracket one launch of kernel class `cls` with events when that class is being recorded.
+struct ProfScope {
+  gqa_model* m;
+  hipStream_t st;
+  hipEvent_t stop = nullptr;
+  ProfScope(gqa_model* m_, int cls, hipStream_t st_) : m(m_), st(st_) {
+    if (m->prof_cls != cls) return;
+    if (m->prof_used >= kProfMax) {
+      m->prof_dropped++;
+      return;
+    }
+    while ((int64_t)m->prof_ev.size() < 2 * (m->prof_used + 1)) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return;
+      m->prof_ev.push_back(e);
+    }
+    hipEvent_t start = m->prof_ev[2 * m->prof_used];
+    stop = m->prof_ev[2 * m->prof_used + 1];
+    m->prof_used++;
+    (void)hipEventRecord(start, st);
+  }
+  ~ProfScope() {
+    if (stop) (void)hipEventRecord(stop, st);
+  }
+};
+
+#define LAUNCH(expr)                                                                                   \
+  do {                                                                                                 \
+    hipError_t e_ = (expr);                                                                            \
+    if (e_ != hipSuccess) return fail(GQA_E_HIP, "launch failed at %s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// Decode / batched decode over B rows whose embeddings are in m->x; ids already on the device.
+int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t* ids_dev, float* logits,
+               int32_t* argmax, hipStream_t st) {
+  const gqa_model_desc& d = m->d;
+  const int H = d.hidden, F = d.ffn, V = d.vocab, NQ = d.n_q_heads, QD = m->QD, QKV = m->QKV;
+  const float eps = d.rms_eps;
+  const int64_t pstride = (int64_t)kMaxBatch * std::max(QKV, H);
+  LAUNCH(launch_embed(m->embed, ids_dev, B, H, V, m->x, m->err, st));
+  LAUNCH(launch_rmsnorm(m->x, H, nullptr, 0, 0, 0, 1.f, m->L[0].attn_norm, H, eps, 1.f, m->xh, m->xl, H, B, st));
+  for (int l = 0; l < d.n_layers; ++l) {
+    const LayerW& w = m->L[l];
+    LAUNCH(launch_gemv(EPI_STORE, w.wqkv, w.qqkv, w.sqkv, H, QKV, m->xh, m->xl, H, B, m->s_qkv, m->part, pstride, QKV,
+                       nullptr, nullptr, 0, 1.f, st));
+    LAUNCH(launch_qk_rope_kv(true, m->part, m->s_qkv, (int)pstride, QKV, NQ, w.q_norm, w.k_norm, eps, m->rcos,
+                             m->rsin, 0, nullptr, rows, w.kpool, w.vpool, m->q, B, st));
+    LAUNCH(launch_attn_decode(m->q, NQ, rows, B, max_ctx, w.kpool, w.vpool, m->apart, m->max_chunks, kAttnOutScale,
+                              m->oh, m->ol, QD, st));
+    LAUNCH(launch_gemv(EPI_STORE, w.wo, w.qo, w.so, QD, H, m->oh, m->ol, QD, B, m->s_o, m->part, pstride, H, nullptr,
+                       nullptr, 0, 1.f, st));
+    LAUNCH(launch_rmsnorm(m->x, H, m->part, m->s_o, (int)pstride, H, 1.f / kAttnOutScale, w.ffn_norm, H, eps, 1.f,
+                          m->xh, m->xl, H, B, st));
+    {
+      ProfScope ps(m, GQA_PROF_DECODE_GATEUP, st);
+      LAUNCH(launch_gemv(EPI_SWIGLU, w.wgu, w.qgu, w.sgu, H, 2 * F, m->xh, m->xl, H, B, 1, nullptr, 0, 0, m->mh,
+                         m->ml, F, 1.f, st));
+    }
+    LAUNCH(launch_gemv(EPI_STORE, w.wd, w.qd, w.sd, F, H, m->mh, m->ml, F, B, m->s_d, m->part, pstride, H, nullptr,
+                       nullptr, 0, 1.f, st));
+    const uint16_t* nw = l + 1 < d.n_layers ? m->L[l + 1].attn_norm : m->final_norm;
+    LAUNCH(launch_rmsnorm(m->x, H, m->part, m->s_d, (int)pstride, H, 1.f, nw, H, eps, 1.f, m->xh, m->xl, H, B, st));
+  }
+  {
+    ProfScope ps(m, GQA_PROF_DECODE_LMHEAD, st);
+    LAUNCH(launch_gemv(EPI_STORE, m->lm_head, nullptr, nullptr, H, V, m->xh, m->xl, H, B, 1, logits, 0, V, nullptr,
+                       nullptr, 0, 1.f, st));
+  }
+  if (argmax) LAUNCH(launch_argmax(logits, V, V, B, argmax, st));
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_session_eval_prefill(gqa_session* s, const int32_t* ids, int32_t n, float* logits, int32_t* argmax,
+                             hipStream_t st) {
+  g_err.clear();
+  if (!s || !ids || !logits) return fail(GQA_E_INVALID, "null argument");
+  gqa_model* m = s->m;
+  const gqa_model_desc& d = m->d;
+  if (n < 1) return fail(GQA_E_INVALID, "n must be >= 1");
+  if ((int64_t)s->pos + n > s->max_pos)
+    return fail(GQA_E_RANGE, "context overflow: %d + %d > %d", s->pos, n, s->max_pos);
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= d.vocab) return fail(GQA_E_RANGE, "token id %d at %d outside [0, %d)", ids[i], i, d.vocab);
+  int rc = upload_ids(m, ids, n, st);
+  if (rc) return rc;
+  const int H = d.hidden, F = d.ffn, V = d.vocab, NQ = d.n_q_heads, QD = m->QD, QKV = m->QKV;
+  const float eps = d.rms_eps;
+  Rows none{};
+  for (int off = 0; off < n; off += m->R) {
+    const int T = std::min(m->R, n - off);
+    const int pos0 = s->pos + off;
+    LAUNCH(launch_embed(m->embed, m->ids_dev + off, T, H, d.vocab, m->x, m->err, st));
+    LAUNCH(launch_rmsnorm(m->x, H, nullptr, 0, 0, 0, 1.f, m->L[0].attn_norm, H, eps, 1.f, m->xh, m->xl, H, T, st));
+    for (int l = 0; l < d.n_layers; ++l) {
+      const LayerW& w = m->L[l];
+      LAUNCH(launch_gemm(EPI_STORE, w.wqkv, w.qqkv, w.sqkv, H, QKV, m->xh, m->xl, H, T, m->qkv, QKV, 1.f, nullptr,
+                         nullptr, 0, 1.f, st));
+      LAUNCH(launch_qk_rope_kv(false, m->qkv, 0, 0, QKV, NQ, w.q_norm, w.k_norm, eps, m->rcos, m->rsin, pos0,
+                               s->d_table, none, w.kpool, w.vpool, m->q, T, st));
+      {
+        ProfScope ps(m, GQA_PROF_PREFILL_ATTN, st);
+        LAUNCH(launch_attn_prefill(m->q, NQ, T, pos0, s->d_table, w.kpool, w.vpool, kAttnOutScale, m->oh, m->ol, QD,
+                                   st));
+      }
+      LAUNCH(launch_gemm(EPI_ADD, w.wo, w.qo, w.so, QD, H, m->oh, m->ol, QD, T, m->x, H, 1.f / kAttnOutScale, nullptr,
+                         nullptr, 0, 1.f, st));
+      LAUNCH(launch_rmsnorm(m->x, H, nullptr, 0, 0, 0, 1.f, w.ffn_norm, H, eps, 1.f, m->xh, m->xl, H, T, st));
+      {
+        ProfScope ps(m, GQA_PROF_PREFILL_GATEUP, st);
+        LAUNCH(launch_gemm(EPI_SWIGLU, w.wgu, w.qgu, w.sgu, H, 2 * F, m->xh, m->xl, H, T, nullptr, 0, 1.f, m->mh,
+                           m->ml, F, 1.f, st));
+      }
+      LAUNCH(launch_gemm(EPI_ADD, w.wd, w.qd, w.sd, F, H, m->mh, m->ml, F, T, m->x, H, 1.f, nullptr, nullptr, 0, 1.f,
+                         st));
+      if (l + 1 < d.n_layers)
+        LAUNCH(launch_rmsnorm(m->x, H, nullptr, 0, 0, 0, 1.f, m->L[l + 1].attn_norm, H, eps, 1.f, m->xh, m->xl, H, T,
+                              st));
+    }
+    if (off + T == n) {
+      LAUNCH(launch_rmsnorm(m->x + (int64_t)(T - 1) * H, H, nullptr, 0, 0, 0, 1.f, m->final_norm, H, eps, 1.f, m->xh,
+                            m->xl, H, 1, st));
+      LAUNCH(launch_gemv(EPI_STORE, m->lm_head, nullptr, nullptr, H, V, m->xh, m->xl, H, 1, 1, logits, 0, V, nullptr,
+                         nullptr, 0, 1.f, st));
+      if (argmax) LAUNCH(launch_argmax(logits, V, V, 1, argmax, st));
+    }
+  }
+  s->pos += n;
+  return GQA_OK;
+}
+
+int gqa_session_eval_batch(gqa_session* const* ss, int32_t B, const int32_t* ids, int32_t ids_on_device,
+                           float* logits, int32_t* argmax, hipStream_t st) {
+  g_err.clear();
+  if (!ss || !ids || !logits) return fail(GQA_E_INVALID, "null argument");
+  if (B < 1 || B > kMaxBatch) return fail(GQA_E_INVALID, "B = %d outside [1, %d]", B, kMaxBatch);
+  gqa_model* m = ss[0] ? ss[0]->m : nullptr;
+  if (!m) return fail(GQA_E_INVALID, "null session");
+  Rows rows{};
+  int max_ctx = 0;
+  for (int b = 0; b < B; ++b) {
+    if (!ss[b]) return fail(GQA_E_INVALID, "null session at %d", b);
+    if (ss[b]->m != m) return fail(GQA_E_INVALID, "sessions of different models");
+    for (int c = 0; c < b; ++c)
+      if (ss[c] == ss[b]) return fail(GQA_E_INVALID, "session repeated at rows %d and %d", c, b);
+    if (ss[b]->pos + 1 > ss[b]->max_pos) return fail(GQA_E_RANGE, "context overflow in row %d", b);
+    rows.pos[b] = ss[b]->pos;
+    rows.table[b] = ss[b]->d_table;
+    max_ctx = std::max(max_ctx, ss[b]->pos + 1);
+  }
+  const int32_t* ids_dev = ids;
+  if (!ids_on_device) {
+    for (int b = 0; b < B; ++b)
+      if (ids[b] < 0 || ids[b] >= m->d.vocab)
+        return fail(GQA_E_RANGE, "token id %d in row %d outside [0, %d)", ids[b], b, m->d.vocab);
+    int rc = upload_ids(m, ids, B, st);
+    if (rc) return rc;
+    ids_dev = m->ids_dev;
+  }
+  int rc = run_decode(m, rows, B, max_ctx, ids_dev, logits, argmax, st);
+  if (rc) return rc;
+  for (int b = 0; b < B; ++b) ss[b]->pos++;
+  return GQA_OK;
+}
+
+int gqa_session_eval_decode(gqa_session* s, const int32_t* id, int32_t id_on_device, float* logits, int32_t* argmax,
+                            hipStream_t st) {
+  return gqa_session_eval_batch(&s, 1, id, id_on_device, logits, argmax, st);
+}
+
+int gqa_model_profile(gqa_model* m, int32_t cls) {
+  if (!m) return fail(GQA_E_INVALID, "null model");
+  if (cls < GQA_PROF_NONE || cls > GQA_PROF_DECODE_LMHEAD) return fail(GQA_E_INVALID, "unknown kernel class %d", cls);
+  HIP_TRY(hipDeviceSynchronize());
+  m->prof_cls = cls;
+  m->prof_used = 0;
+  m->prof_dropped = 0;
+  return GQA_OK;
+}
+
+int gqa_model_profile_read(gqa_model* m, int64_t* launches, double* total_ms, int64_t* dropped) {
+  if (!m || !launches || !total_ms) return fail(GQA_E_INVALID, "null argument");
+  HIP_TRY(hipDeviceSynchronize());
+  double tot = 0.0;
+  for (int64_t i = 0; i < m->prof_used; ++i) {
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, m->prof_ev[2 * i], m->prof_ev[2 * i + 1]));
+    tot += ms;
+  }
+  *launches = m->prof_used;
+  *total_ms = tot;
+  if (dropped) *dropped = m->prof_dropped;
+  return GQA_OK;
+}
+
+int gqa_model_check_device_error(gqa_model* m, hipStream_t st) {
+  if (!m) return fail(GQA_E_INVALID, "null model");
+  HIP_TRY(hipStreamSynchronize(st));
+  int32_t v = 0;
+  HIP_TRY(hipMemcpy(&v, m->err, 4, hipMemcpyDeviceToHost));
+  if (v) {
+    HIP_TRY(hipMemset(m->err, 0, 4));
+    return fail(GQA_E_RANGE, "a device-resident token id was outside [0, %d)", m->d.vocab);
+  }
+  return GQA_OK;
+}
+
+static int physical_row(const gqa_model* m, int kind, int r, const void** base, int* cols, bool q8, int layer) {
+  const gqa_model_desc& d = m->d;
+  const int H = d.hidden, F = d.ffn;
+  const LayerW* w = layer >= 0 && layer < d.n_layers ? &m->L[layer] : nullptr;
+  switch (kind) {
+    case GQA_T_Q: *cols = H; *base = q8 ? (const void*)w->qqkv : w->wqkv; return r;
+    case GQA_T_K: *cols = H; *base = q8 ? (const void*)w->qqkv : w->wqkv; return m->QD + r;
+    case GQA_T_V: *cols = H; *base = q8 ? (const void*)w->qqkv : w->wqkv; return m->QD + kKvHeads * kHeadDim + r;
+    case GQA_T_O: *cols = m->QD; *base = q8 ? (const void*)w->qo : w->wo; return r;
+    case GQA_T_GATE: *cols = H; *base = q8 ? (const void*)w->qgu : w->wgu; return 32 * (r / 16) + (r % 16);
+    case GQA_T_UP: *cols = H; *base = q8 ? (const void*)w->qgu : w->wgu; return 32 * (r / 16) + 16 + (r % 16);
+    case GQA_T_DOWN: *cols = F; *base = q8 ? (const void*)w->qd : w->wd; return r;
+    default: return -1;
+  }
+}
+
+static int logical_rows(const gqa_model* m, int kind) {
+  const gqa_model_desc& d = m->d;
+  switch (kind) {
+    case GQA_T_Q: return m->QD;
+    case GQA_T_K: case GQA_T_V: return kKvHeads * kHeadDim;
+    case GQA_T_O: case GQA_T_DOWN: return d.hidden;
+    case GQA_T_GATE: case GQA_T_UP: return d.ffn;
+    case GQA_T_EMBED: case GQA_T_LM_HEAD: return d.vocab;
+    case GQA_T_ATTN_NORM: case GQA_T_FFN_NORM: case GQA_T_FINAL_NORM: return 1;
+    case GQA_T_Q_NORM: case GQA_T_K_NORM: return 1;
+    default: return -1;
+  }
+}
+
+int gqa_debug_read_weight(gqa_model* m, int32_t kind, int32_t layer, int32_t row0, int32_t rows, uint16_t* dst) {
+  if (!m || !dst) return fail(GQA_E_INVALID, "null argument");
+  const gqa_model_desc& d = m->d;
+  int nrow = logical_rows(m, kind);
+  if (nrow < 0) return fail(GQA_E_INVALID, "unknown tensor kind %d", kind);
+  bool per_layer = !(kind == GQA_T_EMBED || kind == GQA_T_LM_HEAD || kind == GQA_T_FINAL_NORM);
+  if (per_layer && (layer < 0 || layer >= d.n_layers)) return fail(GQA_E_INVALID, "layer %d out of range", layer);
+  if (row0 < 0 || rows < 1 || row0 + rows > nrow) return fail(GQA_E_INVALID, "rows out of range");
+  HIP_TRY(hipDeviceSynchronize());
+  const uint16_t* src = nullptr;
+  int cols = d.hidden;
+  switch (kind) {
+    case GQA_T_EMBED: src = m->embed; break;
+    case GQA_T_LM_HEAD:
+      if (d.tied) return fail(GQA_E_INVALID, "tied model has no separate lm_head");
+      src = m->lm_head;
+      break;
+    case GQA_T_FINAL_NORM: src = m->final_norm; break;
+    case GQA_T_ATTN_NORM: src = m->L[layer].attn_norm; break;
+    case GQA_T_FFN_NORM: src = m->L[layer].ffn_norm; break;
+    case GQA_T_Q_NORM: src = m->L[layer].q_norm; cols = kHeadDim; break;
+    case GQA_T_K_NORM: src = m->L[layer].k_norm; cols = kHeadDim; break;
+    default: break;
+  }
+  if (src) {
+    HIP_TRY(hipMemcpy(dst, src + (int64_t)row0 * cols, (size_t)rows * cols * 2, hipMemcpyDeviceToHost));
+    return GQA_OK;
+  }
+  if (d.scheme == GQA_SCHEME_Q8_0) return fail(GQA_E_INVALID, "Q8_0 model keeps no BF16 projections");
+  for (int r = 0; r < rows; ++r) {
+    const void* base = nullptr;
+    int pr = physical_row(m, kind, row0 + r, &base, &cols, false, layer);
+    HIP_TRY(hipMemcpy(dst + (int64_t)r * cols, (const uint16_t*)base + (int64_t)pr * cols, (size_t)cols * 2,
+                      hipMemcpyDeviceToHost));
+  }
+  return GQA_OK;
+}
+
+int gqa_debug_read_q8(gqa_model* m, int32_t kind, int32_t layer, int32_t row0, int32_t rows, int8_t* quants,
+                      uint16_t* scales) {
+  if (!m || !quants || !scales) return fail(GQA_E_INVALID, "null argument");
+  const gqa_model_desc& d = m->d;
+  if (d.scheme != GQA_SCHEME_Q8_0) return fail(GQA_E_INVALID, "not a Q8_0 model");
+  if (layer < 0 || layer >= d.n_layers) return fail(GQA_E_INVALID, "layer out of range");
+  int nrow = logical_rows(m, kind);
+  const void* base = nullptr;
+  int cols = 0;
+  if (nrow < 0 || physical_row(m, kind, 0, &base, &cols, true, layer) < 0)
+    return fail(GQA_E_INVALID, "not a projection kind");
+  if (row0 < 0 || rows < 1 || row0 + rows > nrow) return fail(GQA_E_INVALID, "rows out of range");
+  HIP_TRY(hipDeviceSynchronize());
+  const LayerW& w = m->L[layer];
+  for (int r = 0; r < rows; ++r) {
+    int pr = physical_row(m, kind, row0 + r, &base, &cols, true, layer);
+    const f16* sb = kind == GQA_T_O ? w.so : kind == GQA_T_DOWN ? w.sd : (kind == GQA_T_GATE || kind == GQA_T_UP) ? w.sgu : w.sqkv;
+    HIP_TRY(hipMemcpy(quants + (int64_t)r * cols, (const int8_t*)base + (int64_t)pr * cols, (size_t)cols,
+                      hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemcpy(scales + (int64_t)r * (cols / 32), sb + (int64_t)pr * (cols / 32), (size_t)(cols / 32) * 2,
+                      hipMemcpyDeviceToHost));
+  }
+  return GQA_OK;
+}
+
+int gqa_debug_read_kv(gqa_session* s, int32_t layer, int32_t pos0, int32_t n, uint16_t* k, uint16_t* v) {
+  if (!s || !k || !v) return fail(GQA_E_INVALID, "null argument");
+  gqa_model* m = s->m;
+  if (layer < 0 || layer >= m->d.n_layers) return fail(GQA_E_INVALID, "layer out of range");
+  if (pos0 < 0 || n < 1 || pos0 + n > s->max_pos) return fail(GQA_E_INVALID, "positions out of range");
+  HIP_TRY(hipDeviceSynchronize());
+  const LayerW& w = m->L[layer];
+  for (int i = 0; i < n; ++i) {
+    int p = pos0 + i;
+    int phys = s->blocks[p / kBlock];
+    for (int h = 0; h < kKvHeads; ++h) {
+      int64_t off = (((int64_t)phys * kKvHeads + h) * kBlock + (p % kBlock)) * kHeadDim;
+      HIP_TRY(hipMemcpy(k + ((int64_t)i * kKvHeads + h) * kHeadDim, w.kpool + off, kHeadDim * 2, hipMemcpyDeviceToHost));
+      HIP_TRY(hipMemcpy(v + ((int64_t)i * kKvHeads + h) * kHeadDim, w.vpool + off, kHeadDim * 2, hipMemcpyDeviceToHost));
+    }
+  }
+  return GQA_OK;
+}
+
+int gqa_debug_read_rope(gqa_model* m, int32_t n, float* c, float* s) {
+  if (!m || !c || !s) return fail(GQA_E_INVALID, "null argument");
+  if (n < 1 || n > m->d.max_positions) return fail(GQA_E_INVALID, "n out of range");
+  HIP_TRY(hipMemcpy(c, m->rcos, (size_t)n * 64 * 4, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(s, m->rsin, (size_t)n * 64 * 4, hipMemcpyDeviceToHost));
+  return GQA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+/*
+ * gqa.h - C ABI of the MI355X (gfx950) dense Qwen3-style GQA decoder library (libgqa355.so).
+ *
+ * The library evaluates the forward pass of a dense grouped-query-attention decoder: prefill
+ * and incremental decode producing full-vocabulary FP32 logits, over a paged BF16 KV cache.
+ * Every step runs in hand-written HIP kernels; there is no CPU fallback. Sources, by page and
+ * section:
+ *   Kipp Model Support, "The registry": dense Qwen3 decoders, BF16 weights, 8 KV heads of width
+ *     128, vocabulary 151,936, RMS epsilon 1e-6, per-model RoPE theta and embedding tying.
+ *   Kipp Model Support, "Validated results" (qwen3-0.6b-base): BF16 K/V storage contract;
+ *     (qwen3-8b-base): untied lm_head.
+ *   Kipp Model Support, "Quantization (Q8_0)": Q8_0 weights for the seven per-layer projections.
+ *   Kipp Roadmap, status v0.0.2: per-session 32-position block table (bitwise equal to the
+ *     contiguous layout), batched evaluation equal to isolated evaluation.
+ *   Kipp Roadmap, status v0.0.3: model-owned KV slab shared by pooled sessions.
+ *   Kipp Roadmap, status v0.0.4: device-derived prefill rounds; activation scratch per model.
+ *   Kipp Reproducing, "Build": backend failures are fatal, never a silent fallback.
+ *
+ * Conventions
+ *   - Every function returning int returns GQA_OK (0) or a negative GQA_E_* code; the message
+ *     of the last failure on the calling thread is available from gqa_last_error(). A failing
+ *     call leaves the model and session state unchanged, unless stated otherwise.
+ *   - "device pointer" means memory of the model's HIP device (hipMalloc, or a torch CUDA
+ *     tensor's data_ptr()); "host pointer" means ordinary CPU memory. The caller owns every
+ *     buffer it passes; the library keeps no reference after the call returns (work it
+ *     enqueued still reads/writes them in stream order).
+ *   - `stream` is a hipStream_t of the model's device (NULL = the legacy default stream). All
+ *     work is enqueued on it and the call returns without synchronising, except where stated.
+ *     Calls on sessions of one model must be serialised on one stream: the activation scratch
+ *     and the split-K partial buffers belong to the model.
+ *   - Weights use row-major [out][in] matrices in the generator's logical layout (below).
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQA_OK 0
+#define GQA_E_INVALID (-1)   /* bad argument or descriptor */
+#define GQA_E_OOM (-2)       /* device memory or KV block pool exhausted */
+#define GQA_E_DEVICE (-3)    /* no gfx950 device, or the current device is not gfx950 */
+#define GQA_E_HIP (-4)       /* a HIP runtime call or kernel launch failed */
+#define GQA_E_RANGE (-5)     /* token id outside [0, vocab) or context overflow */
+
+#define GQA_SCHEME_BF16 0
+#define GQA_SCHEME_Q8_0 1
+
+#define GQA_MAX_BATCH 32
+#define GQA_BLOCK_POSITIONS 32
+
+typedef struct gqa_model gqa_model;
+typedef struct gqa_session gqa_session;
+
+/* Model shape (Kipp Model Support, "The registry"). n_kv_heads must be 8 and head_dim 128;
+ * n_q_heads must be 16 or 32; hidden, 2*ffn and n_q_heads*128 must be multiples of 256 and
+ * hidden <= 4096; vocab must be a multiple of 16. */
+typedef struct {
+  int32_t n_layers;
+  int32_t hidden;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t ffn;
+  int32_t vocab;
+  int32_t tied;             /* 1: lm_head is the token embedding; 0: a separate lm_head */
+  float rope_theta;
+  float rms_eps;
+  int32_t scheme;           /* GQA_SCHEME_BF16 or GQA_SCHEME_Q8_0 (the seven projections) */
+  int32_t kv_pool_blocks;   /* physical 32-position KV blocks in the model-owned pool */
+  int32_t max_positions;    /* longest sequence any session may reach (RoPE table size) */
+  int32_t max_round_tokens; /* prefill round width; 0 derives it from the device (CUs x 8) */
+} gqa_model_desc;
+
+/* Read-only facts about a created model. */
+typedef struct {
+  int32_t round_tokens;       /* prefill round width in use */
+  int32_t cu_count;           /* compute units of the device */
+  int64_t weight_bytes;       /* device bytes of all weights (Q8_0: quants + scales) */
+  int64_t kv_pool_bytes;      /* device bytes of the K and V pools */
+  int64_t scratch_bytes;      /* device bytes of per-model activation scratch */
+  int32_t free_blocks;        /* KV blocks not owned by any session */
+} gqa_model_info;
+
+/* Create a model on the current HIP device with seeded synthetic weights.
+ * Weights: the counter-based generator documented in the library source (SplitMix64 outputs
+ * summed Irwin-Hall style, scaled to std 0.02, rounded to BF16), one key per tensor derived
+ * from `seed`; norm weights are 1.0. For GQA_SCHEME_Q8_0 the seven projections are then
+ * quantised to Q8_0 (32-weight blocks, fp16 scale = max|w|/127, int8 quants).
+ * Allocates weights, the KV pool and per-model scratch; fails with GQA_E_OOM if they do not
+ * fit, GQA_E_DEVICE if the device is not gfx950, GQA_E_INVALID for a bad descriptor.
+ * Synchronises the device before returning. *out is set only on success. */
+int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out);
+
+/* Free a model. All its sessions must have been destroyed. NULL is ignored. */
+void gqa_model_destroy(gqa_model* model);
+
+int gqa_model_get_info(const gqa_model* model, gqa_model_info* info);
+
+/* Create a session that can hold `max_positions` positions. It takes
+ * ceil(max_positions/32) physical blocks from the model pool:
+ *   block_ids == NULL: the lowest-numbered free blocks, in increasing order (identity-like);
+ *   otherwise a host array of that many distinct, currently free block ids (any order:
+ *   logical block i of the session lives in physical block block_ids[i]).
+ * Returns GQA_E_OOM if the pool has too few free blocks, GQA_E_INVALID for a bad id list.
+ * Uploads the block table (synchronously). */
+int gqa_session_create(gqa_model* model, int32_t max_positions, const int32_t* block_ids, gqa_session** out);
+
+/* Return the session's blocks to the pool and free it. NULL is ignored. */
+void gqa_session_destroy(gqa_session* session);
+
+/* Set the position to 0, keeping the blocks. */
+int gqa_session_reset(gqa_session* session);
+
+/* Number of positions evaluated so far. */
+int32_t gqa_session_position(const gqa_session* session);
+
+/* Append n >= 1 prompt tokens (host array of ids in [0, vocab)) at positions
+ * [pos, pos + n), in rounds of the model's round width, and write the logits of the last new
+ * position to `logits` (device, vocab floats) and its argmax (lowest index on ties) to
+ * `argmax` (device, one int32; may be NULL). GQA_E_RANGE if an id is out of range or
+ * pos + n exceeds the session's max_positions. */
+int gqa_session_eval_prefill(gqa_session* session, const int32_t* ids, int32_t n, float* logits, int32_t* argmax,
+                             hipStream_t stream);
+
+/* Evaluate one token at the session's position. `id` is a host pointer when id_on_device is
+ * 0 (validated: GQA_E_RANGE if outside [0, vocab)) or a device pointer when 1 (for greedy
+ * loops without host round trips, e.g. the previous call's argmax buffer). A device id
+ * outside [0, vocab) cannot be reported synchronously: its logits become NaN, argmax -1, and
+ * the model's sticky device error is set (see gqa_model_check_device_error); the position
+ * still advances. Writes vocab logits and the argmax like eval_prefill. */
+int gqa_session_eval_decode(gqa_session* session, const int32_t* id, int32_t id_on_device, float* logits,
+                            int32_t* argmax, hipStream_t stream);
+
+/* One token for each of B distinct sessions of the same model (1 <= B <= 32): row b of
+ * `ids` (host or device per ids_on_device, as for eval_decode) is evaluated at sessions[b]'s
+ * position. Writes logits [B][vocab] and argmax [B] (device). Row b is bit-identical to
+ * gqa_session_eval_decode on sessions[b] alone. GQA_E_INVALID for duplicate sessions, mixed
+ * models or B out of range; GQA_E_RANGE for context overflow or a host id out of range. */
+int gqa_session_eval_batch(gqa_session* const* sessions, int32_t B, const int32_t* ids, int32_t ids_on_device,
+                           float* logits, int32_t* argmax, hipStream_t stream);
+
+/* Synchronise `stream`, then return GQA_E_RANGE (and clear the flag) if a device-resident
+ * token id was out of range since the last check, else GQA_OK. */
+int gqa_model_check_device_error(gqa_model* model, hipStream_t stream);
+
+/* Kernel timing with HIP events on the caller's stream, for roofline reports: while a class is
+ * selected, every launch of that kernel class is bracketed by a pair of events.
+ * gqa_model_profile(model, cls) starts a new recording (cls = GQA_PROF_NONE stops);
+ * gqa_model_profile_read synchronises the device and returns the launch count and the summed
+ * event time in milliseconds of the current recording. At most 65,536 launches are recorded;
+ * later ones are counted in *dropped. */
+#define GQA_PROF_NONE 0
+#define GQA_PROF_DECODE_GATEUP 1   /* decode gate/up matvec with SwiGLU (HBM bound) */
+#define GQA_PROF_PREFILL_GATEUP 2  /* prefill gate/up GEMM with SwiGLU (matrix-core bound) */
+#define GQA_PROF_PREFILL_ATTN 3    /* prefill flash attention */
+#define GQA_PROF_DECODE_LMHEAD 4   /* decode lm_head matvec */
+int gqa_model_profile(gqa_model* model, int32_t kernel_class);
+int gqa_model_profile_read(gqa_model* model, int64_t* launches, double* total_ms, int64_t* dropped);
+
+/* Message of the last failure on this thread ("" if none). Valid until the next call. */
+const char* gqa_last_error(void);
+
+/* ---- inspection, for tests (synchronous) ---- */
+
+/* Tensor kinds for gqa_debug_read_weight, in the generator's order. */
+#define GQA_T_EMBED 0
+#define GQA_T_ATTN_NORM 1
+#define GQA_T_Q 2
+#define GQA_T_K 3
+#define GQA_T_V 4
+#define GQA_T_Q_NORM 5
+#define GQA_T_K_NORM 6
+#define GQA_T_O 7
+#define GQA_T_FFN_NORM 8
+#define GQA_T_GATE 9
+#define GQA_T_UP 10
+#define GQA_T_DOWN 11
+#define GQA_T_FINAL_NORM 12
+#define GQA_T_LM_HEAD 13
+
+/* Copy `rows` logical rows starting at `row0` of a BF16 tensor (before any Q8_0
+ * quantisation the library does not keep BF16 copies of Q8_0 projections: GQA_E_INVALID)
+ * into `dst` (host, rows x cols uint16 BF16 bits, row-major in the logical [out][in] layout). */
+int gqa_debug_read_weight(gqa_model* model, int32_t kind, int32_t layer, int32_t row0, int32_t rows, uint16_t* dst);
+
+/* For a Q8_0 model: copy logical rows [row0, row0+rows) of a projection as int8 quants
+ * (rows x cols) and fp16 scale bits (rows x cols/32) into host buffers. */
+int gqa_debug_read_q8(gqa_model* model, int32_t kind, int32_t layer, int32_t row0, int32_t rows, int8_t* quants,
+                      uint16_t* scales);
+
+/* Copy the BF16 bits of K and V of `layer` for logical positions [pos0, pos0+n) of a session,
+ * read through its block table, into host arrays of n x 8 x 128 uint16 each. */
+int gqa_debug_read_kv(gqa_session* session, int32_t layer, int32_t pos0, int32_t n, uint16_t* k, uint16_t* v);
+
+/* Copy the FP32 RoPE tables (positions [0, n) x 64 cos, then sin) into host arrays. */
+int gqa_debug_read_rope(gqa_model* model, int32_t n, float* cos_out, float* sin_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GQA_H */

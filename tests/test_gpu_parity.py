@@ -1,0 +1,327 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the same seeded
+inputs. Gate (Kipp Model Support, "What the gates check"): identical argmax and full-logit
+NMSE <= 1e-4 at prefill and at every decode position; paged KV bitwise equal to the contiguous
+layout (Kipp Roadmap, status v0.0.2); batched evaluation equal to isolated evaluation."""
+import numpy as np
+import pytest
+
+import synth
+import oracle
+from oracle import model as om
+from parity_util import Gate, nmse
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_gqa_decoder_amd as lib
+    lib.load()
+    return lib
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+
+
+def oracle_greedy(shape, seed, prompt, steps, scheme="bf16"):
+    """Oracle logits at the last prompt position and at each greedy decode step, and the
+    greedy tokens fed at each step."""
+    m = oracle.OracleModel(shape, seed, scheme)
+    s = oracle.OracleSession(m, oracle.ContiguousKV.for_shape(shape, len(prompt) + steps + 1))
+    logits = [s.prefill(prompt)]
+    toks = []
+    for _ in range(steps):
+        t = om.argmax(logits[-1])
+        toks.append(t)
+        logits.append(s.decode(t))
+    return logits, toks
+
+
+def gpu_teacher_forced(model, sess, prompt, toks, vocab):
+    lg = torch.empty(vocab, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    out = []
+    sess.prefill(prompt, lg, am)
+    torch.cuda.synchronize()
+    out.append((lg.cpu().numpy(), int(am.item())))
+    for t in toks:
+        sess.decode(int(t), lg, am)
+        torch.cuda.synchronize()
+        out.append((lg.cpu().numpy(), int(am.item())))
+    return out
+
+
+def test_weights_match_generator(g):
+    shape = synth.TINY
+    say("weights", shape.name)
+    m = g.Model.from_shape(shape, seed=1001, kv_pool_blocks=4, max_positions=64)
+    H = shape.hidden
+    emb = synth.tensor_bits(shape, 1001, "embed")
+    for r0 in (0, 77777, shape.vocab - 8):
+        assert np.array_equal(m.read_weight("embed", -1, r0, 8, H), emb[r0:r0 + 8])
+    for l in range(shape.n_layers):
+        for nm, dims in shape.layer_tensor_shapes().items():
+            if nm in synth.NORM_TENSORS:
+                continue
+            rows, cols = dims
+            ref = synth.tensor_bits(shape, 1001, nm, l)
+            for r0 in (0, rows // 2 + 3, rows - 5):
+                n = min(5, rows - r0)
+                assert np.array_equal(m.read_weight(nm, l, r0, n, cols), ref[r0:r0 + n]), (nm, l, r0)
+    assert np.all(m.read_weight("final_norm", -1, 0, 1, H) == 0x3F80)
+    m.close()
+
+
+def test_untied_lm_head_generated(g):
+    shape = synth.reduced(synth.TINY, tied=False, n_layers=1)
+    m = g.Model.from_shape(shape, seed=7, kv_pool_blocks=2, max_positions=32)
+    ref = synth.tensor_bits(shape, 7, "lm_head")
+    assert np.array_equal(m.read_weight("lm_head", -1, 1000, 4, shape.hidden), ref[1000:1004])
+    m.close()
+
+
+def test_rope_table_matches_oracle(g):
+    shape = synth.TINY
+    m = g.Model.from_shape(shape, seed=1, kv_pool_blocks=2, max_positions=13000)
+    c, s = m.read_rope(13000)
+    rc, rs = om.rope_tables(shape.rope_theta, np.arange(13000))
+    ulp = lambda a, b: np.abs(a.view(np.int32).astype(np.int64) - b.view(np.int32).astype(np.int64))
+    assert ulp(c, rc).max() <= 1 and ulp(s, rs).max() <= 1
+    say("rope ulp mismatches", int((ulp(c, rc) > 0).sum() + (ulp(s, rs) > 0).sum()))
+    m.close()
+
+
+def test_tiny_decoder_parity(g):
+    """Tiny 2-layer decoder: 16-token prompt then 16 teacher-forced greedy steps, contiguous KV."""
+    wl = synth.WORKLOADS["tiny"]
+    shape = wl.shape
+    prompt = synth.token_ids(wl.ids_seed, wl.prompt)
+    say("tiny parity", shape.name)
+    ref, toks = oracle_greedy(shape, wl.weight_seed, prompt, wl.decode)
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=4, max_positions=64)
+    s = g.Session(m, 64)
+    got = gpu_teacher_forced(m, s, prompt, toks, shape.vocab)
+    gate = Gate("tiny")
+    for i, ((lg, am), r) in enumerate(zip(got, ref)):
+        gate.check(i, lg, r, am)
+        assert am == int(np.argmax(lg))                       # device argmax = host argmax of GPU logits
+    gate.assert_ok()
+    s.close()
+    m.close()
+
+
+def test_ragged_multi_round_prefill(g):
+    """A 100-token prompt in rounds of 48 (48 + 48 + 4): ragged tails in every kernel."""
+    shape = synth.TINY
+    prompt = synth.token_ids(77, 100)
+    ref, toks = oracle_greedy(shape, 1001, prompt, 3)
+    m = g.Model.from_shape(shape, seed=1001, kv_pool_blocks=8, max_positions=128, max_round_tokens=48)
+    assert m.info().round_tokens == 48
+    s = g.Session(m, 128)
+    got = gpu_teacher_forced(m, s, prompt, toks, shape.vocab)
+    gate = Gate("ragged rounds")
+    for i, ((lg, am), r) in enumerate(zip(got, ref)):
+        gate.check(i, lg, r, am)
+    gate.assert_ok()
+    # the same prompt in one round
+    m1 = g.Model.from_shape(shape, seed=1001, kv_pool_blocks=8, max_positions=128)
+    s1 = g.Session(m1, 128)
+    one = gpu_teacher_forced(m1, s1, prompt, toks, shape.vocab)
+    for (a, _), (b, _) in zip(got, one):
+        assert nmse(a, b) <= 1e-8
+    for o in (s, s1, m, m1):
+        o.close()
+
+
+def test_paged_shuffled_equals_identity_bitwise(g):
+    shape = synth.TINY
+    prompt = synth.token_ids(5, 70)
+    m = g.Model.from_shape(shape, seed=1001, kv_pool_blocks=16, max_positions=96)
+    a = g.Session(m, 96)                                                # blocks 0, 1, 2
+    free = [b for b in synth.shuffled_blocks(3001, 16).tolist() if b >= 3][:3]
+    b = g.Session(m, 96, block_ids=free)
+    toks = [11, 22, 33, 44, 55, 151935, 0]
+    ra = gpu_teacher_forced(m, a, prompt, toks, shape.vocab)
+    rb = gpu_teacher_forced(m, b, prompt, toks, shape.vocab)
+    for (x, xa), (y, ya) in zip(ra, rb):
+        assert np.array_equal(x, y) and xa == ya
+    for layer in range(shape.n_layers):
+        ka, va = a.read_kv(layer, 0, 77)
+        kb, vb = b.read_kv(layer, 0, 77)
+        assert np.array_equal(ka, kb) and np.array_equal(va, vb)
+    for o in (a, b, m):
+        o.close()
+
+
+def test_kv_cache_matches_oracle_storage(g):
+    """K/V written through the block table are the BF16-rounded post-norm, post-RoPE k and v."""
+    shape = synth.TINY
+    prompt = synth.token_ids(9, 40)
+    m = g.Model.from_shape(shape, seed=1001, kv_pool_blocks=8, max_positions=64)
+    blocks = [5, 2]
+    s = g.Session(m, 64, block_ids=blocks)
+    lg = torch.empty(shape.vocab, device="cuda")
+    s.prefill(prompt, lg)
+    om_ = oracle.OracleModel(shape, 1001)
+    kv = oracle.PagedKV.for_shape(shape, 8, blocks)
+    oracle.OracleSession(om_, kv).prefill(prompt)
+    for layer in range(shape.n_layers):
+        k, v = s.read_kv(layer, 0, 40)
+        kf = synth.bf16_bits_to_f32(k)
+        vf = synth.bf16_bits_to_f32(v)
+        K, V = kv.read(layer, 40)
+        # layer 0: the same BF16 value, or one BF16 step apart where the FP32 inputs straddle a
+        # rounding boundary (tiny elements may move further relative to themselves: FP32 rounding
+        # of the projection is relative to the head's scale). Deeper layers inherit the upstream
+        # differences, so only their overall agreement is bounded.
+        for got, want in ((kf, K), (vf, V)):
+            diff = np.abs(got - want)
+            if layer == 0:
+                scale = np.sqrt(np.mean(want.astype(np.float64) ** 2, axis=-1, keepdims=True))
+                step = np.abs(want) * 2.0 ** -7 + scale * 2.0 ** -14
+                assert np.all(diff <= step), (layer, float((diff - step).max()))
+            assert nmse(got, want) < 1e-5, layer
+            assert np.mean(diff == 0) > 0.9, layer
+    s.close()
+    m.close()
+
+
+def test_batched_equals_isolated_bitwise(g):
+    shape = synth.TINY
+    m = g.Model.from_shape(shape, seed=1001, kv_pool_blocks=64, max_positions=128)
+    lens = [20, 45, 70, 33]
+    prompts = [synth.token_ids(100 + i, n) for i, n in enumerate(lens)]
+    lg = torch.empty(shape.vocab, device="cuda")
+    A = [g.Session(m, 128) for _ in lens]
+    Bs = [g.Session(m, 128) for _ in lens]
+    for sa, sb, p in zip(A, Bs, prompts):
+        sa.prefill(p, lg)
+        sb.prefill(p, lg)
+    blg = torch.empty(len(lens), shape.vocab, device="cuda")
+    bam = torch.empty(len(lens), dtype=torch.int32, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    for step in range(6):
+        ids = [(1000 * step + 7 * i) % shape.vocab for i in range(len(lens))]
+        m.eval_batch(A, ids, blg, bam)
+        torch.cuda.synchronize()
+        batched = blg.cpu().numpy()
+        for i, sb in enumerate(Bs):
+            sb.decode(ids[i], lg, am)
+            torch.cuda.synchronize()
+            assert np.array_equal(lg.cpu().numpy(), batched[i]), (step, i)
+            assert int(am.item()) == int(bam[i].item())
+    for o in A + Bs + [m]:
+        o.close()
+
+
+def test_device_ids_and_errors(g):
+    shape = synth.reduced(synth.TINY, n_layers=1)
+    m = g.Model.from_shape(shape, seed=3, kv_pool_blocks=4, max_positions=40)
+    s = g.Session(m, 40)
+    lg = torch.empty(shape.vocab, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    s.prefill([1, 2, 3], lg, am)
+    with pytest.raises(g.GqaError) as e:
+        s.prefill([5, shape.vocab], lg, am)
+    assert e.value.code == g.GQA_E_RANGE and s.position == 3
+    with pytest.raises(g.GqaError):
+        s.decode(-1, lg, am)
+    assert s.position == 3
+    # device-resident id: the previous argmax feeds the next step without a host round trip
+    ref = torch.empty_like(lg)
+    s2 = g.Session(m, 40)
+    s2.prefill([1, 2, 3], lg, am)
+    tok = int(am.item())
+    s.decode(am, lg, am)                     # s reads its id from the device buffer
+    s2.decode(tok, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(lg, ref)
+    m.check_device_error()
+    bad = torch.tensor([shape.vocab + 5], dtype=torch.int32, device="cuda")
+    s.decode(bad, lg, am)
+    with pytest.raises(g.GqaError) as e:
+        m.check_device_error()
+    assert e.value.code == g.GQA_E_RANGE
+    m.check_device_error()                   # flag cleared
+    with pytest.raises(g.GqaError) as e:
+        s.prefill(list(range(40)), lg, am)
+    assert e.value.code == g.GQA_E_RANGE
+    for o in (s, s2, m):
+        o.close()
+
+
+def test_pool_exhaustion_and_block_validation(g):
+    shape = synth.reduced(synth.TINY, n_layers=1)
+    m = g.Model.from_shape(shape, seed=3, kv_pool_blocks=4, max_positions=128)
+    a = g.Session(m, 64)
+    with pytest.raises(g.GqaError) as e:
+        g.Session(m, 128)
+    assert e.value.code == g.GQA_E_OOM
+    with pytest.raises(g.GqaError):
+        g.Session(m, 64, block_ids=[0, 3])      # block 0 is owned by a
+    with pytest.raises(g.GqaError):
+        g.Session(m, 64, block_ids=[3, 3])
+    b = g.Session(m, 64, block_ids=[3, 2])
+    assert m.info().free_blocks == 0
+    a.close()
+    b.close()
+    assert m.info().free_blocks == 4
+    m.close()
+
+
+def test_q8_0_quantisation_bytes_match_oracle(g):
+    shape = synth.reduced(synth.TINY, n_layers=1)
+    m = g.Model.from_shape(shape, seed=1004, scheme="q8_0", kv_pool_blocks=2, max_positions=32)
+    from oracle.q8_0 import quantize_q8_0
+    for nm, dims in shape.layer_tensor_shapes().items():
+        if nm in synth.NORM_TENSORS:
+            continue
+        rows, cols = dims
+        w = synth.bf16_bits_to_f32(synth.tensor_bits(shape, 1004, nm, 0))
+        sc, q = quantize_q8_0(w)
+        for r0 in (0, rows - 7):
+            gq, gs = m.read_q8(nm, 0, r0, 7, cols)
+            assert np.array_equal(gq, q[r0:r0 + 7]), nm
+            assert np.array_equal(gs, sc[r0:r0 + 7].view(np.uint16)), nm
+    m.close()
+
+
+def test_tiny_q8_0_parity(g):
+    shape = synth.TINY
+    prompt = synth.token_ids(2004, 40)
+    ref, toks = oracle_greedy(shape, 1004, prompt, 8, scheme="q8_0")
+    m = g.Model.from_shape(shape, seed=1004, scheme="q8_0", kv_pool_blocks=4, max_positions=64)
+    s = g.Session(m, 64)
+    got = gpu_teacher_forced(m, s, prompt, toks, shape.vocab)
+    gate = Gate("tiny q8_0")
+    for i, ((lg, am), r) in enumerate(zip(got, ref)):
+        gate.check(i, lg, r, am)
+    gate.assert_ok()
+    s.close()
+    m.close()
+
+
+def test_qwen3_0_6b_shape_parity(g):
+    """0.6B shape: 28 layers, 348-token prompt, 64 teacher-forced greedy steps, paged KV with a
+    shuffled block table drawn from a pool four times the session's size."""
+    wl = synth.WORKLOADS["0.6b"]
+    shape = wl.shape
+    prompt = synth.token_ids(wl.ids_seed, wl.prompt)
+    say("0.6b oracle")
+    ref, toks = oracle_greedy(shape, wl.weight_seed, prompt, wl.decode)
+    nb = synth.blocks_for(wl.prompt + wl.decode)
+    table = synth.shuffled_blocks(wl.shuffle_seed, 4 * nb)[:nb]
+    say("0.6b gpu")
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=4 * nb, max_positions=nb * 32)
+    s = g.Session(m, nb * 32, block_ids=table)
+    got = gpu_teacher_forced(m, s, prompt, toks, shape.vocab)
+    gate = Gate("0.6b")
+    for i, ((lg, am), r) in enumerate(zip(got, ref)):
+        gate.check(i, lg, r, am)
+    gate.assert_ok()
+    s.close()
+    m.close()
