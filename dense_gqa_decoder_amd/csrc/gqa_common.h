@@ -27,6 +27,46 @@ struct Rows {
   const int32_t* table[kMaxBatch];
 };
 
+// Source of the FP16 hi/lo operand rows of a decode matvec (see k_gemv.hip).
+enum XMode : int { X_RAW = 0, X_RESID = 1, X_SWIGLU = 2 };
+struct XSrc {
+  int mode;
+  // X_RAW: hi/lo rows in global memory, row stride ld
+  const f16* hi;
+  const f16* lo;
+  int ld;
+  // X_RESID: x = res[b] + pscale * sum_{s < nsplit} part[s][b] (fixed split order);
+  // operand = x * w (the RMSNorm weight; the 1/rms factor is applied by the consumer of the
+  // projection). x is written to res_out and the sum of squares of x over each K range to
+  // ss_out[range][b] by the workgroups of the first row tile.
+  const float* res;
+  float* res_out;
+  const float* part;
+  int nsplit;
+  int64_t pstride;
+  int pld;
+  float pscale;
+  const uint16_t* w;
+  float* ss_out;
+  // X_SWIGLU: c = 1 / sqrt(sum_r ss[r][b] / H + eps); g = c * sum_s gu[s][b][32*(f/16) + f%16],
+  // u = c * sum_s gu[s][b][32*(f/16) + 16 + f%16]; operand = silu(g) * u.
+  const float* gu;
+  int gu_split;
+  int64_t gu_stride;
+  int gu_ld;
+  const float* ss;
+  int ss_n;
+  int H;
+  float eps;
+};
+
+// Sum-of-squares partials: ss[range][row], kMaxBatch rows per range.
+__device__ __forceinline__ float inv_rms_from_ss(const float* ss, int n, int row, int H, float eps) {
+  float t = 0.f;
+  for (int r = 0; r < n; ++r) t += ss[r * 32 + row];
+  return 1.0f / sqrtf(t / (float)H + eps);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // Round to nearest even; the values handled here are finite.

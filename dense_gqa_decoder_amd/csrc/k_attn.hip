@@ -14,14 +14,13 @@
 // from the S^T accumulator layout: within each 32-key chunk a lane holds keys 4g..4g+3 and
 // 16+4g..16+4g+3 (g = lane / 16), and V^T is read from LDS in the same key order.
 //
-// Decode: one wave per (row, KV head, 64-position chunk), FP32 on the vector ALUs; the
-// per-chunk (max, sum, o) partials are merged by attn_combine_kernel. The chunking depends only
-// on the row's own context length, never on the batch.
+// Decode: one wave per (row, KV head, 32-position block), FP32 on the vector ALUs, four blocks
+// per workgroup; see attn_decode_kernel.
 #include "gqa_common.h"
 
 namespace gqa {
 
-constexpr int kDecodeChunk = 64;
+constexpr int kDecodeChunk = 32;   // positions per decode wave (one KV block)
 constexpr int kPartStride = 132;   // floats per decode partial: m, l, pad, pad, o[128]
 
 template <int G, bool PSPLIT>
@@ -221,128 +220,299 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const float* __restri
   }
 }
 
-// Decode: grid (chunk, kv head, row); one wave. Lane: key slot ks = lane >> 4 (4 keys per step),
-// dims 8*(lane & 15) .. +7. Two passes over the chunk's 64 keys (scores, then values).
-template <int G>
-__global__ __launch_bounds__(64) void attn_decode_kernel(const float* __restrict__ q, int nq, Rows rows,
-                                                         const uint16_t* __restrict__ kpool,
-                                                         const uint16_t* __restrict__ vpool,
-                                                         float* __restrict__ part, int max_chunks) {
-  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int ctx = rows.pos[b] + 1;
-  if (c * kDecodeChunk >= ctx) return;
-  const int32_t* table = rows.table[b];
-  const int lane = threadIdx.x, ks = lane >> 4, dg = lane & 15;
-  const float qscale = kLog2e * 0.08838834764831845f;
+// Decode attention, one kernel per layer: grid (128-position chunk, KV head, row), four waves
+// per workgroup, one 32-position block per wave (the block table is read once per wave).
+//  1. q for the g query heads of the KV head: the fixed-order sum of the q|k|v projection's
+//     split partials, per-head RMSNorm, rotate-half RoPE at the row's position.
+//  2. The wave whose block holds the new position also builds its k (norm + RoPE) and v, rounds
+//     them to BF16, writes them through the block table, and uses those register values for
+//     that position.
+//  3. Scores, softmax and the value sum over the wave's keys in FP32; the four waves merge
+//     through LDS in wave order into one (max, sum, o) partial per chunk.
+//  4. The last workgroup of a (row, KV head) to finish (device-scope release/acquire fences
+//     around an atomic counter, which it resets) merges the chunk partials in chunk order and
+//     writes o / l as FP16 hi/lo operands of the o projection.
+// The q|k|v projection was taken of x * w_norm; its partials are scaled here by the row's 1/rms,
+// recomputed from the sum-of-squares partials the projection's prologue wrote.
+// The chunking depends only on the row's own context length, never on the batch.
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeChunkPos = kDecodeChunk * kDecodeWaves;   // positions per workgroup
+constexpr int kMergeMaxChunks = 128;                            // 16,384 positions
 
+template <int G>
+__global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
+    const float* __restrict__ qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* __restrict__ ss,
+    int ss_n, int H, const uint16_t* __restrict__ wqn, const uint16_t* __restrict__ wkn, float eps,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, Rows rows, uint16_t* __restrict__ kpool,
+    uint16_t* __restrict__ vpool, float* __restrict__ part, int max_chunks, int* __restrict__ counters,
+    float out_scale, f16* __restrict__ ohi, f16* __restrict__ olo, int ldo) {
+  __shared__ float sm[kDecodeWaves][G], sl[kDecodeWaves][G];
+  __shared__ float so[kDecodeWaves][G][kHeadDim];
+  __shared__ float sw[G][kMergeMaxChunks];
+  __shared__ float sL[G][kMergeMaxChunks];
+  __shared__ int s_last;
+  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int pos = rows.pos[b], ctx = pos + 1;
+  const int nchunk = (ctx + kDecodeChunkPos - 1) / kDecodeChunkPos;
+  if (c >= nchunk) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ks = lane >> 4, dg = lane & 15;
+  const int blk = c * kDecodeWaves + wave;                 // logical 32-position block of this wave
+  const int kpos0 = blk * kDecodeChunk;
+  const bool active = kpos0 < ctx;
+  const float qscale = kLog2e * 0.08838834764831845f;
+  const float* qrow = qkvp + (int64_t)b * QKV;
+  // 1/rms of the normalised layer input: the projection was taken of x * w only
+  const float cin = inv_rms_from_ss(ss, ss_n, b, H, eps);
+
+  // sum of the projection's split partials for 8 consecutive dims of one head row, times cin
+  auto head8 = [&](int hrow, float (&o)[8]) {
+    float t[8][8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s < nsplit) {
+        const float* p = qrow + (int64_t)s * pstride + hrow * kHeadDim + dg * 8;
+        float4 a0 = *(const float4*)p, a1 = *(const float4*)(p + 4);
+        t[s][0] = a0.x; t[s][1] = a0.y; t[s][2] = a0.z; t[s][3] = a0.w;
+        t[s][4] = a1.x; t[s][5] = a1.y; t[s][6] = a1.z; t[s][7] = a1.w;
+      }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float acc = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        if (s < nsplit) acc += t[s][e];
+      o[e] = __fmul_rn(acc, cin);
+    }
+  };
+  // per-head RMSNorm over the 16 lanes of a key slot group, then RoPE: dims i < 64 pair with
+  // i + 64, which live in lane dg ^ 8 at the same e.
+  const float* cr = rcos + (int64_t)pos * 64;
+  const float* sr = rsin + (int64_t)pos * 64;
+  auto norm_rope = [&](float (&x)[8], const uint16_t* w) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    ss += __shfl_xor(ss, 4, 64);
+    ss += __shfl_xor(ss, 8, 64);
+    const float inv = 1.0f / sqrtf(ss / (float)kHeadDim + eps);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * bf16_bits_to_f32(w[dg * 8 + e]);
+    const int i0 = (dg & 7) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float partner = __shfl_xor(y[e], 8, 64);
+      float cs = cr[i0 + e], sn = sr[i0 + e];
+      x[e] = dg < 8 ? y[e] * cs - partner * sn : y[e] * cs + partner * sn;
+    }
+  };
+
+  // K/V loads of this wave's block first: they depend only on the block table
+  constexpr int STEPS = kDecodeChunk / 4;
+  uint4 kr[STEPS], vr[STEPS];
+  if (active) {
+    const int phys = rows.table[b][blk];
+    const uint16_t* kbp = kpool + (((int64_t)phys * kKvHeads + kvh) * kBlock) * kHeadDim + dg * 8;
+    const uint16_t* vbp = vpool + (((int64_t)phys * kKvHeads + kvh) * kBlock) * kHeadDim + dg * 8;
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const int j = kpos0 + st * 4 + ks;
+      kr[st] = j < pos ? *(const uint4*)(kbp + (st * 4 + ks) * kHeadDim) : uint4{0, 0, 0, 0};
+      vr[st] = j < pos ? *(const uint4*)(vbp + (st * 4 + ks) * kHeadDim) : uint4{0, 0, 0, 0};
+    }
+  }
   float qv[G][8];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    const float* qr = q + ((int64_t)b * nq + kvh * G + hh) * kHeadDim + dg * 8;
+    head8(kvh * G + hh, qv[hh]);
+    norm_rope(qv[hh], wqn);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[hh][e] = qr[e] * qscale;
+    for (int e = 0; e < 8; ++e) qv[hh][e] *= qscale;
   }
-  constexpr int STEPS = kDecodeChunk / 4;
-  float sc[G][STEPS];
-#pragma unroll
-  for (int st = 0; st < STEPS; ++st) {
-    int j = c * kDecodeChunk + st * 4 + ks;
-    bool valid = j < ctx;
-    uint4 kr = uint4{0, 0, 0, 0};
-    if (valid) {
-      int phys = table[j >> 5];
-      kr = *(const uint4*)(kpool + (((int64_t)phys * kKvHeads + kvh) * kBlock + (j & 31)) * kHeadDim + dg * 8);
-    }
-    float kf[8] = {bf16_bits_to_f32(kr.x & 0xFFFF), bf16_bits_to_f32(kr.x >> 16), bf16_bits_to_f32(kr.y & 0xFFFF),
-                   bf16_bits_to_f32(kr.y >> 16),    bf16_bits_to_f32(kr.z & 0xFFFF), bf16_bits_to_f32(kr.z >> 16),
-                   bf16_bits_to_f32(kr.w & 0xFFFF), bf16_bits_to_f32(kr.w >> 16)};
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) d = fmaf(qv[hh][e], kf[e], d);
-      d += __shfl_xor(d, 1, 64);
-      d += __shfl_xor(d, 2, 64);
-      d += __shfl_xor(d, 4, 64);
-      d += __shfl_xor(d, 8, 64);
-      sc[hh][st] = valid ? d : -INFINITY;
-    }
-  }
-  float m[G], l[G], o[G][8];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) mx = fmaxf(mx, sc[hh][st]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    m[hh] = mx;
-    float sum = 0.f;
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      float p = exp2f(sc[hh][st] - mx);
-      sc[hh][st] = p;
-      sum += p;
-    }
-    sum += __shfl_xor(sum, 16, 64);
-    sum += __shfl_xor(sum, 32, 64);
-    l[hh] = sum;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
-  }
-#pragma unroll
-  for (int st = 0; st < STEPS; ++st) {
-    int j = c * kDecodeChunk + st * 4 + ks;
-    if (j < ctx) {
-      int phys = table[j >> 5];
-      uint4 vr = *(const uint4*)(vpool + (((int64_t)phys * kKvHeads + kvh) * kBlock + (j & 31)) * kHeadDim + dg * 8);
-      float vf[8] = {bf16_bits_to_f32(vr.x & 0xFFFF), bf16_bits_to_f32(vr.x >> 16), bf16_bits_to_f32(vr.y & 0xFFFF),
-                     bf16_bits_to_f32(vr.y >> 16),    bf16_bits_to_f32(vr.z & 0xFFFF), bf16_bits_to_f32(vr.z >> 16),
-                     bf16_bits_to_f32(vr.w & 0xFFFF), bf16_bits_to_f32(vr.w >> 16)};
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(sc[hh][st], vf[e], o[hh][e]);
-    }
-  }
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
+  // the new position's K/V (only in the wave whose block holds it)
+  const bool owner = active && pos >= kpos0 && pos < kpos0 + kDecodeChunk;
+  uint4 knew = uint4{0, 0, 0, 0}, vnew = uint4{0, 0, 0, 0};
+  if (owner) {
+    float kx[8], vx[8];
+    head8(nq + kvh, kx);
+    norm_rope(kx, wkn);
+    head8(nq + kKvHeads + kvh, vx);
+    uint32_t kb16[8], vb16[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      o[hh][e] += __shfl_xor(o[hh][e], 16, 64);
-      o[hh][e] += __shfl_xor(o[hh][e], 32, 64);
+      kb16[e] = f32_to_bf16_rne(kx[e]);
+      vb16[e] = f32_to_bf16_rne(vx[e]);
     }
+    knew = uint4{kb16[0] | (kb16[1] << 16), kb16[2] | (kb16[3] << 16), kb16[4] | (kb16[5] << 16),
+                 kb16[6] | (kb16[7] << 16)};
+    vnew = uint4{vb16[0] | (vb16[1] << 16), vb16[2] | (vb16[3] << 16), vb16[4] | (vb16[5] << 16),
+                 vb16[6] | (vb16[7] << 16)};
     if (ks == 0) {
-      float* pp = part + (((int64_t)b * nq + kvh * G + hh) * max_chunks + c) * kPartStride;
-      if (dg == 0) {
-        pp[0] = m[hh];
-        pp[1] = l[hh];
-      }
-      *(float4*)(pp + 4 + dg * 8) = make_float4(o[hh][0], o[hh][1], o[hh][2], o[hh][3]);
-      *(float4*)(pp + 8 + dg * 8) = make_float4(o[hh][4], o[hh][5], o[hh][6], o[hh][7]);
+      const int phys = rows.table[b][pos >> 5];
+      const int64_t off = (((int64_t)phys * kKvHeads + kvh) * kBlock + (pos & 31)) * kHeadDim + dg * 8;
+      *(uint4*)(kpool + off) = knew;
+      *(uint4*)(vpool + off) = vnew;
     }
   }
-}
 
-// Merge the chunk partials of one (row, head): O = sum_c o_c 2^(m_c - M) / sum_c l_c 2^(m_c - M).
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int nq, Rows rows,
-                                                           int max_chunks, float out_scale, f16* __restrict__ ohi,
-                                                           f16* __restrict__ olo, int ldo) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int n = (rows.pos[b] + 1 + kDecodeChunk - 1) / kDecodeChunk;
-  const float* pp = part + ((int64_t)b * nq + h) * max_chunks * kPartStride;
-  float M = -INFINITY;
-  for (int c = 0; c < n; ++c) M = fmaxf(M, pp[c * kPartStride]);
-  float L = 0.f, O = 0.f;
-  for (int c = 0; c < n; ++c) {
-    float w = exp2f(pp[c * kPartStride] - M);
-    L = fmaf(pp[c * kPartStride + 1], w, L);
-    O = fmaf(pp[c * kPartStride + 4 + d], w, O);
+  float m[G], l[G], o[G][8];
+  if (active) {
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      if (kpos0 + st * 4 + ks == pos) {
+        kr[st] = knew;
+        vr[st] = vnew;
+      }
+    }
+    float sc[G][STEPS];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const bool valid = kpos0 + st * 4 + ks < ctx;
+      uint4 k4 = kr[st];
+      float kf[8] = {bf16_bits_to_f32(k4.x & 0xFFFF), bf16_bits_to_f32(k4.x >> 16), bf16_bits_to_f32(k4.y & 0xFFFF),
+                     bf16_bits_to_f32(k4.y >> 16),    bf16_bits_to_f32(k4.z & 0xFFFF), bf16_bits_to_f32(k4.z >> 16),
+                     bf16_bits_to_f32(k4.w & 0xFFFF), bf16_bits_to_f32(k4.w >> 16)};
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(qv[hh][e], kf[e], d);
+        d += __shfl_xor(d, 1, 64);
+        d += __shfl_xor(d, 2, 64);
+        d += __shfl_xor(d, 4, 64);
+        d += __shfl_xor(d, 8, 64);
+        sc[hh][st] = valid ? d : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) mx = fmaxf(mx, sc[hh][st]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        float p = exp2f(sc[hh][st] - mx);
+        sum += p;
+        uint4 v4 = vr[st];
+        float vf[8] = {bf16_bits_to_f32(v4.x & 0xFFFF), bf16_bits_to_f32(v4.x >> 16), bf16_bits_to_f32(v4.y & 0xFFFF),
+                       bf16_bits_to_f32(v4.y >> 16),    bf16_bits_to_f32(v4.z & 0xFFFF), bf16_bits_to_f32(v4.z >> 16),
+                       bf16_bits_to_f32(v4.w & 0xFFFF), bf16_bits_to_f32(v4.w >> 16)};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(p, vf[e], o[hh][e]);
+      }
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[hh][e] += __shfl_xor(o[hh][e], 16, 64);
+        o[hh][e] += __shfl_xor(o[hh][e], 32, 64);
+      }
+      m[hh] = mx;
+      l[hh] = sum;
+    }
+  } else {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      m[hh] = -INFINITY;
+      l[hh] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+    }
   }
-  f16 hi, lo;
-  split_f16(O / L * out_scale, hi, lo);
-  ohi[(int64_t)b * ldo + h * kHeadDim + d] = hi;
-  olo[(int64_t)b * ldo + h * kHeadDim + d] = lo;
+  // merge the four waves (wave order) into the chunk partial
+  if (ks == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      if (dg == 0) {
+        sm[wave][hh] = m[hh];
+        sl[wave][hh] = l[hh];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) so[wave][hh][dg * 8 + e] = o[hh][e];
+    }
+  }
+  __syncthreads();
+  {
+    // thread -> (head, dim pair): G * 128 outputs over 256 threads
+    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 64 * kDecodeWaves) {
+      const int hh = idx / kHeadDim, d = idx % kHeadDim;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm[w][hh]);
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        const float wt = exp2f(sm[w][hh] - M);
+        L = fmaf(sl[w][hh], wt, L);
+        O = fmaf(so[w][hh][d], wt, O);
+      }
+      float* pp = part + (((int64_t)b * nq + kvh * G + hh) * max_chunks + c) * kPartStride;
+      if (d == 0) {
+        pp[0] = M;
+        pp[1] = L;
+      }
+      pp[4 + d] = O;
+    }
+  }
+  // last workgroup of this (row, KV head) merges the chunk partials
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const int old = __hip_atomic_fetch_add(&counters[b * kKvHeads + kvh], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == nchunk - 1;
+    if (s_last) __threadfence();
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // chunk maxima and sums into LDS (one thread per (head, chunk)), then per-head weights
+  for (int i = threadIdx.x; i < G * nchunk; i += 64 * kDecodeWaves) {
+    const int hh = i / nchunk, cc = i - hh * nchunk;
+    const float* q = part + (((int64_t)b * nq + kvh * G + hh) * max_chunks + cc) * kPartStride;
+    const float2 ml = *(const float2*)q;
+    sw[hh][cc] = ml.x;
+    sL[hh][cc] = ml.y;
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int hh = threadIdx.x;
+    float M = -INFINITY;
+    for (int cc = 0; cc < nchunk; ++cc) M = fmaxf(M, sw[hh][cc]);
+    float L = 0.f;
+    for (int cc = 0; cc < nchunk; ++cc) {
+      const float wt = exp2f(sw[hh][cc] - M);
+      sw[hh][cc] = wt;
+      L = fmaf(sL[hh][cc], wt, L);
+    }
+    sL[hh][0] = L;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 64 * kDecodeWaves) {
+    const int hh = idx / kHeadDim, d = idx % kHeadDim;
+    const float* pp = part + ((int64_t)b * nq + kvh * G + hh) * max_chunks * kPartStride + 4 + d;
+    float O = 0.f;
+    int cc = 0;
+    for (; cc + 8 <= nchunk; cc += 8) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = pp[(int64_t)(cc + u) * kPartStride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) O = fmaf(t[u], sw[hh][cc + u], O);
+    }
+    for (; cc < nchunk; ++cc) O = fmaf(pp[(int64_t)cc * kPartStride], sw[hh][cc], O);
+    f16 hi, lo;
+    split_f16(O / sL[hh][0] * out_scale, hi, lo);
+    ohi[(int64_t)b * ldo + (kvh * G + hh) * kHeadDim + d] = hi;
+    olo[(int64_t)b * ldo + (kvh * G + hh) * kHeadDim + d] = lo;
+  }
+  if (threadIdx.x == 0) counters[b * kKvHeads + kvh] = 0;
 }
 
 hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const int32_t* table, const uint16_t* kpool,
@@ -362,23 +532,26 @@ hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const in
   return hipGetLastError();
 }
 
-hipError_t launch_attn_decode(const float* q, int nq, const Rows& rows, int B, int max_ctx, const uint16_t* kpool,
-                              const uint16_t* vpool, float* part, int max_chunks, float out_scale, f16* ohi,
+hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* ss,
+                              int ss_n, int H, const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
+                              const float* rsin, const Rows& rows, int B, int max_ctx, uint16_t* kpool,
+                              uint16_t* vpool, float* part, int max_chunks, int* counters, float out_scale, f16* ohi,
                               f16* olo, int ldo, hipStream_t st) {
-  int chunks = (max_ctx + kDecodeChunk - 1) / kDecodeChunk;
-  if (chunks > max_chunks) return hipErrorInvalidValue;
+  const int chunks = (max_ctx + kDecodeChunkPos - 1) / kDecodeChunkPos;
+  if (chunks > max_chunks || chunks > kMergeMaxChunks || nsplit < 1 || nsplit > 8) return hipErrorInvalidValue;
   dim3 grid(chunks, kKvHeads, B);
-  int G = nq / kKvHeads;
+  const int G = nq / kKvHeads;
+#define DEC_LAUNCH(GG)                                                                                           \
+  hipLaunchKernelGGL(attn_decode_kernel<GG>, grid, dim3(64 * kDecodeWaves), 0, st, qkvp, nsplit, pstride, QKV, nq, \
+                     ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, kpool, vpool, part, max_chunks, counters,       \
+                     out_scale, ohi, olo, ldo)
   if (G == 4)
-    hipLaunchKernelGGL(attn_decode_kernel<4>, grid, dim3(64), 0, st, q, nq, rows, kpool, vpool, part, max_chunks);
+    DEC_LAUNCH(4);
   else if (G == 2)
-    hipLaunchKernelGGL(attn_decode_kernel<2>, grid, dim3(64), 0, st, q, nq, rows, kpool, vpool, part, max_chunks);
+    DEC_LAUNCH(2);
   else
     return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(nq, B), dim3(128), 0, st, part, nq, rows, max_chunks, out_scale, ohi,
-                     olo, ldo);
+#undef DEC_LAUNCH
   return hipGetLastError();
 }
 

@@ -35,61 +35,61 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
   return s;
 }
 
-// One 256-thread block per row. If nsplit > 0: x[r] += part_scale * sum_{s < nsplit} part[s][r][:]
-// (fixed order), written back. Then y = x / sqrt(mean(x^2) + eps) * w * out_scale, stored as FP16
-// hi/lo pairs (yhi, ylo) for the next projection. H <= 4096 and H % 256 == 0.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, int ldx, const float* __restrict__ part,
-                                                      int nsplit, int part_stride_split, int part_ld, float part_scale,
-                                                      const uint16_t* __restrict__ w, int H, float eps,
-                                                      float out_scale, f16* __restrict__ yhi,
-                                                      f16* __restrict__ ylo, int ldy) {
-  __shared__ float red[4];
-  int r = blockIdx.x;
+// One block of H/4 threads per row (one float4 each; H % 256 == 0, H <= 4096). If NS > 0:
+// x[r] += part_scale * sum_{s < NS} part[s][r][:] (fixed order), written back. Then
+// y = x / sqrt(mean(x^2) + eps) * w * out_scale, stored as FP16 hi/lo pairs (yhi, ylo) for the
+// next projection. Every load of a thread is issued before any is used.
+template <int NS>
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(float* __restrict__ x, int ldx, const float* __restrict__ part,
+                                                       int part_stride_split, int part_ld, float part_scale,
+                                                       const uint16_t* __restrict__ w, int H, float eps,
+                                                       float out_scale, f16* __restrict__ yhi,
+                                                       f16* __restrict__ ylo, int ldy) {
+  __shared__ float red[16];
+  const int r = blockIdx.x, t = threadIdx.x, i = 4 * t;
   float* xr = x + (int64_t)r * ldx;
-  constexpr int kMaxPer = 16;
-  float v[kMaxPer];
-  int per = H / 256;
-  float ss = 0.f;
+  float4 v = *(const float4*)(xr + i);
+  float4 pv[NS > 0 ? NS : 1];
 #pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) {
-    if (j < per) {
-      int i = threadIdx.x + 256 * j;
-      float a = xr[i];
-      if (nsplit > 0) {
-        float acc = 0.f;
-        for (int s = 0; s < nsplit; ++s) acc += part[(int64_t)s * part_stride_split + (int64_t)r * part_ld + i];
-        a += acc * part_scale;
-        xr[i] = a;
-      }
-      v[j] = a;
-      ss += a * a;
-    }
-  }
-  float tot = block_sum_256(ss, red);
-  float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  for (int s = 0; s < NS; ++s) pv[s] = *(const float4*)(part + (int64_t)s * part_stride_split + (int64_t)r * part_ld + i);
+  const uint2 wb = *(const uint2*)(w + i);
+  if (NS > 0) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) {
-    if (j < per) {
-      int i = threadIdx.x + 256 * j;
-      float y = v[j] * inv * bf16_bits_to_f32(w[i]) * out_scale;
-      f16 hi, lo;
-      split_f16(y, hi, lo);
-      yhi[(int64_t)r * ldy + i] = hi;
-      ylo[(int64_t)r * ldy + i] = lo;
+    for (int s = 0; s < NS; ++s) {
+      acc.x += pv[s].x;
+      acc.y += pv[s].y;
+      acc.z += pv[s].z;
+      acc.w += pv[s].w;
     }
+    v.x += acc.x * part_scale;
+    v.y += acc.y * part_scale;
+    v.z += acc.z * part_scale;
+    v.w += acc.w * part_scale;
+    *(float4*)(xr + i) = v;
   }
-}
-
-// Residual reduction only (no norm): x[r] += sum_s part[s][r][:]. Used before the final norm
-// when only the last row continues.
-__global__ void residual_reduce_kernel(float* __restrict__ x, int ldx, const float* __restrict__ part, int nsplit,
-                                       int part_stride_split, int part_ld, float part_scale, int H) {
-  int r = blockIdx.x;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) acc += part[(int64_t)s * part_stride_split + (int64_t)r * part_ld + i];
-    x[(int64_t)r * ldx + i] += acc * part_scale;
+  float ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  ss = wave_sum(ss);
+  const int nw = blockDim.x >> 6;
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int k = 0; k < nw; ++k) tot += red[k];
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  const float y[4] = {v.x * inv * bf16_bits_to_f32(wb.x & 0xFFFF) * out_scale,
+                      v.y * inv * bf16_bits_to_f32(wb.x >> 16) * out_scale,
+                      v.z * inv * bf16_bits_to_f32(wb.y & 0xFFFF) * out_scale,
+                      v.w * inv * bf16_bits_to_f32(wb.y >> 16) * out_scale};
+  f16x4 hv, lv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f16 h, l;
+    split_f16(y[e], h, l);
+    hv[e] = h;
+    lv[e] = l;
   }
+  *(f16x4*)(yhi + (int64_t)r * ldy + i) = hv;
+  *(f16x4*)(ylo + (int64_t)r * ldy + i) = lv;
 }
 
 // Per (row, head) wave: head h < nq is a query head, then 8 key heads, then 8 value heads of
@@ -127,11 +127,18 @@ __global__ __launch_bounds__(256) void qk_rope_kv_kernel(const float* __restrict
     a = qkv[base + l];
     b = qkv[base + l + 64];
   } else {
+    float pa[8], pb[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      pa[s] = s < nsplit ? qkv[(int64_t)s * part_stride + base + l] : 0.f;
+      pb[s] = s < nsplit ? qkv[(int64_t)s * part_stride + base + l + 64] : 0.f;
+    }
     a = 0.f;
     b = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      a += qkv[(int64_t)s * part_stride + base + l];
-      b += qkv[(int64_t)s * part_stride + base + l + 64];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      a += pa[s];
+      b += pb[s];
     }
   }
   bool isq = h < nq, isk = h >= nq && h < nq + kKvHeads;
@@ -160,36 +167,52 @@ __global__ __launch_bounds__(256) void qk_rope_kv_kernel(const float* __restrict
   }
 }
 
-// argmax over each row of logits [B][V]; ties go to the lowest index.
-__global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ logits, int64_t ld, int V,
+// argmax of each token row from the lm_head matvec's per-tile candidates cand[b][t] =
+// (max value, index bits); ties go to the lowest index.
+__global__ __launch_bounds__(1024) void argmax_kernel(const float2* __restrict__ cand, int ntiles,
                                                       int32_t* __restrict__ out) {
-  __shared__ float sv[1024];
-  __shared__ int si[1024];
-  const float* r = logits + (int64_t)blockIdx.x * ld;
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const float2* c = cand + (int64_t)blockIdx.x * ntiles;
   float best = -INFINITY;
   int bi = 0x7FFFFFFF;
-  for (int i = threadIdx.x; i < V; i += 1024) {
-    float v = r[i];
-    if (v > best) {
-      best = v;
-      bi = i;
-    }
-  }
-  sv[threadIdx.x] = best;
-  si[threadIdx.x] = bi;
-  __syncthreads();
-  for (int s = 512; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) {
-      float ov = sv[threadIdx.x + s];
-      int oi = si[threadIdx.x + s];
-      if (ov > sv[threadIdx.x] || (ov == sv[threadIdx.x] && oi < si[threadIdx.x])) {
-        sv[threadIdx.x] = ov;
-        si[threadIdx.x] = oi;
+  for (int i = threadIdx.x; i < ntiles; i += 1024 * 4) {
+    float2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = i + 1024 * u < ntiles ? c[i + 1024 * u] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int idx = __float_as_int(v[u].y);
+      if (v[u].x > best || (v[u].x == best && idx < bi)) {
+        best = v[u].x;
+        bi = idx;
       }
     }
-    __syncthreads();
   }
-  if (threadIdx.x == 0) out[blockIdx.x] = si[0] == 0x7FFFFFFF ? -1 : si[0];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(best, o, 64);
+    int oi = __shfl_xor(bi, o, 64);
+    if (ov > best || (ov == best && oi < bi)) {
+      best = ov;
+      bi = oi;
+    }
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sv[threadIdx.x >> 6] = best;
+    si[threadIdx.x >> 6] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    best = sv[0];
+    bi = si[0];
+    for (int k = 1; k < 16; ++k)
+      if (sv[k] > best || (sv[k] == best && si[k] < bi)) {
+        best = sv[k];
+        bi = si[k];
+      }
+    out[blockIdx.x] = bi == 0x7FFFFFFF ? -1 : bi;
+  }
 }
 
 hipError_t launch_embed(const uint16_t* E, const int32_t* ids, int T, int H, int vocab, float* x, int32_t* err,
@@ -202,15 +225,16 @@ hipError_t launch_rmsnorm(float* x, int ldx, const float* part, int nsplit, int 
                           float part_scale, const uint16_t* w, int H, float eps, float out_scale, f16* yhi, f16* ylo,
                           int ldy, int rows, hipStream_t st) {
   if (H % 256 != 0 || H > 4096) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, st, x, ldx, part, nsplit, part_stride_split, part_ld,
-                     part_scale, w, H, eps, out_scale, yhi, ylo, ldy);
-  return hipGetLastError();
-}
-
-hipError_t launch_residual_reduce(float* x, int ldx, const float* part, int nsplit, int part_stride_split,
-                                  int part_ld, float part_scale, int H, int rows, hipStream_t st) {
-  hipLaunchKernelGGL(residual_reduce_kernel, dim3(rows), dim3(256), 0, st, x, ldx, part, nsplit, part_stride_split,
-                     part_ld, part_scale, H);
+#define RMS_CASE(NS)                                                                                              \
+  case NS:                                                                                                        \
+    hipLaunchKernelGGL(rmsnorm_kernel<NS>, dim3(rows), dim3(H / 4), 0, st, x, ldx, part, part_stride_split, part_ld, \
+                       part_scale, w, H, eps, out_scale, yhi, ylo, ldy);                                         \
+    break;
+  switch (nsplit) {
+    RMS_CASE(0) RMS_CASE(1) RMS_CASE(2) RMS_CASE(3) RMS_CASE(4) RMS_CASE(5) RMS_CASE(6) RMS_CASE(7) RMS_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef RMS_CASE
   return hipGetLastError();
 }
 
@@ -230,8 +254,8 @@ hipError_t launch_qk_rope_kv(bool decode, const float* qkv, int nsplit, int part
   return hipGetLastError();
 }
 
-hipError_t launch_argmax(const float* logits, int64_t ld, int V, int B, int32_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(1024), 0, st, logits, ld, V, out);
+hipError_t launch_argmax(const float2* cand, int ntiles, int B, int32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(1024), 0, st, cand, ntiles, out);
   return hipGetLastError();
 }
 

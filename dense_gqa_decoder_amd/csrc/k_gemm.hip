@@ -67,8 +67,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t* __restrict__ 
         rw[i] = *(const uint4*)(W + (int64_t)(n0 + row) * K + k0 + col);
     }
     if (Q8 && tid < BN) {                          // scales of the two quant blocks of this K-step
-      rd0 = Wd[(int64_t)(n0 + tid) * (K / 32) + k0 / 32];
-      rd1 = Wd[(int64_t)(n0 + tid) * (K / 32) + k0 / 32 + 1];
+      rd0 = Wd[(int64_t)(k0 / 32) * N + n0 + tid];           // block-major scales [K/32][N]
+      rd1 = Wd[(int64_t)(k0 / 32 + 1) * N + n0 + tid];
     }
 #pragma unroll
     for (int i = 0; i < CX; ++i) {

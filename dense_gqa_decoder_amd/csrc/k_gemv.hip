@@ -1,41 +1,172 @@
 // Decode projections for 1..32 token rows: P[s][b][n] = sum_{k in split s} W[n][k] * x[b][k].
 //
-// HBM-streaming matvec: each one-wave workgroup owns 16 weight rows (32 for the fused
-// gate/up SwiGLU epilogue) and one K-split, streams its weight bytes once with 16-byte loads
-// (eight K-steps of 32 in flight per lane), and multiplies them on the matrix cores against
-// the token rows as the 16-wide N side (v_mfma_f32_16x16x32_f16, FP16 hi/lo activations, FP32
-// accumulate). The token count B only widens the padded N side: every output column runs the
-// same instruction sequence in the same K order whatever B is, so a row evaluated in a batch
-// is bit-identical to the same row evaluated alone (Kipp Roadmap, status v0.0.2:
-// batched-equals-isolated).
+// HBM-streaming matvec: each wave owns a 16-row weight tile and streams it over the
+// workgroup's K-split with 16-byte loads in stages of eight 32-wide K-steps, double-buffered so
+// the next stage's weight loads are in flight during the current stage's MFMAs, and multiplies
+// them on the matrix cores against the token rows as the 16-wide N side
+// (v_mfma_f32_16x16x32_f16, FP16 hi/lo activations, FP32 accumulate); the four waves of a
+// workgroup share the operand rows in LDS. The token count B only widens the padded N side:
+// every output column runs the same instruction sequence in the same K order whatever B is, so a
+// row evaluated in a batch is bit-identical to the same row evaluated alone (Kipp Roadmap,
+// status v0.0.2: batched-equals-isolated).
 //
-// Split-K (Kipp Roadmap, status v0.0.4: the split-K partial buffer has its own constant)
-// writes one partial per split; the consumer kernel sums the splits in a fixed order, so the
-// result does not depend on scheduling. Q8_0 weights (Kipp Model Support, "Quantization
-// (Q8_0)") take one MFMA per quant block into a fresh accumulator, scaled in FP32.
+// Split-K (Kipp Roadmap, status v0.0.4: the split-K partial buffer has its own constant): each
+// split writes a partial P[s][b][n]; consumers sum the splits in a fixed order. Q8_0 weights
+// (Kipp Model Support, "Quantization (Q8_0)") take one MFMA per 32-weight quant block into a
+// fresh accumulator, scaled by the block's fp16 scale in FP32; scales are stored block-major
+// ([K/32][N]) so a lane's four row scales are one 8-byte load.
+//
+// For B <= 4 the activation rows of the workgroup's K range are built in LDS by a prologue that
+// performs the producer's elementwise step (X_RAW copy, X_RESID residual add times the norm
+// weight, X_SWIGLU silu(g) * u), so no separate kernel runs between two projections. The RMSNorm
+// 1/rms factor is a per-row scalar, so it is applied after the projection by its consumer; the
+// prologue only touches its own K range. For B > 4 the same arithmetic runs in rows_kernel into
+// global memory (same element-to-thread mapping and reduction order) and the matvec reads its
+// operands there.
 #include "gqa_common.h"
 
 namespace gqa {
 
-template <int EPI, bool Q8, int NT>
-__global__ __launch_bounds__(64) void gemv_kernel(const uint16_t* __restrict__ W, const int8_t* __restrict__ Wq,
-                                                  const f16* __restrict__ Wd, int K, int N,
-                                                  const f16* __restrict__ Xhi, const f16* __restrict__ Xlo, int ldx,
-                                                  int B, int klen, float* __restrict__ P, int64_t part_stride,
-                                                  int ldp, f16* __restrict__ Mhi, f16* __restrict__ Mlo, int ldm,
-                                                  float m_scale) {
-  constexpr int NA = EPI == EPI_SWIGLU ? 2 : 1;  // weight tiles per wave (gate, up)
-  const int lane = threadIdx.x;
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const int n0 = blockIdx.x * 16 * NA;
-  const int s = blockIdx.y;
-  const int kb = s * klen, ke = kb + klen;
+constexpr int kGemvWaves = 4;
+constexpr int kGemvStage = 8;     // 32-wide K-steps per pipeline stage
+constexpr int kXldsMaxRows = 4;
 
-  f32x4 acc[NA][NT];
+// Operand element e (absolute K index) of row b for the X_RESID / X_SWIGLU modes, and the
+// residual value (X_RESID) for the sum of squares. Thread t of a 256-thread block owns elements
+// k0 + t + 256 j of a K range; partial sums are added in split order.
+struct ElemOut {
+  float y;    // operand value before the hi/lo split
+  float x;    // X_RESID: updated residual value
+};
+
+__device__ __forceinline__ void resid_elems(const XSrc& xs, int b, int k0, int klen, int jbeg, float (&xv)[4],
+                                            float (&yv)[4]) {
+  const int t = threadIdx.x;
+  float rv[4], acc[4];
+  float pv[4][8];
 #pragma unroll
-  for (int a = 0; a < NA; ++a)
+  for (int q = 0; q < 4; ++q) {
+    const int off = t + 256 * (jbeg + q);
+    const bool ok = off < klen;
+    rv[q] = ok ? xs.res[(int64_t)b * xs.H + k0 + off] : 0.f;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) acc[a][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 8; ++s)
+      if (s < xs.nsplit) pv[q][s] = ok ? xs.part[(int64_t)s * xs.pstride + (int64_t)b * xs.pld + k0 + off] : 0.f;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[q] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s < xs.nsplit) acc[q] += pv[q][s];
+    const int off = t + 256 * (jbeg + q);
+    xv[q] = xs.nsplit > 0 ? __fadd_rn(rv[q], __fmul_rn(acc[q], xs.pscale)) : rv[q];
+    yv[q] = off < klen ? __fmul_rn(xv[q], bf16_bits_to_f32(xs.w[k0 + off])) : 0.f;
+  }
+}
+
+__device__ __forceinline__ float swiglu_elem(const XSrc& xs, int b, int f, float c) {
+  const int64_t rg = (int64_t)32 * (f / 16) + (f % 16);
+  float g = 0.f, u = 0.f;
+  for (int s = 0; s < xs.gu_split; ++s) {
+    const float* p = xs.gu + (int64_t)s * xs.gu_stride + (int64_t)b * xs.gu_ld;
+    g += p[rg];
+    u += p[rg + 16];
+  }
+  g = __fmul_rn(g, c);
+  u = __fmul_rn(u, c);
+  return __fmul_rn(__fdiv_rn(g, 1.0f + expf(-g)), u);
+}
+
+// Builds the operand rows of one K range [k0, k0 + klen) of row b. dst(e_off, hi, lo) stores
+// one element; with `writer`, X_RESID also stores x to res_out and returns the range's sum of
+// squares (thread order, then the 64 lanes, then the four waves) in ss_out[range][b].
+template <class Store>
+__device__ __forceinline__ void build_range(const XSrc& xs, int b, int k0, int klen, int range, bool writer,
+                                            float* red, Store dst) {
+  const int nj = (klen + 255) / 256;
+  if (xs.mode == X_RESID) {
+    float ssq = 0.f;
+    for (int j0 = 0; j0 < nj; j0 += 4) {
+      float xv[4], yv[4];
+      resid_elems(xs, b, k0, klen, j0, xv, yv);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int off = threadIdx.x + 256 * (j0 + q);
+        if (off < klen) {
+          f16 h, l;
+          split_f16(yv[q], h, l);
+          dst(off, h, l);
+          if (writer) {
+            xs.res_out[(int64_t)b * xs.H + k0 + off] = xv[q];
+            ssq = __fadd_rn(ssq, __fmul_rn(xv[q], xv[q]));
+          }
+        }
+      }
+    }
+    if (writer) {
+      ssq = wave_sum(ssq);
+      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ssq;
+      __syncthreads();
+      if (threadIdx.x == 0) xs.ss_out[range * 32 + b] = __fadd_rn(__fadd_rn(__fadd_rn(red[0], red[1]), red[2]), red[3]);
+      __syncthreads();
+    }
+  } else if (xs.mode == X_SWIGLU) {
+    const float c = inv_rms_from_ss(xs.ss, xs.ss_n, b, xs.H, xs.eps);
+    for (int off = threadIdx.x; off < klen; off += 256) {
+      f16 h, l;
+      split_f16(swiglu_elem(xs, b, k0 + off, c), h, l);
+      dst(off, h, l);
+    }
+  }
+}
+
+template <bool Q8, int NT, bool XLDS>
+__global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* __restrict__ W,
+                                                               const int8_t* __restrict__ Wq,
+                                                               const f16* __restrict__ Wd, int K, int N, XSrc xs,
+                                                               int B, int klen, float* __restrict__ P,
+                                                               int64_t part_stride, int ldp,
+                                                               float2* __restrict__ cand) {
+  constexpr int U = kGemvStage;
+  constexpr int NW = kGemvWaves;
+  __shared__ float red[4];
+  extern __shared__ f16 sx[];                     // XLDS: [B][2][klen] (hi, lo)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int tile = blockIdx.x * NW + wave;        // 16-row tile of this wave
+  const bool has_tile = tile * 16 < N;
+  const int n0 = (has_tile ? tile : 0) * 16;
+  const int s = blockIdx.y;
+  const int k0 = s * klen;
+  const int kb = k0, ke = k0 + klen;
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t rowoff = (int64_t)(n0 + r16) * K;
+  struct Buf {
+    uint4 wv[U];
+    uint2 qv[U];
+    uint2 sc[U];
+  };
+  auto fetch = [&](Buf& f, int k) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = k + u * 32;
+      const bool ok = kk < ke && has_tile;
+      if (Q8) {
+        f.qv[u] = ok ? *(const uint2*)(Wq + rowoff + kk + g4 * 8) : uint2{0, 0};
+        f.sc[u] = ok ? *(const uint2*)(Wd + (int64_t)(kk / 32) * N + n0 + g4 * 4) : uint2{0, 0};
+      } else {
+        f.wv[u] = ok ? *(const uint4*)(W + rowoff + kk + g4 * 8) : uint4{0, 0, 0, 0};
+      }
+    }
+  };
+  constexpr int STEP = 32 * U;
+  Buf b0, b1;
+  fetch(b0, kb);   // first weight stage in flight during the prologue
 
   const f16* xh[NT];
   const f16* xl[NT];
@@ -44,166 +175,223 @@ __global__ __launch_bounds__(64) void gemv_kernel(const uint16_t* __restrict__ W
   for (int j = 0; j < NT; ++j) {
     int b = j * 16 + r16;
     xv[j] = b < B;
-    xh[j] = Xhi + (int64_t)(xv[j] ? b : 0) * ldx + g4 * 8;
-    xl[j] = Xlo + (int64_t)(xv[j] ? b : 0) * ldx + g4 * 8;
+    if (XLDS) {
+      xh[j] = sx + (int64_t)(xv[j] ? b : 0) * 2 * klen + g4 * 8 - k0;
+      xl[j] = xh[j] + klen;
+    } else {
+      xh[j] = xs.hi + (int64_t)(xv[j] ? b : 0) * xs.ld + g4 * 8;
+      xl[j] = xs.lo + (int64_t)(xv[j] ? b : 0) * xs.ld + g4 * 8;
+    }
   }
+  if (XLDS) {
+    if (xs.mode == X_RAW) {
+      const int per_row = klen / 8;
+      for (int c = threadIdx.x; c < B * 2 * per_row; c += 64 * NW) {
+        int b = c / (2 * per_row), rem = c - b * 2 * per_row, hl = rem / per_row, q = rem - hl * per_row;
+        const f16* src = (hl ? xs.lo : xs.hi) + (int64_t)b * xs.ld + k0 + q * 8;
+        *(uint4*)(sx + (int64_t)b * 2 * klen + hl * klen + q * 8) = *(const uint4*)src;
+      }
+    } else {
+      const bool writer = blockIdx.x == 0;
+      for (int b = 0; b < B; ++b) {
+        f16* row = sx + (int64_t)b * 2 * klen;
+        build_range(xs, b, k0, klen, s, writer, red, [&](int off, f16 h, f16 l) {
+          row[off] = h;
+          row[klen + off] = l;
+        });
+      }
+    }
+    __syncthreads();
+  }
+  if (!has_tile) return;
 
-  auto step = [&](const f16x8 (&a)[NA], int k, const float (&sc)[NA][4]) {
+  auto compute = [&](const Buf& f, int k) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      f16x8 bh = f16x8{}, bl = f16x8{};
-      if (xv[j]) {
-        bh = *(const f16x8*)(xh[j] + k);
-        bl = *(const f16x8*)(xl[j] + k);
+    for (int u = 0; u < U; ++u) {
+      const int kk = k + u * 32;
+      const bool ok = kk < ke;
+      f16x8 bh[NT], bl[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        bh[j] = (ok && xv[j]) ? *(const f16x8*)(xh[j] + kk) : f16x8{};
+        bl[j] = (ok && xv[j]) ? *(const f16x8*)(xl[j] + kk) : f16x8{};
+      }
+      f16x8 a;
+      if (Q8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = (f16)(float)(int8_t)((f.qv[u].x >> (8 * e)) & 0xFF);
+          a[4 + e] = (f16)(float)(int8_t)((f.qv[u].y >> (8 * e)) & 0xFF);
+        }
+      } else {
+        a = bf16x8_to_f16x8(f.wv[u]);
+      }
+      float sc[4] = {0.f, 0.f, 0.f, 0.f};
+      if (Q8) {
+        sc[0] = (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x & 0xFFFF));
+        sc[1] = (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x >> 16));
+        sc[2] = (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y & 0xFFFF));
+        sc[3] = (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y >> 16));
       }
 #pragma unroll
-      for (int aa = 0; aa < NA; ++aa) {
+      for (int j = 0; j < NT; ++j) {
         if (Q8) {
           f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
-          p = mfma16(a[aa], bh, p);
-          p = mfma16(a[aa], bl, p);
+          p = mfma16(a, bh[j], p);
+          p = mfma16(a, bl[j], p);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[aa][j][r] = fmaf(sc[aa][r], p[r], acc[aa][j][r]);
+          for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sc[r], p[r], acc[j][r]);
         } else {
-          acc[aa][j] = mfma16(a[aa], bh, acc[aa][j]);
-          acc[aa][j] = mfma16(a[aa], bl, acc[aa][j]);
+          acc[j] = mfma16(a, bh[j], acc[j]);
+          acc[j] = mfma16(a, bl[j], acc[j]);
         }
       }
     }
   };
-
-  constexpr int U = 8;
+  // Steps past ke load zeros (weights and activations), so they add exact zeros.
   int k = kb;
-  for (; k + 32 * U <= ke; k += 32 * U) {
-    uint4 wv[NA][U];
-    uint2 qv[NA][U];
-    float sc[NA][U][4];
-#pragma unroll
-    for (int aa = 0; aa < NA; ++aa)
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        int64_t row = n0 + aa * 16 + r16;
-        int kk = k + u * 32 + g4 * 8;
-        if (Q8) {
-          qv[aa][u] = *(const uint2*)(Wq + row * K + kk);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            sc[aa][u][r] = (float)Wd[(int64_t)(n0 + aa * 16 + g4 * 4 + r) * (K / 32) + (k + u * 32) / 32];
-        } else {
-          wv[aa][u] = *(const uint4*)(W + row * K + kk);
-        }
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      f16x8 a[NA];
-      float scu[NA][4];
-#pragma unroll
-      for (int aa = 0; aa < NA; ++aa) {
-        if (Q8) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a[aa][e] = (f16)(float)(int8_t)((qv[aa][u].x >> (8 * e)) & 0xFF);
-            a[aa][4 + e] = (f16)(float)(int8_t)((qv[aa][u].y >> (8 * e)) & 0xFF);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) scu[aa][r] = sc[aa][u][r];
-        } else {
-          a[aa] = bf16x8_to_f16x8(wv[aa][u]);
-        }
-      }
-      step(a, k + u * 32, scu);
-    }
-  }
-  for (; k < ke; k += 32) {
-    f16x8 a[NA];
-    float scu[NA][4];
-#pragma unroll
-    for (int aa = 0; aa < NA; ++aa) {
-      int64_t row = n0 + aa * 16 + r16;
-      int kk = k + g4 * 8;
-      if (Q8) {
-        uint2 q = *(const uint2*)(Wq + row * K + kk);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[aa][e] = (f16)(float)(int8_t)((q.x >> (8 * e)) & 0xFF);
-          a[aa][4 + e] = (f16)(float)(int8_t)((q.y >> (8 * e)) & 0xFF);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) scu[aa][r] = (float)Wd[(int64_t)(n0 + aa * 16 + g4 * 4 + r) * (K / 32) + k / 32];
-      } else {
-        a[aa] = bf16x8_to_f16x8(*(const uint4*)(W + row * K + kk));
-      }
-    }
-    step(a, k, scu);
+  while (true) {
+    if (k + STEP < ke) fetch(b1, k + STEP);
+    compute(b0, k);
+    k += STEP;
+    if (k >= ke) break;
+    if (k + STEP < ke) fetch(b0, k + STEP);
+    compute(b1, k);
+    k += STEP;
+    if (k >= ke) break;
   }
 
-  // acc[aa][j][r] = value of weight row n0 + aa*16 + 4*g4 + r for token row j*16 + r16.
-  if (EPI == EPI_SWIGLU) {
-    const int f = (n0 / 32) * 16 + g4 * 4;
+  // acc[j][r] = value of weight row n0 + 4*g4 + r for token row j*16 + r16.
+  const int n = n0 + g4 * 4;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      int b = j * 16 + r16;
-      if (b < B) {
-        f16x4 hv, lv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float g = acc[0][j][r], u = acc[NA - 1][j][r];
-          float m = g / (1.0f + expf(-g)) * u * m_scale;
-          f16 h, l;
-          split_f16(m, h, l);
-          hv[r] = h;
-          lv[r] = l;
-        }
-        *(f16x4*)&Mhi[(int64_t)b * ldm + f] = hv;
-        *(f16x4*)&Mlo[(int64_t)b * ldm + f] = lv;
-      }
+  for (int j = 0; j < NT; ++j) {
+    int b = j * 16 + r16;
+    if (b < B) {
+      float4 v = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+      *(float4*)&P[(int64_t)s * part_stride + (int64_t)b * ldp + n] = v;
     }
-  } else {
-    const int n = n0 + g4 * 4;
+    if (cand) {
+      // argmax candidate of these 16 rows for token row b: (value, index), lowest index on ties
+      float bv = acc[j][0];
+      int bi = n;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      int b = j * 16 + r16;
-      if (b < B) {
-        float4 v = make_float4(acc[0][j][0], acc[0][j][1], acc[0][j][2], acc[0][j][3]);
-        *(float4*)&P[(int64_t)s * part_stride + (int64_t)b * ldp + n] = v;
+      for (int r = 1; r < 4; ++r)
+        if (acc[j][r] > bv) {
+          bv = acc[j][r];
+          bi = n + r;
+        }
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        float ov = __shfl_xor(bv, o, 64);
+        int oi = __shfl_xor(bi, o, 64);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
       }
+      if (g4 == 0 && b < B) cand[(int64_t)b * (N / 16) + tile] = make_float2(bv, __int_as_float(bi));
     }
   }
 }
 
-template <int EPI, bool Q8>
-static hipError_t launch_gemv_e(const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
-                                const f16* Xlo, int ldx, int B, int nsplit, float* P, int64_t part_stride, int ldp,
-                                f16* Mhi, f16* Mlo, int ldm, float m_scale, hipStream_t st) {
-  constexpr int NA = EPI == EPI_SWIGLU ? 2 : 1;
-  dim3 grid(N / (16 * NA), nsplit);
-  int klen = K / nsplit;
-  if (B <= 16)
-    hipLaunchKernelGGL((gemv_kernel<EPI, Q8, 1>), grid, dim3(64), 0, st, W, Wq, Wd, K, N, Xhi, Xlo, ldx, B, klen, P,
-                       part_stride, ldp, Mhi, Mlo, ldm, m_scale);
-  else
-    hipLaunchKernelGGL((gemv_kernel<EPI, Q8, 2>), grid, dim3(64), 0, st, W, Wq, Wd, K, N, Xhi, Xlo, ldx, B, klen, P,
-                       part_stride, ldp, Mhi, Mlo, ldm, m_scale);
+// B > 4: the prologue arithmetic of one K range of one row into global hi/lo rows
+// (grid: ranges x rows, 256 threads) -- the same element mapping and order as the LDS path.
+__global__ __launch_bounds__(256) void rows_kernel(XSrc xs, int klen, f16* __restrict__ yhi, f16* __restrict__ ylo,
+                                                   int ldy) {
+  __shared__ float red[4];
+  const int s = blockIdx.x, b = blockIdx.y, k0 = s * klen;
+  f16* hrow = yhi + (int64_t)b * ldy + k0;
+  f16* lrow = ylo + (int64_t)b * ldy + k0;
+  build_range(xs, b, k0, klen, s, true, red, [&](int off, f16 h, f16 l) {
+    hrow[off] = h;
+    lrow[off] = l;
+  });
+}
+
+// Requires K % (32 * nsplit) == 0 and N % 16 == 0. Each wave streams one 16-row tile over the
+// workgroup's K range; a workgroup holds four tiles that share one operand prologue. With
+// B <= 4 the operand rows are built in LDS by the xs.mode prologue; with B > 4 xs must be X_RAW
+// over global FP16 hi/lo rows.
+// cand (optional, nsplit == 1): per token row b and 16-row tile t, the tile's (max value, index
+// as float bits) at cand[b * (N / 16) + t], for a following argmax reduction.
+hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const XSrc& xs, int B,
+                       int nsplit, float* P, int64_t part_stride, int ldp, float2* cand, hipStream_t st) {
+  if (B < 1 || B > kMaxBatch || nsplit < 1 || K % (32 * nsplit) != 0 || N % 16 != 0) return hipErrorInvalidValue;
+  if (cand && nsplit != 1) return hipErrorInvalidValue;
+  const bool lds = B <= kXldsMaxRows;
+  if (!lds && xs.mode != X_RAW) return hipErrorInvalidValue;
+  if (xs.mode == X_RESID && (xs.nsplit > 8 || xs.H != K)) return hipErrorInvalidValue;
+  dim3 grid((N / 16 + kGemvWaves - 1) / kGemvWaves, nsplit);
+  const int klen = K / nsplit;
+  const size_t shm = lds ? (size_t)B * klen * 4 : 0;
+  if (shm > 64 * 1024) return hipErrorInvalidValue;
+  const dim3 blk(64 * kGemvWaves);
+#define GEMV_LAUNCH(Q8, NT, L)                                                                                   \
+  hipLaunchKernelGGL((gemv_kernel<Q8, NT, L>), grid, blk, shm, st, W, Wq, Wd, K, N, xs, B, klen, P, part_stride, \
+                     ldp, cand)
+  if (lds) {
+    if (Wq) GEMV_LAUNCH(true, 1, true);
+    else GEMV_LAUNCH(false, 1, true);
+  } else if (B <= 16) {
+    if (Wq) GEMV_LAUNCH(true, 1, false);
+    else GEMV_LAUNCH(false, 1, false);
+  } else {
+    if (Wq) GEMV_LAUNCH(true, 2, false);
+    else GEMV_LAUNCH(false, 2, false);
+  }
+#undef GEMV_LAUNCH
   return hipGetLastError();
 }
 
-// B <= 16 and B in 17..32 use the same per-column arithmetic (one or two 16-column tiles).
-hipError_t launch_gemv(int epi, const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
-                       const f16* Xlo, int ldx, int B, int nsplit, float* P, int64_t part_stride, int ldp, f16* Mhi,
-                       f16* Mlo, int ldm, float m_scale, hipStream_t st) {
-  if (B < 1 || B > kMaxBatch || nsplit < 1 || K % (32 * nsplit) != 0) return hipErrorInvalidValue;
-  if (epi == EPI_SWIGLU) {
-    if (N % 32 != 0 || nsplit != 1) return hipErrorInvalidValue;
-    return Wq ? launch_gemv_e<EPI_SWIGLU, true>(W, Wq, Wd, K, N, Xhi, Xlo, ldx, B, 1, P, part_stride, ldp, Mhi, Mlo,
-                                                ldm, m_scale, st)
-              : launch_gemv_e<EPI_SWIGLU, false>(W, Wq, Wd, K, N, Xhi, Xlo, ldx, B, 1, P, part_stride, ldp, Mhi, Mlo,
-                                                 ldm, m_scale, st);
+// Operand rows for B > 4 (same K ranges as the matvec that will consume them: nsplit ranges).
+hipError_t launch_rows(const XSrc& xs, int K, int nsplit, int B, f16* yhi, f16* ylo, int ldy, hipStream_t st) {
+  if (xs.mode == X_RAW || K % nsplit != 0 || (xs.mode == X_RESID && xs.nsplit > 8)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rows_kernel, dim3(nsplit, B), dim3(256), 0, st, xs, K / nsplit, yhi, ylo, ldy);
+  return hipGetLastError();
+}
+
+// Full RMSNorm of B rows (res + partials, times w, times 1/rms) into global hi/lo: one
+// 256-thread block per row; used before the lm_head.
+__global__ __launch_bounds__(256) void final_norm_kernel(XSrc xs, f16* __restrict__ yhi, f16* __restrict__ ylo,
+                                                         int ldy) {
+  __shared__ float red[4];
+  const int b = blockIdx.x, H = xs.H;
+  float ssq = 0.f;
+  const int nj = (H + 255) / 256;
+  float xvals[16];
+#pragma unroll
+  for (int j0 = 0; j0 < 16; j0 += 4) {
+    if (j0 < nj) {
+      float xv[4], yv[4];
+      resid_elems(xs, b, 0, H, j0, xv, yv);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xvals[j0 + q] = xv[q];
+        if (threadIdx.x + 256 * (j0 + q) < H) ssq = __fadd_rn(ssq, __fmul_rn(xv[q], xv[q]));
+      }
+    }
   }
-  if (N % 16 != 0) return hipErrorInvalidValue;
-  return Wq ? launch_gemv_e<EPI_STORE, true>(W, Wq, Wd, K, N, Xhi, Xlo, ldx, B, nsplit, P, part_stride, ldp, Mhi,
-                                             Mlo, ldm, m_scale, st)
-            : launch_gemv_e<EPI_STORE, false>(W, Wq, Wd, K, N, Xhi, Xlo, ldx, B, nsplit, P, part_stride, ldp, Mhi,
-                                              Mlo, ldm, m_scale, st);
+  ssq = wave_sum(ssq);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ssq;
+  __syncthreads();
+  const float tot = __fadd_rn(__fadd_rn(__fadd_rn(red[0], red[1]), red[2]), red[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)H + xs.eps);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int e = threadIdx.x + 256 * j;
+    if (j < nj && e < H) {
+      f16 h, l;
+      split_f16(__fmul_rn(__fmul_rn(xvals[j], inv), bf16_bits_to_f32(xs.w[e])), h, l);
+      yhi[(int64_t)b * ldy + e] = h;
+      ylo[(int64_t)b * ldy + e] = l;
+    }
+  }
+}
+
+hipError_t launch_final_norm(const XSrc& xs, int B, f16* yhi, f16* ylo, int ldy, hipStream_t st) {
+  if (xs.mode != X_RESID || xs.H > 4096 || xs.nsplit > 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(final_norm_kernel, dim3(B), dim3(256), 0, st, xs, yhi, ylo, ldy);
+  return hipGetLastError();
 }
 
 }  // namespace gqa

@@ -7,7 +7,7 @@
 // given by the layout mode (plain with a row offset, or the 16-row gate/up interleave).
 //
 // Q8_0 (Kipp Model Support, "Quantization (Q8_0)"): 32-weight blocks along a row, an fp16
-// scale and 32 int8 quants. d = amax / 127 (FP32 division), scale = fp16_rne(d),
+// scale and 32 int8 quants (stored here as an int8 matrix plus a block-major scale matrix). d = amax / 127 (FP32 division), scale = fp16_rne(d),
 // q = clamp(round_half_away(w / d), -127, 127), and q = 0 when d = 0.
 #include "gqa_common.h"
 
@@ -42,7 +42,8 @@ __global__ void fill_u16_kernel(uint16_t* __restrict__ dst, int64_t n, uint16_t 
     dst[i] = v;
 }
 
-// One thread per 32-weight block of a BF16 matrix [rows][cols] -> q int8 [rows][cols], d fp16 [rows][cols/32].
+// One thread per 32-weight block of a BF16 matrix [rows][cols] -> q int8 [rows][cols] and the
+// fp16 scales block-major: d[blk][row] (cols/32 x rows).
 __global__ void quantize_q8_0_kernel(const uint16_t* __restrict__ w, int8_t* __restrict__ q, f16* __restrict__ d,
                                      int64_t rows, int64_t cols) {
   int64_t nb = rows * (cols / 32);
@@ -56,7 +57,8 @@ __global__ void quantize_q8_0_kernel(const uint16_t* __restrict__ w, int8_t* __r
       amax = fmaxf(amax, fabsf(v[i]));
     }
     float dd = __fdiv_rn(amax, 127.0f);
-    d[b] = (f16)dd;
+    const int64_t row = b / (cols / 32), blk = b - row * (cols / 32);
+    d[blk * rows + row] = (f16)dd;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       float r = dd == 0.f ? 0.f : __fdiv_rn(v[i], dd);

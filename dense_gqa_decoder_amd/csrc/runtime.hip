@@ -33,17 +33,20 @@ hipError_t launch_qk_rope_kv(bool decode, const float* qkv, int nsplit, int part
                              const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
                              const float* rsin, int pos0, const int32_t* table0, const Rows& rows, uint16_t* kpool,
                              uint16_t* vpool, float* qout, int nrows, hipStream_t st);
-hipError_t launch_argmax(const float* logits, int64_t ld, int V, int B, int32_t* out, hipStream_t st);
+hipError_t launch_argmax(const float2* cand, int ntiles, int B, int32_t* out, hipStream_t st);
 hipError_t launch_gemm(int epi, const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
                        const f16* Xlo, int ldx, int T, float* C, int ldc, float out_scale, f16* Mhi, f16* Mlo,
                        int ldm, float m_scale, hipStream_t st);
-hipError_t launch_gemv(int epi, const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
-                       const f16* Xlo, int ldx, int B, int nsplit, float* P, int64_t part_stride, int ldp, f16* Mhi,
-                       f16* Mlo, int ldm, float m_scale, hipStream_t st);
+hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const XSrc& xs, int B,
+                       int nsplit, float* P, int64_t part_stride, int ldp, float2* cand, hipStream_t st);
+hipError_t launch_rows(const XSrc& xs, int K, int nsplit, int B, f16* yhi, f16* ylo, int ldy, hipStream_t st);
+hipError_t launch_final_norm(const XSrc& xs, int B, f16* yhi, f16* ylo, int ldy, hipStream_t st);
 hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const int32_t* table, const uint16_t* kpool,
                                const uint16_t* vpool, float out_scale, f16* ohi, f16* olo, int ldo, hipStream_t st);
-hipError_t launch_attn_decode(const float* q, int nq, const Rows& rows, int B, int max_ctx, const uint16_t* kpool,
-                              const uint16_t* vpool, float* part, int max_chunks, float out_scale, f16* ohi,
+hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* ss,
+                              int ss_n, int H, const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
+                              const float* rsin, const Rows& rows, int B, int max_ctx, uint16_t* kpool,
+                              uint16_t* vpool, float* part, int max_chunks, int* counters, float out_scale, f16* ohi,
                               f16* olo, int ldo, hipStream_t st);
 }  // namespace gqa
 
@@ -99,11 +102,15 @@ struct gqa_model {
   int dev = 0, cu = 0, R = 0;
   int QKV = 0, QD = 0;          // fused q|k|v rows, attention width
   int max_chunks = 0;
-  int s_qkv = 1, s_o = 1, s_d = 1;  // decode split-K counts
+  int s_qkv = 1, s_o = 1, s_gu = 1, s_d = 1;  // decode split-K counts
   std::vector<LayerW> L;
   uint16_t *embed = nullptr, *lm_head = nullptr, *final_norm = nullptr;
   float *rcos = nullptr, *rsin = nullptr;
-  float *x = nullptr, *qkv = nullptr, *q = nullptr, *part = nullptr, *apart = nullptr;
+  float *x = nullptr, *x2 = nullptr, *qkv = nullptr, *q = nullptr, *part = nullptr, *part2 = nullptr,
+        *apart = nullptr;
+  int32_t* counters = nullptr;  // decode attention: finished chunks per (row, KV head)
+  float* ss = nullptr;          // decode: sum-of-squares partials [2][8][32] (q|k|v input, gate|up input)
+  float2* cand = nullptr;   // lm_head argmax candidates [32][vocab / 16]
   f16 *xh = nullptr, *xl = nullptr, *oh = nullptr, *ol = nullptr, *mh = nullptr, *ml = nullptr;
   int32_t *ids_dev = nullptr, *err = nullptr;
   int32_t* ids_host = nullptr;  // pinned staging
@@ -168,9 +175,12 @@ int check_desc(const gqa_model_desc* d) {
   return GQA_OK;
 }
 
-// Largest split count <= want with K % (32 * s) == 0.
+// Smallest split count >= want (at most 8) with K % (32 * s) == 0, else the largest below.
 int pick_split(int K, int want) {
-  for (int s = std::min(want, 8); s > 1; --s)
+  want = std::max(1, std::min(want, 8));
+  for (int s = want; s <= 8; ++s)
+    if (K % (32 * s) == 0) return s;
+  for (int s = want; s > 1; --s)
     if (K % (32 * s) == 0) return s;
   return 1;
 }
@@ -217,10 +227,21 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   m->QD = NQ * kHeadDim;
   m->QKV = m->QD + 2 * kKvHeads * kHeadDim;
   m->R = d.max_round_tokens > 0 ? d.max_round_tokens : std::max(64, m->cu * 8);
-  m->max_chunks = (d.max_positions + 63) / 64;
-  m->s_qkv = pick_split(H, std::max(1, 2048 / (m->QKV / 16)));
-  m->s_o = pick_split(m->QD, std::max(1, 2048 / (H / 16)));
-  m->s_d = pick_split(F, std::max(1, 2048 / (H / 16)));
+  m->max_chunks = (d.max_positions + 127) / 128;   // decode attention: 128 positions per chunk
+  // split-K counts of the decode matvecs: enough workgroups (about 2 per CU) to stream weights
+  // from every CU; fixed per model so every row sums its splits in the same order
+  // at least ~1.5 workgroups (four 16-row tiles each) per CU for every matvec, and K ranges of
+  // at most 2560 (the prologue of a workgroup builds its own K range of the operand rows)
+  const int want_wg = 3 * m->cu / 2;
+  auto split_for = [&](int K, int N) {
+    const int wgs = (N / 16 + 3) / 4;
+    int want = std::max((want_wg + wgs - 1) / wgs, (K + 2559) / 2560);
+    return pick_split(K, want);
+  };
+  m->s_qkv = split_for(H, m->QKV);
+  m->s_o = split_for(m->QD, H);
+  m->s_gu = split_for(H, 2 * F);
+  m->s_d = split_for(F, H);
   const bool q8 = d.scheme == GQA_SCHEME_Q8_0;
   int64_t* wb = &m->weight_bytes;
 
@@ -268,6 +289,7 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   const int rows = std::max(m->R, kMaxBatch);
   int64_t* sb = &m->scratch_bytes;
   ALLOC(m->x, (int64_t)rows * H, sb);
+  ALLOC(m->x2, (int64_t)kMaxBatch * H, sb);
   ALLOC(m->xh, (int64_t)rows * H, sb);
   ALLOC(m->xl, (int64_t)rows * H, sb);
   ALLOC(m->qkv, (int64_t)m->R * m->QKV, sb);
@@ -276,10 +298,14 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   ALLOC(m->ol, (int64_t)rows * m->QD, sb);
   ALLOC(m->mh, (int64_t)rows * F, sb);
   ALLOC(m->ml, (int64_t)rows * F, sb);
-  m->part_floats = (int64_t)8 * kMaxBatch * std::max(m->QKV, H);
+  m->part_floats = (int64_t)8 * kMaxBatch * std::max(std::max(m->QKV, 2 * F), H);
   ALLOC(m->part, m->part_floats, sb);
+  ALLOC(m->part2, m->part_floats, sb);
   ALLOC(m->apart, (int64_t)kMaxBatch * NQ * m->max_chunks * 132, sb);
+  ALLOC(m->counters, kMaxBatch * kKvHeads, sb);
+  ALLOC(m->ss, 2 * 8 * 32, sb);
   ALLOC(m->ids_dev, std::max(d.max_positions, kMaxBatch), sb);
+  ALLOC(m->cand, (int64_t)kMaxBatch * (V / 16), sb);
   ALLOC(m->err, 1, sb);
   ALLOC(m->rcos, (int64_t)d.max_positions * 64, sb);
   ALLOC(m->rsin, (int64_t)d.max_positions * 64, sb);
@@ -347,6 +373,7 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
     chk(hipMemsetAsync(w.vpool, 0, pool_elems * 2, st));
   }
   chk(hipMemsetAsync(m->err, 0, 4, st));
+  chk(hipMemsetAsync(m->counters, 0, sizeof(int32_t) * kMaxBatch * kKvHeads, st));
   chk(hipDeviceSynchronize());
   if (tmp) (void)hipFree(tmp);
   if (ge != hipSuccess) {
@@ -513,43 +540,103 @@ struct ProfScope {
     if (e_ != hipSuccess) return fail(GQA_E_HIP, "launch failed at %s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
 
-// Decode / batched decode over B rows whose embeddings are in m->x; ids already on the device.
+// Decode / batched decode over B rows; ids already on the device. Per layer: q|k|v matvec (its
+// prologue adds the previous down projection to the residual stream and multiplies by the
+// norm weight), fused attention (1/rms scale, q/k norm, RoPE, KV write, attention, chunk
+// merge), o matvec, gate|up matvec (prologue: residual add of the o projection times the norm
+// weight), down matvec (prologue: 1/rms scale and SwiGLU). The residual stream alternates
+// between two buffers so a prologue can write the updated stream while other workgroups still
+// read the previous one. With B > 4 the prologue work runs in rows_kernel with the same
+// arithmetic.
 int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t* ids_dev, float* logits,
                int32_t* argmax, hipStream_t st) {
   const gqa_model_desc& d = m->d;
   const int H = d.hidden, F = d.ffn, V = d.vocab, NQ = d.n_q_heads, QD = m->QD, QKV = m->QKV;
   const float eps = d.rms_eps;
-  const int64_t pstride = (int64_t)kMaxBatch * std::max(QKV, H);
-  LAUNCH(launch_embed(m->embed, ids_dev, B, H, V, m->x, m->err, st));
-  LAUNCH(launch_rmsnorm(m->x, H, nullptr, 0, 0, 0, 1.f, m->L[0].attn_norm, H, eps, 1.f, m->xh, m->xl, H, B, st));
+  const bool fused = B <= 4;
+  const int64_t pstride = m->part_floats / 8;
+  float* xa = m->x;
+  float* xb = m->x2;
+  float* P0 = m->part;
+  float* P1 = m->part2;
+  float* ss_qkv = m->ss;
+  float* ss_gu = m->ss + 8 * 32;
+  LAUNCH(launch_embed(m->embed, ids_dev, B, H, V, xa, m->err, st));
+
+  auto resid_src = [&](float* res, float* res_out, const float* part, int nsplit, float pscale, const uint16_t* w,
+                       float* ss_out) {
+    XSrc x{};
+    x.mode = X_RESID;
+    x.res = res;
+    x.res_out = res_out;
+    x.part = part;
+    x.nsplit = part ? nsplit : 0;
+    x.pstride = pstride;
+    x.pld = H;
+    x.pscale = pscale;
+    x.w = w;
+    x.ss_out = ss_out;
+    x.H = H;
+    x.eps = eps;
+    return x;
+  };
+  auto raw_src = [&](const f16* hi, const f16* lo, int ld) {
+    XSrc x{};
+    x.mode = X_RAW;
+    x.hi = hi;
+    x.lo = lo;
+    x.ld = ld;
+    return x;
+  };
+  // matvec over an operand built by a prologue: in LDS (B <= 4) or by rows_kernel first
+  auto gemv_built = [&](const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const XSrc& xs,
+                        int nsplit, float* P, int ldp, f16* hi, f16* lo) -> hipError_t {
+    if (fused) return launch_gemv(W, Wq, Wd, K, N, xs, B, nsplit, P, pstride, ldp, nullptr, st);
+    hipError_t e = launch_rows(xs, K, nsplit, B, hi, lo, K, st);
+    if (e != hipSuccess) return e;
+    return launch_gemv(W, Wq, Wd, K, N, raw_src(hi, lo, K), B, nsplit, P, pstride, ldp, nullptr, st);
+  };
+
+  const float* prev = nullptr;
+  int prev_split = 0;
   for (int l = 0; l < d.n_layers; ++l) {
     const LayerW& w = m->L[l];
-    LAUNCH(launch_gemv(EPI_STORE, w.wqkv, w.qqkv, w.sqkv, H, QKV, m->xh, m->xl, H, B, m->s_qkv, m->part, pstride, QKV,
-                       nullptr, nullptr, 0, 1.f, st));
-    LAUNCH(launch_qk_rope_kv(true, m->part, m->s_qkv, (int)pstride, QKV, NQ, w.q_norm, w.k_norm, eps, m->rcos,
-                             m->rsin, 0, nullptr, rows, w.kpool, w.vpool, m->q, B, st));
-    LAUNCH(launch_attn_decode(m->q, NQ, rows, B, max_ctx, w.kpool, w.vpool, m->apart, m->max_chunks, kAttnOutScale,
-                              m->oh, m->ol, QD, st));
-    LAUNCH(launch_gemv(EPI_STORE, w.wo, w.qo, w.so, QD, H, m->oh, m->ol, QD, B, m->s_o, m->part, pstride, H, nullptr,
-                       nullptr, 0, 1.f, st));
-    LAUNCH(launch_rmsnorm(m->x, H, m->part, m->s_o, (int)pstride, H, 1.f / kAttnOutScale, w.ffn_norm, H, eps, 1.f,
-                          m->xh, m->xl, H, B, st));
+    LAUNCH(gemv_built(w.wqkv, w.qqkv, w.sqkv, H, QKV, resid_src(xa, xb, prev, prev_split, 1.f, w.attn_norm, ss_qkv),
+                      m->s_qkv, P0, QKV, m->xh, m->xl));
+    std::swap(xa, xb);
+    LAUNCH(launch_attn_decode(P0, m->s_qkv, pstride, QKV, NQ, ss_qkv, m->s_qkv, H, w.q_norm, w.k_norm, eps, m->rcos,
+                              m->rsin, rows, B, max_ctx, w.kpool, w.vpool, m->apart, m->max_chunks, m->counters,
+                              kAttnOutScale, m->oh, m->ol, QD, st));
+    LAUNCH(launch_gemv(w.wo, w.qo, w.so, QD, H, raw_src(m->oh, m->ol, QD), B, m->s_o, P1, pstride, H, nullptr, st));
     {
       ProfScope ps(m, GQA_PROF_DECODE_GATEUP, st);
-      LAUNCH(launch_gemv(EPI_SWIGLU, w.wgu, w.qgu, w.sgu, H, 2 * F, m->xh, m->xl, H, B, 1, nullptr, 0, 0, m->mh,
-                         m->ml, F, 1.f, st));
+      LAUNCH(gemv_built(w.wgu, w.qgu, w.sgu, H, 2 * F,
+                        resid_src(xa, xb, P1, m->s_o, 1.f / kAttnOutScale, w.ffn_norm, ss_gu), m->s_gu, P0, 2 * F,
+                        m->xh, m->xl));
     }
-    LAUNCH(launch_gemv(EPI_STORE, w.wd, w.qd, w.sd, F, H, m->mh, m->ml, F, B, m->s_d, m->part, pstride, H, nullptr,
-                       nullptr, 0, 1.f, st));
-    const uint16_t* nw = l + 1 < d.n_layers ? m->L[l + 1].attn_norm : m->final_norm;
-    LAUNCH(launch_rmsnorm(m->x, H, m->part, m->s_d, (int)pstride, H, 1.f, nw, H, eps, 1.f, m->xh, m->xl, H, B, st));
+    std::swap(xa, xb);
+    XSrc sw{};
+    sw.mode = X_SWIGLU;
+    sw.gu = P0;
+    sw.gu_split = m->s_gu;
+    sw.gu_stride = pstride;
+    sw.gu_ld = 2 * F;
+    sw.ss = ss_gu;
+    sw.ss_n = m->s_gu;
+    sw.H = H;
+    sw.eps = eps;
+    LAUNCH(gemv_built(w.wd, w.qd, w.sd, F, H, sw, m->s_d, P1, H, m->mh, m->ml));
+    prev = P1;
+    prev_split = m->s_d;
   }
+  LAUNCH(launch_final_norm(resid_src(xa, nullptr, prev, prev_split, 1.f, m->final_norm, nullptr), B, m->xh, m->xl, H,
+                           st));
   {
     ProfScope ps(m, GQA_PROF_DECODE_LMHEAD, st);
-    LAUNCH(launch_gemv(EPI_STORE, m->lm_head, nullptr, nullptr, H, V, m->xh, m->xl, H, B, 1, logits, 0, V, nullptr,
-                       nullptr, 0, 1.f, st));
+    LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, H, V, raw_src(m->xh, m->xl, H), B, 1, logits, pstride, V,
+                       argmax ? m->cand : nullptr, st));
   }
-  if (argmax) LAUNCH(launch_argmax(logits, V, V, B, argmax, st));
+  if (argmax) LAUNCH(launch_argmax(m->cand, V / 16, B, argmax, st));
   return GQA_OK;
 }
 
@@ -606,9 +693,13 @@ int gqa_session_eval_prefill(gqa_session* s, const int32_t* ids, int32_t n, floa
     if (off + T == n) {
       LAUNCH(launch_rmsnorm(m->x + (int64_t)(T - 1) * H, H, nullptr, 0, 0, 0, 1.f, m->final_norm, H, eps, 1.f, m->xh,
                             m->xl, H, 1, st));
-      LAUNCH(launch_gemv(EPI_STORE, m->lm_head, nullptr, nullptr, H, V, m->xh, m->xl, H, 1, 1, logits, 0, V, nullptr,
-                         nullptr, 0, 1.f, st));
-      if (argmax) LAUNCH(launch_argmax(logits, V, V, 1, argmax, st));
+      XSrc raw{};
+      raw.mode = X_RAW;
+      raw.hi = m->xh;
+      raw.lo = m->xl;
+      raw.ld = H;
+      LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, H, V, raw, 1, 1, logits, 0, V, argmax ? m->cand : nullptr, st));
+      if (argmax) LAUNCH(launch_argmax(m->cand, V / 16, 1, argmax, st));
     }
   }
   s->pos += n;
@@ -776,10 +867,13 @@ int gqa_debug_read_q8(gqa_model* m, int32_t kind, int32_t layer, int32_t row0, i
   for (int r = 0; r < rows; ++r) {
     int pr = physical_row(m, kind, row0 + r, &base, &cols, true, layer);
     const f16* sb = kind == GQA_T_O ? w.so : kind == GQA_T_DOWN ? w.sd : (kind == GQA_T_GATE || kind == GQA_T_UP) ? w.sgu : w.sqkv;
+    const int64_t prow = kind == GQA_T_O || kind == GQA_T_DOWN ? d.hidden
+                         : (kind == GQA_T_GATE || kind == GQA_T_UP) ? 2 * (int64_t)d.ffn : m->QKV;   // physical rows
     HIP_TRY(hipMemcpy(quants + (int64_t)r * cols, (const int8_t*)base + (int64_t)pr * cols, (size_t)cols,
                       hipMemcpyDeviceToHost));
-    HIP_TRY(hipMemcpy(scales + (int64_t)r * (cols / 32), sb + (int64_t)pr * (cols / 32), (size_t)(cols / 32) * 2,
-                      hipMemcpyDeviceToHost));
+    // scales are block-major: [cols / 32][physical rows]
+    HIP_TRY(hipMemcpy2D(scales + (int64_t)r * (cols / 32), 2, sb + pr, (size_t)prow * 2, 2, cols / 32,
+                        hipMemcpyDeviceToHost));
   }
   return GQA_OK;
 }

@@ -190,14 +190,17 @@ def test_kv_cache_matches_oracle_storage(g):
     m.close()
 
 
-def test_batched_equals_isolated_bitwise(g):
+@pytest.mark.parametrize("nseq", [4, 7, 20])
+def test_batched_equals_isolated_bitwise(g, nseq):
+    """Up to four rows build their operands in the matvec prologues, more rows use the row
+    kernels; both must give exactly what a single row gets."""
     shape = synth.TINY
-    m = g.Model.from_shape(shape, seed=1001, kv_pool_blocks=64, max_positions=128)
-    lens = [20, 45, 70, 33]
+    m = g.Model.from_shape(shape, seed=1001, kv_pool_blocks=128 * 4, max_positions=160)
+    lens = [20, 45, 70, 33, 140, 1, 96, 64, 65, 31, 32, 127, 128, 129, 2, 3, 50, 77, 88, 99][:nseq]
     prompts = [synth.token_ids(100 + i, n) for i, n in enumerate(lens)]
     lg = torch.empty(shape.vocab, device="cuda")
-    A = [g.Session(m, 128) for _ in lens]
-    Bs = [g.Session(m, 128) for _ in lens]
+    A = [g.Session(m, 160) for _ in lens]
+    Bs = [g.Session(m, 160) for _ in lens]
     for sa, sb, p in zip(A, Bs, prompts):
         sa.prefill(p, lg)
         sb.prefill(p, lg)
