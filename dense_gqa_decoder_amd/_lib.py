@@ -65,6 +65,7 @@ _SIGS = {
     "gqa_debug_read_q8": (I32, [P, I32, I32, I32, I32, P, P]),
     "gqa_debug_read_kv": (I32, [P, I32, I32, I32, P, P]),
     "gqa_debug_read_rope": (I32, [P, I32, P, P]),
+    "gqa_debug_read_scratch": (I32, [P, I32, ctypes.c_int64, ctypes.c_int64, P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -179,3 +180,7 @@ def gqa_debug_read_kv(session, layer, pos0, n, k_ptr, v_ptr) -> None:
 
 def gqa_debug_read_rope(model, n, c_ptr, s_ptr) -> None:
     _check(lib().gqa_debug_read_rope(model, n, c_ptr, s_ptr))
+
+
+def gqa_debug_read_scratch(model, which, offset, count, dst_ptr) -> None:
+    _check(lib().gqa_debug_read_scratch(model, which, offset, count, dst_ptr))

@@ -76,6 +76,18 @@ class Model:
         L.gqa_debug_read_q8(self.handle, L.GQA_T[kind], layer, row0, rows, q.ctypes.data, s.ctypes.data)
         return q, s
 
+    SCRATCH = {"resid_a": (0, np.float32), "resid_b": (1, np.float32), "part_a": (2, np.float32),
+               "part_b": (3, np.float32), "attn_hi": (4, np.float16), "attn_lo": (5, np.float16),
+               "mlp_hi": (6, np.float16), "mlp_lo": (7, np.float16), "norm_hi": (8, np.float16),
+               "norm_lo": (9, np.float16), "sumsq": (10, np.float32), "qrot": (11, np.float32),
+               "qkv": (12, np.float32)}
+
+    def read_scratch(self, name, offset, count):
+        which, dt = self.SCRATCH[name]
+        out = np.empty(count, dtype=dt)
+        L.gqa_debug_read_scratch(self.handle, which, offset, count, out.ctypes.data)
+        return out
+
     def read_rope(self, n):
         c = np.empty((n, 64), dtype=np.float32)
         s = np.empty((n, 64), dtype=np.float32)

@@ -8,12 +8,16 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgqa355.so")
-SOURCES = ["k_weights.hip", "k_elementwise.hip", "k_gemm.hip", "k_gemv.hip", "k_attn.hip", "runtime.hip"]
+SOURCES = ["k_weights.hip", "k_elementwise.hip", "k_gemm.hip", "k_gemv.hip", "k_gemv_full.hip", "k_attn.hip",
+           "runtime.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed FP32 instructions (v_pk_*_f32) anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no implicit multiply-add contraction: every kernel rounds the same expression the same way
+    # (explicit fmaf() where a fused multiply-add is intended)
+    "-ffp-contract=off",
 ]
 
 

@@ -7,6 +7,7 @@
 typedef _Float16 f16;
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace gqa {
@@ -60,11 +61,74 @@ struct XSrc {
   float eps;
 };
 
+enum FullMode : int { XF_RAW = 0, XF_NORM = 1 };
+
+// Arguments of the whole-K decode matvec (k_gemv_full.hip).
+struct FullArgs {
+  const uint16_t* W;
+  const int8_t* Wq;
+  const f16* Wd;
+  int K, N, B;
+  const f16* xhi;          // XF_RAW: [B][ldx]
+  const f16* xlo;
+  int ldx;
+  const float* xres;       // XF_NORM: [B][K] residual stream
+  const uint16_t* nw;      // XF_NORM: norm weight [K]
+  float eps;
+  float* ss_out;           // XF_NORM: [range][32] sums of squares (written by workgroup 0)
+  float* y;                // EPI_STORE / EPI_ADD: [B][ldy]
+  int ldy;
+  float yscale;
+  f16* mhi;                // EPI_SWIGLU: [B][ldm]
+  f16* mlo;
+  int ldm;
+  float2* cand;            // EPI_STORE: argmax candidates [B][N / 16] or null
+};
+
 // Sum-of-squares partials: ss[range][row], kMaxBatch rows per range.
+// n <= 8; the loads are issued together and summed in range order.
 __device__ __forceinline__ float inv_rms_from_ss(const float* ss, int n, int row, int H, float eps) {
+  float v[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) v[r] = ss[min(r, n - 1) * 32 + row];   // unconditional, no branches
   float t = 0.f;
-  for (int r = 0; r < n; ++r) t += ss[r * 32 + row];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) t += r < n ? v[r] : 0.f;
   return 1.0f / sqrtf(t / (float)H + eps);
+}
+
+// Data-parallel-primitive (DPP) lane moves within rows of 16 lanes: no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <- 7 - i within each half row
+constexpr int kDppMirror = 0x140;       // lane i <- 15 - i within each row
+constexpr int kDppRor8 = 0x128;         // lane i <- (i + 8) mod 16 within each row
+
+// Sum over the 16 lanes of each row; every lane of the row gets the same value.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  return v;
+}
+
+// Weight matrices [rows][cols] (rows % 16 == 0, cols % 32 == 0) are stored tile-major: each
+// 16-row x 32-column tile is one contiguous 512-element chunk laid out in the operand order of
+// v_mfma_f32_16x16x32_f16 (lane l = 16 * g + r holds row r, columns 8g..8g+7), and the chunks of
+// one 16-row band follow each other along the columns. A wave streaming a band therefore reads
+// whole contiguous kilobytes (BF16) and needs no LDS transpose for the matrix operand.
+__host__ __device__ __forceinline__ int64_t tiled_index(int64_t row, int64_t col, int64_t cols) {
+  return ((((row >> 4) * (cols >> 5) + (col >> 5)) << 9) + ((((col & 31) >> 3) * 16 + (row & 15)) << 3) +
+          (col & 7));
+}
+// Q8_0 scale of (row, 32-column block): [row band][block][row within band].
+__host__ __device__ __forceinline__ int64_t tiled_scale_index(int64_t row, int64_t blk, int64_t cols) {
+  return (((row >> 4) * (cols >> 5) + blk) << 4) + (row & 15);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -76,6 +140,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// FP32 -> FP16 conversions of MFMA operands go through one explicit instruction,
+// v_cvt_pkrtz_f16_f32 (round toward zero), never through a plain cast: the compiler is free to
+// lower a cast to different instructions in different kernels (a cast rounds ties to even, the
+// mixed-precision FMA forms fuse a preceding product), and every kernel that builds an operand
+// must produce the same bits for the same value.
+__device__ __forceinline__ f16x2 cvt_rtz2(float a, float b) {
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
 // Eight BF16 weights (one 16-byte load) -> eight FP16 MFMA operands. BF16 has 8 significant
 // bits, so the conversion is exact for |w| in [2^-17, 65504]; smaller magnitudes lose at most
 // 2^-25 absolutely.
@@ -84,33 +157,51 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16x8(uint4 v) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    r[2 * i] = (f16)__uint_as_float(w[i] << 16);
-    r[2 * i + 1] = (f16)__uint_as_float(w[i] & 0xFFFF0000u);
+    const f16x2 p = cvt_rtz2(__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xFFFF0000u));
+    r[2 * i] = p[0];
+    r[2 * i + 1] = p[1];
   }
   return r;
 }
 
-// Split an FP32 value into FP16 hi + lo with x = hi + lo up to 2^-22 relative (2^-25 absolute
-// near zero). Two FP16 MFMAs over (hi, lo) give a near-FP32 product with BF16/FP16 weights.
+// Split an FP32 value into FP16 hi + lo: hi = rtz(x), lo = rtz(x - hi) (the difference is exact
+// in FP32), so x = hi + lo to about 2^-20 relative (2^-24 absolute near zero). Two FP16 MFMAs over
+// (hi, lo) give a near-FP32 product with BF16/FP16 weights.
 __device__ __forceinline__ void split_f16(float x, f16& hi, f16& lo) {
-  hi = (f16)x;
-  lo = (f16)(x - (float)hi);
+  hi = cvt_rtz2(x, 0.f)[0];
+  lo = cvt_rtz2(x - (float)hi, 0.f)[0];
 }
 
 __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Wave-wide sum / max: DPP within each 16-lane row, then the four row results read as scalars
+// and combined in row order (the same value in every lane).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = row16_sum(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((a + b) + c) + d;
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
   return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = row16_max(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
 }  // namespace gqa

@@ -14,14 +14,12 @@
 // from the S^T accumulator layout: within each 32-key chunk a lane holds keys 4g..4g+3 and
 // 16+4g..16+4g+3 (g = lane / 16), and V^T is read from LDS in the same key order.
 //
-// Decode: one wave per (row, KV head, 32-position block), FP32 on the vector ALUs, four blocks
-// per workgroup; see attn_decode_kernel.
+// Decode: split-context attention in FP32 on the vector ALUs, then a chunk merge; see
+// attn_decode_kernel.
 #include "gqa_common.h"
 
 namespace gqa {
 
-constexpr int kDecodeChunk = 32;   // positions per decode wave (one KV block)
-constexpr int kPartStride = 132;   // floats per decode partial: m, l, pad, pad, o[128]
 
 template <int G, bool PSPLIT>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const float* __restrict__ q, int nq, int T, int pos0,
@@ -220,299 +218,309 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const float* __restri
   }
 }
 
-// Decode attention, one kernel per layer: grid (128-position chunk, KV head, row), four waves
-// per workgroup, one 32-position block per wave (the block table is read once per wave).
-//  1. q for the g query heads of the KV head: the fixed-order sum of the q|k|v projection's
-//     split partials, per-head RMSNorm, rotate-half RoPE at the row's position.
-//  2. The wave whose block holds the new position also builds its k (norm + RoPE) and v, rounds
-//     them to BF16, writes them through the block table, and uses those register values for
-//     that position.
-//  3. Scores, softmax and the value sum over the wave's keys in FP32; the four waves merge
-//     through LDS in wave order into one (max, sum, o) partial per chunk.
-//  4. The last workgroup of a (row, KV head) to finish (device-scope release/acquire fences
-//     around an atomic counter, which it resets) merges the chunk partials in chunk order and
-//     writes o / l as FP16 hi/lo operands of the o projection.
-// The q|k|v projection was taken of x * w_norm; its partials are scaled here by the row's 1/rms,
-// recomputed from the sum-of-squares partials the projection's prologue wrote.
-// The chunking depends only on the row's own context length, never on the batch.
+// Decode attention (split context), grid (chunk, KV head, row), four waves per workgroup.
+// A row's context [0, pos] is cut into chunks of decode_chunk_len(ctx) positions (a multiple of
+// 64 chosen from the row's own context length only, so a row gets the same chunks whether it is
+// evaluated alone or in a batch). A workgroup walks its chunk 64 positions at a time: wave w
+// takes 16 consecutive positions, lane (ks, dg) = (lane / 16, lane % 16) holds dims 8dg..8dg+7 of
+// positions ks, ks + 4, ks + 8, ks + 12, so one wave-wide 16-byte load covers four whole K (or V)
+// rows, 1 KiB of contiguous pool memory. Each 16-lane group keeps its own online-softmax state
+// (max, sum, value sum) for the g query heads of the KV head; the 16 states of the workgroup are
+// merged in LDS into one chunk partial (max, sum, o[128]) per head.
+//  1. q for the g query heads: the fixed-order sum of the q|k|v projection's split partials,
+//     times the row's 1/rms (recomputed from the sum-of-squares partials the projection's
+//     prologue wrote), per-head RMSNorm, rotate-half RoPE at the row's position, built once
+//     per workgroup in LDS with every global load of the step issued together.
+//  2. The workgroup whose chunk holds the new position also builds its k (norm + RoPE) and v,
+//     rounds them to BF16, writes them through the block table and uses the rounded values
+//     for that position.
+//  3. The last workgroup of a (row, KV head) to finish combines the chunk partials of its heads in
+//     chunk order (merge_head).
 constexpr int kDecodeWaves = 4;
-constexpr int kDecodeChunkPos = kDecodeChunk * kDecodeWaves;   // positions per workgroup
-constexpr int kMergeMaxChunks = 128;                            // 16,384 positions
+constexpr int kDecodeMaxChunks = 64;
+constexpr int kPartStride = 132;   // floats per chunk partial: m, l, pad, pad, o[128]
+
+__host__ __device__ __forceinline__ int decode_chunk_len(int ctx) {
+  return 64 * ((ctx + 64 * kDecodeMaxChunks - 1) / (64 * kDecodeMaxChunks));
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(uint4 v, float (&f)[8]) {
+  f[0] = bf16_bits_to_f32(v.x & 0xFFFF); f[1] = bf16_bits_to_f32(v.x >> 16);
+  f[2] = bf16_bits_to_f32(v.y & 0xFFFF); f[3] = bf16_bits_to_f32(v.y >> 16);
+  f[4] = bf16_bits_to_f32(v.z & 0xFFFF); f[5] = bf16_bits_to_f32(v.z >> 16);
+  f[6] = bf16_bits_to_f32(v.w & 0xFFFF); f[7] = bf16_bits_to_f32(v.w >> 16);
+}
+
+// Combine the chunk partials of one (row, query head) in chunk order: o = sum_c w_c o_c / sum_c
+// w_c l_c with w_c = 2^(m_c - max m). One wave; lane t owns dims 2t, 2t + 1. The result is
+// written as the FP16 hi/lo operand of the o projection, times out_scale.
+__device__ __forceinline__ void merge_head(const float* pp, int nchunk, int lane, float out_scale, f16* ohi,
+                                           f16* olo) {
+  const float2 ml = *(const float2*)(pp + (int64_t)min(lane, nchunk - 1) * kPartStride);
+  float2 ov[kDecodeMaxChunks];
+#pragma unroll
+  for (int cc = 0; cc < kDecodeMaxChunks; ++cc)
+    ov[cc] = *(const float2*)(pp + (int64_t)min(cc, nchunk - 1) * kPartStride + 4 + 2 * lane);
+  const float mv = lane < nchunk ? ml.x : -INFINITY;
+  const float M = wave_max(mv);
+  const float wt = lane < nchunk ? exp2f(mv - M) : 0.f;
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < kDecodeMaxChunks; ++cc) {
+    if (cc < nchunk) {
+      const float w = __shfl(wt, cc, 64);
+      L = fmaf(__shfl(ml.y, cc, 64), w, L);
+      o0 = fmaf(ov[cc].x, w, o0);
+      o1 = fmaf(ov[cc].y, w, o1);
+    }
+  }
+  const float inv = out_scale / L;
+  f16 h0, l0, h1, l1;
+  split_f16(o0 * inv, h0, l0);
+  split_f16(o1 * inv, h1, l1);
+  *(f16x2*)(ohi + 2 * lane) = f16x2{h0, h1};
+  *(f16x2*)(olo + 2 * lane) = f16x2{l0, l1};
+}
 
 template <int G>
 __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
     const float* __restrict__ qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* __restrict__ ss,
     int ss_n, int H, const uint16_t* __restrict__ wqn, const uint16_t* __restrict__ wkn, float eps,
     const float* __restrict__ rcos, const float* __restrict__ rsin, Rows rows, uint16_t* __restrict__ kpool,
-    uint16_t* __restrict__ vpool, float* __restrict__ part, int max_chunks, int* __restrict__ counters,
-    float out_scale, f16* __restrict__ ohi, f16* __restrict__ olo, int ldo) {
-  __shared__ float sm[kDecodeWaves][G], sl[kDecodeWaves][G];
-  __shared__ float so[kDecodeWaves][G][kHeadDim];
-  __shared__ float sw[G][kMergeMaxChunks];
-  __shared__ float sL[G][kMergeMaxChunks];
+    uint16_t* __restrict__ vpool, float* part, int* __restrict__ counters, float out_scale, f16* __restrict__ ohi,
+    f16* __restrict__ olo, int ldo) {
+  constexpr int NST = 4 * kDecodeWaves;                   // softmax states per workgroup
+  constexpr int NE = (G + 2) * kHeadDim;                  // q heads, then k and v of the new position
+  __shared__ float sraw[NE];                              // projection sums (times 1/rms)
+  __shared__ float sq[NE];                                // normed + rotated q (scaled), k; v
+  __shared__ float sm[NST][G], sl[NST][G];
+  __shared__ float so[NST][G][kHeadDim];
   __shared__ int s_last;
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int pos = rows.pos[b], ctx = pos + 1;
-  const int nchunk = (ctx + kDecodeChunkPos - 1) / kDecodeChunkPos;
+  const int CH = decode_chunk_len(ctx);
+  const int nchunk = (ctx + CH - 1) / CH;
   if (c >= nchunk) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ks = lane >> 4, dg = lane & 15;
-  const int blk = c * kDecodeWaves + wave;                 // logical 32-position block of this wave
-  const int kpos0 = blk * kDecodeChunk;
-  const bool active = kpos0 < ctx;
-  const float qscale = kLog2e * 0.08838834764831845f;
-  const float* qrow = qkvp + (int64_t)b * QKV;
-  // 1/rms of the normalised layer input: the projection was taken of x * w only
-  const float cin = inv_rms_from_ss(ss, ss_n, b, H, eps);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ks = lane >> 4, dg = lane & 15;
+  const int p_begin = c * CH, p_end = min(p_begin + CH, ctx);
+  const int niter = (p_end - p_begin + 63) / 64;
+  const bool owner = pos >= p_begin && pos < p_end;     // this chunk holds the new position
+  const int32_t* table = rows.table[b];
+  const uint16_t* kbase = kpool + (int64_t)kvh * kBlock * kHeadDim + dg * 8;
+  const uint16_t* vbase = vpool + (int64_t)kvh * kBlock * kHeadDim + dg * 8;
+  constexpr int64_t kBlockElems = (int64_t)kKvHeads * kBlock * kHeadDim;
 
-  // sum of the projection's split partials for 8 consecutive dims of one head row, times cin
-  auto head8 = [&](int hrow, float (&o)[8]) {
-    float t[8][8];
+  // K/V of iteration `it` for this lane: positions p0 + 4 st + ks, all in one 32-position block.
+  // The loads are unconditional (no branch between them): a position past the chunk reads a slot
+  // of a block the session owns (or of the pool's block 0 when the whole group is past it) and
+  // its value is discarded in step().
+  auto phys_of = [&](int it) { return table[min(p_begin + it * 64 + wave * 16, p_end - 1) >> 5]; };
+  auto load = [&](int it, int phys, uint4 (&kr)[4], uint4 (&vr)[4]) {
+    const int p0 = p_begin + it * 64 + wave * 16;
+    const int64_t off = (int64_t)phys * kBlockElems + (int64_t)(p0 & 31) * kHeadDim;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      if (s < nsplit) {
-        const float* p = qrow + (int64_t)s * pstride + hrow * kHeadDim + dg * 8;
-        float4 a0 = *(const float4*)p, a1 = *(const float4*)(p + 4);
-        t[s][0] = a0.x; t[s][1] = a0.y; t[s][2] = a0.z; t[s][3] = a0.w;
-        t[s][4] = a1.x; t[s][5] = a1.y; t[s][6] = a1.z; t[s][7] = a1.w;
-      }
+    for (int st = 0; st < 4; ++st) {
+      kr[st] = *(const uint4*)(kbase + off + (st * 4 + ks) * kHeadDim);
+      vr[st] = *(const uint4*)(vbase + off + (st * 4 + ks) * kHeadDim);
+    }
+  };
+  uint4 kA[4], vA[4], kB[4], vB[4];
+  // Issue order matters (vector loads complete in order): the block-table entry, the RoPE and
+  // norm constants, the projection partials, then the first K/V, so q is built while the K/V
+  // are in flight.
+  const int phys0 = phys_of(0);
+  nsplit = max(1, min(nsplit, 8));
+  const float cs = rcos[(int64_t)pos * 64 + lane], sn = rsin[(int64_t)pos * 64 + lane];
+  const float wq0 = bf16_bits_to_f32(wqn[lane]), wq1 = bf16_bits_to_f32(wqn[64 + lane]);
+  const float wk0 = bf16_bits_to_f32(wkn[lane]), wk1 = bf16_bits_to_f32(wkn[64 + lane]);
+
+  // 1. projection sums for the g q heads (and k, v in the owner): element e of the head rows
+  //    kvh*g .. (q), nq + kvh (k), nq + 8 + kvh (v); split partials summed in split order
+  {
+    const float* qrow = qkvp + (int64_t)b * QKV;
+    const int nel = owner ? NE : G * kHeadDim;
+    constexpr int NI = (NE + 64 * kDecodeWaves - 1) / (64 * kDecodeWaves);
+    float t[NI][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int i = 0; i < NI; ++i) {                       // every load first
+      const int e = i * 64 * kDecodeWaves + tid;
+      const int hrow = e < G * kHeadDim ? kvh * G + e / kHeadDim
+                                        : (e < (G + 1) * kHeadDim ? nq + kvh : nq + kKvHeads + kvh);
+      const float* p = qrow + (e < nel ? hrow * kHeadDim + (e % kHeadDim) : 0);
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) t[i][s2] = p[(int64_t)min(s2, nsplit - 1) * pstride];   // unconditional
+    }
+    load(0, phys0, kA, vA);
+    const float cin = inv_rms_from_ss(ss, ss_n, b, H, eps);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int e = i * 64 * kDecodeWaves + tid;
       float acc = 0.f;
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        if (s < nsplit) acc += t[s][e];
-      o[e] = __fmul_rn(acc, cin);
+      for (int s2 = 0; s2 < 8; ++s2) acc += s2 < nsplit ? t[i][s2] : 0.f;   // select, not a branch
+      if (e < nel) sraw[e] = __fmul_rn(acc, cin);
     }
-  };
-  // per-head RMSNorm over the 16 lanes of a key slot group, then RoPE: dims i < 64 pair with
-  // i + 64, which live in lane dg ^ 8 at the same e.
-  const float* cr = rcos + (int64_t)pos * 64;
-  const float* sr = rsin + (int64_t)pos * 64;
-  auto norm_rope = [&](float (&x)[8], const uint16_t* w) {
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    ss += __shfl_xor(ss, 4, 64);
-    ss += __shfl_xor(ss, 8, 64);
-    const float inv = 1.0f / sqrtf(ss / (float)kHeadDim + eps);
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * bf16_bits_to_f32(w[dg * 8 + e]);
-    const int i0 = (dg & 7) * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float partner = __shfl_xor(y[e], 8, 64);
-      float cs = cr[i0 + e], sn = sr[i0 + e];
-      x[e] = dg < 8 ? y[e] * cs - partner * sn : y[e] * cs + partner * sn;
+  }
+  __syncthreads();
+  // 2. per-head RMSNorm(128) and rotate-half RoPE at `pos`: wave w handles heads w, w + 4, ...;
+  //    lane t owns dims t and t + 64 (a RoPE pair). q is pre-scaled by log2(e)/sqrt(128).
+  {
+    const float qscale = kLog2e * 0.08838834764831845f;
+    const int nh = owner ? G + 1 : G;
+    for (int hh = wave; hh < nh; hh += kDecodeWaves) {
+      const float x0 = sraw[hh * kHeadDim + lane], x1 = sraw[hh * kHeadDim + 64 + lane];
+      const float inv = 1.0f / sqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)kHeadDim + eps);
+      const float y0 = x0 * inv * (hh < G ? wq0 : wk0), y1 = x1 * inv * (hh < G ? wq1 : wk1);
+      float r0 = y0 * cs - y1 * sn, r1 = y1 * cs + y0 * sn;
+      if (hh < G) {
+        r0 *= qscale;
+        r1 *= qscale;
+      } else {                                            // k: BF16 storage rounding
+        r0 = bf16_bits_to_f32(f32_to_bf16_rne(r0));
+        r1 = bf16_bits_to_f32(f32_to_bf16_rne(r1));
+      }
+      sq[hh * kHeadDim + lane] = r0;
+      sq[hh * kHeadDim + 64 + lane] = r1;
     }
-  };
-
-  // K/V loads of this wave's block first: they depend only on the block table
-  constexpr int STEPS = kDecodeChunk / 4;
-  uint4 kr[STEPS], vr[STEPS];
-  if (active) {
-    const int phys = rows.table[b][blk];
-    const uint16_t* kbp = kpool + (((int64_t)phys * kKvHeads + kvh) * kBlock) * kHeadDim + dg * 8;
-    const uint16_t* vbp = vpool + (((int64_t)phys * kKvHeads + kvh) * kBlock) * kHeadDim + dg * 8;
+    if (owner && tid < kHeadDim) sq[(G + 1) * kHeadDim + tid] = bf16_bits_to_f32(f32_to_bf16_rne(sraw[(G + 1) * kHeadDim + tid]));
+  }
+  __syncthreads();
+  // the new position's K/V into the pool, through the block table
+  if (owner && tid < 2 * kHeadDim / 8) {
+    const int kv = tid >> 4, d0 = (tid & 15) * 8;       // tid < 16: K, else V
+    const float* src = sq + (G + kv) * kHeadDim + d0;
+    uint32_t h[8];
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const int j = kpos0 + st * 4 + ks;
-      kr[st] = j < pos ? *(const uint4*)(kbp + (st * 4 + ks) * kHeadDim) : uint4{0, 0, 0, 0};
-      vr[st] = j < pos ? *(const uint4*)(vbp + (st * 4 + ks) * kHeadDim) : uint4{0, 0, 0, 0};
-    }
+    for (int e = 0; e < 8; ++e) h[e] = f32_to_bf16_rne(src[e]);
+    const int64_t off = (int64_t)table[pos >> 5] * kBlockElems + ((int64_t)kvh * kBlock + (pos & 31)) * kHeadDim + d0;
+    *(uint4*)((kv ? vpool : kpool) + off) =
+        uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
   }
   float qv[G][8];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    head8(kvh * G + hh, qv[hh]);
-    norm_rope(qv[hh], wqn);
+  for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[hh][e] *= qscale;
-  }
-  // the new position's K/V (only in the wave whose block holds it)
-  const bool owner = active && pos >= kpos0 && pos < kpos0 + kDecodeChunk;
-  uint4 knew = uint4{0, 0, 0, 0}, vnew = uint4{0, 0, 0, 0};
-  if (owner) {
-    float kx[8], vx[8];
-    head8(nq + kvh, kx);
-    norm_rope(kx, wkn);
-    head8(nq + kKvHeads + kvh, vx);
-    uint32_t kb16[8], vb16[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kb16[e] = f32_to_bf16_rne(kx[e]);
-      vb16[e] = f32_to_bf16_rne(vx[e]);
-    }
-    knew = uint4{kb16[0] | (kb16[1] << 16), kb16[2] | (kb16[3] << 16), kb16[4] | (kb16[5] << 16),
-                 kb16[6] | (kb16[7] << 16)};
-    vnew = uint4{vb16[0] | (vb16[1] << 16), vb16[2] | (vb16[3] << 16), vb16[4] | (vb16[5] << 16),
-                 vb16[6] | (vb16[7] << 16)};
-    if (ks == 0) {
-      const int phys = rows.table[b][pos >> 5];
-      const int64_t off = (((int64_t)phys * kKvHeads + kvh) * kBlock + (pos & 31)) * kHeadDim + dg * 8;
-      *(uint4*)(kpool + off) = knew;
-      *(uint4*)(vpool + off) = vnew;
-    }
-  }
+    for (int e = 0; e < 8; ++e) qv[hh][e] = sq[hh * kHeadDim + dg * 8 + e];
 
+  // 3. online softmax over the chunk, one state per 16-lane row group
   float m[G], l[G], o[G][8];
-  if (active) {
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      if (kpos0 + st * 4 + ks == pos) {
-        kr[st] = knew;
-        vr[st] = vnew;
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+  }
+  auto step = [&](int it, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
+    const int p0 = p_begin + it * 64 + wave * 16;
+    float kf[4][8], vf[4][8];
+    bool valid[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int p = p0 + st * 4 + ks;
+      valid[st] = p < p_end;
+      bf16x8_to_f32(kr[st], kf[st]);
+      bf16x8_to_f32(vr[st], vf[st]);
+      if (owner && p == pos) {                            // the new position, not yet in the pool
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kf[st][e] = sq[G * kHeadDim + dg * 8 + e];
+          vf[st][e] = sq[(G + 1) * kHeadDim + dg * 8 + e];
+        }
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vf[st][e] = valid[st] ? vf[st][e] : 0.f;
     }
-    float sc[G][STEPS];
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const bool valid = kpos0 + st * 4 + ks < ctx;
-      uint4 k4 = kr[st];
-      float kf[8] = {bf16_bits_to_f32(k4.x & 0xFFFF), bf16_bits_to_f32(k4.x >> 16), bf16_bits_to_f32(k4.y & 0xFFFF),
-                     bf16_bits_to_f32(k4.y >> 16),    bf16_bits_to_f32(k4.z & 0xFFFF), bf16_bits_to_f32(k4.z >> 16),
-                     bf16_bits_to_f32(k4.w & 0xFFFF), bf16_bits_to_f32(k4.w >> 16)};
+    for (int hh = 0; hh < G; ++hh) {
+      float sc[4];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
+      for (int st = 0; st < 4; ++st) {
         float d = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(qv[hh][e], kf[e], d);
-        d += __shfl_xor(d, 1, 64);
-        d += __shfl_xor(d, 2, 64);
-        d += __shfl_xor(d, 4, 64);
-        d += __shfl_xor(d, 8, 64);
-        sc[hh][st] = valid ? d : -INFINITY;
+        for (int e = 0; e < 8; ++e) d = fmaf(qv[hh][e], kf[st][e], d);
+        d = row16_sum(d);
+        sc[st] = valid[st] ? d : -INFINITY;
       }
-    }
+      const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      const float mn = fmaxf(m[hh], mx);
+      if (mn == -INFINITY) continue;                     // nothing visible yet in this group
+      const float alpha = exp2f(m[hh] - mn);
+      float lsum = l[hh] * alpha;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float mx = -INFINITY;
+      for (int e = 0; e < 8; ++e) o[hh][e] *= alpha;
 #pragma unroll
-      for (int st = 0; st < STEPS; ++st) mx = fmaxf(mx, sc[hh][st]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      float sum = 0.f;
+      for (int st = 0; st < 4; ++st) {
+        const float pr = exp2f(sc[st] - mn);
+        lsum += pr;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
-#pragma unroll
-      for (int st = 0; st < STEPS; ++st) {
-        float p = exp2f(sc[hh][st] - mx);
-        sum += p;
-        uint4 v4 = vr[st];
-        float vf[8] = {bf16_bits_to_f32(v4.x & 0xFFFF), bf16_bits_to_f32(v4.x >> 16), bf16_bits_to_f32(v4.y & 0xFFFF),
-                       bf16_bits_to_f32(v4.y >> 16),    bf16_bits_to_f32(v4.z & 0xFFFF), bf16_bits_to_f32(v4.z >> 16),
-                       bf16_bits_to_f32(v4.w & 0xFFFF), bf16_bits_to_f32(v4.w >> 16)};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(p, vf[e], o[hh][e]);
+        for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(pr, vf[st][e], o[hh][e]);
       }
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        o[hh][e] += __shfl_xor(o[hh][e], 16, 64);
-        o[hh][e] += __shfl_xor(o[hh][e], 32, 64);
-      }
-      m[hh] = mx;
-      l[hh] = sum;
+      l[hh] = lsum;
+      m[hh] = mn;
     }
-  } else {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      m[hh] = -INFINITY;
-      l[hh] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
-    }
+  };
+  for (int it = 0; it < niter; it += 2) {
+    if (it + 1 < niter) load(it + 1, phys_of(it + 1), kB, vB);
+    step(it, kA, vA);
+    if (it + 1 >= niter) break;
+    if (it + 2 < niter) load(it + 2, phys_of(it + 2), kA, vA);
+    step(it + 1, kB, vB);
   }
-  // merge the four waves (wave order) into the chunk partial
-  if (ks == 0) {
+
+  // 4. merge the 16 row-group states of the workgroup (state index 4 * wave + ks, in order)
+  const int si = wave * 4 + ks;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      if (dg == 0) {
-        sm[wave][hh] = m[hh];
-        sl[wave][hh] = l[hh];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) so[wave][hh][dg * 8 + e] = o[hh][e];
+  for (int hh = 0; hh < G; ++hh) {
+    if (dg == 0) {
+      sm[si][hh] = m[hh];
+      sl[si][hh] = l[hh];
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) so[si][hh][dg * 8 + e] = o[hh][e];
   }
   __syncthreads();
-  {
-    // thread -> (head, dim pair): G * 128 outputs over 256 threads
-    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 64 * kDecodeWaves) {
-      const int hh = idx / kHeadDim, d = idx % kHeadDim;
-      float M = -INFINITY;
+  for (int idx = tid; idx < G * kHeadDim; idx += 64 * kDecodeWaves) {
+    const int hh = idx / kHeadDim, d = idx % kHeadDim;
+    float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm[w][hh]);
-      float L = 0.f, O = 0.f;
+    for (int w = 0; w < NST; ++w) M = fmaxf(M, sm[w][hh]);
+    float L = 0.f, O = 0.f;
 #pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        const float wt = exp2f(sm[w][hh] - M);
-        L = fmaf(sl[w][hh], wt, L);
-        O = fmaf(so[w][hh][d], wt, O);
-      }
-      float* pp = part + (((int64_t)b * nq + kvh * G + hh) * max_chunks + c) * kPartStride;
-      if (d == 0) {
-        pp[0] = M;
-        pp[1] = L;
-      }
-      pp[4 + d] = O;
+    for (int w = 0; w < NST; ++w) {
+      const float wt = sm[w][hh] == -INFINITY ? 0.f : exp2f(sm[w][hh] - M);
+      L = fmaf(sl[w][hh], wt, L);
+      O = fmaf(so[w][hh][d], wt, O);
     }
+    float* pp = part + (((int64_t)b * nq + kvh * G + hh) * kDecodeMaxChunks + c) * kPartStride;
+    if (d == 0) {
+      pp[0] = M;
+      pp[1] = L;
+    }
+    pp[4 + d] = O;
   }
-  // last workgroup of this (row, KV head) merges the chunk partials
+  // 5. the last workgroup of this (row, KV head) to finish merges the chunk partials. Every wave
+  //    waits until its partial stores have completed, then one thread publishes them device-wide
+  //    (a device-scope release writes back this XCD's L2) and counts the workgroup in; the last
+  //    workgroup acquires (invalidating its stale cache lines) before any wave reads the other
+  //    workgroups' partials, and resets the count for the next call.
+  __builtin_amdgcn_s_waitcnt(0);          // vmcnt = lgkmcnt = 0: this wave's stores are done
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const int old = __hip_atomic_fetch_add(&counters[b * kKvHeads + kvh], 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
     s_last = old == nchunk - 1;
-    if (s_last) __threadfence();
+    if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
   if (!s_last) return;
-  // chunk maxima and sums into LDS (one thread per (head, chunk)), then per-head weights
-  for (int i = threadIdx.x; i < G * nchunk; i += 64 * kDecodeWaves) {
-    const int hh = i / nchunk, cc = i - hh * nchunk;
-    const float* q = part + (((int64_t)b * nq + kvh * G + hh) * max_chunks + cc) * kPartStride;
-    const float2 ml = *(const float2*)q;
-    sw[hh][cc] = ml.x;
-    sL[hh][cc] = ml.y;
+  if (wave < G) {
+    const int h = kvh * G + wave;
+    merge_head(part + ((int64_t)b * nq + h) * kDecodeMaxChunks * kPartStride, nchunk, lane, out_scale,
+               ohi + (int64_t)b * ldo + h * kHeadDim, olo + (int64_t)b * ldo + h * kHeadDim);
   }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    const int hh = threadIdx.x;
-    float M = -INFINITY;
-    for (int cc = 0; cc < nchunk; ++cc) M = fmaxf(M, sw[hh][cc]);
-    float L = 0.f;
-    for (int cc = 0; cc < nchunk; ++cc) {
-      const float wt = exp2f(sw[hh][cc] - M);
-      sw[hh][cc] = wt;
-      L = fmaf(sL[hh][cc], wt, L);
-    }
-    sL[hh][0] = L;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 64 * kDecodeWaves) {
-    const int hh = idx / kHeadDim, d = idx % kHeadDim;
-    const float* pp = part + ((int64_t)b * nq + kvh * G + hh) * max_chunks * kPartStride + 4 + d;
-    float O = 0.f;
-    int cc = 0;
-    for (; cc + 8 <= nchunk; cc += 8) {
-      float t[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = pp[(int64_t)(cc + u) * kPartStride];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) O = fmaf(t[u], sw[hh][cc + u], O);
-    }
-    for (; cc < nchunk; ++cc) O = fmaf(pp[(int64_t)cc * kPartStride], sw[hh][cc], O);
-    f16 hi, lo;
-    split_f16(O / sL[hh][0] * out_scale, hi, lo);
-    ohi[(int64_t)b * ldo + (kvh * G + hh) * kHeadDim + d] = hi;
-    olo[(int64_t)b * ldo + (kvh * G + hh) * kHeadDim + d] = lo;
-  }
-  if (threadIdx.x == 0) counters[b * kKvHeads + kvh] = 0;
+  if (tid == 0) counters[b * kKvHeads + kvh] = 0;
 }
 
 hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const int32_t* table, const uint16_t* kpool,
@@ -535,16 +543,17 @@ hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const in
 hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* ss,
                               int ss_n, int H, const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
                               const float* rsin, const Rows& rows, int B, int max_ctx, uint16_t* kpool,
-                              uint16_t* vpool, float* part, int max_chunks, int* counters, float out_scale, f16* ohi,
-                              f16* olo, int ldo, hipStream_t st) {
-  const int chunks = (max_ctx + kDecodeChunkPos - 1) / kDecodeChunkPos;
-  if (chunks > max_chunks || chunks > kMergeMaxChunks || nsplit < 1 || nsplit > 8) return hipErrorInvalidValue;
+                              uint16_t* vpool, float* part, int* counters, float out_scale, f16* ohi, f16* olo,
+                              int ldo, hipStream_t st) {
+  if (nsplit < 1 || nsplit > 8 || B < 1 || B > kMaxBatch || max_ctx < 1) return hipErrorInvalidValue;
+  const int CH = decode_chunk_len(max_ctx);
+  const int chunks = (max_ctx + CH - 1) / CH;          // rows with shorter contexts exit early
   dim3 grid(chunks, kKvHeads, B);
   const int G = nq / kKvHeads;
 #define DEC_LAUNCH(GG)                                                                                           \
   hipLaunchKernelGGL(attn_decode_kernel<GG>, grid, dim3(64 * kDecodeWaves), 0, st, qkvp, nsplit, pstride, QKV, nq, \
-                     ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, kpool, vpool, part, max_chunks, counters,       \
-                     out_scale, ohi, olo, ldo)
+                     ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, kpool, vpool, part, counters, out_scale, ohi, olo, \
+                     ldo)
   if (G == 4)
     DEC_LAUNCH(4);
   else if (G == 2)
@@ -554,5 +563,8 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
 #undef DEC_LAUNCH
   return hipGetLastError();
 }
+
+// floats of the chunk-partial buffer for B rows of nq heads
+int64_t attn_decode_part_floats(int nq) { return (int64_t)kMaxBatch * nq * kDecodeMaxChunks * kPartStride; }
 
 }  // namespace gqa

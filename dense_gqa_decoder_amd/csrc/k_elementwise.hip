@@ -21,8 +21,18 @@ __global__ void embed_kernel(const uint16_t* __restrict__ E, const int32_t* __re
     for (int i = threadIdx.x; i < H; i += blockDim.x) xr[i] = __builtin_nanf("");
     return;
   }
-  const uint16_t* er = E + (int64_t)id * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) xr[i] = bf16_bits_to_f32(er[i]);
+  // the embedding is tile-major (tiled_index): 8 consecutive columns are one 16-byte piece
+  for (int i = threadIdx.x * 8; i < H; i += blockDim.x * 8) {
+    const uint4 v = *(const uint4*)(E + tiled_index(id, i, H));
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float4 a, b;
+    a.x = bf16_bits_to_f32(w[0] & 0xFFFF); a.y = bf16_bits_to_f32(w[0] >> 16);
+    a.z = bf16_bits_to_f32(w[1] & 0xFFFF); a.w = bf16_bits_to_f32(w[1] >> 16);
+    b.x = bf16_bits_to_f32(w[2] & 0xFFFF); b.y = bf16_bits_to_f32(w[2] >> 16);
+    b.z = bf16_bits_to_f32(w[3] & 0xFFFF); b.w = bf16_bits_to_f32(w[3] >> 16);
+    *(float4*)(xr + i) = a;
+    *(float4*)(xr + i + 4) = b;
+  }
 }
 
 __device__ __forceinline__ float block_sum_256(float v, float* red) {

@@ -1,7 +1,9 @@
 // Prefill projections: C[t][n] = sum_k W[n][k] * x[t][k] on the gfx950 matrix cores.
 //
 // W is BF16 (or Q8_0: int8 quants with an fp16 scale per 32-weight block, Kipp Model
-// Support, "Quantization (Q8_0)") in row-major [N][K]. x is the FP32 activation, held as an
+// Support, "Quantization (Q8_0)") [N][K], tile-major (tiled_index): a workgroup's weight tile
+// for one K-step is BN/16 contiguous 2 KiB pieces, copied to LDS unchanged, and each 16x32
+// MFMA operand is one conflict-free 16-byte LDS read per lane. x is the FP32 activation, held as an
 // FP16 hi/lo pair so that two FP16 MFMAs (v_mfma_f32_16x16x32_f16) per K-step give a
 // near-FP32 product; accumulation is FP32. BF16 weights become FP16 operands exactly.
 // For Q8_0 each 32-wide K-step is one quant block: the int8 quants are exact FP16 operands,
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t* __restrict__ 
   constexpr int CX = BT * BK / 8 / 256;          // 16-byte activation chunks per thread (each of hi, lo)
   static_assert(CW >= 1 && CX >= 1, "tile too small");
   static_assert(BN <= 256, "one scale row per thread");
-  __shared__ f16 sW[BN * LD];
+  __shared__ f16 sW[BN * BK];                    // tile-major, as in memory: [band][k-chunk][lane][8]
   __shared__ f16 sXh[BT * LD];
   __shared__ f16 sXl[BT * LD];
   __shared__ float sD[Q8 ? BN * 2 : 1];          // Q8: block scales of this K-step (2 blocks x BN rows)
@@ -60,15 +62,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t* __restrict__ 
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < CW; ++i) {
-      int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
+      // unit c: band c / 128, then 128 consecutive 8-element pieces (two 32-wide chunks)
+      const int c = tid + 256 * i;
+      const int64_t at = ((int64_t)((n0 >> 4) + (c >> 7)) * (K >> 5) + (k0 >> 5)) * 512 + (c & 127) * 8;
       if (Q8)
-        rq[i] = *(const uint2*)(Wq + (int64_t)(n0 + row) * K + k0 + col);
+        rq[i] = *(const uint2*)(Wq + at);
       else
-        rw[i] = *(const uint4*)(W + (int64_t)(n0 + row) * K + k0 + col);
+        rw[i] = *(const uint4*)(W + at);
     }
     if (Q8 && tid < BN) {                          // scales of the two quant blocks of this K-step
-      rd0 = Wd[(int64_t)(k0 / 32) * N + n0 + tid];           // block-major scales [K/32][N]
-      rd1 = Wd[(int64_t)(k0 / 32 + 1) * N + n0 + tid];
+      const int64_t at = ((int64_t)((n0 >> 4) + (tid >> 4)) * (K >> 5) + (k0 >> 5)) * 16 + (tid & 15);
+      rd0 = Wd[at];
+      rd1 = Wd[at + 16];
     }
 #pragma unroll
     for (int i = 0; i < CX; ++i) {
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t* __restrict__ 
   auto sstore = [&]() {
 #pragma unroll
     for (int i = 0; i < CW; ++i) {
-      int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
+      const int c = tid + 256 * i;
       f16x8 v;
       if (Q8) {
         uint32_t lo = rq[i].x, hi = rq[i].y;
@@ -99,7 +104,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t* __restrict__ 
       } else {
         v = bf16x8_to_f16x8(rw[i]);
       }
-      *(f16x8*)&sW[row * LD + col] = v;
+      *(f16x8*)&sW[c * 8] = v;
     }
     if (Q8 && tid < BN) {
       sD[tid * 2] = (float)rd0;
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t* __restrict__ 
       const int koff = kk * 32 + (lane >> 4) * 8;
       f16x8 a[TN], bh[TT], bl[TT];
 #pragma unroll
-      for (int i = 0; i < TN; ++i) a[i] = *(const f16x8*)&sW[(wn + i * 16 + r16) * LD + koff];
+      for (int i = 0; i < TN; ++i) a[i] = *(const f16x8*)&sW[((((wn >> 4) + i) * 2 + kk) * 64 + lane) * 8];
 #pragma unroll
       for (int j = 0; j < TT; ++j) {
         bh[j] = *(const f16x8*)&sXh[(wt + j * 16 + r16) * LD + koff];

@@ -1,7 +1,8 @@
 // Decode projections for 1..32 token rows: P[s][b][n] = sum_{k in split s} W[n][k] * x[b][k].
 //
-// HBM-streaming matvec: each wave owns a 16-row weight tile and streams it over the
-// workgroup's K-split with 16-byte loads in stages of eight 32-wide K-steps, double-buffered so
+// HBM-streaming matvec: each wave owns a 16-row weight band (tile-major, so the band is one
+// contiguous stretch of memory and every wave-wide load is a whole kilobyte) and streams it over
+// the workgroup's K-split with 16-byte loads in stages of eight 32-wide K-steps, double-buffered so
 // the next stage's weight loads are in flight during the current stage's MFMAs, and multiplies
 // them on the matrix cores against the token rows as the 16-wide N side
 // (v_mfma_f32_16x16x32_f16, FP16 hi/lo activations, FP32 accumulate); the four waves of a
@@ -13,8 +14,8 @@
 // Split-K (Kipp Roadmap, status v0.0.4: the split-K partial buffer has its own constant): each
 // split writes a partial P[s][b][n]; consumers sum the splits in a fixed order. Q8_0 weights
 // (Kipp Model Support, "Quantization (Q8_0)") take one MFMA per 32-weight quant block into a
-// fresh accumulator, scaled by the block's fp16 scale in FP32; scales are stored block-major
-// ([K/32][N]) so a lane's four row scales are one 8-byte load.
+// fresh accumulator, scaled by the block's fp16 scale in FP32; the 16 scales of a tile are
+// contiguous, so a lane's four row scales are one 8-byte load.
 //
 // For B <= 4 the activation rows of the workgroup's K range are built in LDS by a prologue that
 // performs the producer's elementwise step (X_RAW copy, X_RESID residual add times the norm
@@ -145,7 +146,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* _
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t rowoff = (int64_t)(n0 + r16) * K;
+  // the wave's 16-row band is contiguous (tile-major weights): chunk ks at band + ks * 512
+  const int64_t band = (int64_t)(n0 >> 4) * (K >> 5);
   struct Buf {
     uint4 wv[U];
     uint2 qv[U];
@@ -156,11 +158,12 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* _
     for (int u = 0; u < U; ++u) {
       const int kk = k + u * 32;
       const bool ok = kk < ke && has_tile;
+      const int64_t chunk = band + (kk >> 5);
       if (Q8) {
-        f.qv[u] = ok ? *(const uint2*)(Wq + rowoff + kk + g4 * 8) : uint2{0, 0};
-        f.sc[u] = ok ? *(const uint2*)(Wd + (int64_t)(kk / 32) * N + n0 + g4 * 4) : uint2{0, 0};
+        f.qv[u] = ok ? *(const uint2*)(Wq + chunk * 512 + lane * 8) : uint2{0, 0};
+        f.sc[u] = ok ? *(const uint2*)(Wd + chunk * 16 + g4 * 4) : uint2{0, 0};
       } else {
-        f.wv[u] = ok ? *(const uint4*)(W + rowoff + kk + g4 * 8) : uint4{0, 0, 0, 0};
+        f.wv[u] = ok ? *(const uint4*)(W + chunk * 512 + lane * 8) : uint4{0, 0, 0, 0};
       }
     }
   };

@@ -1,0 +1,314 @@
+// Decode projections for a few token rows with the whole K range in one workgroup.
+//
+// Y[b][n] = sum_k W[n][k] * x[b][k] for B <= 4 rows whose FP16 hi/lo operand rows fit in LDS.
+// A workgroup owns NBW 16-row weight bands; the K range of a band is cut into S = NWB equal
+// ranges, one wave each (the same ranges as the split-K matvec in k_gemv.hip), so every wave
+// streams one contiguous stretch of the tile-major weights with 16-byte loads, U K-steps per
+// stage with two stages in flight, and multiplies them on the matrix cores
+// (v_mfma_f32_16x16x32_f16, FP16 hi/lo activations, FP32 accumulate). The S range partials of a
+// band are then summed in LDS in range order, starting from zero -- the same additions the
+// split-K path's consumers perform on its global partials -- so a row gives bit-identical
+// results on both paths (Kipp Roadmap, status v0.0.2: batched evaluation equals isolated).
+//
+// Operand prologues (the whole row is read by every workgroup; it is small and L2-resident):
+//   XF_RAW  copy FP16 hi/lo rows from global memory.
+//   XF_NORM the RMSNorm input of a projection: x * w_norm, split hi/lo; the sum of squares of x
+//           per K range is formed with the split-K path's element-to-thread mapping and order
+//           (thread t of a 256-thread group takes elements t + 256 j of the range, then the
+//           wave sums, then the four waves in order); workgroup 0 publishes the range sums in
+//           ss_out[range][row] for later consumers. The 1/rms factor is a per-row scalar applied
+//           after the projection (by the epilogue or by the consumer).
+// Epilogues:
+//   EPI_STORE  y = sum (q|k|v, lm_head; optional argmax candidates per band)
+//   EPI_ADD    y = y + sum * yscale (residual stream update after o and down)
+//   EPI_SWIGLU bands 2j, 2j+1 are gate and up of features 16j..16j+15: m = silu(g c) * (u c),
+//              c = 1/rms of the layer input, written as FP16 hi/lo rows for the down projection.
+#include "gqa_common.h"
+
+namespace gqa {
+
+constexpr int kFullMaxB = 4;
+constexpr int kFullMaxLds = 64 * 1024;   // operand rows (hi + lo) in LDS
+
+template <bool Q8, int NWB, int NBW, int U, int MODE, int EPI, int MAXB>
+__global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
+  constexpr int NT = 64 * NWB * NBW;
+  constexpr int S = NWB;
+  extern __shared__ f16 sx[];                         // [2][B][K] (+ one padding piece)
+  __shared__ f32x4 red[NBW][NWB][64];
+  __shared__ float sred[kFullMaxB][8][4];
+  __shared__ float sinv[kFullMaxB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bw = wave / NWB, kp = wave % NWB;
+  const int band = blockIdx.x * NBW + bw;
+  const int K = a.K, B = a.B, KS = K >> 5;
+  const int s0 = kp * (KS / S), s1 = s0 + KS / S;
+  const int r16 = lane & 15, g4 = lane >> 4;
+
+  // weight stream of this wave: band `band`, K-steps [s0, s1)
+  const int64_t chunk0 = (int64_t)band * KS;
+  struct Buf {
+    uint4 w[U];
+    uint2 q[U];
+    uint2 sc[U];
+  };
+  auto fetch = [&](Buf& f, int s) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t ch = chunk0 + min(s + u, s1 - 1);     // unconditional: no branch between loads
+      if (Q8) {
+        f.q[u] = *(const uint2*)(a.Wq + ch * 512 + lane * 8);
+        f.sc[u] = *(const uint2*)(a.Wd + ch * 16 + g4 * 4);
+      } else {
+        f.w[u] = *(const uint4*)(a.W + ch * 512 + lane * 8);
+      }
+    }
+  };
+  Buf b0, b1;
+  fetch(b0, s0);
+  fetch(b1, s0 + U);
+
+  // ---- operand rows into LDS: [0][b][k] = hi, [1][b][k] = lo
+  const int BK = B * K;
+  if constexpr (MODE == XF_RAW) {
+    constexpr int CMAX = (MAXB == 1 ? kFullMaxLds / 4 : kFullMaxLds) / 16 / NT;
+    const int npiece = 2 * BK / 8;
+    uint4 v[CMAX];
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) {
+      const int c = min(tid + i * NT, npiece - 1);
+      const int hl = c >= BK / 8, rem = c - hl * (BK / 8), b = rem / (K / 8), q = rem - b * (K / 8);
+      v[i] = *(const uint4*)((hl ? a.xlo : a.xhi) + (int64_t)b * a.ldx + q * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) *(uint4*)(sx + (int64_t)min(tid + i * NT, npiece) * 8) = v[i];
+  } else {
+    // thread (g, t): ranges r = g, g + G, ...; elements t + 256 j of each range
+    constexpr int G = NT >= 256 ? NT / 256 : 1;
+    constexpr int P = S / G;                          // ranges per 256-thread group
+    constexpr int JMAX = (4096 / S + 255) / 256;      // K <= 4096 for normed inputs
+    const int g = tid >> 8, t = tid & 255;
+    const int klen = K / S;
+    float xv[MAXB][P][JMAX], wv[P][JMAX];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int j = 0; j < JMAX; ++j) {                // every load first, unconditional
+        const int r = p * G + g, off = min(t + 256 * j, klen - 1);
+        wv[p][j] = bf16_bits_to_f32(a.nw[r * klen + off]);
+#pragma unroll
+        for (int b = 0; b < MAXB; ++b) xv[b][p][j] = a.xres[(int64_t)min(b, B - 1) * K + r * klen + off];
+      }
+#pragma unroll
+    for (int b = 0; b < MAXB; ++b) {
+      if (b >= B) break;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int r = p * G + g;
+        float ssq = 0.f;
+#pragma unroll
+        for (int j = 0; j < JMAX; ++j) {
+          const int off = t + 256 * j;
+          if (off < klen) {
+            const float x = xv[b][p][j];
+            f16 h, l;
+            split_f16(__fmul_rn(x, wv[p][j]), h, l);
+            sx[(int64_t)b * K + r * klen + off] = h;
+            sx[(int64_t)BK + b * K + r * klen + off] = l;
+            ssq = __fadd_rn(ssq, __fmul_rn(x, x));
+          }
+        }
+        ssq = wave_sum(ssq);
+        if (lane == 0) sred[b][r][(t >> 6)] = ssq;
+      }
+    }
+  }
+  __syncthreads();
+  if constexpr (MODE == XF_NORM) {
+    if (tid < kFullMaxB) {
+      const int b = tid;
+      float tot = 0.f;
+      for (int r = 0; r < S && b < B; ++r) {
+        const float sr = __fadd_rn(__fadd_rn(__fadd_rn(sred[b][r][0], sred[b][r][1]), sred[b][r][2]), sred[b][r][3]);
+        if (blockIdx.x == 0 && a.ss_out) a.ss_out[r * 32 + b] = sr;
+        tot += sr;
+      }
+      sinv[b] = 1.0f / sqrtf(tot / (float)K + a.eps);
+    }
+    __syncthreads();
+  }
+
+  // ---- stream the weights
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const bool xvalid = r16 < B;
+  const f16* xh = sx + (int64_t)(xvalid ? r16 : 0) * K + g4 * 8;
+  const f16* xl = xh + BK;
+  auto compute = [&](const Buf& f, int s) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s + u < s1) {
+        const int kk = (s + u) * 32;
+        const f16x8 bh = xvalid ? *(const f16x8*)(xh + kk) : f16x8{};
+        const f16x8 bl = xvalid ? *(const f16x8*)(xl + kk) : f16x8{};
+        f16x8 w;
+        if (Q8) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w[e] = (f16)(float)(int8_t)((f.q[u].x >> (8 * e)) & 0xFF);
+            w[4 + e] = (f16)(float)(int8_t)((f.q[u].y >> (8 * e)) & 0xFF);
+          }
+          const float sc[4] = {(float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x & 0xFFFF)),
+                               (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x >> 16)),
+                               (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y & 0xFFFF)),
+                               (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y >> 16))};
+          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+          p = mfma16(w, bh, p);
+          p = mfma16(w, bl, p);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc[r], p[r], acc[r]);
+        } else {
+          w = bf16x8_to_f16x8(f.w[u]);
+          acc = mfma16(w, bh, acc);
+          acc = mfma16(w, bl, acc);
+        }
+      }
+    }
+  };
+  for (int s = s0; s < s1; s += 2 * U) {
+    compute(b0, s);
+    if (s + U >= s1) break;
+    if (s + 2 * U < s1) fetch(b0, s + 2 * U);
+    compute(b1, s + U);
+    if (s + 3 * U < s1) fetch(b1, s + 3 * U);
+  }
+
+  // ---- range partials summed in range order
+  red[bw][kp][lane] = acc;
+  __syncthreads();
+  // acc[r] of lane (r16, g4) = row 16 band + 4 g4 + r of token row r16
+  if constexpr (EPI == EPI_SWIGLU) {
+    static_assert(NBW == 2, "gate and up bands");
+    if (wave != 0) return;
+    f32x4 gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NWB; ++w) {
+      const f32x4 o0 = red[0][w][lane], o1 = red[1][w][lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        gs[r] += o0[r];
+        us[r] += o1[r];
+      }
+    }
+    if (r16 < B) {
+      const float c = sinv[r16];
+      const int f = blockIdx.x * 16 + g4 * 4;          // band pair blockIdx.x: features 16 j ..
+      f16x4 hv, lv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gg = __fmul_rn(gs[r], c), uu = __fmul_rn(us[r], c);
+        const float m = __fmul_rn(__fdiv_rn(gg, 1.0f + expf(-gg)), uu);
+        f16 h, l;
+        split_f16(m, h, l);
+        hv[r] = h;
+        lv[r] = l;
+      }
+      *(f16x4*)(a.mhi + (int64_t)r16 * a.ldm + f) = hv;
+      *(f16x4*)(a.mlo + (int64_t)r16 * a.ldm + f) = lv;
+    }
+    return;
+  }
+  if (kp != 0) return;
+  f32x4 tsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < NWB; ++w) {
+    const f32x4 o = red[bw][w][lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tsum[r] += o[r];
+  }
+  const int n = band * 16 + g4 * 4;
+  if (r16 < B) {
+    float* dst = a.y + (int64_t)r16 * a.ldy + n;
+    if (EPI == EPI_ADD) {
+      const float4 o = *(const float4*)dst;
+      *(float4*)dst = make_float4(__fadd_rn(o.x, __fmul_rn(tsum[0], a.yscale)), __fadd_rn(o.y, __fmul_rn(tsum[1], a.yscale)),
+                                  __fadd_rn(o.z, __fmul_rn(tsum[2], a.yscale)), __fadd_rn(o.w, __fmul_rn(tsum[3], a.yscale)));
+    } else {
+      *(float4*)dst = make_float4(tsum[0], tsum[1], tsum[2], tsum[3]);
+    }
+  }
+  if (EPI == EPI_STORE && a.cand) {
+    // argmax candidate of the band's 16 rows for token row r16: (value, index), lowest index on ties
+    float bv = tsum[0];
+    int bi = n;
+#pragma unroll
+    for (int r = 1; r < 4; ++r)
+      if (tsum[r] > bv) {
+        bv = tsum[r];
+        bi = n + r;
+      }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (g4 == 0 && r16 < B) a.cand[(int64_t)r16 * (a.N / 16) + band] = make_float2(bv, __int_as_float(bi));
+  }
+}
+
+// Whether the whole-K path can take B rows of a K-wide operand.
+bool gemv_full_fits(int K, int B) { return B >= 1 && B <= kFullMaxB && (size_t)4 * B * K + 16 <= kFullMaxLds; }
+
+// S = waves per band = K ranges; EPI_SWIGLU takes band pairs (gate, up). Requires
+// K % (32 * S) == 0, N % (16 * bands per workgroup) == 0, and for XF_NORM K <= 4096.
+hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStream_t st) {
+  if (!gemv_full_fits(a.K, a.B) || a.K % (32 * S) != 0 || a.N % 16 != 0) return hipErrorInvalidValue;
+  if (mode == XF_NORM && (a.K > 4096 || !a.xres || !a.nw)) return hipErrorInvalidValue;
+  const bool q8 = a.Wq != nullptr;
+  const size_t shm = (size_t)4 * a.B * a.K + 16;
+#define FULL(Q, NWB, NBW, U, MO, EP)                                                                          \
+  do {                                                                                                        \
+    if (a.B == 1 && (size_t)4 * a.K + 16 <= kFullMaxLds / 4)                                                  \
+      hipLaunchKernelGGL((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, 1>), dim3(a.N / 16 / NBW),                 \
+                         dim3(64 * NWB * NBW), shm, st, a);                                                    \
+    else                                                                                                      \
+      hipLaunchKernelGGL((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, kFullMaxB>), dim3(a.N / 16 / NBW),         \
+                         dim3(64 * NWB * NBW), shm, st, a);                                                    \
+  } while (0)
+#define BY_Q8(NWB, NBW, U, MO, EP) \
+  do {                             \
+    if (q8)                        \
+      FULL(true, NWB, NBW, U, MO, EP); \
+    else                           \
+      FULL(false, NWB, NBW, U, MO, EP); \
+  } while (0)
+  if (epi == EPI_SWIGLU) {
+    if (mode != XF_NORM || S != 4 || a.N % 32 != 0) return hipErrorInvalidValue;
+    BY_Q8(4, 2, 4, XF_NORM, EPI_SWIGLU);
+  } else if (S == 8) {
+    if (mode == XF_NORM) {
+      if (epi != EPI_STORE) return hipErrorInvalidValue;
+      BY_Q8(8, 1, 4, XF_NORM, EPI_STORE);
+    } else if (epi == EPI_ADD) {
+      BY_Q8(8, 1, 4, XF_RAW, EPI_ADD);
+    } else {
+      BY_Q8(8, 1, 4, XF_RAW, EPI_STORE);
+    }
+  } else if (S == 1) {
+    if (mode != XF_RAW || epi != EPI_STORE || q8) return hipErrorInvalidValue;
+    if (a.N % 64 == 0)
+      FULL(false, 1, 4, 8, XF_RAW, EPI_STORE);
+    else
+      FULL(false, 1, 1, 8, XF_RAW, EPI_STORE);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef BY_Q8
+#undef FULL
+  return hipGetLastError();
+}
+
+}  // namespace gqa

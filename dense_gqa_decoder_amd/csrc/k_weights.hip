@@ -4,10 +4,12 @@
 // u = SplitMix64 finaliser of (key + (i+1) * 0x9E3779B97F4A7C15) (Steele, Lea and Flood,
 // OOPSLA 2014), S = sum of the four 16-bit fields of u, z = S - 131070, and
 // w = bf16_rne(fp32(z) * scale) with one FP32 multiply. The value lands at the physical row
-// given by the layout mode (plain with a row offset, or the 16-row gate/up interleave).
+// given by the layout mode (plain with a row offset, or the 16-row gate/up interleave), stored
+// tile-major (tiled_index).
 //
 // Q8_0 (Kipp Model Support, "Quantization (Q8_0)"): 32-weight blocks along a row, an fp16
-// scale and 32 int8 quants (stored here as an int8 matrix plus a block-major scale matrix). d = amax / 127 (FP32 division), scale = fp16_rne(d),
+// scale and 32 int8 quants (stored here as a tile-major int8 matrix plus a scale array indexed by
+// tiled_scale_index). d = amax / 127 (FP32 division), scale = fp16_rne(d),
 // q = clamp(round_half_away(w / d), -127, 127), and q = 0 when d = 0.
 #include "gqa_common.h"
 
@@ -33,7 +35,7 @@ __global__ void gen_weights_kernel(uint16_t* __restrict__ dst, uint64_t key, int
     float w = __fmul_rn(z, scale);
     int64_t r = i / cols, c = i - r * cols;
     int64_t pr = mode == 0 ? row_off + r : (mode == 1 ? 32 * (r / 16) + (r % 16) : 32 * (r / 16) + 16 + (r % 16));
-    dst[pr * cols + c] = f32_to_bf16_rne(w);
+    dst[tiled_index(pr, c, cols)] = f32_to_bf16_rne(w);
   }
 }
 
@@ -42,29 +44,31 @@ __global__ void fill_u16_kernel(uint16_t* __restrict__ dst, int64_t n, uint16_t 
     dst[i] = v;
 }
 
-// One thread per 32-weight block of a BF16 matrix [rows][cols] -> q int8 [rows][cols] and the
-// fp16 scales block-major: d[blk][row] (cols/32 x rows).
+// One thread per 32-weight block (row, blk) of a tile-major BF16 matrix [rows][cols] -> the
+// tile-major int8 quants at the same element positions and the scale at tiled_scale_index.
 __global__ void quantize_q8_0_kernel(const uint16_t* __restrict__ w, int8_t* __restrict__ q, f16* __restrict__ d,
                                      int64_t rows, int64_t cols) {
   int64_t nb = rows * (cols / 32);
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += (int64_t)gridDim.x * blockDim.x) {
-    const uint16_t* src = w + b * 32;
+    const int64_t row = b / (cols / 32), blk = b - row * (cols / 32);
+    int64_t at[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) at[g] = tiled_index(row, blk * 32 + g * 8, cols);   // 8 contiguous columns each
     float v[32];
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      v[i] = bf16_bits_to_f32(src[i]);
+      v[i] = bf16_bits_to_f32(w[at[i / 8] + i % 8]);
       amax = fmaxf(amax, fabsf(v[i]));
     }
     float dd = __fdiv_rn(amax, 127.0f);
-    const int64_t row = b / (cols / 32), blk = b - row * (cols / 32);
-    d[blk * rows + row] = (f16)dd;
+    d[tiled_scale_index(row, blk, cols)] = (f16)dd;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       float r = dd == 0.f ? 0.f : __fdiv_rn(v[i], dd);
       float qi = roundf(r);                      // half away from zero
       qi = fminf(fmaxf(qi, -127.f), 127.f);
-      q[b * 32 + i] = (int8_t)(int)qi;
+      q[at[i / 8] + i % 8] = (int8_t)(int)qi;
     }
   }
 }

@@ -40,14 +40,17 @@ hipError_t launch_gemm(int epi, const uint16_t* W, const int8_t* Wq, const f16* 
 hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const XSrc& xs, int B,
                        int nsplit, float* P, int64_t part_stride, int ldp, float2* cand, hipStream_t st);
 hipError_t launch_rows(const XSrc& xs, int K, int nsplit, int B, f16* yhi, f16* ylo, int ldy, hipStream_t st);
+bool gemv_full_fits(int K, int B);
+hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStream_t st);
 hipError_t launch_final_norm(const XSrc& xs, int B, f16* yhi, f16* ylo, int ldy, hipStream_t st);
 hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const int32_t* table, const uint16_t* kpool,
                                const uint16_t* vpool, float out_scale, f16* ohi, f16* olo, int ldo, hipStream_t st);
 hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* ss,
                               int ss_n, int H, const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
                               const float* rsin, const Rows& rows, int B, int max_ctx, uint16_t* kpool,
-                              uint16_t* vpool, float* part, int max_chunks, int* counters, float out_scale, f16* ohi,
-                              f16* olo, int ldo, hipStream_t st);
+                              uint16_t* vpool, float* part, int* counters, float out_scale, f16* ohi, f16* olo,
+                              int ldo, hipStream_t st);
+int64_t attn_decode_part_floats(int nq);
 }  // namespace gqa
 
 using namespace gqa;
@@ -101,7 +104,6 @@ struct gqa_model {
   gqa_model_desc d{};
   int dev = 0, cu = 0, R = 0;
   int QKV = 0, QD = 0;          // fused q|k|v rows, attention width
-  int max_chunks = 0;
   int s_qkv = 1, s_o = 1, s_gu = 1, s_d = 1;  // decode split-K counts
   std::vector<LayerW> L;
   uint16_t *embed = nullptr, *lm_head = nullptr, *final_norm = nullptr;
@@ -175,16 +177,6 @@ int check_desc(const gqa_model_desc* d) {
   return GQA_OK;
 }
 
-// Smallest split count >= want (at most 8) with K % (32 * s) == 0, else the largest below.
-int pick_split(int K, int want) {
-  want = std::max(1, std::min(want, 8));
-  for (int s = want; s <= 8; ++s)
-    if (K % (32 * s) == 0) return s;
-  for (int s = want; s > 1; --s)
-    if (K % (32 * s) == 0) return s;
-  return 1;
-}
-
 // Generator tensor ids: embedding 0; layer l, kind j (attn_norm, q, k, v, q_norm, k_norm, o,
 // ffn_norm, gate, up, down) -> 1 + 11 l + j; final norm 1 + 11 L; lm_head 2 + 11 L.
 uint64_t tensor_key(uint64_t seed, int L, int kind, int layer) {
@@ -227,21 +219,13 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   m->QD = NQ * kHeadDim;
   m->QKV = m->QD + 2 * kKvHeads * kHeadDim;
   m->R = d.max_round_tokens > 0 ? d.max_round_tokens : std::max(64, m->cu * 8);
-  m->max_chunks = (d.max_positions + 127) / 128;   // decode attention: 128 positions per chunk
-  // split-K counts of the decode matvecs: enough workgroups (about 2 per CU) to stream weights
-  // from every CU; fixed per model so every row sums its splits in the same order
-  // at least ~1.5 workgroups (four 16-row tiles each) per CU for every matvec, and K ranges of
-  // at most 2560 (the prologue of a workgroup builds its own K range of the operand rows)
-  const int want_wg = 3 * m->cu / 2;
-  auto split_for = [&](int K, int N) {
-    const int wgs = (N / 16 + 3) / 4;
-    int want = std::max((want_wg + wgs - 1) / wgs, (K + 2559) / 2560);
-    return pick_split(K, want);
-  };
-  m->s_qkv = split_for(H, m->QKV);
-  m->s_o = split_for(m->QD, H);
-  m->s_gu = split_for(H, 2 * F);
-  m->s_d = split_for(F, H);
+  // K ranges of the decode matvecs, fixed per model and shared by the whole-K path (one wave
+  // per range) and the split-K path (one workgroup column per range), so every row sums the
+  // same range partials in the same order on both paths
+  m->s_qkv = 8;
+  m->s_o = 8;
+  m->s_gu = 4;
+  m->s_d = (F / 32) % 8 == 0 ? 8 : 4;
   const bool q8 = d.scheme == GQA_SCHEME_Q8_0;
   int64_t* wb = &m->weight_bytes;
 
@@ -301,7 +285,7 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   m->part_floats = (int64_t)8 * kMaxBatch * std::max(std::max(m->QKV, 2 * F), H);
   ALLOC(m->part, m->part_floats, sb);
   ALLOC(m->part2, m->part_floats, sb);
-  ALLOC(m->apart, (int64_t)kMaxBatch * NQ * m->max_chunks * 132, sb);
+  ALLOC(m->apart, attn_decode_part_floats(NQ), sb);
   ALLOC(m->counters, kMaxBatch * kKvHeads, sb);
   ALLOC(m->ss, 2 * 8 * 32, sb);
   ALLOC(m->ids_dev, std::max(d.max_positions, kMaxBatch), sb);
@@ -597,6 +581,53 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
     return launch_gemv(W, Wq, Wd, K, N, raw_src(hi, lo, K), B, nsplit, P, pstride, ldp, nullptr, st);
   };
 
+  // Whole-K path (few rows): the residual stream xa is final after every projection, no split
+  // partials; bit-identical per row to the split-K path below.
+  if (gemv_full_fits(std::max(std::max(H, QD), F), B)) {
+    auto fa = [&]() {
+      FullArgs a{};
+      a.B = B;
+      a.eps = eps;
+      return a;
+    };
+    for (int l = 0; l < d.n_layers; ++l) {
+      const LayerW& w = m->L[l];
+      FullArgs q = fa();
+      q.W = w.wqkv; q.Wq = w.qqkv; q.Wd = w.sqkv; q.K = H; q.N = QKV;
+      q.xres = xa; q.nw = w.attn_norm; q.ss_out = ss_qkv; q.y = P0; q.ldy = QKV;
+      LAUNCH(launch_gemv_full(XF_NORM, EPI_STORE, m->s_qkv, q, st));
+      LAUNCH(launch_attn_decode(P0, 1, pstride, QKV, NQ, ss_qkv, m->s_qkv, H, w.q_norm, w.k_norm, eps, m->rcos,
+                                m->rsin, rows, B, max_ctx, w.kpool, w.vpool, m->apart, m->counters, kAttnOutScale, m->oh, m->ol, QD,
+                                st));
+      FullArgs o = fa();
+      o.W = w.wo; o.Wq = w.qo; o.Wd = w.so; o.K = QD; o.N = H;
+      o.xhi = m->oh; o.xlo = m->ol; o.ldx = QD; o.y = xa; o.ldy = H; o.yscale = 1.f / kAttnOutScale;
+      LAUNCH(launch_gemv_full(XF_RAW, EPI_ADD, m->s_o, o, st));
+      FullArgs g = fa();
+      g.W = w.wgu; g.Wq = w.qgu; g.Wd = w.sgu; g.K = H; g.N = 2 * F;
+      g.xres = xa; g.nw = w.ffn_norm; g.ss_out = ss_gu; g.mhi = m->mh; g.mlo = m->ml; g.ldm = F;
+      {
+        ProfScope ps(m, GQA_PROF_DECODE_GATEUP, st);
+        LAUNCH(launch_gemv_full(XF_NORM, EPI_SWIGLU, m->s_gu, g, st));
+      }
+      FullArgs dn = fa();
+      dn.W = w.wd; dn.Wq = w.qd; dn.Wd = w.sd; dn.K = F; dn.N = H;
+      dn.xhi = m->mh; dn.xlo = m->ml; dn.ldx = F; dn.y = xa; dn.ldy = H; dn.yscale = 1.f;
+      LAUNCH(launch_gemv_full(XF_RAW, EPI_ADD, m->s_d, dn, st));
+    }
+    LAUNCH(launch_final_norm(resid_src(xa, nullptr, nullptr, 0, 1.f, m->final_norm, nullptr), B, m->xh, m->xl, H,
+                             st));
+    FullArgs lm = fa();
+    lm.W = m->lm_head; lm.K = H; lm.N = V; lm.xhi = m->xh; lm.xlo = m->xl; lm.ldx = H; lm.y = logits; lm.ldy = V;
+    lm.cand = argmax ? m->cand : nullptr;
+    {
+      ProfScope ps(m, GQA_PROF_DECODE_LMHEAD, st);
+      LAUNCH(launch_gemv_full(XF_RAW, EPI_STORE, 1, lm, st));
+    }
+    if (argmax) LAUNCH(launch_argmax(m->cand, V / 16, B, argmax, st));
+    return GQA_OK;
+  }
+
   const float* prev = nullptr;
   int prev_split = 0;
   for (int l = 0; l < d.n_layers; ++l) {
@@ -605,8 +636,8 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
                       m->s_qkv, P0, QKV, m->xh, m->xl));
     std::swap(xa, xb);
     LAUNCH(launch_attn_decode(P0, m->s_qkv, pstride, QKV, NQ, ss_qkv, m->s_qkv, H, w.q_norm, w.k_norm, eps, m->rcos,
-                              m->rsin, rows, B, max_ctx, w.kpool, w.vpool, m->apart, m->max_chunks, m->counters,
-                              kAttnOutScale, m->oh, m->ol, QD, st));
+                              m->rsin, rows, B, max_ctx, w.kpool, w.vpool, m->apart, m->counters, kAttnOutScale, m->oh, m->ol, QD,
+                              st));
     LAUNCH(launch_gemv(w.wo, w.qo, w.so, QD, H, raw_src(m->oh, m->ol, QD), B, m->s_o, P1, pstride, H, nullptr, st));
     {
       ProfScope ps(m, GQA_PROF_DECODE_GATEUP, st);
@@ -812,6 +843,33 @@ static int logical_rows(const gqa_model* m, int kind) {
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+// Copy logical row `prow` of a tile-major matrix [*][cols] with elements of `esize` bytes (and,
+// for Q8_0, its cols/32 scales) to host memory: the row's 16-row band is copied, then the row is
+// gathered with tiled_index.
+int read_tiled_row(const void* base, int esize, int64_t prow, int cols, void* dst, const f16* scales,
+                   uint16_t* sdst) {
+  const int64_t band_elems = (int64_t)16 * cols;
+  std::vector<char> band((size_t)band_elems * esize);
+  HIP_TRY(hipMemcpy(band.data(), (const char*)base + (prow >> 4) * band_elems * esize, band.size(),
+                    hipMemcpyDeviceToHost));
+  for (int c = 0; c < cols; ++c)
+    memcpy((char*)dst + (int64_t)c * esize, band.data() + tiled_index(prow & 15, c, cols) * esize, esize);
+  if (scales) {
+    std::vector<uint16_t> sb((size_t)(cols / 32) * 16);
+    HIP_TRY(hipMemcpy(sb.data(), scales + (prow >> 4) * (cols / 32) * 16, sb.size() * 2, hipMemcpyDeviceToHost));
+    for (int k = 0; k < cols / 32; ++k) sdst[k] = sb[tiled_scale_index(prow & 15, k, cols)];
+  }
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int gqa_debug_read_weight(gqa_model* m, int32_t kind, int32_t layer, int32_t row0, int32_t rows, uint16_t* dst) {
   if (!m || !dst) return fail(GQA_E_INVALID, "null argument");
   const gqa_model_desc& d = m->d;
@@ -824,11 +882,16 @@ int gqa_debug_read_weight(gqa_model* m, int32_t kind, int32_t layer, int32_t row
   const uint16_t* src = nullptr;
   int cols = d.hidden;
   switch (kind) {
-    case GQA_T_EMBED: src = m->embed; break;
-    case GQA_T_LM_HEAD:
-      if (d.tied) return fail(GQA_E_INVALID, "tied model has no separate lm_head");
-      src = m->lm_head;
-      break;
+    case GQA_T_EMBED:
+    case GQA_T_LM_HEAD: {
+      if (kind == GQA_T_LM_HEAD && d.tied) return fail(GQA_E_INVALID, "tied model has no separate lm_head");
+      const uint16_t* base = kind == GQA_T_EMBED ? m->embed : m->lm_head;
+      for (int r = 0; r < rows; ++r) {
+        int rc = read_tiled_row(base, 2, row0 + r, cols, dst + (int64_t)r * cols, nullptr, nullptr);
+        if (rc) return rc;
+      }
+      return GQA_OK;
+    }
     case GQA_T_FINAL_NORM: src = m->final_norm; break;
     case GQA_T_ATTN_NORM: src = m->L[layer].attn_norm; break;
     case GQA_T_FFN_NORM: src = m->L[layer].ffn_norm; break;
@@ -844,8 +907,8 @@ int gqa_debug_read_weight(gqa_model* m, int32_t kind, int32_t layer, int32_t row
   for (int r = 0; r < rows; ++r) {
     const void* base = nullptr;
     int pr = physical_row(m, kind, row0 + r, &base, &cols, false, layer);
-    HIP_TRY(hipMemcpy(dst + (int64_t)r * cols, (const uint16_t*)base + (int64_t)pr * cols, (size_t)cols * 2,
-                      hipMemcpyDeviceToHost));
+    int rc = read_tiled_row(base, 2, pr, cols, dst + (int64_t)r * cols, nullptr, nullptr);
+    if (rc) return rc;
   }
   return GQA_OK;
 }
@@ -864,16 +927,11 @@ int gqa_debug_read_q8(gqa_model* m, int32_t kind, int32_t layer, int32_t row0, i
   if (row0 < 0 || rows < 1 || row0 + rows > nrow) return fail(GQA_E_INVALID, "rows out of range");
   HIP_TRY(hipDeviceSynchronize());
   const LayerW& w = m->L[layer];
+  const f16* sb = kind == GQA_T_O ? w.so : kind == GQA_T_DOWN ? w.sd : (kind == GQA_T_GATE || kind == GQA_T_UP) ? w.sgu : w.sqkv;
   for (int r = 0; r < rows; ++r) {
     int pr = physical_row(m, kind, row0 + r, &base, &cols, true, layer);
-    const f16* sb = kind == GQA_T_O ? w.so : kind == GQA_T_DOWN ? w.sd : (kind == GQA_T_GATE || kind == GQA_T_UP) ? w.sgu : w.sqkv;
-    const int64_t prow = kind == GQA_T_O || kind == GQA_T_DOWN ? d.hidden
-                         : (kind == GQA_T_GATE || kind == GQA_T_UP) ? 2 * (int64_t)d.ffn : m->QKV;   // physical rows
-    HIP_TRY(hipMemcpy(quants + (int64_t)r * cols, (const int8_t*)base + (int64_t)pr * cols, (size_t)cols,
-                      hipMemcpyDeviceToHost));
-    // scales are block-major: [cols / 32][physical rows]
-    HIP_TRY(hipMemcpy2D(scales + (int64_t)r * (cols / 32), 2, sb + pr, (size_t)prow * 2, 2, cols / 32,
-                        hipMemcpyDeviceToHost));
+    int rc = read_tiled_row(base, 1, pr, cols, quants + (int64_t)r * cols, sb, scales + (int64_t)r * (cols / 32));
+    if (rc) return rc;
   }
   return GQA_OK;
 }
@@ -894,6 +952,34 @@ int gqa_debug_read_kv(gqa_session* s, int32_t layer, int32_t pos0, int32_t n, ui
       HIP_TRY(hipMemcpy(v + ((int64_t)i * kKvHeads + h) * kHeadDim, w.vpool + off, kHeadDim * 2, hipMemcpyDeviceToHost));
     }
   }
+  return GQA_OK;
+}
+
+int gqa_debug_read_scratch(gqa_model* m, int32_t which, int64_t offset, int64_t count, void* dst) {
+  if (!m || !dst) return fail(GQA_E_INVALID, "null argument");
+  const gqa_model_desc& d = m->d;
+  const int rows = std::max(m->R, kMaxBatch);
+  const void* base = nullptr;
+  int64_t n = 0, esize = 4;
+  switch (which) {
+    case GQA_S_RESID_A: base = m->x; n = (int64_t)rows * d.hidden; break;
+    case GQA_S_RESID_B: base = m->x2; n = (int64_t)kMaxBatch * d.hidden; break;
+    case GQA_S_PART_A: base = m->part; n = m->part_floats; break;
+    case GQA_S_PART_B: base = m->part2; n = m->part_floats; break;
+    case GQA_S_ATTN_HI: base = m->oh; n = (int64_t)rows * m->QD; esize = 2; break;
+    case GQA_S_ATTN_LO: base = m->ol; n = (int64_t)rows * m->QD; esize = 2; break;
+    case GQA_S_MLP_HI: base = m->mh; n = (int64_t)rows * d.ffn; esize = 2; break;
+    case GQA_S_MLP_LO: base = m->ml; n = (int64_t)rows * d.ffn; esize = 2; break;
+    case GQA_S_NORM_HI: base = m->xh; n = (int64_t)rows * d.hidden; esize = 2; break;
+    case GQA_S_NORM_LO: base = m->xl; n = (int64_t)rows * d.hidden; esize = 2; break;
+    case GQA_S_SUMSQ: base = m->ss; n = 2 * 8 * 32; break;
+    case GQA_S_QROT: base = m->q; n = (int64_t)rows * m->QD; break;
+    case GQA_S_QKV: base = m->qkv; n = (int64_t)m->R * m->QKV; break;
+    default: return fail(GQA_E_INVALID, "unknown scratch buffer %d", which);
+  }
+  if (offset < 0 || count < 1 || offset + count > n) return fail(GQA_E_INVALID, "range outside the buffer");
+  HIP_TRY(hipDeviceSynchronize());
+  HIP_TRY(hipMemcpy(dst, (const char*)base + offset * esize, (size_t)(count * esize), hipMemcpyDeviceToHost));
   return GQA_OK;
 }
 

@@ -198,6 +198,24 @@ int gqa_debug_read_q8(gqa_model* model, int32_t kind, int32_t layer, int32_t row
  * read through its block table, into host arrays of n x 8 x 128 uint16 each. */
 int gqa_debug_read_kv(gqa_session* session, int32_t layer, int32_t pos0, int32_t n, uint16_t* k, uint16_t* v);
 
+/* Activation scratch buffers of the model (contents are those left by the last call; layouts
+ * are internal and may change): copy elements [offset, offset + count) of buffer `which` into
+ * host memory `dst` (FP32 buffers 4 bytes per element, FP16 buffers 2). */
+#define GQA_S_RESID_A 0   /* FP32 residual stream (prefill rows / decode rows) */
+#define GQA_S_RESID_B 1   /* FP32 second residual buffer (split-K decode path) */
+#define GQA_S_PART_A 2    /* FP32 projection outputs or split partials */
+#define GQA_S_PART_B 3
+#define GQA_S_ATTN_HI 4   /* FP16 hi / lo of the attention output (o projection operand) */
+#define GQA_S_ATTN_LO 5
+#define GQA_S_MLP_HI 6    /* FP16 hi / lo of silu(gate) * up (down projection operand) */
+#define GQA_S_MLP_LO 7
+#define GQA_S_NORM_HI 8   /* FP16 hi / lo of normalised rows (prefill projection operand, lm_head) */
+#define GQA_S_NORM_LO 9
+#define GQA_S_SUMSQ 10    /* FP32 per-range sums of squares [2][8][32] */
+#define GQA_S_QROT 11     /* FP32 normed, rotated q of a prefill round */
+#define GQA_S_QKV 12      /* FP32 q|k|v projection of a prefill round */
+int gqa_debug_read_scratch(gqa_model* model, int32_t which, int64_t offset, int64_t count, void* dst);
+
 /* Copy the FP32 RoPE tables (positions [0, n) x 64 cos, then sin) into host arrays. */
 int gqa_debug_read_rope(gqa_model* model, int32_t n, float* cos_out, float* sin_out);
 
