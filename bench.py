@@ -82,6 +82,8 @@ def main():
     ap.add_argument("--workload", default="4b", choices=["4b", "0.6b", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prompt", type=int, default=256)
+    ap.add_argument("--prefill", default="split", choices=["split", "fp16"],
+                    help="prefill matrix-core operands: FP16 hi+lo (near-FP32, default) or one FP16 value")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: the decoder is evaluated unsharded on one MI355X "
@@ -99,7 +101,8 @@ def main():
     nb = synth.blocks_for(wl.prompt + wl.decode)
     pool = 4 * nb
     table = synth.shuffled_blocks(wl.shuffle_seed, pool)[:nb]
-    m = g.Model.from_shape(shape, seed=wl.weight_seed, scheme=wl.scheme, kv_pool_blocks=pool, max_positions=nb * 32)
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, scheme=wl.scheme, kv_pool_blocks=pool, max_positions=nb * 32,
+                           prefill=args.prefill)
     s = g.Session(m, nb * 32, block_ids=table)
     ids = synth.token_ids(wl.ids_seed, wl.prompt)
     lg = torch.empty(shape.vocab, device="cuda")

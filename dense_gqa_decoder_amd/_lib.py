@@ -32,13 +32,14 @@ class ModelDesc(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("vocab", ctypes.c_int32), ("tied", ctypes.c_int32), ("rope_theta", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("scheme", ctypes.c_int32), ("kv_pool_blocks", ctypes.c_int32),
-                ("max_positions", ctypes.c_int32), ("max_round_tokens", ctypes.c_int32)]
+                ("max_positions", ctypes.c_int32), ("max_round_tokens", ctypes.c_int32),
+                ("prefill_operands", ctypes.c_int32)]
 
 
 class ModelInfo(ctypes.Structure):
     _fields_ = [("round_tokens", ctypes.c_int32), ("cu_count", ctypes.c_int32), ("weight_bytes", ctypes.c_int64),
                 ("kv_pool_bytes", ctypes.c_int64), ("scratch_bytes", ctypes.c_int64),
-                ("free_blocks", ctypes.c_int32)]
+                ("prefill_copy_bytes", ctypes.c_int64), ("free_blocks", ctypes.c_int32)]
 
 
 _lib = None

@@ -126,6 +126,13 @@ __host__ __device__ __forceinline__ int64_t tiled_index(int64_t row, int64_t col
   return ((((row >> 4) * (cols >> 5) + (col >> 5)) << 9) + ((((col & 31) >> 3) * 16 + (row & 15)) << 3) +
           (col & 7));
 }
+// FP16 prefill copy of a BF16 weight matrix [rows][cols] (rows % 32 == 0, cols % 32 == 0): per
+// 32-row block and 32-column step one contiguous 1024-element piece ordered [kh][hf][row][8], the
+// A-operand order of v_mfma_f32_32x32x16_f16 for the two 16-wide halves kh of the step.
+__host__ __device__ __forceinline__ int64_t prefill_weight_index(int64_t row, int64_t col, int64_t cols) {
+  return ((((row >> 5) * (cols >> 5) + (col >> 5)) << 10) + (((col >> 4) & 1) << 9) + (((col >> 3) & 1) << 8) +
+          ((row & 31) << 3) + (col & 7));
+}
 // Q8_0 scale of (row, 32-column block): [row band][block][row within band].
 __host__ __device__ __forceinline__ int64_t tiled_scale_index(int64_t row, int64_t blk, int64_t cols) {
   return (((row >> 4) * (cols >> 5) + blk) << 4) + (row & 15);

@@ -73,6 +73,27 @@ __global__ void quantize_q8_0_kernel(const uint16_t* __restrict__ w, int8_t* __r
   }
 }
 
+// FP16 prefill copy (prefill_weight_index) of a tile-major BF16 matrix: one thread per 8-element
+// piece of the destination, converted exactly like the matrix-core operand path (bf16x8_to_f16x8).
+__global__ void prefill_copy_kernel(const uint16_t* __restrict__ src, f16* __restrict__ dst, int64_t rows,
+                                    int64_t cols) {
+  const int64_t npieces = rows * cols / 8, ksteps = cols >> 5;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < npieces; p += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t bp = p >> 7, pos = p & 127;
+    const int64_t row = (bp / ksteps) * 32 + (pos & 31);
+    const int64_t col = (bp % ksteps) * 32 + ((pos >> 6) & 1) * 16 + ((pos >> 5) & 1) * 8;
+    const uint4 v = *(const uint4*)(src + tiled_index(row, col, cols));
+    *(f16x8*)(dst + p * 8) = bf16x8_to_f16x8(v);
+  }
+}
+
+hipError_t launch_prefill_copy(const uint16_t* src, f16* dst, int64_t rows, int64_t cols, hipStream_t st) {
+  const int64_t n = rows * cols / 8;
+  const int grid = (int)std::min<int64_t>((n + 255) / 256, 65536);
+  hipLaunchKernelGGL(prefill_copy_kernel, dim3(grid), dim3(256), 0, st, src, dst, rows, cols);
+  return hipGetLastError();
+}
+
 hipError_t launch_gen_weights(uint16_t* dst, uint64_t key, int64_t rows, int64_t cols, int mode, int64_t row_off,
                               float scale, hipStream_t st) {
   int64_t n = rows * cols;

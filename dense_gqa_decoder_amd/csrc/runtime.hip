@@ -34,7 +34,8 @@ hipError_t launch_qk_rope_kv(bool decode, const float* qkv, int nsplit, int part
                              const float* rsin, int pos0, const int32_t* table0, const Rows& rows, uint16_t* kpool,
                              uint16_t* vpool, float* qout, int nrows, hipStream_t st);
 hipError_t launch_argmax(const float2* cand, int ntiles, int B, int32_t* out, hipStream_t st);
-hipError_t launch_gemm(int epi, const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
+hipError_t launch_prefill_copy(const uint16_t* src, f16* dst, int64_t rows, int64_t cols, hipStream_t st);
+hipError_t launch_gemm(int epi, bool split, const f16* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
                        const f16* Xlo, int ldx, int T, float* C, int ldc, float out_scale, f16* Mhi, f16* Mlo,
                        int ldm, float m_scale, hipStream_t st);
 hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const XSrc& xs, int B,
@@ -93,6 +94,7 @@ constexpr float kAttnOutScale = 16.0f;
 struct LayerW {
   uint16_t *attn_norm = nullptr, *ffn_norm = nullptr, *q_norm = nullptr, *k_norm = nullptr;
   uint16_t *wqkv = nullptr, *wo = nullptr, *wgu = nullptr, *wd = nullptr;                  // BF16
+  f16 *pqkv = nullptr, *po = nullptr, *pgu = nullptr, *pd = nullptr;                       // FP16 prefill copies
   int8_t *qqkv = nullptr, *qo = nullptr, *qgu = nullptr, *qd = nullptr;                    // Q8_0 quants
   f16 *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sd = nullptr;                       // Q8_0 scales
   uint16_t *kpool = nullptr, *vpool = nullptr;
@@ -121,7 +123,7 @@ struct gqa_model {
   std::vector<void*> allocs;
   std::vector<char> block_used;
   int free_blocks = 0, sessions = 0;
-  int64_t weight_bytes = 0, kv_bytes = 0, scratch_bytes = 0;
+  int64_t weight_bytes = 0, kv_bytes = 0, scratch_bytes = 0, prefill_copy_bytes = 0;
   std::mutex mu;
   // kernel timing (gqa_model_profile)
   int prof_cls = GQA_PROF_NONE;
@@ -171,6 +173,8 @@ int check_desc(const gqa_model_desc* d) {
       (2 * d->ffn) % 256 || d->vocab < 16 || d->vocab % 16)
     return fail(GQA_E_INVALID, "unsupported shape (hidden %% 256, hidden <= 4096, 2*ffn %% 256, vocab %% 16)");
   if (d->scheme != GQA_SCHEME_BF16 && d->scheme != GQA_SCHEME_Q8_0) return fail(GQA_E_INVALID, "unknown scheme");
+  if (d->prefill_operands != GQA_PREFILL_SPLIT && d->prefill_operands != GQA_PREFILL_FP16)
+    return fail(GQA_E_INVALID, "unknown prefill_operands");
   if (d->kv_pool_blocks < 1 || d->max_positions < 1 || d->max_round_tokens < 0)
     return fail(GQA_E_INVALID, "kv_pool_blocks and max_positions must be positive");
   if (!(d->rope_theta > 1.0f) || !(d->rms_eps > 0.0f)) return fail(GQA_E_INVALID, "bad rope_theta or rms_eps");
@@ -266,6 +270,10 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
       ALLOC(w.wo, (int64_t)H * m->QD, wb);
       ALLOC(w.wgu, (int64_t)2 * F * H, wb);
       ALLOC(w.wd, (int64_t)H * F, wb);
+      ALLOC(w.pqkv, (int64_t)m->QKV * H, &m->prefill_copy_bytes);
+      ALLOC(w.po, (int64_t)H * m->QD, &m->prefill_copy_bytes);
+      ALLOC(w.pgu, (int64_t)2 * F * H, &m->prefill_copy_bytes);
+      ALLOC(w.pd, (int64_t)H * F, &m->prefill_copy_bytes);
     }
     ALLOC(w.kpool, pool_elems, &m->kv_bytes);
     ALLOC(w.vpool, pool_elems, &m->kv_bytes);
@@ -352,6 +360,12 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
     uint16_t* dD = q8 ? tmp : w.wd;
     chk(gen(dD, GQA_T_DOWN, l, H, F, 0, 0));
     if (q8) chk(launch_quantize_q8_0(tmp, w.qd, w.sd, H, F, st));
+    if (!q8) {
+      chk(launch_prefill_copy(w.wqkv, w.pqkv, m->QKV, H, st));
+      chk(launch_prefill_copy(w.wo, w.po, H, m->QD, st));
+      chk(launch_prefill_copy(w.wgu, w.pgu, 2 * F, H, st));
+      chk(launch_prefill_copy(w.wd, w.pd, H, F, st));
+    }
     if (q8) chk(hipStreamSynchronize(st));
     chk(hipMemsetAsync(w.kpool, 0, pool_elems * 2, st));
     chk(hipMemsetAsync(w.vpool, 0, pool_elems * 2, st));
@@ -401,6 +415,7 @@ int gqa_model_get_info(const gqa_model* m, gqa_model_info* info) {
   info->weight_bytes = m->weight_bytes;
   info->kv_pool_bytes = m->kv_bytes;
   info->scratch_bytes = m->scratch_bytes;
+  info->prefill_copy_bytes = m->prefill_copy_bytes;
   info->free_blocks = m->free_blocks;
   return GQA_OK;
 }
@@ -691,6 +706,7 @@ int gqa_session_eval_prefill(gqa_session* s, const int32_t* ids, int32_t n, floa
   const int H = d.hidden, F = d.ffn, V = d.vocab, NQ = d.n_q_heads, QD = m->QD, QKV = m->QKV;
   const float eps = d.rms_eps;
   Rows none{};
+  const bool split = d.prefill_operands == GQA_PREFILL_SPLIT;
   for (int off = 0; off < n; off += m->R) {
     const int T = std::min(m->R, n - off);
     const int pos0 = s->pos + off;
@@ -698,7 +714,7 @@ int gqa_session_eval_prefill(gqa_session* s, const int32_t* ids, int32_t n, floa
     LAUNCH(launch_rmsnorm(m->x, H, nullptr, 0, 0, 0, 1.f, m->L[0].attn_norm, H, eps, 1.f, m->xh, m->xl, H, T, st));
     for (int l = 0; l < d.n_layers; ++l) {
       const LayerW& w = m->L[l];
-      LAUNCH(launch_gemm(EPI_STORE, w.wqkv, w.qqkv, w.sqkv, H, QKV, m->xh, m->xl, H, T, m->qkv, QKV, 1.f, nullptr,
+      LAUNCH(launch_gemm(EPI_STORE, split, w.pqkv, w.qqkv, w.sqkv, H, QKV, m->xh, m->xl, H, T, m->qkv, QKV, 1.f, nullptr,
                          nullptr, 0, 1.f, st));
       LAUNCH(launch_qk_rope_kv(false, m->qkv, 0, 0, QKV, NQ, w.q_norm, w.k_norm, eps, m->rcos, m->rsin, pos0,
                                s->d_table, none, w.kpool, w.vpool, m->q, T, st));
@@ -707,15 +723,15 @@ int gqa_session_eval_prefill(gqa_session* s, const int32_t* ids, int32_t n, floa
         LAUNCH(launch_attn_prefill(m->q, NQ, T, pos0, s->d_table, w.kpool, w.vpool, kAttnOutScale, m->oh, m->ol, QD,
                                    st));
       }
-      LAUNCH(launch_gemm(EPI_ADD, w.wo, w.qo, w.so, QD, H, m->oh, m->ol, QD, T, m->x, H, 1.f / kAttnOutScale, nullptr,
+      LAUNCH(launch_gemm(EPI_ADD, split, w.po, w.qo, w.so, QD, H, m->oh, m->ol, QD, T, m->x, H, 1.f / kAttnOutScale, nullptr,
                          nullptr, 0, 1.f, st));
       LAUNCH(launch_rmsnorm(m->x, H, nullptr, 0, 0, 0, 1.f, w.ffn_norm, H, eps, 1.f, m->xh, m->xl, H, T, st));
       {
         ProfScope ps(m, GQA_PROF_PREFILL_GATEUP, st);
-        LAUNCH(launch_gemm(EPI_SWIGLU, w.wgu, w.qgu, w.sgu, H, 2 * F, m->xh, m->xl, H, T, nullptr, 0, 1.f, m->mh,
+        LAUNCH(launch_gemm(EPI_SWIGLU, split, w.pgu, w.qgu, w.sgu, H, 2 * F, m->xh, m->xl, H, T, nullptr, 0, 1.f, m->mh,
                            m->ml, F, 1.f, st));
       }
-      LAUNCH(launch_gemm(EPI_ADD, w.wd, w.qd, w.sd, F, H, m->mh, m->ml, F, T, m->x, H, 1.f, nullptr, nullptr, 0, 1.f,
+      LAUNCH(launch_gemm(EPI_ADD, split, w.pd, w.qd, w.sd, F, H, m->mh, m->ml, F, T, m->x, H, 1.f, nullptr, nullptr, 0, 1.f,
                          st));
       if (l + 1 < d.n_layers)
         LAUNCH(launch_rmsnorm(m->x, H, nullptr, 0, 0, 0, 1.f, m->L[l + 1].attn_norm, H, eps, 1.f, m->xh, m->xl, H, T,

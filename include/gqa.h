@@ -75,7 +75,13 @@ typedef struct {
   int32_t kv_pool_blocks;   /* physical 32-position KV blocks in the model-owned pool */
   int32_t max_positions;    /* longest sequence any session may reach (RoPE table size) */
   int32_t max_round_tokens; /* prefill round width; 0 derives it from the device (CUs x 8) */
+  int32_t prefill_operands; /* GQA_PREFILL_SPLIT (0): FP32 activations enter the prefill matrix-core
+                               products as FP16 hi + lo (near-FP32); GQA_PREFILL_FP16 (1): as one
+                               FP16 value (half the matrix-core work, FP16-rounded activations) */
 } gqa_model_desc;
+
+#define GQA_PREFILL_SPLIT 0
+#define GQA_PREFILL_FP16 1
 
 /* Read-only facts about a created model. */
 typedef struct {
@@ -84,6 +90,7 @@ typedef struct {
   int64_t weight_bytes;       /* device bytes of all weights (Q8_0: quants + scales) */
   int64_t kv_pool_bytes;      /* device bytes of the K and V pools */
   int64_t scratch_bytes;      /* device bytes of per-model activation scratch */
+  int64_t prefill_copy_bytes; /* device bytes of the FP16 copies of BF16 projections used by prefill */
   int32_t free_blocks;        /* KV blocks not owned by any session */
 } gqa_model_info;
 
