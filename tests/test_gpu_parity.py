@@ -27,6 +27,16 @@ def say(*a):
     print("[gpu]", *a, flush=True)
 
 
+_ORACLE_CACHE = {}
+
+
+def oracle_greedy_cached(key, shape, seed, prompt, steps, scheme="bf16"):
+    """oracle_greedy, computed once per key for the whole test module."""
+    if key not in _ORACLE_CACHE:
+        _ORACLE_CACHE[key] = oracle_greedy(shape, seed, prompt, steps, scheme)
+    return _ORACLE_CACHE[key]
+
+
 def oracle_greedy(shape, seed, prompt, steps, scheme="bf16"):
     """Oracle logits at the last prompt position and at each greedy decode step, and the
     greedy tokens fed at each step."""
@@ -308,21 +318,52 @@ def test_tiny_q8_0_parity(g):
     m.close()
 
 
-def test_qwen3_0_6b_shape_parity(g):
+@pytest.mark.parametrize("prefill", ["split", "fp16"])
+def test_qwen3_0_6b_shape_parity(g, prefill):
     """0.6B shape: 28 layers, 348-token prompt, 64 teacher-forced greedy steps, paged KV with a
-    shuffled block table drawn from a pool four times the session's size."""
+    shuffled block table drawn from a pool four times the session's size; prefill products with
+    FP16 hi/lo activations (split) and with single FP16 activations (fp16)."""
     wl = synth.WORKLOADS["0.6b"]
     shape = wl.shape
     prompt = synth.token_ids(wl.ids_seed, wl.prompt)
     say("0.6b oracle")
-    ref, toks = oracle_greedy(shape, wl.weight_seed, prompt, wl.decode)
+    ref, toks = oracle_greedy_cached("0.6b", shape, wl.weight_seed, prompt, wl.decode)
     nb = synth.blocks_for(wl.prompt + wl.decode)
     table = synth.shuffled_blocks(wl.shuffle_seed, 4 * nb)[:nb]
-    say("0.6b gpu")
-    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=4 * nb, max_positions=nb * 32)
+    say("0.6b gpu", prefill)
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=4 * nb, max_positions=nb * 32,
+                           prefill=prefill)
     s = g.Session(m, nb * 32, block_ids=table)
     got = gpu_teacher_forced(m, s, prompt, toks, shape.vocab)
-    gate = Gate("0.6b")
+    gate = Gate("0.6b " + prefill)
+    for i, ((lg, am), r) in enumerate(zip(got, ref)):
+        gate.check(i, lg, r, am)
+    gate.assert_ok()
+    s.close()
+    m.close()
+
+
+@pytest.mark.parametrize("prefill", ["split", "fp16"])
+def test_qwen3_4b_shape_parity(g, prefill):
+    """Qwen3-4B shape at its full prompt: 36 layers, hidden 2560, 32 Q / 8 KV heads, FFN 9728,
+    the 2,048-token prompt prefilled in one round (the launch configuration bench.py times), then
+    4 teacher-forced greedy decode steps over a shuffled paged KV; full-logit NMSE and exact
+    argmax against the oracle at every position."""
+    wl = synth.WORKLOADS["4b"]
+    shape = wl.shape
+    steps = 4
+    prompt = synth.token_ids(wl.ids_seed, wl.prompt)
+    say("4b oracle (2048-token prefill, %d steps)" % steps)
+    ref, toks = oracle_greedy_cached("4b", shape, wl.weight_seed, prompt, steps)
+    nb = synth.blocks_for(wl.prompt + wl.decode)
+    table = synth.shuffled_blocks(wl.shuffle_seed, 4 * nb)[:nb]
+    say("4b gpu", prefill)
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=4 * nb, max_positions=nb * 32,
+                           prefill=prefill)
+    assert m.info().round_tokens >= wl.prompt
+    s = g.Session(m, nb * 32, block_ids=table)
+    got = gpu_teacher_forced(m, s, prompt, toks, shape.vocab)
+    gate = Gate("4b " + prefill)
     for i, ((lg, am), r) in enumerate(zip(got, ref)):
         gate.check(i, lg, r, am)
     gate.assert_ok()
