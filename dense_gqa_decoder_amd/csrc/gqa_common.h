@@ -179,6 +179,22 @@ __device__ __forceinline__ void split_f16(float x, f16& hi, f16& lo) {
   lo = cvt_rtz2(x - (float)hi, 0.f)[0];
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16v8 __attribute__((ext_vector_type(8)));
+
+// One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l's 16 bytes land at
+// lds_dst + 16 l, where lds_dst is the same for the whole wave. Issued as inline assembly: the
+// compiler cannot tell which LDS bytes such a load writes and would otherwise wait for it before
+// every LDS read. Being invisible to the compiler, the copies are also not covered by the waits
+// it places before a barrier: a barrier that publishes them must follow vm_wait_all().
+__device__ __forceinline__ void lds_dma16(const void* src, const void* lds_dst) {
+  const uint32_t la = (uint32_t)(uintptr_t)lds_dst;
+  // one wait state between the M0 write and the load that reads it
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la), "v"(src)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

@@ -6,13 +6,28 @@
 // position p iff j <= p; scores are q.k / sqrt(128) and the output is the softmax-weighted sum of
 // V. Softmax runs in base 2 on scores pre-multiplied by log2(e) / sqrt(128).
 //
-// Prefill: one 256-thread workgroup per (query tile, KV head). Each wave owns 32 query positions
-// of one head of the group, so the g heads that share a KV head share every K/V tile staged in
-// LDS. S^T = K Q^T and O^T = V^T P^T run on the matrix cores (v_mfma_f32_16x16x32_f16): K and V
-// are exact FP16 operands, Q and P enter as FP16 hi/lo pairs (near-FP32), accumulation is FP32,
-// and the online softmax keeps a running max and sum per query column. P^T is consumed straight
-// from the S^T accumulator layout: within each 32-key chunk a lane holds keys 4g..4g+3 and
-// 16+4g..16+4g+3 (g = lane / 16), and V^T is read from LDS in the same key order.
+// Prefill (attn_prefill_kernel): 512-thread workgroups, one per (KV head, pair of 32-query
+// tiles). The pair is tile i and tile n-1-i of the n tiles of the round, so every workgroup
+// walks the same number of causal key tiles (the round costs n + 1 key sweeps per pair whatever
+// i is), and workgroup b serves KV head b % 8, so all workgroups of one KV head run on one XCD
+// and share its L2. The eight waves are g heads x 8/g key splits: wave (h, s) owns the 32
+// queries of head h and, of every staged tile of 32 * 8/g keys, the 32-key subtile s, with its
+// own online-softmax state; the split states are merged in LDS at the end of the query tile.
+//  - K and V tiles go from the pool to LDS by direct-to-LDS loads (no register staging), double
+//    buffered; the block ids of the keys are staged in LDS once per workgroup. K runs one tile
+//    ahead of V, so each iteration issues the score MFMAs of the next subtile in the same
+//    straight-line block as the softmax and P V products of the current one.
+//  - S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K is the exact BF16 A operand (one 16-byte LDS
+//    read per lane and step), Q^T the B operand held in registers as a BF16 hi/lo pair
+//    (hi = RNE(x), lo = RNE of the exact remainder: about 2^-17 relative).
+//  - The accumulator gives each lane one query and 16 keys, which is already the B-operand
+//    layout of O^T = V^T P^T once the keys of each 16-key step are taken in the order
+//    (4 hf + 0..3, 8 + 4 hf + 0..3) for lane half hf; P enters as a BF16 hi/lo pair too.
+//  - V^T, the A operand, comes straight from the row-major V tile through the transposing LDS
+//    read ds_read_b64_tr_b16: lane i of each 16-lane group addresses key row i / 4, 8-byte piece
+//    i % 4 of a 4-key x 16-dim block and receives the 4 keys of dim i.
+//  - The running max is kept lazily: the accumulator and sum are rescaled only when a new score
+//    exceeds the reference max by more than 2^8, so p = 2^(s - m) stays below 256.
 //
 // Decode: split-context attention in FP32 on the vector ALUs, then a chunk merge; see
 // attn_decode_kernel.
@@ -20,200 +35,308 @@
 
 namespace gqa {
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16v8 a, bf16v8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// BF16 hi/lo of two FP32 values, packed two per dword: hi = RNE(x), lo = RNE(x - hi) (the
+// remainder is exact in FP32), so hi + lo = x to about 2^-17 relative.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pk_bf16(a, b);
+  lo = pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
+}
+
+__device__ __forceinline__ bf16v8 as_bf16v8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(bf16v8, uint4{a, b, c, d});
+}
+
+// max and sum of a lane's value with the value of lane l ^ 32 (same result in both lanes)
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// LDS of the prefill kernel. A staged tile holds KT keys. K tile: 8 planes, one per 16-dim step
+// st, each KT rows x 32 bytes, the two 16-byte halves of row r swapped when bit 3 of r is set
+// (16 consecutive rows read at one half then cover all 64 banks). V tile: 4 planes, one per
+// 32-dim tile dt, each KT rows x 64 bytes (4 consecutive rows are 256 contiguous bytes, the
+// footprint of a transposing read by 32 lanes). Both layouts put every step, dim tile and key
+// offset of a lane's reads into the instruction's immediate offset.
+template <int G>
+struct PrefillLds {
+  static constexpr int NS = 8 / G;                       // key splits
+  static constexpr int KT = 32 * NS;                     // keys per staged tile
+  static constexpr int TILE = KT * kHeadDim;             // BF16 elements of one K (or V) tile
+  static constexpr int KPLANE = KT * 16, VPLANE = KT * 32;
+  static constexpr int KV_BYTES = 4 * TILE * 2;          // two buffers of K, two of V
+  static constexpr int MERGE_BYTES = G * (NS - 1) * 66 * 64 * 4;   // per lane: m, l, o[64]
+  static constexpr int MAX_BLOCKS = 4096;                // block-table entries staged in LDS
+  static constexpr int AREA = KV_BYTES > MERGE_BYTES ? KV_BYTES : MERGE_BYTES;   // K/V buffers, or the merge
+  static constexpr int BYTES = AREA + MAX_BLOCKS * 4;
+};
 
 template <int G, bool PSPLIT>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(const float* __restrict__ q, int nq, int T, int pos0,
+__global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restrict__ q, int nq, int T, int pos0,
                                                            const int32_t* __restrict__ table,
-                                                           const uint16_t* __restrict__ kpool,
-                                                           const uint16_t* __restrict__ vpool, float out_scale,
-                                                           f16* __restrict__ ohi, f16* __restrict__ olo, int ldo) {
-  constexpr int WPH = 4 / G;            // waves per head
-  constexpr int BQ = 32 * WPH;          // query positions per workgroup
-  constexpr int KT = 64;                // keys per iteration
-  constexpr int LDK = kHeadDim + 8, LDV = KT + 8;
-  __shared__ f16 sK[KT * LDK];
-  __shared__ f16 sVt[kHeadDim * LDV];
+                                                           const uint16_t* kpool, const uint16_t* vpool,
+                                                           float out_scale, f16* __restrict__ ohi,
+                                                           f16* __restrict__ olo, int ldo) {
+  using L = PrefillLds<G>;
+  constexpr int NS = L::NS, KT = L::KT, TILE = L::TILE, KPLANE = L::KPLANE, VPLANE = L::VPLANE;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[L::BYTES / 2];
+  int* const tbl = (int*)(lds + L::AREA / 2);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const int qtile = gridDim.x - 1 - blockIdx.x;     // longest rows first
-  const int kvh = blockIdx.y;
-  const int tq0 = qtile * BQ;                        // first query row (round-relative) of the workgroup
-  const int head = kvh * G + wave / WPH;
-  const int tw0 = tq0 + (wave % WPH) * 32;           // first query row of this wave
-  const int kend = pos0 + min(tq0 + BQ, T);          // keys needed by the workgroup's valid rows
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = wave % G, ks = wave / G;
+  const int kvh = blockIdx.x & 7, pair = blockIdx.x >> 3;
+  const int head = kvh * G + hh;
+  const int nt = (T + 31) >> 5;
+  const int hf = lane >> 5, c32 = lane & 31;
   const float qscale = kLog2e * 0.08838834764831845f;
+  const int64_t blk_elems = (int64_t)kKvHeads * kBlock * kHeadDim;
+  const uint16_t* kbase = kpool + (int64_t)kvh * kBlock * kHeadDim;
+  const uint16_t* vbase = vpool + (int64_t)kvh * kBlock * kHeadDim;
 
-  // Q fragments (B operand of S^T): lane -> query column r16 of tile qt, dims kk*32 + 8*g4 .. +7.
-  f16x8 qh[2][4], ql[2][4];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    int t = tw0 + qt * 16 + r16;
-    const float* qr = q + ((int64_t)min(t, T - 1) * nq + head) * kHeadDim;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      float4 v0 = *(const float4*)(qr + kk * 32 + g4 * 8);
-      float4 v1 = *(const float4*)(qr + kk * 32 + g4 * 8 + 4);
-      float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        f16 h, l;
-        split_f16(v[e] * qscale, h, l);
-        qh[qt][kk][e] = h;
-        ql[qt][kk][e] = l;
-      }
-    }
+  // Staging: wave w copies the 1 KiB segments w + 8 i (i < NS) of each tile. A K segment is 32
+  // rows (one pool block) of plane (w + 8 i) / NS, rows 32 (w % NS) ..; lane l brings row l / 2,
+  // half l % 2. A V segment is 16 rows of plane (w + 8 i) / (2 NS), rows 16 (w % 2NS) ..; lane l
+  // brings row l / 4, chunk l % 4. Each wave's segments of a tile lie in one pool block.
+  const int krg = wave % NS, vrg = wave % (2 * NS);
+  const int kchunk = (((lane & 1) ^ ((lane >> 4) & 1)) << 3);
+  // K operand: row 32 ks + c32 of the tile, dims 16 st + 8 hf ..
+  const int kl = (ks * 32 + c32) * 16 + ((hf ^ ((c32 >> 3) & 1)) << 3);
+  // V^T operand: 16-lane group g reads dims 16 (g % 2) .. of a 4-key block at rows 4 hf + ..
+  const int vi = lane & 15;
+  const int vl = (ks * 32 + 4 * hf + (vi >> 2)) * 32 + ((lane >> 4) & 1) * 16 + (vi & 3) * 4;
+
+  // the block ids of every key the workgroup reads (the first query tile is the longer one)
+  {
+    const int nblk = (pos0 + min(32 * (nt - pair), T) + 31) >> 5;
+    for (int i = tid; i < nblk; i += 512) tbl[i] = table[i];
   }
+  __syncthreads();
 
-  f32x4 o[8][2];
-#pragma unroll
-  for (int d = 0; d < 8; ++d) o[d][0] = o[d][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[2] = {-1e30f, -1e30f}, lrow[2] = {0.f, 0.f};
+  for (int which = 0; which < 2; ++which) {
+    const int qt = which == 0 ? nt - 1 - pair : pair;
+    if (which == 1 && qt == nt - 1 - pair) break;
+    const int t0 = qt * 32;
+    const int qfirst = pos0 + t0, qlast = pos0 + min(t0 + 32, T) - 1;
+    const int kend = qlast + 1;
+    const int ntile = (kend + KT - 1) / KT;
+    const int myq = pos0 + min(t0 + c32, T - 1);
 
-  // staging: K chunk c = tid + 256*i -> key c >> 4, dims (c & 15) * 8; V chunk -> key c & 63,
-  // dims ((c >> 6)) * 8 (so consecutive lanes write consecutive keys of one V^T row).
-  uint4 rk[4], rv[4];
-  auto gload = [&](int kb) {
+    // Pipeline over staged tiles: iteration t needs K(t + 1) (for S(t + 1)) and V(t) (for
+    // P(t) V(t)), so the K stream runs one tile ahead of the V stream; tile u of a stream sits
+    // in buffer u & 1. Iteration t issues the copies of K(t + 2) and V(t + 1) into the buffers
+    // that iteration t - 1 finished with; they land while it computes.
+    auto issue_k = [&](int u) {
+      const int ph = tbl[min(u * KT + krg * 32, kend - 1) >> 5];
+      const int key = min(u * KT + krg * 32 + (lane >> 1), kend - 1);   // rows past the last query: a valid row
+      const uint16_t* src = kbase + (int64_t)ph * blk_elems + (key & 31) * kHeadDim + kchunk;
+      uint16_t* dst = lds + (u & 1) * TILE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + 256 * i;
-      int key = kb + (c >> 4);
-      if (key < kend) {
-        int phys = table[key >> 5];
-        rk[i] = *(const uint4*)(kpool + (((int64_t)phys * kKvHeads + kvh) * kBlock + (key & 31)) * kHeadDim +
-                                (c & 15) * 8);
-      } else {
-        rk[i] = uint4{0, 0, 0, 0};
+      for (int i = 0; i < NS; ++i) {
+        const int sg = wave + 8 * i;
+        lds_dma16(src + 16 * (sg / NS), dst + sg * 512);
       }
-      int vkey = kb + (c & 63);
-      if (vkey < kend) {
-        int phys = table[vkey >> 5];
-        rv[i] = *(const uint4*)(vpool + (((int64_t)phys * kKvHeads + kvh) * kBlock + (vkey & 31)) * kHeadDim +
-                                (c >> 6) * 8);
-      } else {
-        rv[i] = uint4{0, 0, 0, 0};
+    };
+    auto issue_v = [&](int u) {
+      const int ph = tbl[min(u * KT + vrg * 16, kend - 1) >> 5];
+      const int key = min(u * KT + vrg * 16 + (lane >> 2), kend - 1);
+      const uint16_t* src = vbase + (int64_t)ph * blk_elems + (key & 31) * kHeadDim + (lane & 3) * 8;
+      uint16_t* dst = lds + (2 + (u & 1)) * TILE;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int sg = wave + 8 * i;
+        lds_dma16(src + 32 * (sg / (2 * NS)), dst + sg * 512);
+      }
+    };
+    // first copies, then the Q loads (their latencies overlap)
+    issue_k(0);
+    issue_v(0);
+    if (ntile > 1) issue_k(1);
+
+    // Q^T operand: lane holds query c32, dims 16 st + 8 hf .. +7, pre-scaled, as BF16 hi/lo
+    bf16v8 qh[8], ql[8];
+    {
+      const float* qr = q + ((int64_t)min(t0 + c32, T - 1) * nq + head) * kHeadDim + 8 * hf;
+      float4 qa[8], qb[8];
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        qa[st] = *(const float4*)(qr + 16 * st);
+        qb[st] = *(const float4*)(qr + 16 * st + 4);
+      }
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const float4 a = qa[st], b = qb[st];
+        uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+        split_bf16x2(a.x * qscale, a.y * qscale, h0, l0);
+        split_bf16x2(a.z * qscale, a.w * qscale, h1, l1);
+        split_bf16x2(b.x * qscale, b.y * qscale, h2, l2);
+        split_bf16x2(b.z * qscale, b.w * qscale, h3, l3);
+        qh[st] = as_bf16v8(h0, h1, h2, h3);
+        ql[st] = as_bf16v8(l0, l1, l2, l3);
       }
     }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + 256 * i;
-      *(f16x8*)&sK[(c >> 4) * LDK + (c & 15) * 8] = bf16x8_to_f16x8(rk[i]);
-      f16x8 v = bf16x8_to_f16x8(rv[i]);
-      int key = c & 63, d0 = (c >> 6) * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sVt[(d0 + e) * LDV + key] = v[e];
-    }
-  };
 
-  gload(0);
-  for (int kb = 0; kb < kend; kb += KT) {
+    f32x16 o[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+    float m = -1e30f, lsum = 0.f;
+
+    // S^T of subtile ks of K tile u: sc[e] = score of key u KT + 32 ks + 8 (e / 4) + 4 hf + e % 4
+    auto scores = [&](int u) {
+      const uint16_t* kp = lds + (u & 1) * TILE + kl;
+      f32x16 sc = f32x16{};
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const bf16v8 a = *(const bf16v8*)(kp + st * KPLANE);
+        sc = mfma32_bf16(a, qh[st], sc);
+        sc = mfma32_bf16(a, ql[st], sc);
+      }
+      return sc;
+    };
+
+    vm_wait_all();                     // K(0) (and everything else issued so far)
     __syncthreads();
-    sstore();
-    __syncthreads();
-    if (kb + KT < kend) gload(kb + KT);
+    f32x16 sc = scores(0);
+    for (int t = 0; t < ntile; ++t) {
+      vm_wait_all();                   // this wave's copies of K(t + 1) and V(t)
+      __syncthreads();                 // ... and every wave's; the buffers of K(t), V(t - 1) are free
+      if (t + 2 < ntile) issue_k(t + 2);
+      if (t + 1 < ntile) issue_v(t + 1);
 
-    // S^T tiles: s[kt][qt][r] = score of key kb + kt*16 + 4*g4 + r for query column qt*16 + r16.
-    f32x4 s[4][2];
+      const int sub = t * KT + ks * 32;
+      if (sub > qlast) continue;       // every key of this and later subtiles is masked
+      if (sub + 31 > qfirst) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      s[kt][0] = s[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        f16x8 a = *(const f16x8*)&sK[(kt * 16 + r16) * LDK + kk * 32 + g4 * 8];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          s[kt][qt] = mfma16(a, qh[qt][kk], s[kt][qt]);
-          s[kt][qt] = mfma16(a, ql[qt][kk], s[kt][qt]);
+        for (int e = 0; e < 16; ++e) {
+          const int key = sub + 8 * (e >> 2) + 4 * hf + (e & 3);
+          sc[e] = key <= myq ? sc[e] : -INFINITY;
         }
       }
-    }
-    // causal mask + online softmax per query column
+      float mx = sc[0];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      int qpos = pos0 + tw0 + qt * 16 + r16;
-      float mx = -INFINITY;
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+      const float mnew = fmaxf(m, xhalf_max(mx));
+      if (__any(mnew > m + 8.f)) {
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        m = mnew;
+        lsum *= alpha;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+      }
+      // S(t + 1) (on the last tile it reads a stale buffer and is discarded), P(t), O += V(t)^T P(t)^T
+      const f32x16 sn = scores(t + 1);
+      uint32_t ph[8], pl[8];
+      float ps = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int kpos = kb + kt * 16 + g4 * 4 + r;
-          float v = kpos <= qpos ? s[kt][qt][r] : -INFINITY;
-          s[kt][qt][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      float mnew = fmaxf(mrow[qt], mx);
-      float alpha = exp2f(mrow[qt] - mnew);
-      float sum = 0.f;
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(sc[e] - m), p1 = __builtin_amdgcn_exp2f(sc[e + 1] - m);
+        ps += p0;
+        ps += p1;
+        if (PSPLIT)
+          split_bf16x2(p0, p1, ph[e >> 1], pl[e >> 1]);
+        else
+          ph[e >> 1] = pk_bf16(p0, p1);
+      }
+      lsum += ps;
+      const uint16_t* vt = lds + (2 + (t & 1)) * TILE + vl;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int j = 0; j < 2; ++j) {
+        const bf16v8 bh = as_bf16v8(ph[4 * j], ph[4 * j + 1], ph[4 * j + 2], ph[4 * j + 3]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float p = exp2f(s[kt][qt][r] - mnew);
-          s[kt][qt][r] = p;
-          sum += p;
-        }
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
-      lrow[qt] = lrow[qt] * alpha + sum;
-      mrow[qt] = mnew;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) o[d][qt] *= alpha;
-    }
-    // O^T += V^T P^T over two 32-key chunks
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      f16x8 ph[2], pl[2];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          f16 h, l;
-          split_f16(s[2 * c][qt][r], h, l);
-          ph[qt][r] = h;
-          pl[qt][r] = l;
-          split_f16(s[2 * c + 1][qt][r], h, l);
-          ph[qt][4 + r] = h;
-          pl[qt][4 + r] = l;
-        }
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const f16* vr = &sVt[(d * 16 + r16) * LDV + c * 32 + g4 * 4];
-        f16x4 v0 = *(const f16x4*)vr;
-        f16x4 v1 = *(const f16x4*)(vr + 16);
-        f16x8 a = f16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          o[d][qt] = mfma16(a, ph[qt], o[d][qt]);
-          if (PSPLIT) o[d][qt] = mfma16(a, pl[qt], o[d][qt]);
+        for (int dt = 0; dt < 4; ++dt) {
+          const s16x4 v0 = lds_read_tr16(vt + dt * VPLANE + 16 * j * 32);
+          const s16x4 v1 = lds_read_tr16(vt + dt * VPLANE + (16 * j + 8) * 32);
+          const bf16v8 a = __builtin_bit_cast(bf16v8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[dt] = mfma32_bf16(a, bh, o[dt]);
+          if (PSPLIT) {
+            const bf16v8 bl = as_bf16v8(pl[4 * j], pl[4 * j + 1], pl[4 * j + 2], pl[4 * j + 3]);
+            o[dt] = mfma32_bf16(a, bl, o[dt]);
+          }
         }
       }
+      sc = sn;
     }
-  }
+    lsum = xhalf_sum(lsum);
 
-  // o[d][qt][r] = O^T[dim d*16 + 4*g4 + r][query qt*16 + r16]
+    auto store = [&](float Lsum) {
+      const int t = t0 + c32;
+      if (t >= T) return;
+      const float inv = out_scale / Lsum;
+      const int64_t base = (int64_t)t * ldo + head * kHeadDim + 4 * hf;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    int t = tw0 + qt * 16 + r16;
-    if (t < T) {
-      float inv = out_scale / lrow[qt];
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        f16x4 hv, lv;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f16x4 hv, lv;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          f16 h, l;
-          split_f16(o[d][qt][r] * inv, h, l);
-          hv[r] = h;
-          lv[r] = l;
+          for (int r = 0; r < 4; ++r) {
+            f16 h, l;
+            split_f16(o[dt][4 * g4 + r] * inv, h, l);
+            hv[r] = h;
+            lv[r] = l;
+          }
+          *(f16x4*)&ohi[base + dt * 32 + 8 * g4] = hv;
+          *(f16x4*)&olo[base + dt * 32 + 8 * g4] = lv;
         }
-        int64_t off = (int64_t)t * ldo + head * kHeadDim + d * 16 + g4 * 4;
-        *(f16x4*)&ohi[off] = hv;
-        *(f16x4*)&olo[off] = lv;
+    };
+
+    if constexpr (NS == 1) {
+      store(lsum);
+      __syncthreads();                 // the next query tile's first copies reuse buffer 0
+    } else {
+      float* sm = (float*)lds;
+      __syncthreads();                 // every wave is done with the K/V buffers
+      if (ks > 0) {
+        float* d = sm + (hh * (NS - 1) + ks - 1) * 66 * 64 + lane;
+        d[0] = m;
+        d[64] = lsum;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) d[(2 + dt * 16 + e) * 64] = o[dt][e];
       }
+      __syncthreads();
+      if (ks == 0) {
+        const float* src = sm + hh * (NS - 1) * 66 * 64 + lane;
+        float M = m;
+#pragma unroll
+        for (int k = 0; k < NS - 1; ++k) M = fmaxf(M, src[k * 66 * 64]);
+        const float w0 = __builtin_amdgcn_exp2f(m - M);
+        float Ls = lsum * w0;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] *= w0;
+#pragma unroll
+        for (int k = 0; k < NS - 1; ++k) {
+          const float* sk = src + k * 66 * 64;
+          const float w = __builtin_amdgcn_exp2f(sk[0] - M);
+          Ls = fmaf(sk[64], w, Ls);
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[dt][e] = fmaf(sk[(2 + dt * 16 + e) * 64], w, o[dt][e]);
+        }
+        store(Ls);
+      }
+      __syncthreads();                 // the merge area is the next query tile's K/V buffer
     }
   }
 }
@@ -525,14 +648,16 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
 
 hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const int32_t* table, const uint16_t* kpool,
                                const uint16_t* vpool, float out_scale, f16* ohi, f16* olo, int ldo, hipStream_t st) {
-  int G = nq / kKvHeads;
+  if (T <= 0) return hipSuccess;
+  if ((pos0 + T + 31) / 32 > PrefillLds<4>::MAX_BLOCKS) return hipErrorInvalidValue;   // context too long
+  const int G = nq / kKvHeads;
+  const int pairs = ((T + 31) / 32 + 1) / 2;
+  const dim3 grid(pairs * kKvHeads);
   if (G == 4) {
-    dim3 grid((T + 31) / 32, kKvHeads);
-    hipLaunchKernelGGL((attn_prefill_kernel<4, true>), grid, dim3(256), 0, st, q, nq, T, pos0, table, kpool, vpool,
+    hipLaunchKernelGGL((attn_prefill_kernel<4, true>), grid, dim3(512), 0, st, q, nq, T, pos0, table, kpool, vpool,
                        out_scale, ohi, olo, ldo);
   } else if (G == 2) {
-    dim3 grid((T + 63) / 64, kKvHeads);
-    hipLaunchKernelGGL((attn_prefill_kernel<2, true>), grid, dim3(256), 0, st, q, nq, T, pos0, table, kpool, vpool,
+    hipLaunchKernelGGL((attn_prefill_kernel<2, true>), grid, dim3(512), 0, st, q, nq, T, pos0, table, kpool, vpool,
                        out_scale, ohi, olo, ldo);
   } else {
     return hipErrorInvalidValue;

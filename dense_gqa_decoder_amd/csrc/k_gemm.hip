@@ -29,8 +29,6 @@
 
 namespace gqa {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
@@ -260,17 +258,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
       const int slot = (wv * 2 + i) * 64 + lane, t = slot >> 2, kc = (slot & 3) ^ xswz(t);
       dx[i] = (uint32_t)(min(t0 + t, T - 1) * g.ldx + kc * 8);      // rows past T: a valid row, never stored
     }
-    // The loads are issued as inline assembly: the compiler cannot tell which LDS bytes a
-    // direct-to-LDS load writes and would otherwise wait for every one of them before each LDS
-    // read. Being invisible to the compiler, they are also not covered by the waits it places
-    // before a barrier, so every barrier that publishes a filled buffer is preceded by an
-    // explicit wait for all of the wave's vector memory operations (dma_wait).
-    auto dma1 = [](const f16* src, const f16* lds_dst) {
-      const uint32_t la = (uint32_t)(uintptr_t)lds_dst;
-      // one wait state between the M0 write and the load that reads it
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la), "v"(src)
-                   : "memory", "m0");
-    };
+    // Direct-to-LDS copies: every barrier that publishes a filled buffer follows dma_wait().
+    auto dma1 = [](const f16* src, const f16* lds_dst) { lds_dma16(src, lds_dst); };
     auto dma = [&](int buf, int k0) {
       const f16* wsrc = g.W + (blk0 + (k0 >> 5)) * 1024;
 #pragma unroll
@@ -281,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
         if (SPLIT) dma1(g.Xlo + k0 + dx[i], &bufXl(buf)[(wv * 2 + i) * 512]);
       }
     };
-    auto dma_wait = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+    auto dma_wait = []() { vm_wait_all(); };
     dma(0, 0);
     dma_wait();
     __syncthreads();
