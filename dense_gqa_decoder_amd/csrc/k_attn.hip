@@ -390,9 +390,9 @@ __device__ __forceinline__ void merge_head(const float* pp, int nchunk, int lane
   float L = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
   for (int cc = 0; cc < kDecodeMaxChunks; ++cc) {
-    if (cc < nchunk) {
-      const float w = __shfl(wt, cc, 64);
-      L = fmaf(__shfl(ml.y, cc, 64), w, L);
+    if (cc < nchunk) {                                  // chunk cc's weight and sum, read as scalars
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), cc));
+      L = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.y), cc)), w, L);
       o0 = fmaf(ov[cc].x, w, o0);
       o1 = fmaf(ov[cc].y, w, o1);
     }
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
   constexpr int NE = (G + 2) * kHeadDim;                  // q heads, then k and v of the new position
   __shared__ float sraw[NE];                              // projection sums (times 1/rms)
   __shared__ float sq[NE];                                // normed + rotated q (scaled), k; v
-  __shared__ float sm[NST][G], sl[NST][G];
+  __shared__ float sm[NST][G], sl[NST][G], sw[NST][G], sML[G][2];
   __shared__ float so[NST][G][kHeadDim];
   __shared__ int s_last;
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -603,22 +603,33 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
     for (int e = 0; e < 8; ++e) so[si][hh][dg * 8 + e] = o[hh][e];
   }
   __syncthreads();
-  for (int idx = tid; idx < G * kHeadDim; idx += 64 * kDecodeWaves) {
-    const int hh = idx / kHeadDim, d = idx % kHeadDim;
+  // per head: the max over the states, the state weights 2^(m_w - max) and the weighted sum,
+  // computed once (thread hh), in state order
+  if (tid < G) {
+    const int hh = tid;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NST; ++w) M = fmaxf(M, sm[w][hh]);
-    float L = 0.f, O = 0.f;
+    float L = 0.f;
 #pragma unroll
     for (int w = 0; w < NST; ++w) {
       const float wt = sm[w][hh] == -INFINITY ? 0.f : exp2f(sm[w][hh] - M);
+      sw[w][hh] = wt;
       L = fmaf(sl[w][hh], wt, L);
-      O = fmaf(so[w][hh][d], wt, O);
     }
+    sML[hh][0] = M;
+    sML[hh][1] = L;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * kHeadDim; idx += 64 * kDecodeWaves) {
+    const int hh = idx / kHeadDim, d = idx % kHeadDim;
+    float O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NST; ++w) O = fmaf(so[w][hh][d], sw[w][hh], O);
     float* pp = part + (((int64_t)b * nq + kvh * G + hh) * kDecodeMaxChunks + c) * kPartStride;
     if (d == 0) {
-      pp[0] = M;
-      pp[1] = L;
+      pp[0] = sML[hh][0];
+      pp[1] = sML[hh][1];
     }
     pp[4 + d] = O;
   }

@@ -293,7 +293,7 @@ hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStre
       if (epi != EPI_STORE) return hipErrorInvalidValue;
       BY_Q8(8, 1, 4, XF_NORM, EPI_STORE);
     } else if (epi == EPI_ADD) {
-      BY_Q8(8, 1, 4, XF_RAW, EPI_ADD);
+      BY_Q8(8, 1, 8, XF_RAW, EPI_ADD);
     } else {
       BY_Q8(8, 1, 4, XF_RAW, EPI_STORE);
     }
