@@ -40,9 +40,10 @@ def algorithmic(shape, prompt, decode):
     return flops, dec_bytes, w_bytes
 
 
-def cpu_baseline(wl, n_prompt=256, n_decode=8):
+def cpu_baseline(wl, n_prompt, n_decode):
     """The oracle on a bounded sample of the same workload: n_prompt prompt tokens then n_decode
-    greedy steps of the same model, timed after weight generation."""
+    greedy steps of the same model, timed after weight generation (by default the whole step:
+    the 2,048-token prompt and 64 decode steps)."""
     import numpy as np
     import oracle
     import synth
@@ -65,6 +66,81 @@ def cpu_baseline(wl, n_prompt=256, n_decode=8):
                       f"+ {n_decode} greedy decode steps, weight generation untimed"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gateup_4b_hbm_traffic.json")
+# sources whose code the decode gate/up matvec is built from: its PMC traffic is reported only
+# while these are unchanged since the counters were taken
+TRAFFIC_SOURCES = ["dense_gqa_decoder_amd/csrc/k_gemv_full.hip", "dense_gqa_decoder_amd/csrc/gqa_common.h"]
+
+
+def sources_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode gate/up matvec from the committed PMC summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's reading for a plain copy of
+    known size), or None when the summary is missing or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != sources_digest(TRAFFIC_SOURCES):
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def pmc_workload(n_decode):
+    """The benchmark's model, prompt and decode loop without torch, for rocprofv3 --pmc passes:
+    device buffers come from hipMalloc through the HIP runtime the library is linked against, and
+    a 256 MiB device-to-device copy of known size follows, whose FETCH_SIZE / WRITE_SIZE readings
+    calibrate the byte counters. Prints the copy size and exits."""
+    import ctypes
+    import dense_gqa_decoder_amd as g
+    import synth
+    g.load()
+    hip = ctypes.CDLL("libamdhip64.so.7")          # the runtime already loaded by the library
+
+    class DevBuf:
+        def __init__(self, nbytes):
+            p = ctypes.c_void_p()
+            if hip.hipMalloc(ctypes.byref(p), ctypes.c_size_t(nbytes)) != 0:
+                raise RuntimeError("hipMalloc failed")
+            self.p = p.value
+
+        def data_ptr(self):
+            return self.p
+
+    class NullStream:
+        cuda_stream = None
+
+    wl = synth.WORKLOADS["4b"]
+    nb = synth.blocks_for(wl.prompt + wl.decode)
+    table = synth.shuffled_blocks(wl.shuffle_seed, 4 * nb)[:nb]
+    m = g.Model.from_shape(wl.shape, seed=wl.weight_seed, scheme=wl.scheme, kv_pool_blocks=4 * nb,
+                           max_positions=nb * 32)
+    s = g.Session(m, nb * 32, block_ids=table)
+    lg, am = DevBuf(wl.shape.vocab * 4), DevBuf(4)
+    s.prefill(synth.token_ids(wl.ids_seed, wl.prompt), lg, am, NullStream)
+    for _ in range(n_decode):
+        s.decode(am, lg, am, NullStream)
+    size = 256 << 20
+    src, dst = DevBuf(size), DevBuf(size)
+    if hip.hipMemset(ctypes.c_void_p(src.p), 1, ctypes.c_size_t(size)) != 0 or \
+            hip.hipMemcpy(ctypes.c_void_p(dst.p), ctypes.c_void_p(src.p), ctypes.c_size_t(size), 3) != 0 or \
+            hip.hipDeviceSynchronize() != 0:
+        raise RuntimeError("calibration copy failed")
+    s.close()
+    m.close()
+    print(json.dumps({"pmc_workload": wl.shape.name, "decode_steps": n_decode, "calibration_copy_bytes": size}),
+          flush=True)
+
+
 def git_rev():
     try:
         r = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True, text=True)
@@ -81,10 +157,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="4b", choices=["4b", "0.6b", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-prompt", type=int, default=256)
+    ap.add_argument("--cpu-prompt", type=int, default=2048, help="oracle baseline: prompt tokens")
+    ap.add_argument("--cpu-decode", type=int, default=64, help="oracle baseline: decode steps")
     ap.add_argument("--prefill", default="split", choices=["split", "fp16"],
                     help="prefill matrix-core operands: FP16 hi+lo (near-FP32, default) or one FP16 value")
+    ap.add_argument("--pmc-workload", type=int, default=0, metavar="N",
+                    help="run the 4B prompt + N decode steps and a known-size copy without torch, "
+                         "for rocprofv3 --pmc passes (no timing output)")
     args = ap.parse_args()
+    if args.pmc_workload:
+        pmc_workload(args.pmc_workload)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: the decoder is evaluated unsharded on one MI355X "
               f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
@@ -104,7 +187,8 @@ def main():
     m = g.Model.from_shape(shape, seed=wl.weight_seed, scheme=wl.scheme, kv_pool_blocks=pool, max_positions=nb * 32,
                            prefill=args.prefill)
     s = g.Session(m, nb * 32, block_ids=table)
-    ids = synth.token_ids(wl.ids_seed, wl.prompt)
+    # the prompt is resident in HBM before timing (eval_prefill_device reads it there)
+    ids = torch.from_numpy(synth.token_ids(wl.ids_seed, wl.prompt).astype("int32")).to("cuda")
     lg = torch.empty(shape.vocab, device="cuda")
     am = torch.empty(1, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -120,6 +204,14 @@ def main():
             s.decode(am, lg, am, stream)
         if evs:
             evs[2].record(stream)
+
+    # A plain device copy of known size (256 MiB read + 256 MiB written), outside the timed
+    # region: under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE calibrate the HBM byte counters.
+    calib_src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     for _ in range(args.warmup):
         step()
@@ -179,9 +271,10 @@ def main():
         "prefill_frac_mfma_peak": round(flops / (pre_ms * 1e-3) / PEAK_BF16_FLOPS, 4),
         "decode_frac_hbm_peak": round(dec_bytes / (dec_ms / wl.decode * 1e-3) / PEAK_HBM, 4),
         "algorithmic": {"prefill_flop": flops, "decode_bytes_per_token": int(dec_bytes), "weight_bytes": w_bytes},
-        "roofline": {"kernel": "gemv_kernel<EPI_SWIGLU> decode gate/up matvec with SwiGLU",
+        "roofline": {"kernel": "gemv_full_kernel<XF_NORM, EPI_SWIGLU>: decode gate/up matvec with fused "
+                               "RMSNorm prologue and SwiGLU epilogue",
                      "bound": "hbm", "achieved": round(gu_gbs, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                     "frac": round(gu_gbs * 1e9 / PEAK_HBM, 4), "traffic": None,
+                     "frac": round(gu_gbs * 1e9 / PEAK_HBM, 4), "traffic": measured_traffic(),
                      "launch_us": round(gu_ms * 1e3, 2), "bytes_per_launch": gu_bytes,
                      "launches": kernels["decode_gateup"][0]},
         "prefill_roofline": {"kernel": "gemm_kernel<EPI_SWIGLU> prefill gate/up GEMM with SwiGLU",
@@ -193,7 +286,7 @@ def main():
         "commit": rev, "dirty": dirty, "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, n_prompt=args.cpu_prompt)
+        out["cpu_baseline"] = cpu_baseline(wl, n_prompt=min(args.cpu_prompt, wl.prompt), n_decode=args.cpu_decode)
     s.close()
     m.close()
     print(json.dumps(out), flush=True)

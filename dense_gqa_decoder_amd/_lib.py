@@ -55,6 +55,7 @@ _SIGS = {
     "gqa_session_reset": (I32, [P]),
     "gqa_session_position": (I32, [P]),
     "gqa_session_eval_prefill": (I32, [P, P, I32, P, P, P]),
+    "gqa_session_eval_prefill_device": (I32, [P, P, I32, P, P, P]),
     "gqa_session_eval_decode": (I32, [P, P, I32, P, P, P]),
     "gqa_session_eval_batch": (I32, [P, I32, P, I32, P, P, P]),
     "gqa_model_check_device_error": (I32, [P, P]),
@@ -138,6 +139,10 @@ def gqa_session_position(session: int) -> int:
 
 def gqa_session_eval_prefill(session, ids_ptr, n, logits_ptr, argmax_ptr, stream) -> None:
     _check(lib().gqa_session_eval_prefill(session, ids_ptr, n, logits_ptr, argmax_ptr, stream))
+
+
+def gqa_session_eval_prefill_device(session, ids_dev_ptr, n, logits_ptr, argmax_ptr, stream) -> None:
+    _check(lib().gqa_session_eval_prefill_device(session, ids_dev_ptr, n, logits_ptr, argmax_ptr, stream))
 
 
 def gqa_session_eval_decode(session, id_ptr, id_on_device, logits_ptr, argmax_ptr, stream) -> None:

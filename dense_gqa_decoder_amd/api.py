@@ -146,8 +146,13 @@ class Session:
         L.gqa_session_reset(self.handle)
 
     def prefill(self, ids, logits, argmax=None, stream=None):
-        h = np.ascontiguousarray(ids, dtype=np.int32)
-        L.gqa_session_eval_prefill(self.handle, h.ctypes.data, len(h), _ptr(logits), _ptr(argmax), _stream(stream))
+        """ids: host ints (checked on the host), or an int32 device tensor (checked on the device)."""
+        if hasattr(ids, "data_ptr"):
+            L.gqa_session_eval_prefill_device(self.handle, ids.data_ptr(), ids.numel(), _ptr(logits), _ptr(argmax),
+                                              _stream(stream))
+        else:
+            h = np.ascontiguousarray(ids, dtype=np.int32)
+            L.gqa_session_eval_prefill(self.handle, h.ctypes.data, len(h), _ptr(logits), _ptr(argmax), _stream(stream))
 
     def decode(self, token, logits, argmax=None, stream=None):
         """token: a host int, or an int32 device tensor holding the id."""

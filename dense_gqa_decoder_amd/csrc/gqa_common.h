@@ -2,6 +2,7 @@
 // wave reductions and the launch-error plumbing used by every kernel file.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 typedef _Float16 f16;
@@ -11,6 +12,25 @@ typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace gqa {
+
+// Timing of single launches: when armed, the next kernel launched through GQA_LAUNCH records
+// `start` and `stop` from its own dispatch packet (hipExtLaunchKernelGGL), so the interval is the
+// kernel's execution and nothing else; the pair is consumed by that launch.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchEvents g_launch_events;
+#define GQA_LAUNCH(kernel, grid, block, shm, st, ...)                                                         \
+  do {                                                                                                      \
+    if (::gqa::g_launch_events.start) {                                                                     \
+      const ::gqa::LaunchEvents ev_ = ::gqa::g_launch_events;                                               \
+      ::gqa::g_launch_events = ::gqa::LaunchEvents{};                                                       \
+      hipExtLaunchKernelGGL(kernel, grid, block, shm, st, ev_.start, ev_.stop, 0, __VA_ARGS__);            \
+    } else {                                                                                                \
+      hipLaunchKernelGGL(kernel, grid, block, shm, st, __VA_ARGS__);                                        \
+    }                                                                                                       \
+  } while (0)
+
 
 constexpr int kHeadDim = 128;
 constexpr int kKvHeads = 8;

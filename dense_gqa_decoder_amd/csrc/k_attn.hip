@@ -665,10 +665,10 @@ hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const in
   const int pairs = ((T + 31) / 32 + 1) / 2;
   const dim3 grid(pairs * kKvHeads);
   if (G == 4) {
-    hipLaunchKernelGGL((attn_prefill_kernel<4, true>), grid, dim3(512), 0, st, q, nq, T, pos0, table, kpool, vpool,
+    GQA_LAUNCH((attn_prefill_kernel<4, true>), grid, dim3(512), 0, st, q, nq, T, pos0, table, kpool, vpool,
                        out_scale, ohi, olo, ldo);
   } else if (G == 2) {
-    hipLaunchKernelGGL((attn_prefill_kernel<2, true>), grid, dim3(512), 0, st, q, nq, T, pos0, table, kpool, vpool,
+    GQA_LAUNCH((attn_prefill_kernel<2, true>), grid, dim3(512), 0, st, q, nq, T, pos0, table, kpool, vpool,
                        out_scale, ohi, olo, ldo);
   } else {
     return hipErrorInvalidValue;

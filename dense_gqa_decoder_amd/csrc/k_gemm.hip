@@ -354,11 +354,11 @@ static hipError_t launch_gemm_t(int epi, const GemmArgs& a, hipStream_t st) {
   const int total = (a.N / kGemmBN) * ((a.T + kGemmBT - 1) / kGemmBT);
   dim3 grid(8 * ((total + 7) / 8));
   if (epi == EPI_STORE)
-    hipLaunchKernelGGL((gemm_kernel<EPI_STORE, Q8, SPLIT>), grid, dim3(256), 0, st, a);
+    GQA_LAUNCH((gemm_kernel<EPI_STORE, Q8, SPLIT>), grid, dim3(256), 0, st, a);
   else if (epi == EPI_ADD)
-    hipLaunchKernelGGL((gemm_kernel<EPI_ADD, Q8, SPLIT>), grid, dim3(256), 0, st, a);
+    GQA_LAUNCH((gemm_kernel<EPI_ADD, Q8, SPLIT>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<EPI_SWIGLU, Q8, SPLIT>), grid, dim3(256), 0, st, a);
+    GQA_LAUNCH((gemm_kernel<EPI_SWIGLU, Q8, SPLIT>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -272,11 +272,11 @@ hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStre
 #define FULL(Q, NWB, NBW, U, MO, EP)                                                                          \
   do {                                                                                                        \
     if (a.B == 1 && (size_t)4 * a.K + 16 <= kFullMaxLds / 4)                                                  \
-      hipLaunchKernelGGL((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, 1>), dim3(a.N / 16 / NBW),                 \
-                         dim3(64 * NWB * NBW), shm, st, a);                                                    \
+      GQA_LAUNCH((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, 1>), dim3(a.N / 16 / NBW),                         \
+                 dim3(64 * NWB * NBW), shm, st, a);                                                            \
     else                                                                                                      \
-      hipLaunchKernelGGL((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, kFullMaxB>), dim3(a.N / 16 / NBW),         \
-                         dim3(64 * NWB * NBW), shm, st, a);                                                    \
+      GQA_LAUNCH((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, kFullMaxB>), dim3(a.N / 16 / NBW),                 \
+                 dim3(64 * NWB * NBW), shm, st, a);                                                            \
   } while (0)
 #define BY_Q8(NWB, NBW, U, MO, EP) \
   do {                             \

@@ -54,6 +54,10 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
 int64_t attn_decode_part_floats(int nq);
 }  // namespace gqa
 
+namespace gqa {
+thread_local LaunchEvents g_launch_events;
+}
+
 using namespace gqa;
 
 namespace {
@@ -507,11 +511,11 @@ int upload_ids(gqa_model* m, const int32_t* ids, int n, hipStream_t st) {
 
 constexpr int64_t kProfMax = 65536;
 
-// Bracket one launch of kernel class `cls` with events when that class is being recorded.
+// Time the next launch of kernel class `cls` when that class is being recorded: the launch
+// stamps a start/stop event pair from its own dispatch (GQA_LAUNCH).
 struct ProfScope {
   gqa_model* m;
   hipStream_t st;
-  hipEvent_t stop = nullptr;
   ProfScope(gqa_model* m_, int cls, hipStream_t st_) : m(m_), st(st_) {
     if (m->prof_cls != cls) return;
     if (m->prof_used >= kProfMax) {
@@ -523,14 +527,11 @@ struct ProfScope {
       if (hipEventCreate(&e) != hipSuccess) return;
       m->prof_ev.push_back(e);
     }
-    hipEvent_t start = m->prof_ev[2 * m->prof_used];
-    stop = m->prof_ev[2 * m->prof_used + 1];
+    g_launch_events.start = m->prof_ev[2 * m->prof_used];
+    g_launch_events.stop = m->prof_ev[2 * m->prof_used + 1];
     m->prof_used++;
-    (void)hipEventRecord(start, st);
   }
-  ~ProfScope() {
-    if (stop) (void)hipEventRecord(stop, st);
-  }
+  ~ProfScope() { g_launch_events = LaunchEvents{}; }   // unused if the launch failed
 };
 
 #define LAUNCH(expr)                                                                                   \
@@ -686,23 +687,10 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
   return GQA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int gqa_session_eval_prefill(gqa_session* s, const int32_t* ids, int32_t n, float* logits, int32_t* argmax,
-                             hipStream_t st) {
-  g_err.clear();
-  if (!s || !ids || !logits) return fail(GQA_E_INVALID, "null argument");
+// Prefill rounds over n ids already in device memory (ids_dev); see gqa_session_eval_prefill.
+int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, float* logits, int32_t* argmax, hipStream_t st) {
   gqa_model* m = s->m;
   const gqa_model_desc& d = m->d;
-  if (n < 1) return fail(GQA_E_INVALID, "n must be >= 1");
-  if ((int64_t)s->pos + n > s->max_pos)
-    return fail(GQA_E_RANGE, "context overflow: %d + %d > %d", s->pos, n, s->max_pos);
-  for (int i = 0; i < n; ++i)
-    if (ids[i] < 0 || ids[i] >= d.vocab) return fail(GQA_E_RANGE, "token id %d at %d outside [0, %d)", ids[i], i, d.vocab);
-  int rc = upload_ids(m, ids, n, st);
-  if (rc) return rc;
   const int H = d.hidden, F = d.ffn, V = d.vocab, NQ = d.n_q_heads, QD = m->QD, QKV = m->QKV;
   const float eps = d.rms_eps;
   Rows none{};
@@ -710,7 +698,7 @@ int gqa_session_eval_prefill(gqa_session* s, const int32_t* ids, int32_t n, floa
   for (int off = 0; off < n; off += m->R) {
     const int T = std::min(m->R, n - off);
     const int pos0 = s->pos + off;
-    LAUNCH(launch_embed(m->embed, m->ids_dev + off, T, H, d.vocab, m->x, m->err, st));
+    LAUNCH(launch_embed(m->embed, ids_dev + off, T, H, d.vocab, m->x, m->err, st));
     LAUNCH(launch_rmsnorm(m->x, H, nullptr, 0, 0, 0, 1.f, m->L[0].attn_norm, H, eps, 1.f, m->xh, m->xl, H, T, st));
     for (int l = 0; l < d.n_layers; ++l) {
       const LayerW& w = m->L[l];
@@ -751,6 +739,36 @@ int gqa_session_eval_prefill(gqa_session* s, const int32_t* ids, int32_t n, floa
   }
   s->pos += n;
   return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_session_eval_prefill(gqa_session* s, const int32_t* ids, int32_t n, float* logits, int32_t* argmax,
+                             hipStream_t st) {
+  g_err.clear();
+  if (!s || !ids || !logits) return fail(GQA_E_INVALID, "null argument");
+  gqa_model* m = s->m;
+  const gqa_model_desc& d = m->d;
+  if (n < 1) return fail(GQA_E_INVALID, "n must be >= 1");
+  if ((int64_t)s->pos + n > s->max_pos)
+    return fail(GQA_E_RANGE, "context overflow: %d + %d > %d", s->pos, n, s->max_pos);
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= d.vocab) return fail(GQA_E_RANGE, "token id %d at %d outside [0, %d)", ids[i], i, d.vocab);
+  int rc = upload_ids(m, ids, n, st);
+  if (rc) return rc;
+  return run_prefill(s, m->ids_dev, n, logits, argmax, st);
+}
+
+int gqa_session_eval_prefill_device(gqa_session* s, const int32_t* ids_dev, int32_t n, float* logits,
+                                    int32_t* argmax, hipStream_t st) {
+  g_err.clear();
+  if (!s || !ids_dev || !logits) return fail(GQA_E_INVALID, "null argument");
+  if (n < 1) return fail(GQA_E_INVALID, "n must be >= 1");
+  if ((int64_t)s->pos + n > s->max_pos)
+    return fail(GQA_E_RANGE, "context overflow: %d + %d > %d", s->pos, n, s->max_pos);
+  return run_prefill(s, ids_dev, n, logits, argmax, st);
 }
 
 int gqa_session_eval_batch(gqa_session* const* ss, int32_t B, const int32_t* ids, int32_t ids_on_device,

@@ -135,6 +135,15 @@ int32_t gqa_session_position(const gqa_session* session);
 int gqa_session_eval_prefill(gqa_session* session, const int32_t* ids, int32_t n, float* logits, int32_t* argmax,
                              hipStream_t stream);
 
+/* As gqa_session_eval_prefill with the n ids already in device memory (`ids`, read on
+ * `stream`; the caller keeps them alive until the call's work completes), so no host copy is
+ * made. Ids cannot be checked synchronously: an id outside [0, vocab) makes its embedding row
+ * NaN (hence the logits NaN and the argmax -1) and sets the model's sticky device error (see
+ * gqa_model_check_device_error); the position still advances. GQA_E_RANGE for a context
+ * overflow. (Kipp Roadmap, status v0.0.4: prompt rounds evaluated on the device.) */
+int gqa_session_eval_prefill_device(gqa_session* session, const int32_t* ids, int32_t n, float* logits,
+                                    int32_t* argmax, hipStream_t stream);
+
 /* Evaluate one token at the session's position. `id` is a host pointer when id_on_device is
  * 0 (validated: GQA_E_RANGE if outside [0, vocab)) or a device pointer when 1 (for greedy
  * loops without host round trips, e.g. the previous call's argmax buffer). A device id

@@ -267,6 +267,31 @@ def test_device_ids_and_errors(g):
         o.close()
 
 
+def test_prefill_device_ids(g):
+    """eval_prefill_device (ids already in HBM) gives the bits of eval_prefill (host ids), across
+    two rounds; an out-of-range device id is reported through the sticky device error."""
+    shape = synth.reduced(synth.TINY, n_layers=2)
+    m = g.Model.from_shape(shape, seed=5, kv_pool_blocks=8, max_positions=96, max_round_tokens=32)
+    ids = synth.token_ids(17, 50)
+    a, b = g.Session(m, 96), g.Session(m, 96)
+    la, lb = torch.empty(shape.vocab, device="cuda"), torch.empty(shape.vocab, device="cuda")
+    aa, ab = torch.empty(1, dtype=torch.int32, device="cuda"), torch.empty(1, dtype=torch.int32, device="cuda")
+    a.prefill(ids, la, aa)
+    b.prefill(torch.from_numpy(ids.astype(np.int32)).to("cuda"), lb, ab)
+    torch.cuda.synchronize()
+    assert a.position == b.position == 50
+    assert torch.equal(la, lb) and torch.equal(aa, ab)
+    m.check_device_error()
+    bad = torch.tensor([3, shape.vocab], dtype=torch.int32, device="cuda")
+    b.prefill(bad, lb, ab)
+    with pytest.raises(g.GqaError) as e:
+        m.check_device_error()
+    assert e.value.code == g.GQA_E_RANGE
+    assert b.position == 52
+    for o in (a, b, m):
+        o.close()
+
+
 def test_pool_exhaustion_and_block_validation(g):
     shape = synth.reduced(synth.TINY, n_layers=1)
     m = g.Model.from_shape(shape, seed=3, kv_pool_blocks=4, max_positions=128)
