@@ -394,3 +394,187 @@ def test_qwen3_4b_shape_parity(g, prefill):
     gate.assert_ok()
     s.close()
     m.close()
+
+
+def _bf16_to_f64(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_qwen3_4b_q8_0_reduced_depth_parity(g):
+    """Q8_0 at the 4B hidden sizes (hidden 2560, 32/8 heads, FFN 9728, tied vocab) with 4 layers,
+    a 1,500-token prompt evaluated in rounds of 512 (two full rounds and a ragged one, so the
+    attention of later rounds starts at pos0 > 0), then 3 teacher-forced decode steps over a
+    shuffled paged KV: full-logit NMSE and exact argmax against the oracle, which dequantises
+    the same Q8_0 bytes."""
+    wl = synth.WORKLOADS["4b-q8"]
+    shape = synth.reduced(wl.shape, n_layers=4)
+    prompt = synth.token_ids(wl.ids_seed, 1500)
+    steps = 3
+    say("4b-q8 depth-4 oracle (1500-token prefill, %d steps)" % steps)
+    ref, toks = oracle_greedy(shape, wl.weight_seed, prompt, steps, scheme="q8_0")
+    nb = synth.blocks_for(len(prompt) + steps)
+    table = synth.shuffled_blocks(wl.shuffle_seed, 4 * nb)[:nb]
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, scheme="q8_0", kv_pool_blocks=4 * nb,
+                           max_positions=nb * 32, max_round_tokens=512)
+    s = g.Session(m, nb * 32, block_ids=table)
+    got = gpu_teacher_forced(m, s, prompt, toks, shape.vocab)
+    gate = Gate("4b q8_0 depth 4")
+    for i, ((lg, am), r) in enumerate(zip(got, ref)):
+        gate.check(i, lg, r, am)
+    gate.assert_ok()
+    s.close()
+    m.close()
+
+
+def test_qwen3_4b_q8_0_full_prompt(g):
+    """The Q8_0 4B workload at full size: 36 layers, the 12,800-token prompt in the device's
+    rounds over a shuffled paged KV (pool four times the session's need).
+    (1) The last layer's attention output for sampled rows of the last round equals an FP64
+        softmax(q K^T / sqrt(128)) V over all visible positions, computed on the host from the
+        read-back rotated q of that round and the BF16 K/V of all 12,800 positions.
+    (2) Decoding the prompt's argmax token gives the logits of prefilling the 12,801 tokens in a
+        second session (matvec path vs GEMM path), within NMSE 1e-5, same argmax unless the
+        top-2 margin is a near tie."""
+    wl = synth.WORKLOADS["4b-q8"]
+    shape = wl.shape
+    T = wl.prompt
+    nb = synth.blocks_for(T + 8)
+    table = synth.shuffled_blocks(wl.shuffle_seed, 4 * nb)[:nb]
+    say("4b-q8 full prompt (12800 tokens)")
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, scheme="q8_0", kv_pool_blocks=6 * nb, max_positions=nb * 32)
+    R = m.info().round_tokens
+    assert T > R
+    s = g.Session(m, nb * 32, block_ids=table)
+    prompt = synth.token_ids(wl.ids_seed, T)
+    lg = torch.empty(shape.vocab, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    s.prefill(prompt, lg, am)
+    torch.cuda.synchronize()
+    first = lg.cpu().numpy()
+    assert np.isfinite(first).all()
+    tok = int(am.item())
+    assert tok == int(np.argmax(first))
+
+    # (1) attention of layer L-1 in the last round (rows last0 .. T-1)
+    nq, G = shape.n_q_heads, shape.n_q_heads // 8
+    last0 = ((T - 1) // R) * R
+    Tl = T - last0
+    q = m.read_scratch("qrot", 0, Tl * nq * 128).reshape(Tl, nq, 128).astype(np.float64)
+    o_hi = m.read_scratch("attn_hi", 0, Tl * nq * 128).astype(np.float64)
+    o_lo = m.read_scratch("attn_lo", 0, Tl * nq * 128).astype(np.float64)
+    o_gpu = ((o_hi + o_lo) / 16.0).reshape(Tl, nq, 128)      # the operand rows are stored times 16
+    kb, vb = s.read_kv(shape.n_layers - 1, 0, T)
+    worst = 0.0
+    for t in (0, Tl // 2, Tl - 1):
+        p = last0 + t
+        for h in (0, 13, nq - 1):
+            kf = _bf16_to_f64(kb[: p + 1, h // G])
+            vf = _bf16_to_f64(vb[: p + 1, h // G])
+            sc = kf @ q[t, h] / np.sqrt(128.0)
+            w = np.exp(sc - sc.max())
+            ref_o = (w @ vf) / w.sum()
+            e = float(np.sum((o_gpu[t, h] - ref_o) ** 2) / np.sum(ref_o ** 2))
+            worst = max(worst, e)
+    say("4b-q8 attention spot check at %d positions: worst NMSE %.3e" % (T, worst))
+    assert worst <= 1e-9
+
+    # (2) decode after the prompt vs prefill of prompt + token
+    s.decode(tok, lg, am)
+    torch.cuda.synchronize()
+    dec = lg.cpu().numpy()
+    s2 = g.Session(m, nb * 32)
+    lg2 = torch.empty(shape.vocab, device="cuda")
+    am2 = torch.empty(1, dtype=torch.int32, device="cuda")
+    s2.prefill(np.concatenate([prompt, np.array([tok], dtype=prompt.dtype)]), lg2, am2)
+    torch.cuda.synchronize()
+    pre = lg2.cpu().numpy()
+    gate = Gate("4b q8_0 decode vs prefill at 12801")
+    gate.check(T, dec, pre, int(am.item()))
+    w = gate.assert_ok()
+    assert w <= 1e-5
+    for o in (s, s2, m):
+        o.close()
+
+
+def test_qwen3_8b_batched_32_sessions(g):
+    """The 8B batched workload at full size: 36 layers, hidden 4096, untied lm_head, 32
+    sessions with contexts L_i ~ U{512..8192} (seed 4005), each prefilled alone over its own
+    shuffled blocks, then 3 batched decode steps (B = 32, each row greedy on its own argmax):
+    every batched row equals a twin session stepped alone, bit for bit."""
+    wl = synth.WORKLOADS["8b-batch"]
+    shape = wl.shape
+    lens = [int(x) for x in synth.context_lengths(synth.CONTEXT_SEED_8B, wl.n_seqs)]
+    steps = 3
+    need = sum(synth.blocks_for(n + steps) for n in lens)
+    say("8b batch: contexts", min(lens), "..", max(lens), "total", sum(lens))
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=2 * need + 64, max_positions=8192 + 64)
+    lg = torch.empty(shape.vocab, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    A, Bs, nxt = [], [], []
+    for i, n in enumerate(lens):
+        p = synth.token_ids(wl.ids_seed, n, offset=i * 8192)
+        a, b = g.Session(m, n + steps), g.Session(m, n + steps)
+        a.prefill(p, lg, am)
+        b.prefill(p, lg)
+        torch.cuda.synchronize()
+        nxt.append(int(am.item()))
+        A.append(a)
+        Bs.append(b)
+    say("8b batch: prefilled 2 x 32 sessions")
+    B = len(lens)
+    blg = torch.empty(B, shape.vocab, device="cuda")
+    bam = torch.empty(B, dtype=torch.int32, device="cuda")
+    for step in range(steps):
+        m.eval_batch(A, nxt, blg, bam)
+        torch.cuda.synchronize()
+        batched = blg.cpu().numpy()
+        bam_h = bam.cpu().numpy()
+        for i, sb in enumerate(Bs):
+            sb.decode(nxt[i], lg, am)
+            torch.cuda.synchronize()
+            assert np.array_equal(lg.cpu().numpy(), batched[i]), (step, i)
+            assert int(am.item()) == int(bam_h[i])
+        assert np.isfinite(batched).all()
+        nxt = [int(x) for x in bam_h]
+    for o in A + Bs + [m]:
+        o.close()
+
+
+def test_qwen3_8b_batched_row_reduced_depth_parity(g):
+    """A batched row against the oracle at the 8B hidden sizes (hidden 4096, 32/8 heads, FFN
+    12288, untied lm_head) with 4 layers: 8 sessions with contexts 512..1400 are prefilled alone,
+    then 3 batched steps (B = 8, the split-K row path) teacher-force session 0 with the oracle's
+    tokens; its prefill and batched logits match the oracle (NMSE, exact argmax)."""
+    wl = synth.WORKLOADS["8b-batch"]
+    shape = synth.reduced(wl.shape, n_layers=4)
+    lens = [600, 512, 1400, 777, 1024, 900, 513, 1100]
+    steps = 3
+    p0 = synth.token_ids(wl.ids_seed, lens[0])
+    say("8b depth-4 oracle (%d-token prefill, %d steps)" % (lens[0], steps))
+    ref, toks = oracle_greedy(shape, wl.weight_seed, p0, steps)
+    need = sum(synth.blocks_for(n + steps) for n in lens)
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=need + 16, max_positions=2048)
+    lg = torch.empty(shape.vocab, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    sess, nxt = [], []
+    gate = Gate("8b depth 4, batched row 0")
+    for i, n in enumerate(lens):
+        p = p0 if i == 0 else synth.token_ids(wl.ids_seed, n, offset=i * 8192)
+        s = g.Session(m, n + steps)
+        s.prefill(p, lg, am)
+        torch.cuda.synchronize()
+        if i == 0:
+            gate.check(0, lg.cpu().numpy(), ref[0], int(am.item()))
+        nxt.append(int(am.item()))
+        sess.append(s)
+    blg = torch.empty(len(lens), shape.vocab, device="cuda")
+    bam = torch.empty(len(lens), dtype=torch.int32, device="cuda")
+    for step in range(steps):
+        nxt[0] = int(toks[step])
+        m.eval_batch(sess, nxt, blg, bam)
+        torch.cuda.synchronize()
+        gate.check(step + 1, blg[0].cpu().numpy(), ref[step + 1], int(bam[0].item()))
+        nxt = [int(x) for x in bam.cpu().numpy()]
+    gate.assert_ok()
+    for o in sess + [m]:
+        o.close()
