@@ -167,11 +167,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// FP32 -> FP16 conversions of MFMA operands go through one explicit instruction,
-// v_cvt_pkrtz_f16_f32 (round toward zero), never through a plain cast: the compiler is free to
-// lower a cast to different instructions in different kernels (a cast rounds ties to even, the
-// mixed-precision FMA forms fuse a preceding product), and every kernel that builds an operand
-// must produce the same bits for the same value.
+// FP32 -> FP16 conversions of MFMA operands go through explicit instructions, never through a
+// plain cast: the compiler is free to lower a cast to different instructions in different
+// kernels (mixed-precision FMA forms fuse a preceding product), and every kernel that builds an
+// operand must produce the same bits for the same value. Activations use cvt_rne2 (below);
+// BF16 weights, exact in FP16 over their range, use v_cvt_pkrtz_f16_f32.
 __device__ __forceinline__ f16x2 cvt_rtz2(float a, float b) {
   return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
@@ -191,12 +191,21 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16x8(uint4 v) {
   return r;
 }
 
-// Split an FP32 value into FP16 hi + lo: hi = rtz(x), lo = rtz(x - hi) (the difference is exact
-// in FP32), so x = hi + lo to about 2^-20 relative (2^-24 absolute near zero). Two FP16 MFMAs over
-// (hi, lo) give a near-FP32 product with BF16/FP16 weights.
+// FP32 pair -> FP16 pair rounded to nearest even, always by the one instruction
+// v_cvt_pk_f16_f32 (written out so that no kernel lowers it differently).
+__device__ __forceinline__ f16x2 cvt_rne2(float a, float b) {
+  uint32_t r;
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return __builtin_bit_cast(f16x2, r);
+}
+
+// Split an FP32 value into FP16 hi + lo: hi = rne(x), lo = rne(x - hi) (the difference is exact
+// in FP32), so x = hi + lo to about 2^-22 relative (2^-25 absolute near zero). Two FP16 MFMAs
+// over (hi, lo) give a near-FP32 product with BF16/FP16 weights; hi alone is the FP16 operand
+// of the single-operand prefill mode (unbiased rounding, 2^-11 relative).
 __device__ __forceinline__ void split_f16(float x, f16& hi, f16& lo) {
-  hi = cvt_rtz2(x, 0.f)[0];
-  lo = cvt_rtz2(x - (float)hi, 0.f)[0];
+  hi = cvt_rne2(x, 0.f)[0];
+  lo = cvt_rne2(x - (float)hi, 0.f)[0];
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
