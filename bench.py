@@ -28,11 +28,16 @@ METRIC = "prefill tok/s @2048 + decode tok/s, Qwen3-4B-shape BF16, 1 MI355X (% r
 
 
 def algorithmic(shape, prompt, decode):
-    """Algorithmic FLOP of the prefill and bytes per decode token (weights + KV, no scratch)."""
+    """Algorithmic FLOP of the prefill and bytes per decode token (weights + KV, no scratch).
+    The prefill's output is the last position's logits plus the K/V of every position, so the
+    last layer needs q|k|v for every row but attention, o and the MLP for the last row only."""
     H, F, V, L, QD = shape.hidden, shape.ffn, shape.vocab, shape.n_layers, shape.q_dim
     KVD = shape.kv_dim
-    P = H * QD + 2 * H * KVD + QD * H + 3 * H * F                     # projection weights per layer
-    flops = 2 * L * P * prompt + L * shape.n_q_heads * 4 * 128 * prompt * (prompt + 1) // 2 + 2 * V * H
+    P_qkv = H * QD + 2 * H * KVD
+    P = P_qkv + QD * H + 3 * H * F                                     # projection weights per layer
+    attn = shape.n_q_heads * 4 * 128
+    flops = (2 * (L - 1) * P * prompt + attn * (L - 1) * prompt * (prompt + 1) // 2
+             + 2 * P_qkv * prompt + 2 * (P - P_qkv) + attn * prompt + 2 * V * H)
     w_bytes = 2 * (L * P + V * H + (2 * L + 1) * H + 2 * L * 128) + 2 * H
     kv_pos = 2 * L * KVD * 2                                            # K and V bytes per cached position
     ctx_mean = prompt + (decode + 1) / 2.0

@@ -48,6 +48,8 @@ struct GemmArgs {
   f16* Mlo;
   int ldm;
   float m_scale;
+  int ksplit;                // K ranges (EPI_STORE only): range s writes C + s * split_stride
+  int64_t split_stride;
 };
 
 constexpr int kGemmBN = 256, kGemmBT = 128, kGemmBK = 32;
@@ -70,12 +72,18 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   auto bufXl = [&](int b) -> f16* { return sXl[SPLIT ? b : 0]; };
   __shared__ float sD[2][Q8 ? BN : 1];
 
-  // ---- tile of this workgroup: XCD-contiguous runs of a grouped order
+  // ---- tile and K range of this workgroup: XCD-contiguous runs of a grouped order of
+  //      (K range, tile) items, tiles of one K range consecutive
   const int K = g.K, T = g.T;
-  const int nnb = g.N / BN, ntb = (T + BT - 1) / BT, total = nnb * ntb;
-  const int per_xcd = (total + 7) / 8;
-  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (tile >= total || (blockIdx.x >> 3) >= per_xcd) return;
+  const int nnb = g.N / BN, ntb = (T + BT - 1) / BT, total = nnb * ntb, items = total * g.ksplit;
+  const int per_xcd = (items + 7) / 8;
+  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (item >= items || (blockIdx.x >> 3) >= per_xcd) return;
+  const int kr = item / total, tile = item - kr * total;
+  const int ns_all = K / BK;
+  const int s_begin = kr * ns_all / g.ksplit, s_end = (kr + 1) * ns_all / g.ksplit;
+  const int kbase = s_begin * BK;
+  float* const Cout = g.C ? g.C + (int64_t)kr * g.split_stride : nullptr;
   const int grp = tile / (kGemmGroup * ntb), rem = tile - grp * kGemmGroup * ntb;
   const int gsz = min(kGemmGroup, nnb - grp * kGemmGroup);
   const int nb = grp * kGemmGroup + rem % gsz, tb = rem / gsz;
@@ -240,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     }
   };
 
-  const int nsteps = K / BK;
+  const int nsteps = s_end - s_begin;
   int cur = 0;
   if constexpr (DMA) {
     // Pipeline: LDS buffer s % 2 holds step s; step s + 1 streams into the other buffer by
@@ -271,12 +279,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
       }
     };
     auto dma_wait = []() { vm_wait_all(); };
-    dma(0, 0);
+    dma(0, kbase);
     dma_wait();
     __syncthreads();
     for (int s = 0; s < nsteps; ++s) {            // buffer cur holds step s
       const bool more = s + 1 < nsteps;
-      if (more) dma(cur ^ 1, (s + 1) * BK);
+      if (more) dma(cur ^ 1, kbase + (s + 1) * BK);
       compute(cur);
       if (more) {
         dma_wait();                               // this wave's loads of step s + 1 have landed
@@ -288,12 +296,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     // Pipeline: LDS buffer s % 2 holds step s; the registers hold step s + 1, whose global loads
     // are in flight during step s's MFMAs.
     Stage r;
-    gload(r, 0);
+    gload(r, kbase);
     sstore(r, 0);
     __syncthreads();
     for (int s = 0; s < nsteps; ++s) {
       const bool more = s + 1 < nsteps;
-      if (more) gload(r, (s + 1) * BK);
+      if (more) gload(r, kbase + (s + 1) * BK);
       compute(cur);
       if (more) {
         sstore(r, cur ^ 1);
@@ -332,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float4* dst = (float4*)&g.C[(int64_t)t * g.ldc + nbase + 8 * q];
+          float4* dst = (float4*)&Cout[(int64_t)t * g.ldc + nbase + 8 * q];
           float4 v = make_float4(acc[i][j][q * 4 + 0] * g.out_scale, acc[i][j][q * 4 + 1] * g.out_scale,
                                  acc[i][j][q * 4 + 2] * g.out_scale, acc[i][j][q * 4 + 3] * g.out_scale);
           if (EPI == EPI_ADD) {
@@ -351,8 +359,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 
 template <bool Q8, bool SPLIT>
 static hipError_t launch_gemm_t(int epi, const GemmArgs& a, hipStream_t st) {
-  const int total = (a.N / kGemmBN) * ((a.T + kGemmBT - 1) / kGemmBT);
-  dim3 grid(8 * ((total + 7) / 8));
+  const int items = (a.N / kGemmBN) * ((a.T + kGemmBT - 1) / kGemmBT) * a.ksplit;
+  dim3 grid(8 * ((items + 7) / 8));
   if (epi == EPI_STORE)
     GQA_LAUNCH((gemm_kernel<EPI_STORE, Q8, SPLIT>), grid, dim3(256), 0, st, a);
   else if (epi == EPI_ADD)
@@ -363,11 +371,14 @@ static hipError_t launch_gemm_t(int epi, const GemmArgs& a, hipStream_t st) {
 }
 
 // split: FP16 hi/lo activations (two MFMAs per operand pair); otherwise hi only.
+// ksplit > 1 (EPI_STORE only): the K steps are cut into ksplit consecutive ranges and range s
+// stores its partial product at C + s * split_stride; the consumer sums them in range order.
 hipError_t launch_gemm(int epi, bool split, const f16* W, const int8_t* Wq, const f16* Wd, int K, int N,
                        const f16* Xhi, const f16* Xlo, int ldx, int T, float* C, int ldc, float out_scale, f16* Mhi,
-                       f16* Mlo, int ldm, float m_scale, hipStream_t st) {
+                       f16* Mlo, int ldm, float m_scale, int ksplit, int64_t split_stride, hipStream_t st) {
   if (N % kGemmBN != 0 || K % kGemmBK != 0 || T <= 0) return hipErrorInvalidValue;
-  GemmArgs a{W, Wq, Wd, K, N, Xhi, Xlo, ldx, T, C, ldc, out_scale, Mhi, Mlo, ldm, m_scale};
+  if (ksplit < 1 || ksplit > K / kGemmBK || (ksplit > 1 && epi != EPI_STORE)) return hipErrorInvalidValue;
+  GemmArgs a{W, Wq, Wd, K, N, Xhi, Xlo, ldx, T, C, ldc, out_scale, Mhi, Mlo, ldm, m_scale, ksplit, split_stride};
   if (Wq) return split ? launch_gemm_t<true, true>(epi, a, st) : launch_gemm_t<true, false>(epi, a, st);
   return split ? launch_gemm_t<false, true>(epi, a, st) : launch_gemm_t<false, false>(epi, a, st);
 }

@@ -37,7 +37,7 @@ hipError_t launch_argmax(const float2* cand, int ntiles, int B, int32_t* out, hi
 hipError_t launch_prefill_copy(const uint16_t* src, f16* dst, int64_t rows, int64_t cols, hipStream_t st);
 hipError_t launch_gemm(int epi, bool split, const f16* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
                        const f16* Xlo, int ldx, int T, float* C, int ldc, float out_scale, f16* Mhi, f16* Mlo,
-                       int ldm, float m_scale, hipStream_t st);
+                       int ldm, float m_scale, int ksplit, int64_t split_stride, hipStream_t st);
 hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const XSrc& xs, int B,
                        int nsplit, float* P, int64_t part_stride, int ldp, float2* cand, hipStream_t st);
 hipError_t launch_rows(const XSrc& xs, int K, int nsplit, int B, f16* yhi, f16* ylo, int ldy, hipStream_t st);
@@ -116,6 +116,7 @@ struct gqa_model {
   float *rcos = nullptr, *rsin = nullptr;
   float *x = nullptr, *x2 = nullptr, *qkv = nullptr, *q = nullptr, *part = nullptr, *part2 = nullptr,
         *apart = nullptr;
+  float* ppart = nullptr;       // prefill: K-range partials of the o and down projections [<= 4 R][H]
   int32_t* counters = nullptr;  // decode attention: finished chunks per (row, KV head)
   float* ss = nullptr;          // decode: sum-of-squares partials [2][8][32] (q|k|v input, gate|up input)
   float2* cand = nullptr;   // lm_head argmax candidates [32][vocab / 16]
@@ -298,6 +299,7 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   ALLOC(m->part, m->part_floats, sb);
   ALLOC(m->part2, m->part_floats, sb);
   ALLOC(m->apart, attn_decode_part_floats(NQ), sb);
+  ALLOC(m->ppart, (int64_t)4 * m->R * H, sb);
   ALLOC(m->counters, kMaxBatch * kKvHeads, sb);
   ALLOC(m->ss, 2 * 8 * 32, sb);
   ALLOC(m->ids_dev, std::max(d.max_positions, kMaxBatch), sb);
@@ -687,7 +689,23 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
   return GQA_OK;
 }
 
+// K ranges of a prefill projection onto the residual stream (N = hidden outputs over T rows):
+// about two workgroups per CU when the output tiles alone are too few, at most 8 ranges, at
+// least 4 K-steps per range, and at most 4 R rows of partials.
+int prefill_ksplit(const gqa_model* m, int N, int K, int T) {
+  const int tiles = (N / 256) * ((T + 127) / 128);
+  const int want = (2 * m->cu + tiles / 2) / tiles;
+  return std::max(1, std::min({want, 8, 4 * m->R / T, K / 32 / 4}));
+}
+
+constexpr int kProfNever = -1;   // a ProfScope class no recording selects
+
 // Prefill rounds over n ids already in device memory (ids_dev); see gqa_session_eval_prefill.
+// Per layer: q|k|v GEMM, q/k norm + RoPE + KV write, attention, o GEMM (K-range partials),
+// residual add of the partials + RMSNorm, gate|up GEMM with SwiGLU, down GEMM (partials), and
+// the next layer's residual add + RMSNorm. The logits need only the last row of the last layer:
+// after writing that layer's K/V, its attention, o and MLP run for the last row alone (and are
+// skipped in rounds before the last).
 int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, float* logits, int32_t* argmax, hipStream_t st) {
   gqa_model* m = s->m;
   const gqa_model_desc& d = m->d;
@@ -698,43 +716,48 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, float* logits, in
   for (int off = 0; off < n; off += m->R) {
     const int T = std::min(m->R, n - off);
     const int pos0 = s->pos + off;
+    const bool final_round = off + T == n;
     LAUNCH(launch_embed(m->embed, ids_dev + off, T, H, d.vocab, m->x, m->err, st));
     LAUNCH(launch_rmsnorm(m->x, H, nullptr, 0, 0, 0, 1.f, m->L[0].attn_norm, H, eps, 1.f, m->xh, m->xl, H, T, st));
     for (int l = 0; l < d.n_layers; ++l) {
       const LayerW& w = m->L[l];
+      const bool last = l + 1 == d.n_layers;
       LAUNCH(launch_gemm(EPI_STORE, split, w.pqkv, w.qqkv, w.sqkv, H, QKV, m->xh, m->xl, H, T, m->qkv, QKV, 1.f, nullptr,
-                         nullptr, 0, 1.f, st));
+                         nullptr, 0, 1.f, 1, 0, st));
       LAUNCH(launch_qk_rope_kv(false, m->qkv, 0, 0, QKV, NQ, w.q_norm, w.k_norm, eps, m->rcos, m->rsin, pos0,
                                s->d_table, none, w.kpool, w.vpool, m->q, T, st));
+      if (last && !final_round) break;
+      const int rows = last ? 1 : T, r0 = last ? T - 1 : 0;   // rows that feed the logits
       {
-        ProfScope ps(m, GQA_PROF_PREFILL_ATTN, st);
-        LAUNCH(launch_attn_prefill(m->q, NQ, T, pos0, s->d_table, w.kpool, w.vpool, kAttnOutScale, m->oh, m->ol, QD,
-                                   st));
+        ProfScope ps(m, last ? kProfNever : GQA_PROF_PREFILL_ATTN, st);
+        LAUNCH(launch_attn_prefill(m->q + (int64_t)r0 * QD, NQ, rows, pos0 + r0, s->d_table, w.kpool, w.vpool,
+                                   kAttnOutScale, m->oh, m->ol, QD, st));
       }
-      LAUNCH(launch_gemm(EPI_ADD, split, w.po, w.qo, w.so, QD, H, m->oh, m->ol, QD, T, m->x, H, 1.f / kAttnOutScale, nullptr,
-                         nullptr, 0, 1.f, st));
-      LAUNCH(launch_rmsnorm(m->x, H, nullptr, 0, 0, 0, 1.f, w.ffn_norm, H, eps, 1.f, m->xh, m->xl, H, T, st));
+      const int so = prefill_ksplit(m, H, QD, rows);
+      LAUNCH(launch_gemm(EPI_STORE, split, w.po, w.qo, w.so, QD, H, m->oh, m->ol, QD, rows, m->ppart, H, 1.f, nullptr,
+                         nullptr, 0, 1.f, so, (int64_t)rows * H, st));
+      LAUNCH(launch_rmsnorm(m->x + (int64_t)r0 * H, H, m->ppart, so, rows * H, H, 1.f / kAttnOutScale, w.ffn_norm, H,
+                            eps, 1.f, m->xh, m->xl, H, rows, st));
       {
-        ProfScope ps(m, GQA_PROF_PREFILL_GATEUP, st);
-        LAUNCH(launch_gemm(EPI_SWIGLU, split, w.pgu, w.qgu, w.sgu, H, 2 * F, m->xh, m->xl, H, T, nullptr, 0, 1.f, m->mh,
-                           m->ml, F, 1.f, st));
+        ProfScope ps(m, last ? kProfNever : GQA_PROF_PREFILL_GATEUP, st);
+        LAUNCH(launch_gemm(EPI_SWIGLU, split, w.pgu, w.qgu, w.sgu, H, 2 * F, m->xh, m->xl, H, rows, nullptr, 0, 1.f,
+                           m->mh, m->ml, F, 1.f, 1, 0, st));
       }
-      LAUNCH(launch_gemm(EPI_ADD, split, w.pd, w.qd, w.sd, F, H, m->mh, m->ml, F, T, m->x, H, 1.f, nullptr, nullptr, 0, 1.f,
-                         st));
-      if (l + 1 < d.n_layers)
-        LAUNCH(launch_rmsnorm(m->x, H, nullptr, 0, 0, 0, 1.f, m->L[l + 1].attn_norm, H, eps, 1.f, m->xh, m->xl, H, T,
-                              st));
-    }
-    if (off + T == n) {
-      LAUNCH(launch_rmsnorm(m->x + (int64_t)(T - 1) * H, H, nullptr, 0, 0, 0, 1.f, m->final_norm, H, eps, 1.f, m->xh,
-                            m->xl, H, 1, st));
-      XSrc raw{};
-      raw.mode = X_RAW;
-      raw.hi = m->xh;
-      raw.lo = m->xl;
-      raw.ld = H;
-      LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, H, V, raw, 1, 1, logits, 0, V, argmax ? m->cand : nullptr, st));
-      if (argmax) LAUNCH(launch_argmax(m->cand, V / 16, 1, argmax, st));
+      const int sd = prefill_ksplit(m, H, F, rows);
+      LAUNCH(launch_gemm(EPI_STORE, split, w.pd, w.qd, w.sd, F, H, m->mh, m->ml, F, rows, m->ppart, H, 1.f, nullptr,
+                         nullptr, 0, 1.f, sd, (int64_t)rows * H, st));
+      const uint16_t* next_norm = last ? m->final_norm : m->L[l + 1].attn_norm;
+      LAUNCH(launch_rmsnorm(m->x + (int64_t)r0 * H, H, m->ppart, sd, rows * H, H, 1.f, next_norm, H, eps, 1.f, m->xh,
+                            m->xl, H, rows, st));
+      if (last) {
+        XSrc raw{};
+        raw.mode = X_RAW;
+        raw.hi = m->xh;
+        raw.lo = m->xl;
+        raw.ld = H;
+        LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, H, V, raw, 1, 1, logits, 0, V, argmax ? m->cand : nullptr, st));
+        if (argmax) LAUNCH(launch_argmax(m->cand, V / 16, 1, argmax, st));
+      }
     }
   }
   s->pos += n;

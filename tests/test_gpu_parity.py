@@ -429,9 +429,9 @@ def test_qwen3_4b_q8_0_reduced_depth_parity(g):
 def test_qwen3_4b_q8_0_full_prompt(g):
     """The Q8_0 4B workload at full size: 36 layers, the 12,800-token prompt in the device's
     rounds over a shuffled paged KV (pool four times the session's need).
-    (1) The last layer's attention output for sampled rows of the last round equals an FP64
-        softmax(q K^T / sqrt(128)) V over all visible positions, computed on the host from the
-        read-back rotated q of that round and the BF16 K/V of all 12,800 positions.
+    (1) The last layer's attention output at the last position (all 32 heads) equals an FP64
+        softmax(q K^T / sqrt(128)) V over all 12,800 positions, computed on the host from the
+        read-back rotated q and BF16 K/V.
     (2) Decoding the prompt's argmax token gives the logits of prefilling the 12,801 tokens in a
         second session (matvec path vs GEMM path), within NMSE 1e-5, same argmax unless the
         top-2 margin is a near tie."""
@@ -455,27 +455,25 @@ def test_qwen3_4b_q8_0_full_prompt(g):
     tok = int(am.item())
     assert tok == int(np.argmax(first))
 
-    # (1) attention of layer L-1 in the last round (rows last0 .. T-1)
+    # (1) attention of layer L-1 for the last position: the prefill evaluates the last layer's
+    #     attention for the last row only and stores it as row 0 of the operand rows (times 16)
     nq, G = shape.n_q_heads, shape.n_q_heads // 8
     last0 = ((T - 1) // R) * R
     Tl = T - last0
-    q = m.read_scratch("qrot", 0, Tl * nq * 128).reshape(Tl, nq, 128).astype(np.float64)
-    o_hi = m.read_scratch("attn_hi", 0, Tl * nq * 128).astype(np.float64)
-    o_lo = m.read_scratch("attn_lo", 0, Tl * nq * 128).astype(np.float64)
-    o_gpu = ((o_hi + o_lo) / 16.0).reshape(Tl, nq, 128)      # the operand rows are stored times 16
+    q = m.read_scratch("qrot", (Tl - 1) * nq * 128, nq * 128).reshape(nq, 128).astype(np.float64)
+    o_hi = m.read_scratch("attn_hi", 0, nq * 128).astype(np.float64)
+    o_lo = m.read_scratch("attn_lo", 0, nq * 128).astype(np.float64)
+    o_gpu = ((o_hi + o_lo) / 16.0).reshape(nq, 128)
     kb, vb = s.read_kv(shape.n_layers - 1, 0, T)
     worst = 0.0
-    for t in (0, Tl // 2, Tl - 1):
-        p = last0 + t
-        for h in (0, 13, nq - 1):
-            kf = _bf16_to_f64(kb[: p + 1, h // G])
-            vf = _bf16_to_f64(vb[: p + 1, h // G])
-            sc = kf @ q[t, h] / np.sqrt(128.0)
-            w = np.exp(sc - sc.max())
-            ref_o = (w @ vf) / w.sum()
-            e = float(np.sum((o_gpu[t, h] - ref_o) ** 2) / np.sum(ref_o ** 2))
-            worst = max(worst, e)
-    say("4b-q8 attention spot check at %d positions: worst NMSE %.3e" % (T, worst))
+    for h in range(nq):
+        kf = _bf16_to_f64(kb[:, h // G])
+        vf = _bf16_to_f64(vb[:, h // G])
+        sc = kf @ q[h] / np.sqrt(128.0)
+        w = np.exp(sc - sc.max())
+        ref_o = (w @ vf) / w.sum()
+        worst = max(worst, float(np.sum((o_gpu[h] - ref_o) ** 2) / np.sum(ref_o ** 2)))
+    say("4b-q8 attention of position %d over %d keys, 32 heads: worst NMSE %.3e" % (T - 1, T, worst))
     assert worst <= 1e-9
 
     # (2) decode after the prompt vs prefill of prompt + token
