@@ -405,7 +405,7 @@ __device__ __forceinline__ void merge_head(const float* pp, int nchunk, int lane
   *(f16x2*)(olo + 2 * lane) = f16x2{l0, l1};
 }
 
-template <int G>
+template <int G, bool FUSED>
 __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
     const float* __restrict__ qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* __restrict__ ss,
     int ss_n, int H, const uint16_t* __restrict__ wqn, const uint16_t* __restrict__ wkn, float eps,
@@ -633,6 +633,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
     }
     pp[4 + d] = O;
   }
+  if (!FUSED) return;                     // attn_merge_kernel combines the partials
   // 5. the last workgroup of this (row, KV head) to finish merges the chunk partials. Every wave
   //    waits until its partial stores have completed, then one thread publishes them device-wide
   //    (a device-scope release writes back this XCD's L2) and counts the workgroup in; the last
@@ -655,6 +656,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
                ohi + (int64_t)b * ldo + h * kHeadDim, olo + (int64_t)b * ldo + h * kHeadDim);
   }
   if (tid == 0) counters[b * kKvHeads + kvh] = 0;
+}
+
+// Chunk merge as a kernel of its own, for large batches: grid (KV head, row), one wave per query
+// head of the group. The kernel boundary orders it after every chunk partial, so no workgroup
+// of the attention kernel needs a device-scope fence (with thousands of workgroups those
+// fences, each writing back an XCD's L2, serialise). Same arithmetic as the fused merge.
+template <int G>
+__global__ __launch_bounds__(64 * G) void attn_merge_kernel(const float* __restrict__ part, int nq, Rows rows,
+                                                           float out_scale, f16* __restrict__ ohi,
+                                                           f16* __restrict__ olo, int ldo) {
+  const int kvh = blockIdx.x, b = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ctx = rows.pos[b] + 1, CH = decode_chunk_len(ctx), nchunk = (ctx + CH - 1) / CH;
+  const int h = kvh * G + wave;
+  merge_head(part + ((int64_t)b * nq + h) * kDecodeMaxChunks * kPartStride, nchunk, lane, out_scale,
+             ohi + (int64_t)b * ldo + h * kHeadDim, olo + (int64_t)b * ldo + h * kHeadDim);
 }
 
 hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const int32_t* table, const uint16_t* kpool,
@@ -686,16 +702,27 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
   const int chunks = (max_ctx + CH - 1) / CH;          // rows with shorter contexts exit early
   dim3 grid(chunks, kKvHeads, B);
   const int G = nq / kKvHeads;
-#define DEC_LAUNCH(GG)                                                                                           \
-  hipLaunchKernelGGL(attn_decode_kernel<GG>, grid, dim3(64 * kDecodeWaves), 0, st, qkvp, nsplit, pstride, QKV, nq, \
-                     ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, kpool, vpool, part, counters, out_scale, ohi, olo, \
-                     ldo)
-  if (G == 4)
-    DEC_LAUNCH(4);
-  else if (G == 2)
-    DEC_LAUNCH(2);
-  else
-    return hipErrorInvalidValue;
+  // up to four rows: the last workgroup of a (row, KV head) merges; more rows: a merge kernel
+  const bool fused = B <= 4;
+#define DEC_LAUNCH(GG, FU)                                                                                         \
+  hipLaunchKernelGGL((attn_decode_kernel<GG, FU>), grid, dim3(64 * kDecodeWaves), 0, st, qkvp, nsplit, pstride, QKV, \
+                     nq, ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, kpool, vpool, part, counters, out_scale, ohi,  \
+                     olo, ldo)
+  if (G != 4 && G != 2) return hipErrorInvalidValue;
+  if (fused) {
+    if (G == 4) DEC_LAUNCH(4, true);
+    else DEC_LAUNCH(2, true);
+  } else {
+    if (G == 4) {
+      DEC_LAUNCH(4, false);
+      hipLaunchKernelGGL(attn_merge_kernel<4>, dim3(kKvHeads, B), dim3(256), 0, st, part, nq, rows, out_scale, ohi, olo,
+                         ldo);
+    } else {
+      DEC_LAUNCH(2, false);
+      hipLaunchKernelGGL(attn_merge_kernel<2>, dim3(kKvHeads, B), dim3(128), 0, st, part, nq, rows, out_scale, ohi, olo,
+                         ldo);
+    }
+  }
 #undef DEC_LAUNCH
   return hipGetLastError();
 }
