@@ -13,8 +13,10 @@
 //
 // Tiling: a 256-thread workgroup computes a 256 (weight rows) x 128 (tokens) tile; each wave a
 // 128 x 64 quadrant of 4 x 2 v_mfma_f32_32x32x16_f16 tiles (A = 32 weight rows, B = 32 tokens).
-// K advances 32 per step through two LDS buffers: the next step's global loads are in flight
-// during the current step's MFMAs and are written to the other buffer, one barrier per step.
+// K advances 32 per step through two LDS buffers filled by direct-to-LDS loads: the next step's
+// copies are in flight during the current step's MFMAs, one barrier per step. Q8_0 quants are
+// copied as bytes (half the traffic of FP16) and widened to FP16 when the A operand is read
+// (exact: 0x6400 | (q + 128) is the FP16 value 1152 + q).
 // Workgroups walk the output tiles in groups of 8 weight-row blocks x all token blocks, and the
 // tiles are dealt to the eight XCDs in contiguous runs, so the workgroups resident on one XCD at
 // a time share their weight and activation tiles in that XCD's L2.
@@ -28,6 +30,25 @@
 #include "gqa_common.h"
 
 namespace gqa {
+
+// Eight int8 quants (two dwords) -> eight exact FP16 values: the byte q + 128 (q ^ 0x80) below the
+// FP16 pattern 0x64 is the value 1152 + q, and subtracting 1152 is exact.
+__device__ __forceinline__ f16x8 i8x8_to_f16x8(uint2 v) {
+  const uint32_t x0 = v.x ^ 0x80808080u, x1 = v.y ^ 0x80808080u;
+  const uint32_t h[4] = {__builtin_amdgcn_perm(0x64646464u, x0, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, x0, 0x05030402u),
+                         __builtin_amdgcn_perm(0x64646464u, x1, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, x1, 0x05030402u)};
+  const f16x2 bias = {(f16)1152.0f, (f16)1152.0f};
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 q = __builtin_bit_cast(f16x2, h[i]) - bias;
+    r[2 * i] = q[0];
+    r[2 * i + 1] = q[1];
+  }
+  return r;
+}
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -55,22 +76,23 @@ struct GemmArgs {
 constexpr int kGemmBN = 256, kGemmBT = 128, kGemmBK = 32;
 constexpr int kGemmGroup = 8;        // weight-row blocks per tile group
 
+// The Q8_0 instances decode quants and apply per-block scales in registers; bounding them to one workgroup per CU
+// gives them the full register file (no spills), which measured 2.3-2.8x faster than two spilling workgroups.
 template <int EPI, bool Q8, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256, Q8 ? 1 : 2) void gemm_kernel(GemmArgs g) {
   constexpr int BN = kGemmBN, BT = kGemmBT, BK = kGemmBK;
-  // BF16 models (FP16 prefill copy): global -> LDS by direct-to-LDS loads (no registers, no
-  // conversion), activation rows swizzled instead of padded. Q8_0 models: through registers
-  // (int8 -> FP16), activation rows padded to 80 bytes. Both give conflict-free operand reads.
-  constexpr bool DMA = !Q8;
-  constexpr int XLD = DMA ? BK : BK + 8;         // halves per token row in LDS
   constexpr int TN = 4, TT = 2;                  // 32x32 tiles per wave
+  // Per buffer: weights (FP16 in operand order, or Q8_0 int8 quants: 16 bands x 512 bytes, the
+  // odd bands rotated by 128 bytes so that the two bands a half-wave reads hit different banks),
+  // the Q8_0 scales of the step (256 fp16), and the activation hi / lo rows (token t's 16-byte
+  // pieces swizzled by xswz).
   __shared__ __attribute__((aligned(16))) f16 sW[2][BN * BK];
-  __shared__ __attribute__((aligned(16))) f16 sXh[2][BT * XLD];
-  __shared__ __attribute__((aligned(16))) f16 sXl[SPLIT ? 2 : 1][SPLIT ? BT * XLD : 8];
+  __shared__ __attribute__((aligned(16))) f16 sS[2][Q8 ? 512 : 8];
+  __shared__ __attribute__((aligned(16))) f16 sXh[2][BT * BK];
+  __shared__ __attribute__((aligned(16))) f16 sXl[SPLIT ? 2 : 1][SPLIT ? BT * BK : 8];
   auto bufW = [&](int b) -> f16* { return sW[b]; };
   auto bufXh = [&](int b) -> f16* { return sXh[b]; };
   auto bufXl = [&](int b) -> f16* { return sXl[SPLIT ? b : 0]; };
-  __shared__ float sD[2][Q8 ? BN : 1];
 
   // ---- tile and K range of this workgroup: XCD-contiguous runs of a grouped order of
   //      (K range, tile) items, tiles of one K range consecutive
@@ -93,78 +115,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   const int wn = (wave & 1) * 128, wt = (wave >> 1) * 64;
   const int l32 = lane & 31, hf = lane >> 5;
 
-  // ---- global -> register staging of one K-step
-  constexpr int PW = BN * BK / 8 / 256;          // 16-byte weight pieces per thread (4)
-  constexpr int PX = BT * BK / 8 / 256;          // 16-byte activation pieces per thread and half (2)
-  struct Stage {
-    uint4 w[PW];
-    uint2 q[Q8 ? PW : 1];
-    uint4 xh[PX], xl[SPLIT ? PX : 1];
-    f16 d;
-  };
-  // 32-bit per-thread offsets from workgroup-uniform bases (one scalar base + one VGPR per load)
-  // BF16 models read the FP16 prefill copy: piece c = 32-row block c / 128, position c % 128 of
-  // its 2 KiB K-step (already in LDS order). Q8_0 models read the tile-major quants: piece c =
-  // 16-row band c / 64, lane-order position c % 64.
-  const int64_t band0 = (int64_t)(n0 >> 4) * (K >> 5);
-  const int64_t blk0 = (int64_t)(n0 >> 5) * (K >> 5);
-  uint32_t woff[PW], xoff[PX];
-#pragma unroll
-  for (int i = 0; i < PW; ++i) {
-    const int c = tid + 256 * i;
-    woff[i] = Q8 ? (uint32_t)((c >> 6) * (K >> 5)) * 512u + (uint32_t)(c & 63) * 8u
-                 : (uint32_t)((c >> 7) * (K >> 5)) * 1024u + (uint32_t)(c & 127) * 8u;
-  }
-#pragma unroll
-  for (int i = 0; i < PX; ++i) {
-    const int c = tid + 256 * i, tok = c >> 2, kc = c & 3;
-    xoff[i] = (uint32_t)(min(t0 + tok, T - 1) * g.ldx + kc * 8);   // rows past T: a valid row, never stored
-  }
-  const uint32_t doff = (uint32_t)((tid >> 4) * (K >> 5)) * 16u + (uint32_t)(tid & 15);
-  auto gload = [&](Stage& r, int k0) {
-    k0 = min(k0, K - BK);                        // past the end: reload the last step (never used)
-    const int64_t kw = band0 + (k0 >> 5), kb = blk0 + (k0 >> 5);
-#pragma unroll
-    for (int i = 0; i < PW; ++i) {
-      if (Q8)
-        r.q[i] = *(const uint2*)(g.Wq + kw * 512 + woff[i]);
-      else
-        r.w[i] = *(const uint4*)(g.W + kb * 1024 + woff[i]);
-    }
-    if (Q8) r.d = g.Wd[kw * 16 + doff];
-#pragma unroll
-    for (int i = 0; i < PX; ++i) {
-      r.xh[i] = *(const uint4*)(g.Xhi + k0 + xoff[i]);
-      if (SPLIT) r.xl[i] = *(const uint4*)(g.Xlo + k0 + xoff[i]);
-    }
-  };
-  auto sstore = [&](const Stage& r, int buf) {
-#pragma unroll
-    for (int i = 0; i < PW; ++i) {
-      const int c = tid + 256 * i;
-      if (Q8) {
-        f16x8 v;
-        const uint32_t lo = r.q[i].x, hi = r.q[i].y;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = (f16)(float)(int8_t)((lo >> (8 * e)) & 0xFF);      // exact small integers
-          v[4 + e] = (f16)(float)(int8_t)((hi >> (8 * e)) & 0xFF);
-        }
-        // band c / 64, position g * 16 + r -> LDS order [block][kh][hf][row 32][8]
-        const int band = c >> 6, gq = (c >> 4) & 3, rr = c & 15;
-        *(f16x8*)&bufW(buf)[(band >> 1) * 1024 + (gq >> 1) * 512 + (gq & 1) * 256 + ((band & 1) * 16 + rr) * 8] = v;
-      } else {
-        *(uint4*)&bufW(buf)[c * 8] = r.w[i];
-      }
-    }
-    if (Q8) sD[buf][tid] = (float)r.d;
-#pragma unroll
-    for (int i = 0; i < PX; ++i) {
-      const int c = tid + 256 * i, tok = c >> 2, kc = c & 3;
-      *(uint4*)&bufXh(buf)[tok * XLD + kc * 8] = r.xh[i];
-      if (SPLIT) *(uint4*)&bufXl(buf)[tok * XLD + kc * 8] = r.xl[i];
-    }
-  };
+  const int64_t band0 = (int64_t)(n0 >> 4) * (K >> 5);   // Q8_0: first 16-row band's chunk index
+  const int64_t blk0 = (int64_t)(n0 >> 5) * (K >> 5);    // FP16: first 32-row block's piece index
 
   f32x16 acc[TN][TT];
 #pragma unroll
@@ -185,8 +137,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   auto xswz = [](int t) { return ((t >> 2) ^ (t >> 3)) & 3; };
   auto b_op = [&](const f16* sx, int j, int kh) {
     const int t = wt + 32 * j + l32;
-    if (DMA) return *(const f16x8*)&sx[(t * 4 + ((2 * kh + hf) ^ xswz(t))) * 8];
-    return *(const f16x8*)&sx[t * XLD + kh * 16 + hf * 8];
+    return *(const f16x8*)&sx[(t * 4 + ((2 * kh + hf) ^ xswz(t))) * 8];
   };
 
   auto compute = [&](int cur) {
@@ -201,29 +152,35 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
           bh[j][kh] = b_op(sxh, j, kh);
           if (SPLIT) bl[j][kh] = b_op(sxl, j, kh);
         }
+      const uint8_t* wq = (const uint8_t*)bufW(cur);
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
-        const f16x8 a0 = a_op(cur, i, 0), a1 = a_op(cur, i, 1);
-        float sc[16];
+        // rows wn + 32 i + l32: band 2 ((wn >> 5) + i) + l32 / 16, row l32 % 16 of it; the quants
+        // of K-half kh for lane half hf are chunk position (16 (2 kh + hf) + row) * 8
+        const int band = 2 * ((wn >> 5) + i) + (l32 >> 4), r = l32 & 15;
+        f16x8 a[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const int slot = ((8 * (2 * kh + hf) + (r >> 1)) + 8 * (band & 1)) & 31;
+          a[kh] = i8x8_to_f16x8(*(const uint2*)(wq + band * 512 + slot * 16 + (r & 1) * 8));
+        }
+        // scales of the accumulator rows 32 i + 8 q + 4 hf + 0..3 of this wave's quadrant
+        f16 sc[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float4 v = *(const float4*)&sD[cur][wn + 32 * i + q * 8 + hf * 4];
-          sc[4 * q] = v.x;
-          sc[4 * q + 1] = v.y;
-          sc[4 * q + 2] = v.z;
-          sc[4 * q + 3] = v.w;
+          const f16x4 v = *(const f16x4*)&sS[cur][wn + 32 * i + 8 * q + 4 * hf];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[4 * q + e] = v[e];
         }
 #pragma unroll
         for (int j = 0; j < TT; ++j) {
-          f32x16 p;
+          f32x16 p = f32x16{};
+          p = mfma32(a[0], bh[j][0], p);
+          if (SPLIT) p = mfma32(a[0], bl[j][0], p);
+          p = mfma32(a[1], bh[j][1], p);
+          if (SPLIT) p = mfma32(a[1], bl[j][1], p);
 #pragma unroll
-          for (int e = 0; e < 16; ++e) p[e] = 0.f;
-          p = mfma32(a0, bh[j][0], p);
-          if (SPLIT) p = mfma32(a0, bl[j][0], p);
-          p = mfma32(a1, bh[j][1], p);
-          if (SPLIT) p = mfma32(a1, bl[j][1], p);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[i][j][e] = fmaf(sc[e], p[e], acc[i][j][e]);
+          for (int e = 0; e < 16; ++e) acc[i][j][e] = fmaf((float)sc[e], p[e], acc[i][j][e]);
         }
       }
     } else {
@@ -250,64 +207,61 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 
   const int nsteps = s_end - s_begin;
   int cur = 0;
-  if constexpr (DMA) {
-    // Pipeline: LDS buffer s % 2 holds step s; step s + 1 streams into the other buffer by
-    // direct-to-LDS loads during step s's MFMAs. Each wave issues 4 + 2 (+ 2) kilobyte loads per
-    // step; the LDS destination of a wave-wide load is contiguous in lane order.
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    uint32_t dw[4], dx[2];
+  // Pipeline: LDS buffer s % 2 holds step s; step s + 1 streams into the other buffer by
+  // direct-to-LDS loads during step s's MFMAs. Per step each wave copies 2 KiB of activation
+  // hi (and lo) rows, and 4 KiB of FP16 weights or 2 KiB of Q8_0 quants (wave 0 also the 512
+  // bytes of scales); the LDS destination of a wave-wide load is contiguous in lane order.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t dw[4], dx[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 4; ++i) {
+    if (Q8) {
+      // quants: load 2 wv + i (i < 2) covers bands 2 (2 wv + i) + l / 32; LDS slot l % 32 holds
+      // chunk slot (l % 32 - 8 (band & 1)) & 31
+      const int b = 2 * (2 * wv + (i & 1)) + (lane >> 5), slot = ((lane & 31) - 8 * (b & 1)) & 31;
+      dw[i] = (uint32_t)(b * (K >> 5)) * 512u + (uint32_t)slot * 16u;
+    } else {
       const int c = (wv * 4 + i) * 64 + lane;    // piece c of the step, as in memory
       dw[i] = (uint32_t)((c >> 7) * (K >> 5)) * 1024u + (uint32_t)(c & 127) * 8u;
     }
+  }
+  // scales: lane l < 32 brings half l % 2 of band l / 2's 16 scales (lanes 32.. repeat them)
+  const uint32_t ds = (uint32_t)(((lane & 31) >> 1) * (K >> 5)) * 16u + (uint32_t)(lane & 1) * 8u;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int slot = (wv * 2 + i) * 64 + lane, t = slot >> 2, kc = (slot & 3) ^ xswz(t);
-      dx[i] = (uint32_t)(min(t0 + t, T - 1) * g.ldx + kc * 8);      // rows past T: a valid row, never stored
-    }
-    // Direct-to-LDS copies: every barrier that publishes a filled buffer follows dma_wait().
-    auto dma1 = [](const f16* src, const f16* lds_dst) { lds_dma16(src, lds_dst); };
-    auto dma = [&](int buf, int k0) {
+  for (int i = 0; i < 2; ++i) {
+    const int slot = (wv * 2 + i) * 64 + lane, t = slot >> 2, kc = (slot & 3) ^ xswz(t);
+    dx[i] = (uint32_t)(min(t0 + t, T - 1) * g.ldx + kc * 8);      // rows past T: a valid row, never stored
+  }
+  // Direct-to-LDS copies: every barrier that publishes a filled buffer follows dma_wait().
+  auto dma = [&](int buf, int k0) {
+    if (Q8) {
+      const int8_t* qsrc = g.Wq + (band0 + (k0 >> 5)) * 512;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) lds_dma16(qsrc + dw[i], (const uint8_t*)bufW(buf) + (2 * wv + i) * 1024);
+      if (wv == 0) lds_dma16(g.Wd + (band0 + (k0 >> 5)) * 16 + ds, sS[buf]);
+    } else {
       const f16* wsrc = g.W + (blk0 + (k0 >> 5)) * 1024;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma1(wsrc + dw[i], &bufW(buf)[(wv * 4 + i) * 512]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        dma1(g.Xhi + k0 + dx[i], &bufXh(buf)[(wv * 2 + i) * 512]);
-        if (SPLIT) dma1(g.Xlo + k0 + dx[i], &bufXl(buf)[(wv * 2 + i) * 512]);
-      }
-    };
-    auto dma_wait = []() { vm_wait_all(); };
-    dma(0, kbase);
-    dma_wait();
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {            // buffer cur holds step s
-      const bool more = s + 1 < nsteps;
-      if (more) dma(cur ^ 1, kbase + (s + 1) * BK);
-      compute(cur);
-      if (more) {
-        dma_wait();                               // this wave's loads of step s + 1 have landed
-        __syncthreads();                          // ... and every other wave's
-        cur ^= 1;
-      }
+      for (int i = 0; i < 4; ++i) lds_dma16(wsrc + dw[i], &bufW(buf)[(wv * 4 + i) * 512]);
     }
-  } else {
-    // Pipeline: LDS buffer s % 2 holds step s; the registers hold step s + 1, whose global loads
-    // are in flight during step s's MFMAs.
-    Stage r;
-    gload(r, kbase);
-    sstore(r, 0);
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-      const bool more = s + 1 < nsteps;
-      if (more) gload(r, kbase + (s + 1) * BK);
-      compute(cur);
-      if (more) {
-        sstore(r, cur ^ 1);
-        __syncthreads();
-        cur ^= 1;
-      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lds_dma16(g.Xhi + k0 + dx[i], &bufXh(buf)[(wv * 2 + i) * 512]);
+      if (SPLIT) lds_dma16(g.Xlo + k0 + dx[i], &bufXl(buf)[(wv * 2 + i) * 512]);
+    }
+  };
+  auto dma_wait = []() { vm_wait_all(); };
+  dma(0, kbase);
+  dma_wait();
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {            // buffer cur holds step s
+    const bool more = s + 1 < nsteps;
+    if (more) dma(cur ^ 1, kbase + (s + 1) * BK);
+    compute(cur);
+    if (more) {
+      dma_wait();                               // this wave's loads of step s + 1 have landed
+      __syncthreads();                          // ... and every other wave's
+      cur ^= 1;
     }
   }
 
