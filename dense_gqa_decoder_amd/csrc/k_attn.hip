@@ -374,16 +374,27 @@ __device__ __forceinline__ void bf16x8_to_f32(uint4 v, float (&f)[8]) {
   f[6] = bf16_bits_to_f32(v.w & 0xFFFF); f[7] = bf16_bits_to_f32(v.w >> 16);
 }
 
+// Device-scope (sc1) accesses: coherent across the XCDs' L2 caches without an L2 writeback or
+// invalidate. The fused chunk merge passes its partials through these, so the only ordering it
+// needs is that the stores have completed before the workgroup is counted in.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_dev2(const float* p) {
+  const uint64_t v = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(float2, v);
+}
+
 // Combine the chunk partials of one (row, query head) in chunk order: o = sum_c w_c o_c / sum_c
 // w_c l_c with w_c = 2^(m_c - max m). One wave; lane t owns dims 2t, 2t + 1. The result is
 // written as the FP16 hi/lo operand of the o projection, times out_scale.
 __device__ __forceinline__ void merge_head(const float* pp, int nchunk, int lane, float out_scale, f16* ohi,
                                            f16* olo) {
-  const float2 ml = *(const float2*)(pp + (int64_t)min(lane, nchunk - 1) * kPartStride);
+  const float2 ml = load_dev2(pp + (int64_t)min(lane, nchunk - 1) * kPartStride);
   float2 ov[kDecodeMaxChunks];
 #pragma unroll
   for (int cc = 0; cc < kDecodeMaxChunks; ++cc)
-    ov[cc] = *(const float2*)(pp + (int64_t)min(cc, nchunk - 1) * kPartStride + 4 + 2 * lane);
+    ov[cc] = load_dev2(pp + (int64_t)min(cc, nchunk - 1) * kPartStride + 4 + 2 * lane);
   const float mv = lane < nchunk ? ml.x : -INFINITY;
   const float M = wave_max(mv);
   const float wt = lane < nchunk ? exp2f(mv - M) : 0.f;
@@ -627,26 +638,32 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
 #pragma unroll
     for (int w = 0; w < NST; ++w) O = fmaf(so[w][hh][d], sw[w][hh], O);
     float* pp = part + (((int64_t)b * nq + kvh * G + hh) * kDecodeMaxChunks + c) * kPartStride;
-    if (d == 0) {
-      pp[0] = sML[hh][0];
-      pp[1] = sML[hh][1];
+    if (FUSED) {                          // read by another workgroup of this launch
+      if (d == 0) {
+        store_dev(pp, sML[hh][0]);
+        store_dev(pp + 1, sML[hh][1]);
+      }
+      store_dev(pp + 4 + d, O);
+    } else {                              // read by attn_merge_kernel after this launch
+      if (d == 0) {
+        pp[0] = sML[hh][0];
+        pp[1] = sML[hh][1];
+      }
+      pp[4 + d] = O;
     }
-    pp[4 + d] = O;
   }
   if (!FUSED) return;                     // attn_merge_kernel combines the partials
-  // 5. the last workgroup of this (row, KV head) to finish merges the chunk partials. Every wave
-  //    waits until its partial stores have completed, then one thread publishes them device-wide
-  //    (a device-scope release writes back this XCD's L2) and counts the workgroup in; the last
-  //    workgroup acquires (invalidating its stale cache lines) before any wave reads the other
-  //    workgroups' partials, and resets the count for the next call.
+  // 5. the last workgroup of this (row, KV head) to finish merges the chunk partials. The
+  //    partials went out as device-scope stores and are read back with device-scope loads, so
+  //    no cache writeback or invalidate is needed: every wave waits until its stores have
+  //    completed, then one thread counts the workgroup in; the last workgroup merges and resets
+  //    the count for the next call.
   __builtin_amdgcn_s_waitcnt(0);          // vmcnt = lgkmcnt = 0: this wave's stores are done
   __syncthreads();
   if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const int old = __hip_atomic_fetch_add(&counters[b * kKvHeads + kvh], 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
     s_last = old == nchunk - 1;
-    if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
   if (!s_last) return;
