@@ -387,14 +387,17 @@ __device__ __forceinline__ float2 load_dev2(const float* p) {
 
 // Combine the chunk partials of one (row, query head) in chunk order: o = sum_c w_c o_c / sum_c
 // w_c l_c with w_c = 2^(m_c - max m). One wave; lane t owns dims 2t, 2t + 1. The result is
-// written as the FP16 hi/lo operand of the o projection, times out_scale.
+// written as the FP16 hi/lo operand of the o projection, times out_scale. DEV: the partials
+// were written by other workgroups of the same launch (device-scope loads).
+template <bool DEV>
 __device__ __forceinline__ void merge_head(const float* pp, int nchunk, int lane, float out_scale, f16* ohi,
                                            f16* olo) {
-  const float2 ml = load_dev2(pp + (int64_t)min(lane, nchunk - 1) * kPartStride);
+  auto ld2 = [](const float* p) { return DEV ? load_dev2(p) : *(const float2*)p; };
+  const float2 ml = ld2(pp + (int64_t)min(lane, nchunk - 1) * kPartStride);
   float2 ov[kDecodeMaxChunks];
 #pragma unroll
   for (int cc = 0; cc < kDecodeMaxChunks; ++cc)
-    ov[cc] = load_dev2(pp + (int64_t)min(cc, nchunk - 1) * kPartStride + 4 + 2 * lane);
+    ov[cc] = ld2(pp + (int64_t)min(cc, nchunk - 1) * kPartStride + 4 + 2 * lane);
   const float mv = lane < nchunk ? ml.x : -INFINITY;
   const float M = wave_max(mv);
   const float wt = lane < nchunk ? exp2f(mv - M) : 0.f;
@@ -669,8 +672,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
   if (!s_last) return;
   if (wave < G) {
     const int h = kvh * G + wave;
-    merge_head(part + ((int64_t)b * nq + h) * kDecodeMaxChunks * kPartStride, nchunk, lane, out_scale,
-               ohi + (int64_t)b * ldo + h * kHeadDim, olo + (int64_t)b * ldo + h * kHeadDim);
+    merge_head<true>(part + ((int64_t)b * nq + h) * kDecodeMaxChunks * kPartStride, nchunk, lane, out_scale,
+                     ohi + (int64_t)b * ldo + h * kHeadDim, olo + (int64_t)b * ldo + h * kHeadDim);
   }
   if (tid == 0) counters[b * kKvHeads + kvh] = 0;
 }
@@ -686,8 +689,8 @@ __global__ __launch_bounds__(64 * G) void attn_merge_kernel(const float* __restr
   const int kvh = blockIdx.x, b = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ctx = rows.pos[b] + 1, CH = decode_chunk_len(ctx), nchunk = (ctx + CH - 1) / CH;
   const int h = kvh * G + wave;
-  merge_head(part + ((int64_t)b * nq + h) * kDecodeMaxChunks * kPartStride, nchunk, lane, out_scale,
-             ohi + (int64_t)b * ldo + h * kHeadDim, olo + (int64_t)b * ldo + h * kHeadDim);
+  merge_head<false>(part + ((int64_t)b * nq + h) * kDecodeMaxChunks * kPartStride, nchunk, lane, out_scale,
+                    ohi + (int64_t)b * ldo + h * kHeadDim, olo + (int64_t)b * ldo + h * kHeadDim);
 }
 
 hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const int32_t* table, const uint16_t* kpool,

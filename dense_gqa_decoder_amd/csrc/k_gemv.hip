@@ -297,6 +297,176 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* _
   }
 }
 
+// B > 4 token rows (X_RAW operands in global memory). The operand rows of the workgroup's K
+// range pass through LDS 256 K-elements at a time: per stage each staged row is one 1 KiB
+// direct-to-LDS copy (hi then lo half), double-buffered, shared by the eight waves (eight 16-row
+// bands) of the workgroup, so the activations cross the L2-to-CU path once per workgroup instead
+// of once per wave. Each wave streams its band's weights one stage ahead in registers and runs
+// the same MFMA chain per (band, K range) as gemv_kernel, so the partials are bit-identical to
+// the B <= 4 paths. The weight loads and copies are unconditional (clamped addresses; steps past
+// the range are skipped in compute), so a wave issues exactly the same number per stage and one
+// vmcnt wait covers a stage's operand copies and the weights of the stage before.
+constexpr int kRowsWaves = 8;
+constexpr int kRowsStageK = 256;
+constexpr int kRowsPitch = 2 * kRowsStageK + 8;   // f16 per staged row: hi | lo | 16 bytes pad
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <bool Q8, int NT>
+__global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows_kernel(const uint16_t* __restrict__ W,
+                                                                   const int8_t* __restrict__ Wq,
+                                                                   const f16* __restrict__ Wd, int K, int N, XSrc xs,
+                                                                   int B, int klen, float* __restrict__ P,
+                                                                   int64_t part_stride, int ldp,
+                                                                   float2* __restrict__ cand) {
+  constexpr int U = kRowsStageK / 32;                 // K-steps per stage
+  constexpr int ROWS = 16 * NT;                       // staged token rows
+  constexpr int RPW = ROWS / kRowsWaves;              // staged rows copied per wave
+  constexpr int BUF = ROWS * kRowsPitch;              // f16 per buffer
+  constexpr int NF = Q8 ? 2 * U : U;                  // weight loads per stage and wave
+  __shared__ __attribute__((aligned(16))) f16 sx[2 * BUF];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int tile = blockIdx.x * kRowsWaves + wave;
+  const bool has_tile = tile * 16 < N;
+  const int n0 = (has_tile ? tile : 0) * 16;
+  const int s = blockIdx.y;
+  const int k0 = s * klen, ke = k0 + klen;
+  const int nstage = (klen + kRowsStageK - 1) / kRowsStageK;
+  const int64_t band = (int64_t)(n0 >> 4) * (K >> 5);
+
+  struct Buf {
+    uint4 wv[U];
+    uint2 qv[U];
+    uint2 sc[U];
+  };
+  auto fetch = [&](Buf& f, int t) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = min(k0 + t * kRowsStageK + u * 32, ke - 32);
+      const int64_t chunk = band + (kk >> 5);
+      if (Q8) {
+        f.qv[u] = *(const uint2*)(Wq + chunk * 512 + lane * 8);
+        f.sc[u] = *(const uint2*)(Wd + chunk * 16 + g4 * 4);
+      } else {
+        f.wv[u] = *(const uint4*)(W + chunk * 512 + lane * 8);
+      }
+    }
+  };
+  // stage t's operand rows into buffer t & 1: lanes 0-31 copy the hi pieces, 32-63 the lo pieces
+  auto issue_x = [&](int t) {
+    const int hl = lane >> 5;
+    const int kk = min(k0 + t * kRowsStageK + (lane & 31) * 8, ke - 8);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int row = wave * RPW + i;
+      const f16* src = (hl ? xs.lo : xs.hi) + (int64_t)min(row, B - 1) * xs.ld + kk;
+      lds_dma16(src, sx + (t & 1) * BUF + row * kRowsPitch);
+    }
+  };
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Buf& f, int t) {
+    const f16* xb = sx + (t & 1) * BUF + r16 * kRowsPitch + g4 * 8;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k0 + t * kRowsStageK + u * 32 >= ke) break;
+      f16x8 bh[NT], bl[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        bh[j] = *(const f16x8*)(xb + j * 16 * kRowsPitch + u * 32);
+        bl[j] = *(const f16x8*)(xb + j * 16 * kRowsPitch + kRowsStageK + u * 32);
+      }
+      f16x8 a;
+      if (Q8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = (f16)(float)(int8_t)((f.qv[u].x >> (8 * e)) & 0xFF);
+          a[4 + e] = (f16)(float)(int8_t)((f.qv[u].y >> (8 * e)) & 0xFF);
+        }
+        const float sc[4] = {(float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x & 0xFFFF)),
+                             (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x >> 16)),
+                             (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y & 0xFFFF)),
+                             (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y >> 16))};
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+          p = mfma16(a, bh[j], p);
+          p = mfma16(a, bl[j], p);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sc[r], p[r], acc[j][r]);
+        }
+      } else {
+        a = bf16x8_to_f16x8(f.wv[u]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          acc[j] = mfma16(a, bh[j], acc[j]);
+          acc[j] = mfma16(a, bl[j], acc[j]);
+        }
+      }
+    }
+  };
+
+  // issue order per wave: weights(0), x(0), weights(1), then per stage t: x(t+1), weights(t+2);
+  // so when stage t starts, only weights(t+1) may still be in flight after x(t).
+  // Every stage issues the same copies and loads (past the range they repeat the last piece, an
+  // L2 hit, into the buffer not being read), so every path has the same number in flight.
+  Buf b0, b1;
+  fetch(b0, 0);
+  issue_x(0);
+  fetch(b1, 1);
+  auto stage = [&](Buf& f, int t) {
+    vm_wait<NF>();                                    // x(t) and everything before it have landed
+    __syncthreads();                                  // stage t's rows are in LDS; buffer (t+1)&1 is free
+    issue_x(t + 1);
+    compute(f, t);
+    fetch(f, t + 2);
+  };
+  for (int t = 0; t < nstage; t += 2) {               // unrolled by two: b0 and b1 keep their registers
+    stage(b0, t);
+    if (t + 1 >= nstage) break;
+    stage(b1, t + 1);
+  }
+  vm_wait<0>();                                       // no copy into LDS outlives the workgroup
+  if (!has_tile) return;
+
+  // acc[j][r] = value of weight row n0 + 4*g4 + r for token row j*16 + r16.
+  const int n = n0 + g4 * 4;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int b = j * 16 + r16;
+    if (b < B) {
+      const float4 v = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+      *(float4*)&P[(int64_t)s * part_stride + (int64_t)b * ldp + n] = v;
+    }
+    if (cand) {
+      float bv = acc[j][0];
+      int bi = n;
+#pragma unroll
+      for (int r = 1; r < 4; ++r)
+        if (acc[j][r] > bv) {
+          bv = acc[j][r];
+          bi = n + r;
+        }
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if (g4 == 0 && b < B) cand[(int64_t)b * (N / 16) + tile] = make_float2(bv, __int_as_float(bi));
+    }
+  }
+}
+
 // B > 4: the prologue arithmetic of one K range of one row into global hi/lo rows
 // (grid: ranges x rows, 256 threads) -- the same element mapping and order as the LDS path.
 __global__ __launch_bounds__(256) void rows_kernel(XSrc xs, int klen, f16* __restrict__ yhi, f16* __restrict__ ylo,
@@ -335,12 +505,19 @@ hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, int K
   if (lds) {
     if (Wq) GEMV_LAUNCH(true, 1, true);
     else GEMV_LAUNCH(false, 1, true);
-  } else if (B <= 16) {
-    if (Wq) GEMV_LAUNCH(true, 1, false);
-    else GEMV_LAUNCH(false, 1, false);
   } else {
-    if (Wq) GEMV_LAUNCH(true, 2, false);
-    else GEMV_LAUNCH(false, 2, false);
+    const dim3 rgrid((N / 16 + kRowsWaves - 1) / kRowsWaves, nsplit), rblk(64 * kRowsWaves);
+#define ROWS_LAUNCH(Q8, NT)                                                                                      \
+  hipLaunchKernelGGL((gemv_rows_kernel<Q8, NT>), rgrid, rblk, 0, st, W, Wq, Wd, K, N, xs, B, klen, P, part_stride, \
+                     ldp, cand)
+    if (B <= 16) {
+      if (Wq) ROWS_LAUNCH(true, 1);
+      else ROWS_LAUNCH(false, 1);
+    } else {
+      if (Wq) ROWS_LAUNCH(true, 2);
+      else ROWS_LAUNCH(false, 2);
+    }
+#undef ROWS_LAUNCH
   }
 #undef GEMV_LAUNCH
   return hipGetLastError();
