@@ -402,14 +402,16 @@ __device__ __forceinline__ void merge_head(const float* pp, int nchunk, int lane
   const float M = wave_max(mv);
   const float wt = lane < nchunk ? exp2f(mv - M) : 0.f;
   float L = 0.f, o0 = 0.f, o1 = 0.f;
+  // Every chunk slot enters the chains: past nchunk the weight is exactly 0 and the (clamped)
+  // values are finite, so those steps add +0 to sums that started at +0 and cannot be -0, which
+  // leaves them unchanged. No branch per chunk, so the compiler cannot sink each load next to
+  // its use (which serialised the loads).
 #pragma unroll
-  for (int cc = 0; cc < kDecodeMaxChunks; ++cc) {
-    if (cc < nchunk) {                                  // chunk cc's weight and sum, read as scalars
-      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), cc));
-      L = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.y), cc)), w, L);
-      o0 = fmaf(ov[cc].x, w, o0);
-      o1 = fmaf(ov[cc].y, w, o1);
-    }
+  for (int cc = 0; cc < kDecodeMaxChunks; ++cc) {       // chunk cc's weight and sum, read as scalars
+    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), cc));
+    L = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.y), cc)), w, L);
+    o0 = fmaf(ov[cc].x, w, o0);
+    o1 = fmaf(ov[cc].y, w, o1);
   }
   const float inv = out_scale / L;
   f16 h0, l0, h1, l1;
