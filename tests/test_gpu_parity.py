@@ -494,6 +494,44 @@ def test_qwen3_4b_q8_0_full_prompt(g):
         o.close()
 
 
+def test_decode_across_chunk_length_change(g):
+    """Decode attention cuts a context into chunks whose length grows with the context (64
+    positions up to 4,096, then 128, ...). Tiny shape, a 4,094-token prompt over shuffled blocks,
+    then five greedy decode steps at contexts 4,095 .. 4,099 -- across the change at 4,097: each
+    step's logits equal those of prefilling the same tokens in a fresh session (matvec and split
+    attention vs GEMM and flash attention) within NMSE 1e-5, same argmax unless the top-2
+    margin is a near tie."""
+    wl = synth.WORKLOADS["tiny"]
+    shape = wl.shape
+    T, steps = 4094, 5
+    nb = synth.blocks_for(T + steps + 1)
+    table = synth.shuffled_blocks(wl.shuffle_seed, 2 * nb)[:nb]
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=4 * nb, max_positions=nb * 32)
+    s = g.Session(m, nb * 32, block_ids=table)
+    prompt = synth.token_ids(wl.ids_seed, T)
+    lg = torch.empty(shape.vocab, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    s.prefill(prompt, lg, am)
+    torch.cuda.synchronize()
+    seq = list(prompt)
+    gate = Gate("tiny decode across the chunk-length change")
+    lg2 = torch.empty(shape.vocab, device="cuda")
+    for i in range(steps):
+        tok = int(am.item())
+        seq.append(tok)
+        s.decode(tok, lg, am)
+        torch.cuda.synchronize()
+        s2 = g.Session(m, nb * 32)
+        s2.prefill(np.array(seq, dtype=prompt.dtype), lg2)
+        torch.cuda.synchronize()
+        gate.check(len(seq) - 1, lg.cpu().numpy(), lg2.cpu().numpy(), int(am.item()))
+        s2.close()
+    w = gate.assert_ok()
+    assert w <= 1e-5
+    s.close()
+    m.close()
+
+
 def test_qwen3_8b_batched_32_sessions(g):
     """The 8B batched workload at full size: 36 layers, hidden 4096, untied lm_head, 32
     sessions with contexts L_i ~ U{512..8192} (seed 4005), each prefilled alone over its own
