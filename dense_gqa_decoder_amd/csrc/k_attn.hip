@@ -344,12 +344,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
 // Decode attention (split context), grid (chunk, KV head, row), four waves per workgroup.
 // A row's context [0, pos] is cut into chunks of decode_chunk_len(ctx) positions (a multiple of
 // 64 chosen from the row's own context length only, so a row gets the same chunks whether it is
-// evaluated alone or in a batch). A workgroup walks its chunk 64 positions at a time: wave w
-// takes 16 consecutive positions, lane (ks, dg) = (lane / 16, lane % 16) holds dims 8dg..8dg+7 of
-// positions ks, ks + 4, ks + 8, ks + 12, so one wave-wide 16-byte load covers four whole K (or V)
-// rows, 1 KiB of contiguous pool memory. Each 16-lane group keeps its own online-softmax state
-// (max, sum, value sum) for the g query heads of the KV head; the 16 states of the workgroup are
-// merged in LDS into one chunk partial (max, sum, o[128]) per head.
+// evaluated alone or in a batch). A workgroup walks its chunk 64 positions at a time, wave w
+// taking 16 consecutive keys on the matrix cores (section 3 below); each wave keeps its own
+// online-softmax state (max, sum, value sum) for the g query heads of the KV head, and the four
+// states are merged in LDS, in wave order, into one chunk partial (max, sum, o[128]) per head.
 //  1. q for the g query heads: the fixed-order sum of the q|k|v projection's split partials,
 //     times the row's 1/rms (recomputed from the sum-of-squares partials the projection's
 //     prologue wrote), per-head RMSNorm, rotate-half RoPE at the row's position, built once
@@ -365,13 +363,6 @@ constexpr int kPartStride = 132;   // floats per chunk partial: m, l, pad, pad, 
 
 __host__ __device__ __forceinline__ int decode_chunk_len(int ctx) {
   return 64 * ((ctx + 64 * kDecodeMaxChunks - 1) / (64 * kDecodeMaxChunks));
-}
-
-__device__ __forceinline__ void bf16x8_to_f32(uint4 v, float (&f)[8]) {
-  f[0] = bf16_bits_to_f32(v.x & 0xFFFF); f[1] = bf16_bits_to_f32(v.x >> 16);
-  f[2] = bf16_bits_to_f32(v.y & 0xFFFF); f[3] = bf16_bits_to_f32(v.y >> 16);
-  f[4] = bf16_bits_to_f32(v.z & 0xFFFF); f[5] = bf16_bits_to_f32(v.z >> 16);
-  f[6] = bf16_bits_to_f32(v.w & 0xFFFF); f[7] = bf16_bits_to_f32(v.w >> 16);
 }
 
 // Device-scope (sc1) accesses: coherent across the XCDs' L2 caches without an L2 writeback or
@@ -428,42 +419,47 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
     const float* __restrict__ rcos, const float* __restrict__ rsin, Rows rows, uint16_t* __restrict__ kpool,
     uint16_t* __restrict__ vpool, float* part, int* __restrict__ counters, float out_scale, f16* __restrict__ ohi,
     f16* __restrict__ olo, int ldo) {
-  constexpr int NST = 4 * kDecodeWaves;                   // softmax states per workgroup
+  constexpr int NW = kDecodeWaves;                        // softmax states per workgroup (one per wave)
   constexpr int NE = (G + 2) * kHeadDim;                  // q heads, then k and v of the new position
   __shared__ float sraw[NE];                              // projection sums (times 1/rms)
   __shared__ float sq[NE];                                // normed + rotated q (scaled), k; v
-  __shared__ float sm[NST][G], sl[NST][G], sw[NST][G], sML[G][2];
-  __shared__ float so[NST][G][kHeadDim];
+  __shared__ float wm[NW][G], wl[NW][G], ww[NW][G], sML[G][2];
+  __shared__ float wo[NW][G][kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint16_t vlds[NW][2][16 * kHeadDim];   // V planes, two steps
   __shared__ int s_last;
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int pos = rows.pos[b], ctx = pos + 1;
   const int CH = decode_chunk_len(ctx);
   const int nchunk = (ctx + CH - 1) / CH;
   if (c >= nchunk) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ks = lane >> 4, dg = lane & 15;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int hq = lane & 15, g4 = lane >> 4;
   const int p_begin = c * CH, p_end = min(p_begin + CH, ctx);
   const int niter = (p_end - p_begin + 63) / 64;
   const bool owner = pos >= p_begin && pos < p_end;     // this chunk holds the new position
   const int32_t* table = rows.table[b];
-  const uint16_t* kbase = kpool + (int64_t)kvh * kBlock * kHeadDim + dg * 8;
-  const uint16_t* vbase = vpool + (int64_t)kvh * kBlock * kHeadDim + dg * 8;
   constexpr int64_t kBlockElems = (int64_t)kKvHeads * kBlock * kHeadDim;
 
-  // K/V of iteration `it` for this lane: positions p0 + 4 st + ks, all in one 32-position block.
-  // The loads are unconditional (no branch between them): a position past the chunk reads a slot
-  // of a block the session owns (or of the pool's block 0 when the whole group is past it) and
-  // its value is discarded in step().
+  // Keys of 64-position step `it` for this wave: p0 .. p0 + 15 with p0 = chunk start + 64 it + 16 w,
+  // all in one 32-position block. The loads are unconditional: a key past the chunk reads a slot
+  // of a block the session owns (or the pool's block 0 when the whole wave is past it); its score
+  // is masked and its V row zeroed in LDS before use.
+  //   K: lane l loads key l % 16, dims 32 s + 8 (l / 16) .. + 7 for s = 0..3 (the A operand rows).
+  //   V: four 1 KiB direct-to-LDS copies into 16-dim planes (16 keys x 32 bytes each); copy j
+  //      fills planes 2 j, 2 j + 1, lane l bringing key (l % 32) / 2, half l % 2 of the plane.
   auto phys_of = [&](int it) { return table[min(p_begin + it * 64 + wave * 16, p_end - 1) >> 5]; };
-  auto load = [&](int it, int phys, uint4 (&kr)[4], uint4 (&vr)[4]) {
-    const int p0 = p_begin + it * 64 + wave * 16;
-    const int64_t off = (int64_t)phys * kBlockElems + (int64_t)(p0 & 31) * kHeadDim;
+  auto issue = [&](int it, int phys, uint4 (&kr)[4], int buf) {
+    const int64_t rows = (int64_t)phys * kBlockElems + ((int64_t)kvh * kBlock + ((wave * 16) & 31)) * kHeadDim;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      kr[st] = *(const uint4*)(kbase + off + (st * 4 + ks) * kHeadDim);
-      vr[st] = *(const uint4*)(vbase + off + (st * 4 + ks) * kHeadDim);
+    for (int s4 = 0; s4 < 4; ++s4) kr[s4] = *(const uint4*)(kpool + rows + hq * kHeadDim + 32 * s4 + 8 * g4);
+    const int vrow = (lane & 31) >> 1, vhalf = lane & 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int plane = 2 * j + (lane >> 5);
+      lds_dma16(vpool + rows + vrow * kHeadDim + 16 * plane + 8 * vhalf, &vlds[wave][buf][j * 512]);
     }
   };
-  uint4 kA[4], vA[4], kB[4], vB[4];
+  uint4 kA[4], kB[4];
   // Issue order matters (vector loads complete in order): the block-table entry, the RoPE and
   // norm constants, the projection partials, then the first K/V, so q is built while the K/V
   // are in flight.
@@ -489,7 +485,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2) t[i][s2] = p[(int64_t)min(s2, nsplit - 1) * pstride];   // unconditional
     }
-    load(0, phys0, kA, vA);
+    issue(0, phys0, kA, 0);
     const float cin = inv_rms_from_ss(ss, ss_n, b, H, eps);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -535,103 +531,164 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
     *(uint4*)((kv ? vpool : kpool) + off) =
         uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
   }
-  float qv[G][8];
+  // 3. attention over the chunk on the matrix cores; wave w takes keys 16 w .. 16 w + 15 of every
+  //    64-position step and keeps its own online-softmax state per head.
+  //    Scores S^T[key][head] = K q^T by v_mfma_f32_16x16x32_bf16: A = the 16 keys' K rows, B = q as
+  //    BF16 hi/lo (lane l: head l % 16, zero for heads >= g), four 32-dim steps x hi/lo. The score
+  //    accumulator (lane l: keys 4 (l / 16) + i, head l % 16) is, as BF16 hi/lo, the A operand of
+  //    v_mfma_f32_16x16x16_bf16 for O[head][dim] += P[head][key] V[key][dim]; V is read from its
+  //    LDS planes transposed (ds_read_b64_tr_b16: lane i of a 16-lane group addresses key i / 4,
+  //    piece i % 4, and receives dim i of the group's four keys).
+  bf16v8 qh[4], ql[4];
+  {
+    const int hc = min(hq, G - 1);
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
+    for (int s4 = 0; s4 < 4; ++s4) {
+      uint32_t h[4], lo[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[hh][e] = sq[hh * kHeadDim + dg * 8 + e];
-
-  // 3. online softmax over the chunk, one state per 16-lane row group
-  float m[G], l[G], o[G][8];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * s4 + 8 * g4 + 2 * j;
+        const float a0 = hq < G ? sq[hc * kHeadDim + d] : 0.f, a1 = hq < G ? sq[hc * kHeadDim + d + 1] : 0.f;
+        split_bf16x2(a0, a1, h[j], lo[j]);
+      }
+      qh[s4] = as_bf16v8(h[0], h[1], h[2], h[3]);
+      ql[s4] = as_bf16v8(lo[0], lo[1], lo[2], lo[3]);
+    }
   }
-  auto step = [&](int it, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
+  f32x4 O[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;                   // head hq: the wave's running max and sum
+  auto xrow_max = [](float v) {                            // max over lanes l, l ^ 16
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+  auto xrow_sum = [](float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  };
+  auto compute = [&](int it, uint4 (&kr)[4], int buf) {
     const int p0 = p_begin + it * 64 + wave * 16;
-    float kf[4][8], vf[4][8];
-    bool valid[4];
+    uint16_t* vl = vlds[wave][buf];
+    if (owner && p0 + hq == pos) {                        // the new position: K from LDS, not the pool
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int p = p0 + st * 4 + ks;
-      valid[st] = p < p_end;
-      bf16x8_to_f32(kr[st], kf[st]);
-      bf16x8_to_f32(vr[st], vf[st]);
-      if (owner && p == pos) {                            // the new position, not yet in the pool
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const float* kq = sq + G * kHeadDim + 32 * s4 + 8 * g4;
+        uint32_t w4[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kf[st][e] = sq[G * kHeadDim + dg * 8 + e];
-          vf[st][e] = sq[(G + 1) * kHeadDim + dg * 8 + e];
+        for (int j = 0; j < 4; ++j) w4[j] = f32_to_bf16_rne(kq[2 * j]) | (f32_to_bf16_rne(kq[2 * j + 1]) << 16);
+        kr[s4] = uint4{w4[0], w4[1], w4[2], w4[3]};
+      }
+    }
+    f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const bf16v8 ka = as_bf16v8(kr[s4].x, kr[s4].y, kr[s4].z, kr[s4].w);
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[s4], st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[s4], st, 0, 0, 0);
+    }
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = p0 + 4 * g4 + i < p_end ? st[i] : -INFINITY;
+    const float mx = xhalf_max(xrow_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
+    const float mnew = fmaxf(m_run, mx);
+    const bool any = mnew != -INFINITY;                   // a visible key so far for this head
+    const float alpha = any ? exp2f(m_run - mnew) : 1.f;
+    float pv[4], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = any ? exp2f(sc[i] - mnew) : 0.f;
+      ps += pv[i];
+    }
+    ps = xhalf_sum(xrow_sum(ps));
+    l_run = l_run * alpha + ps;
+    m_run = mnew;
+    // O rows 0 .. g - 1 (lanes 0..15) are the heads; head r's alpha sits in lane r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), r < G ? r : 0));
+#pragma unroll
+      for (int n = 0; n < 8; ++n) O[n][r] *= ar;
+    }
+    uint32_t ph0, pl0, ph1, pl1;
+    split_bf16x2(pv[0], pv[1], ph0, pl0);
+    split_bf16x2(pv[2], pv[3], ph1, pl1);
+    const s16x4 pah = __builtin_bit_cast(s16x4, uint2{ph0, ph1}), pal = __builtin_bit_cast(s16x4, uint2{pl0, pl1});
+    // V rows of keys past the chunk to zero (masked keys must add 0 * finite), the new position's
+    // row from LDS; lane l covers key l % 16, planes 2 (l / 16), 2 (l / 16) + 1
+    {
+      const int key = hq, pl2 = 2 * g4;
+      if (p0 + key >= p_end) {
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          *(uint4*)(vl + (pl2 + q2) * 256 + key * 16) = uint4{0, 0, 0, 0};
+          *(uint4*)(vl + (pl2 + q2) * 256 + key * 16 + 8) = uint4{0, 0, 0, 0};
+        }
+      } else if (owner && p0 + key == pos) {
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const float* vq = sq + (G + 1) * kHeadDim + 16 * (pl2 + q2);
+          uint32_t w8[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w8[j] = f32_to_bf16_rne(vq[2 * j]) | (f32_to_bf16_rne(vq[2 * j + 1]) << 16);
+          *(uint4*)(vl + (pl2 + q2) * 256 + key * 16) = uint4{w8[0], w8[1], w8[2], w8[3]};
+          *(uint4*)(vl + (pl2 + q2) * 256 + key * 16 + 8) = uint4{w8[4], w8[5], w8[6], w8[7]};
         }
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vf[st][e] = valid[st] ? vf[st][e] : 0.f;
     }
+    const uint16_t* vt = vl + (4 * g4 + (hq >> 2)) * 16 + (hq & 3) * 4;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float sc[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(qv[hh][e], kf[st][e], d);
-        d = row16_sum(d);
-        sc[st] = valid[st] ? d : -INFINITY;
-      }
-      const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      const float mn = fmaxf(m[hh], mx);
-      if (mn == -INFINITY) continue;                     // nothing visible yet in this group
-      const float alpha = exp2f(m[hh] - mn);
-      float lsum = l[hh] * alpha;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[hh][e] *= alpha;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const float pr = exp2f(sc[st] - mn);
-        lsum += pr;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(pr, vf[st][e], o[hh][e]);
-      }
-      l[hh] = lsum;
-      m[hh] = mn;
+    for (int n = 0; n < 8; ++n) {
+      const s16x4 vb = lds_read_tr16(vt + n * 256);
+      O[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pah, vb, O[n], 0, 0, 0);
+      O[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pal, vb, O[n], 0, 0, 0);
     }
   };
+  // steps double-buffered (K in registers, V in two LDS buffers per wave); a step's copies and
+  // loads have landed once at most the next step's eight are in flight
   for (int it = 0; it < niter; it += 2) {
-    if (it + 1 < niter) load(it + 1, phys_of(it + 1), kB, vB);
-    step(it, kA, vA);
+    if (it + 1 < niter) {
+      issue(it + 1, phys_of(it + 1), kB, 1);
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      vm_wait_all();
+    }
+    compute(it, kA, 0);
     if (it + 1 >= niter) break;
-    if (it + 2 < niter) load(it + 2, phys_of(it + 2), kA, vA);
-    step(it + 1, kB, vB);
+    if (it + 2 < niter) {
+      issue(it + 2, phys_of(it + 2), kA, 0);
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      vm_wait_all();
+    }
+    compute(it + 1, kB, 1);
   }
 
-  // 4. merge the 16 row-group states of the workgroup (state index 4 * wave + ks, in order)
-  const int si = wave * 4 + ks;
+  // 4. merge the wave states of the workgroup (in wave order) into the chunk partial
+  if (lane < G) {
+    wm[wave][lane] = m_run;
+    wl[wave][lane] = l_run;
+  }
+  if (lane < 16) {
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    if (dg == 0) {
-      sm[si][hh] = m[hh];
-      sl[si][hh] = l[hh];
-    }
+    for (int n = 0; n < 8; ++n)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) so[si][hh][dg * 8 + e] = o[hh][e];
+      for (int r = 0; r < G; ++r) wo[wave][r][16 * n + lane] = O[n][r];
   }
   __syncthreads();
-  // per head: the max over the states, the state weights 2^(m_w - max) and the weighted sum,
-  // computed once (thread hh), in state order
+  // per head: the max over the wave states, the state weights 2^(m_w - max) and the weighted sum,
+  // computed once (thread hh), in wave order
   if (tid < G) {
     const int hh = tid;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NST; ++w) M = fmaxf(M, sm[w][hh]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][hh]);
     float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < NST; ++w) {
-      const float wt = sm[w][hh] == -INFINITY ? 0.f : exp2f(sm[w][hh] - M);
-      sw[w][hh] = wt;
-      L = fmaf(sl[w][hh], wt, L);
+    for (int w = 0; w < NW; ++w) {
+      const float wt = wm[w][hh] == -INFINITY ? 0.f : exp2f(wm[w][hh] - M);
+      ww[w][hh] = wt;
+      L = fmaf(wl[w][hh], wt, L);
     }
     sML[hh][0] = M;
     sML[hh][1] = L;
@@ -639,22 +696,22 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
   __syncthreads();
   for (int idx = tid; idx < G * kHeadDim; idx += 64 * kDecodeWaves) {
     const int hh = idx / kHeadDim, d = idx % kHeadDim;
-    float O = 0.f;
+    float Ov = 0.f;
 #pragma unroll
-    for (int w = 0; w < NST; ++w) O = fmaf(so[w][hh][d], sw[w][hh], O);
+    for (int w = 0; w < NW; ++w) Ov = fmaf(wo[w][hh][d], ww[w][hh], Ov);
     float* pp = part + (((int64_t)b * nq + kvh * G + hh) * kDecodeMaxChunks + c) * kPartStride;
     if (FUSED) {                          // read by another workgroup of this launch
       if (d == 0) {
         store_dev(pp, sML[hh][0]);
         store_dev(pp + 1, sML[hh][1]);
       }
-      store_dev(pp + 4 + d, O);
+      store_dev(pp + 4 + d, Ov);
     } else {                              // read by attn_merge_kernel after this launch
       if (d == 0) {
         pp[0] = sML[hh][0];
         pp[1] = sML[hh][1];
       }
-      pp[4 + d] = O;
+      pp[4 + d] = Ov;
     }
   }
   if (!FUSED) return;                     // attn_merge_kernel combines the partials
