@@ -413,7 +413,7 @@ __device__ __forceinline__ void merge_head(const float* pp, int nchunk, int lane
 }
 
 template <int G, bool FUSED>
-__global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_kernel(
+__global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_kernel(
     const float* __restrict__ qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* __restrict__ ss,
     int ss_n, int H, const uint16_t* __restrict__ wqn, const uint16_t* __restrict__ wkn, float eps,
     const float* __restrict__ rcos, const float* __restrict__ rsin, Rows rows, uint16_t* __restrict__ kpool,
