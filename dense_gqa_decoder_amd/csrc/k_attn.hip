@@ -424,8 +424,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
   __shared__ float sraw[NE];                              // projection sums (times 1/rms)
   __shared__ float sq[NE];                                // normed + rotated q (scaled), k; v
   __shared__ float wm[NW][G], wl[NW][G], ww[NW][G], sML[G][2];
-  __shared__ float wo[NW][G][kHeadDim];
   __shared__ __attribute__((aligned(16))) uint16_t vlds[NW][2][16 * kHeadDim];   // V planes, two steps
+  // the wave states' value sums, after the chunk's steps, in the V buffers' space
+  static_assert(sizeof(float) * NW * G * kHeadDim <= sizeof(vlds), "merge area");
+  float (*const wo)[G][kHeadDim] = reinterpret_cast<float (*)[G][kHeadDim]>(&vlds[0][0][0]);
   __shared__ int s_last;
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int pos = rows.pos[b], ctx = pos + 1;
@@ -665,6 +667,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
   }
 
   // 4. merge the wave states of the workgroup (in wave order) into the chunk partial
+  __syncthreads();                                        // every wave is done with its V buffers
   if (lane < G) {
     wm[wave][lane] = m_run;
     wl[wave][lane] = l_run;
