@@ -358,6 +358,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
 //  3. The last workgroup of a (row, KV head) to finish combines the chunk partials of its heads in
 //     chunk order (merge_head).
 constexpr int kDecodeWaves = 4;
+constexpr int kBatchChunksPerWorkgroup = 4;
 constexpr int kDecodeMaxChunks = 64;
 constexpr int kPartStride = 132;   // floats per chunk partial: m, l, pad, pad, o[128]
 
@@ -416,7 +417,7 @@ template <int G, bool FUSED>
 __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_kernel(
     const float* __restrict__ qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* __restrict__ ss,
     int ss_n, int H, const uint16_t* __restrict__ wqn, const uint16_t* __restrict__ wkn, float eps,
-    const float* __restrict__ rcos, const float* __restrict__ rsin, Rows rows, uint16_t* __restrict__ kpool,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, Rows rows, int cpw, uint16_t* __restrict__ kpool,
     uint16_t* __restrict__ vpool, float* part, int* __restrict__ counters, float out_scale, f16* __restrict__ ohi,
     f16* __restrict__ olo, int ldo) {
   constexpr int NW = kDecodeWaves;                        // softmax states per workgroup (one per wave)
@@ -424,21 +425,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
   __shared__ float sraw[NE];                              // projection sums (times 1/rms)
   __shared__ float sq[NE];                                // normed + rotated q (scaled), k; v
   __shared__ float wm[NW][G], wl[NW][G], ww[NW][G], sML[G][2];
+  __shared__ float wo[NW][G][kHeadDim];
   __shared__ __attribute__((aligned(16))) uint16_t vlds[NW][2][16 * kHeadDim];   // V planes, two steps
-  // the wave states' value sums, after the chunk's steps, in the V buffers' space
-  static_assert(sizeof(float) * NW * G * kHeadDim <= sizeof(vlds), "merge area");
-  float (*const wo)[G][kHeadDim] = reinterpret_cast<float (*)[G][kHeadDim]>(&vlds[0][0][0]);
   __shared__ int s_last;
-  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int kvh = blockIdx.y, b = blockIdx.z;
   const int pos = rows.pos[b], ctx = pos + 1;
   const int CH = decode_chunk_len(ctx);
   const int nchunk = (ctx + CH - 1) / CH;
-  if (c >= nchunk) return;
+  const int c0 = blockIdx.x * cpw;                        // this workgroup's chunks [c0, c1)
+  if (c0 >= nchunk) return;
+  const int c1 = min(c0 + cpw, nchunk);
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int hq = lane & 15, g4 = lane >> 4;
-  const int p_begin = c * CH, p_end = min(p_begin + CH, ctx);
-  const int niter = (p_end - p_begin + 63) / 64;
-  const bool owner = pos >= p_begin && pos < p_end;     // this chunk holds the new position
+  const bool owner = c1 == nchunk;                        // the last chunk holds the new position
+  auto p_end_of = [&](int cc) { return min(cc * CH + CH, ctx); };
+  auto niter_of = [&](int cc) { return (p_end_of(cc) - cc * CH + 63) / 64; };
   const int32_t* table = rows.table[b];
   constexpr int64_t kBlockElems = (int64_t)kKvHeads * kBlock * kHeadDim;
 
@@ -449,8 +450,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
   //   K: lane l loads key l % 16, dims 32 s + 8 (l / 16) .. + 7 for s = 0..3 (the A operand rows).
   //   V: four 1 KiB direct-to-LDS copies into 16-dim planes (16 keys x 32 bytes each); copy j
   //      fills planes 2 j, 2 j + 1, lane l bringing key (l % 32) / 2, half l % 2 of the plane.
-  auto phys_of = [&](int it) { return table[min(p_begin + it * 64 + wave * 16, p_end - 1) >> 5]; };
-  auto issue = [&](int it, int phys, uint4 (&kr)[4], int buf) {
+  auto phys_of = [&](int cc, int it) { return table[min(cc * CH + it * 64 + wave * 16, p_end_of(cc) - 1) >> 5]; };
+  auto issue = [&](int phys, uint4 (&kr)[4], int buf) {
     const int64_t rows = (int64_t)phys * kBlockElems + ((int64_t)kvh * kBlock + ((wave * 16) & 31)) * kHeadDim;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) kr[s4] = *(const uint4*)(kpool + rows + hq * kHeadDim + 32 * s4 + 8 * g4);
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
   // Issue order matters (vector loads complete in order): the block-table entry, the RoPE and
   // norm constants, the projection partials, then the first K/V, so q is built while the K/V
   // are in flight.
-  const int phys0 = phys_of(0);
+  const int phys0 = phys_of(c0, 0);
   nsplit = max(1, min(nsplit, 8));
   const float cs = rcos[(int64_t)pos * 64 + lane], sn = rsin[(int64_t)pos * 64 + lane];
   const float wq0 = bf16_bits_to_f32(wqn[lane]), wq1 = bf16_bits_to_f32(wqn[64 + lane]);
@@ -487,7 +488,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2) t[i][s2] = p[(int64_t)min(s2, nsplit - 1) * pstride];   // unconditional
     }
-    issue(0, phys0, kA, 0);
+    issue(phys0, kA, 0);
     const float cin = inv_rms_from_ss(ss, ss_n, b, H, eps);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -569,8 +570,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
   };
-  auto compute = [&](int it, uint4 (&kr)[4], int buf) {
-    const int p0 = p_begin + it * 64 + wave * 16;
+  auto compute = [&](int cc, int it, uint4 (&kr)[4], int buf) {
+    const int p0 = cc * CH + it * 64 + wave * 16, p_end = p_end_of(cc);
     uint16_t* vl = vlds[wave][buf];
     if (owner && p0 + hq == pos) {                        // the new position: K from LDS, not the pool
 #pragma unroll
@@ -646,76 +647,103 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
       O[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pal, vb, O[n], 0, 0, 0);
     }
   };
-  // steps double-buffered (K in registers, V in two LDS buffers per wave); a step's copies and
-  // loads have landed once at most the next step's eight are in flight
-  for (int it = 0; it < niter; it += 2) {
-    if (it + 1 < niter) {
-      issue(it + 1, phys_of(it + 1), kB, 1);
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    } else {
-      vm_wait_all();
+  // 4. per chunk: merge the wave states of the workgroup (in wave order) into the chunk partial,
+  //    then start the next chunk from empty states
+  auto finish = [&](int cc) {
+    if (lane < G) {
+      wm[wave][lane] = m_run;
+      wl[wave][lane] = l_run;
     }
-    compute(it, kA, 0);
-    if (it + 1 >= niter) break;
-    if (it + 2 < niter) {
-      issue(it + 2, phys_of(it + 2), kA, 0);
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    } else {
-      vm_wait_all();
+    if (lane < 16) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int r = 0; r < G; ++r) wo[wave][r][16 * n + lane] = O[n][r];
     }
-    compute(it + 1, kB, 1);
-  }
+    __syncthreads();
+    // per head: the max over the wave states, the state weights 2^(m_w - max) and the weighted sum,
+    // computed once (thread hh), in wave order
+    if (tid < G) {
+      const int hh = tid;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][hh]);
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float wt = wm[w][hh] == -INFINITY ? 0.f : exp2f(wm[w][hh] - M);
+        ww[w][hh] = wt;
+        L = fmaf(wl[w][hh], wt, L);
+      }
+      sML[hh][0] = M;
+      sML[hh][1] = L;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * kHeadDim; idx += 64 * kDecodeWaves) {
+      const int hh = idx / kHeadDim, d = idx % kHeadDim;
+      float Ov = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) Ov = fmaf(wo[w][hh][d], ww[w][hh], Ov);
+      float* pp = part + (((int64_t)b * nq + kvh * G + hh) * kDecodeMaxChunks + cc) * kPartStride;
+      if (FUSED) {                          // read by another workgroup of this launch
+        if (d == 0) {
+          store_dev(pp, sML[hh][0]);
+          store_dev(pp + 1, sML[hh][1]);
+        }
+        store_dev(pp + 4 + d, Ov);
+      } else {                              // read by attn_merge_kernel after this launch
+        if (d == 0) {
+          pp[0] = sML[hh][0];
+          pp[1] = sML[hh][1];
+        }
+        pp[4 + d] = Ov;
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+    __syncthreads();                      // the merge arrays are reused by the next chunk
+  };
 
-  // 4. merge the wave states of the workgroup (in wave order) into the chunk partial
-  __syncthreads();                                        // every wave is done with its V buffers
-  if (lane < G) {
-    wm[wave][lane] = m_run;
-    wl[wave][lane] = l_run;
-  }
-  if (lane < 16) {
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-#pragma unroll
-      for (int r = 0; r < G; ++r) wo[wave][r][16 * n + lane] = O[n][r];
-  }
-  __syncthreads();
-  // per head: the max over the wave states, the state weights 2^(m_w - max) and the weighted sum,
-  // computed once (thread hh), in wave order
-  if (tid < G) {
-    const int hh = tid;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][hh]);
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float wt = wm[w][hh] == -INFINITY ? 0.f : exp2f(wm[w][hh] - M);
-      ww[w][hh] = wt;
-      L = fmaf(wl[w][hh], wt, L);
+  // The workgroup's steps (chunk, 64-position step) in order, double-buffered (K in registers, V
+  // in two LDS buffers per wave) across chunk boundaries, so the next chunk's first copies are in
+  // flight during a chunk's merge; a step's copies and loads have landed once at most the next
+  // step's eight are in flight. (lc, lit): next step to issue; (cc, cit): next step to compute.
+  int lc = c0, lit = 0, cc = c0, cit = 0;
+  auto advance = [&](int& ch, int& it) {
+    if (++it >= niter_of(ch)) {
+      it = 0;
+      ++ch;
     }
-    sML[hh][0] = M;
-    sML[hh][1] = L;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * kHeadDim; idx += 64 * kDecodeWaves) {
-    const int hh = idx / kHeadDim, d = idx % kHeadDim;
-    float Ov = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) Ov = fmaf(wo[w][hh][d], ww[w][hh], Ov);
-    float* pp = part + (((int64_t)b * nq + kvh * G + hh) * kDecodeMaxChunks + c) * kPartStride;
-    if (FUSED) {                          // read by another workgroup of this launch
-      if (d == 0) {
-        store_dev(pp, sML[hh][0]);
-        store_dev(pp + 1, sML[hh][1]);
-      }
-      store_dev(pp + 4 + d, Ov);
-    } else {                              // read by attn_merge_kernel after this launch
-      if (d == 0) {
-        pp[0] = sML[hh][0];
-        pp[1] = sML[hh][1];
-      }
-      pp[4 + d] = Ov;
+  };
+  advance(lc, lit);                                      // step (c0, 0) was issued into kA, buffer 0
+  auto run = [&](uint4 (&kr)[4], int buf) {
+    compute(cc, cit, kr, buf);
+    if (cit + 1 == niter_of(cc)) finish(cc);
+    advance(cc, cit);
+  };
+  while (true) {
+    const bool more = lc < c1;
+    if (more) {
+      issue(phys_of(lc, lit), kB, 1);
+      advance(lc, lit);
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      vm_wait_all();
     }
+    run(kA, 0);
+    if (!more) break;
+    const bool more2 = lc < c1;
+    if (more2) {
+      issue(phys_of(lc, lit), kA, 0);
+      advance(lc, lit);
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      vm_wait_all();
+    }
+    run(kB, 1);
+    if (!more2) break;
   }
   if (!FUSED) return;                     // attn_merge_kernel combines the partials
   // 5. the last workgroup of this (row, KV head) to finish merges the chunk partials. The
@@ -782,14 +810,18 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
   if (nsplit < 1 || nsplit > 8 || B < 1 || B > kMaxBatch || max_ctx < 1) return hipErrorInvalidValue;
   const int CH = decode_chunk_len(max_ctx);
   const int chunks = (max_ctx + CH - 1) / CH;          // rows with shorter contexts exit early
-  dim3 grid(chunks, kKvHeads, B);
   const int G = nq / kKvHeads;
   // up to four rows: the last workgroup of a (row, KV head) merges; more rows: a merge kernel
   const bool fused = B <= 4;
+  // chunks per workgroup: one for few rows (parallelism; the fused merge counts one workgroup per
+  // chunk), several for many rows (q is built once per workgroup and the K/V stream runs on
+  // across its chunks); the chunks and their partials are the same either way
+  const int cpw = fused ? 1 : kBatchChunksPerWorkgroup;
+  dim3 grid((chunks + cpw - 1) / cpw, kKvHeads, B);
 #define DEC_LAUNCH(GG, FU)                                                                                         \
   hipLaunchKernelGGL((attn_decode_kernel<GG, FU>), grid, dim3(64 * kDecodeWaves), 0, st, qkvp, nsplit, pstride, QKV, \
-                     nq, ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, kpool, vpool, part, counters, out_scale, ohi,  \
-                     olo, ldo)
+                     nq, ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, cpw, kpool, vpool, part, counters, out_scale, \
+                     ohi, olo, ldo)
   if (G != 4 && G != 2) return hipErrorInvalidValue;
   if (fused) {
     if (G == 4) DEC_LAUNCH(4, true);
