@@ -224,6 +224,25 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* lds_dst) 
 }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Eight int8 quants (two dwords) -> eight exact FP16 values: the byte q + 128 (q ^ 0x80) below the
+// FP16 pattern 0x64 is the value 1152 + q, and subtracting 1152 is exact.
+__device__ __forceinline__ f16x8 i8x8_to_f16x8(uint2 v) {
+  const uint32_t x0 = v.x ^ 0x80808080u, x1 = v.y ^ 0x80808080u;
+  const uint32_t h[4] = {__builtin_amdgcn_perm(0x64646464u, x0, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, x0, 0x05030402u),
+                         __builtin_amdgcn_perm(0x64646464u, x1, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, x1, 0x05030402u)};
+  const f16x2 bias = {(f16)1152.0f, (f16)1152.0f};
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 q = __builtin_bit_cast(f16x2, h[i]) - bias;
+    r[2 * i] = q[0];
+    r[2 * i + 1] = q[1];
+  }
+  return r;
+}
+
 __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

@@ -221,11 +221,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* _
       }
       f16x8 a;
       if (Q8) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = (f16)(float)(int8_t)((f.qv[u].x >> (8 * e)) & 0xFF);
-          a[4 + e] = (f16)(float)(int8_t)((f.qv[u].y >> (8 * e)) & 0xFF);
-        }
+        a = i8x8_to_f16x8(f.qv[u]);
       } else {
         a = bf16x8_to_f16x8(f.wv[u]);
       }
@@ -384,11 +380,7 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows_kernel(const uint16
       }
       f16x8 a;
       if (Q8) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = (f16)(float)(int8_t)((f.qv[u].x >> (8 * e)) & 0xFF);
-          a[4 + e] = (f16)(float)(int8_t)((f.qv[u].y >> (8 * e)) & 0xFF);
-        }
+        a = i8x8_to_f16x8(f.qv[u]);
         const float sc[4] = {(float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x & 0xFFFF)),
                              (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x >> 16)),
                              (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y & 0xFFFF)),

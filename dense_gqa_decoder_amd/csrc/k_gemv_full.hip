@@ -152,11 +152,7 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
         const f16x8 bl = xvalid ? *(const f16x8*)(xl + kk) : f16x8{};
         f16x8 w;
         if (Q8) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            w[e] = (f16)(float)(int8_t)((f.q[u].x >> (8 * e)) & 0xFF);
-            w[4 + e] = (f16)(float)(int8_t)((f.q[u].y >> (8 * e)) & 0xFF);
-          }
+          w = i8x8_to_f16x8(f.q[u]);
           const float sc[4] = {(float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x & 0xFFFF)),
                                (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x >> 16)),
                                (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y & 0xFFFF)),
