@@ -24,6 +24,9 @@ Sources, cited by page title and section:
   norms stay BF16.
 * Kipp Reproducing, "Mutation gate": four KV addressing faults (read-block,
   read-slot, rollover, K/V swap), used here as oracle fault modes.
+* Kipp Roadmap, status v0.0.2 and v0.0.3: logits of several positions from one
+  call, and scoring of several rows (the log-probability of each next id).
+* Kipp Model Support, "What the gates check": truncate/resume of a session.
 
 The layer equations themselves (pre-norm blocks, per-head q/k RMSNorm before a
 rotate-half RoPE, SwiGLU) are the standard Qwen3 block; the pages name the
@@ -32,5 +35,5 @@ against a library routine (transformers' Qwen3 model) with the BF16 KV rounding
 switched off, against brute force, closed forms and invariants; absolute
 agreement with trained Qwen3 checkpoints is parity unpinned (no trained weights).
 """
-from .model import OracleModel, OracleSession, ContiguousKV, PagedKV, nmse  # noqa: F401
+from .model import OracleModel, OracleSession, ContiguousKV, PagedKV, nmse, next_token_log_probs  # noqa: F401
 from .q8_0 import quantize_q8_0, dequantize_q8_0  # noqa: F401

@@ -238,8 +238,32 @@ class OracleSession:
     def prefill(self, ids):
         return self.forward(ids)
 
+    def truncate(self, pos: int):
+        """Keep the first ``pos`` positions; later KV entries are rewritten when evaluated again
+        (Kipp Model Support, "What the gates check": truncate/resume)."""
+        if not 0 <= pos <= self.pos:
+            raise ValueError("truncate position out of range")
+        self.pos = pos
+
+    def score(self, ids):
+        """Append ``ids`` (n >= 2) and return the n-1 log-probabilities log p(ids[i+1] | ..ids[i])
+        (Kipp Roadmap, status v0.0.3: multi-row scoring)."""
+        if len(ids) < 2:
+            raise ValueError("scoring needs at least two ids")
+        logits = self.forward(ids, all_logits=True)
+        return next_token_log_probs(logits[:-1], np.asarray(ids[1:], dtype=np.int64))
+
     def decode(self, token: int):
         return self.forward([token])
+
+
+def next_token_log_probs(logits: np.ndarray, targets: np.ndarray) -> np.ndarray:
+    """Row i: log softmax(logits[i])[targets[i]] = logits[i, t] - log sum_j exp(logits[i, j]),
+    in float64, with the row maximum taken out before exponentiating."""
+    z = np.asarray(logits, dtype=np.float64)
+    mx = z.max(axis=1, keepdims=True)
+    lse = mx[:, 0] + np.log(np.exp(z - mx).sum(axis=1))
+    return z[np.arange(len(z)), targets] - lse
 
 
 def argmax(logits: np.ndarray) -> int:

@@ -336,3 +336,69 @@ def test_seeded_inputs_are_deterministic_and_in_range():
     assert sorted(p.tolist()) == list(range(264))
     L = synth.context_lengths(synth.CONTEXT_SEED_8B, 32)
     assert L.min() >= 512 and L.max() <= 8192
+
+
+def test_next_token_log_probs_closed_forms():
+    """Kipp Roadmap, status v0.0.3 (multi-row scoring): a score is the natural log of the softmax
+    probability of the next id. Uniform logits give -log V; two-level logits give closed forms."""
+    V = 1000
+    z = np.full((1, V), 3.25, dtype=np.float32)
+    assert abs(om.next_token_log_probs(z, np.array([17]))[0] + math.log(V)) < 1e-12
+    a, b = 2.0, -1.5
+    z = np.full((2, V), b, dtype=np.float32)
+    z[:, 5] = a
+    got = om.next_token_log_probs(z, np.array([5, 6]))
+    assert abs(got[0] + math.log1p((V - 1) * math.exp(b - a))) < 1e-12
+    assert abs(got[1] - (b - a - math.log1p((V - 1) * math.exp(b - a)))) < 1e-12
+
+
+def test_next_token_log_probs_invariants_and_torch():
+    """Every target's probability sums to one, a constant shift changes nothing, large logits do
+    not overflow, and torch's cross entropy (a library routine) gives the negated scores."""
+    import torch
+    rng = np.random.default_rng(5)
+    z = (rng.standard_normal((4, 300)) * 4).astype(np.float32)
+    all_t = np.stack([om.next_token_log_probs(z, np.full(4, t)) for t in range(300)], axis=1)
+    assert np.allclose(np.exp(all_t).sum(axis=1), 1.0, atol=1e-12)
+    t = np.array([0, 7, 299, 150])
+    s = om.next_token_log_probs(z, t)
+    assert np.allclose(om.next_token_log_probs(z.astype(np.float64) + 1e4, t), s, atol=1e-9)
+    assert np.all(np.isfinite(om.next_token_log_probs(z * 1e3, t)))
+    ce = torch.nn.functional.cross_entropy(torch.from_numpy(z.astype(np.float64)), torch.from_numpy(t),
+                                           reduction="none").numpy()
+    assert np.allclose(-ce, s, atol=1e-12)
+
+
+def test_session_score_is_next_token_log_prob_of_every_row():
+    """Scoring n ids gives the n-1 log-probabilities of ids[1:] under the logits of rows 0..n-2,
+    each row's logits depending only on the ids up to it (checked against a fresh session per row)."""
+    m = oracle.OracleModel(MINI, 21)
+    ids = synth.token_ids(22, 9, MINI.vocab)
+    sc = oracle.OracleSession(m, oracle.ContiguousKV.for_shape(MINI, 16)).score(ids)
+    assert sc.shape == (8,)
+    for i in (0, 3, 7):
+        lg = oracle.OracleSession(m, oracle.ContiguousKV.for_shape(MINI, 16)).forward(ids[:i + 1])
+        z = lg.astype(np.float64)
+        want = z[ids[i + 1]] - (z.max() + math.log(np.exp(z - z.max()).sum()))
+        assert abs(sc[i] - want) < 2e-5       # FP32 logits of a 1-row and a 9-row pass differ in rounding
+    assert np.all(sc < 0)
+
+
+def test_truncate_resume_equals_fresh_evaluation():
+    """Kipp Model Support, "What the gates check": after a truncation, resuming gives the logits of
+    the kept prefix plus the new ids evaluated from scratch; a truncation one position off fails."""
+    m = oracle.OracleModel(MINI, 23)
+    a, b, c = synth.token_ids(24, 37, MINI.vocab), synth.token_ids(25, 20, MINI.vocab), synth.token_ids(26, 11, MINI.vocab)
+    ref = oracle.OracleSession(m, oracle.ContiguousKV.for_shape(MINI, 96)).forward(np.concatenate([a, c]),
+                                                                                    all_logits=True)[len(a):]
+    s = oracle.OracleSession(m, oracle.PagedKV.for_shape(MINI, 4, synth.shuffled_blocks(27, 4)[:3]))
+    s.forward(np.concatenate([a, b]))
+    s.truncate(len(a))
+    got = s.forward(c, all_logits=True)
+    assert s.pos == len(a) + len(c)
+    assert max(om.nmse(g, r) for g, r in zip(got, ref)) < 1e-10
+    s.truncate(len(a) - 1)
+    off = s.forward(c, all_logits=True)
+    assert max(om.nmse(g, r) for g, r in zip(off, ref)) > 1e-4
+    with pytest.raises(ValueError):
+        s.truncate(s.pos + 1)
