@@ -250,6 +250,38 @@ def main():
     pgu_flop = 2.0 * wl.prompt * 2 * F * H
     pgu_ms = kernels["prefill_gateup"][1]
 
+    # Multi-row evaluation of the same prompt, outside the step: every row's logits (eval_n) and
+    # the prompt's next-token scores (eval_scored), median of three, HIP events on the stream;
+    # then the lm_head launches over groups of up to 32 rows, timed like the kernels above.
+    host_ids = synth.token_ids(wl.ids_seed, wl.prompt)
+    rows_lg = torch.empty((wl.prompt, shape.vocab), device="cuda")
+    rows_am = torch.empty(wl.prompt, dtype=torch.int32, device="cuda")
+    scores = torch.empty(wl.prompt - 1, device="cuda")
+    rows_t = []
+    for _ in range(3):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        s.reset()
+        ev[0].record(stream)
+        s.eval_n(host_ids, rows_lg, rows_am, stream)
+        ev[1].record(stream)
+        s.reset()
+        ev[2].record(stream)
+        s.eval_scored(host_ids, scores, stream)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        rows_t.append((ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])))
+    evn_ms = sorted(t[0] for t in rows_t)[1]
+    evs_ms = sorted(t[1] for t in rows_t)[1]
+    m.profile("rows_lmhead")
+    s.reset()
+    s.eval_n(host_ids, rows_lg, rows_am, stream)
+    n_lm, lm_ms, _ = m.profile_read()
+    m.profile("none")
+    lm_ms /= max(n_lm, 1)
+    lm_rows = min(32, wl.prompt)
+    lm_bytes = shape.vocab * shape.hidden * 2 + lm_rows * shape.hidden * 4 + lm_rows * shape.vocab * 4
+    del rows_lg
+
     rev, dirty = git_rev()
     out = {
         "metric": METRIC,
@@ -288,6 +320,13 @@ def main():
                              "frac": round(pgu_flop / (pgu_ms * 1e-3) / PEAK_BF16_FLOPS, 4),
                              "launch_us": round(pgu_ms * 1e3, 1),
                              "attn_launch_us": round(kernels["prefill_attn"][1] * 1e3, 1)},
+        "multi_row": {"rows": wl.prompt, "eval_n_ms": round(evn_ms, 3),
+                      "eval_n_tok_s": round(wl.prompt / (evn_ms * 1e-3), 1),
+                      "eval_scored_ms": round(evs_ms, 3),
+                      "lm_head_group": {"rows": lm_rows, "launches": n_lm, "launch_us": round(lm_ms * 1e3, 2),
+                                        "bytes_per_launch": lm_bytes,
+                                        "achieved_gbs": round(lm_bytes / (lm_ms * 1e-3) / 1e9, 1),
+                                        "frac_hbm_peak": round(lm_bytes / (lm_ms * 1e-3) / PEAK_HBM, 4)}},
         "commit": rev, "dirty": dirty, "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:

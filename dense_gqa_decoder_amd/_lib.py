@@ -56,6 +56,9 @@ _SIGS = {
     "gqa_session_position": (I32, [P]),
     "gqa_session_eval_prefill": (I32, [P, P, I32, P, P, P]),
     "gqa_session_eval_prefill_device": (I32, [P, P, I32, P, P, P]),
+    "gqa_session_eval_n": (I32, [P, P, I32, P, P, P]),
+    "gqa_session_eval_scored": (I32, [P, P, I32, P, P]),
+    "gqa_session_truncate": (I32, [P, I32]),
     "gqa_session_eval_decode": (I32, [P, P, I32, P, P, P]),
     "gqa_session_eval_batch": (I32, [P, I32, P, I32, P, P, P]),
     "gqa_model_check_device_error": (I32, [P, P]),
@@ -145,6 +148,18 @@ def gqa_session_eval_prefill_device(session, ids_dev_ptr, n, logits_ptr, argmax_
     _check(lib().gqa_session_eval_prefill_device(session, ids_dev_ptr, n, logits_ptr, argmax_ptr, stream))
 
 
+def gqa_session_eval_n(session, ids_ptr, n, logits_ptr, argmax_ptr, stream) -> None:
+    _check(lib().gqa_session_eval_n(session, ids_ptr, n, logits_ptr, argmax_ptr, stream))
+
+
+def gqa_session_eval_scored(session, ids_ptr, n, scores_ptr, stream) -> None:
+    _check(lib().gqa_session_eval_scored(session, ids_ptr, n, scores_ptr, stream))
+
+
+def gqa_session_truncate(session, pos) -> None:
+    _check(lib().gqa_session_truncate(session, pos))
+
+
 def gqa_session_eval_decode(session, id_ptr, id_on_device, logits_ptr, argmax_ptr, stream) -> None:
     _check(lib().gqa_session_eval_decode(session, id_ptr, id_on_device, logits_ptr, argmax_ptr, stream))
 
@@ -157,7 +172,7 @@ def gqa_model_check_device_error(model, stream) -> None:
     _check(lib().gqa_model_check_device_error(model, stream))
 
 
-GQA_PROF = {"none": 0, "decode_gateup": 1, "prefill_gateup": 2, "prefill_attn": 3, "decode_lmhead": 4}
+GQA_PROF = {"none": 0, "decode_gateup": 1, "prefill_gateup": 2, "prefill_attn": 3, "decode_lmhead": 4, "rows_lmhead": 5}
 
 
 def gqa_model_profile(model, kernel_class: int) -> None:

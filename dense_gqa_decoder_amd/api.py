@@ -154,6 +154,19 @@ class Session:
             h = np.ascontiguousarray(ids, dtype=np.int32)
             L.gqa_session_eval_prefill(self.handle, h.ctypes.data, len(h), _ptr(logits), _ptr(argmax), _stream(stream))
 
+    def eval_n(self, ids, logits, argmax=None, stream=None):
+        """Append host ids and write logits [n][vocab] (and argmax [n]) for every new position."""
+        h = np.ascontiguousarray(ids, dtype=np.int32)
+        L.gqa_session_eval_n(self.handle, h.ctypes.data, len(h), _ptr(logits), _ptr(argmax), _stream(stream))
+
+    def eval_scored(self, ids, scores, stream=None):
+        """Append host ids and write scores [n-1]: log p(ids[i+1] | ids[..i], earlier context)."""
+        h = np.ascontiguousarray(ids, dtype=np.int32)
+        L.gqa_session_eval_scored(self.handle, h.ctypes.data, len(h), _ptr(scores), _stream(stream))
+
+    def truncate(self, pos):
+        L.gqa_session_truncate(self.handle, pos)
+
     def decode(self, token, logits, argmax=None, stream=None):
         """token: a host int, or an int32 device tensor holding the id."""
         if hasattr(token, "data_ptr"):

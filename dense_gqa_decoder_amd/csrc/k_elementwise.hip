@@ -264,6 +264,43 @@ hipError_t launch_qk_rope_kv(bool decode, const float* qkv, int nsplit, int part
   return hipGetLastError();
 }
 
+// Log-probability of a given next token from a row of logits (Kipp Roadmap, status v0.0.3:
+// multi-row scoring): out[b] = l[t] - (m + log sum_v exp(l[v] - m)), m = max_v l[v], t =
+// targets[b]. One 1024-thread workgroup per row; every sum and max in a fixed order (thread
+// strides, then the 64 lanes, then the 16 waves in order), in FP32.
+__global__ __launch_bounds__(1024) void score_kernel(const float* __restrict__ logits, int V,
+                                                    const int32_t* __restrict__ targets, float* __restrict__ out) {
+  __shared__ float red[16];
+  const float* l = logits + (int64_t)blockIdx.x * V;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float mx = -INFINITY;
+  for (int i = threadIdx.x; i < V; i += 1024) mx = fmaxf(mx, l[i]);
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) mx = fmaxf(mx, red[w]);
+  __syncthreads();
+  float sum = 0.f;
+  for (int i = threadIdx.x; i < V; i += 1024) sum += expf(l[i] - mx);
+  sum = wave_sum(sum);
+  if (lane == 0) red[wave] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) tot += red[w];
+    out[blockIdx.x] = l[targets[blockIdx.x]] - (mx + logf(tot));
+  }
+}
+
+hipError_t launch_score(const float* logits, int V, const int32_t* targets, int B, float* out, hipStream_t st) {
+  if (B < 1) return hipSuccess;
+  hipLaunchKernelGGL(score_kernel, dim3(B), dim3(1024), 0, st, logits, V, targets, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_argmax(const float2* cand, int ntiles, int B, int32_t* out, hipStream_t st) {
   hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(1024), 0, st, cand, ntiles, out);
   return hipGetLastError();

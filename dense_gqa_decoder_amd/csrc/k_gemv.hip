@@ -492,16 +492,15 @@ hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, int K
   if (shm > 64 * 1024) return hipErrorInvalidValue;
   const dim3 blk(64 * kGemvWaves);
 #define GEMV_LAUNCH(Q8, NT, L)                                                                                   \
-  hipLaunchKernelGGL((gemv_kernel<Q8, NT, L>), grid, blk, shm, st, W, Wq, Wd, K, N, xs, B, klen, P, part_stride, \
-                     ldp, cand)
+  GQA_LAUNCH((gemv_kernel<Q8, NT, L>), grid, blk, shm, st, W, Wq, Wd, K, N, xs, B, klen, P, part_stride, ldp, cand)
   if (lds) {
     if (Wq) GEMV_LAUNCH(true, 1, true);
     else GEMV_LAUNCH(false, 1, true);
   } else {
     const dim3 rgrid((N / 16 + kRowsWaves - 1) / kRowsWaves, nsplit), rblk(64 * kRowsWaves);
 #define ROWS_LAUNCH(Q8, NT)                                                                                      \
-  hipLaunchKernelGGL((gemv_rows_kernel<Q8, NT>), rgrid, rblk, 0, st, W, Wq, Wd, K, N, xs, B, klen, P, part_stride, \
-                     ldp, cand)
+  GQA_LAUNCH((gemv_rows_kernel<Q8, NT>), rgrid, rblk, 0, st, W, Wq, Wd, K, N, xs, B, klen, P, part_stride, ldp, \
+             cand)
     if (B <= 16) {
       if (Wq) ROWS_LAUNCH(true, 1);
       else ROWS_LAUNCH(false, 1);

@@ -34,6 +34,7 @@ hipError_t launch_qk_rope_kv(bool decode, const float* qkv, int nsplit, int part
                              const float* rsin, int pos0, const int32_t* table0, const Rows& rows, uint16_t* kpool,
                              uint16_t* vpool, float* qout, int nrows, hipStream_t st);
 hipError_t launch_argmax(const float2* cand, int ntiles, int B, int32_t* out, hipStream_t st);
+hipError_t launch_score(const float* logits, int V, const int32_t* targets, int B, float* out, hipStream_t st);
 hipError_t launch_prefill_copy(const uint16_t* src, f16* dst, int64_t rows, int64_t cols, hipStream_t st);
 hipError_t launch_gemm(int epi, bool split, const f16* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
                        const f16* Xlo, int ldx, int T, float* C, int ldc, float out_scale, f16* Mhi, f16* Mlo,
@@ -120,6 +121,7 @@ struct gqa_model {
   int32_t* counters = nullptr;  // decode attention: finished chunks per (row, KV head)
   float* ss = nullptr;          // decode: sum-of-squares partials [2][8][32] (q|k|v input, gate|up input)
   float2* cand = nullptr;   // lm_head argmax candidates [32][vocab / 16]
+  float* slog = nullptr;    // logits of up to 32 rows being scored [32][vocab]
   f16 *xh = nullptr, *xl = nullptr, *oh = nullptr, *ol = nullptr, *mh = nullptr, *ml = nullptr;
   int32_t *ids_dev = nullptr, *err = nullptr;
   int32_t* ids_host = nullptr;  // pinned staging
@@ -304,6 +306,7 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   ALLOC(m->ss, 2 * 8 * 32, sb);
   ALLOC(m->ids_dev, std::max(d.max_positions, kMaxBatch), sb);
   ALLOC(m->cand, (int64_t)kMaxBatch * (V / 16), sb);
+  ALLOC(m->slog, (int64_t)kMaxBatch * V, sb);
   ALLOC(m->err, 1, sb);
   ALLOC(m->rcos, (int64_t)d.max_positions * 64, sb);
   ALLOC(m->rsin, (int64_t)d.max_positions * 64, sb);
@@ -514,10 +517,12 @@ int upload_ids(gqa_model* m, const int32_t* ids, int n, hipStream_t st) {
 constexpr int64_t kProfMax = 65536;
 
 // Time the next launch of kernel class `cls` when that class is being recorded: the launch
-// stamps a start/stop event pair from its own dispatch (GQA_LAUNCH).
+// stamps a start/stop event pair from its own dispatch (GQA_LAUNCH). A pair that no launch
+// consumed (a failed launch, or a kernel started another way) is not counted.
 struct ProfScope {
   gqa_model* m;
   hipStream_t st;
+  bool armed = false;
   ProfScope(gqa_model* m_, int cls, hipStream_t st_) : m(m_), st(st_) {
     if (m->prof_cls != cls) return;
     if (m->prof_used >= kProfMax) {
@@ -532,8 +537,12 @@ struct ProfScope {
     g_launch_events.start = m->prof_ev[2 * m->prof_used];
     g_launch_events.stop = m->prof_ev[2 * m->prof_used + 1];
     m->prof_used++;
+    armed = true;
   }
-  ~ProfScope() { g_launch_events = LaunchEvents{}; }   // unused if the launch failed
+  ~ProfScope() {
+    if (armed && g_launch_events.start) m->prof_used--;
+    g_launch_events = LaunchEvents{};
+  }
 };
 
 #define LAUNCH(expr)                                                                                   \
@@ -706,7 +715,12 @@ constexpr int kProfNever = -1;   // a ProfScope class no recording selects
 // the next layer's residual add + RMSNorm. The logits need only the last row of the last layer:
 // after writing that layer's K/V, its attention, o and MLP run for the last row alone (and are
 // skipped in rounds before the last).
-int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, float* logits, int32_t* argmax, hipStream_t st) {
+// What a prefill call returns: the last row's logits (and argmax), every row's, or the
+// log-probability of each next token.
+enum PrefillOut { kOutLast = 0, kOutAll = 1, kOutScores = 2 };
+
+int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* logits, int32_t* argmax,
+                float* scores, hipStream_t st) {
   gqa_model* m = s->m;
   const gqa_model_desc& d = m->d;
   const int H = d.hidden, F = d.ffn, V = d.vocab, NQ = d.n_q_heads, QD = m->QD, QKV = m->QKV;
@@ -726,8 +740,9 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, float* logits, in
                          nullptr, 0, 1.f, 1, 0, st));
       LAUNCH(launch_qk_rope_kv(false, m->qkv, 0, 0, QKV, NQ, w.q_norm, w.k_norm, eps, m->rcos, m->rsin, pos0,
                                s->d_table, none, w.kpool, w.vpool, m->q, T, st));
-      if (last && !final_round) break;
-      const int rows = last ? 1 : T, r0 = last ? T - 1 : 0;   // rows that feed the logits
+      const bool one = last && out == kOutLast;                // only the final row feeds the logits
+      if (one && !final_round) break;
+      const int rows = one ? 1 : T, r0 = one ? T - 1 : 0;
       {
         ProfScope ps(m, last ? kProfNever : GQA_PROF_PREFILL_ATTN, st);
         LAUNCH(launch_attn_prefill(m->q + (int64_t)r0 * QD, NQ, rows, pos0 + r0, s->d_table, w.kpool, w.vpool,
@@ -750,13 +765,28 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, float* logits, in
       LAUNCH(launch_rmsnorm(m->x + (int64_t)r0 * H, H, m->ppart, sd, rows * H, H, 1.f, next_norm, H, eps, 1.f, m->xh,
                             m->xl, H, rows, st));
       if (last) {
-        XSrc raw{};
-        raw.mode = X_RAW;
-        raw.hi = m->xh;
-        raw.lo = m->xl;
-        raw.ld = H;
-        LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, H, V, raw, 1, 1, logits, 0, V, argmax ? m->cand : nullptr, st));
-        if (argmax) LAUNCH(launch_argmax(m->cand, V / 16, 1, argmax, st));
+        // lm_head over the rows, up to 32 at a time (the batched decode matvec)
+        for (int g0 = 0; g0 < rows; g0 += kMaxBatch) {
+          const int i0 = off + r0 + g0;                       // call-relative index of the group's first row
+          int Bg = std::min(kMaxBatch, rows - g0);
+          if (out == kOutScores) Bg = std::min(Bg, n - 1 - i0);   // rows with a next token
+          if (Bg < 1) break;
+          XSrc raw{};
+          raw.mode = X_RAW;
+          raw.hi = m->xh + (int64_t)g0 * H;
+          raw.lo = m->xl + (int64_t)g0 * H;
+          raw.ld = H;
+          ProfScope ps(m, out == kOutLast ? kProfNever : GQA_PROF_ROWS_LMHEAD, st);
+          if (out == kOutScores) {
+            LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, H, V, raw, Bg, 1, m->slog, 0, V, nullptr, st));
+            LAUNCH(launch_score(m->slog, V, ids_dev + i0 + 1, Bg, scores + i0, st));
+          } else {
+            float* dst = logits + (int64_t)(out == kOutAll ? i0 : 0) * V;
+            LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, H, V, raw, Bg, 1, dst, 0, V, argmax ? m->cand : nullptr,
+                               st));
+            if (argmax) LAUNCH(launch_argmax(m->cand, V / 16, Bg, argmax + (out == kOutAll ? i0 : 0), st));
+          }
+        }
       }
     }
   }
@@ -781,7 +811,7 @@ int gqa_session_eval_prefill(gqa_session* s, const int32_t* ids, int32_t n, floa
     if (ids[i] < 0 || ids[i] >= d.vocab) return fail(GQA_E_RANGE, "token id %d at %d outside [0, %d)", ids[i], i, d.vocab);
   int rc = upload_ids(m, ids, n, st);
   if (rc) return rc;
-  return run_prefill(s, m->ids_dev, n, logits, argmax, st);
+  return run_prefill(s, m->ids_dev, n, kOutLast, logits, argmax, nullptr, st);
 }
 
 int gqa_session_eval_prefill_device(gqa_session* s, const int32_t* ids_dev, int32_t n, float* logits,
@@ -791,7 +821,43 @@ int gqa_session_eval_prefill_device(gqa_session* s, const int32_t* ids_dev, int3
   if (n < 1) return fail(GQA_E_INVALID, "n must be >= 1");
   if ((int64_t)s->pos + n > s->max_pos)
     return fail(GQA_E_RANGE, "context overflow: %d + %d > %d", s->pos, n, s->max_pos);
-  return run_prefill(s, ids_dev, n, logits, argmax, st);
+  return run_prefill(s, ids_dev, n, kOutLast, logits, argmax, nullptr, st);
+}
+
+int gqa_session_eval_n(gqa_session* s, const int32_t* ids, int32_t n, float* logits, int32_t* argmax, hipStream_t st) {
+  g_err.clear();
+  if (!s || !ids || !logits) return fail(GQA_E_INVALID, "null argument");
+  if (n < 1) return fail(GQA_E_INVALID, "n must be >= 1");
+  if ((int64_t)s->pos + n > s->max_pos)
+    return fail(GQA_E_RANGE, "context overflow: %d + %d > %d", s->pos, n, s->max_pos);
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= s->m->d.vocab)
+      return fail(GQA_E_RANGE, "token id %d at %d outside [0, %d)", ids[i], i, s->m->d.vocab);
+  int rc = upload_ids(s->m, ids, n, st);
+  if (rc) return rc;
+  return run_prefill(s, s->m->ids_dev, n, kOutAll, logits, argmax, nullptr, st);
+}
+
+int gqa_session_eval_scored(gqa_session* s, const int32_t* ids, int32_t n, float* scores, hipStream_t st) {
+  g_err.clear();
+  if (!s || !ids || !scores) return fail(GQA_E_INVALID, "null argument");
+  if (n < 2) return fail(GQA_E_INVALID, "n must be >= 2 (a token to score needs the one before it)");
+  if ((int64_t)s->pos + n > s->max_pos)
+    return fail(GQA_E_RANGE, "context overflow: %d + %d > %d", s->pos, n, s->max_pos);
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= s->m->d.vocab)
+      return fail(GQA_E_RANGE, "token id %d at %d outside [0, %d)", ids[i], i, s->m->d.vocab);
+  int rc = upload_ids(s->m, ids, n, st);
+  if (rc) return rc;
+  return run_prefill(s, s->m->ids_dev, n, kOutScores, nullptr, nullptr, scores, st);
+}
+
+int gqa_session_truncate(gqa_session* s, int32_t pos) {
+  g_err.clear();
+  if (!s) return fail(GQA_E_INVALID, "null session");
+  if (pos < 0 || pos > s->pos) return fail(GQA_E_RANGE, "position %d outside [0, %d]", pos, s->pos);
+  s->pos = pos;
+  return GQA_OK;
 }
 
 int gqa_session_eval_batch(gqa_session* const* ss, int32_t B, const int32_t* ids, int32_t ids_on_device,
@@ -835,7 +901,7 @@ int gqa_session_eval_decode(gqa_session* s, const int32_t* id, int32_t id_on_dev
 
 int gqa_model_profile(gqa_model* m, int32_t cls) {
   if (!m) return fail(GQA_E_INVALID, "null model");
-  if (cls < GQA_PROF_NONE || cls > GQA_PROF_DECODE_LMHEAD) return fail(GQA_E_INVALID, "unknown kernel class %d", cls);
+  if (cls < GQA_PROF_NONE || cls > GQA_PROF_ROWS_LMHEAD) return fail(GQA_E_INVALID, "unknown kernel class %d", cls);
   HIP_TRY(hipDeviceSynchronize());
   m->prof_cls = cls;
   m->prof_used = 0;

@@ -144,6 +144,31 @@ int gqa_session_eval_prefill(gqa_session* session, const int32_t* ids, int32_t n
 int gqa_session_eval_prefill_device(gqa_session* session, const int32_t* ids, int32_t n, float* logits,
                                     int32_t* argmax, hipStream_t stream);
 
+/* Multi-row evaluation (Kipp Roadmap, status v0.0.2: logits for several positions from one
+ * call). Appends n >= 1 host ids like gqa_session_eval_prefill, but writes the logits of every
+ * new position: logits [n][vocab] (device, row i is position pos + i) and, when `argmax` is
+ * not NULL, argmax [n] (device, lowest index on ties). Row n-1 equals what eval_prefill
+ * writes for the same call. Errors as eval_prefill. */
+int gqa_session_eval_n(gqa_session* session, const int32_t* ids, int32_t n, float* logits, int32_t* argmax,
+                       hipStream_t stream);
+
+/* Multi-row scoring (Kipp Roadmap, status v0.0.3: tolerance-bound scoring of several rows).
+ * Appends n >= 2 host ids like gqa_session_eval_prefill and writes scores [n-1] (device):
+ * scores[i] = log softmax(logits of position pos + i)[ids[i + 1]], the natural-log
+ * probability of each id given the ones before it (the sum of -scores is the negative
+ * log-likelihood a perplexity is built from). No logits are returned. The log-softmax is taken
+ * in FP32 over the FP32 logits. GQA_E_INVALID for n < 2; otherwise errors as eval_prefill. */
+int gqa_session_eval_scored(gqa_session* session, const int32_t* ids, int32_t n, float* scores, hipStream_t stream);
+
+/* Truncate the session to its first `pos` positions (0 <= pos <= current position), so the
+ * next evaluation continues at `pos`; the KV of later positions is overwritten as they are
+ * evaluated again. Resuming after a truncation gives the same logits as evaluating the kept
+ * prefix and the new tokens from scratch (Kipp Model Support, "What the gates check":
+ * truncate/resume among the compared paths). GQA_E_RANGE for pos out of range. Host-only,
+ * no device work: call it once the previous evaluation's stream work is ordered before the
+ * next. */
+int gqa_session_truncate(gqa_session* session, int32_t pos);
+
 /* Evaluate one token at the session's position. `id` is a host pointer when id_on_device is
  * 0 (validated: GQA_E_RANGE if outside [0, vocab)) or a device pointer when 1 (for greedy
  * loops without host round trips, e.g. the previous call's argmax buffer). A device id
@@ -176,6 +201,7 @@ int gqa_model_check_device_error(gqa_model* model, hipStream_t stream);
 #define GQA_PROF_PREFILL_GATEUP 2  /* prefill gate/up GEMM with SwiGLU (matrix-core bound) */
 #define GQA_PROF_PREFILL_ATTN 3    /* prefill flash attention */
 #define GQA_PROF_DECODE_LMHEAD 4   /* decode lm_head matvec */
+#define GQA_PROF_ROWS_LMHEAD 5     /* lm_head over a group of up to 32 rows in eval_n / eval_scored */
 int gqa_model_profile(gqa_model* model, int32_t kernel_class);
 int gqa_model_profile_read(gqa_model* model, int64_t* launches, double* total_ms, int64_t* dropped);
 

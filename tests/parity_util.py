@@ -32,8 +32,7 @@ class Gate:
         top2 = np.partition(r, -2)[-2:]
         margin = float(top2[1] - top2[0])
         rms = float(np.sqrt(np.mean((g.astype(np.float64) - r) ** 2)))
-        runner_up = int(np.argsort(r)[-2])
-        near_tie = ga != ra and margin < 4 * rms and ga == runner_up
+        near_tie = ga != ra and margin < 4 * rms and ga == int(np.argsort(r)[-2])   # runner-up
         self.rows.append(dict(pos=pos, nmse=e, ok=ga == ra, near_tie=near_tie, margin=margin, rms=rms))
         return e
 

@@ -31,24 +31,32 @@ _ORACLE_CACHE = {}
 
 
 def oracle_greedy_cached(key, shape, seed, prompt, steps, scheme="bf16"):
-    """oracle_greedy, computed once per key for the whole test module."""
+    """oracle_greedy (with the logits of every prompt row), computed once per key for the whole
+    test module."""
     if key not in _ORACLE_CACHE:
-        _ORACLE_CACHE[key] = oracle_greedy(shape, seed, prompt, steps, scheme)
-    return _ORACLE_CACHE[key]
+        _ORACLE_CACHE[key] = oracle_greedy(shape, seed, prompt, steps, scheme, prompt_rows=True)
+    ref, toks, _ = _ORACLE_CACHE[key]
+    return ref, toks
 
 
-def oracle_greedy(shape, seed, prompt, steps, scheme="bf16"):
+def oracle_prompt_rows(key):
+    """Logits [len(prompt)][vocab] of every prompt position of a cached oracle_greedy run."""
+    return _ORACLE_CACHE[key][2]
+
+
+def oracle_greedy(shape, seed, prompt, steps, scheme="bf16", prompt_rows=False):
     """Oracle logits at the last prompt position and at each greedy decode step, and the
-    greedy tokens fed at each step."""
+    greedy tokens fed at each step (and, with prompt_rows, the logits of every prompt row)."""
     m = oracle.OracleModel(shape, seed, scheme)
     s = oracle.OracleSession(m, oracle.ContiguousKV.for_shape(shape, len(prompt) + steps + 1))
-    logits = [s.prefill(prompt)]
+    rows = s.forward(prompt, all_logits=True) if prompt_rows else None
+    logits = [rows[-1] if prompt_rows else s.prefill(prompt)]
     toks = []
     for _ in range(steps):
         t = om.argmax(logits[-1])
         toks.append(t)
         logits.append(s.decode(t))
-    return logits, toks
+    return (logits, toks, rows) if prompt_rows else (logits, toks)
 
 
 def gpu_teacher_forced(model, sess, prompt, toks, vocab):
@@ -528,6 +536,179 @@ def test_decode_across_chunk_length_change(g):
         s2.close()
     w = gate.assert_ok()
     assert w <= 1e-5
+    s.close()
+    m.close()
+
+
+def _rows(sess, ids, vocab):
+    lg = torch.empty((len(ids), vocab), device="cuda")
+    am = torch.empty(len(ids), dtype=torch.int32, device="cuda")
+    sess.eval_n(ids, lg, am)
+    torch.cuda.synchronize()
+    return lg.cpu().numpy(), am.cpu().numpy()
+
+
+def _scores(sess, ids):
+    sc = torch.empty(len(ids) - 1, device="cuda")
+    sess.eval_scored(ids, sc)
+    torch.cuda.synchronize()
+    return sc.cpu().numpy().astype(np.float64)
+
+
+# Scores are log-probabilities taken in FP32 from FP32 logits. If every logit of a row is off
+# by at most e, the row's score is off by at most 2e (the target's logit and the log-sum-exp
+# each move by at most e); the FP32 log-softmax itself is held to 1e-4 against a float64 one of
+# the same logits. So a row's score may differ from the oracle's by 2e + 1e-4, with e that
+# row's largest logit error (the logits themselves pass the gate).
+SCORE_FP32_TOL = 1e-4
+
+
+def test_eval_n_every_row_parity(g):
+    """Multi-row evaluation (Kipp Roadmap, status v0.0.2): the tiny decoder in rounds of 48, a
+    100-token call (48 + 48 + 4 rows, every row of every round returned) and then a 37-token call
+    (lm_head over row groups of 32 + 5); every row against the oracle's logits of the same
+    positions (identical argmax, NMSE <= 1e-4), the device argmax equal to the host argmax, and
+    the last row equal to what eval_prefill writes for the same call."""
+    wl = synth.WORKLOADS["tiny"]
+    shape = wl.shape
+    ids = synth.token_ids(31, 137)
+    say("eval_n tiny oracle")
+    ref = oracle.OracleSession(oracle.OracleModel(shape, wl.weight_seed),
+                               oracle.ContiguousKV.for_shape(shape, 160)).forward(ids, all_logits=True)
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=12, max_positions=160, max_round_tokens=48)
+    s = g.Session(m, 160)
+    a_lg, a_am = _rows(s, ids[:100], shape.vocab)
+    b_lg, b_am = _rows(s, ids[100:], shape.vocab)
+    assert s.position == 137
+    lg, am = np.concatenate([a_lg, b_lg]), np.concatenate([a_am, b_am])
+    gate = Gate("eval_n tiny")
+    for i in range(137):
+        gate.check(i, lg[i], ref[i], int(am[i]))
+        assert am[i] == int(np.argmax(lg[i]))
+    gate.assert_ok()
+    s2 = g.Session(m, 160)
+    last = torch.empty(shape.vocab, device="cuda")
+    s2.prefill(ids[:100], last)
+    torch.cuda.synchronize()
+    assert nmse(a_lg[-1], last.cpu().numpy()) <= 1e-8
+    for o in (s, s2, m):
+        o.close()
+
+
+def test_eval_scored_parity(g):
+    """Multi-row scoring (Kipp Roadmap, status v0.0.3): 70 ids in rounds of 48 give 69 scores,
+    each the log-probability of the next id; against the log-softmax (in float64) of the
+    library's own eval_n logits within SCORE_FP32_TOL (which isolates the scoring kernel), and
+    against the oracle within 2e + SCORE_FP32_TOL, e being the largest logit error. Fewer than
+    two ids is an error."""
+    wl = synth.WORKLOADS["tiny"]
+    shape = wl.shape
+    ids = synth.token_ids(33, 70)
+    say("eval_scored tiny")
+    om_ = oracle.OracleModel(shape, wl.weight_seed)
+    ref_rows = oracle.OracleSession(om_, oracle.ContiguousKV.for_shape(shape, 96)).forward(ids, all_logits=True)
+    ref = om.next_token_log_probs(ref_rows[:-1], ids[1:])
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=8, max_positions=96, max_round_tokens=48)
+    s = g.Session(m, 96)
+    got = _scores(s, ids)
+    assert s.position == 70 and got.shape == (69,)
+    s2 = g.Session(m, 96)
+    lg, _ = _rows(s2, ids, shape.vocab)
+    own = np.max(np.abs(got - om.next_token_log_probs(lg[:-1], ids[1:])))
+    e = np.max(np.abs(lg[:-1].astype(np.float64) - ref_rows[:-1]))
+    d = np.max(np.abs(got - ref))
+    say("score |diff| vs oracle %.3g, vs own logits %.3g, largest logit error %.3g" % (d, own, e))
+    assert own <= SCORE_FP32_TOL
+    assert d <= 2 * e + SCORE_FP32_TOL
+    with pytest.raises(g.GqaError):
+        s2.eval_scored(ids[:1], torch.empty(1, device="cuda"))
+    for o in (s, s2, m):
+        o.close()
+
+
+def test_truncate_resume_parity(g):
+    """Truncate/resume (Kipp Model Support, "What the gates check"): prefill 40 ids, evaluate 20
+    more, truncate back to 40, then evaluate 11 new ids (all rows) and 3 greedy decode steps over
+    shuffled blocks: every position against the oracle evaluating the kept 40 plus the new ids
+    from scratch. Truncating past the position is an error; truncating to 0 restarts the
+    session."""
+    wl = synth.WORKLOADS["tiny"]
+    shape = wl.shape
+    a, b, c = synth.token_ids(41, 40), synth.token_ids(42, 20), synth.token_ids(43, 11)
+    say("truncate tiny oracle")
+    osess = oracle.OracleSession(oracle.OracleModel(shape, wl.weight_seed), oracle.ContiguousKV.for_shape(shape, 96))
+    ref_rows = osess.forward(np.concatenate([a, c]), all_logits=True)[len(a):]
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=16, max_positions=96)
+    s = g.Session(m, 96, block_ids=synth.shuffled_blocks(44, 16)[:3])
+    lg = torch.empty(shape.vocab, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    s.prefill(a, lg)
+    s.eval_n(b, torch.empty((len(b), shape.vocab), device="cuda"))
+    s.truncate(len(a))
+    assert s.position == len(a)
+    rows, row_am = _rows(s, c, shape.vocab)
+    gate = Gate("truncate/resume")
+    for i in range(len(c)):
+        gate.check(len(a) + i, rows[i], ref_rows[i], int(row_am[i]))
+    tok = int(row_am[-1])
+    for step in range(3):
+        want = osess.decode(tok)
+        s.decode(tok, lg, am)
+        torch.cuda.synchronize()
+        gate.check(len(a) + len(c) + step, lg.cpu().numpy(), want, int(am.item()))
+        tok = int(am.item())
+    gate.assert_ok()
+    with pytest.raises(g.GqaError):
+        s.truncate(s.position + 1)
+    s.truncate(0)
+    s.prefill(a, lg)
+    torch.cuda.synchronize()
+    ref0 = oracle_greedy(shape, wl.weight_seed, a, 0)[0][0]
+    g1 = Gate("truncate to 0")
+    g1.check(0, lg.cpu().numpy(), ref0)
+    g1.assert_ok()
+    s.close()
+    m.close()
+
+
+def test_qwen3_4b_eval_n_and_scores_full_prompt(g):
+    """Qwen3-4B shape at its full 2,048-token prompt in one round (the launch configuration
+    bench.py times): eval_n returns every row (lm_head over 64 groups of 32 rows); all 2,048
+    rows against the oracle's logits of the same positions (NMSE <= 1e-4; identical argmax,
+    device argmax included, unless the gate's near-tie rule applies), and each of eval_scored's
+    2,047 scores within 2e + SCORE_FP32_TOL of the oracle's, e being that row's largest logit
+    error."""
+    wl = synth.WORKLOADS["4b"]
+    shape = wl.shape
+    prompt = synth.token_ids(wl.ids_seed, wl.prompt)
+    say("4b oracle rows")
+    oracle_greedy_cached("4b", shape, wl.weight_seed, prompt, 4)
+    ref = oracle_prompt_rows("4b")
+    nb = synth.blocks_for(wl.prompt + 1)
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=2 * nb, max_positions=nb * 32)
+    s = g.Session(m, nb * 32, block_ids=synth.shuffled_blocks(wl.shuffle_seed, 2 * nb)[:nb])
+    say("4b eval_n")
+    lg = torch.empty((wl.prompt, shape.vocab), device="cuda")
+    am = torch.empty(wl.prompt, dtype=torch.int32, device="cuda")
+    s.eval_n(prompt, lg, am)
+    torch.cuda.synchronize()
+    am = am.cpu().numpy()
+    lg = lg.cpu().numpy()
+    gate = Gate("4b eval_n rows")
+    err = np.empty(wl.prompt)
+    for i in range(wl.prompt):
+        gate.check(i, lg[i], ref[i], int(am[i]))
+        err[i] = np.max(np.abs(lg[i].astype(np.float64) - ref[i]))
+    gate.assert_ok()
+    say("4b rows: largest logit error %.3g (median row %.3g)" % (err.max(), np.median(err)))
+    del lg
+    s.reset()
+    say("4b eval_scored")
+    got = _scores(s, prompt)
+    want = om.next_token_log_probs(ref[:-1], prompt[1:])
+    d = np.abs(got - want)
+    say("4b score largest |diff| %.3g" % d.max())
+    assert np.all(d <= 2 * err[:-1] + SCORE_FP32_TOL)
     s.close()
     m.close()
 
