@@ -39,7 +39,8 @@ class ModelDesc(ctypes.Structure):
 class ModelInfo(ctypes.Structure):
     _fields_ = [("round_tokens", ctypes.c_int32), ("cu_count", ctypes.c_int32), ("weight_bytes", ctypes.c_int64),
                 ("kv_pool_bytes", ctypes.c_int64), ("scratch_bytes", ctypes.c_int64),
-                ("prefill_copy_bytes", ctypes.c_int64), ("free_blocks", ctypes.c_int32)]
+                ("prefill_copy_bytes", ctypes.c_int64), ("free_blocks", ctypes.c_int32),
+                ("cached_blocks", ctypes.c_int32)]
 
 
 _lib = None
@@ -53,6 +54,9 @@ _SIGS = {
     "gqa_session_create": (I32, [P, I32, P, ctypes.POINTER(P)]),
     "gqa_session_destroy": (None, [P]),
     "gqa_session_reset": (I32, [P]),
+    "gqa_session_create_pooled": (I32, [P, I32, ctypes.POINTER(P)]),
+    "gqa_session_publish": (I32, [P]),
+    "gqa_session_reused": (I32, [P]),
     "gqa_session_position": (I32, [P]),
     "gqa_session_eval_prefill": (I32, [P, P, I32, P, P, P]),
     "gqa_session_eval_prefill_device": (I32, [P, P, I32, P, P, P]),
@@ -130,6 +134,20 @@ def gqa_session_create(model: int, max_positions: int, block_ids_ptr: int | None
 
 def gqa_session_destroy(session: int) -> None:
     lib().gqa_session_destroy(session)
+
+
+def gqa_session_create_pooled(model, max_positions):
+    out = P()
+    _check(lib().gqa_session_create_pooled(model, max_positions, ctypes.byref(out)))
+    return out.value
+
+
+def gqa_session_publish(session) -> None:
+    _check(lib().gqa_session_publish(session))
+
+
+def gqa_session_reused(session) -> int:
+    return lib().gqa_session_reused(session)
 
 
 def gqa_session_reset(session: int) -> None:

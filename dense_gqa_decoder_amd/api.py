@@ -127,16 +127,31 @@ class Model:
 
 
 class Session:
-    def __init__(self, model: Model, max_positions: int, block_ids=None):
+    def __init__(self, model: Model, max_positions: int, block_ids=None, pooled=False):
+        """pooled=True: blocks mapped on demand from the model's pool, with prefix sharing
+        (gqa_session_create_pooled); block_ids must then be None."""
         self.model = model
         self._ids = None
         ptr = None
         if block_ids is not None:
+            if pooled:
+                raise ValueError("a pooled session takes no block ids")
             self._ids = np.ascontiguousarray(block_ids, dtype=np.int32)
             ptr = self._ids.ctypes.data
         self.handle = None
-        self.handle = L.gqa_session_create(model.handle, max_positions, ptr)
+        if pooled:
+            self.handle = L.gqa_session_create_pooled(model.handle, max_positions)
+        else:
+            self.handle = L.gqa_session_create(model.handle, max_positions, ptr)
         _live_sessions.add(self)
+
+    @property
+    def reused(self):
+        """Positions the last prefill took from the prefix cache."""
+        return L.gqa_session_reused(self.handle)
+
+    def publish(self):
+        L.gqa_session_publish(self.handle)
 
     @property
     def position(self):

@@ -36,6 +36,14 @@ constexpr int kHeadDim = 128;
 constexpr int kKvHeads = 8;
 constexpr int kBlock = 32;          // positions per KV block
 constexpr int kMaxBatch = 32;       // rows of one batched decode
+
+// Block-table entries written by one launch (values passed as kernel arguments).
+constexpr int kTableWritesMax = 32;
+struct TableWrites {
+  int32_t idx[kTableWritesMax];
+  int32_t val[kTableWritesMax];
+  int32_t n;
+};
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Epilogues of the projection kernels.

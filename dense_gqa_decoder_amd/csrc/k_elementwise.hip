@@ -301,6 +301,20 @@ hipError_t launch_score(const float* logits, int V, const int32_t* targets, int 
   return hipGetLastError();
 }
 
+// Entries of a pooled session's block table. The values travel as kernel arguments, so they are
+// fixed at launch and stream-ordered with the evaluation that reads them.
+__global__ __launch_bounds__(64) void table_write_kernel(int32_t* __restrict__ table, TableWrites t) {
+  const int i = threadIdx.x;
+  if (i < t.n) table[t.idx[i]] = t.val[i];
+}
+
+hipError_t launch_table_writes(int32_t* table, const TableWrites& t, hipStream_t st) {
+  if (t.n < 1) return hipSuccess;
+  if (t.n > kTableWritesMax) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(table_write_kernel, dim3(1), dim3(64), 0, st, table, t);
+  return hipGetLastError();
+}
+
 hipError_t launch_argmax(const float2* cand, int ntiles, int B, int32_t* out, hipStream_t st) {
   hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(1024), 0, st, cand, ntiles, out);
   return hipGetLastError();

@@ -12,12 +12,14 @@
 #include <string.h>
 
 #include <algorithm>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
 
 #include "../../include/gqa.h"
 #include "gqa_common.h"
+#include "kv_pool.h"
 
 namespace gqa {
 hipError_t launch_gen_weights(uint16_t* dst, uint64_t key, int64_t rows, int64_t cols, int mode, int64_t row_off,
@@ -35,6 +37,7 @@ hipError_t launch_qk_rope_kv(bool decode, const float* qkv, int nsplit, int part
                              uint16_t* vpool, float* qout, int nrows, hipStream_t st);
 hipError_t launch_argmax(const float2* cand, int ntiles, int B, int32_t* out, hipStream_t st);
 hipError_t launch_score(const float* logits, int V, const int32_t* targets, int B, float* out, hipStream_t st);
+hipError_t launch_table_writes(int32_t* table, const TableWrites& t, hipStream_t st);
 hipError_t launch_prefill_copy(const uint16_t* src, f16* dst, int64_t rows, int64_t cols, hipStream_t st);
 hipError_t launch_gemm(int epi, bool split, const f16* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
                        const f16* Xlo, int ldx, int T, float* C, int ldc, float out_scale, f16* Mhi, f16* Mlo,
@@ -128,8 +131,8 @@ struct gqa_model {
   hipEvent_t ids_evt = nullptr;
   int64_t part_floats = 0;
   std::vector<void*> allocs;
-  std::vector<char> block_used;
-  int free_blocks = 0, sessions = 0;
+  std::unique_ptr<KvPool> pool;   // block states and the prefix cache
+  int sessions = 0;
   int64_t weight_bytes = 0, kv_bytes = 0, scratch_bytes = 0, prefill_copy_bytes = 0;
   std::mutex mu;
   // kernel timing (gqa_model_profile)
@@ -141,7 +144,9 @@ struct gqa_model {
 struct gqa_session {
   gqa_model* m = nullptr;
   int max_pos = 0, pos = 0;
-  std::vector<int32_t> blocks;
+  std::vector<int32_t> blocks;          // fixed table (sessions created with gqa_session_create)
+  std::unique_ptr<PooledSeq> seq;       // on-demand table with prefix sharing (pooled sessions)
+  int32_t reused = 0;                   // positions the last eval_prefill took from the cache
   int32_t* d_table = nullptr;
 };
 
@@ -405,8 +410,7 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
       return fail(GQA_E_HIP, "RoPE table upload failed: %s", hipGetErrorString(e));
     }
   }
-  m->block_used.assign(d.kv_pool_blocks, 0);
-  m->free_blocks = d.kv_pool_blocks;
+  m->pool.reset(new KvPool(d.kv_pool_blocks));
   *out = m;
   return GQA_OK;
 }
@@ -425,7 +429,8 @@ int gqa_model_get_info(const gqa_model* m, gqa_model_info* info) {
   info->kv_pool_bytes = m->kv_bytes;
   info->scratch_bytes = m->scratch_bytes;
   info->prefill_copy_bytes = m->prefill_copy_bytes;
-  info->free_blocks = m->free_blocks;
+  info->free_blocks = m->pool->available();
+  info->cached_blocks = m->pool->cached_count();
   return GQA_OK;
 }
 
@@ -437,21 +442,22 @@ int gqa_session_create(gqa_model* m, int32_t max_positions, const int32_t* block
   int nb = (max_positions + kBlock - 1) / kBlock;
   std::lock_guard<std::mutex> lk(m->mu);
   std::vector<int32_t> blocks(nb);
+  KvPool& pool = *m->pool;
   if (block_ids) {
     std::vector<char> seen(m->d.kv_pool_blocks, 0);
     for (int i = 0; i < nb; ++i) {
       int b = block_ids[i];
       if (b < 0 || b >= m->d.kv_pool_blocks) return fail(GQA_E_INVALID, "block id %d outside the pool", b);
       if (seen[b]) return fail(GQA_E_INVALID, "block id %d repeated", b);
-      if (m->block_used[b]) return fail(GQA_E_INVALID, "block id %d already owned by a session", b);
+      if (pool.state(b) == KvPool::PRIVATE || pool.refs(b) > 0)
+        return fail(GQA_E_INVALID, "block id %d already owned by a session", b);
       seen[b] = 1;
       blocks[i] = b;
     }
+    for (int b : blocks) pool.take(b);
   } else {
-    if (m->free_blocks < nb) return fail(GQA_E_OOM, "KV pool has %d free blocks, %d needed", m->free_blocks, nb);
-    int k = 0;
-    for (int b = 0; b < m->d.kv_pool_blocks && k < nb; ++b)
-      if (!m->block_used[b]) blocks[k++] = b;
+    if (pool.available() < nb) return fail(GQA_E_OOM, "KV pool has %d free blocks, %d needed", pool.available(), nb);
+    for (int i = 0; i < nb; ++i) blocks[i] = pool.take_any();
   }
   gqa_session* s = new gqa_session();
   s->m = m;
@@ -468,11 +474,10 @@ int gqa_session_create(gqa_model* m, int32_t max_positions, const int32_t* block
   e = hipMemcpy(s->d_table, blocks.data(), sizeof(int32_t) * nb, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(v);
+    for (int b : blocks) pool.unref(b);
     delete s;
     return fail(GQA_E_HIP, "block table upload failed: %s", hipGetErrorString(e));
   }
-  for (int b : blocks) m->block_used[b] = 1;
-  m->free_blocks -= nb;
   m->sessions++;
   *out = s;
   return GQA_OK;
@@ -484,19 +489,65 @@ void gqa_session_destroy(gqa_session* s) {
   (void)hipDeviceSynchronize();
   {
     std::lock_guard<std::mutex> lk(m->mu);
-    for (int b : s->blocks) m->block_used[b] = 0;
-    m->free_blocks += (int)s->blocks.size();
+    if (s->seq) s->seq->finish(s->pos);   // publish at finish
+    for (int b : s->blocks) m->pool->unref(b);
     m->sessions--;
   }
   (void)hipFree(s->d_table);
   delete s;
 }
 
-int gqa_session_reset(gqa_session* s) {
-  if (!s) return fail(GQA_E_INVALID, "null session");
-  s->pos = 0;
+int gqa_session_create_pooled(gqa_model* m, int32_t max_positions, gqa_session** out) {
+  g_err.clear();
+  if (!m || !out) return fail(GQA_E_INVALID, "null argument");
+  if (max_positions < 1 || max_positions > m->d.max_positions)
+    return fail(GQA_E_INVALID, "max_positions %d outside [1, %d]", max_positions, m->d.max_positions);
+  const int nb = (max_positions + kBlock - 1) / kBlock;
+  void* v = nullptr;
+  hipError_t e = hipMalloc(&v, sizeof(int32_t) * nb);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(GQA_E_OOM, "block table allocation failed");
+  }
+  // unmapped entries point at block 0: never read below the session's position, and a valid
+  // address if a kernel's rounding ever reads one
+  e = hipMemset(v, 0, sizeof(int32_t) * nb);
+  if (e != hipSuccess) {
+    (void)hipFree(v);
+    return fail(GQA_E_HIP, "block table initialisation failed: %s", hipGetErrorString(e));
+  }
+  gqa_session* s = new gqa_session();
+  s->m = m;
+  s->max_pos = max_positions;
+  s->d_table = (int32_t*)v;
+  std::lock_guard<std::mutex> lk(m->mu);
+  s->seq.reset(new PooledSeq(*m->pool, max_positions));
+  m->sessions++;
+  *out = s;
   return GQA_OK;
 }
+
+int gqa_session_reset(gqa_session* s) {
+  if (!s) return fail(GQA_E_INVALID, "null session");
+  if (s->seq) {
+    std::lock_guard<std::mutex> lk(s->m->mu);
+    s->seq->finish(s->pos);
+  }
+  s->pos = 0;
+  s->reused = 0;
+  return GQA_OK;
+}
+
+int gqa_session_publish(gqa_session* s) {
+  g_err.clear();
+  if (!s) return fail(GQA_E_INVALID, "null session");
+  if (!s->seq) return fail(GQA_E_INVALID, "not a pooled session");
+  std::lock_guard<std::mutex> lk(s->m->mu);
+  s->seq->publish(s->pos);
+  return GQA_OK;
+}
+
+int32_t gqa_session_reused(const gqa_session* s) { return s ? s->reused : -1; }
 
 int32_t gqa_session_position(const gqa_session* s) { return s ? s->pos : -1; }
 
@@ -512,6 +563,45 @@ int upload_ids(gqa_model* m, const int32_t* ids, int n, hipStream_t st) {
   HIP_TRY(hipMemcpyAsync(m->ids_dev, m->ids_host, sizeof(int32_t) * n, hipMemcpyHostToDevice, st));
   HIP_TRY(hipEventRecord(m->ids_evt, st));
   return GQA_OK;
+}
+
+// Apply a pooled session's block changes on `st` before its evaluation: whole-block K/V copies
+// (copy on write) in every layer, then the table entries.
+int apply_pool_changes(gqa_session* s, const std::vector<TableWrite>& tw, const std::vector<BlockCopy>& cp,
+                       hipStream_t st) {
+  gqa_model* m = s->m;
+  const size_t blk = (size_t)kKvHeads * kBlock * kHeadDim;
+  for (const BlockCopy& c : cp)
+    for (const LayerW& w : m->L) {
+      HIP_TRY(hipMemcpyAsync(w.kpool + c.dst * blk, w.kpool + c.src * blk, blk * 2, hipMemcpyDeviceToDevice, st));
+      HIP_TRY(hipMemcpyAsync(w.vpool + c.dst * blk, w.vpool + c.src * blk, blk * 2, hipMemcpyDeviceToDevice, st));
+    }
+  for (size_t i = 0; i < tw.size(); i += kTableWritesMax) {
+    TableWrites t{};
+    t.n = (int)std::min(tw.size() - i, (size_t)kTableWritesMax);
+    for (int k = 0; k < t.n; ++k) {
+      t.idx[k] = tw[i + k].idx;
+      t.val[k] = tw[i + k].val;
+    }
+    HIP_TRY(launch_table_writes(s->d_table, t, st));
+  }
+  return GQA_OK;
+}
+
+// Map and make private the blocks a pooled session writes for positions [p0, p1), recording
+// the ids (nullptr: not known on the host). GQA_E_OOM, with nothing changed, if the pool is
+// exhausted. No-op for sessions with a fixed table.
+int prepare_write(gqa_session* s, int p0, int p1, const int32_t* ids, hipStream_t st) {
+  if (!s->seq) return GQA_OK;
+  std::vector<TableWrite> tw;
+  std::vector<BlockCopy> cp;
+  {
+    std::lock_guard<std::mutex> lk(s->m->mu);
+    if (!s->seq->prepare_write(p0, p1, tw, cp))
+      return fail(GQA_E_OOM, "KV pool exhausted: no block free or evictable for positions [%d, %d)", p0, p1);
+    s->seq->record(p0, ids, p1 - p0);
+  }
+  return apply_pool_changes(s, tw, cp, st);
 }
 
 constexpr int64_t kProfMax = 65536;
@@ -809,9 +899,33 @@ int gqa_session_eval_prefill(gqa_session* s, const int32_t* ids, int32_t n, floa
     return fail(GQA_E_RANGE, "context overflow: %d + %d > %d", s->pos, n, s->max_pos);
   for (int i = 0; i < n; ++i)
     if (ids[i] < 0 || ids[i] >= d.vocab) return fail(GQA_E_RANGE, "token id %d at %d outside [0, %d)", ids[i], i, d.vocab);
-  int rc = upload_ids(m, ids, n, st);
+  // a pooled session at position 0 first maps the cached blocks of its prompt's leading whole
+  // blocks and evaluates only the rest
+  int reuse = 0;
+  if (s->seq && s->pos == 0) {
+    std::vector<TableWrite> tw;
+    {
+      std::lock_guard<std::mutex> lk(m->mu);
+      reuse = s->seq->map_prefix(ids, n, tw);
+    }
+    int rc = apply_pool_changes(s, tw, {}, st);
+    if (rc) return rc;
+    s->pos = reuse;
+  }
+  s->reused = reuse;
+  int rc = prepare_write(s, s->pos, s->pos + n - reuse, ids + reuse, st);
+  if (rc) {
+    if (reuse) {
+      std::lock_guard<std::mutex> lk(m->mu);
+      s->seq->release();
+      s->pos = 0;
+      s->reused = 0;
+    }
+    return rc;
+  }
+  rc = upload_ids(m, ids, n, st);
   if (rc) return rc;
-  return run_prefill(s, m->ids_dev, n, kOutLast, logits, argmax, nullptr, st);
+  return run_prefill(s, m->ids_dev + reuse, n - reuse, kOutLast, logits, argmax, nullptr, st);
 }
 
 int gqa_session_eval_prefill_device(gqa_session* s, const int32_t* ids_dev, int32_t n, float* logits,
@@ -821,6 +935,8 @@ int gqa_session_eval_prefill_device(gqa_session* s, const int32_t* ids_dev, int3
   if (n < 1) return fail(GQA_E_INVALID, "n must be >= 1");
   if ((int64_t)s->pos + n > s->max_pos)
     return fail(GQA_E_RANGE, "context overflow: %d + %d > %d", s->pos, n, s->max_pos);
+  int rc = prepare_write(s, s->pos, s->pos + n, nullptr, st);
+  if (rc) return rc;
   return run_prefill(s, ids_dev, n, kOutLast, logits, argmax, nullptr, st);
 }
 
@@ -833,7 +949,9 @@ int gqa_session_eval_n(gqa_session* s, const int32_t* ids, int32_t n, float* log
   for (int i = 0; i < n; ++i)
     if (ids[i] < 0 || ids[i] >= s->m->d.vocab)
       return fail(GQA_E_RANGE, "token id %d at %d outside [0, %d)", ids[i], i, s->m->d.vocab);
-  int rc = upload_ids(s->m, ids, n, st);
+  int rc = prepare_write(s, s->pos, s->pos + n, ids, st);
+  if (rc) return rc;
+  rc = upload_ids(s->m, ids, n, st);
   if (rc) return rc;
   return run_prefill(s, s->m->ids_dev, n, kOutAll, logits, argmax, nullptr, st);
 }
@@ -847,7 +965,9 @@ int gqa_session_eval_scored(gqa_session* s, const int32_t* ids, int32_t n, float
   for (int i = 0; i < n; ++i)
     if (ids[i] < 0 || ids[i] >= s->m->d.vocab)
       return fail(GQA_E_RANGE, "token id %d at %d outside [0, %d)", ids[i], i, s->m->d.vocab);
-  int rc = upload_ids(s->m, ids, n, st);
+  int rc = prepare_write(s, s->pos, s->pos + n, ids, st);
+  if (rc) return rc;
+  rc = upload_ids(s->m, ids, n, st);
   if (rc) return rc;
   return run_prefill(s, s->m->ids_dev, n, kOutScores, nullptr, nullptr, scores, st);
 }
@@ -887,6 +1007,10 @@ int gqa_session_eval_batch(gqa_session* const* ss, int32_t B, const int32_t* ids
     int rc = upload_ids(m, ids, B, st);
     if (rc) return rc;
     ids_dev = m->ids_dev;
+  }
+  for (int b = 0; b < B; ++b) {
+    int rc = prepare_write(ss[b], ss[b]->pos, ss[b]->pos + 1, ids_on_device ? nullptr : ids + b, st);
+    if (rc) return rc;
   }
   int rc = run_decode(m, rows, B, max_ctx, ids_dev, logits, argmax, st);
   if (rc) return rc;

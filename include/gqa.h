@@ -91,7 +91,8 @@ typedef struct {
   int64_t kv_pool_bytes;      /* device bytes of the K and V pools */
   int64_t scratch_bytes;      /* device bytes of per-model activation scratch */
   int64_t prefill_copy_bytes; /* device bytes of the FP16 copies of BF16 projections used by prefill */
-  int32_t free_blocks;        /* KV blocks not owned by any session */
+  int32_t free_blocks;        /* KV blocks a new session can take: free, or cached and mapped by no session */
+  int32_t cached_blocks;      /* KV blocks in the prefix cache (mapped or not) */
 } gqa_model_info;
 
 /* Create a model on the current HIP device with seeded synthetic weights.
@@ -111,17 +112,49 @@ int gqa_model_get_info(const gqa_model* model, gqa_model_info* info);
 
 /* Create a session that can hold `max_positions` positions. It takes
  * ceil(max_positions/32) physical blocks from the model pool:
- *   block_ids == NULL: the lowest-numbered free blocks, in increasing order (identity-like);
+ *   block_ids == NULL: the lowest-numbered free blocks, in increasing order (identity-like),
+ *   then, if too few are free, cached prefix blocks no session maps, least recently used first;
  *   otherwise a host array of that many distinct, currently free block ids (any order:
  *   logical block i of the session lives in physical block block_ids[i]).
  * Returns GQA_E_OOM if the pool has too few free blocks, GQA_E_INVALID for a bad id list.
  * Uploads the block table (synchronously). */
 int gqa_session_create(gqa_model* model, int32_t max_positions, const int32_t* block_ids, gqa_session** out);
 
-/* Return the session's blocks to the pool and free it. NULL is ignored. */
+/* Create a pooled session that can hold `max_positions` positions (Kipp Roadmap, status
+ * v0.0.3: pooled sessions sharing one model-owned slab through a content-addressed pool of
+ * 32-token blocks). It takes no blocks up front: a block is mapped when a position in it is
+ * first written (GQA_E_OOM from that evaluation if no block is free or evictable).
+ *   - Prefix reuse: gqa_session_eval_prefill with host ids at position 0 first maps the cached
+ *     blocks holding the prompt's leading whole 32-token blocks (matched by token ids and by the
+ *     chain of blocks before them, compared exactly, not by hash alone), keeping at least one id
+ *     to evaluate, and evaluates only the rest; gqa_session_reused reports how many positions
+ *     it took. Its logits equal those of evaluating the whole prompt, up to rounding.
+ *   - Publishing: gqa_session_destroy and gqa_session_reset (the end of a request) publish the
+ *     session's whole blocks whose ids it knows (those evaluated from host ids), from the first
+ *     block on, into the cache; gqa_session_publish does so without ending the request.
+ *   - Cached blocks stay in the model's pool after their sessions end; when a block is needed
+ *     and none is free, the least recently used cached block that no session maps is evicted.
+ *   - Writing into a cached block (after gqa_session_truncate) first gives the session a
+ *     private copy of it, so other sessions' blocks never change.
+ * Blocks are handed from one session to another on the host as soon as a call returns, so all
+ * sessions of a model must enqueue their work on one stream (as the model's scratch already
+ * requires). The device table is updated on the evaluation's stream. */
+int gqa_session_create_pooled(gqa_model* model, int32_t max_positions, gqa_session** out);
+
+/* Publish a pooled session's whole known blocks below its position now (see
+ * gqa_session_create_pooled). GQA_E_INVALID for a session with a fixed table. */
+int gqa_session_publish(gqa_session* session);
+
+/* Positions the session's last gqa_session_eval_prefill took from the prefix cache (0 for
+ * sessions with a fixed table). */
+int32_t gqa_session_reused(const gqa_session* session);
+
+/* Return the session's blocks to the pool and free it (a pooled session publishes first).
+ * NULL is ignored. */
 void gqa_session_destroy(gqa_session* session);
 
-/* Set the position to 0, keeping the blocks. */
+/* Set the position to 0. A session with a fixed table keeps its blocks; a pooled session
+ * publishes and then gives up its blocks. */
 int gqa_session_reset(gqa_session* session);
 
 /* Number of positions evaluated so far. */

@@ -671,6 +671,152 @@ def test_truncate_resume_parity(g):
     m.close()
 
 
+def _prefill(sess, ids, vocab):
+    lg = torch.empty(vocab, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    sess.prefill(ids, lg, am)
+    torch.cuda.synchronize()
+    return lg.cpu().numpy(), int(am.item())
+
+
+def _oracle_last(shape, seed, ids):
+    return oracle.OracleSession(oracle.OracleModel(shape, seed),
+                                oracle.ContiguousKV.for_shape(shape, len(ids) + 1)).forward(ids)
+
+
+def test_pooled_prefix_reuse_parity(g):
+    """Content-addressed prefix blocks (Kipp Roadmap, status v0.0.3), tiny decoder. A pooled
+    session prefills a 200-id prompt P and ends (publishing its 6 whole blocks); a second maps
+    them and evaluates only the last 8 ids; a third shares P's first 100 ids (3 blocks reused);
+    a 192-id prompt reuses 5 blocks (one id is always evaluated); a session truncated into a
+    shared block writes a private copy, after which P still hits its intact blocks; greedy
+    decode after a reused prefix. Every logit vector against the oracle evaluating the whole
+    prompt from scratch (gate)."""
+    wl = synth.WORKLOADS["tiny"]
+    shape, seed = wl.shape, wl.weight_seed
+    P = synth.token_ids(51, 200)
+    other = synth.token_ids(52, 60)
+    m = g.Model.from_shape(shape, seed=seed, kv_pool_blocks=64, max_positions=512)
+    gate = Gate("pooled prefix reuse")
+    say("pooled: cold prompt")
+    a = g.Session(m, 512, pooled=True)
+    la, _ = _prefill(a, P, shape.vocab)
+    assert a.reused == 0
+    ref_p = _oracle_last(shape, seed, P)
+    gate.check(0, la, ref_p)
+    a.close()
+    assert m.info().cached_blocks == 6
+    say("pooled: warm prompt")
+    b = g.Session(m, 512, pooled=True)
+    lb, amb = _prefill(b, P, shape.vocab)
+    assert b.reused == 192
+    gate.check(1, lb, ref_p, amb)
+    assert nmse(lb, la) <= 1e-8
+    # greedy decode after the reused prefix, teacher-forced with the oracle's tokens
+    osess = oracle.OracleSession(oracle.OracleModel(shape, seed), oracle.ContiguousKV.for_shape(shape, 256))
+    r = osess.forward(P)
+    lg = torch.empty(shape.vocab, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    for step in range(3):
+        t = om.argmax(r)
+        r = osess.decode(t)
+        b.decode(t, lg, am)
+        torch.cuda.synchronize()
+        gate.check(2 + step, lg.cpu().numpy(), r, int(am.item()))
+    say("pooled: shared first 100 ids")
+    Q = np.concatenate([P[:100], other])
+    c = g.Session(m, 512, pooled=True)
+    lc, amc = _prefill(c, Q, shape.vocab)
+    assert c.reused == 96
+    gate.check(5, lc, _oracle_last(shape, seed, Q), amc)
+    d = g.Session(m, 512, pooled=True)
+    ld, amd = _prefill(d, P[:192], shape.vocab)
+    assert d.reused == 160
+    gate.check(6, ld, _oracle_last(shape, seed, P[:192]), amd)
+    say("pooled: truncate into a shared block, copy on write")
+    b.truncate(100)
+    lt, amt = _prefill(b, other[:20], shape.vocab)
+    gate.check(7, lt, _oracle_last(shape, seed, np.concatenate([P[:100], other[:20]])), amt)
+    e = g.Session(m, 512, pooled=True)
+    le, ame = _prefill(e, P, shape.vocab)
+    assert e.reused == 192
+    gate.check(8, le, ref_p, ame)
+    gate.assert_ok()
+    for o in (b, c, d, e, m):
+        o.close()
+
+
+def test_pooled_eviction_and_exhaustion(g):
+    """A 16-block pool: a 150-id prompt X publishes 4 blocks; a 400-id prompt Y needs 13 blocks,
+    so the least recently used of X's blocks (its first) is evicted, which breaks X's chain: X
+    again reuses nothing and is still right. With every block held by fixed-table sessions, a
+    pooled prefill fails with GQA_E_OOM and leaves the session at position 0."""
+    wl = synth.WORKLOADS["tiny"]
+    shape, seed = wl.shape, wl.weight_seed
+    X, Y = synth.token_ids(53, 150), synth.token_ids(54, 400)
+    m = g.Model.from_shape(shape, seed=seed, kv_pool_blocks=16, max_positions=512)
+    gate = Gate("pooled eviction")
+    s1 = g.Session(m, 512, pooled=True)
+    gate.check(0, _prefill(s1, X, shape.vocab)[0], _oracle_last(shape, seed, X))
+    s1.close()
+    assert m.info().cached_blocks == 4 and m.info().free_blocks == 16
+    s2 = g.Session(m, 512, pooled=True)
+    l2, a2 = _prefill(s2, Y, shape.vocab)
+    gate.check(1, l2, _oracle_last(shape, seed, Y), a2)
+    s2.close()
+    s3 = g.Session(m, 512, pooled=True)
+    l3, a3 = _prefill(s3, X, shape.vocab)
+    assert s3.reused == 0
+    gate.check(2, l3, _oracle_last(shape, seed, X), a3)
+    s3.close()
+    gate.assert_ok()
+    fixed = [g.Session(m, 32 * 8), g.Session(m, 32 * 8)]          # all 16 blocks (cached ones evicted)
+    assert m.info().free_blocks == 0 and m.info().cached_blocks == 0
+    s4 = g.Session(m, 512, pooled=True)
+    with pytest.raises(g.GqaError):
+        s4.prefill(X, torch.empty(shape.vocab, device="cuda"))
+    assert s4.position == 0
+    for o in fixed + [s4, m]:
+        o.close()
+
+
+def test_pooled_batched_decode(g):
+    """Pooled sessions in batched decode: three sessions share a 70-id prefix (the last two
+    reuse its 2 blocks), then 40 batched greedy steps cross block boundaries, so blocks are
+    mapped on demand inside eval_batch; each row against the oracle (gate, teacher-forced)."""
+    wl = synth.WORKLOADS["tiny"]
+    shape, seed = wl.shape, wl.weight_seed
+    pre = synth.token_ids(55, 70)
+    tails = [synth.token_ids(56 + i, 5 + 7 * i) for i in range(3)]
+    m = g.Model.from_shape(shape, seed=seed, kv_pool_blocks=64, max_positions=256)
+    ss, ors, refs = [], [], []
+    for i in range(3):
+        ids = np.concatenate([pre, tails[i]])
+        s = g.Session(m, 256, pooled=True)
+        _prefill(s, ids, shape.vocab)
+        if i:
+            assert s.reused == 64
+        s.publish()
+        ss.append(s)
+        o = oracle.OracleSession(oracle.OracleModel(shape, seed), oracle.ContiguousKV.for_shape(shape, 256))
+        refs.append(o.forward(ids))
+        ors.append(o)
+    gate = Gate("pooled batched")
+    lg = torch.empty((3, shape.vocab), device="cuda")
+    am = torch.empty(3, dtype=torch.int32, device="cuda")
+    for step in range(40):
+        toks = [om.argmax(r) for r in refs]
+        m.eval_batch(ss, toks, lg, am)
+        torch.cuda.synchronize()
+        got, ga = lg.cpu().numpy(), am.cpu().numpy()
+        refs = [o.decode(t) for o, t in zip(ors, toks)]
+        for i in range(3):
+            gate.check(step * 3 + i, got[i], refs[i], int(ga[i]))
+    gate.assert_ok()
+    for o in ss + [m]:
+        o.close()
+
+
 def test_qwen3_4b_eval_n_and_scores_full_prompt(g):
     """Qwen3-4B shape at its full 2,048-token prompt in one round (the launch configuration
     bench.py times): eval_n returns every row (lm_head over 64 groups of 32 rows); all 2,048
