@@ -25,6 +25,7 @@ PEAK_BF16_FLOPS = 2.5e15    # dense FP16/BF16 MFMA, MI355X
 PEAK_HBM = 8.0e12           # bytes/s, MI355X HBM3E
 
 METRIC = "prefill tok/s @2048 + decode tok/s, Qwen3-4B-shape BF16, 1 MI355X (% roofline)"
+PREFIX_PROMPT = 6890        # repeated-prompt length of the prefix-reuse measurement (Kipp Roadmap, status v0.0.3)
 
 
 def algorithmic(shape, prompt, decode):
@@ -189,8 +190,10 @@ def main():
     nb = synth.blocks_for(wl.prompt + wl.decode)
     pool = 4 * nb
     table = synth.shuffled_blocks(wl.shuffle_seed, pool)[:nb]
-    m = g.Model.from_shape(shape, seed=wl.weight_seed, scheme=wl.scheme, kv_pool_blocks=pool, max_positions=nb * 32,
-                           prefill=args.prefill)
+    # room for the prefix-reuse measurement's pooled sessions beside the timed one
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, scheme=wl.scheme,
+                           kv_pool_blocks=pool + synth.blocks_for(PREFIX_PROMPT) + 1,
+                           max_positions=max(nb * 32, synth.blocks_for(PREFIX_PROMPT) * 32), prefill=args.prefill)
     s = g.Session(m, nb * 32, block_ids=table)
     # the prompt is resident in HBM before timing (eval_prefill_device reads it there)
     ids = torch.from_numpy(synth.token_ids(wl.ids_seed, wl.prompt).astype("int32")).to("cuda")
@@ -282,6 +285,26 @@ def main():
     lm_bytes = shape.vocab * shape.hidden * 2 + lm_rows * shape.hidden * 4 + lm_rows * shape.vocab * 4
     del rows_lg
 
+    # Prefix reuse (pooled sessions): time to the first logits of a PREFIX_PROMPT-token prompt
+    # in a fresh pooled session (cold), then of the same prompt in another pooled session after
+    # the first ended and published its blocks (warm: only the ids after the last whole cached
+    # block are evaluated). Wall clock from the call to the logits on the host side of a
+    # synchronize; median over three prompts.
+    cold, warm, reused = [], [], []
+    for k in range(3):
+        p_ids = synth.token_ids(wl.ids_seed + 100 + k, PREFIX_PROMPT)
+        for bucket in (cold, warm):
+            ps = g.Session(m, synth.blocks_for(PREFIX_PROMPT) * 32, pooled=True)
+            torch.cuda.synchronize()
+            t_a = time.perf_counter()
+            ps.prefill(p_ids, lg, am, stream)
+            torch.cuda.synchronize()
+            bucket.append((time.perf_counter() - t_a) * 1e3)
+            if bucket is warm:
+                reused.append(ps.reused)
+            ps.close()
+    cold_ms, warm_ms = sorted(cold)[1], sorted(warm)[1]
+
     rev, dirty = git_rev()
     out = {
         "metric": METRIC,
@@ -327,6 +350,8 @@ def main():
                                         "bytes_per_launch": lm_bytes,
                                         "achieved_gbs": round(lm_bytes / (lm_ms * 1e-3) / 1e9, 1),
                                         "frac_hbm_peak": round(lm_bytes / (lm_ms * 1e-3) / PEAK_HBM, 4)}},
+        "prefix_reuse": {"prompt": PREFIX_PROMPT, "reused_positions": reused[1], "ttft_cold_ms": round(cold_ms, 3),
+                         "ttft_warm_ms": round(warm_ms, 3), "speedup": round(cold_ms / warm_ms, 1)},
         "commit": rev, "dirty": dirty, "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:

@@ -301,6 +301,35 @@ hipError_t launch_score(const float* logits, int V, const int32_t* targets, int 
   return hipGetLastError();
 }
 
+// SwiGLU of prefill rows from the split-K partials of the fused gate|up matvec, whose output
+// interleaves 16 gate and 16 up rows: m[t][f] = silu(g) * u, g and u summed over the splits in
+// order, stored as FP16 hi/lo. grid (ceil(F / 256), rows).
+__global__ __launch_bounds__(256) void swiglu_rows_kernel(const float* __restrict__ gu, int nsplit, int64_t stride,
+                                                          int ldgu, int F, f16* __restrict__ mh,
+                                                          f16* __restrict__ ml, int ldm) {
+  const int t = blockIdx.y, f = blockIdx.x * 256 + threadIdx.x;
+  if (f >= F) return;
+  const int64_t rg = (int64_t)t * ldgu + 32 * (f / 16) + (f % 16);
+  float g = 0.f, u = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    g += gu[s * stride + rg];
+    u += gu[s * stride + rg + 16];
+  }
+  const float m = __fmul_rn(__fdiv_rn(g, 1.0f + expf(-g)), u);
+  f16 h, l;
+  split_f16(m, h, l);
+  mh[(int64_t)t * ldm + f] = h;
+  ml[(int64_t)t * ldm + f] = l;
+}
+
+hipError_t launch_swiglu_rows(const float* gu, int nsplit, int64_t stride, int ldgu, int F, int rows, f16* mh, f16* ml,
+                              int ldm, hipStream_t st) {
+  if (rows < 1 || nsplit < 1 || F % 16 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(swiglu_rows_kernel, dim3((F + 255) / 256, rows), dim3(256), 0, st, gu, nsplit, stride, ldgu, F,
+                     mh, ml, ldm);
+  return hipGetLastError();
+}
+
 // Entries of a pooled session's block table. The values travel as kernel arguments, so they are
 // fixed at launch and stream-ordered with the evaluation that reads them.
 __global__ __launch_bounds__(64) void table_write_kernel(int32_t* __restrict__ table, TableWrites t) {

@@ -479,11 +479,12 @@ __global__ __launch_bounds__(256) void rows_kernel(XSrc xs, int klen, f16* __res
 // over global FP16 hi/lo rows.
 // cand (optional, nsplit == 1): per token row b and 16-row tile t, the tile's (max value, index
 // as float bits) at cand[b * (N / 16) + t], for a following argmax reduction.
+// staged: use the LDS-staged kernel for any B (X_RAW rows only).
 hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const XSrc& xs, int B,
-                       int nsplit, float* P, int64_t part_stride, int ldp, float2* cand, hipStream_t st) {
+                       int nsplit, float* P, int64_t part_stride, int ldp, float2* cand, hipStream_t st, bool staged) {
   if (B < 1 || B > kMaxBatch || nsplit < 1 || K % (32 * nsplit) != 0 || N % 16 != 0) return hipErrorInvalidValue;
   if (cand && nsplit != 1) return hipErrorInvalidValue;
-  const bool lds = B <= kXldsMaxRows;
+  const bool lds = B <= kXldsMaxRows && !staged;
   if (!lds && xs.mode != X_RAW) return hipErrorInvalidValue;
   if (xs.mode == X_RESID && (xs.nsplit > 8 || xs.H != K)) return hipErrorInvalidValue;
   dim3 grid((N / 16 + kGemvWaves - 1) / kGemvWaves, nsplit);

@@ -38,12 +38,15 @@ hipError_t launch_qk_rope_kv(bool decode, const float* qkv, int nsplit, int part
 hipError_t launch_argmax(const float2* cand, int ntiles, int B, int32_t* out, hipStream_t st);
 hipError_t launch_score(const float* logits, int V, const int32_t* targets, int B, float* out, hipStream_t st);
 hipError_t launch_table_writes(int32_t* table, const TableWrites& t, hipStream_t st);
+hipError_t launch_swiglu_rows(const float* gu, int nsplit, int64_t stride, int ldgu, int F, int rows, f16* mh, f16* ml,
+                              int ldm, hipStream_t st);
 hipError_t launch_prefill_copy(const uint16_t* src, f16* dst, int64_t rows, int64_t cols, hipStream_t st);
 hipError_t launch_gemm(int epi, bool split, const f16* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
                        const f16* Xlo, int ldx, int T, float* C, int ldc, float out_scale, f16* Mhi, f16* Mlo,
                        int ldm, float m_scale, int ksplit, int64_t split_stride, hipStream_t st);
 hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const XSrc& xs, int B,
-                       int nsplit, float* P, int64_t part_stride, int ldp, float2* cand, hipStream_t st);
+                       int nsplit, float* P, int64_t part_stride, int ldp, float2* cand, hipStream_t st,
+                       bool staged = false);
 hipError_t launch_rows(const XSrc& xs, int K, int nsplit, int B, f16* yhi, f16* ylo, int ldy, hipStream_t st);
 bool gemv_full_fits(int K, int B);
 hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStream_t st);
@@ -802,7 +805,8 @@ constexpr int kProfNever = -1;   // a ProfScope class no recording selects
 // Prefill rounds over n ids already in device memory (ids_dev); see gqa_session_eval_prefill.
 // Per layer: q|k|v GEMM, q/k norm + RoPE + KV write, attention, o GEMM (K-range partials),
 // residual add of the partials + RMSNorm, gate|up GEMM with SwiGLU, down GEMM (partials), and
-// the next layer's residual add + RMSNorm. The logits need only the last row of the last layer:
+// the next layer's residual add + RMSNorm. Rounds of at most 32 rows run the projections as
+// matvecs (gate|up then a SwiGLU pass over its partials). The logits need only the last row of the last layer:
 // after writing that layer's K/V, its attention, o and MLP run for the last row alone (and are
 // skipped in rounds before the last).
 // What a prefill call returns: the last row's logits (and argmax), every row's, or the
@@ -817,19 +821,41 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
   const float eps = d.rms_eps;
   Rows none{};
   const bool split = d.prefill_operands == GQA_PREFILL_SPLIT;
+  // Projection of `rows` operand rows (FP16 hi/lo, row stride ldx) for a round of at most 32
+  // rows: the LDS-staged matvec over the decode weights with the decode K ranges, partials
+  // P[range][row][N] (range stride rows * N) summed in range order by the consumer. A 128-row
+  // GEMM tile would leave most of the chip idle and stream each weight tile on few CUs.
+  auto matvec = [&](const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* xh, const f16* xl,
+                    int ldx, int rows, int nsplit, float* P) -> int {
+    XSrc raw{};
+    raw.mode = X_RAW;
+    raw.hi = xh;
+    raw.lo = xl;
+    raw.ld = ldx;
+    LAUNCH(launch_gemv(W, Wq, Wd, K, N, raw, rows, nsplit, P, (int64_t)rows * N, N, nullptr, st, true));
+    return GQA_OK;
+  };
   for (int off = 0; off < n; off += m->R) {
     const int T = std::min(m->R, n - off);
     const int pos0 = s->pos + off;
     const bool final_round = off + T == n;
+    const bool mv = T <= kMaxBatch;   // matvec projections for this round
     LAUNCH(launch_embed(m->embed, ids_dev + off, T, H, d.vocab, m->x, m->err, st));
     LAUNCH(launch_rmsnorm(m->x, H, nullptr, 0, 0, 0, 1.f, m->L[0].attn_norm, H, eps, 1.f, m->xh, m->xl, H, T, st));
     for (int l = 0; l < d.n_layers; ++l) {
       const LayerW& w = m->L[l];
       const bool last = l + 1 == d.n_layers;
-      LAUNCH(launch_gemm(EPI_STORE, split, w.pqkv, w.qqkv, w.sqkv, H, QKV, m->xh, m->xl, H, T, m->qkv, QKV, 1.f, nullptr,
-                         nullptr, 0, 1.f, 1, 0, st));
-      LAUNCH(launch_qk_rope_kv(false, m->qkv, 0, 0, QKV, NQ, w.q_norm, w.k_norm, eps, m->rcos, m->rsin, pos0,
-                               s->d_table, none, w.kpool, w.vpool, m->q, T, st));
+      if (mv) {
+        int rc = matvec(w.wqkv, w.qqkv, w.sqkv, H, QKV, m->xh, m->xl, H, T, m->s_qkv, m->part);
+        if (rc) return rc;
+        LAUNCH(launch_qk_rope_kv(false, m->part, m->s_qkv, T * QKV, QKV, NQ, w.q_norm, w.k_norm, eps, m->rcos,
+                                 m->rsin, pos0, s->d_table, none, w.kpool, w.vpool, m->q, T, st));
+      } else {
+        LAUNCH(launch_gemm(EPI_STORE, split, w.pqkv, w.qqkv, w.sqkv, H, QKV, m->xh, m->xl, H, T, m->qkv, QKV, 1.f,
+                           nullptr, nullptr, 0, 1.f, 1, 0, st));
+        LAUNCH(launch_qk_rope_kv(false, m->qkv, 0, 0, QKV, NQ, w.q_norm, w.k_norm, eps, m->rcos, m->rsin, pos0,
+                                 s->d_table, none, w.kpool, w.vpool, m->q, T, st));
+      }
       const bool one = last && out == kOutLast;                // only the final row feeds the logits
       if (one && !final_round) break;
       const int rows = one ? 1 : T, r0 = one ? T - 1 : 0;
@@ -838,22 +864,39 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
         LAUNCH(launch_attn_prefill(m->q + (int64_t)r0 * QD, NQ, rows, pos0 + r0, s->d_table, w.kpool, w.vpool,
                                    kAttnOutScale, m->oh, m->ol, QD, st));
       }
-      const int so = prefill_ksplit(m, H, QD, rows);
-      LAUNCH(launch_gemm(EPI_STORE, split, w.po, w.qo, w.so, QD, H, m->oh, m->ol, QD, rows, m->ppart, H, 1.f, nullptr,
-                         nullptr, 0, 1.f, so, (int64_t)rows * H, st));
-      LAUNCH(launch_rmsnorm(m->x + (int64_t)r0 * H, H, m->ppart, so, rows * H, H, 1.f / kAttnOutScale, w.ffn_norm, H,
-                            eps, 1.f, m->xh, m->xl, H, rows, st));
-      {
-        ProfScope ps(m, last ? kProfNever : GQA_PROF_PREFILL_GATEUP, st);
-        LAUNCH(launch_gemm(EPI_SWIGLU, split, w.pgu, w.qgu, w.sgu, H, 2 * F, m->xh, m->xl, H, rows, nullptr, 0, 1.f,
-                           m->mh, m->ml, F, 1.f, 1, 0, st));
+      float* pp = mv ? m->part2 : m->ppart;     // o and down partials
+      int so = 0, sd = 0;
+      if (mv) {
+        so = m->s_o;
+        int rc = matvec(w.wo, w.qo, w.so, QD, H, m->oh, m->ol, QD, rows, so, pp);
+        if (rc) return rc;
+      } else {
+        so = prefill_ksplit(m, H, QD, rows);
+        LAUNCH(launch_gemm(EPI_STORE, split, w.po, w.qo, w.so, QD, H, m->oh, m->ol, QD, rows, pp, H, 1.f, nullptr,
+                           nullptr, 0, 1.f, so, (int64_t)rows * H, st));
       }
-      const int sd = prefill_ksplit(m, H, F, rows);
-      LAUNCH(launch_gemm(EPI_STORE, split, w.pd, w.qd, w.sd, F, H, m->mh, m->ml, F, rows, m->ppart, H, 1.f, nullptr,
-                         nullptr, 0, 1.f, sd, (int64_t)rows * H, st));
+      LAUNCH(launch_rmsnorm(m->x + (int64_t)r0 * H, H, pp, so, rows * H, H, 1.f / kAttnOutScale, w.ffn_norm, H, eps,
+                            1.f, m->xh, m->xl, H, rows, st));
+      if (mv) {
+        int rc = matvec(w.wgu, w.qgu, w.sgu, H, 2 * F, m->xh, m->xl, H, rows, m->s_gu, m->part);
+        if (rc) return rc;
+        LAUNCH(launch_swiglu_rows(m->part, m->s_gu, (int64_t)rows * 2 * F, 2 * F, F, rows, m->mh, m->ml, F, st));
+        sd = m->s_d;
+        rc = matvec(w.wd, w.qd, w.sd, F, H, m->mh, m->ml, F, rows, sd, pp);
+        if (rc) return rc;
+      } else {
+        {
+          ProfScope ps(m, last ? kProfNever : GQA_PROF_PREFILL_GATEUP, st);
+          LAUNCH(launch_gemm(EPI_SWIGLU, split, w.pgu, w.qgu, w.sgu, H, 2 * F, m->xh, m->xl, H, rows, nullptr, 0, 1.f,
+                             m->mh, m->ml, F, 1.f, 1, 0, st));
+        }
+        sd = prefill_ksplit(m, H, F, rows);
+        LAUNCH(launch_gemm(EPI_STORE, split, w.pd, w.qd, w.sd, F, H, m->mh, m->ml, F, rows, pp, H, 1.f, nullptr,
+                           nullptr, 0, 1.f, sd, (int64_t)rows * H, st));
+      }
       const uint16_t* next_norm = last ? m->final_norm : m->L[l + 1].attn_norm;
-      LAUNCH(launch_rmsnorm(m->x + (int64_t)r0 * H, H, m->ppart, sd, rows * H, H, 1.f, next_norm, H, eps, 1.f, m->xh,
-                            m->xl, H, rows, st));
+      LAUNCH(launch_rmsnorm(m->x + (int64_t)r0 * H, H, pp, sd, rows * H, H, 1.f, next_norm, H, eps, 1.f, m->xh, m->xl,
+                            H, rows, st));
       if (last) {
         // lm_head over the rows, up to 32 at a time (the batched decode matvec)
         for (int g0 = 0; g0 < rows; g0 += kMaxBatch) {
