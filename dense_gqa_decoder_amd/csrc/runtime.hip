@@ -1233,9 +1233,11 @@ int gqa_debug_read_kv(gqa_session* s, int32_t layer, int32_t pos0, int32_t n, ui
   if (pos0 < 0 || n < 1 || pos0 + n > s->max_pos) return fail(GQA_E_INVALID, "positions out of range");
   HIP_TRY(hipDeviceSynchronize());
   const LayerW& w = m->L[layer];
+  const std::vector<int32_t>& table = s->seq ? s->seq->blocks : s->blocks;
   for (int i = 0; i < n; ++i) {
     int p = pos0 + i;
-    int phys = s->blocks[p / kBlock];
+    int phys = table[p / kBlock];
+    if (phys < 0) return fail(GQA_E_INVALID, "position %d is in no block of the session", p);
     for (int h = 0; h < kKvHeads; ++h) {
       int64_t off = (((int64_t)phys * kKvHeads + h) * kBlock + (p % kBlock)) * kHeadDim;
       HIP_TRY(hipMemcpy(k + ((int64_t)i * kKvHeads + h) * kHeadDim, w.kpool + off, kHeadDim * 2, hipMemcpyDeviceToHost));

@@ -270,7 +270,8 @@ int gqa_debug_read_q8(gqa_model* model, int32_t kind, int32_t layer, int32_t row
                       uint16_t* scales);
 
 /* Copy the BF16 bits of K and V of `layer` for logical positions [pos0, pos0+n) of a session,
- * read through its block table, into host arrays of n x 8 x 128 uint16 each. */
+ * read through its block table, into host arrays of n x 8 x 128 uint16 each. GQA_E_INVALID for
+ * a position whose block a pooled session has not mapped. */
 int gqa_debug_read_kv(gqa_session* session, int32_t layer, int32_t pos0, int32_t n, uint16_t* k, uint16_t* v);
 
 /* Activation scratch buffers of the model (contents are those left by the last call; layouts
