@@ -22,6 +22,8 @@ Sources, cited by page title and section:
 * Kipp Model Support, "Quantization (Q8_0)": seven per-layer projections in
   32-weight blocks of an fp16 scale and int8 quants; embedding, lm_head and
   norms stay BF16.
+* Kipp Model Support, "Quantization (AFFINE4_GS32)": 32-weight groups of 4-bit
+  codes with an fp16 scale and an fp16 bias (5.0 bits per weight), w = scale*q + bias.
 * Kipp Reproducing, "Mutation gate": four KV addressing faults (read-block,
   read-slot, rollover, K/V swap), used here as oracle fault modes.
 * Kipp Roadmap, status v0.0.2 and v0.0.3: logits of several positions from one
@@ -37,3 +39,4 @@ agreement with trained Qwen3 checkpoints is parity unpinned (no trained weights)
 """
 from .model import OracleModel, OracleSession, ContiguousKV, PagedKV, nmse, next_token_log_probs  # noqa: F401
 from .q8_0 import quantize_q8_0, dequantize_q8_0  # noqa: F401
+from .affine4 import quantize_affine4, dequantize_affine4  # noqa: F401

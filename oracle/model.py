@@ -170,7 +170,7 @@ class OracleModel:
     PROJ = ("q", "k", "v", "o", "gate", "up", "down")
 
     def __init__(self, shape: synth.ModelShape, seed: int, scheme: str = "bf16", cache: bool = True):
-        if scheme not in ("bf16", "q8_0"):
+        if scheme not in ("bf16", "q8_0", "affine4"):
             raise ValueError(scheme)
         self.shape, self.seed, self.scheme, self.cache = shape, seed, scheme, cache
         self._layers = {}
@@ -180,11 +180,14 @@ class OracleModel:
 
     def _make_layer(self, l):
         from .q8_0 import quantize_q8_0, dequantize_q8_0
+        from .affine4 import quantize_affine4, dequantize_affine4
         out = {}
         for nm in synth.LAYER_TENSORS:
             w = synth.bf16_bits_to_f32(synth.tensor_bits(self.shape, self.seed, nm, l))
             if self.scheme == "q8_0" and nm in self.PROJ:
                 w = dequantize_q8_0(*quantize_q8_0(w))
+            elif self.scheme == "affine4" and nm in self.PROJ:
+                w = dequantize_affine4(*quantize_affine4(w)).astype(np.float32)
             out[nm] = w
         return out
 

@@ -188,6 +188,68 @@ def test_q8_0_error_bound():
     assert np.all(np.abs(q) <= 127)
 
 
+def test_affine4_exact_grid_ties_and_constant_groups():
+    """AFFINE4_GS32 (Kipp Model Support, "Quantization (AFFINE4_GS32)"): values on the group's
+    16-level grid come back exactly; half-way values round away from zero; a constant group has
+    scale 0, codes 0 and the fp16 bias as its value."""
+    from oracle.affine4 import quantize_affine4, dequantize_affine4
+    d, b = 2.0 ** -8, -0.0625
+    g0 = (b + d * np.arange(16)).astype(np.float32)
+    row = np.concatenate([g0, g0[::-1], np.full(32, 0.03125, np.float32), np.zeros(32, np.float32)])
+    row[64 + 1] = 0.0                                   # group 2: min 0, max 2^-5 -> d = 2^-5 / 15
+    grid = np.concatenate([g0, g0]).astype(np.float32)
+    grid[5] = np.float32(b + 2.5 * d)                   # tie: (v - bias) / scale = 2.5 -> 3
+    grid[6] = np.float32(b + 0.49 * d)                  # -> 0
+    scale, bias, q = quantize_affine4(grid[None, :])
+    assert scale.dtype == np.float16 and float(scale[0, 0]) == d and float(bias[0, 0]) == b
+    assert q[0, 5] == 3 and q[0, 6] == 0
+    want = list(range(16)) * 2
+    want[5], want[6] = 3, 0
+    assert list(q[0]) == want
+    deq = dequantize_affine4(scale, bias, q)[0]
+    exact = [i for i in range(32) if i not in (5, 6)]
+    assert np.array_equal(deq[exact], grid[exact].astype(np.float64))
+    c = np.full((1, 32), 0.1, np.float32)               # constant group
+    cs, cb, cq = quantize_affine4(c)
+    assert float(cs[0, 0]) == 0.0 and not cq.any()
+    assert dequantize_affine4(cs, cb, cq)[0, 0] == float(np.float16(np.float32(0.1)))
+    rs, rb, rq = quantize_affine4(row[None, :])
+    assert rq.max() <= 15 and np.array_equal(dequantize_affine4(rs, rb, rq)[0, :32], row[:32].astype(np.float64))
+
+
+def test_affine4_error_bound():
+    """Per group: |w - dequantised| <= scale/2 (code rounding) + 15 |scale - d| + |bias - min|
+    (the fp16 roundings of the FP32 scale and minimum), and every code is in 0..15."""
+    from oracle.affine4 import quantize_affine4, dequantize_affine4
+    w = synth.bf16_bits_to_f32(synth.weight_bits(12, (64, 256)))
+    scale, bias, q = quantize_affine4(w)
+    deq = dequantize_affine4(scale, bias, q)
+    g = w.reshape(64, 8, 32).astype(np.float64)
+    mn, mx = g.min(axis=2), g.max(axis=2)
+    d = (mx - mn) / 15
+    s64, b64 = scale.astype(np.float64), bias.astype(np.float64)
+    bound = s64 / 2 + 15 * np.abs(s64 - d) + np.abs(b64 - mn)
+    err = np.abs(deq - w).reshape(64, 8, 32).max(axis=2)
+    assert np.all(err <= bound * (1 + 1e-6) + 1e-12)
+    assert q.max() <= 15 and np.all(scale.astype(np.float64) > 0)
+    assert np.array_equal(deq.astype(np.float32).astype(np.float64), deq)   # the FP32 copy is exact
+
+
+def test_affine4_size_matches_published_ratio():
+    """Kipp Model Support, "Quantization (AFFINE4_GS32)": 5.0 bits per weight (16 bytes of codes +
+    fp16 scale + fp16 bias per 32 weights); Kipp Roadmap, "Delivered since": about 2.6x smaller
+    than BF16 -- the 4B shape with its seven projections in AFFINE4 and the tied embedding and
+    norms in BF16 gives that ratio."""
+    assert (16 + 2 + 2) * 8 / 32 == 5.0
+    sh = synth.SHAPES["qwen3-4b-shape"]
+    proj = sum(int(np.prod(s)) for nm, s in sh.layer_tensor_shapes().items() if nm in oracle.OracleModel.PROJ)
+    norms = sum(int(np.prod(s)) for nm, s in sh.layer_tensor_shapes().items() if nm not in oracle.OracleModel.PROJ)
+    emb = sh.vocab * sh.hidden * (1 if sh.tied else 2)
+    bf16 = 2 * (sh.n_layers * (proj + norms) + emb + sh.hidden)
+    a4 = sh.n_layers * (proj * 20 // 32 + 2 * norms) + 2 * (emb + sh.hidden)
+    assert 2.55 <= bf16 / a4 <= 2.7
+
+
 def test_parameter_inventory_matches_published_sizes():
     g = json.load(open(os.path.join(GOLDEN, "artifact_sizes.json")))
     sh = synth.SHAPES[g["shape"]]
