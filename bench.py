@@ -28,7 +28,11 @@ METRIC = "prefill tok/s @2048 + decode tok/s, Qwen3-4B-shape BF16, 1 MI355X (% r
 PREFIX_PROMPT = 6890        # repeated-prompt length of the prefix-reuse measurement (Kipp Roadmap, status v0.0.3)
 
 
-def algorithmic(shape, prompt, decode):
+# bytes per projection weight: BF16; Q8_0 (34-byte blocks of 32); AFFINE4_GS32 (20-byte groups of 32)
+WEIGHT_BYTES = {"bf16": 2.0, "q8_0": 34 / 32, "affine4": 20 / 32}
+
+
+def algorithmic(shape, prompt, decode, scheme="bf16"):
     """Algorithmic FLOP of the prefill and bytes per decode token (weights + KV, no scratch).
     The prefill's output is the last position's logits plus the K/V of every position, so the
     last layer needs q|k|v for every row but attention, o and the MLP for the last row only."""
@@ -39,7 +43,7 @@ def algorithmic(shape, prompt, decode):
     attn = shape.n_q_heads * 4 * 128
     flops = (2 * (L - 1) * P * prompt + attn * (L - 1) * prompt * (prompt + 1) // 2
              + 2 * P_qkv * prompt + 2 * (P - P_qkv) + attn * prompt + 2 * V * H)
-    w_bytes = 2 * (L * P + V * H + (2 * L + 1) * H + 2 * L * 128) + 2 * H
+    w_bytes = int(WEIGHT_BYTES[scheme] * L * P) + 2 * (V * H + (2 * L + 1) * H + 2 * L * 128) + 2 * H
     kv_pos = 2 * L * KVD * 2                                            # K and V bytes per cached position
     ctx_mean = prompt + (decode + 1) / 2.0
     dec_bytes = w_bytes + kv_pos * ctx_mean + kv_pos
@@ -55,7 +59,7 @@ def cpu_baseline(wl, n_prompt, n_decode):
     import synth
     from oracle import model as om
     cores = len(os.sched_getaffinity(0))
-    m = oracle.OracleModel(wl.shape, wl.weight_seed)
+    m = oracle.OracleModel(wl.shape, wl.weight_seed, wl.scheme)
     for l in range(wl.shape.n_layers):
         m.layer(l)
     ids = synth.token_ids(wl.ids_seed, n_prompt)
@@ -68,7 +72,7 @@ def cpu_baseline(wl, n_prompt, n_decode):
     t2 = time.perf_counter()
     return {"value": round((n_prompt + n_decode) / (t2 - t0), 3), "unit": "tok/s", "cores": cores, "kind": "oracle",
             "prefill_tok_s": round(n_prompt / (t1 - t0), 3), "decode_tok_s": round(n_decode / (t2 - t1), 3),
-            "sample": f"{wl.shape.name} BF16 oracle (NumPy FP32, OpenBLAS on {cores} cores): {n_prompt}-token prompt "
+            "sample": f"{wl.shape.name} {wl.scheme} oracle (NumPy FP32, OpenBLAS on {cores} cores): {n_prompt}-token prompt "
                       f"+ {n_decode} greedy decode steps, weight generation untimed"}
 
 
@@ -161,7 +165,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="4b", choices=["4b", "0.6b", "tiny"])
+    ap.add_argument("--workload", default="4b", choices=["4b", "0.6b", "tiny", "4b-q8", "4b-a4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prompt", type=int, default=2048, help="oracle baseline: prompt tokens")
     ap.add_argument("--cpu-decode", type=int, default=64, help="oracle baseline: decode steps")
@@ -235,7 +239,7 @@ def main():
     pre_ms = sorted(e[0].elapsed_time(e[1]) for e in events)[args.steps // 2]
     dec_ms = sorted(e[1].elapsed_time(e[2]) for e in events)[args.steps // 2]
     tokens = wl.prompt + wl.decode
-    flops, dec_bytes, w_bytes = algorithmic(shape, wl.prompt, wl.decode)
+    flops, dec_bytes, w_bytes = algorithmic(shape, wl.prompt, wl.decode, wl.scheme)
 
     # dominant kernel (decode gate/up matvec): HIP events around each of its launches in one
     # more step identical to the timed ones
@@ -247,7 +251,7 @@ def main():
         m.profile("none")
         kernels[cls] = (n, tot_ms / max(n, 1))
     H, F = shape.hidden, shape.ffn
-    gu_bytes = 2 * F * H * 2 + H * 4 + F * 4                     # weights + x hi/lo + m hi/lo, one row
+    gu_bytes = int(2 * F * H * WEIGHT_BYTES[wl.scheme]) + H * 4 + F * 4   # weights + x hi/lo + m hi/lo, one row
     gu_ms = kernels["decode_gateup"][1]
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
     pgu_flop = 2.0 * wl.prompt * 2 * F * H
@@ -317,7 +321,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": {"bf16": "bf16", "q8_0": "q8_0 weights (fp16 MFMA, fp32 accumulate)",
+                  "affine4": "affine4 weights (fp16 MFMA, fp32 accumulate)"}[wl.scheme],
         "data": "synthetic (seeded random-init weights ~N(0,0.02), uniform random token ids)",
         "config": {"workload": f"{shape.name} {wl.scheme}: {wl.prompt}-token prefill + {wl.decode} greedy decode "
                                f"steps, paged KV (shuffled 32-position blocks)",
@@ -334,7 +339,7 @@ def main():
         "roofline": {"kernel": "gemv_full_kernel<XF_NORM, EPI_SWIGLU>: decode gate/up matvec with fused "
                                "RMSNorm prologue and SwiGLU epilogue",
                      "bound": "hbm", "achieved": round(gu_gbs, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                     "frac": round(gu_gbs * 1e9 / PEAK_HBM, 4), "traffic": measured_traffic(),
+                     "frac": round(gu_gbs * 1e9 / PEAK_HBM, 4), "traffic": measured_traffic() if args.workload == "4b" else None,
                      "launch_us": round(gu_ms * 1e3, 2), "bytes_per_launch": gu_bytes,
                      "launches": kernels["decode_gateup"][0]},
         "prefill_roofline": {"kernel": "gemm_kernel<EPI_SWIGLU> prefill gate/up GEMM with SwiGLU",

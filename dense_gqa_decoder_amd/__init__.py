@@ -13,7 +13,7 @@ import os
 
 from ._lib import (  # noqa: F401
     GQA_OK, GQA_E_INVALID, GQA_E_OOM, GQA_E_DEVICE, GQA_E_HIP, GQA_E_RANGE,
-    GQA_SCHEME_BF16, GQA_SCHEME_Q8_0, GQA_BLOCK_POSITIONS, GQA_MAX_BATCH,
+    GQA_SCHEME_BF16, GQA_SCHEME_Q8_0, GQA_SCHEME_AFFINE4, GQA_BLOCK_POSITIONS, GQA_MAX_BATCH,
     GQA_T, GqaError, ModelDesc, ModelInfo, lib, lib_path, load,
     gqa_model_create, gqa_model_destroy, gqa_model_get_info, gqa_session_create, gqa_session_destroy,
     gqa_session_reset, gqa_session_position, gqa_session_eval_prefill, gqa_session_eval_decode,
@@ -21,6 +21,6 @@ from ._lib import (  # noqa: F401
     gqa_session_create_pooled, gqa_session_publish, gqa_session_reused,
     gqa_model_check_device_error, gqa_model_profile, gqa_model_profile_read, GQA_PROF,
     gqa_last_error, gqa_debug_read_weight,
-    gqa_debug_read_q8, gqa_debug_read_kv, gqa_debug_read_rope,
+    gqa_debug_read_q8, gqa_debug_read_affine4, gqa_debug_read_kv, gqa_debug_read_rope,
 )
 from .api import Model, Session  # noqa: F401

@@ -15,6 +15,8 @@ GQA_E_HIP = -4
 GQA_E_RANGE = -5
 GQA_SCHEME_BF16 = 0
 GQA_SCHEME_Q8_0 = 1
+GQA_SCHEME_AFFINE4 = 2
+SCHEMES = {"bf16": GQA_SCHEME_BF16, "q8_0": GQA_SCHEME_Q8_0, "affine4": GQA_SCHEME_AFFINE4}
 GQA_MAX_BATCH = 32
 GQA_BLOCK_POSITIONS = 32
 GQA_T = {"embed": 0, "attn_norm": 1, "q": 2, "k": 3, "v": 4, "q_norm": 5, "k_norm": 6, "o": 7, "ffn_norm": 8,
@@ -72,6 +74,7 @@ _SIGS = {
     "gqa_last_error": (ctypes.c_char_p, []),
     "gqa_debug_read_weight": (I32, [P, I32, I32, I32, I32, P]),
     "gqa_debug_read_q8": (I32, [P, I32, I32, I32, I32, P, P]),
+    "gqa_debug_read_affine4": (I32, [P, I32, I32, I32, I32, P, P, P]),
     "gqa_debug_read_kv": (I32, [P, I32, I32, I32, P, P]),
     "gqa_debug_read_rope": (I32, [P, I32, P, P]),
     "gqa_debug_read_scratch": (I32, [P, I32, ctypes.c_int64, ctypes.c_int64, P]),
@@ -207,6 +210,10 @@ def gqa_model_profile_read(model):
 
 def gqa_debug_read_weight(model, kind, layer, row0, rows, dst_ptr) -> None:
     _check(lib().gqa_debug_read_weight(model, kind, layer, row0, rows, dst_ptr))
+
+
+def gqa_debug_read_affine4(model, kind, layer, row0, rows, q_ptr, s_ptr, b_ptr) -> None:
+    _check(lib().gqa_debug_read_affine4(model, kind, layer, row0, rows, q_ptr, s_ptr, b_ptr))
 
 
 def gqa_debug_read_q8(model, kind, layer, row0, rows, q_ptr, s_ptr) -> None:

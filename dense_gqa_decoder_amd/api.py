@@ -40,7 +40,7 @@ class Model:
     def __init__(self, *, n_layers, hidden, n_q_heads, ffn, vocab=151936, tied=True, rope_theta=1e6, rms_eps=1e-6,
                  scheme="bf16", kv_pool_blocks, max_positions, max_round_tokens=0, seed=0, prefill="split"):
         self.desc = L.ModelDesc(n_layers, hidden, n_q_heads, 8, 128, ffn, vocab, 1 if tied else 0, rope_theta,
-                                rms_eps, L.GQA_SCHEME_Q8_0 if scheme == "q8_0" else L.GQA_SCHEME_BF16,
+                                rms_eps, L.SCHEMES[scheme],
                                 kv_pool_blocks, max_positions, max_round_tokens,
                                 {"split": 0, "fp16": 1}[prefill])
         self.vocab, self.hidden, self.n_layers = vocab, hidden, n_layers
@@ -77,6 +77,14 @@ class Model:
         s = np.empty((rows, cols // 32), dtype=np.uint16)
         L.gqa_debug_read_q8(self.handle, L.GQA_T[kind], layer, row0, rows, q.ctypes.data, s.ctypes.data)
         return q, s
+
+    def read_affine4(self, kind, layer, row0, rows, cols):
+        q = np.empty((rows, cols), dtype=np.uint8)
+        s = np.empty((rows, cols // 32), dtype=np.uint16)
+        b = np.empty((rows, cols // 32), dtype=np.uint16)
+        L.gqa_debug_read_affine4(self.handle, L.GQA_T[kind], layer, row0, rows, q.ctypes.data, s.ctypes.data,
+                                 b.ctypes.data)
+        return q, s, b
 
     SCRATCH = {"resid_a": (0, np.float32), "resid_b": (1, np.float32), "part_a": (2, np.float32),
                "part_b": (3, np.float32), "attn_hi": (4, np.float16), "attn_lo": (5, np.float16),

@@ -94,8 +94,9 @@ enum FullMode : int { XF_RAW = 0, XF_NORM = 1 };
 // Arguments of the whole-K decode matvec (k_gemv_full.hip).
 struct FullArgs {
   const uint16_t* W;
-  const int8_t* Wq;
-  const f16* Wd;
+  const int8_t* Wq;        // Q8_0 quants, or AFFINE4 packed codes when Wb is set
+  const f16* Wd;           // Q8_0 / AFFINE4 scales
+  const f16* Wb;           // AFFINE4 biases (null otherwise)
   int K, N, B;
   const f16* xhi;          // XF_RAW: [B][ldx]
   const f16* xlo;
@@ -234,6 +235,33 @@ __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)
 
 // Eight int8 quants (two dwords) -> eight exact FP16 values: the byte q + 128 (q ^ 0x80) below the
 // FP16 pattern 0x64 is the value 1152 + q, and subtracting 1152 is exact.
+// Weight formats of the matvec kernels.
+enum WeightMode : int { WM_BF16 = 0, WM_Q8 = 1, WM_A4 = 2 };
+
+// AFFINE4 codes of one operand lane, 8 K-elements of one weight row in a 32-bit word: nibble j
+// holds element 2 j and nibble j + 4 element 2 j + 1 (j = 0..3), so (w >> 4 j) & 0x000F000F puts
+// a pair under the FP16 exponent bits 0x6400 (the value 1024 + q) and one packed subtraction of
+// 1024 leaves the exact codes.
+__device__ __forceinline__ f16x8 u4x8_to_f16x8(uint32_t w) {
+  const f16x2 base = {(f16)1024.0f, (f16)1024.0f};
+  f16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f16x2 q = __builtin_bit_cast(f16x2, ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u) - base;
+    r[2 * j] = q[0];
+    r[2 * j + 1] = q[1];
+  }
+  return r;
+}
+
+// Four fp16 values (two 32-bit words) as FP32.
+__device__ __forceinline__ void f16x4_bits_to_f32(uint2 v, float (&o)[4]) {
+  o[0] = (float)__builtin_bit_cast(f16, (uint16_t)(v.x & 0xFFFF));
+  o[1] = (float)__builtin_bit_cast(f16, (uint16_t)(v.x >> 16));
+  o[2] = (float)__builtin_bit_cast(f16, (uint16_t)(v.y & 0xFFFF));
+  o[3] = (float)__builtin_bit_cast(f16, (uint16_t)(v.y >> 16));
+}
+
 __device__ __forceinline__ f16x8 i8x8_to_f16x8(uint2 v) {
   const uint32_t x0 = v.x ^ 0x80808080u, x1 = v.y ^ 0x80808080u;
   const uint32_t h[4] = {__builtin_amdgcn_perm(0x64646464u, x0, 0x05010400u),
@@ -253,6 +281,23 @@ __device__ __forceinline__ f16x8 i8x8_to_f16x8(uint2 v) {
 
 __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// One 32-wide K-step of an AFFINE4 band against one token column's operand (hi, lo): the
+// codes' products and the operand's sum over the step (an all-ones A operand) on the matrix
+// cores, then per weight row acc += scale * sum(q x) + bias * sum(x). Every matvec path uses
+// this same sequence, so a row's result does not depend on the path.
+__device__ __forceinline__ void a4_step(f32x4& acc, f16x8 a, f16x8 bh, f16x8 bl, const float (&sc)[4],
+                                        const float (&bs)[4]) {
+  const f16 one = (f16)1.0f;
+  const f16x8 ones = {one, one, one, one, one, one, one, one};
+  f32x4 p = {0.f, 0.f, 0.f, 0.f}, xs = {0.f, 0.f, 0.f, 0.f};
+  p = mfma16(a, bh, p);
+  p = mfma16(a, bl, p);
+  xs = mfma16(ones, bh, xs);
+  xs = mfma16(ones, bl, xs);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc[r], p[r], fmaf(bs[r], xs[r], acc[r]));
 }
 
 // Wave-wide sum / max: DPP within each 16-lane row, then the four row results read as scalars

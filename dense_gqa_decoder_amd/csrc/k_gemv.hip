@@ -122,10 +122,11 @@ __device__ __forceinline__ void build_range(const XSrc& xs, int b, int k0, int k
   }
 }
 
-template <bool Q8, int NT, bool XLDS>
+template <int QM, int NT, bool XLDS>
 __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* __restrict__ W,
                                                                const int8_t* __restrict__ Wq,
-                                                               const f16* __restrict__ Wd, int K, int N, XSrc xs,
+                                                               const f16* __restrict__ Wd,
+                                                               const f16* __restrict__ Wb, int K, int N, XSrc xs,
                                                                int B, int klen, float* __restrict__ P,
                                                                int64_t part_stride, int ldp,
                                                                float2* __restrict__ cand) {
@@ -151,7 +152,9 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* _
   struct Buf {
     uint4 wv[U];
     uint2 qv[U];
+    uint32_t q4[U];
     uint2 sc[U];
+    uint2 bs[U];
   };
   auto fetch = [&](Buf& f, int k) {
 #pragma unroll
@@ -159,9 +162,13 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* _
       const int kk = k + u * 32;
       const bool ok = kk < ke && has_tile;
       const int64_t chunk = band + (kk >> 5);
-      if (Q8) {
+      if (QM == WM_Q8) {
         f.qv[u] = ok ? *(const uint2*)(Wq + chunk * 512 + lane * 8) : uint2{0, 0};
         f.sc[u] = ok ? *(const uint2*)(Wd + chunk * 16 + g4 * 4) : uint2{0, 0};
+      } else if (QM == WM_A4) {
+        f.q4[u] = ok ? *(const uint32_t*)(Wq + chunk * 256 + lane * 4) : 0u;
+        f.sc[u] = ok ? *(const uint2*)(Wd + chunk * 16 + g4 * 4) : uint2{0, 0};
+        f.bs[u] = ok ? *(const uint2*)(Wb + chunk * 16 + g4 * 4) : uint2{0, 0};
       } else {
         f.wv[u] = ok ? *(const uint4*)(W + chunk * 512 + lane * 8) : uint4{0, 0, 0, 0};
       }
@@ -220,13 +227,19 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* _
         bl[j] = (ok && xv[j]) ? *(const f16x8*)(xl[j] + kk) : f16x8{};
       }
       f16x8 a;
-      if (Q8) {
+      if (QM == WM_Q8) {
         a = i8x8_to_f16x8(f.qv[u]);
+      } else if (QM == WM_A4) {
+        a = u4x8_to_f16x8(f.q4[u]);
       } else {
         a = bf16x8_to_f16x8(f.wv[u]);
       }
-      float sc[4] = {0.f, 0.f, 0.f, 0.f};
-      if (Q8) {
+      float sc[4] = {0.f, 0.f, 0.f, 0.f}, bs[4] = {0.f, 0.f, 0.f, 0.f};
+      if (QM == WM_A4) {
+        f16x4_bits_to_f32(f.sc[u], sc);
+        f16x4_bits_to_f32(f.bs[u], bs);
+      }
+      if (QM == WM_Q8) {
         sc[0] = (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x & 0xFFFF));
         sc[1] = (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x >> 16));
         sc[2] = (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y & 0xFFFF));
@@ -234,7 +247,9 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* _
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        if (Q8) {
+        if (QM == WM_A4) {
+          a4_step(acc[j], a, bh[j], bl[j], sc, bs);
+        } else if (QM == WM_Q8) {
           f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
           p = mfma16(a, bh[j], p);
           p = mfma16(a, bl[j], p);
@@ -311,10 +326,11 @@ __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <bool Q8, int NT>
+template <int QM, int NT>
 __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows_kernel(const uint16_t* __restrict__ W,
                                                                    const int8_t* __restrict__ Wq,
-                                                                   const f16* __restrict__ Wd, int K, int N, XSrc xs,
+                                                                   const f16* __restrict__ Wd,
+                                                                   const f16* __restrict__ Wb, int K, int N, XSrc xs,
                                                                    int B, int klen, float* __restrict__ P,
                                                                    int64_t part_stride, int ldp,
                                                                    float2* __restrict__ cand) {
@@ -322,7 +338,7 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows_kernel(const uint16
   constexpr int ROWS = 16 * NT;                       // staged token rows
   constexpr int RPW = ROWS / kRowsWaves;              // staged rows copied per wave
   constexpr int BUF = ROWS * kRowsPitch;              // f16 per buffer
-  constexpr int NF = Q8 ? 2 * U : U;                  // weight loads per stage and wave
+  constexpr int NF = QM == WM_Q8 ? 2 * U : QM == WM_A4 ? 3 * U : U;   // weight loads per stage and wave
   __shared__ __attribute__((aligned(16))) f16 sx[2 * BUF];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -337,16 +353,22 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows_kernel(const uint16
   struct Buf {
     uint4 wv[U];
     uint2 qv[U];
+    uint32_t q4[U];
     uint2 sc[U];
+    uint2 bs[U];
   };
   auto fetch = [&](Buf& f, int t) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kk = min(k0 + t * kRowsStageK + u * 32, ke - 32);
       const int64_t chunk = band + (kk >> 5);
-      if (Q8) {
+      if (QM == WM_Q8) {
         f.qv[u] = *(const uint2*)(Wq + chunk * 512 + lane * 8);
         f.sc[u] = *(const uint2*)(Wd + chunk * 16 + g4 * 4);
+      } else if (QM == WM_A4) {
+        f.q4[u] = *(const uint32_t*)(Wq + chunk * 256 + lane * 4);
+        f.sc[u] = *(const uint2*)(Wd + chunk * 16 + g4 * 4);
+        f.bs[u] = *(const uint2*)(Wb + chunk * 16 + g4 * 4);
       } else {
         f.wv[u] = *(const uint4*)(W + chunk * 512 + lane * 8);
       }
@@ -379,7 +401,14 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows_kernel(const uint16
         bl[j] = *(const f16x8*)(xb + j * 16 * kRowsPitch + kRowsStageK + u * 32);
       }
       f16x8 a;
-      if (Q8) {
+      if (QM == WM_A4) {
+        float sc[4], bs[4];
+        f16x4_bits_to_f32(f.sc[u], sc);
+        f16x4_bits_to_f32(f.bs[u], bs);
+        a = u4x8_to_f16x8(f.q4[u]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) a4_step(acc[j], a, bh[j], bl[j], sc, bs);
+      } else if (QM == WM_Q8) {
         a = i8x8_to_f16x8(f.qv[u]);
         const float sc[4] = {(float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x & 0xFFFF)),
                              (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x >> 16)),
@@ -480,8 +509,9 @@ __global__ __launch_bounds__(256) void rows_kernel(XSrc xs, int klen, f16* __res
 // cand (optional, nsplit == 1): per token row b and 16-row tile t, the tile's (max value, index
 // as float bits) at cand[b * (N / 16) + t], for a following argmax reduction.
 // staged: use the LDS-staged kernel for any B (X_RAW rows only).
-hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const XSrc& xs, int B,
-                       int nsplit, float* P, int64_t part_stride, int ldp, float2* cand, hipStream_t st, bool staged) {
+hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, const f16* Wb, int K, int N, const XSrc& xs,
+                       int B, int nsplit, float* P, int64_t part_stride, int ldp, float2* cand, hipStream_t st,
+                       bool staged) {
   if (B < 1 || B > kMaxBatch || nsplit < 1 || K % (32 * nsplit) != 0 || N % 16 != 0) return hipErrorInvalidValue;
   if (cand && nsplit != 1) return hipErrorInvalidValue;
   const bool lds = B <= kXldsMaxRows && !staged;
@@ -492,22 +522,26 @@ hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, int K
   const size_t shm = lds ? (size_t)B * klen * 4 : 0;
   if (shm > 64 * 1024) return hipErrorInvalidValue;
   const dim3 blk(64 * kGemvWaves);
-#define GEMV_LAUNCH(Q8, NT, L)                                                                                   \
-  GQA_LAUNCH((gemv_kernel<Q8, NT, L>), grid, blk, shm, st, W, Wq, Wd, K, N, xs, B, klen, P, part_stride, ldp, cand)
+#define GEMV_LAUNCH(QM, NT, L)                                                                                   \
+  GQA_LAUNCH((gemv_kernel<QM, NT, L>), grid, blk, shm, st, W, Wq, Wd, Wb, K, N, xs, B, klen, P, part_stride, ldp, cand)
+  const int qm = Wb ? WM_A4 : Wq ? WM_Q8 : WM_BF16;
   if (lds) {
-    if (Wq) GEMV_LAUNCH(true, 1, true);
-    else GEMV_LAUNCH(false, 1, true);
+    if (qm == WM_A4) GEMV_LAUNCH(WM_A4, 1, true);
+    else if (qm == WM_Q8) GEMV_LAUNCH(WM_Q8, 1, true);
+    else GEMV_LAUNCH(WM_BF16, 1, true);
   } else {
     const dim3 rgrid((N / 16 + kRowsWaves - 1) / kRowsWaves, nsplit), rblk(64 * kRowsWaves);
-#define ROWS_LAUNCH(Q8, NT)                                                                                      \
-  GQA_LAUNCH((gemv_rows_kernel<Q8, NT>), rgrid, rblk, 0, st, W, Wq, Wd, K, N, xs, B, klen, P, part_stride, ldp, \
+#define ROWS_LAUNCH(QM, NT)                                                                                      \
+  GQA_LAUNCH((gemv_rows_kernel<QM, NT>), rgrid, rblk, 0, st, W, Wq, Wd, Wb, K, N, xs, B, klen, P, part_stride, ldp, \
              cand)
     if (B <= 16) {
-      if (Wq) ROWS_LAUNCH(true, 1);
-      else ROWS_LAUNCH(false, 1);
+      if (qm == WM_A4) ROWS_LAUNCH(WM_A4, 1);
+      else if (qm == WM_Q8) ROWS_LAUNCH(WM_Q8, 1);
+      else ROWS_LAUNCH(WM_BF16, 1);
     } else {
-      if (Wq) ROWS_LAUNCH(true, 2);
-      else ROWS_LAUNCH(false, 2);
+      if (qm == WM_A4) ROWS_LAUNCH(WM_A4, 2);
+      else if (qm == WM_Q8) ROWS_LAUNCH(WM_Q8, 2);
+      else ROWS_LAUNCH(WM_BF16, 2);
     }
 #undef ROWS_LAUNCH
   }

@@ -30,7 +30,7 @@ namespace gqa {
 constexpr int kFullMaxB = 4;
 constexpr int kFullMaxLds = 64 * 1024;   // operand rows (hi + lo) in LDS
 
-template <bool Q8, int NWB, int NBW, int U, int MODE, int EPI, int MAXB>
+template <int QM, int NWB, int NBW, int U, int MODE, int EPI, int MAXB>
 __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
   constexpr int NT = 64 * NWB * NBW;
   constexpr int S = NWB;
@@ -50,15 +50,21 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
   struct Buf {
     uint4 w[U];
     uint2 q[U];
+    uint32_t q4[U];
     uint2 sc[U];
+    uint2 bs[U];
   };
   auto fetch = [&](Buf& f, int s) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t ch = chunk0 + min(s + u, s1 - 1);     // unconditional: no branch between loads
-      if (Q8) {
+      if (QM == WM_Q8) {
         f.q[u] = *(const uint2*)(a.Wq + ch * 512 + lane * 8);
         f.sc[u] = *(const uint2*)(a.Wd + ch * 16 + g4 * 4);
+      } else if (QM == WM_A4) {
+        f.q4[u] = *(const uint32_t*)(a.Wq + ch * 256 + lane * 4);
+        f.sc[u] = *(const uint2*)(a.Wd + ch * 16 + g4 * 4);
+        f.bs[u] = *(const uint2*)(a.Wb + ch * 16 + g4 * 4);
       } else {
         f.w[u] = *(const uint4*)(a.W + ch * 512 + lane * 8);
       }
@@ -151,7 +157,12 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
         const f16x8 bh = xvalid ? *(const f16x8*)(xh + kk) : f16x8{};
         const f16x8 bl = xvalid ? *(const f16x8*)(xl + kk) : f16x8{};
         f16x8 w;
-        if (Q8) {
+        if (QM == WM_A4) {
+          float sc[4], bs[4];
+          f16x4_bits_to_f32(f.sc[u], sc);
+          f16x4_bits_to_f32(f.bs[u], bs);
+          a4_step(acc, u4x8_to_f16x8(f.q4[u]), bh, bl, sc, bs);
+        } else if (QM == WM_Q8) {
           w = i8x8_to_f16x8(f.q[u]);
           const float sc[4] = {(float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x & 0xFFFF)),
                                (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x >> 16)),
@@ -263,7 +274,7 @@ bool gemv_full_fits(int K, int B) { return B >= 1 && B <= kFullMaxB && (size_t)4
 hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStream_t st) {
   if (!gemv_full_fits(a.K, a.B) || a.K % (32 * S) != 0 || a.N % 16 != 0) return hipErrorInvalidValue;
   if (mode == XF_NORM && (a.K > 4096 || !a.xres || !a.nw)) return hipErrorInvalidValue;
-  const bool q8 = a.Wq != nullptr;
+  const int qm = a.Wb ? WM_A4 : a.Wq ? WM_Q8 : WM_BF16;
   const size_t shm = (size_t)4 * a.B * a.K + 16;
 #define FULL(Q, NWB, NBW, U, MO, EP)                                                                          \
   do {                                                                                                        \
@@ -274,35 +285,37 @@ hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStre
       GQA_LAUNCH((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, kFullMaxB>), dim3(a.N / 16 / NBW),                 \
                  dim3(64 * NWB * NBW), shm, st, a);                                                            \
   } while (0)
-#define BY_Q8(NWB, NBW, U, MO, EP) \
-  do {                             \
-    if (q8)                        \
-      FULL(true, NWB, NBW, U, MO, EP); \
-    else                           \
-      FULL(false, NWB, NBW, U, MO, EP); \
+#define BY_QM(NWB, NBW, U, MO, EP)        \
+  do {                                    \
+    if (qm == WM_A4)                      \
+      FULL(WM_A4, NWB, NBW, U, MO, EP);   \
+    else if (qm == WM_Q8)                 \
+      FULL(WM_Q8, NWB, NBW, U, MO, EP);   \
+    else                                  \
+      FULL(WM_BF16, NWB, NBW, U, MO, EP); \
   } while (0)
   if (epi == EPI_SWIGLU) {
     if (mode != XF_NORM || S != 4 || a.N % 32 != 0) return hipErrorInvalidValue;
-    BY_Q8(4, 2, 4, XF_NORM, EPI_SWIGLU);
+    BY_QM(4, 2, 4, XF_NORM, EPI_SWIGLU);
   } else if (S == 8) {
     if (mode == XF_NORM) {
       if (epi != EPI_STORE) return hipErrorInvalidValue;
-      BY_Q8(8, 1, 4, XF_NORM, EPI_STORE);
+      BY_QM(8, 1, 4, XF_NORM, EPI_STORE);
     } else if (epi == EPI_ADD) {
-      BY_Q8(8, 1, 8, XF_RAW, EPI_ADD);
+      BY_QM(8, 1, 8, XF_RAW, EPI_ADD);
     } else {
-      BY_Q8(8, 1, 4, XF_RAW, EPI_STORE);
+      BY_QM(8, 1, 4, XF_RAW, EPI_STORE);
     }
   } else if (S == 1) {
-    if (mode != XF_RAW || epi != EPI_STORE || q8) return hipErrorInvalidValue;
+    if (mode != XF_RAW || epi != EPI_STORE || qm != WM_BF16) return hipErrorInvalidValue;
     if (a.N % 64 == 0)
-      FULL(false, 1, 4, 8, XF_RAW, EPI_STORE);
+      FULL(WM_BF16, 1, 4, 8, XF_RAW, EPI_STORE);
     else
-      FULL(false, 1, 1, 8, XF_RAW, EPI_STORE);
+      FULL(WM_BF16, 1, 1, 8, XF_RAW, EPI_STORE);
   } else {
     return hipErrorInvalidValue;
   }
-#undef BY_Q8
+#undef BY_QM
 #undef FULL
   return hipGetLastError();
 }

@@ -11,6 +11,14 @@
 // scale and 32 int8 quants (stored here as a tile-major int8 matrix plus a scale array indexed by
 // tiled_scale_index). d = amax / 127 (FP32 division), scale = fp16_rne(d),
 // q = clamp(round_half_away(w / d), -127, 127), and q = 0 when d = 0.
+//
+// AFFINE4_GS32 (Kipp Model Support, "Quantization (AFFINE4_GS32)"): 32-weight groups along a row
+// of 4-bit codes with an fp16 scale and an fp16 bias, w = scale * q + bias. d = (max - min) / 15
+// (FP32), scale = fp16_rne(d), bias = fp16_rne(min), q = clamp(round_half_away((w - bias) /
+// scale), 0, 15) from the stored scale and bias in FP32, q = 0 when the scale is 0. Codes are
+// stored tile-major like the BF16 weights at half a byte each: the 8 codes an operand lane reads
+// (tiled_index positions 8 i .. 8 i + 7) form the 32-bit word i, element 2 j in nibble j and
+// element 2 j + 1 in nibble j + 4; scales and biases at tiled_scale_index.
 #include "gqa_common.h"
 
 namespace gqa {
@@ -73,6 +81,64 @@ __global__ void quantize_q8_0_kernel(const uint16_t* __restrict__ w, int8_t* __r
   }
 }
 
+// One thread per 32-weight group (row, blk) of a tile-major BF16 matrix [rows][cols].
+__global__ void quantize_affine4_kernel(const uint16_t* __restrict__ w, uint32_t* __restrict__ q4,
+                                        f16* __restrict__ d, f16* __restrict__ bias, int64_t rows, int64_t cols) {
+  int64_t nb = rows * (cols / 32);
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = b / (cols / 32), blk = b - row * (cols / 32);
+    int64_t at[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) at[g] = tiled_index(row, blk * 32 + g * 8, cols);   // 8 contiguous columns each
+    float v[32];
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      v[i] = bf16_bits_to_f32(w[at[i / 8] + i % 8]);
+      mn = fminf(mn, v[i]);
+      mx = fmaxf(mx, v[i]);
+    }
+    const f16 sd = (f16)__fdiv_rn(__fsub_rn(mx, mn), 15.0f), sb = (f16)mn;
+    d[tiled_scale_index(row, blk, cols)] = sd;
+    bias[tiled_scale_index(row, blk, cols)] = sb;
+    const float D = (float)sd, Bv = (float)sb;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float r = D == 0.f ? 0.f : __fdiv_rn(__fsub_rn(v[g * 8 + e], Bv), D);
+        const float qf = fminf(fmaxf(roundf(r), 0.f), 15.f);   // half away from zero
+        word |= (uint32_t)(int)qf << (4 * ((e & 1) * 4 + (e >> 1)));
+      }
+      q4[at[g] / 8] = word;
+    }
+  }
+}
+
+// FP16 prefill copy (prefill_weight_index) of a tile-major AFFINE4 matrix: one thread per
+// 8-element piece, w = fp16_rne(fmaf(scale, q, bias)) (the prefill GEMM's operand).
+__global__ void prefill_copy_affine4_kernel(const uint32_t* __restrict__ q4, const f16* __restrict__ d,
+                                            const f16* __restrict__ bias, f16* __restrict__ dst, int64_t rows,
+                                            int64_t cols) {
+  const int64_t npieces = rows * cols / 8, ksteps = cols >> 5;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < npieces; p += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t bp = p >> 7, pos = p & 127;
+    const int64_t row = (bp / ksteps) * 32 + (pos & 31);
+    const int64_t col = (bp % ksteps) * 32 + ((pos >> 6) & 1) * 16 + ((pos >> 5) & 1) * 8;
+    const uint32_t word = q4[tiled_index(row, col, cols) / 8];
+    const float D = (float)d[tiled_scale_index(row, col >> 5, cols)];
+    const float Bv = (float)bias[tiled_scale_index(row, col >> 5, cols)];
+    f16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float q = (float)((word >> (4 * ((e & 1) * 4 + (e >> 1)))) & 15u);
+      o[e] = (f16)fmaf(D, q, Bv);
+    }
+    *(f16x8*)(dst + p * 8) = o;
+  }
+}
+
 // FP16 prefill copy (prefill_weight_index) of a tile-major BF16 matrix: one thread per 8-element
 // piece of the destination, converted exactly like the matrix-core operand path (bf16x8_to_f16x8).
 __global__ void prefill_copy_kernel(const uint16_t* __restrict__ src, f16* __restrict__ dst, int64_t rows,
@@ -91,6 +157,23 @@ hipError_t launch_prefill_copy(const uint16_t* src, f16* dst, int64_t rows, int6
   const int64_t n = rows * cols / 8;
   const int grid = (int)std::min<int64_t>((n + 255) / 256, 65536);
   hipLaunchKernelGGL(prefill_copy_kernel, dim3(grid), dim3(256), 0, st, src, dst, rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_affine4(const uint16_t* w, uint8_t* q4, f16* d, f16* bias, int64_t rows, int64_t cols,
+                                  hipStream_t st) {
+  int64_t nb = rows * (cols / 32);
+  int grid = (int)std::min<int64_t>((nb + 255) / 256, 65536);
+  hipLaunchKernelGGL(quantize_affine4_kernel, dim3(grid), dim3(256), 0, st, w, (uint32_t*)q4, d, bias, rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_copy_affine4(const uint8_t* q4, const f16* d, const f16* bias, f16* dst, int64_t rows,
+                                       int64_t cols, hipStream_t st) {
+  const int64_t n = rows * cols / 8;
+  const int grid = (int)std::min<int64_t>((n + 255) / 256, 65536);
+  hipLaunchKernelGGL(prefill_copy_affine4_kernel, dim3(grid), dim3(256), 0, st, (const uint32_t*)q4, d, bias, dst, rows,
+                     cols);
   return hipGetLastError();
 }
 

@@ -26,6 +26,10 @@ hipError_t launch_gen_weights(uint16_t* dst, uint64_t key, int64_t rows, int64_t
                               float scale, hipStream_t st);
 hipError_t launch_fill_u16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t st);
 hipError_t launch_quantize_q8_0(const uint16_t* w, int8_t* q, f16* d, int64_t rows, int64_t cols, hipStream_t st);
+hipError_t launch_quantize_affine4(const uint16_t* w, uint8_t* q4, f16* d, f16* bias, int64_t rows, int64_t cols,
+                                  hipStream_t st);
+hipError_t launch_prefill_copy_affine4(const uint8_t* q4, const f16* d, const f16* bias, f16* dst, int64_t rows,
+                                       int64_t cols, hipStream_t st);
 hipError_t launch_embed(const uint16_t* E, const int32_t* ids, int T, int H, int vocab, float* x, int32_t* err,
                         hipStream_t st);
 hipError_t launch_rmsnorm(float* x, int ldx, const float* part, int nsplit, int part_stride_split, int part_ld,
@@ -44,7 +48,7 @@ hipError_t launch_prefill_copy(const uint16_t* src, f16* dst, int64_t rows, int6
 hipError_t launch_gemm(int epi, bool split, const f16* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
                        const f16* Xlo, int ldx, int T, float* C, int ldc, float out_scale, f16* Mhi, f16* Mlo,
                        int ldm, float m_scale, int ksplit, int64_t split_stride, hipStream_t st);
-hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const XSrc& xs, int B,
+hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, const f16* Wb, int K, int N, const XSrc& xs, int B,
                        int nsplit, float* P, int64_t part_stride, int ldp, float2* cand, hipStream_t st,
                        bool staged = false);
 hipError_t launch_rows(const XSrc& xs, int K, int nsplit, int B, f16* yhi, f16* ylo, int ldy, hipStream_t st);
@@ -106,8 +110,9 @@ struct LayerW {
   uint16_t *attn_norm = nullptr, *ffn_norm = nullptr, *q_norm = nullptr, *k_norm = nullptr;
   uint16_t *wqkv = nullptr, *wo = nullptr, *wgu = nullptr, *wd = nullptr;                  // BF16
   f16 *pqkv = nullptr, *po = nullptr, *pgu = nullptr, *pd = nullptr;                       // FP16 prefill copies
-  int8_t *qqkv = nullptr, *qo = nullptr, *qgu = nullptr, *qd = nullptr;                    // Q8_0 quants
-  f16 *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sd = nullptr;                       // Q8_0 scales
+  int8_t *qqkv = nullptr, *qo = nullptr, *qgu = nullptr, *qd = nullptr;   // Q8_0 quants / AFFINE4 codes
+  f16 *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sd = nullptr;       // Q8_0 / AFFINE4 scales
+  f16 *bqkv = nullptr, *bo = nullptr, *bgu = nullptr, *bd = nullptr;       // AFFINE4 biases
   uint16_t *kpool = nullptr, *vpool = nullptr;
 };
 
@@ -187,7 +192,8 @@ int check_desc(const gqa_model_desc* d) {
   if (d->n_layers < 1 || d->hidden < 256 || d->hidden > 4096 || d->hidden % 256 || d->ffn < 128 ||
       (2 * d->ffn) % 256 || d->vocab < 16 || d->vocab % 16)
     return fail(GQA_E_INVALID, "unsupported shape (hidden %% 256, hidden <= 4096, 2*ffn %% 256, vocab %% 16)");
-  if (d->scheme != GQA_SCHEME_BF16 && d->scheme != GQA_SCHEME_Q8_0) return fail(GQA_E_INVALID, "unknown scheme");
+  if (d->scheme != GQA_SCHEME_BF16 && d->scheme != GQA_SCHEME_Q8_0 && d->scheme != GQA_SCHEME_AFFINE4)
+    return fail(GQA_E_INVALID, "unknown scheme");
   if (d->prefill_operands != GQA_PREFILL_SPLIT && d->prefill_operands != GQA_PREFILL_FP16)
     return fail(GQA_E_INVALID, "unknown prefill_operands");
   if (d->kv_pool_blocks < 1 || d->max_positions < 1 || d->max_round_tokens < 0)
@@ -245,7 +251,7 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   m->s_o = 8;
   m->s_gu = 4;
   m->s_d = (F / 32) % 8 == 0 ? 8 : 4;
-  const bool q8 = d.scheme == GQA_SCHEME_Q8_0;
+  const bool q8 = d.scheme == GQA_SCHEME_Q8_0, a4 = d.scheme == GQA_SCHEME_AFFINE4;
   int64_t* wb = &m->weight_bytes;
 
 #define ALLOC(p, n, ctr)                      \
@@ -280,6 +286,24 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
       ALLOC(w.sgu, (int64_t)2 * F * H / 32, wb);
       ALLOC(w.qd, (int64_t)H * F, wb);
       ALLOC(w.sd, (int64_t)H * F / 32, wb);
+    } else if (a4) {
+      // codes (half a byte per weight), scales and biases; FP16 dequantised copies for prefill
+      ALLOC(w.qqkv, (int64_t)m->QKV * H / 2, wb);
+      ALLOC(w.sqkv, (int64_t)m->QKV * H / 32, wb);
+      ALLOC(w.bqkv, (int64_t)m->QKV * H / 32, wb);
+      ALLOC(w.qo, (int64_t)H * m->QD / 2, wb);
+      ALLOC(w.so, (int64_t)H * m->QD / 32, wb);
+      ALLOC(w.bo, (int64_t)H * m->QD / 32, wb);
+      ALLOC(w.qgu, (int64_t)2 * F * H / 2, wb);
+      ALLOC(w.sgu, (int64_t)2 * F * H / 32, wb);
+      ALLOC(w.bgu, (int64_t)2 * F * H / 32, wb);
+      ALLOC(w.qd, (int64_t)H * F / 2, wb);
+      ALLOC(w.sd, (int64_t)H * F / 32, wb);
+      ALLOC(w.bd, (int64_t)H * F / 32, wb);
+      ALLOC(w.pqkv, (int64_t)m->QKV * H, &m->prefill_copy_bytes);
+      ALLOC(w.po, (int64_t)H * m->QD, &m->prefill_copy_bytes);
+      ALLOC(w.pgu, (int64_t)2 * F * H, &m->prefill_copy_bytes);
+      ALLOC(w.pd, (int64_t)H * F, &m->prefill_copy_bytes);
     } else {
       ALLOC(w.wqkv, (int64_t)m->QKV * H, wb);
       ALLOC(w.wo, (int64_t)H * m->QD, wb);
@@ -334,7 +358,7 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   hipStream_t st = nullptr;
   const float sc = weight_scale();
   uint16_t* tmp = nullptr;
-  if (q8) {
+  if (q8 || a4) {
     int64_t biggest = std::max<int64_t>(std::max<int64_t>((int64_t)2 * F * H, (int64_t)m->QKV * H),
                                         std::max<int64_t>((int64_t)H * m->QD, (int64_t)H * F));
     void* v = nullptr;
@@ -362,28 +386,37 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
     chk(launch_fill_u16(w.ffn_norm, H, 0x3F80, st));
     chk(launch_fill_u16(w.q_norm, kHeadDim, 0x3F80, st));
     chk(launch_fill_u16(w.k_norm, kHeadDim, 0x3F80, st));
-    uint16_t* dqkv = q8 ? tmp : w.wqkv;
+    // quantised schemes generate each projection into tmp and quantise it from there
+    auto quant = [&](int8_t* q, f16* sc_, f16* b_, f16* pcopy, int64_t r, int64_t c) {
+      if (q8) chk(launch_quantize_q8_0(tmp, q, sc_, r, c, st));
+      if (a4) {
+        chk(launch_quantize_affine4(tmp, (uint8_t*)q, sc_, b_, r, c, st));
+        chk(launch_prefill_copy_affine4((const uint8_t*)q, sc_, b_, pcopy, r, c, st));
+      }
+    };
+    const bool qs = q8 || a4;
+    uint16_t* dqkv = qs ? tmp : w.wqkv;
     chk(gen(dqkv, GQA_T_Q, l, m->QD, H, 0, 0));
     chk(gen(dqkv, GQA_T_K, l, KVD, H, 0, m->QD));
     chk(gen(dqkv, GQA_T_V, l, KVD, H, 0, m->QD + KVD));
-    if (q8) chk(launch_quantize_q8_0(tmp, w.qqkv, w.sqkv, m->QKV, H, st));
-    uint16_t* dO = q8 ? tmp : w.wo;
+    if (qs) quant(w.qqkv, w.sqkv, w.bqkv, w.pqkv, m->QKV, H);
+    uint16_t* dO = qs ? tmp : w.wo;
     chk(gen(dO, GQA_T_O, l, H, m->QD, 0, 0));
-    if (q8) chk(launch_quantize_q8_0(tmp, w.qo, w.so, H, m->QD, st));
-    uint16_t* dgu = q8 ? tmp : w.wgu;
+    if (qs) quant(w.qo, w.so, w.bo, w.po, H, m->QD);
+    uint16_t* dgu = qs ? tmp : w.wgu;
     chk(gen(dgu, GQA_T_GATE, l, F, H, 1, 0));
     chk(gen(dgu, GQA_T_UP, l, F, H, 2, 0));
-    if (q8) chk(launch_quantize_q8_0(tmp, w.qgu, w.sgu, 2 * F, H, st));
-    uint16_t* dD = q8 ? tmp : w.wd;
+    if (qs) quant(w.qgu, w.sgu, w.bgu, w.pgu, 2 * F, H);
+    uint16_t* dD = qs ? tmp : w.wd;
     chk(gen(dD, GQA_T_DOWN, l, H, F, 0, 0));
-    if (q8) chk(launch_quantize_q8_0(tmp, w.qd, w.sd, H, F, st));
-    if (!q8) {
+    if (qs) quant(w.qd, w.sd, w.bd, w.pd, H, F);
+    if (!qs) {
       chk(launch_prefill_copy(w.wqkv, w.pqkv, m->QKV, H, st));
       chk(launch_prefill_copy(w.wo, w.po, H, m->QD, st));
       chk(launch_prefill_copy(w.wgu, w.pgu, 2 * F, H, st));
       chk(launch_prefill_copy(w.wd, w.pd, H, F, st));
     }
-    if (q8) chk(hipStreamSynchronize(st));
+    if (qs) chk(hipStreamSynchronize(st));
     chk(hipMemsetAsync(w.kpool, 0, pool_elems * 2, st));
     chk(hipMemsetAsync(w.vpool, 0, pool_elems * 2, st));
   }
@@ -693,12 +726,12 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
     return x;
   };
   // matvec over an operand built by a prologue: in LDS (B <= 4) or by rows_kernel first
-  auto gemv_built = [&](const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const XSrc& xs,
+  auto gemv_built = [&](const uint16_t* W, const int8_t* Wq, const f16* Wd, const f16* Wb, int K, int N, const XSrc& xs,
                         int nsplit, float* P, int ldp, f16* hi, f16* lo) -> hipError_t {
-    if (fused) return launch_gemv(W, Wq, Wd, K, N, xs, B, nsplit, P, pstride, ldp, nullptr, st);
+    if (fused) return launch_gemv(W, Wq, Wd, Wb, K, N, xs, B, nsplit, P, pstride, ldp, nullptr, st);
     hipError_t e = launch_rows(xs, K, nsplit, B, hi, lo, K, st);
     if (e != hipSuccess) return e;
-    return launch_gemv(W, Wq, Wd, K, N, raw_src(hi, lo, K), B, nsplit, P, pstride, ldp, nullptr, st);
+    return launch_gemv(W, Wq, Wd, Wb, K, N, raw_src(hi, lo, K), B, nsplit, P, pstride, ldp, nullptr, st);
   };
 
   // Whole-K path (few rows): the residual stream xa is final after every projection, no split
@@ -713,25 +746,25 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
     for (int l = 0; l < d.n_layers; ++l) {
       const LayerW& w = m->L[l];
       FullArgs q = fa();
-      q.W = w.wqkv; q.Wq = w.qqkv; q.Wd = w.sqkv; q.K = H; q.N = QKV;
+      q.W = w.wqkv; q.Wq = w.qqkv; q.Wd = w.sqkv; q.Wb = w.bqkv; q.K = H; q.N = QKV;
       q.xres = xa; q.nw = w.attn_norm; q.ss_out = ss_qkv; q.y = P0; q.ldy = QKV;
       LAUNCH(launch_gemv_full(XF_NORM, EPI_STORE, m->s_qkv, q, st));
       LAUNCH(launch_attn_decode(P0, 1, pstride, QKV, NQ, ss_qkv, m->s_qkv, H, w.q_norm, w.k_norm, eps, m->rcos,
                                 m->rsin, rows, B, max_ctx, w.kpool, w.vpool, m->apart, m->counters, kAttnOutScale, m->oh, m->ol, QD,
                                 st));
       FullArgs o = fa();
-      o.W = w.wo; o.Wq = w.qo; o.Wd = w.so; o.K = QD; o.N = H;
+      o.W = w.wo; o.Wq = w.qo; o.Wd = w.so; o.Wb = w.bo; o.K = QD; o.N = H;
       o.xhi = m->oh; o.xlo = m->ol; o.ldx = QD; o.y = xa; o.ldy = H; o.yscale = 1.f / kAttnOutScale;
       LAUNCH(launch_gemv_full(XF_RAW, EPI_ADD, m->s_o, o, st));
       FullArgs g = fa();
-      g.W = w.wgu; g.Wq = w.qgu; g.Wd = w.sgu; g.K = H; g.N = 2 * F;
+      g.W = w.wgu; g.Wq = w.qgu; g.Wd = w.sgu; g.Wb = w.bgu; g.K = H; g.N = 2 * F;
       g.xres = xa; g.nw = w.ffn_norm; g.ss_out = ss_gu; g.mhi = m->mh; g.mlo = m->ml; g.ldm = F;
       {
         ProfScope ps(m, GQA_PROF_DECODE_GATEUP, st);
         LAUNCH(launch_gemv_full(XF_NORM, EPI_SWIGLU, m->s_gu, g, st));
       }
       FullArgs dn = fa();
-      dn.W = w.wd; dn.Wq = w.qd; dn.Wd = w.sd; dn.K = F; dn.N = H;
+      dn.W = w.wd; dn.Wq = w.qd; dn.Wd = w.sd; dn.Wb = w.bd; dn.K = F; dn.N = H;
       dn.xhi = m->mh; dn.xlo = m->ml; dn.ldx = F; dn.y = xa; dn.ldy = H; dn.yscale = 1.f;
       LAUNCH(launch_gemv_full(XF_RAW, EPI_ADD, m->s_d, dn, st));
     }
@@ -752,16 +785,17 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
   int prev_split = 0;
   for (int l = 0; l < d.n_layers; ++l) {
     const LayerW& w = m->L[l];
-    LAUNCH(gemv_built(w.wqkv, w.qqkv, w.sqkv, H, QKV, resid_src(xa, xb, prev, prev_split, 1.f, w.attn_norm, ss_qkv),
+    LAUNCH(gemv_built(w.wqkv, w.qqkv, w.sqkv, w.bqkv, H, QKV, resid_src(xa, xb, prev, prev_split, 1.f, w.attn_norm, ss_qkv),
                       m->s_qkv, P0, QKV, m->xh, m->xl));
     std::swap(xa, xb);
     LAUNCH(launch_attn_decode(P0, m->s_qkv, pstride, QKV, NQ, ss_qkv, m->s_qkv, H, w.q_norm, w.k_norm, eps, m->rcos,
                               m->rsin, rows, B, max_ctx, w.kpool, w.vpool, m->apart, m->counters, kAttnOutScale, m->oh, m->ol, QD,
                               st));
-    LAUNCH(launch_gemv(w.wo, w.qo, w.so, QD, H, raw_src(m->oh, m->ol, QD), B, m->s_o, P1, pstride, H, nullptr, st));
+    LAUNCH(launch_gemv(w.wo, w.qo, w.so, w.bo, QD, H, raw_src(m->oh, m->ol, QD), B, m->s_o, P1, pstride, H, nullptr,
+                       st));
     {
       ProfScope ps(m, GQA_PROF_DECODE_GATEUP, st);
-      LAUNCH(gemv_built(w.wgu, w.qgu, w.sgu, H, 2 * F,
+      LAUNCH(gemv_built(w.wgu, w.qgu, w.sgu, w.bgu, H, 2 * F,
                         resid_src(xa, xb, P1, m->s_o, 1.f / kAttnOutScale, w.ffn_norm, ss_gu), m->s_gu, P0, 2 * F,
                         m->xh, m->xl));
     }
@@ -776,7 +810,7 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
     sw.ss_n = m->s_gu;
     sw.H = H;
     sw.eps = eps;
-    LAUNCH(gemv_built(w.wd, w.qd, w.sd, F, H, sw, m->s_d, P1, H, m->mh, m->ml));
+    LAUNCH(gemv_built(w.wd, w.qd, w.sd, w.bd, F, H, sw, m->s_d, P1, H, m->mh, m->ml));
     prev = P1;
     prev_split = m->s_d;
   }
@@ -784,7 +818,7 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
                            st));
   {
     ProfScope ps(m, GQA_PROF_DECODE_LMHEAD, st);
-    LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, H, V, raw_src(m->xh, m->xl, H), B, 1, logits, pstride, V,
+    LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, nullptr, H, V, raw_src(m->xh, m->xl, H), B, 1, logits, pstride, V,
                        argmax ? m->cand : nullptr, st));
   }
   if (argmax) LAUNCH(launch_argmax(m->cand, V / 16, B, argmax, st));
@@ -821,18 +855,20 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
   const float eps = d.rms_eps;
   Rows none{};
   const bool split = d.prefill_operands == GQA_PREFILL_SPLIT;
+  // the GEMM reads Q8_0 quants directly; BF16 and AFFINE4 models use their FP16 prefill copies
+  auto gq = [&](const int8_t* q) { return d.scheme == GQA_SCHEME_Q8_0 ? q : nullptr; };
   // Projection of `rows` operand rows (FP16 hi/lo, row stride ldx) for a round of at most 32
   // rows: the LDS-staged matvec over the decode weights with the decode K ranges, partials
   // P[range][row][N] (range stride rows * N) summed in range order by the consumer. A 128-row
   // GEMM tile would leave most of the chip idle and stream each weight tile on few CUs.
-  auto matvec = [&](const uint16_t* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* xh, const f16* xl,
-                    int ldx, int rows, int nsplit, float* P) -> int {
+  auto matvec = [&](const uint16_t* W, const int8_t* Wq, const f16* Wd, const f16* Wb, int K, int N, const f16* xh,
+                    const f16* xl, int ldx, int rows, int nsplit, float* P) -> int {
     XSrc raw{};
     raw.mode = X_RAW;
     raw.hi = xh;
     raw.lo = xl;
     raw.ld = ldx;
-    LAUNCH(launch_gemv(W, Wq, Wd, K, N, raw, rows, nsplit, P, (int64_t)rows * N, N, nullptr, st, true));
+    LAUNCH(launch_gemv(W, Wq, Wd, Wb, K, N, raw, rows, nsplit, P, (int64_t)rows * N, N, nullptr, st, true));
     return GQA_OK;
   };
   for (int off = 0; off < n; off += m->R) {
@@ -846,12 +882,12 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
       const LayerW& w = m->L[l];
       const bool last = l + 1 == d.n_layers;
       if (mv) {
-        int rc = matvec(w.wqkv, w.qqkv, w.sqkv, H, QKV, m->xh, m->xl, H, T, m->s_qkv, m->part);
+        int rc = matvec(w.wqkv, w.qqkv, w.sqkv, w.bqkv, H, QKV, m->xh, m->xl, H, T, m->s_qkv, m->part);
         if (rc) return rc;
         LAUNCH(launch_qk_rope_kv(false, m->part, m->s_qkv, T * QKV, QKV, NQ, w.q_norm, w.k_norm, eps, m->rcos,
                                  m->rsin, pos0, s->d_table, none, w.kpool, w.vpool, m->q, T, st));
       } else {
-        LAUNCH(launch_gemm(EPI_STORE, split, w.pqkv, w.qqkv, w.sqkv, H, QKV, m->xh, m->xl, H, T, m->qkv, QKV, 1.f,
+        LAUNCH(launch_gemm(EPI_STORE, split, w.pqkv, gq(w.qqkv), w.sqkv, H, QKV, m->xh, m->xl, H, T, m->qkv, QKV, 1.f,
                            nullptr, nullptr, 0, 1.f, 1, 0, st));
         LAUNCH(launch_qk_rope_kv(false, m->qkv, 0, 0, QKV, NQ, w.q_norm, w.k_norm, eps, m->rcos, m->rsin, pos0,
                                  s->d_table, none, w.kpool, w.vpool, m->q, T, st));
@@ -868,30 +904,30 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
       int so = 0, sd = 0;
       if (mv) {
         so = m->s_o;
-        int rc = matvec(w.wo, w.qo, w.so, QD, H, m->oh, m->ol, QD, rows, so, pp);
+        int rc = matvec(w.wo, w.qo, w.so, w.bo, QD, H, m->oh, m->ol, QD, rows, so, pp);
         if (rc) return rc;
       } else {
         so = prefill_ksplit(m, H, QD, rows);
-        LAUNCH(launch_gemm(EPI_STORE, split, w.po, w.qo, w.so, QD, H, m->oh, m->ol, QD, rows, pp, H, 1.f, nullptr,
+        LAUNCH(launch_gemm(EPI_STORE, split, w.po, gq(w.qo), w.so, QD, H, m->oh, m->ol, QD, rows, pp, H, 1.f, nullptr,
                            nullptr, 0, 1.f, so, (int64_t)rows * H, st));
       }
       LAUNCH(launch_rmsnorm(m->x + (int64_t)r0 * H, H, pp, so, rows * H, H, 1.f / kAttnOutScale, w.ffn_norm, H, eps,
                             1.f, m->xh, m->xl, H, rows, st));
       if (mv) {
-        int rc = matvec(w.wgu, w.qgu, w.sgu, H, 2 * F, m->xh, m->xl, H, rows, m->s_gu, m->part);
+        int rc = matvec(w.wgu, w.qgu, w.sgu, w.bgu, H, 2 * F, m->xh, m->xl, H, rows, m->s_gu, m->part);
         if (rc) return rc;
         LAUNCH(launch_swiglu_rows(m->part, m->s_gu, (int64_t)rows * 2 * F, 2 * F, F, rows, m->mh, m->ml, F, st));
         sd = m->s_d;
-        rc = matvec(w.wd, w.qd, w.sd, F, H, m->mh, m->ml, F, rows, sd, pp);
+        rc = matvec(w.wd, w.qd, w.sd, w.bd, F, H, m->mh, m->ml, F, rows, sd, pp);
         if (rc) return rc;
       } else {
         {
           ProfScope ps(m, last ? kProfNever : GQA_PROF_PREFILL_GATEUP, st);
-          LAUNCH(launch_gemm(EPI_SWIGLU, split, w.pgu, w.qgu, w.sgu, H, 2 * F, m->xh, m->xl, H, rows, nullptr, 0, 1.f,
+          LAUNCH(launch_gemm(EPI_SWIGLU, split, w.pgu, gq(w.qgu), w.sgu, H, 2 * F, m->xh, m->xl, H, rows, nullptr, 0, 1.f,
                              m->mh, m->ml, F, 1.f, 1, 0, st));
         }
         sd = prefill_ksplit(m, H, F, rows);
-        LAUNCH(launch_gemm(EPI_STORE, split, w.pd, w.qd, w.sd, F, H, m->mh, m->ml, F, rows, pp, H, 1.f, nullptr,
+        LAUNCH(launch_gemm(EPI_STORE, split, w.pd, gq(w.qd), w.sd, F, H, m->mh, m->ml, F, rows, pp, H, 1.f, nullptr,
                            nullptr, 0, 1.f, sd, (int64_t)rows * H, st));
       }
       const uint16_t* next_norm = last ? m->final_norm : m->L[l + 1].attn_norm;
@@ -911,11 +947,12 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
           raw.ld = H;
           ProfScope ps(m, out == kOutLast ? kProfNever : GQA_PROF_ROWS_LMHEAD, st);
           if (out == kOutScores) {
-            LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, H, V, raw, Bg, 1, m->slog, 0, V, nullptr, st));
+            LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, nullptr, H, V, raw, Bg, 1, m->slog, 0, V, nullptr, st));
             LAUNCH(launch_score(m->slog, V, ids_dev + i0 + 1, Bg, scores + i0, st));
           } else {
             float* dst = logits + (int64_t)(out == kOutAll ? i0 : 0) * V;
-            LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, H, V, raw, Bg, 1, dst, 0, V, argmax ? m->cand : nullptr,
+            LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, nullptr, H, V, raw, Bg, 1, dst, 0, V,
+                               argmax ? m->cand : nullptr,
                                st));
             if (argmax) LAUNCH(launch_argmax(m->cand, V / 16, Bg, argmax + (out == kOutAll ? i0 : 0), st));
           }
@@ -1193,7 +1230,7 @@ int gqa_debug_read_weight(gqa_model* m, int32_t kind, int32_t layer, int32_t row
     HIP_TRY(hipMemcpy(dst, src + (int64_t)row0 * cols, (size_t)rows * cols * 2, hipMemcpyDeviceToHost));
     return GQA_OK;
   }
-  if (d.scheme == GQA_SCHEME_Q8_0) return fail(GQA_E_INVALID, "Q8_0 model keeps no BF16 projections");
+  if (d.scheme != GQA_SCHEME_BF16) return fail(GQA_E_INVALID, "a quantised model keeps no BF16 projections");
   for (int r = 0; r < rows; ++r) {
     const void* base = nullptr;
     int pr = physical_row(m, kind, row0 + r, &base, &cols, false, layer);
@@ -1222,6 +1259,48 @@ int gqa_debug_read_q8(gqa_model* m, int32_t kind, int32_t layer, int32_t row0, i
     int pr = physical_row(m, kind, row0 + r, &base, &cols, true, layer);
     int rc = read_tiled_row(base, 1, pr, cols, quants + (int64_t)r * cols, sb, scales + (int64_t)r * (cols / 32));
     if (rc) return rc;
+  }
+  return GQA_OK;
+}
+
+int gqa_debug_read_affine4(gqa_model* m, int32_t kind, int32_t layer, int32_t row0, int32_t rows, uint8_t* codes,
+                           uint16_t* scales, uint16_t* biases) {
+  if (!m || !codes || !scales || !biases) return fail(GQA_E_INVALID, "null argument");
+  const gqa_model_desc& d = m->d;
+  if (d.scheme != GQA_SCHEME_AFFINE4) return fail(GQA_E_INVALID, "not an AFFINE4 model");
+  if (layer < 0 || layer >= d.n_layers) return fail(GQA_E_INVALID, "layer out of range");
+  int nrow = logical_rows(m, kind);
+  const void* base = nullptr;
+  int cols = 0;
+  if (nrow < 0 || physical_row(m, kind, 0, &base, &cols, true, layer) < 0)
+    return fail(GQA_E_INVALID, "not a projection kind");
+  if (row0 < 0 || rows < 1 || row0 + rows > nrow) return fail(GQA_E_INVALID, "rows out of range");
+  HIP_TRY(hipDeviceSynchronize());
+  const LayerW& w = m->L[layer];
+  const bool gu = kind == GQA_T_GATE || kind == GQA_T_UP;
+  const f16* sp = kind == GQA_T_O ? w.so : kind == GQA_T_DOWN ? w.sd : gu ? w.sgu : w.sqkv;
+  const f16* bp = kind == GQA_T_O ? w.bo : kind == GQA_T_DOWN ? w.bd : gu ? w.bgu : w.bqkv;
+  std::vector<uint32_t> band;
+  std::vector<uint16_t> sb, bb;
+  for (int r = 0; r < rows; ++r) {
+    const int pr = physical_row(m, kind, row0 + r, &base, &cols, true, layer);
+    const int64_t band_words = (int64_t)16 * cols / 8;            // 8 codes per 32-bit word
+    band.resize((size_t)band_words);
+    HIP_TRY(hipMemcpy(band.data(), (const uint32_t*)base + (pr >> 4) * band_words, band.size() * 4,
+                      hipMemcpyDeviceToHost));
+    for (int c = 0; c < cols; ++c) {
+      const int64_t t = tiled_index(pr & 15, c, cols);
+      const int e = (int)(t & 7);
+      codes[(int64_t)r * cols + c] = (uint8_t)((band[(size_t)(t >> 3)] >> (4 * ((e & 1) * 4 + (e >> 1)))) & 15u);
+    }
+    sb.resize((size_t)(cols / 32) * 16);
+    bb.resize(sb.size());
+    HIP_TRY(hipMemcpy(sb.data(), sp + (int64_t)(pr >> 4) * (cols / 32) * 16, sb.size() * 2, hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemcpy(bb.data(), bp + (int64_t)(pr >> 4) * (cols / 32) * 16, bb.size() * 2, hipMemcpyDeviceToHost));
+    for (int k = 0; k < cols / 32; ++k) {
+      scales[(int64_t)r * (cols / 32) + k] = sb[tiled_scale_index(pr & 15, k, cols)];
+      biases[(int64_t)r * (cols / 32) + k] = bb[tiled_scale_index(pr & 15, k, cols)];
+    }
   }
   return GQA_OK;
 }

@@ -50,6 +50,7 @@ extern "C" {
 
 #define GQA_SCHEME_BF16 0
 #define GQA_SCHEME_Q8_0 1
+#define GQA_SCHEME_AFFINE4 2   /* AFFINE4_GS32 (Kipp Model Support, "Quantization (AFFINE4_GS32)") */
 
 #define GQA_MAX_BATCH 32
 #define GQA_BLOCK_POSITIONS 32
@@ -71,7 +72,7 @@ typedef struct {
   int32_t tied;             /* 1: lm_head is the token embedding; 0: a separate lm_head */
   float rope_theta;
   float rms_eps;
-  int32_t scheme;           /* GQA_SCHEME_BF16 or GQA_SCHEME_Q8_0 (the seven projections) */
+  int32_t scheme;           /* GQA_SCHEME_BF16, _Q8_0 or _AFFINE4 (the seven projections) */
   int32_t kv_pool_blocks;   /* physical 32-position KV blocks in the model-owned pool */
   int32_t max_positions;    /* longest sequence any session may reach (RoPE table size) */
   int32_t max_round_tokens; /* prefill round width; 0 derives it from the device (CUs x 8) */
@@ -99,7 +100,12 @@ typedef struct {
  * Weights: the counter-based generator documented in the library source (SplitMix64 outputs
  * summed Irwin-Hall style, scaled to std 0.02, rounded to BF16), one key per tensor derived
  * from `seed`; norm weights are 1.0. For GQA_SCHEME_Q8_0 the seven projections are then
- * quantised to Q8_0 (32-weight blocks, fp16 scale = max|w|/127, int8 quants).
+ * quantised to Q8_0 (32-weight blocks, fp16 scale = max|w|/127, int8 quants); for
+ * GQA_SCHEME_AFFINE4 to AFFINE4_GS32: per 32-weight group along a row an fp16 scale
+ * fp16((max - min) / 15), an fp16 bias fp16(min) and 4-bit codes
+ * q = clamp(round_half_away((w - bias) / scale), 0, 15) (FP32, from the stored scale and bias;
+ * q = 0 when the scale is 0), w = scale * q + bias. Decode computes with these values exactly
+ * (scale * sum(q x) + bias * sum(x) per group); prefill GEMMs read an FP16 rounding of them.
  * Allocates weights, the KV pool and per-model scratch; fails with GQA_E_OOM if they do not
  * fit, GQA_E_DEVICE if the device is not gfx950, GQA_E_INVALID for a bad descriptor.
  * Synchronises the device before returning. *out is set only on success. */
@@ -268,6 +274,12 @@ int gqa_debug_read_weight(gqa_model* model, int32_t kind, int32_t layer, int32_t
  * (rows x cols) and fp16 scale bits (rows x cols/32) into host buffers. */
 int gqa_debug_read_q8(gqa_model* model, int32_t kind, int32_t layer, int32_t row0, int32_t rows, int8_t* quants,
                       uint16_t* scales);
+
+/* For an AFFINE4 model: copy logical rows [row0, row0+rows) of a projection as 4-bit codes (one
+ * per byte, rows x cols), fp16 scale bits and fp16 bias bits (rows x cols/32 each) into host
+ * buffers. */
+int gqa_debug_read_affine4(gqa_model* model, int32_t kind, int32_t layer, int32_t row0, int32_t rows, uint8_t* codes,
+                           uint16_t* scales, uint16_t* biases);
 
 /* Copy the BF16 bits of K and V of `layer` for logical positions [pos0, pos0+n) of a session,
  * read through its block table, into host arrays of n x 8 x 128 uint16 each. GQA_E_INVALID for

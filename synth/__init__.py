@@ -258,6 +258,7 @@ WORKLOADS = {
     "0.6b": Workload("0.6b", Q06B, "bf16", 348, 64, "shuffled", k=2),
     "4b": Workload("4b", Q4B, "bf16", 2048, 64, "shuffled", k=3),
     "4b-q8": Workload("4b-q8", Q4B, "q8_0", 12800, 32, "shuffled", k=4),
+    "4b-a4": Workload("4b-a4", Q4B, "affine4", 2048, 64, "shuffled", k=6),
     "8b-batch": Workload("8b-batch", Q8B, "bf16", 0, 128, "shuffled", n_seqs=32, k=5),
 }
 

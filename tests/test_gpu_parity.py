@@ -351,6 +351,105 @@ def test_tiny_q8_0_parity(g):
     m.close()
 
 
+def test_affine4_codes_match_oracle(g):
+    """AFFINE4_GS32 codes, scales and biases the library computes on the device equal the
+    oracle's quantiser output, for rows of every projection kind (tiny shape)."""
+    from oracle.affine4 import quantize_affine4
+    shape = synth.TINY
+    m = g.Model.from_shape(shape, seed=1001, scheme="affine4", kv_pool_blocks=2, max_positions=64)
+    for l in range(shape.n_layers):
+        for nm, dims in shape.layer_tensor_shapes().items():
+            if nm in synth.NORM_TENSORS:
+                continue
+            rows, cols = dims
+            w = synth.bf16_bits_to_f32(synth.tensor_bits(shape, 1001, nm, l))
+            for r0 in (0, rows // 2 + 5, rows - 3):
+                n = min(3, rows - r0)
+                sc, bi, q = quantize_affine4(w[r0:r0 + n])
+                gq, gs, gb = m.read_affine4(nm, l, r0, n, cols)
+                assert np.array_equal(gq, q), (nm, l, r0)
+                assert np.array_equal(gs, sc.view(np.uint16)) and np.array_equal(gb, bi.view(np.uint16)), (nm, l, r0)
+    m.close()
+
+
+def test_tiny_affine4_parity(g):
+    """AFFINE4 tiny decoder against the oracle computing with the same dequantised weights: a
+    16-token prompt (a round of few rows: matvec projections) and 16 teacher-forced decode steps,
+    then a 100-token prompt in rounds of 48 (GEMMs over the FP16 dequantised copies, then a
+    4-row matvec round) and 3 steps (gate: exact argmax, NMSE <= 1e-4)."""
+    wl = synth.WORKLOADS["tiny"]
+    shape = wl.shape
+    prompt = synth.token_ids(wl.ids_seed, wl.prompt)
+    say("tiny affine4 oracle")
+    ref, toks = oracle_greedy(shape, wl.weight_seed, prompt, wl.decode, scheme="affine4")
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, scheme="affine4", kv_pool_blocks=8, max_positions=128,
+                           max_round_tokens=48)
+    s = g.Session(m, 128)
+    got = gpu_teacher_forced(m, s, prompt, toks, shape.vocab)
+    gate = Gate("tiny affine4")
+    for i, ((lg, am), r) in enumerate(zip(got, ref)):
+        gate.check(i, lg, r, am)
+    long_prompt = synth.token_ids(61, 100)
+    ref2, toks2 = oracle_greedy(shape, wl.weight_seed, long_prompt, 3, scheme="affine4")
+    s2 = g.Session(m, 128)
+    got2 = gpu_teacher_forced(m, s2, long_prompt, toks2, shape.vocab)
+    for i, ((lg, am), r) in enumerate(zip(got2, ref2)):
+        gate.check(100 + i, lg, r, am)
+    gate.assert_ok()
+    for o in (s, s2, m):
+        o.close()
+
+
+def test_affine4_batched_equals_isolated_bitwise(g):
+    """AFFINE4 batched decode (7 rows: the staged split-K matvec) equals each row stepped alone
+    (the whole-K matvec), bit for bit (Kipp Roadmap, status v0.0.2)."""
+    shape = synth.TINY
+    m = g.Model.from_shape(shape, seed=1001, scheme="affine4", kv_pool_blocks=64, max_positions=128)
+    B = 7
+    ss = [g.Session(m, 128) for _ in range(B)]
+    twins = [g.Session(m, 128) for _ in range(B)]
+    lg1 = torch.empty(shape.vocab, device="cuda")
+    for b in range(B):
+        p = synth.token_ids(70 + b, 5 + 3 * b)
+        ss[b].prefill(p, lg1)
+        twins[b].prefill(p, lg1)
+    lg = torch.empty((B, shape.vocab), device="cuda")
+    am = torch.empty(B, dtype=torch.int32, device="cuda")
+    toks = [int(t) for t in synth.token_ids(80, B)]
+    for step in range(3):
+        m.eval_batch(ss, toks, lg, am)
+        batched = lg.cpu().numpy()
+        for b in range(B):
+            twins[b].decode(toks[b], lg1)
+            torch.cuda.synchronize()
+            assert np.array_equal(batched[b], lg1.cpu().numpy()), (step, b)
+        toks = [int(t) for t in am.cpu().numpy()]
+    for o in ss + twins + [m]:
+        o.close()
+
+
+def test_qwen3_4b_affine4_reduced_depth_parity(g):
+    """AFFINE4 at the 4B hidden sizes with 2 layers: a 300-token prompt (GEMMs over the FP16
+    dequantised copies) and 3 teacher-forced decode steps (the whole-K matvec on the codes) over
+    a shuffled paged KV, against the oracle (gate)."""
+    wl = synth.WORKLOADS["4b-a4"]
+    shape = synth.reduced(wl.shape, n_layers=2)
+    prompt = synth.token_ids(wl.ids_seed, 300)
+    say("4b affine4 depth-2 oracle")
+    ref, toks = oracle_greedy(shape, wl.weight_seed, prompt, 3, scheme="affine4")
+    nb = synth.blocks_for(len(prompt) + 4)
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, scheme="affine4", kv_pool_blocks=4 * nb,
+                           max_positions=nb * 32)
+    s = g.Session(m, nb * 32, block_ids=synth.shuffled_blocks(wl.shuffle_seed, 4 * nb)[:nb])
+    got = gpu_teacher_forced(m, s, prompt, toks, shape.vocab)
+    gate = Gate("4b affine4 depth 2")
+    for i, ((lg, am), r) in enumerate(zip(got, ref)):
+        gate.check(i, lg, r, am)
+    gate.assert_ok()
+    s.close()
+    m.close()
+
+
 @pytest.mark.parametrize("prefill", ["split", "fp16"])
 def test_qwen3_0_6b_shape_parity(g, prefill):
     """0.6B shape: 28 layers, 348-token prompt, 64 teacher-forced greedy steps, paged KV with a
