@@ -283,21 +283,47 @@ __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// One 32-wide K-step of an AFFINE4 band against one token column's operand (hi, lo): the
-// codes' products and the operand's sum over the step (an all-ones A operand) on the matrix
-// cores, then per weight row acc += scale * sum(q x) + bias * sum(x). Every matvec path uses
-// this same sequence, so a row's result does not depend on the path.
-__device__ __forceinline__ void a4_step(f32x4& acc, f16x8 a, f16x8 bh, f16x8 bl, const float (&sc)[4],
-                                        const float (&bs)[4]) {
-  const f16 one = (f16)1.0f;
-  const f16x8 ones = {one, one, one, one, one, one, one, one};
-  f32x4 p = {0.f, 0.f, 0.f, 0.f}, xs = {0.f, 0.f, 0.f, 0.f};
+// One 32-wide K-step of a quantised band against one token column's operand (hi, lo), in two
+// parts that every matvec path uses in the same order, so a row's result does not depend on the
+// path. qstep_products: the codes' block products into a fresh accumulator p, and for AFFINE4 the
+// operand's sum over the step xs (an all-ones A operand) -- both on the matrix cores.
+// qstep_accumulate: per weight row acc += scale * p (Q8_0), or acc += scale * p + bias * xs
+// (AFFINE4, w = scale * q + bias), in FP32. The kernels issue the products of several steps
+// before accumulating them in step order, so no FMA waits on the MFMA just before it.
+template <int QM>
+__device__ __forceinline__ void qstep_products(f16x8 a, f16x8 bh, f16x8 bl, f32x4& p, f32x4& xs) {
+  p = f32x4{0.f, 0.f, 0.f, 0.f};
   p = mfma16(a, bh, p);
   p = mfma16(a, bl, p);
-  xs = mfma16(ones, bh, xs);
-  xs = mfma16(ones, bl, xs);
+  if constexpr (QM == WM_A4) {
+    const f16 one = (f16)1.0f;
+    const f16x8 ones = {one, one, one, one, one, one, one, one};
+    xs = f32x4{0.f, 0.f, 0.f, 0.f};
+    xs = mfma16(ones, bh, xs);
+    xs = mfma16(ones, bl, xs);
+  }
+}
+
+template <int QM>
+__device__ __forceinline__ void qstep_accumulate(f32x4& acc, const f32x4& p, const f32x4& xs, uint2 sc2, uint2 bs2) {
+  float sc[4];
+  f16x4_bits_to_f32(sc2, sc);
+  if constexpr (QM == WM_A4) {
+    float bs[4];
+    f16x4_bits_to_f32(bs2, bs);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc[r], p[r], fmaf(bs[r], xs[r], acc[r]));
+    for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc[r], p[r], fmaf(bs[r], xs[r], acc[r]));
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc[r], p[r], acc[r]);
+  }
+}
+
+// Widened codes of one operand lane.
+template <int QM>
+__device__ __forceinline__ f16x8 qwiden(uint2 q8, uint32_t q4) {
+  if constexpr (QM == WM_A4) return u4x8_to_f16x8(q4);
+  else return i8x8_to_f16x8(q8);
 }
 
 // Wave-wide sum / max: DPP within each 16-lane row, then the four row results read as scalars

@@ -216,49 +216,42 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* _
   if (!has_tile) return;
 
   auto compute = [&](const Buf& f, int k) {
+    if constexpr (QM == WM_BF16) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kk = k + u * 32;
-      const bool ok = kk < ke;
-      f16x8 bh[NT], bl[NT];
+      for (int u = 0; u < U; ++u) {
+        const int kk = k + u * 32;
+        const bool ok = kk < ke;
+        const f16x8 a = bf16x8_to_f16x8(f.wv[u]);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        bh[j] = (ok && xv[j]) ? *(const f16x8*)(xh[j] + kk) : f16x8{};
-        bl[j] = (ok && xv[j]) ? *(const f16x8*)(xl[j] + kk) : f16x8{};
-      }
-      f16x8 a;
-      if (QM == WM_Q8) {
-        a = i8x8_to_f16x8(f.qv[u]);
-      } else if (QM == WM_A4) {
-        a = u4x8_to_f16x8(f.q4[u]);
-      } else {
-        a = bf16x8_to_f16x8(f.wv[u]);
-      }
-      float sc[4] = {0.f, 0.f, 0.f, 0.f}, bs[4] = {0.f, 0.f, 0.f, 0.f};
-      if (QM == WM_A4) {
-        f16x4_bits_to_f32(f.sc[u], sc);
-        f16x4_bits_to_f32(f.bs[u], bs);
-      }
-      if (QM == WM_Q8) {
-        sc[0] = (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x & 0xFFFF));
-        sc[1] = (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x >> 16));
-        sc[2] = (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y & 0xFFFF));
-        sc[3] = (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y >> 16));
-      }
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        if (QM == WM_A4) {
-          a4_step(acc[j], a, bh[j], bl[j], sc, bs);
-        } else if (QM == WM_Q8) {
-          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
-          p = mfma16(a, bh[j], p);
-          p = mfma16(a, bl[j], p);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sc[r], p[r], acc[j][r]);
-        } else {
-          acc[j] = mfma16(a, bh[j], acc[j]);
-          acc[j] = mfma16(a, bl[j], acc[j]);
+        for (int j = 0; j < NT; ++j) {
+          const f16x8 bh = (ok && xv[j]) ? *(const f16x8*)(xh[j] + kk) : f16x8{};
+          const f16x8 bl = (ok && xv[j]) ? *(const f16x8*)(xl[j] + kk) : f16x8{};
+          acc[j] = mfma16(a, bh, acc[j]);
+          acc[j] = mfma16(a, bl, acc[j]);
         }
+      }
+    } else {
+      // four steps' block products at a time, then their scaled accumulation in step order
+      constexpr int G = 4;
+#pragma unroll
+      for (int u0 = 0; u0 < U; u0 += G) {
+        f32x4 p[G][NT], xs[G][NT];
+#pragma unroll
+        for (int v = 0; v < G; ++v) {
+          const int u = u0 + v, kk = k + u * 32;
+          const bool ok = kk < ke;
+          const f16x8 a = qwiden<QM>(f.qv[u], f.q4[u]);
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            const f16x8 bh = (ok && xv[j]) ? *(const f16x8*)(xh[j] + kk) : f16x8{};
+            const f16x8 bl = (ok && xv[j]) ? *(const f16x8*)(xl[j] + kk) : f16x8{};
+            qstep_products<QM>(a, bh, bl, p[v][j], xs[v][j]);
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < G; ++v)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) qstep_accumulate<QM>(acc[j], p[v][j], xs[v][j], f.sc[u0 + v], f.bs[u0 + v]);
       }
     }
   };
@@ -391,43 +384,42 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows_kernel(const uint16
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const Buf& f, int t) {
     const f16* xb = sx + (t & 1) * BUF + r16 * kRowsPitch + g4 * 8;
+    if constexpr (QM == WM_BF16) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (k0 + t * kRowsStageK + u * 32 >= ke) break;
-      f16x8 bh[NT], bl[NT];
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        bh[j] = *(const f16x8*)(xb + j * 16 * kRowsPitch + u * 32);
-        bl[j] = *(const f16x8*)(xb + j * 16 * kRowsPitch + kRowsStageK + u * 32);
-      }
-      f16x8 a;
-      if (QM == WM_A4) {
-        float sc[4], bs[4];
-        f16x4_bits_to_f32(f.sc[u], sc);
-        f16x4_bits_to_f32(f.bs[u], bs);
-        a = u4x8_to_f16x8(f.q4[u]);
-#pragma unroll
-        for (int j = 0; j < NT; ++j) a4_step(acc[j], a, bh[j], bl[j], sc, bs);
-      } else if (QM == WM_Q8) {
-        a = i8x8_to_f16x8(f.qv[u]);
-        const float sc[4] = {(float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x & 0xFFFF)),
-                             (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x >> 16)),
-                             (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y & 0xFFFF)),
-                             (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y >> 16))};
+      for (int u = 0; u < U; ++u) {
+        if (k0 + t * kRowsStageK + u * 32 >= ke) break;
+        const f16x8 a = bf16x8_to_f16x8(f.wv[u]);
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
-          p = mfma16(a, bh[j], p);
-          p = mfma16(a, bl[j], p);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sc[r], p[r], acc[j][r]);
+          const f16x8 bh = *(const f16x8*)(xb + j * 16 * kRowsPitch + u * 32);
+          const f16x8 bl = *(const f16x8*)(xb + j * 16 * kRowsPitch + kRowsStageK + u * 32);
+          acc[j] = mfma16(a, bh, acc[j]);
+          acc[j] = mfma16(a, bl, acc[j]);
         }
-      } else {
-        a = bf16x8_to_f16x8(f.wv[u]);
+      }
+    } else {
+      // four steps' block products at a time, then their scaled accumulation in step order
+      constexpr int G = 4;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          acc[j] = mfma16(a, bh[j], acc[j]);
-          acc[j] = mfma16(a, bl[j], acc[j]);
+      for (int u0 = 0; u0 < U; u0 += G) {
+        f32x4 p[G][NT], xs[G][NT];
+#pragma unroll
+        for (int v = 0; v < G; ++v) {
+          const int u = u0 + v;
+          if (k0 + t * kRowsStageK + u * 32 >= ke) break;
+          const f16x8 a = qwiden<QM>(f.qv[u], f.q4[u]);
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            const f16x8 bh = *(const f16x8*)(xb + j * 16 * kRowsPitch + u * 32);
+            const f16x8 bl = *(const f16x8*)(xb + j * 16 * kRowsPitch + kRowsStageK + u * 32);
+            qstep_products<QM>(a, bh, bl, p[v][j], xs[v][j]);
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < G; ++v) {
+          if (k0 + t * kRowsStageK + (u0 + v) * 32 >= ke) break;
+#pragma unroll
+          for (int j = 0; j < NT; ++j) qstep_accumulate<QM>(acc[j], p[v][j], xs[v][j], f.sc[u0 + v], f.bs[u0 + v]);
         }
       }
     }

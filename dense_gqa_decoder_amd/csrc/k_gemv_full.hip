@@ -150,35 +150,33 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
   const f16* xh = sx + (int64_t)(xvalid ? r16 : 0) * K + g4 * 8;
   const f16* xl = xh + BK;
   auto compute = [&](const Buf& f, int s) {
+    if constexpr (QM == WM_BF16) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (s + u < s1) {
-        const int kk = (s + u) * 32;
-        const f16x8 bh = xvalid ? *(const f16x8*)(xh + kk) : f16x8{};
-        const f16x8 bl = xvalid ? *(const f16x8*)(xl + kk) : f16x8{};
-        f16x8 w;
-        if (QM == WM_A4) {
-          float sc[4], bs[4];
-          f16x4_bits_to_f32(f.sc[u], sc);
-          f16x4_bits_to_f32(f.bs[u], bs);
-          a4_step(acc, u4x8_to_f16x8(f.q4[u]), bh, bl, sc, bs);
-        } else if (QM == WM_Q8) {
-          w = i8x8_to_f16x8(f.q[u]);
-          const float sc[4] = {(float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x & 0xFFFF)),
-                               (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].x >> 16)),
-                               (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y & 0xFFFF)),
-                               (float)__builtin_bit_cast(f16, (uint16_t)(f.sc[u].y >> 16))};
-          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
-          p = mfma16(w, bh, p);
-          p = mfma16(w, bl, p);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc[r], p[r], acc[r]);
-        } else {
-          w = bf16x8_to_f16x8(f.w[u]);
+      for (int u = 0; u < U; ++u) {
+        if (s + u < s1) {
+          const int kk = (s + u) * 32;
+          const f16x8 bh = xvalid ? *(const f16x8*)(xh + kk) : f16x8{};
+          const f16x8 bl = xvalid ? *(const f16x8*)(xl + kk) : f16x8{};
+          const f16x8 w = bf16x8_to_f16x8(f.w[u]);
           acc = mfma16(w, bh, acc);
           acc = mfma16(w, bl, acc);
         }
       }
+    } else {
+      // every step's block products first, then the scaled accumulation in step order
+      f32x4 p[U], xs[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s + u < s1) {
+          const int kk = (s + u) * 32;
+          const f16x8 bh = xvalid ? *(const f16x8*)(xh + kk) : f16x8{};
+          const f16x8 bl = xvalid ? *(const f16x8*)(xl + kk) : f16x8{};
+          qstep_products<QM>(qwiden<QM>(f.q[u], f.q4[u]), bh, bl, p[u], xs[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (s + u < s1) qstep_accumulate<QM>(acc, p[u], xs[u], f.sc[u], f.bs[u]);
     }
   };
   for (int s = s0; s < s1; s += 2 * U) {
