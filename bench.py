@@ -259,7 +259,8 @@ def main():
 
     # Multi-row evaluation of the same prompt, outside the step: every row's logits (eval_n) and
     # the prompt's next-token scores (eval_scored), median of three, HIP events on the stream;
-    # then the lm_head launches over groups of up to 32 rows, timed like the kernels above.
+    # then the lm_head launches (for a round of more than 32 rows one GEMM over all its rows, else
+    # the matvec over groups of up to 32 rows), timed like the kernels above.
     host_ids = synth.token_ids(wl.ids_seed, wl.prompt)
     rows_lg = torch.empty((wl.prompt, shape.vocab), device="cuda")
     rows_am = torch.empty(wl.prompt, dtype=torch.int32, device="cuda")
@@ -285,8 +286,10 @@ def main():
     n_lm, lm_ms, _ = m.profile_read()
     m.profile("none")
     lm_ms /= max(n_lm, 1)
-    lm_rows = min(32, wl.prompt)
+    lm_gemm = min(m.info().round_tokens, wl.prompt) > 32
+    lm_rows = wl.prompt // max(n_lm, 1)                    # rows per launch
     lm_bytes = shape.vocab * shape.hidden * 2 + lm_rows * shape.hidden * 4 + lm_rows * shape.vocab * 4
+    lm_flop = 2.0 * lm_rows * shape.hidden * shape.vocab
     del rows_lg
 
     # Prefix reuse (pooled sessions): time to the first logits of a PREFIX_PROMPT-token prompt
@@ -351,10 +354,13 @@ def main():
         "multi_row": {"rows": wl.prompt, "eval_n_ms": round(evn_ms, 3),
                       "eval_n_tok_s": round(wl.prompt / (evn_ms * 1e-3), 1),
                       "eval_scored_ms": round(evs_ms, 3),
-                      "lm_head_group": {"rows": lm_rows, "launches": n_lm, "launch_us": round(lm_ms * 1e3, 2),
-                                        "bytes_per_launch": lm_bytes,
-                                        "achieved_gbs": round(lm_bytes / (lm_ms * 1e-3) / 1e9, 1),
-                                        "frac_hbm_peak": round(lm_bytes / (lm_ms * 1e-3) / PEAK_HBM, 4)}},
+                      "lm_head": {"kernel": "gemm_kernel (FP16 hi/lo, padded vocab)" if lm_gemm else "gemv_rows_kernel",
+                                  "bound": "mfma" if lm_gemm else "hbm", "rows_per_launch": lm_rows,
+                                  "launches": n_lm, "launch_us": round(lm_ms * 1e3, 2),
+                                  "achieved_tflops": round(lm_flop / (lm_ms * 1e-3) / 1e12, 1),
+                                  "frac_mfma_peak": round(lm_flop / (lm_ms * 1e-3) / PEAK_BF16_FLOPS, 4),
+                                  "bytes_per_launch": lm_bytes,
+                                  "achieved_gbs": round(lm_bytes / (lm_ms * 1e-3) / 1e9, 1)}},
         "prefix_reuse": {"prompt": PREFIX_PROMPT, "reused_positions": reused[1], "ttft_cold_ms": round(cold_ms, 3),
                          "ttft_warm_ms": round(warm_ms, 3), "speedup": round(cold_ms / warm_ms, 1)},
         "commit": rev, "dirty": dirty, "device": torch.cuda.get_device_name(0),

@@ -344,6 +344,57 @@ hipError_t launch_table_writes(int32_t* table, const TableWrites& t, hipStream_t
   return hipGetLastError();
 }
 
+// argmax of each of `rows` logit rows (row stride ld) read in full; ties go to the lowest index,
+// and a row with no value above -inf (all NaN) gives -1.
+__global__ __launch_bounds__(1024) void argmax_rows_kernel(const float* __restrict__ logits, int V, int64_t ld,
+                                                           int32_t* __restrict__ out) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const float* l = logits + (int64_t)blockIdx.x * ld;
+  float best = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int i = threadIdx.x * 4; i < V; i += 1024 * 4) {        // V % 4 == 0
+    const float4 v = *(const float4*)(l + i);
+    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (e[u] > best) {                                       // first index of the thread's maximum
+        best = e[u];
+        bi = i + u;
+      }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ov > best || (ov == best && oi < bi)) {
+      best = ov;
+      bi = oi;
+    }
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sv[threadIdx.x >> 6] = best;
+    si[threadIdx.x >> 6] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    best = sv[0];
+    bi = si[0];
+    for (int k = 1; k < 16; ++k)
+      if (sv[k] > best || (sv[k] == best && si[k] < bi)) {
+        best = sv[k];
+        bi = si[k];
+      }
+    out[blockIdx.x] = bi == 0x7FFFFFFF ? -1 : bi;
+  }
+}
+
+hipError_t launch_argmax_rows(const float* logits, int V, int64_t ld, int rows, int32_t* out, hipStream_t st) {
+  if (rows < 1 || V % 4 != 0 || ld % 4 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(argmax_rows_kernel, dim3(rows), dim3(1024), 0, st, logits, V, ld, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_argmax(const float2* cand, int ntiles, int B, int32_t* out, hipStream_t st) {
   hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(1024), 0, st, cand, ntiles, out);
   return hipGetLastError();

@@ -52,6 +52,7 @@ struct GemmArgs {
   float m_scale;
   int ksplit;                // K ranges (EPI_STORE only): range s writes C + s * split_stride
   int64_t split_stride;
+  int Nvalid;                // EPI_STORE: columns >= Nvalid are not stored (N padded to the tile)
 };
 
 constexpr int kGemmBN = 256, kGemmBT = 128, kGemmBK = 32;
@@ -275,6 +276,7 @@ __global__ __launch_bounds__(256, Q8 ? 1 : 2) void gemm_kernel(GemmArgs g) {
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          if (EPI == EPI_STORE && nbase + 8 * q >= g.Nvalid) continue;   // Nvalid % 4 == 0
           float4* dst = (float4*)&Cout[(int64_t)t * g.ldc + nbase + 8 * q];
           float4 v = make_float4(acc[i][j][q * 4 + 0] * g.out_scale, acc[i][j][q * 4 + 1] * g.out_scale,
                                  acc[i][j][q * 4 + 2] * g.out_scale, acc[i][j][q * 4 + 3] * g.out_scale);
@@ -308,12 +310,16 @@ static hipError_t launch_gemm_t(int epi, const GemmArgs& a, hipStream_t st) {
 // split: FP16 hi/lo activations (two MFMAs per operand pair); otherwise hi only.
 // ksplit > 1 (EPI_STORE only): the K steps are cut into ksplit consecutive ranges and range s
 // stores its partial product at C + s * split_stride; the consumer sums them in range order.
+// nvalid (EPI_STORE): only columns below it are stored (0: all N); a multiple of 4.
 hipError_t launch_gemm(int epi, bool split, const f16* W, const int8_t* Wq, const f16* Wd, int K, int N,
                        const f16* Xhi, const f16* Xlo, int ldx, int T, float* C, int ldc, float out_scale, f16* Mhi,
-                       f16* Mlo, int ldm, float m_scale, int ksplit, int64_t split_stride, hipStream_t st) {
+                       f16* Mlo, int ldm, float m_scale, int ksplit, int64_t split_stride, hipStream_t st, int nvalid) {
   if (N % kGemmBN != 0 || K % kGemmBK != 0 || T <= 0) return hipErrorInvalidValue;
   if (ksplit < 1 || ksplit > K / kGemmBK || (ksplit > 1 && epi != EPI_STORE)) return hipErrorInvalidValue;
-  GemmArgs a{W, Wq, Wd, K, N, Xhi, Xlo, ldx, T, C, ldc, out_scale, Mhi, Mlo, ldm, m_scale, ksplit, split_stride};
+  if (nvalid == 0) nvalid = N;
+  if (nvalid % 4 != 0 || nvalid > N || (nvalid != N && epi != EPI_STORE)) return hipErrorInvalidValue;
+  GemmArgs a{W, Wq, Wd, K, N, Xhi, Xlo, ldx, T, C, ldc, out_scale, Mhi, Mlo, ldm, m_scale, ksplit, split_stride,
+             nvalid};
   if (Wq) return split ? launch_gemm_t<true, true>(epi, a, st) : launch_gemm_t<true, false>(epi, a, st);
   return split ? launch_gemm_t<false, true>(epi, a, st) : launch_gemm_t<false, false>(epi, a, st);
 }

@@ -40,6 +40,7 @@ hipError_t launch_qk_rope_kv(bool decode, const float* qkv, int nsplit, int part
                              const float* rsin, int pos0, const int32_t* table0, const Rows& rows, uint16_t* kpool,
                              uint16_t* vpool, float* qout, int nrows, hipStream_t st);
 hipError_t launch_argmax(const float2* cand, int ntiles, int B, int32_t* out, hipStream_t st);
+hipError_t launch_argmax_rows(const float* logits, int V, int64_t ld, int rows, int32_t* out, hipStream_t st);
 hipError_t launch_score(const float* logits, int V, const int32_t* targets, int B, float* out, hipStream_t st);
 hipError_t launch_table_writes(int32_t* table, const TableWrites& t, hipStream_t st);
 hipError_t launch_swiglu_rows(const float* gu, int nsplit, int64_t stride, int ldgu, int F, int rows, f16* mh, f16* ml,
@@ -47,7 +48,8 @@ hipError_t launch_swiglu_rows(const float* gu, int nsplit, int64_t stride, int l
 hipError_t launch_prefill_copy(const uint16_t* src, f16* dst, int64_t rows, int64_t cols, hipStream_t st);
 hipError_t launch_gemm(int epi, bool split, const f16* W, const int8_t* Wq, const f16* Wd, int K, int N, const f16* Xhi,
                        const f16* Xlo, int ldx, int T, float* C, int ldc, float out_scale, f16* Mhi, f16* Mlo,
-                       int ldm, float m_scale, int ksplit, int64_t split_stride, hipStream_t st);
+                       int ldm, float m_scale, int ksplit, int64_t split_stride, hipStream_t st,
+                       int nvalid = 0);
 hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, const f16* Wb, int K, int N, const XSrc& xs, int B,
                        int nsplit, float* P, int64_t part_stride, int ldp, float2* cand, hipStream_t st,
                        bool staged = false);
@@ -106,6 +108,9 @@ float weight_scale() { return (float)(0.02 / sqrt(4.0 * (65536.0 * 65536.0 - 1.0
 // projection result is divided by it), keeping the FP16 lo half of small outputs normal.
 constexpr float kAttnOutScale = 16.0f;
 
+// Rows of one scoring GEMM (the logits scratch holds this many rows).
+constexpr int kScoreRows = 256;
+
 struct LayerW {
   uint16_t *attn_norm = nullptr, *ffn_norm = nullptr, *q_norm = nullptr, *k_norm = nullptr;
   uint16_t *wqkv = nullptr, *wo = nullptr, *wgu = nullptr, *wd = nullptr;                  // BF16
@@ -125,6 +130,8 @@ struct gqa_model {
   int s_qkv = 1, s_o = 1, s_gu = 1, s_d = 1;  // decode split-K counts
   std::vector<LayerW> L;
   uint16_t *embed = nullptr, *lm_head = nullptr, *final_norm = nullptr;
+  f16* plm = nullptr;           // FP16 prefill copy of the lm_head, rows padded with zeros to Vpad
+  int Vpad = 0;                 // vocab rounded up to the GEMM's 256-row tile
   float *rcos = nullptr, *rsin = nullptr;
   float *x = nullptr, *x2 = nullptr, *qkv = nullptr, *q = nullptr, *part = nullptr, *part2 = nullptr,
         *apart = nullptr;
@@ -132,7 +139,7 @@ struct gqa_model {
   int32_t* counters = nullptr;  // decode attention: finished chunks per (row, KV head)
   float* ss = nullptr;          // decode: sum-of-squares partials [2][8][32] (q|k|v input, gate|up input)
   float2* cand = nullptr;   // lm_head argmax candidates [32][vocab / 16]
-  float* slog = nullptr;    // logits of up to 32 rows being scored [32][vocab]
+  float* slog = nullptr;    // logits of up to kScoreRows rows being scored [kScoreRows][vocab]
   f16 *xh = nullptr, *xl = nullptr, *oh = nullptr, *ol = nullptr, *mh = nullptr, *ml = nullptr;
   int32_t *ids_dev = nullptr, *err = nullptr;
   int32_t* ids_host = nullptr;  // pinned staging
@@ -338,7 +345,9 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   ALLOC(m->ss, 2 * 8 * 32, sb);
   ALLOC(m->ids_dev, std::max(d.max_positions, kMaxBatch), sb);
   ALLOC(m->cand, (int64_t)kMaxBatch * (V / 16), sb);
-  ALLOC(m->slog, (int64_t)kMaxBatch * V, sb);
+  ALLOC(m->slog, (int64_t)kScoreRows * V, sb);
+  m->Vpad = (V + 255) / 256 * 256;
+  ALLOC(m->plm, (int64_t)m->Vpad * H, &m->prefill_copy_bytes);
   ALLOC(m->err, 1, sb);
   ALLOC(m->rcos, (int64_t)d.max_positions * 64, sb);
   ALLOC(m->rsin, (int64_t)d.max_positions * 64, sb);
@@ -378,6 +387,8 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   };
   chk(gen(m->embed, GQA_T_EMBED, -1, V, H, 0, 0));
   if (!d.tied) chk(gen(m->lm_head, GQA_T_LM_HEAD, -1, V, H, 0, 0));
+  chk(launch_prefill_copy(m->lm_head, m->plm, V, H, st));
+  chk(hipMemsetAsync(m->plm + (int64_t)V * H, 0, (size_t)(m->Vpad - V) * H * 2, st));
   chk(launch_fill_u16(m->final_norm, H, 0x3F80, st));
   const int KVD = kKvHeads * kHeadDim;
   for (int l = 0; l < d.n_layers && ge == hipSuccess; ++l) {
@@ -933,7 +944,28 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
       const uint16_t* next_norm = last ? m->final_norm : m->L[l + 1].attn_norm;
       LAUNCH(launch_rmsnorm(m->x + (int64_t)r0 * H, H, pp, sd, rows * H, H, 1.f, next_norm, H, eps, 1.f, m->xh, m->xl,
                             H, rows, st));
-      if (last) {
+      if (last && out != kOutLast && !mv) {
+        // lm_head over every row of a GEMM round: one GEMM over the padded FP16 copy (only the
+        // vocab's columns stored); scores go through the logits scratch kScoreRows rows at a time
+        if (out == kOutAll) {
+          ProfScope ps(m, GQA_PROF_ROWS_LMHEAD, st);
+          LAUNCH(launch_gemm(EPI_STORE, split, m->plm, nullptr, nullptr, H, m->Vpad, m->xh, m->xl, H, rows,
+                             logits + (int64_t)off * V, V, 1.f, nullptr, nullptr, 0, 1.f, 1, 0, st, V));
+          if (argmax) LAUNCH(launch_argmax_rows(logits + (int64_t)off * V, V, V, rows, argmax + off, st));
+        } else {
+          for (int c0 = 0; c0 < rows; c0 += kScoreRows) {
+            const int i0 = off + c0, Bc = std::min(std::min(kScoreRows, rows - c0), n - 1 - i0);
+            if (Bc < 1) break;
+            {
+              ProfScope ps(m, GQA_PROF_ROWS_LMHEAD, st);
+              LAUNCH(launch_gemm(EPI_STORE, split, m->plm, nullptr, nullptr, H, m->Vpad, m->xh + (int64_t)c0 * H,
+                                 m->xl + (int64_t)c0 * H, H, Bc, m->slog, V, 1.f, nullptr, nullptr, 0, 1.f, 1, 0, st,
+                                 V));
+            }
+            LAUNCH(launch_score(m->slog, V, ids_dev + i0 + 1, Bc, scores + i0, st));
+          }
+        }
+      } else if (last) {
         // lm_head over the rows, up to 32 at a time (the batched decode matvec)
         for (int g0 = 0; g0 < rows; g0 += kMaxBatch) {
           const int i0 = off + r0 + g0;                       // call-relative index of the group's first row
