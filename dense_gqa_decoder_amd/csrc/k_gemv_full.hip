@@ -60,11 +60,8 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
       const int64_t ch = chunk0 + min(s + u, s1 - 1);     // unconditional: no branch between loads
       if (QM == WM_Q8) {
         f.q[u] = *(const uint2*)(a.Wq + ch * 512 + lane * 8);
-        f.sc[u] = *(const uint2*)(a.Wd + ch * 16 + g4 * 4);
       } else if (QM == WM_A4) {
         f.q4[u] = *(const uint32_t*)(a.Wq + ch * 256 + lane * 4);
-        f.sc[u] = *(const uint2*)(a.Wd + ch * 16 + g4 * 4);
-        f.bs[u] = *(const uint2*)(a.Wb + ch * 16 + g4 * 4);
       } else {
         f.w[u] = *(const uint4*)(a.W + ch * 512 + lane * 8);
       }
@@ -73,6 +70,21 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
   Buf b0, b1;
   fetch(b0, s0);
   fetch(b1, s0 + U);
+
+  // Q8_0 / AFFINE4: the scales (and biases) of the workgroup's bands, staged in LDS once, in their
+  // memory order [band][K-step][16 rows] after the operand rows, so the weight stream issues one
+  // load per lane and step (the scale reads, repeated by the 16 token lanes, come from LDS).
+  f16* const ssc = sx + 2 * B * K + 8;
+  f16* const sbs = ssc + NBW * KS * 16;
+  if constexpr (QM != WM_BF16) {
+    const int per = KS * 2;                             // 16-byte pieces per band
+    for (int i = tid; i < NBW * per; i += NT) {
+      const int bb = i / per, c = i - bb * per;
+      const int64_t src = (int64_t)(blockIdx.x * NBW + bb) * KS * 16 + c * 8;
+      *(uint4*)(ssc + bb * KS * 16 + c * 8) = *(const uint4*)(a.Wd + src);
+      if (QM == WM_A4) *(uint4*)(sbs + bb * KS * 16 + c * 8) = *(const uint4*)(a.Wb + src);
+    }
+  }
 
   // ---- operand rows into LDS: [0][b][k] = hi, [1][b][k] = lo
   const int BK = B * K;
@@ -176,7 +188,10 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (s + u < s1) qstep_accumulate<QM>(acc, p[u], xs[u], f.sc[u], f.bs[u]);
+        if (s + u < s1) {
+          const int at = (bw * KS + s + u) * 16 + g4 * 4;
+          qstep_accumulate<QM>(acc, p[u], xs[u], *(const uint2*)(ssc + at), *(const uint2*)(sbs + at));
+        }
     }
   };
   for (int s = s0; s < s1; s += 2 * U) {
@@ -276,12 +291,13 @@ hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStre
   const size_t shm = (size_t)4 * a.B * a.K + 16;
 #define FULL(Q, NWB, NBW, U, MO, EP)                                                                          \
   do {                                                                                                        \
+    const size_t shm_ = shm + (Q == WM_BF16 ? 0 : (size_t)NBW * (a.K / 32) * 32 * (Q == WM_A4 ? 2 : 1));    \
     if (a.B == 1 && (size_t)4 * a.K + 16 <= kFullMaxLds / 4)                                                  \
       GQA_LAUNCH((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, 1>), dim3(a.N / 16 / NBW),                         \
-                 dim3(64 * NWB * NBW), shm, st, a);                                                            \
+                 dim3(64 * NWB * NBW), shm_, st, a);                                                           \
     else                                                                                                      \
       GQA_LAUNCH((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, kFullMaxB>), dim3(a.N / 16 / NBW),                 \
-                 dim3(64 * NWB * NBW), shm, st, a);                                                            \
+                 dim3(64 * NWB * NBW), shm_, st, a);                                                           \
   } while (0)
 #define BY_QM(NWB, NBW, U, MO, EP)        \
   do {                                    \
