@@ -71,6 +71,9 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
+constexpr int kDecodeMaxChunks = 64;
+constexpr int kPartStride = 132;   // floats per chunk partial: m, l, pad, pad, o[128]
+
 // LDS of the prefill kernel. A staged tile holds KT keys. K tile: 8 planes, one per 16-dim step
 // st, each KT rows x 32 bytes, the two 16-byte halves of row r swapped when bit 3 of r is set
 // (16 consecutive rows read at one half then cover all 64 banks). V tile: 4 planes, one per
@@ -90,12 +93,17 @@ struct PrefillLds {
   static constexpr int BYTES = AREA + MAX_BLOCKS * 4;
 };
 
+// part == nullptr: o of each query row written as FP16 hi/lo. Otherwise (one query tile, T <= 32)
+// the keys are split over gridDim.y workgroups: split c takes its share of the key tiles and
+// writes, per query row t and head h, the partial (m, l, o[128]) of its keys at
+// part[((t * nq + h) * kDecodeMaxChunks + c) * kPartStride] (the decode chunk-partial layout; m in
+// log2 units, o relative to m), merged afterwards by attn_merge_rows_kernel.
 template <int G, bool PSPLIT>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restrict__ q, int nq, int T, int pos0,
                                                            const int32_t* __restrict__ table,
                                                            const uint16_t* kpool, const uint16_t* vpool,
                                                            float out_scale, f16* __restrict__ ohi,
-                                                           f16* __restrict__ olo, int ldo) {
+                                                           f16* __restrict__ olo, int ldo, float* __restrict__ part) {
   using L = PrefillLds<G>;
   constexpr int NS = L::NS, KT = L::KT, TILE = L::TILE, KPLANE = L::KPLANE, VPLANE = L::VPLANE;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[L::BYTES / 2];
@@ -138,7 +146,11 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
     const int t0 = qt * 32;
     const int qfirst = pos0 + t0, qlast = pos0 + min(t0 + 32, T) - 1;
     const int kend = qlast + 1;
-    const int ntile = (kend + KT - 1) / KT;
+    const int ntile_all = (kend + KT - 1) / KT;
+    // this workgroup's key tiles [tb, ntile): all of them, or split c's share
+    const int per_split = (ntile_all + gridDim.y - 1) / gridDim.y;
+    const int tb = part ? min((int)blockIdx.y * per_split, ntile_all) : 0;
+    const int ntile = part ? min(tb + per_split, ntile_all) : ntile_all;
     const int myq = pos0 + min(t0 + c32, T - 1);
 
     // Pipeline over staged tiles: iteration t needs K(t + 1) (for S(t + 1)) and V(t) (for
@@ -168,9 +180,11 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
       }
     };
     // first copies, then the Q loads (their latencies overlap)
-    issue_k(0);
-    issue_v(0);
-    if (ntile > 1) issue_k(1);
+    if (tb < ntile) {
+      issue_k(tb);
+      issue_v(tb);
+      if (tb + 1 < ntile) issue_k(tb + 1);
+    }
 
     // Q^T operand: lane holds query c32, dims 16 st + 8 hf .. +7, pre-scaled, as BF16 hi/lo
     bf16v8 qh[8], ql[8];
@@ -213,10 +227,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
       return sc;
     };
 
-    vm_wait_all();                     // K(0) (and everything else issued so far)
+    vm_wait_all();                     // K(tb) (and everything else issued so far)
     __syncthreads();
-    f32x16 sc = scores(0);
-    for (int t = 0; t < ntile; ++t) {
+    f32x16 sc = scores(tb);
+    for (int t = tb; t < ntile; ++t) {
       vm_wait_all();                   // this wave's copies of K(t + 1) and V(t)
       __syncthreads();                 // ... and every wave's; the buffers of K(t), V(t - 1) are free
       if (t + 2 < ntile) issue_k(t + 2);
@@ -334,7 +348,24 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
 #pragma unroll
             for (int e = 0; e < 16; ++e) o[dt][e] = fmaf(sk[(2 + dt * 16 + e) * 64], w, o[dt][e]);
         }
-        store(Ls);
+        if (part) {
+          const int t = t0 + c32;
+          if (t < T) {
+            float* pp = part + (((int64_t)t * nq + head) * kDecodeMaxChunks + blockIdx.y) * kPartStride;
+            if (hf == 0) {
+              pp[0] = M;
+              pp[1] = Ls;
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4)
+                *(float4*)(pp + 4 + dt * 32 + 8 * g4 + 4 * hf) =
+                    make_float4(o[dt][4 * g4], o[dt][4 * g4 + 1], o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]);
+          }
+        } else {
+          store(Ls);
+        }
       }
       __syncthreads();                 // the merge area is the next query tile's K/V buffer
     }
@@ -359,8 +390,6 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
 //     chunk order (merge_head).
 constexpr int kDecodeWaves = 4;
 constexpr int kBatchChunksPerWorkgroup = 4;
-constexpr int kDecodeMaxChunks = 64;
-constexpr int kPartStride = 132;   // floats per chunk partial: m, l, pad, pad, o[128]
 
 __host__ __device__ __forceinline__ int decode_chunk_len(int ctx) {
   return 64 * ((ctx + 64 * kDecodeMaxChunks - 1) / (64 * kDecodeMaxChunks));
@@ -783,21 +812,48 @@ __global__ __launch_bounds__(64 * G) void attn_merge_kernel(const float* __restr
                     ohi + (int64_t)b * ldo + h * kHeadDim, olo + (int64_t)b * ldo + h * kHeadDim);
 }
 
+// Merge of a split prefill attention: grid (KV head, query row), one wave per query head of the
+// group; the same arithmetic as the decode chunk merge.
+template <int G>
+__global__ __launch_bounds__(64 * G) void attn_merge_rows_kernel(const float* __restrict__ part, int nq, int nchunk,
+                                                                float out_scale, f16* __restrict__ ohi,
+                                                                f16* __restrict__ olo, int ldo) {
+  const int kvh = blockIdx.x, t = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = kvh * G + wave;
+  merge_head<false>(part + ((int64_t)t * nq + h) * kDecodeMaxChunks * kPartStride, nchunk, lane, out_scale,
+                    ohi + (int64_t)t * ldo + h * kHeadDim, olo + (int64_t)t * ldo + h * kHeadDim);
+}
+
+// part (optional): chunk-partial scratch for up to 32 rows (attn_decode_part_floats). With it, a
+// round of at most 32 rows over a long context splits the keys over several workgroups per KV
+// head (a single query tile would otherwise run on eight workgroups) and merges them after.
 hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const int32_t* table, const uint16_t* kpool,
-                               const uint16_t* vpool, float out_scale, f16* ohi, f16* olo, int ldo, hipStream_t st) {
+                               const uint16_t* vpool, float out_scale, f16* ohi, f16* olo, int ldo, float* part,
+                               hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if ((pos0 + T + 31) / 32 > PrefillLds<4>::MAX_BLOCKS) return hipErrorInvalidValue;   // context too long
   const int G = nq / kKvHeads;
+  if (G != 4 && G != 2) return hipErrorInvalidValue;
   const int pairs = ((T + 31) / 32 + 1) / 2;
-  const dim3 grid(pairs * kKvHeads);
-  if (G == 4) {
-    GQA_LAUNCH((attn_prefill_kernel<4, true>), grid, dim3(512), 0, st, q, nq, T, pos0, table, kpool, vpool,
-                       out_scale, ohi, olo, ldo);
-  } else if (G == 2) {
-    GQA_LAUNCH((attn_prefill_kernel<2, true>), grid, dim3(512), 0, st, q, nq, T, pos0, table, kpool, vpool,
-                       out_scale, ohi, olo, ldo);
-  } else {
-    return hipErrorInvalidValue;
+  // key splits: about four 64-key tiles each, at most kDecodeMaxChunks
+  const int kt = G == 4 ? PrefillLds<4>::KT : PrefillLds<2>::KT;
+  const int ntile = (pos0 + T + kt - 1) / kt;
+  const int csplit = (part && T <= 32) ? std::min(kDecodeMaxChunks, std::max(1, (ntile * kt + 255) / 256)) : 1;
+  float* const pp = csplit > 1 ? part : nullptr;
+  const dim3 grid(pairs * kKvHeads, csplit);
+  if (G == 4)
+    GQA_LAUNCH((attn_prefill_kernel<4, true>), grid, dim3(512), 0, st, q, nq, T, pos0, table, kpool, vpool, out_scale,
+               ohi, olo, ldo, pp);
+  else
+    GQA_LAUNCH((attn_prefill_kernel<2, true>), grid, dim3(512), 0, st, q, nq, T, pos0, table, kpool, vpool, out_scale,
+               ohi, olo, ldo, pp);
+  if (pp) {
+    if (G == 4)
+      hipLaunchKernelGGL(attn_merge_rows_kernel<4>, dim3(kKvHeads, T), dim3(256), 0, st, pp, nq, csplit, out_scale, ohi,
+                         olo, ldo);
+    else
+      hipLaunchKernelGGL(attn_merge_rows_kernel<2>, dim3(kKvHeads, T), dim3(128), 0, st, pp, nq, csplit, out_scale, ohi,
+                         olo, ldo);
   }
   return hipGetLastError();
 }

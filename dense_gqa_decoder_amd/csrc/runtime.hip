@@ -58,7 +58,8 @@ bool gemv_full_fits(int K, int B);
 hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStream_t st);
 hipError_t launch_final_norm(const XSrc& xs, int B, f16* yhi, f16* ylo, int ldy, hipStream_t st);
 hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const int32_t* table, const uint16_t* kpool,
-                               const uint16_t* vpool, float out_scale, f16* ohi, f16* olo, int ldo, hipStream_t st);
+                               const uint16_t* vpool, float out_scale, f16* ohi, f16* olo, int ldo, float* part,
+                               hipStream_t st);
 hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* ss,
                               int ss_n, int H, const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
                               const float* rsin, const Rows& rows, int B, int max_ctx, uint16_t* kpool,
@@ -909,7 +910,7 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
       {
         ProfScope ps(m, last ? kProfNever : GQA_PROF_PREFILL_ATTN, st);
         LAUNCH(launch_attn_prefill(m->q + (int64_t)r0 * QD, NQ, rows, pos0 + r0, s->d_table, w.kpool, w.vpool,
-                                   kAttnOutScale, m->oh, m->ol, QD, st));
+                                   kAttnOutScale, m->oh, m->ol, QD, m->apart, st));
       }
       float* pp = mv ? m->part2 : m->ppart;     // o and down partials
       int so = 0, sd = 0;

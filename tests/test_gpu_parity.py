@@ -725,6 +725,81 @@ def test_eval_scored_parity(g):
         o.close()
 
 
+def test_multi_row_edges(g):
+    """Edges of multi-row evaluation (tiny decoder, rounds of 48): n = 1, 32 (the largest matvec
+    round), 33 (the smallest GEMM round, lm_head over the padded vocabulary) and 48 (a full
+    round) rows of eval_n against the oracle; eval_scored with n = 2 (one score); eval_n on a
+    pooled session; a session filled to its last position, after which one more token is a
+    context overflow that leaves the position unchanged."""
+    wl = synth.WORKLOADS["tiny"]
+    shape = wl.shape
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=32, max_positions=256, max_round_tokens=48)
+    om_ = oracle.OracleModel(shape, wl.weight_seed)
+    gate = Gate("multi-row edges")
+    k = 0
+    for n in (1, 32, 33, 48):
+        ids = synth.token_ids(90 + n, n)
+        ref = oracle.OracleSession(om_, oracle.ContiguousKV.for_shape(shape, 64)).forward(ids, all_logits=True)
+        s = g.Session(m, 64)
+        lg, am = _rows(s, ids, shape.vocab)
+        for i in range(n):
+            gate.check(k, lg[i], ref[i], int(am[i]))
+            assert am[i] == int(np.argmax(lg[i]))
+            k += 1
+        s.close()
+    ids = synth.token_ids(95, 2)
+    s = g.Session(m, 64)
+    sc = _scores(s, ids)
+    r = oracle.OracleSession(om_, oracle.ContiguousKV.for_shape(shape, 8)).score(ids)
+    assert sc.shape == (1,) and abs(sc[0] - r[0]) < 2e-2
+    s.close()
+    ids = synth.token_ids(96, 40)
+    ref = oracle.OracleSession(om_, oracle.ContiguousKV.for_shape(shape, 64)).forward(ids, all_logits=True)
+    ps = g.Session(m, 64, pooled=True)
+    lg, am = _rows(ps, ids, shape.vocab)
+    for i in range(40):
+        gate.check(k, lg[i], ref[i], int(am[i]))
+        k += 1
+    ps.close()
+    gate.assert_ok()
+    full = g.Session(m, 40)
+    _prefill(full, synth.token_ids(97, 40), shape.vocab)
+    assert full.position == 40
+    with pytest.raises(g.GqaError):
+        full.decode(5, torch.empty(shape.vocab, device="cuda"))
+    with pytest.raises(g.GqaError):
+        full.eval_n([1, 2], torch.empty((2, shape.vocab), device="cuda"))
+    assert full.position == 40
+    full.close()
+    m.close()
+
+
+def test_short_round_after_long_context(g):
+    """A round of few rows over a long context splits its keys over several workgroups per KV
+    head and merges the partials: the tiny decoder prefills 2,000 ids, then evaluates 10 more
+    (eval_n: 2,010 keys, 8 key splits) and 1 more through eval_prefill; every row against the
+    oracle's logits of the same positions (gate)."""
+    wl = synth.WORKLOADS["tiny"]
+    shape = wl.shape
+    ids = synth.token_ids(98, 2011)
+    say("short round oracle")
+    ref = oracle.OracleSession(oracle.OracleModel(shape, wl.weight_seed),
+                               oracle.ContiguousKV.for_shape(shape, 2048)).forward(ids, all_logits=True)
+    nb = synth.blocks_for(2048)
+    m = g.Model.from_shape(shape, seed=wl.weight_seed, kv_pool_blocks=2 * nb, max_positions=nb * 32)
+    s = g.Session(m, nb * 32, block_ids=synth.shuffled_blocks(99, 2 * nb)[:nb])
+    _prefill(s, ids[:2000], shape.vocab)
+    lg, am = _rows(s, ids[2000:2010], shape.vocab)
+    last, last_am = _prefill(s, ids[2010:], shape.vocab)
+    gate = Gate("short round after a long context")
+    for i in range(10):
+        gate.check(2000 + i, lg[i], ref[2000 + i], int(am[i]))
+    gate.check(2010, last, ref[2010], last_am)
+    gate.assert_ok()
+    s.close()
+    m.close()
+
+
 def test_truncate_resume_parity(g):
     """Truncate/resume (Kipp Model Support, "What the gates check"): prefill 40 ids, evaluate 20
     more, truncate back to 40, then evaluate 11 new ids (all rows) and 3 greedy decode steps over
