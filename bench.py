@@ -151,6 +151,50 @@ def pmc_workload(n_decode):
           flush=True)
 
 
+def pmc_batch_workload(n_steps):
+    """The 8B batched workload without torch, for rocprofv3 --pmc passes: 32 sessions of contexts
+    L_i ~ U{512..8192} prefilled alone, then n_steps batched decode steps of all 32."""
+    import ctypes
+    import dense_gqa_decoder_amd as g
+    import synth
+    g.load()
+    hip = ctypes.CDLL("libamdhip64.so.7")
+
+    class DevBuf:
+        def __init__(self, nbytes):
+            p = ctypes.c_void_p()
+            if hip.hipMalloc(ctypes.byref(p), ctypes.c_size_t(nbytes)) != 0 or \
+                    hip.hipMemset(p, 0, ctypes.c_size_t(nbytes)) != 0:
+                raise RuntimeError("hipMalloc failed")
+            self.p = p.value
+
+        def data_ptr(self):
+            return self.p
+
+    class NullStream:
+        cuda_stream = None
+
+    wl = synth.WORKLOADS["8b-batch"]
+    lens = [int(x) for x in synth.context_lengths(synth.CONTEXT_SEED_8B, wl.n_seqs)]
+    need = sum(synth.blocks_for(n + n_steps) for n in lens)
+    m = g.Model.from_shape(wl.shape, seed=wl.weight_seed, kv_pool_blocks=need + 64, max_positions=8192 + n_steps)
+    lg, am = DevBuf(wl.shape.vocab * 4), DevBuf(4)
+    sess = []
+    for i, n in enumerate(lens):
+        se = g.Session(m, n + n_steps)
+        se.prefill(synth.token_ids(wl.ids_seed, n, offset=i * 8192), lg, am, NullStream)
+        sess.append(se)
+    blg, bam = DevBuf(len(sess) * wl.shape.vocab * 4), DevBuf(len(sess) * 4)
+    for _ in range(n_steps):
+        m.eval_batch(sess, bam, blg, bam, NullStream)
+    if hip.hipDeviceSynchronize() != 0:
+        raise RuntimeError("batched workload failed")
+    for se in sess:
+        se.close()
+    m.close()
+    print(json.dumps({"pmc_workload": wl.shape.name + " batched", "steps": n_steps}), flush=True)
+
+
 def git_rev():
     try:
         r = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True, text=True)
@@ -174,9 +218,15 @@ def main():
     ap.add_argument("--pmc-workload", type=int, default=0, metavar="N",
                     help="run the 4B prompt + N decode steps and a known-size copy without torch, "
                          "for rocprofv3 --pmc passes (no timing output)")
+    ap.add_argument("--pmc-batch", type=int, default=0, metavar="N",
+                    help="run the 8B batched workload (32 sessions, N batched steps) without torch, for "
+                         "rocprofv3 --pmc passes (no timing output)")
     args = ap.parse_args()
     if args.pmc_workload:
         pmc_workload(args.pmc_workload)
+        return
+    if args.pmc_batch:
+        pmc_batch_workload(args.pmc_batch)
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: the decoder is evaluated unsharded on one MI355X "
