@@ -35,7 +35,7 @@ class ModelDesc(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("tied", ctypes.c_int32), ("rope_theta", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("scheme", ctypes.c_int32), ("kv_pool_blocks", ctypes.c_int32),
                 ("max_positions", ctypes.c_int32), ("max_round_tokens", ctypes.c_int32),
-                ("prefill_operands", ctypes.c_int32)]
+                ("prefill_operands", ctypes.c_int32), ("prefill_q8_direct", ctypes.c_int32)]
 
 
 class ModelInfo(ctypes.Structure):

@@ -38,11 +38,12 @@ class Model:
     """A model on the current HIP device with seeded synthetic weights."""
 
     def __init__(self, *, n_layers, hidden, n_q_heads, ffn, vocab=151936, tied=True, rope_theta=1e6, rms_eps=1e-6,
-                 scheme="bf16", kv_pool_blocks, max_positions, max_round_tokens=0, seed=0, prefill="split"):
+                 scheme="bf16", kv_pool_blocks, max_positions, max_round_tokens=0, seed=0, prefill="split",
+                 q8_prefill="copy"):
         self.desc = L.ModelDesc(n_layers, hidden, n_q_heads, 8, 128, ffn, vocab, 1 if tied else 0, rope_theta,
                                 rms_eps, L.SCHEMES[scheme],
                                 kv_pool_blocks, max_positions, max_round_tokens,
-                                {"split": 0, "fp16": 1}[prefill])
+                                {"split": 0, "fp16": 1}[prefill], {"copy": 0, "direct": 1}[q8_prefill])
         self.vocab, self.hidden, self.n_layers = vocab, hidden, n_layers
         self.handle = None
         self.handle = L.gqa_model_create(self.desc, seed)
@@ -50,11 +51,11 @@ class Model:
 
     @classmethod
     def from_shape(cls, shape, *, seed, scheme="bf16", kv_pool_blocks, max_positions, max_round_tokens=0,
-                   prefill="split"):
+                   prefill="split", q8_prefill="copy"):
         return cls(n_layers=shape.n_layers, hidden=shape.hidden, n_q_heads=shape.n_q_heads, ffn=shape.ffn,
                    vocab=shape.vocab, tied=shape.tied, rope_theta=shape.rope_theta, rms_eps=shape.rms_eps,
                    scheme=scheme, kv_pool_blocks=kv_pool_blocks, max_positions=max_positions,
-                   max_round_tokens=max_round_tokens, seed=seed, prefill=prefill)
+                   max_round_tokens=max_round_tokens, seed=seed, prefill=prefill, q8_prefill=q8_prefill)
 
     def info(self):
         return L.gqa_model_get_info(self.handle)

@@ -139,6 +139,31 @@ __global__ void prefill_copy_affine4_kernel(const uint32_t* __restrict__ q4, con
   }
 }
 
+// FP16 prefill copy (prefill_weight_index) of a tile-major Q8_0 matrix: one thread per 8-element
+// piece, w = fp16_rne(scale * q) (the product is exact in FP32; one FP16 rounding).
+__global__ void prefill_copy_q8_kernel(const int8_t* __restrict__ q, const f16* __restrict__ d, f16* __restrict__ dst,
+                                       int64_t rows, int64_t cols) {
+  const int64_t npieces = rows * cols / 8, ksteps = cols >> 5;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < npieces; p += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t bp = p >> 7, pos = p & 127;
+    const int64_t row = (bp / ksteps) * 32 + (pos & 31);
+    const int64_t col = (bp % ksteps) * 32 + ((pos >> 6) & 1) * 16 + ((pos >> 5) & 1) * 8;
+    const int8_t* src = q + tiled_index(row, col, cols);
+    const float D = (float)d[tiled_scale_index(row, col >> 5, cols)];
+    f16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (f16)(D * (float)src[e]);
+    *(f16x8*)(dst + p * 8) = o;
+  }
+}
+
+hipError_t launch_prefill_copy_q8(const int8_t* q, const f16* d, f16* dst, int64_t rows, int64_t cols, hipStream_t st) {
+  const int64_t n = rows * cols / 8;
+  const int grid = (int)std::min<int64_t>((n + 255) / 256, 65536);
+  hipLaunchKernelGGL(prefill_copy_q8_kernel, dim3(grid), dim3(256), 0, st, q, d, dst, rows, cols);
+  return hipGetLastError();
+}
+
 // FP16 prefill copy (prefill_weight_index) of a tile-major BF16 matrix: one thread per 8-element
 // piece of the destination, converted exactly like the matrix-core operand path (bf16x8_to_f16x8).
 __global__ void prefill_copy_kernel(const uint16_t* __restrict__ src, f16* __restrict__ dst, int64_t rows,

@@ -28,6 +28,7 @@ hipError_t launch_fill_u16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t st)
 hipError_t launch_quantize_q8_0(const uint16_t* w, int8_t* q, f16* d, int64_t rows, int64_t cols, hipStream_t st);
 hipError_t launch_quantize_affine4(const uint16_t* w, uint8_t* q4, f16* d, f16* bias, int64_t rows, int64_t cols,
                                   hipStream_t st);
+hipError_t launch_prefill_copy_q8(const int8_t* q, const f16* d, f16* dst, int64_t rows, int64_t cols, hipStream_t st);
 hipError_t launch_prefill_copy_affine4(const uint8_t* q4, const f16* d, const f16* bias, f16* dst, int64_t rows,
                                        int64_t cols, hipStream_t st);
 hipError_t launch_embed(const uint16_t* E, const int32_t* ids, int T, int H, int vocab, float* x, int32_t* err,
@@ -204,6 +205,7 @@ int check_desc(const gqa_model_desc* d) {
     return fail(GQA_E_INVALID, "unknown scheme");
   if (d->prefill_operands != GQA_PREFILL_SPLIT && d->prefill_operands != GQA_PREFILL_FP16)
     return fail(GQA_E_INVALID, "unknown prefill_operands");
+  if (d->prefill_q8_direct != 0 && d->prefill_q8_direct != 1) return fail(GQA_E_INVALID, "prefill_q8_direct must be 0 or 1");
   if (d->kv_pool_blocks < 1 || d->max_positions < 1 || d->max_round_tokens < 0)
     return fail(GQA_E_INVALID, "kv_pool_blocks and max_positions must be positive");
   if (!(d->rope_theta > 1.0f) || !(d->rms_eps > 0.0f)) return fail(GQA_E_INVALID, "bad rope_theta or rms_eps");
@@ -260,6 +262,7 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   m->s_gu = 4;
   m->s_d = (F / 32) % 8 == 0 ? 8 : 4;
   const bool q8 = d.scheme == GQA_SCHEME_Q8_0, a4 = d.scheme == GQA_SCHEME_AFFINE4;
+  const bool q8copy = q8 && !d.prefill_q8_direct;       // Q8_0 prefill over FP16 copies
   int64_t* wb = &m->weight_bytes;
 
 #define ALLOC(p, n, ctr)                      \
@@ -294,6 +297,12 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
       ALLOC(w.sgu, (int64_t)2 * F * H / 32, wb);
       ALLOC(w.qd, (int64_t)H * F, wb);
       ALLOC(w.sd, (int64_t)H * F / 32, wb);
+      if (q8copy) {
+        ALLOC(w.pqkv, (int64_t)m->QKV * H, &m->prefill_copy_bytes);
+        ALLOC(w.po, (int64_t)H * m->QD, &m->prefill_copy_bytes);
+        ALLOC(w.pgu, (int64_t)2 * F * H, &m->prefill_copy_bytes);
+        ALLOC(w.pd, (int64_t)H * F, &m->prefill_copy_bytes);
+      }
     } else if (a4) {
       // codes (half a byte per weight), scales and biases; FP16 dequantised copies for prefill
       ALLOC(w.qqkv, (int64_t)m->QKV * H / 2, wb);
@@ -401,6 +410,7 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
     // quantised schemes generate each projection into tmp and quantise it from there
     auto quant = [&](int8_t* q, f16* sc_, f16* b_, f16* pcopy, int64_t r, int64_t c) {
       if (q8) chk(launch_quantize_q8_0(tmp, q, sc_, r, c, st));
+      if (q8copy) chk(launch_prefill_copy_q8(q, sc_, pcopy, r, c, st));
       if (a4) {
         chk(launch_quantize_affine4(tmp, (uint8_t*)q, sc_, b_, r, c, st));
         chk(launch_prefill_copy_affine4((const uint8_t*)q, sc_, b_, pcopy, r, c, st));
@@ -867,8 +877,9 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
   const float eps = d.rms_eps;
   Rows none{};
   const bool split = d.prefill_operands == GQA_PREFILL_SPLIT;
-  // the GEMM reads Q8_0 quants directly; BF16 and AFFINE4 models use their FP16 prefill copies
-  auto gq = [&](const int8_t* q) { return d.scheme == GQA_SCHEME_Q8_0 ? q : nullptr; };
+  // the GEMM reads Q8_0 quants directly if so configured; otherwise every scheme uses the FP16
+  // prefill copies
+  auto gq = [&](const int8_t* q) { return d.scheme == GQA_SCHEME_Q8_0 && d.prefill_q8_direct ? q : nullptr; };
   // Projection of `rows` operand rows (FP16 hi/lo, row stride ldx) for a round of at most 32
   // rows: the LDS-staged matvec over the decode weights with the decode K ranges, partials
   // P[range][row][N] (range stride rows * N) summed in range order by the consumer. A 128-row

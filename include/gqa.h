@@ -79,6 +79,10 @@ typedef struct {
   int32_t prefill_operands; /* GQA_PREFILL_SPLIT (0): FP32 activations enter the prefill matrix-core
                                products as FP16 hi + lo (near-FP32); GQA_PREFILL_FP16 (1): as one
                                FP16 value (half the matrix-core work, FP16-rounded activations) */
+  int32_t prefill_q8_direct; /* Q8_0 models: 0 (default): prefill GEMMs read FP16 copies of the
+                               dequantised weights made at creation (one FP16 rounding of
+                               scale * q; the BF16 GEMM speed); 1: they read the int8 quants and
+                               scales directly (exact dequantisation, no copies, slower) */
 } gqa_model_desc;
 
 #define GQA_PREFILL_SPLIT 0
@@ -91,7 +95,8 @@ typedef struct {
   int64_t weight_bytes;       /* device bytes of all weights (Q8_0: quants + scales) */
   int64_t kv_pool_bytes;      /* device bytes of the K and V pools */
   int64_t scratch_bytes;      /* device bytes of per-model activation scratch */
-  int64_t prefill_copy_bytes; /* device bytes of the FP16 copies of BF16 projections used by prefill */
+  int64_t prefill_copy_bytes; /* device bytes of the FP16 copies prefill GEMMs read: projections
+                                 (BF16, or dequantised Q8_0 / AFFINE4) and the padded lm_head */
   int32_t free_blocks;        /* KV blocks a new session can take: free, or cached and mapped by no session */
   int32_t cached_blocks;      /* KV blocks in the prefix cache (mapped or not) */
 } gqa_model_info;
@@ -105,7 +110,8 @@ typedef struct {
  * fp16((max - min) / 15), an fp16 bias fp16(min) and 4-bit codes
  * q = clamp(round_half_away((w - bias) / scale), 0, 15) (FP32, from the stored scale and bias;
  * q = 0 when the scale is 0), w = scale * q + bias. Decode computes with these values exactly
- * (scale * sum(q x) + bias * sum(x) per group); prefill GEMMs read an FP16 rounding of them.
+ * (scale * sum(q x) + bias * sum(x) per group); prefill GEMMs read an FP16 rounding of them,
+ * as they do for Q8_0 unless prefill_q8_direct is set.
  * Allocates weights, the KV pool and per-model scratch; fails with GQA_E_OOM if they do not
  * fit, GQA_E_DEVICE if the device is not gfx950, GQA_E_INVALID for a bad descriptor.
  * Synchronises the device before returning. *out is set only on success. */

@@ -507,12 +507,14 @@ def _bf16_to_f64(bits):
     return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def test_qwen3_4b_q8_0_reduced_depth_parity(g):
+@pytest.mark.parametrize("q8_prefill", ["copy", "direct"])
+def test_qwen3_4b_q8_0_reduced_depth_parity(g, q8_prefill):
     """Q8_0 at the 4B hidden sizes (hidden 2560, 32/8 heads, FFN 9728, tied vocab) with 4 layers,
     a 1,500-token prompt evaluated in rounds of 512 (two full rounds and a ragged one, so the
     attention of later rounds starts at pos0 > 0), then 3 teacher-forced decode steps over a
     shuffled paged KV: full-logit NMSE and exact argmax against the oracle, which dequantises
-    the same Q8_0 bytes."""
+    the same Q8_0 bytes. Prefill GEMMs over the FP16 dequantised copies ("copy") or over the
+    quants and scales directly ("direct")."""
     wl = synth.WORKLOADS["4b-q8"]
     shape = synth.reduced(wl.shape, n_layers=4)
     prompt = synth.token_ids(wl.ids_seed, 1500)
@@ -522,10 +524,10 @@ def test_qwen3_4b_q8_0_reduced_depth_parity(g):
     nb = synth.blocks_for(len(prompt) + steps)
     table = synth.shuffled_blocks(wl.shuffle_seed, 4 * nb)[:nb]
     m = g.Model.from_shape(shape, seed=wl.weight_seed, scheme="q8_0", kv_pool_blocks=4 * nb,
-                           max_positions=nb * 32, max_round_tokens=512)
+                           max_positions=nb * 32, max_round_tokens=512, q8_prefill=q8_prefill)
     s = g.Session(m, nb * 32, block_ids=table)
     got = gpu_teacher_forced(m, s, prompt, toks, shape.vocab)
-    gate = Gate("4b q8_0 depth 4")
+    gate = Gate("4b q8_0 depth 4 " + q8_prefill)
     for i, ((lg, am), r) in enumerate(zip(got, ref)):
         gate.check(i, lg, r, am)
     gate.assert_ok()
