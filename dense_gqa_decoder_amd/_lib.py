@@ -42,7 +42,8 @@ class ModelInfo(ctypes.Structure):
     _fields_ = [("round_tokens", ctypes.c_int32), ("cu_count", ctypes.c_int32), ("weight_bytes", ctypes.c_int64),
                 ("kv_pool_bytes", ctypes.c_int64), ("scratch_bytes", ctypes.c_int64),
                 ("prefill_copy_bytes", ctypes.c_int64), ("free_blocks", ctypes.c_int32),
-                ("cached_blocks", ctypes.c_int32)]
+                ("cached_blocks", ctypes.c_int32), ("prefix_lookups", ctypes.c_int64),
+                ("prefix_hits", ctypes.c_int64), ("prefix_evictions", ctypes.c_int64)]
 
 
 _lib = None

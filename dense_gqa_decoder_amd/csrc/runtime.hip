@@ -489,6 +489,9 @@ int gqa_model_get_info(const gqa_model* m, gqa_model_info* info) {
   info->prefill_copy_bytes = m->prefill_copy_bytes;
   info->free_blocks = m->pool->available();
   info->cached_blocks = m->pool->cached_count();
+  info->prefix_lookups = (int64_t)m->pool->lookups;
+  info->prefix_hits = (int64_t)m->pool->hits;
+  info->prefix_evictions = (int64_t)m->pool->evictions;
   return GQA_OK;
 }
 

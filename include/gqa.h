@@ -99,6 +99,9 @@ typedef struct {
                                  (BF16, or dequantised Q8_0 / AFFINE4) and the padded lm_head */
   int32_t free_blocks;        /* KV blocks a new session can take: free, or cached and mapped by no session */
   int32_t cached_blocks;      /* KV blocks in the prefix cache (mapped or not) */
+  int64_t prefix_lookups;     /* prefix-cache block lookups so far (pooled prefills) */
+  int64_t prefix_hits;        /* lookups that mapped a cached block */
+  int64_t prefix_evictions;   /* cached blocks evicted to make room */
 } gqa_model_info;
 
 /* Create a model on the current HIP device with seeded synthetic weights.

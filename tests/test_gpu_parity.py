@@ -882,10 +882,12 @@ def test_pooled_prefix_reuse_parity(g):
     gate.check(0, la, ref_p)
     a.close()
     assert m.info().cached_blocks == 6
+    assert m.info().prefix_lookups == 1 and m.info().prefix_hits == 0     # the cold prompt's first block
     say("pooled: warm prompt")
     b = g.Session(m, 512, pooled=True)
     lb, amb = _prefill(b, P, shape.vocab)
     assert b.reused == 192
+    assert m.info().prefix_hits == 6
     gate.check(1, lb, ref_p, amb)
     assert nmse(lb, la) <= 1e-8
     # greedy decode after the reused prefix, teacher-forced with the oracle's tokens
