@@ -1,5 +1,6 @@
 """CPU checks of the C ABI: the built library loads and exports every function include/gqa.h
-declares, and a call without a GPU fails with an error code instead of falling back."""
+declares, the Python mirrors of its structs have the header's layout, and a call without a GPU
+fails with an error code instead of falling back."""
 import os
 import re
 
@@ -41,3 +42,37 @@ def test_create_without_gpu_reports_an_error():
     with pytest.raises(g.GqaError) as ei:
         g.gqa_model_create(d, 1)
     assert ei.value.code in (g.GQA_E_HIP, g.GQA_E_DEVICE)
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors of gqa_model_desc and gqa_model_info have the header's field offsets and
+    sizes (compiled from include/gqa.h with the host C compiler)."""
+    import ctypes
+    import shutil
+    import subprocess
+    from dense_gqa_decoder_amd import _lib
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    structs = {"gqa_model_desc": _lib.ModelDesc, "gqa_model_info": _lib.ModelInfo}
+    body = ""
+    for cname, py in structs.items():
+        body += '  printf("%s size %%zu\\n", sizeof(%s));\n' % (cname, cname)
+        for fname, _ in py._fields_:
+            body += '  printf("%s %s %%zu\\n", offsetof(%s, %s));\n' % (cname, fname, cname, fname)
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include "%s"\nint main(void) {\n%s  return 0;\n}\n'
+                   % (os.path.join(ROOT, "include", "gqa.h"), body))
+    exe = tmp_path / "layout"
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    r = subprocess.run([cc, "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+                        str(src), "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines():
+        parts = line.split()
+        got[tuple(parts[:-1])] = int(parts[-1])
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
