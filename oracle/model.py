@@ -27,6 +27,8 @@ import numpy as np
 
 import synth
 
+from .q8_0 import dequantize_q8_0, quantize_q8_0
+
 HEAD_DIM = 128
 BLOCK = 32
 
@@ -200,11 +202,25 @@ class OracleModel:
         return w
 
 
-class OracleSession:
-    """One sequence: a KV cache and a position counter."""
+def kv_q8_0_roundtrip(x: np.ndarray) -> np.ndarray:
+    """What attention reads back from a Q8_0 KV cache (Kipp Roadmap, status v0.0.4: the opt-in
+    Q8_0 KV cache). Each head row of 128 FP32 values is stored as four Q8_0 blocks of 32 (the
+    weight format of Model Support, "Quantization (Q8_0)", with its scale and rounding rule);
+    reading gives fp32(scale) * q, exact in FP32, which enters attention rounded to BF16, the
+    operand format of the BF16 cache (the pages fix no read precision; this is the reading)."""
+    x = np.asarray(x, dtype=np.float32)
+    scale, q = quantize_q8_0(x.reshape(-1, HEAD_DIM))
+    return bf16_round(dequantize_q8_0(scale, q)).reshape(x.shape)
 
-    def __init__(self, model: OracleModel, kv, kv_round: bool = True):
-        self.m, self.kv, self.pos, self.kv_round = model, kv, 0, kv_round
+
+class OracleSession:
+    """One sequence: a KV cache and a position counter. kv_quant "bf16" stores K/V as BF16;
+    "q8_0" stores them as Q8_0 blocks (kv_q8_0_roundtrip)."""
+
+    def __init__(self, model: OracleModel, kv, kv_round: bool = True, kv_quant: str = "bf16"):
+        if kv_quant not in ("bf16", "q8_0"):
+            raise ValueError("kv_quant must be bf16 or q8_0")
+        self.m, self.kv, self.pos, self.kv_round, self.kv_quant = model, kv, 0, kv_round, kv_quant
 
     def forward(self, ids, all_logits: bool = False):
         """Append tokens ``ids`` at positions pos.. and return logits of the last (or every) new position."""
@@ -225,7 +241,9 @@ class OracleSession:
             v = (a @ w["v"].T).reshape(T, sh.n_kv_heads, sh.head_dim)
             q = rope(rmsnorm(q, w["q_norm"], eps), cos, sin)
             k = rope(rmsnorm(k, w["k_norm"], eps), cos, sin)
-            if self.kv_round:
+            if self.kv_quant == "q8_0":
+                k, v = kv_q8_0_roundtrip(k), kv_q8_0_roundtrip(v)
+            elif self.kv_round:
                 k, v = bf16_round(k), bf16_round(v)
             self.kv.write(l, positions, k, v)
             K, V = self.kv.read(l, self.pos + T)

@@ -464,3 +464,65 @@ def test_truncate_resume_equals_fresh_evaluation():
     assert max(om.nmse(g, r) for g, r in zip(off, ref)) > 1e-4
     with pytest.raises(ValueError):
         s.truncate(s.pos + 1)
+
+
+def test_kv_q8_0_roundtrip_exact_on_the_grid():
+    """Q8_0 KV rows (Kipp Roadmap, status v0.0.4): a block whose values are integers times a power
+    of two, with max |x| = 127 times it, has scale exactly that power and quantises without error;
+    an all-zero block stays zero; the read value is then exact in BF16 too."""
+    rng = np.random.default_rng(31)
+    q = rng.integers(-127, 128, size=(3, 8, 128)).astype(np.float64)
+    q[..., ::32] = 127.0                     # every block reaches the full code range
+    q[1, :, 32:64] = 0.0                     # one zero block per row of the second position
+    q[2, :, ::32] = -127.0                   # the maximum magnitude taken by a negative value
+    x = (q * 2.0 ** -10).astype(np.float32)
+    got = om.kv_q8_0_roundtrip(x)
+    assert got.shape == x.shape
+    assert np.array_equal(got, x)
+    scale, codes = quantize_q8_0(x.reshape(-1, 128))
+    sc = scale.astype(np.float32).reshape(3, 8, 4)
+    assert np.all(sc[0] == 2.0 ** -10) and np.all(sc[1][:, 1] == 0) and np.all(sc[2] == 2.0 ** -10)
+
+
+def test_kv_q8_0_roundtrip_error_bound():
+    """|read - x| <= 0.57 d + 2^-8 |read| per element, d = max|x| / 127 of the element's block (half a
+    code step, the fp16 rounding of the scale over at most 127 codes, then the BF16 read)."""
+    rng = np.random.default_rng(32)
+    x = (rng.standard_normal((64, 8, 128)) * rng.uniform(0.01, 30, size=(64, 8, 1))).astype(np.float32)
+    got = om.kv_q8_0_roundtrip(x).astype(np.float64)
+    d = np.abs(x.astype(np.float64)).reshape(64, 8, 4, 32).max(axis=3, keepdims=True) / 127
+    d = np.broadcast_to(d, (64, 8, 4, 32)).reshape(64, 8, 128)
+    err = np.abs(got - x)
+    assert np.all(err <= 0.57 * d + 2.0 ** -8 * np.abs(got) + 1e-30)
+    assert err.max() > 0                     # it does quantise
+
+
+def test_kv_q8_0_session_invariants():
+    """With the Q8_0 KV cache: cached decode equals no-cache recomputation (NMSE <= 1e-6, same argmax),
+    a shuffled block table equals the contiguous layout bitwise, and logits move from the BF16-cache
+    ones by a small nonzero amount (the pages gate the option by a tolerance)."""
+    shape = MINI
+    m = oracle.OracleModel(shape, 33)
+    ids = synth.token_ids(34, 60, shape.vocab)
+    full = oracle.OracleSession(m, oracle.ContiguousKV.for_shape(shape, 64), kv_quant="q8_0").forward(ids, all_logits=True)
+    s = oracle.OracleSession(m, oracle.ContiguousKV.for_shape(shape, 64), kv_quant="q8_0")
+    s.prefill(ids[:35])
+    for t in range(35, 60):
+        lg = s.decode(int(ids[t]))
+        assert om.nmse(lg, full[t]) <= 1e-6
+        assert om.argmax(lg) == om.argmax(full[t])
+
+    def run(kv):
+        ss = oracle.OracleSession(m, kv, kv_quant="q8_0")
+        out = [ss.prefill(ids[:33])]
+        out += [ss.decode(int(t)) for t in ids[33:]]
+        return np.stack(out)
+
+    ref = run(oracle.ContiguousKV.for_shape(shape, 64))
+    got = run(oracle.PagedKV.for_shape(shape, 12, synth.shuffled_blocks(35, 12)[:2]))
+    assert np.array_equal(got, ref)
+    bf = oracle.OracleSession(m, oracle.ContiguousKV.for_shape(shape, 64)).forward(ids, all_logits=True)
+    worst = max(om.nmse(full[t], bf[t]) for t in range(len(ids)))
+    assert 0 < worst < 1e-3, worst
+    with pytest.raises(ValueError):
+        oracle.OracleSession(m, oracle.ContiguousKV.for_shape(shape, 64), kv_quant="q4")
