@@ -35,7 +35,8 @@ class ModelDesc(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("tied", ctypes.c_int32), ("rope_theta", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("scheme", ctypes.c_int32), ("kv_pool_blocks", ctypes.c_int32),
                 ("max_positions", ctypes.c_int32), ("max_round_tokens", ctypes.c_int32),
-                ("prefill_operands", ctypes.c_int32), ("prefill_q8_direct", ctypes.c_int32)]
+                ("prefill_operands", ctypes.c_int32), ("prefill_q8_direct", ctypes.c_int32),
+                ("kv_quant", ctypes.c_int32)]
 
 
 class ModelInfo(ctypes.Structure):
@@ -77,6 +78,7 @@ _SIGS = {
     "gqa_debug_read_q8": (I32, [P, I32, I32, I32, I32, P, P]),
     "gqa_debug_read_affine4": (I32, [P, I32, I32, I32, I32, P, P, P]),
     "gqa_debug_read_kv": (I32, [P, I32, I32, I32, P, P]),
+    "gqa_debug_read_kv_q8": (I32, [P, I32, I32, I32, P, P, P, P]),
     "gqa_debug_read_rope": (I32, [P, I32, P, P]),
     "gqa_debug_read_scratch": (I32, [P, I32, ctypes.c_int64, ctypes.c_int64, P]),
 }
@@ -223,6 +225,10 @@ def gqa_debug_read_q8(model, kind, layer, row0, rows, q_ptr, s_ptr) -> None:
 
 def gqa_debug_read_kv(session, layer, pos0, n, k_ptr, v_ptr) -> None:
     _check(lib().gqa_debug_read_kv(session, layer, pos0, n, k_ptr, v_ptr))
+
+
+def gqa_debug_read_kv_q8(session, layer, pos0, n, kc_ptr, ks_ptr, vc_ptr, vs_ptr) -> None:
+    _check(lib().gqa_debug_read_kv_q8(session, layer, pos0, n, kc_ptr, ks_ptr, vc_ptr, vs_ptr))
 
 
 def gqa_debug_read_rope(model, n, c_ptr, s_ptr) -> None:

@@ -39,11 +39,12 @@ class Model:
 
     def __init__(self, *, n_layers, hidden, n_q_heads, ffn, vocab=151936, tied=True, rope_theta=1e6, rms_eps=1e-6,
                  scheme="bf16", kv_pool_blocks, max_positions, max_round_tokens=0, seed=0, prefill="split",
-                 q8_prefill="copy"):
+                 q8_prefill="copy", kv_quant="bf16"):
         self.desc = L.ModelDesc(n_layers, hidden, n_q_heads, 8, 128, ffn, vocab, 1 if tied else 0, rope_theta,
                                 rms_eps, L.SCHEMES[scheme],
                                 kv_pool_blocks, max_positions, max_round_tokens,
-                                {"split": 0, "fp16": 1}[prefill], {"copy": 0, "direct": 1}[q8_prefill])
+                                {"split": 0, "fp16": 1}[prefill], {"copy": 0, "direct": 1}[q8_prefill],
+                                {"bf16": 0, "q8_0": 1}[kv_quant])
         self.vocab, self.hidden, self.n_layers = vocab, hidden, n_layers
         self.handle = None
         self.handle = L.gqa_model_create(self.desc, seed)
@@ -51,11 +52,12 @@ class Model:
 
     @classmethod
     def from_shape(cls, shape, *, seed, scheme="bf16", kv_pool_blocks, max_positions, max_round_tokens=0,
-                   prefill="split", q8_prefill="copy"):
+                   prefill="split", q8_prefill="copy", kv_quant="bf16"):
         return cls(n_layers=shape.n_layers, hidden=shape.hidden, n_q_heads=shape.n_q_heads, ffn=shape.ffn,
                    vocab=shape.vocab, tied=shape.tied, rope_theta=shape.rope_theta, rms_eps=shape.rms_eps,
                    scheme=scheme, kv_pool_blocks=kv_pool_blocks, max_positions=max_positions,
-                   max_round_tokens=max_round_tokens, seed=seed, prefill=prefill, q8_prefill=q8_prefill)
+                   max_round_tokens=max_round_tokens, seed=seed, prefill=prefill, q8_prefill=q8_prefill,
+                   kv_quant=kv_quant)
 
     def info(self):
         return L.gqa_model_get_info(self.handle)
@@ -204,6 +206,16 @@ class Session:
         v = np.empty((n, 8, 128), dtype=np.uint16)
         L.gqa_debug_read_kv(self.handle, layer, pos0, n, k.ctypes.data, v.ctypes.data)
         return k, v
+
+    def read_kv_q8(self, layer, pos0, n):
+        """Q8_0 KV cache: (K codes, K scale bits, V codes, V scale bits), [n, 8, 128] int8 and [n, 8, 4] uint16."""
+        kc = np.empty((n, 8, 128), dtype=np.int8)
+        vc = np.empty((n, 8, 128), dtype=np.int8)
+        ks = np.empty((n, 8, 4), dtype=np.uint16)
+        vs = np.empty((n, 8, 4), dtype=np.uint16)
+        L.gqa_debug_read_kv_q8(self.handle, layer, pos0, n, kc.ctypes.data, ks.ctypes.data, vc.ctypes.data,
+                               vs.ctypes.data)
+        return kc, ks, vc, vs
 
     def close(self):
         if self.handle:

@@ -176,6 +176,26 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Q8_0 KV cache (Kipp Roadmap, status v0.0.4: opt-in Q8_0 KV). Each head row of 128 K or V values
+// is stored as four blocks of 32 int8 codes with an fp16 scale, the Q8_0 weight format and rule:
+// d = max|x| / 127 (FP32), scale = fp16(d), code = clamp(round_half_away(x / d), -127, 127), 0 when
+// d = 0. The codes sit at the element offsets of the BF16 pool (one byte each), scale j of the row
+// at element offset / 32. Attention reads bf16(fp32(scale) * code), the BF16 cache's operand format.
+struct KvQ8 {
+  int8_t* kq;      // nullptr: the cache is BF16
+  int8_t* vq;
+  f16* ks;
+  f16* vs;
+};
+__device__ __forceinline__ float q8kv_scale(float amax) { return __fdiv_rn(amax, 127.0f); }
+__device__ __forceinline__ int q8kv_code(float x, float d) {
+  if (d == 0.f) return 0;
+  return (int)fminf(fmaxf(roundf(__fdiv_rn(x, d)), -127.f), 127.f);
+}
+__device__ __forceinline__ uint16_t q8kv_read_bf16(f16 scale, int code) {
+  return f32_to_bf16_rne((float)scale * (float)code);
+}
+
 // FP32 -> FP16 conversions of MFMA operands go through explicit instructions, never through a
 // plain cast: the compiler is free to lower a cast to different instructions in different
 // kernels (mixed-precision FMA forms fuse a preceding product), and every kernel that builds an

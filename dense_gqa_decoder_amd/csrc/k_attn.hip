@@ -447,7 +447,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
     const float* __restrict__ qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* __restrict__ ss,
     int ss_n, int H, const uint16_t* __restrict__ wqn, const uint16_t* __restrict__ wkn, float eps,
     const float* __restrict__ rcos, const float* __restrict__ rsin, Rows rows, int cpw, uint16_t* __restrict__ kpool,
-    uint16_t* __restrict__ vpool, float* part, int* __restrict__ counters, float out_scale, f16* __restrict__ ohi,
+    uint16_t* __restrict__ vpool, KvQ8 kq8, float* part, int* __restrict__ counters, float out_scale, f16* __restrict__ ohi,
     f16* __restrict__ olo, int ldo) {
   constexpr int NW = kDecodeWaves;                        // softmax states per workgroup (one per wave)
   constexpr int NE = (G + 2) * kHeadDim;                  // q heads, then k and v of the new position
@@ -542,18 +542,49 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
       if (hh < G) {
         r0 *= qscale;
         r1 *= qscale;
-      } else {                                            // k: BF16 storage rounding
+      } else if (!kq8.kq) {                               // k: BF16 storage rounding
         r0 = bf16_bits_to_f32(f32_to_bf16_rne(r0));
         r1 = bf16_bits_to_f32(f32_to_bf16_rne(r1));
       }
       sq[hh * kHeadDim + lane] = r0;
       sq[hh * kHeadDim + 64 + lane] = r1;
     }
-    if (owner && tid < kHeadDim) sq[(G + 1) * kHeadDim + tid] = bf16_bits_to_f32(f32_to_bf16_rne(sraw[(G + 1) * kHeadDim + tid]));
+    if (owner && tid < kHeadDim) {
+      const float vr = sraw[(G + 1) * kHeadDim + tid];
+      sq[(G + 1) * kHeadDim + tid] = kq8.kq ? vr : bf16_bits_to_f32(f32_to_bf16_rne(vr));
+    }
   }
   __syncthreads();
-  // the new position's K/V into the pool, through the block table
-  if (owner && tid < 2 * kHeadDim / 8) {
+  // the new position's K/V into the pool, through the block table. Q8_0 cache: thread 4 kv + j
+  // quantises block j of the K (kv = 0) or V row, stores codes and scale, and replaces the row in
+  // LDS by the values attention reads back, bf16(scale * code).
+  if (kq8.kq) {
+    if (owner) {
+      if (tid < 8) {
+        const int kv = tid >> 2, blk = tid & 3;
+        float* src = sq + (G + kv) * kHeadDim + 32 * blk;
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(src[e]));
+        const float d = q8kv_scale(amax);
+        const f16 sc = (f16)d;
+        const int64_t off =
+            (int64_t)table[pos >> 5] * kBlockElems + ((int64_t)kvh * kBlock + (pos & 31)) * kHeadDim + 32 * blk;
+        uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const int c = q8kv_code(src[e], d);
+          w[e >> 2] |= ((uint32_t)c & 0xFFu) << (8 * (e & 3));
+          src[e] = bf16_bits_to_f32(q8kv_read_bf16(sc, c));
+        }
+        int8_t* dq = (kv ? kq8.vq : kq8.kq) + off;
+        *(uint4*)dq = uint4{w[0], w[1], w[2], w[3]};
+        *(uint4*)(dq + 16) = uint4{w[4], w[5], w[6], w[7]};
+        (kv ? kq8.vs : kq8.ks)[off >> 5] = sc;
+      }
+      __syncthreads();
+    }
+  } else if (owner && tid < 2 * kHeadDim / 8) {
     const int kv = tid >> 4, d0 = (tid & 15) * 8;       // tid < 16: K, else V
     const float* src = sq + (G + kv) * kHeadDim + d0;
     uint32_t h[8];
@@ -861,8 +892,8 @@ hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const in
 hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* ss,
                               int ss_n, int H, const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
                               const float* rsin, const Rows& rows, int B, int max_ctx, uint16_t* kpool,
-                              uint16_t* vpool, float* part, int* counters, float out_scale, f16* ohi, f16* olo,
-                              int ldo, hipStream_t st) {
+                              uint16_t* vpool, const KvQ8& kq8, float* part, int* counters, float out_scale, f16* ohi,
+                              f16* olo, int ldo, hipStream_t st) {
   if (nsplit < 1 || nsplit > 8 || B < 1 || B > kMaxBatch || max_ctx < 1) return hipErrorInvalidValue;
   const int CH = decode_chunk_len(max_ctx);
   const int chunks = (max_ctx + CH - 1) / CH;          // rows with shorter contexts exit early
@@ -876,7 +907,7 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
   dim3 grid((chunks + cpw - 1) / cpw, kKvHeads, B);
 #define DEC_LAUNCH(GG, FU)                                                                                         \
   hipLaunchKernelGGL((attn_decode_kernel<GG, FU>), grid, dim3(64 * kDecodeWaves), 0, st, qkvp, nsplit, pstride, QKV, \
-                     nq, ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, cpw, kpool, vpool, part, counters, out_scale, \
+                     nq, ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, cpw, kpool, vpool, kq8, part, counters, out_scale, \
                      ohi, olo, ldo)
   if (G != 4 && G != 2) return hipErrorInvalidValue;
   if (fused) {

@@ -39,7 +39,9 @@ hipError_t launch_rmsnorm(float* x, int ldx, const float* part, int nsplit, int 
 hipError_t launch_qk_rope_kv(bool decode, const float* qkv, int nsplit, int part_stride, int ldqkv, int nq,
                              const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
                              const float* rsin, int pos0, const int32_t* table0, const Rows& rows, uint16_t* kpool,
-                             uint16_t* vpool, float* qout, int nrows, hipStream_t st);
+                             uint16_t* vpool, const KvQ8& kq8, float* qout, int nrows, hipStream_t st);
+hipError_t launch_kv_q8_window(const Rows& rows, int B, int max_n, const KvQ8& kq8, uint16_t* kwin, uint16_t* vwin,
+                               hipStream_t st);
 hipError_t launch_argmax(const float2* cand, int ntiles, int B, int32_t* out, hipStream_t st);
 hipError_t launch_argmax_rows(const float* logits, int V, int64_t ld, int rows, int32_t* out, hipStream_t st);
 hipError_t launch_score(const float* logits, int V, const int32_t* targets, int B, float* out, hipStream_t st);
@@ -64,7 +66,8 @@ hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const in
 hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* ss,
                               int ss_n, int H, const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
                               const float* rsin, const Rows& rows, int B, int max_ctx, uint16_t* kpool,
-                              uint16_t* vpool, float* part, int* counters, float out_scale, f16* ohi, f16* olo,
+                              uint16_t* vpool, const KvQ8& kq8, float* part, int* counters, float out_scale, f16* ohi,
+                              f16* olo,
                               int ldo, hipStream_t st);
 int64_t attn_decode_part_floats(int nq);
 }  // namespace gqa
@@ -120,7 +123,8 @@ struct LayerW {
   int8_t *qqkv = nullptr, *qo = nullptr, *qgu = nullptr, *qd = nullptr;   // Q8_0 quants / AFFINE4 codes
   f16 *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sd = nullptr;       // Q8_0 / AFFINE4 scales
   f16 *bqkv = nullptr, *bo = nullptr, *bgu = nullptr, *bd = nullptr;       // AFFINE4 biases
-  uint16_t *kpool = nullptr, *vpool = nullptr;
+  uint16_t *kpool = nullptr, *vpool = nullptr;   // BF16 cache; with a Q8_0 cache: null
+  KvQ8 kq8{nullptr, nullptr, nullptr, nullptr};   // Q8_0 cache: codes and scales
 };
 
 }  // namespace
@@ -139,6 +143,7 @@ struct gqa_model {
         *apart = nullptr;
   float* ppart = nullptr;       // prefill: K-range partials of the o and down projections [<= 4 R][H]
   int32_t* counters = nullptr;  // decode attention: finished chunks per (row, KV head)
+  uint16_t *kwin = nullptr, *vwin = nullptr;   // Q8_0 KV cache: the BF16 read window of one layer
   float* ss = nullptr;          // decode: sum-of-squares partials [2][8][32] (q|k|v input, gate|up input)
   float2* cand = nullptr;   // lm_head argmax candidates [32][vocab / 16]
   float* slog = nullptr;    // logits of up to kScoreRows rows being scored [kScoreRows][vocab]
@@ -206,6 +211,7 @@ int check_desc(const gqa_model_desc* d) {
   if (d->prefill_operands != GQA_PREFILL_SPLIT && d->prefill_operands != GQA_PREFILL_FP16)
     return fail(GQA_E_INVALID, "unknown prefill_operands");
   if (d->prefill_q8_direct != 0 && d->prefill_q8_direct != 1) return fail(GQA_E_INVALID, "prefill_q8_direct must be 0 or 1");
+  if (d->kv_quant != GQA_KV_BF16 && d->kv_quant != GQA_KV_Q8_0) return fail(GQA_E_INVALID, "kv_quant must be 0 or 1");
   if (d->kv_pool_blocks < 1 || d->max_positions < 1 || d->max_round_tokens < 0)
     return fail(GQA_E_INVALID, "kv_pool_blocks and max_positions must be positive");
   if (!(d->rope_theta > 1.0f) || !(d->rms_eps > 0.0f)) return fail(GQA_E_INVALID, "bad rope_theta or rms_eps");
@@ -331,8 +337,19 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
       ALLOC(w.pgu, (int64_t)2 * F * H, &m->prefill_copy_bytes);
       ALLOC(w.pd, (int64_t)H * F, &m->prefill_copy_bytes);
     }
-    ALLOC(w.kpool, pool_elems, &m->kv_bytes);
-    ALLOC(w.vpool, pool_elems, &m->kv_bytes);
+    if (d.kv_quant == GQA_KV_Q8_0) {
+      ALLOC(w.kq8.kq, pool_elems, &m->kv_bytes);
+      ALLOC(w.kq8.vq, pool_elems, &m->kv_bytes);
+      ALLOC(w.kq8.ks, pool_elems / 32, &m->kv_bytes);
+      ALLOC(w.kq8.vs, pool_elems / 32, &m->kv_bytes);
+    } else {
+      ALLOC(w.kpool, pool_elems, &m->kv_bytes);
+      ALLOC(w.vpool, pool_elems, &m->kv_bytes);
+    }
+  }
+  if (d.kv_quant == GQA_KV_Q8_0) {           // one layer's BF16 read window
+    ALLOC(m->kwin, pool_elems, &m->kv_bytes);
+    ALLOC(m->vwin, pool_elems, &m->kv_bytes);
   }
   const int rows = std::max(m->R, kMaxBatch);
   int64_t* sb = &m->scratch_bytes;
@@ -439,8 +456,19 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
       chk(launch_prefill_copy(w.wd, w.pd, H, F, st));
     }
     if (qs) chk(hipStreamSynchronize(st));
-    chk(hipMemsetAsync(w.kpool, 0, pool_elems * 2, st));
-    chk(hipMemsetAsync(w.vpool, 0, pool_elems * 2, st));
+    if (d.kv_quant == GQA_KV_Q8_0) {
+      chk(hipMemsetAsync(w.kq8.kq, 0, pool_elems, st));
+      chk(hipMemsetAsync(w.kq8.vq, 0, pool_elems, st));
+      chk(hipMemsetAsync(w.kq8.ks, 0, pool_elems / 32 * 2, st));
+      chk(hipMemsetAsync(w.kq8.vs, 0, pool_elems / 32 * 2, st));
+    } else {
+      chk(hipMemsetAsync(w.kpool, 0, pool_elems * 2, st));
+      chk(hipMemsetAsync(w.vpool, 0, pool_elems * 2, st));
+    }
+  }
+  if (d.kv_quant == GQA_KV_Q8_0) {
+    chk(hipMemsetAsync(m->kwin, 0, pool_elems * 2, st));
+    chk(hipMemsetAsync(m->vwin, 0, pool_elems * 2, st));
   }
   chk(hipMemsetAsync(m->err, 0, 4, st));
   chk(hipMemsetAsync(m->counters, 0, sizeof(int32_t) * kMaxBatch * kKvHeads, st));
@@ -634,8 +662,17 @@ int apply_pool_changes(gqa_session* s, const std::vector<TableWrite>& tw, const 
   const size_t blk = (size_t)kKvHeads * kBlock * kHeadDim;
   for (const BlockCopy& c : cp)
     for (const LayerW& w : m->L) {
-      HIP_TRY(hipMemcpyAsync(w.kpool + c.dst * blk, w.kpool + c.src * blk, blk * 2, hipMemcpyDeviceToDevice, st));
-      HIP_TRY(hipMemcpyAsync(w.vpool + c.dst * blk, w.vpool + c.src * blk, blk * 2, hipMemcpyDeviceToDevice, st));
+      if (w.kq8.kq) {
+        HIP_TRY(hipMemcpyAsync(w.kq8.kq + c.dst * blk, w.kq8.kq + c.src * blk, blk, hipMemcpyDeviceToDevice, st));
+        HIP_TRY(hipMemcpyAsync(w.kq8.vq + c.dst * blk, w.kq8.vq + c.src * blk, blk, hipMemcpyDeviceToDevice, st));
+        HIP_TRY(hipMemcpyAsync(w.kq8.ks + c.dst * blk / 32, w.kq8.ks + c.src * blk / 32, blk / 32 * 2,
+                               hipMemcpyDeviceToDevice, st));
+        HIP_TRY(hipMemcpyAsync(w.kq8.vs + c.dst * blk / 32, w.kq8.vs + c.src * blk / 32, blk / 32 * 2,
+                               hipMemcpyDeviceToDevice, st));
+      } else {
+        HIP_TRY(hipMemcpyAsync(w.kpool + c.dst * blk, w.kpool + c.src * blk, blk * 2, hipMemcpyDeviceToDevice, st));
+        HIP_TRY(hipMemcpyAsync(w.vpool + c.dst * blk, w.vpool + c.src * blk, blk * 2, hipMemcpyDeviceToDevice, st));
+      }
     }
   for (size_t i = 0; i < tw.size(); i += kTableWritesMax) {
     TableWrites t{};
@@ -715,6 +752,9 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
   const gqa_model_desc& d = m->d;
   const int H = d.hidden, F = d.ffn, V = d.vocab, NQ = d.n_q_heads, QD = m->QD, QKV = m->QKV;
   const float eps = d.rms_eps;
+  // the K/V attention reads: the BF16 cache, or the read window of a Q8_0 cache
+  auto kv_k = [m](const LayerW& w) { return w.kq8.kq ? m->kwin : w.kpool; };
+  auto kv_v = [m](const LayerW& w) { return w.kq8.kq ? m->vwin : w.vpool; };
   const bool fused = B <= 4;
   const int64_t pstride = m->part_floats / 8;
   float* xa = m->x;
@@ -774,9 +814,10 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
       q.W = w.wqkv; q.Wq = w.qqkv; q.Wd = w.sqkv; q.Wb = w.bqkv; q.K = H; q.N = QKV;
       q.xres = xa; q.nw = w.attn_norm; q.ss_out = ss_qkv; q.y = P0; q.ldy = QKV;
       LAUNCH(launch_gemv_full(XF_NORM, EPI_STORE, m->s_qkv, q, st));
+      if (w.kq8.kq) LAUNCH(launch_kv_q8_window(rows, B, max_ctx - 1, w.kq8, m->kwin, m->vwin, st));
       LAUNCH(launch_attn_decode(P0, 1, pstride, QKV, NQ, ss_qkv, m->s_qkv, H, w.q_norm, w.k_norm, eps, m->rcos,
-                                m->rsin, rows, B, max_ctx, w.kpool, w.vpool, m->apart, m->counters, kAttnOutScale, m->oh, m->ol, QD,
-                                st));
+                                m->rsin, rows, B, max_ctx, kv_k(w), kv_v(w), w.kq8, m->apart, m->counters, kAttnOutScale,
+                                m->oh, m->ol, QD, st));
       FullArgs o = fa();
       o.W = w.wo; o.Wq = w.qo; o.Wd = w.so; o.Wb = w.bo; o.K = QD; o.N = H;
       o.xhi = m->oh; o.xlo = m->ol; o.ldx = QD; o.y = xa; o.ldy = H; o.yscale = 1.f / kAttnOutScale;
@@ -813,9 +854,10 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
     LAUNCH(gemv_built(w.wqkv, w.qqkv, w.sqkv, w.bqkv, H, QKV, resid_src(xa, xb, prev, prev_split, 1.f, w.attn_norm, ss_qkv),
                       m->s_qkv, P0, QKV, m->xh, m->xl));
     std::swap(xa, xb);
+    if (w.kq8.kq) LAUNCH(launch_kv_q8_window(rows, B, max_ctx - 1, w.kq8, m->kwin, m->vwin, st));
     LAUNCH(launch_attn_decode(P0, m->s_qkv, pstride, QKV, NQ, ss_qkv, m->s_qkv, H, w.q_norm, w.k_norm, eps, m->rcos,
-                              m->rsin, rows, B, max_ctx, w.kpool, w.vpool, m->apart, m->counters, kAttnOutScale, m->oh, m->ol, QD,
-                              st));
+                              m->rsin, rows, B, max_ctx, kv_k(w), kv_v(w), w.kq8, m->apart, m->counters, kAttnOutScale,
+                              m->oh, m->ol, QD, st));
     LAUNCH(launch_gemv(w.wo, w.qo, w.so, w.bo, QD, H, raw_src(m->oh, m->ol, QD), B, m->s_o, P1, pstride, H, nullptr,
                        st));
     {
@@ -879,6 +921,8 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
   const int H = d.hidden, F = d.ffn, V = d.vocab, NQ = d.n_q_heads, QD = m->QD, QKV = m->QKV;
   const float eps = d.rms_eps;
   Rows none{};
+  auto kv_k = [m](const LayerW& w) { return w.kq8.kq ? m->kwin : w.kpool; };
+  auto kv_v = [m](const LayerW& w) { return w.kq8.kq ? m->vwin : w.vpool; };
   const bool split = d.prefill_operands == GQA_PREFILL_SPLIT;
   // the GEMM reads Q8_0 quants directly if so configured; otherwise every scheme uses the FP16
   // prefill copies
@@ -907,23 +951,29 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
     for (int l = 0; l < d.n_layers; ++l) {
       const LayerW& w = m->L[l];
       const bool last = l + 1 == d.n_layers;
+      if (w.kq8.kq && pos0 > 0) {             // Q8_0 cache: the earlier positions into the read window
+        Rows win{};
+        win.pos[0] = pos0;
+        win.table[0] = s->d_table;
+        LAUNCH(launch_kv_q8_window(win, 1, pos0, w.kq8, m->kwin, m->vwin, st));
+      }
       if (mv) {
         int rc = matvec(w.wqkv, w.qqkv, w.sqkv, w.bqkv, H, QKV, m->xh, m->xl, H, T, m->s_qkv, m->part);
         if (rc) return rc;
         LAUNCH(launch_qk_rope_kv(false, m->part, m->s_qkv, T * QKV, QKV, NQ, w.q_norm, w.k_norm, eps, m->rcos,
-                                 m->rsin, pos0, s->d_table, none, w.kpool, w.vpool, m->q, T, st));
+                                 m->rsin, pos0, s->d_table, none, kv_k(w), kv_v(w), w.kq8, m->q, T, st));
       } else {
         LAUNCH(launch_gemm(EPI_STORE, split, w.pqkv, gq(w.qqkv), w.sqkv, H, QKV, m->xh, m->xl, H, T, m->qkv, QKV, 1.f,
                            nullptr, nullptr, 0, 1.f, 1, 0, st));
         LAUNCH(launch_qk_rope_kv(false, m->qkv, 0, 0, QKV, NQ, w.q_norm, w.k_norm, eps, m->rcos, m->rsin, pos0,
-                                 s->d_table, none, w.kpool, w.vpool, m->q, T, st));
+                                 s->d_table, none, kv_k(w), kv_v(w), w.kq8, m->q, T, st));
       }
       const bool one = last && out == kOutLast;                // only the final row feeds the logits
       if (one && !final_round) break;
       const int rows = one ? 1 : T, r0 = one ? T - 1 : 0;
       {
         ProfScope ps(m, last ? kProfNever : GQA_PROF_PREFILL_ATTN, st);
-        LAUNCH(launch_attn_prefill(m->q + (int64_t)r0 * QD, NQ, rows, pos0 + r0, s->d_table, w.kpool, w.vpool,
+        LAUNCH(launch_attn_prefill(m->q + (int64_t)r0 * QD, NQ, rows, pos0 + r0, s->d_table, kv_k(w), kv_v(w),
                                    kAttnOutScale, m->oh, m->ol, QD, m->apart, st));
       }
       float* pp = mv ? m->part2 : m->ppart;     // o and down partials
@@ -1366,8 +1416,54 @@ int gqa_debug_read_kv(gqa_session* s, int32_t layer, int32_t pos0, int32_t n, ui
     if (phys < 0) return fail(GQA_E_INVALID, "position %d is in no block of the session", p);
     for (int h = 0; h < kKvHeads; ++h) {
       int64_t off = (((int64_t)phys * kKvHeads + h) * kBlock + (p % kBlock)) * kHeadDim;
-      HIP_TRY(hipMemcpy(k + ((int64_t)i * kKvHeads + h) * kHeadDim, w.kpool + off, kHeadDim * 2, hipMemcpyDeviceToHost));
-      HIP_TRY(hipMemcpy(v + ((int64_t)i * kKvHeads + h) * kHeadDim, w.vpool + off, kHeadDim * 2, hipMemcpyDeviceToHost));
+      uint16_t* kd = k + ((int64_t)i * kKvHeads + h) * kHeadDim;
+      uint16_t* vd = v + ((int64_t)i * kKvHeads + h) * kHeadDim;
+      if (w.kq8.kq) {                          // bf16(scale * code), as attention reads it
+        int8_t c[2][kHeadDim];
+        _Float16 sc[2][kHeadDim / 32];
+        HIP_TRY(hipMemcpy(c[0], w.kq8.kq + off, kHeadDim, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(c[1], w.kq8.vq + off, kHeadDim, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(sc[0], w.kq8.ks + off / 32, kHeadDim / 32 * 2, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(sc[1], w.kq8.vs + off / 32, kHeadDim / 32 * 2, hipMemcpyDeviceToHost));
+        for (int e = 0; e < kHeadDim; ++e) {
+          for (int kv = 0; kv < 2; ++kv) {
+            float x = (float)sc[kv][e / 32] * (float)c[kv][e];
+            uint32_t u;
+            memcpy(&u, &x, 4);
+            u += 0x7FFFu + ((u >> 16) & 1u);
+            (kv ? vd : kd)[e] = (uint16_t)(u >> 16);
+          }
+        }
+      } else {
+        HIP_TRY(hipMemcpy(kd, w.kpool + off, kHeadDim * 2, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(vd, w.vpool + off, kHeadDim * 2, hipMemcpyDeviceToHost));
+      }
+    }
+  }
+  return GQA_OK;
+}
+
+int gqa_debug_read_kv_q8(gqa_session* s, int32_t layer, int32_t pos0, int32_t n, int8_t* kc, uint16_t* ks,
+                         int8_t* vc, uint16_t* vs) {
+  if (!s || !kc || !ks || !vc || !vs) return fail(GQA_E_INVALID, "null argument");
+  gqa_model* m = s->m;
+  if (layer < 0 || layer >= m->d.n_layers) return fail(GQA_E_INVALID, "layer out of range");
+  if (pos0 < 0 || n < 1 || pos0 + n > s->max_pos) return fail(GQA_E_INVALID, "positions out of range");
+  const LayerW& w = m->L[layer];
+  if (!w.kq8.kq) return fail(GQA_E_INVALID, "the model's KV cache is BF16");
+  HIP_TRY(hipDeviceSynchronize());
+  const std::vector<int32_t>& table = s->seq ? s->seq->blocks : s->blocks;
+  for (int i = 0; i < n; ++i) {
+    int p = pos0 + i;
+    int phys = table[p / kBlock];
+    if (phys < 0) return fail(GQA_E_INVALID, "position %d is in no block of the session", p);
+    for (int h = 0; h < kKvHeads; ++h) {
+      const int64_t off = (((int64_t)phys * kKvHeads + h) * kBlock + (p % kBlock)) * kHeadDim;
+      const int64_t o = (int64_t)i * kKvHeads + h;
+      HIP_TRY(hipMemcpy(kc + o * kHeadDim, w.kq8.kq + off, kHeadDim, hipMemcpyDeviceToHost));
+      HIP_TRY(hipMemcpy(vc + o * kHeadDim, w.kq8.vq + off, kHeadDim, hipMemcpyDeviceToHost));
+      HIP_TRY(hipMemcpy(ks + o * 4, w.kq8.ks + off / 32, 8, hipMemcpyDeviceToHost));
+      HIP_TRY(hipMemcpy(vs + o * 4, w.kq8.vs + off / 32, 8, hipMemcpyDeviceToHost));
     }
   }
   return GQA_OK;

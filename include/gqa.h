@@ -83,17 +83,28 @@ typedef struct {
                                dequantised weights made at creation (one FP16 rounding of
                                scale * q; the BF16 GEMM speed); 1: they read the int8 quants and
                                scales directly (exact dequantisation, no copies, slower) */
+  int32_t kv_quant;         /* KV cache format (Kipp Roadmap, status v0.0.4: the opt-in Q8_0 KV
+                               cache, about 1.9x smaller than BF16). GQA_KV_BF16 (0): K/V stored
+                               as BF16. GQA_KV_Q8_0 (1): each head row of 128 K or V values stored
+                               as four Q8_0 blocks of 32 (int8 codes, fp16 scale = fp16(max|x|/127),
+                               codes round(x / (max|x|/127)) half away from zero, the Q8_0 weight
+                               rule): 136 bytes instead of 256. Attention reads
+                               bf16(scale * code); the model also holds one layer's BF16 read
+                               window, rebuilt from the codes before each layer's attention */
 } gqa_model_desc;
 
 #define GQA_PREFILL_SPLIT 0
 #define GQA_PREFILL_FP16 1
+#define GQA_KV_BF16 0
+#define GQA_KV_Q8_0 1
 
 /* Read-only facts about a created model. */
 typedef struct {
   int32_t round_tokens;       /* prefill round width in use */
   int32_t cu_count;           /* compute units of the device */
   int64_t weight_bytes;       /* device bytes of all weights (Q8_0: quants + scales) */
-  int64_t kv_pool_bytes;      /* device bytes of the K and V pools */
+  int64_t kv_pool_bytes;      /* device bytes of the K and V pools (with a Q8_0 cache: codes, scales
+                                 and the one-layer BF16 read window) */
   int64_t scratch_bytes;      /* device bytes of per-model activation scratch */
   int64_t prefill_copy_bytes; /* device bytes of the FP16 copies prefill GEMMs read: projections
                                  (BF16, or dequantised Q8_0 / AFFINE4) and the padded lm_head */
@@ -291,9 +302,16 @@ int gqa_debug_read_affine4(gqa_model* model, int32_t kind, int32_t layer, int32_
                            uint16_t* scales, uint16_t* biases);
 
 /* Copy the BF16 bits of K and V of `layer` for logical positions [pos0, pos0+n) of a session,
- * read through its block table, into host arrays of n x 8 x 128 uint16 each. GQA_E_INVALID for
- * a position whose block a pooled session has not mapped. */
+ * read through its block table, into host arrays of n x 8 x 128 uint16 each (with a Q8_0 cache:
+ * the values attention reads, bf16(scale * code)). GQA_E_INVALID for a position whose block a
+ * pooled session has not mapped. */
 int gqa_debug_read_kv(gqa_session* session, int32_t layer, int32_t pos0, int32_t n, uint16_t* k, uint16_t* v);
+
+/* For a model with a Q8_0 KV cache: copy the int8 codes (n x 8 x 128 each) and the fp16 scale bits
+ * (n x 8 x 4 each) of K and V of `layer` for logical positions [pos0, pos0+n) of a session into
+ * host arrays. GQA_E_INVALID if the cache is BF16 or a position is unmapped. */
+int gqa_debug_read_kv_q8(gqa_session* session, int32_t layer, int32_t pos0, int32_t n, int8_t* kcodes,
+                         uint16_t* kscales, int8_t* vcodes, uint16_t* vscales);
 
 /* Activation scratch buffers of the model (contents are those left by the last call; layouts
  * are internal and may change): copy elements [offset, offset + count) of buffer `which` into
