@@ -32,7 +32,7 @@ PREFIX_PROMPT = 6890        # repeated-prompt length of the prefix-reuse measure
 WEIGHT_BYTES = {"bf16": 2.0, "q8_0": 34 / 32, "affine4": 20 / 32}
 
 
-def algorithmic(shape, prompt, decode, scheme="bf16"):
+def algorithmic(shape, prompt, decode, scheme="bf16", kv_quant="bf16"):
     """Algorithmic FLOP of the prefill and bytes per decode token (weights + KV, no scratch).
     The prefill's output is the last position's logits plus the K/V of every position, so the
     last layer needs q|k|v for every row but attention, o and the MLP for the last row only."""
@@ -44,7 +44,8 @@ def algorithmic(shape, prompt, decode, scheme="bf16"):
     flops = (2 * (L - 1) * P * prompt + attn * (L - 1) * prompt * (prompt + 1) // 2
              + 2 * P_qkv * prompt + 2 * (P - P_qkv) + attn * prompt + 2 * V * H)
     w_bytes = int(WEIGHT_BYTES[scheme] * L * P) + 2 * (V * H + (2 * L + 1) * H + 2 * L * 128) + 2 * H
-    kv_pos = 2 * L * KVD * 2                                            # K and V bytes per cached position
+    # K and V bytes per cached position: BF16, or Q8_0 (an int8 code per value, an fp16 scale per 32)
+    kv_pos = 2 * L * KVD * (2 if kv_quant == "bf16" else 34 / 32)
     ctx_mean = prompt + (decode + 1) / 2.0
     dec_bytes = w_bytes + kv_pos * ctx_mean + kv_pos
     return flops, dec_bytes, w_bytes
@@ -63,7 +64,8 @@ def cpu_baseline(wl, n_prompt, n_decode):
     for l in range(wl.shape.n_layers):
         m.layer(l)
     ids = synth.token_ids(wl.ids_seed, n_prompt)
-    s = oracle.OracleSession(m, oracle.ContiguousKV.for_shape(wl.shape, n_prompt + n_decode + 1))
+    s = oracle.OracleSession(m, oracle.ContiguousKV.for_shape(wl.shape, n_prompt + n_decode + 1),
+                             kv_quant=wl.kv_quant)
     t0 = time.perf_counter()
     lg = s.prefill(ids)
     t1 = time.perf_counter()
@@ -281,7 +283,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="4b", choices=["4b", "0.6b", "tiny", "4b-q8", "4b-a4", "8b-batch"])
+    ap.add_argument("--workload", default="4b", choices=["4b", "0.6b", "tiny", "4b-q8", "4b-a4", "4b-kvq8",
+                                                         "8b-batch"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prompt", type=int, default=2048, help="oracle baseline: prompt tokens")
     ap.add_argument("--cpu-decode", type=int, default=64, help="oracle baseline: decode steps")
@@ -322,7 +325,8 @@ def main():
     # room for the prefix-reuse measurement's pooled sessions beside the timed one
     m = g.Model.from_shape(shape, seed=wl.weight_seed, scheme=wl.scheme,
                            kv_pool_blocks=pool + synth.blocks_for(PREFIX_PROMPT) + 1,
-                           max_positions=max(nb * 32, synth.blocks_for(PREFIX_PROMPT) * 32), prefill=args.prefill)
+                           max_positions=max(nb * 32, synth.blocks_for(PREFIX_PROMPT) * 32), prefill=args.prefill,
+                           kv_quant=wl.kv_quant)
     s = g.Session(m, nb * 32, block_ids=table)
     # the prompt is resident in HBM before timing (eval_prefill_device reads it there)
     ids = torch.from_numpy(synth.token_ids(wl.ids_seed, wl.prompt).astype("int32")).to("cuda")
@@ -364,7 +368,7 @@ def main():
     pre_ms = sorted(e[0].elapsed_time(e[1]) for e in events)[args.steps // 2]
     dec_ms = sorted(e[1].elapsed_time(e[2]) for e in events)[args.steps // 2]
     tokens = wl.prompt + wl.decode
-    flops, dec_bytes, w_bytes = algorithmic(shape, wl.prompt, wl.decode, wl.scheme)
+    flops, dec_bytes, w_bytes = algorithmic(shape, wl.prompt, wl.decode, wl.scheme, wl.kv_quant)
 
     # dominant kernel (decode gate/up matvec): HIP events around each of its launches in one
     # more step identical to the timed ones
@@ -440,7 +444,8 @@ def main():
     rev, dirty = git_rev()
     out = {
         "metric": METRIC if args.workload == "4b" else
-        "prefill tok/s @%d + decode tok/s, %s %s, 1 MI355X (%% roofline)" % (wl.prompt, shape.name, wl.scheme),
+        "prefill tok/s @%d + decode tok/s, %s %s%s, 1 MI355X (%% roofline)" % (
+            wl.prompt, shape.name, wl.scheme, "" if wl.kv_quant == "bf16" else ", Q8_0 KV cache"),
         "value": round(tokens / (ms_step * 1e-3), 2),
         "unit": "tok/s",
         "n_gpus": 1,
@@ -454,7 +459,9 @@ def main():
                   "affine4": "affine4 weights (fp16 MFMA, fp32 accumulate)"}[wl.scheme],
         "data": "synthetic (seeded random-init weights ~N(0,0.02), uniform random token ids)",
         "config": {"workload": f"{shape.name} {wl.scheme}: {wl.prompt}-token prefill + {wl.decode} greedy decode "
-                               f"steps, paged KV (shuffled 32-position blocks)",
+                               f"steps, paged {'BF16' if wl.kv_quant == 'bf16' else 'Q8_0'} KV (shuffled "
+                               f"32-position blocks)",
+                   "kv_cache": wl.kv_quant, "kv_pool_bytes": m.info().kv_pool_bytes,
                    "layers": shape.n_layers, "hidden": shape.hidden, "q_heads": shape.n_q_heads, "kv_heads": 8,
                    "ffn": shape.ffn, "vocab": shape.vocab, "prompt": wl.prompt, "decode_steps": wl.decode,
                    "round_tokens": m.info().round_tokens},

@@ -206,13 +206,14 @@ __global__ __launch_bounds__(256) void qk_rope_kv_kernel(const float* __restrict
 // Read window of a Q8_0 KV cache: the values attention reads, bf16(fp32(scale) * code), of
 // positions [0, rows.pos[b]) of each row b, written to a BF16 pool at the offsets the codes have
 // in the Q8_0 pool (whole 32-position blocks, through the row's block table). grid
-// (ceil(max_n / 32), B), 256 threads; a thread converts 16 codes, which share one scale.
+// (ceil(max_n / 32) * 8, B): one workgroup per (block, KV head), 256 threads; a thread converts
+// 16 codes, which share one scale.
 __global__ __launch_bounds__(256) void kv_q8_window_kernel(Rows rows, KvQ8 kq8, uint16_t* __restrict__ kwin,
                                                           uint16_t* __restrict__ vwin) {
-  const int j = blockIdx.x, b = blockIdx.y;
+  const int j = blockIdx.x / kKvHeads, kvh = blockIdx.x % kKvHeads, b = blockIdx.y;
   if (j * kBlock >= rows.pos[b]) return;
-  const int64_t base = (int64_t)rows.table[b][j] * kKvHeads * kBlock * kHeadDim;
-  constexpr int kChunks = kKvHeads * kBlock * kHeadDim / 16;
+  const int64_t base = ((int64_t)rows.table[b][j] * kKvHeads + kvh) * kBlock * kHeadDim;
+  constexpr int kChunks = kBlock * kHeadDim / 16;
   for (int c = threadIdx.x; c < 2 * kChunks; c += 256) {
     const bool isv = c >= kChunks;
     const int64_t off = base + (int64_t)(c - (isv ? kChunks : 0)) * 16;
@@ -236,8 +237,8 @@ hipError_t launch_kv_q8_window(const Rows& rows, int B, int max_n, const KvQ8& k
                                hipStream_t st) {
   if (B < 1 || B > kMaxBatch || !kq8.kq) return hipErrorInvalidValue;
   if (max_n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kv_q8_window_kernel, dim3((max_n + kBlock - 1) / kBlock, B), dim3(256), 0, st, rows, kq8, kwin,
-                     vwin);
+  hipLaunchKernelGGL(kv_q8_window_kernel, dim3((max_n + kBlock - 1) / kBlock * kKvHeads, B), dim3(256), 0, st, rows,
+                     kq8, kwin, vwin);
   return hipGetLastError();
 }
 

@@ -239,6 +239,7 @@ class Workload:
     paged: str             # "identity" or "shuffled"
     n_seqs: int = 1
     k: int = 1
+    kv_quant: str = "bf16"  # KV cache format: "bf16" or "q8_0"
 
     @property
     def weight_seed(self) -> int:
@@ -259,6 +260,7 @@ WORKLOADS = {
     "4b": Workload("4b", Q4B, "bf16", 2048, 64, "shuffled", k=3),
     "4b-q8": Workload("4b-q8", Q4B, "q8_0", 12800, 32, "shuffled", k=4),
     "4b-a4": Workload("4b-a4", Q4B, "affine4", 2048, 64, "shuffled", k=6),
+    "4b-kvq8": Workload("4b-kvq8", Q4B, "bf16", 2048, 64, "shuffled", k=7, kv_quant="q8_0"),
     "8b-batch": Workload("8b-batch", Q8B, "bf16", 0, 128, "shuffled", n_seqs=32, k=5),
 }
 
