@@ -555,32 +555,28 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
     }
   }
   __syncthreads();
-  // the new position's K/V into the pool, through the block table. Q8_0 cache: thread 4 kv + j
-  // quantises block j of the K (kv = 0) or V row, stores codes and scale, and replaces the row in
-  // LDS by the values attention reads back, bf16(scale * code).
+  // the new position's K/V into the pool, through the block table. Q8_0 cache: thread t < 256
+  // quantises element t % 128 of the K (t < 128) or V row; each 32-dim block is one half-wave, whose
+  // maximum comes from lane exchanges. Codes and scales go to the pool, and the row in LDS is
+  // replaced by the values attention reads back, bf16(scale * code).
   if (kq8.kq) {
+    static_assert(64 * kDecodeWaves >= 2 * kHeadDim, "one thread per K and V element");
     if (owner) {
-      if (tid < 8) {
-        const int kv = tid >> 2, blk = tid & 3;
-        float* src = sq + (G + kv) * kHeadDim + 32 * blk;
-        float amax = 0.f;
+      if (tid < 2 * kHeadDim) {
+        const int kv = tid / kHeadDim, e = tid % kHeadDim;
+        float* src = sq + (G + kv) * kHeadDim;
+        const float x = src[e];
+        float amax = fabsf(x);
 #pragma unroll
-        for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(src[e]));
+        for (int msk = 16; msk >= 1; msk >>= 1) amax = fmaxf(amax, __shfl_xor(amax, msk));
         const float d = q8kv_scale(amax);
         const f16 sc = (f16)d;
+        const int c = q8kv_code(x, d);
         const int64_t off =
-            (int64_t)table[pos >> 5] * kBlockElems + ((int64_t)kvh * kBlock + (pos & 31)) * kHeadDim + 32 * blk;
-        uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          const int c = q8kv_code(src[e], d);
-          w[e >> 2] |= ((uint32_t)c & 0xFFu) << (8 * (e & 3));
-          src[e] = bf16_bits_to_f32(q8kv_read_bf16(sc, c));
-        }
-        int8_t* dq = (kv ? kq8.vq : kq8.kq) + off;
-        *(uint4*)dq = uint4{w[0], w[1], w[2], w[3]};
-        *(uint4*)(dq + 16) = uint4{w[4], w[5], w[6], w[7]};
-        (kv ? kq8.vs : kq8.ks)[off >> 5] = sc;
+            (int64_t)table[pos >> 5] * kBlockElems + ((int64_t)kvh * kBlock + (pos & 31)) * kHeadDim;
+        (kv ? kq8.vq : kq8.kq)[off + e] = (int8_t)c;
+        if ((e & 31) == 0) (kv ? kq8.vs : kq8.ks)[(off >> 5) + (e >> 5)] = sc;
+        src[e] = bf16_bits_to_f32(q8kv_read_bf16(sc, c));
       }
       __syncthreads();
     }
