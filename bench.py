@@ -14,7 +14,6 @@ launches) and the CPU oracle on a bounded sample are reported beside it.
 import argparse
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -74,7 +73,7 @@ def cpu_baseline(wl, n_prompt, n_decode):
     t2 = time.perf_counter()
     return {"value": round((n_prompt + n_decode) / (t2 - t0), 3), "unit": "tok/s", "cores": cores, "kind": "oracle",
             "prefill_tok_s": round(n_prompt / (t1 - t0), 3), "decode_tok_s": round(n_decode / (t2 - t1), 3),
-            "sample": f"{wl.shape.name} {wl.scheme} oracle (NumPy FP32, OpenBLAS on {cores} cores): {n_prompt}-token prompt "
+            "sample": f"{wl.shape.name} {wl.scheme} oracle (NumPy FP32 on {cores} cores): {n_prompt}-token prompt "
                       f"+ {n_decode} greedy decode steps, weight generation untimed"}
 
 
@@ -246,7 +245,6 @@ def bench_batch(args):
     kv_bytes = 2 * sh.n_layers * sh.kv_dim * 2 * ctx_mean * B             # K/V read per batched step
     _, _, w_bytes = algorithmic(sh, 0, 0, wl.scheme)
     step_ms = ms_step / wl.decode
-    rev, dirty = git_rev()
     out = {
         "metric": "batched decode tok/s, Qwen3-8B-shape BF16, 32 sessions, 1 MI355X",
         "value": round(B * wl.decode / (ms_step * 1e-3), 1), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
@@ -261,21 +259,63 @@ def bench_batch(args):
         "hbm": {"weight_bytes": w_bytes, "kv_bytes_per_batched_step": int(kv_bytes),
                 "achieved_gbs": round((w_bytes + kv_bytes) / (step_ms * 1e-3) / 1e9, 1),
                 "frac": round((w_bytes + kv_bytes) / (step_ms * 1e-3) / PEAK_HBM, 4)},
-        "commit": rev, "dirty": dirty, "device": torch.cuda.get_device_name(0),
     }
+    out.update(run_record(g))
     for se in sess:
         se.close()
     m.close()
     print(json.dumps(out), flush=True)
 
 
-def git_rev():
+def run_record(g):
+    """Build, software and hardware record of the run (Kipp Reproducing, "Benchmarks": commit,
+    dirty state, binary, compiler, hardware). The commit and dirty state are the ones baked into
+    the library when it was built (git is not needed where the bench runs); "library_current"
+    says whether the library's sources hash equals the current tree's, i.e. whether the binary
+    measured was built from the sources beside it. Unknown facts are null, never guessed."""
+    import hashlib
+    import platform
+    import numpy as np
+    import torch
+    from dense_gqa_decoder_amd import build as b
+    info = g.gqa_build_info()
+    with open(g.lib_path, "rb") as f:
+        lib_sha = hashlib.sha256(f.read()).hexdigest()
+    rocm = None
+    for p in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(p) as f:
+                rocm = f.read().strip()
+            break
+        except OSError:
+            pass
+    cpu = None
     try:
-        r = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True, text=True)
-        d = subprocess.run(["git", "status", "--porcelain"], cwd=ROOT, capture_output=True, text=True)
-        return r.stdout.strip() or None, bool(d.stdout.strip())
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        bl = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = " ".join(str(bl.get(k)) for k in ("name", "version") if bl.get(k)) or None
     except Exception:
-        return None, None
+        pass
+    dev = g.gqa_device_describe(torch.cuda.current_device())
+    return {
+        "commit": info.get("commit"), "dirty": info.get("dirty"),
+        "library": {"sha256": lib_sha, "sources_sha256": info.get("sources_sha256"),
+                    "library_current": info.get("sources_sha256") == b.sources_sha256(),
+                    "hipcc": info.get("hipcc"), "flags": info.get("flags"), "built_utc": info.get("built_utc")},
+        "software": {"rocm": rocm, "hip_runtime": dev["runtime_version"], "hip_driver": dev["driver_version"],
+                     "torch": torch.__version__, "torch_hip": getattr(torch.version, "hip", None),
+                     "python": platform.python_version(), "numpy": np.__version__},
+        "device": {"name": dev["name"], "arch": dev["arch"], "cu_count": dev["cu_count"],
+                   "clock_mhz": dev["clock_khz"] / 1000.0, "memory_clock_mhz": dev["memory_clock_khz"] / 1000.0,
+                   "memory_bus_bits": dev["memory_bus_bits"], "memory_bytes": dev["total_memory"]},
+        "host": {"cpu_model": cpu, "cores_available": len(os.sched_getaffinity(0)), "blas": blas},
+    }
 
 
 def main():
@@ -383,8 +423,23 @@ def main():
     gu_bytes = int(2 * F * H * WEIGHT_BYTES[wl.scheme]) + H * 4 + F * 4   # weights + x hi/lo + m hi/lo, one row
     gu_ms = kernels["decode_gateup"][1]
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
-    pgu_flop = 2.0 * wl.prompt * 2 * F * H
+    # Prefill GEMM and attention launches: layers 0..L-2 of every round of more than 32 rows
+    # (shorter rounds use the matvec; the last layer runs its MLP and attention for one row and
+    # is not recorded). FLOP per launch = the class's FLOP over all its launches / launches.
+    R = m.info().round_tokens
+    rounds = [(o, min(R, wl.prompt - o)) for o in range(0, wl.prompt, R)]
+    gemm_rounds = [(o, t) for o, t in rounds if t > 32]
+    n_rec = (shape.n_layers - 1) * len(gemm_rounds)
+    assert kernels["prefill_gateup"][0] == n_rec, (kernels["prefill_gateup"][0], n_rec)
+    pgu_flop = sum(2.0 * t * 2 * F * H for _, t in gemm_rounds) * (shape.n_layers - 1) / n_rec
     pgu_ms = kernels["prefill_gateup"][1]
+    # causal attention of a round at offset o with t rows: q.K and P.V over o + i + 1 keys for row i
+    attn_unit = shape.n_q_heads * 4 * shape.head_dim
+    pat_flop = sum(attn_unit * (t * o + t * (t + 1) / 2) for o, t in rounds) * (shape.n_layers - 1) / \
+        max(kernels["prefill_attn"][0], 1)
+    pat_ms = kernels["prefill_attn"][1]
+    for name, fl, ms in (("prefill gate/up", pgu_flop, pgu_ms), ("prefill attention", pat_flop, pat_ms)):
+        assert fl / (ms * 1e-3) <= PEAK_BF16_FLOPS, f"{name}: rate above the MFMA peak: accounting error"
 
     # Multi-row evaluation of the same prompt, outside the step: every row's logits (eval_n) and
     # the prompt's next-token scores (eval_scored), median of three, HIP events on the stream;
@@ -441,7 +496,6 @@ def main():
             ps.close()
     cold_ms, warm_ms = sorted(cold)[1], sorted(warm)[1]
 
-    rev, dirty = git_rev()
     out = {
         "metric": METRIC if args.workload == "4b" else
         "prefill tok/s @%d + decode tok/s, %s %s%s, 1 MI355X (%% roofline)" % (
@@ -482,8 +536,15 @@ def main():
                              "bound": "mfma", "achieved": round(pgu_flop / (pgu_ms * 1e-3) / 1e12, 1),
                              "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                              "frac": round(pgu_flop / (pgu_ms * 1e-3) / PEAK_BF16_FLOPS, 4),
-                             "launch_us": round(pgu_ms * 1e3, 1),
-                             "attn_launch_us": round(kernels["prefill_attn"][1] * 1e3, 1)},
+                             "launch_us": round(pgu_ms * 1e3, 1), "flop_per_launch": pgu_flop,
+                             "launches": kernels["prefill_gateup"][0], "rounds": [t for _, t in rounds]},
+        "prefill_attn_roofline": {"kernel": "attn_prefill_kernel: causal GQA flash attention over the paged "
+                                            "BF16 KV (BF16 MFMA, q and P as BF16 hi/lo)",
+                                  "bound": "mfma", "achieved": round(pat_flop / (pat_ms * 1e-3) / 1e12, 1),
+                                  "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                                  "frac": round(pat_flop / (pat_ms * 1e-3) / PEAK_BF16_FLOPS, 4),
+                                  "launch_us": round(pat_ms * 1e3, 1), "flop_per_launch": pat_flop,
+                                  "launches": kernels["prefill_attn"][0]},
         "multi_row": {"rows": wl.prompt, "eval_n_ms": round(evn_ms, 3),
                       "eval_n_tok_s": round(wl.prompt / (evn_ms * 1e-3), 1),
                       "eval_scored_ms": round(evs_ms, 3),
@@ -496,10 +557,11 @@ def main():
                                   "achieved_gbs": round(lm_bytes / (lm_ms * 1e-3) / 1e9, 1)}},
         "prefix_reuse": {"prompt": PREFIX_PROMPT, "reused_positions": reused[1], "ttft_cold_ms": round(cold_ms, 3),
                          "ttft_warm_ms": round(warm_ms, 3), "speedup": round(cold_ms / warm_ms, 1)},
-        "commit": rev, "dirty": dirty, "device": torch.cuda.get_device_name(0),
     }
+    out.update(run_record(g))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, n_prompt=min(args.cpu_prompt, wl.prompt), n_decode=args.cpu_decode)
+        out["cpu_baseline"].update(cpu_model=out["host"]["cpu_model"], blas=out["host"]["blas"])
     s.close()
     m.close()
     print(json.dumps(out), flush=True)

@@ -20,7 +20,7 @@ from ._lib import (  # noqa: F401
     gqa_session_eval_batch, gqa_session_eval_n, gqa_session_eval_scored, gqa_session_truncate,
     gqa_session_create_pooled, gqa_session_publish, gqa_session_reused,
     gqa_model_check_device_error, gqa_model_profile, gqa_model_profile_read, GQA_PROF,
-    gqa_last_error, gqa_debug_read_weight,
+    gqa_last_error, gqa_build_info, gqa_device_describe, DeviceDesc, gqa_debug_read_weight,
     gqa_debug_read_q8, gqa_debug_read_affine4, gqa_debug_read_kv, gqa_debug_read_kv_q8, gqa_debug_read_rope,
 )
 from .api import Model, Session  # noqa: F401

@@ -47,6 +47,14 @@ class ModelInfo(ctypes.Structure):
                 ("prefix_hits", ctypes.c_int64), ("prefix_evictions", ctypes.c_int64)]
 
 
+class DeviceDesc(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 256), ("arch", ctypes.c_char * 64), ("cu_count", ctypes.c_int32),
+                ("clock_khz", ctypes.c_int32), ("memory_clock_khz", ctypes.c_int32),
+                ("memory_bus_bits", ctypes.c_int32), ("total_memory", ctypes.c_int64),
+                ("l2_bytes", ctypes.c_int64), ("lds_per_cu", ctypes.c_int64), ("runtime_version", ctypes.c_int32),
+                ("driver_version", ctypes.c_int32)]
+
+
 _lib = None
 P = ctypes.c_void_p
 I32 = ctypes.c_int32
@@ -74,6 +82,8 @@ _SIGS = {
     "gqa_model_profile_read": (I32, [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int64)]),
     "gqa_last_error": (ctypes.c_char_p, []),
+    "gqa_build_info": (ctypes.c_char_p, []),
+    "gqa_device_describe": (I32, [I32, ctypes.POINTER(DeviceDesc)]),
     "gqa_debug_read_weight": (I32, [P, I32, I32, I32, I32, P]),
     "gqa_debug_read_q8": (I32, [P, I32, I32, I32, I32, P, P]),
     "gqa_debug_read_affine4": (I32, [P, I32, I32, I32, I32, P, P, P]),
@@ -114,6 +124,19 @@ def _check(rc: int):
 
 def gqa_last_error() -> str:
     return lib().gqa_last_error().decode(errors="replace")
+
+
+def gqa_build_info() -> dict:
+    import json
+    return json.loads(lib().gqa_build_info().decode())
+
+
+def gqa_device_describe(device: int = 0) -> dict:
+    d = DeviceDesc()
+    _check(lib().gqa_device_describe(device, ctypes.byref(d)))
+    out = {k: getattr(d, k) for k, _ in DeviceDesc._fields_}
+    out["name"], out["arch"] = d.name.decode(errors="replace"), d.arch.decode(errors="replace")
+    return out
 
 
 def gqa_model_create(desc: ModelDesc, seed: int) -> int:

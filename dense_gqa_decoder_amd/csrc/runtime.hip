@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "../../include/gqa.h"
+#include "_build/build_info.h"   // GQA_BUILD_INFO, written by build.py before every build
 #include "gqa_common.h"
 #include "kv_pool.h"
 
@@ -238,6 +239,31 @@ uint64_t tensor_key(uint64_t seed, int L, int kind, int layer) {
 extern "C" {
 
 const char* gqa_last_error(void) { return g_err.c_str(); }
+
+const char* gqa_build_info(void) { return GQA_BUILD_INFO; }
+
+int gqa_device_describe(int32_t device, gqa_device_desc* out) {
+  g_err.clear();
+  if (!out) return fail(GQA_E_INVALID, "null out pointer");
+  int n = 0;
+  HIP_TRY(hipGetDeviceCount(&n));
+  if (device < 0 || device >= n) return fail(GQA_E_INVALID, "device %d outside [0, %d)", device, n);
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, device));
+  memset(out, 0, sizeof(*out));
+  snprintf(out->name, sizeof(out->name), "%s", prop.name);
+  snprintf(out->arch, sizeof(out->arch), "%s", prop.gcnArchName);
+  out->cu_count = prop.multiProcessorCount;
+  out->clock_khz = prop.clockRate;
+  out->memory_clock_khz = prop.memoryClockRate;
+  out->memory_bus_bits = prop.memoryBusWidth;
+  out->total_memory = (int64_t)prop.totalGlobalMem;
+  out->l2_bytes = prop.l2CacheSize;
+  out->lds_per_cu = (int64_t)prop.maxSharedMemoryPerMultiProcessor;
+  HIP_TRY(hipRuntimeGetVersion(&out->runtime_version));
+  HIP_TRY(hipDriverGetVersion(&out->driver_version));
+  return GQA_OK;
+}
 
 int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out) {
   g_err.clear();

@@ -267,6 +267,32 @@ int gqa_model_profile_read(gqa_model* model, int64_t* launches, double* total_ms
 /* Message of the last failure on this thread ("" if none). Valid until the next call. */
 const char* gqa_last_error(void);
 
+/* Build record baked into the library when it was compiled (Kipp Reproducing, "Benchmarks":
+ * every benchmark record carries the commit, whether the tree was dirty, the binary and the
+ * compiler): a static JSON object string with "commit" (git HEAD at build time, or null),
+ * "dirty" (true / false, or null when unknown), "sources_sha256" (hash of the library's
+ * sources and header), "hipcc" (the compiler's version line), "flags" and "built_utc". Never
+ * NULL; owned by the library. */
+const char* gqa_build_info(void);
+
+/* Hardware record of HIP device `device` for benchmark records (same source): fills *out.
+ * GQA_E_INVALID for a device index out of range or a NULL out; GQA_E_HIP if the runtime
+ * query fails. Does not require a gfx950 device (it only reports). */
+typedef struct {
+  char name[256];           /* marketing name reported by the runtime */
+  char arch[64];            /* gcnArchName, e.g. "gfx950:sramecc+:xnack-" */
+  int32_t cu_count;         /* compute units */
+  int32_t clock_khz;        /* peak shader clock reported by the runtime */
+  int32_t memory_clock_khz; /* peak memory clock reported by the runtime */
+  int32_t memory_bus_bits;  /* memory bus width */
+  int64_t total_memory;     /* device memory bytes */
+  int64_t l2_bytes;         /* L2 bytes as reported */
+  int64_t lds_per_cu;       /* LDS bytes per compute unit */
+  int32_t runtime_version;  /* hipRuntimeGetVersion */
+  int32_t driver_version;   /* hipDriverGetVersion */
+} gqa_device_desc;
+int gqa_device_describe(int32_t device, gqa_device_desc* out);
+
 /* ---- inspection, for tests (synchronous) ---- */
 
 /* Tensor kinds for gqa_debug_read_weight, in the generator's order. */

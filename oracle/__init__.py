@@ -37,6 +37,6 @@ against a library routine (transformers' Qwen3 model) with the BF16 KV rounding
 switched off, against brute force, closed forms and invariants; absolute
 agreement with trained Qwen3 checkpoints is parity unpinned (no trained weights).
 """
-from .model import OracleModel, OracleSession, ContiguousKV, PagedKV, kv_q8_0_roundtrip, nmse, next_token_log_probs  # noqa: F401
+from .model import OracleModel, OracleSession, ContiguousKV, PagedKV, kv_q8_0_roundtrip, nmse, next_token_log_probs, final_logits  # noqa: F401
 from .q8_0 import quantize_q8_0, dequantize_q8_0  # noqa: F401
 from .affine4 import quantize_affine4, dequantize_affine4  # noqa: F401

@@ -202,6 +202,14 @@ class OracleModel:
         return w
 
 
+def final_logits(model: OracleModel, x: np.ndarray) -> np.ndarray:
+    """logits = (RMSNorm(x) * w_final) W_lm^T for residual rows x [rows, hidden]; W_lm is the
+    embedding when tied, the separate lm_head otherwise (Kipp Model Support, "Validated
+    results", qwen3-8b-base)."""
+    x = np.asarray(x, dtype=np.float32)
+    return rmsnorm(x, model.final_norm, model.shape.rms_eps) @ model.lm_head.T
+
+
 def kv_q8_0_roundtrip(x: np.ndarray) -> np.ndarray:
     """What attention reads back from a Q8_0 KV cache (Kipp Roadmap, status v0.0.4: the opt-in
     Q8_0 KV cache). Each head row of 128 FP32 values is stored as four Q8_0 blocks of 32 (the
@@ -224,6 +232,14 @@ class OracleSession:
 
     def forward(self, ids, all_logits: bool = False):
         """Append tokens ``ids`` at positions pos.. and return logits of the last (or every) new position."""
+        x = self.residual(ids)
+        xs = x if all_logits else x[-1:]
+        logits = final_logits(self.m, xs)
+        return logits if all_logits else logits[0]
+
+    def residual(self, ids):
+        """Append tokens ``ids`` at positions pos.. and return the residual stream x [T, hidden]
+        of the new positions after the last layer (the input of the final norm)."""
         sh, m = self.m.shape, self.m
         ids = np.asarray(ids, dtype=np.int64)
         if ids.min() < 0 or ids.max() >= sh.vocab:
@@ -252,9 +268,7 @@ class OracleSession:
             b = rmsnorm(x, w["ffn_norm"], eps)
             x = x + (silu(b @ w["gate"].T) * (b @ w["up"].T)) @ w["down"].T
         self.pos += T
-        xs = x if all_logits else x[-1:]
-        logits = rmsnorm(xs, m.final_norm, eps) @ m.lm_head.T
-        return logits if all_logits else logits[0]
+        return x
 
     def prefill(self, ids):
         return self.forward(ids)

@@ -6,17 +6,22 @@ Random-init logits are close to i.i.d. Gaussian over 151,936 entries, so the top
 tiny and two correct FP32 implementations (the oracle and a more exact one) already differ by
 NMSE ~1e-7 through BF16 K/V rounding flips. A position whose argmax differs is accepted as a
 near tie only if the oracle's top-2 margin is below 4x the RMS logit error actually observed at
-that position and the GPU's pick is the oracle's runner-up; every other mismatch fails.
+that position and the GPU's pick is the oracle's runner-up; every other mismatch fails. Near
+ties are never hidden: every gate's summary (positions, worst NMSE, mismatches, near ties) is
+kept in ``SUMMARIES`` and printed at the end of the pytest run by ``conftest.py``.
+
+The NMSE and the argmax tie rule are the oracle's own functions (pinned in
+``test_oracle_pins.py``).
 """
 import numpy as np
 
+from oracle.model import argmax as oracle_argmax
+from oracle.model import nmse
+
 NMSE_BOUND = 1e-4
 
-
-def nmse(y, ref):
-    y = np.asarray(y, dtype=np.float64)
-    r = np.asarray(ref, dtype=np.float64)
-    return float(np.sum((y - r) ** 2) / np.sum(r ** 2))
+#: one dict per finished gate, in the order the gates finished
+SUMMARIES = []
 
 
 class Gate:
@@ -27,24 +32,30 @@ class Gate:
         g = np.asarray(gpu_logits, dtype=np.float32)
         r = np.asarray(ref_logits, dtype=np.float32)
         e = nmse(g, r)
-        ra = int(np.argmax(r))
-        ga = int(np.argmax(g)) if gpu_argmax is None else int(gpu_argmax)
-        top2 = np.partition(r, -2)[-2:]
-        margin = float(top2[1] - top2[0])
+        ra = oracle_argmax(r)
+        ga = oracle_argmax(g) if gpu_argmax is None else int(gpu_argmax)
+        order = np.argsort(-r, kind="stable")            # descending, lowest index first on ties
+        margin = float(r[order[0]] - r[order[1]])
         rms = float(np.sqrt(np.mean((g.astype(np.float64) - r) ** 2)))
-        near_tie = ga != ra and margin < 4 * rms and ga == int(np.argsort(r)[-2])   # runner-up
+        near_tie = ga != ra and margin < 4 * rms and ga == int(order[1])
         self.rows.append(dict(pos=pos, nmse=e, ok=ga == ra, near_tie=near_tie, margin=margin, rms=rms))
         return e
 
+    def worst(self):
+        return max(self.rows, key=lambda r: r["nmse"])
+
     def assert_ok(self):
         assert self.rows, "nothing checked"
-        worst = max(r["nmse"] for r in self.rows)
+        w = self.worst()
         bad = [r for r in self.rows if not r["ok"] and not r["near_tie"]]
         ties = [r for r in self.rows if r["near_tie"]]
-        print(f"[{self.name}] positions={len(self.rows)} worst_nmse={worst:.3e} argmax_mismatch={len(bad)} "
-              f"near_ties={len(ties)}", flush=True)
+        SUMMARIES.append(dict(name=self.name, positions=len(self.rows), worst_nmse=w["nmse"],
+                              worst_pos=w["pos"], mismatches=len(bad), near_ties=len(ties),
+                              near_tie_pos=[r["pos"] for r in ties]))
+        print(f"[{self.name}] positions={len(self.rows)} worst_nmse={w['nmse']:.3e} (at {w['pos']}) "
+              f"argmax_mismatch={len(bad)} near_ties={len(ties)}", flush=True)
         for r in ties:
             print(f"  near tie at {r['pos']}: margin {r['margin']:.3e} rms {r['rms']:.3e}", flush=True)
-        assert worst <= NMSE_BOUND, f"worst NMSE {worst:.3e} > {NMSE_BOUND}"
+        assert w["nmse"] <= NMSE_BOUND, f"worst NMSE {w['nmse']:.3e} > {NMSE_BOUND}"
         assert not bad, f"argmax mismatches: {bad[:5]}"
-        return worst
+        return w["nmse"]

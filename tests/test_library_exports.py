@@ -45,7 +45,7 @@ def test_create_without_gpu_reports_an_error():
 
 
 def test_struct_layouts_match_the_header(tmp_path):
-    """The ctypes mirrors of gqa_model_desc and gqa_model_info have the header's field offsets and
+    """The ctypes mirrors of gqa_model_desc, gqa_model_info and gqa_device_desc have the header's field offsets and
     sizes (compiled from include/gqa.h with the host C compiler)."""
     import ctypes
     import shutil
@@ -54,7 +54,7 @@ def test_struct_layouts_match_the_header(tmp_path):
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no host C compiler")
-    structs = {"gqa_model_desc": _lib.ModelDesc, "gqa_model_info": _lib.ModelInfo}
+    structs = {"gqa_model_desc": _lib.ModelDesc, "gqa_model_info": _lib.ModelInfo, "gqa_device_desc": _lib.DeviceDesc}
     body = ""
     for cname, py in structs.items():
         body += '  printf("%s size %%zu\\n", sizeof(%s));\n' % (cname, cname)
@@ -76,3 +76,14 @@ def test_struct_layouts_match_the_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for fname, _ in py._fields_:
             assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
+
+
+def test_build_info_is_baked_into_the_library():
+    """The build record (commit, dirty state, sources hash, compiler) is a JSON object compiled
+    into the library, and its sources hash is that of the current sources (the library in the
+    tree was built from them)."""
+    import dense_gqa_decoder_amd as g
+    from dense_gqa_decoder_amd import build
+    info = g.gqa_build_info()
+    assert set(info) >= {"commit", "dirty", "sources_sha256", "hipcc", "flags", "built_utc"}
+    assert info["sources_sha256"] == build.sources_sha256()

@@ -526,3 +526,45 @@ def test_kv_q8_0_session_invariants():
     assert 0 < worst < 1e-3, worst
     with pytest.raises(ValueError):
         oracle.OracleSession(m, oracle.ContiguousKV.for_shape(shape, 64), kv_quant="q4")
+
+
+def test_nmse_closed_forms():
+    """The gate's NMSE (Kipp Model Support, "What the gates check"; the pages do not define it,
+    the reading is sum((y - ref)^2) / sum(ref^2) over one position's logits): closed forms that
+    fail if the normaliser is the candidate's energy, if absolute instead of squared errors are
+    summed, or if the sums are accumulated in FP32."""
+    r = np.array([3.0, 4.0], dtype=np.float32)
+    assert om.nmse(np.array([3.0, 4.5], dtype=np.float32), r) == 0.25 / 25.0
+    assert om.nmse(r, r) == 0.0
+    # normaliser is the reference's energy, not the candidate's: nmse(2r, r) = 1, nmse(r, 2r) = 1/4
+    assert om.nmse(2 * r, r) == 1.0
+    assert om.nmse(r, 2 * r) == 0.25
+    # squared, not absolute, errors
+    ones = np.ones(4, dtype=np.float32)
+    assert om.nmse(np.array([1.5, 0.5, 1.0, 1.0], dtype=np.float32), ones) == 0.125
+    # relative scaling y = (1 + c) r gives c^2 for any r
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal(1000)
+    assert abs(om.nmse((1 + 2.0 ** -10) * z, z) / 2.0 ** -20 - 1) < 1e-12
+    # scale invariance
+    y = z + 1e-3 * rng.standard_normal(1000)
+    assert abs(om.nmse(7.5 * y, 7.5 * z) / om.nmse(y, z) - 1) < 1e-12
+    # float64 accumulation over a full vocabulary of FP32 logits: every term is exact in float64
+    big = np.full(synth.VOCAB, 1000.0, dtype=np.float32)
+    off = big + np.float32(1e-3)                      # 1000.0009765625 in FP32: error 2^-10 exactly
+    want = (2.0 ** -10) ** 2 / 1000.0 ** 2
+    assert abs(om.nmse(off, big) / want - 1) < 1e-12
+
+
+def test_argmax_lowest_index_on_ties():
+    """Argmax ties go to the lowest index (the reading for greedy decoding; the pages fix none)."""
+    assert om.argmax(np.array([0.0, 5.0, 5.0, 1.0], dtype=np.float32)) == 1
+    assert om.argmax(np.full(17, -2.5, dtype=np.float32)) == 0
+    assert om.argmax(np.array([-np.inf, -1.0, -1.0], dtype=np.float32)) == 1
+    z = np.random.default_rng(4).standard_normal(synth.VOCAB).astype(np.float32)
+    top = z.max() + 1
+    z[100000] = top
+    z[7] = top
+    assert om.argmax(z) == 7
+    z[7] = np.nextafter(top, np.float32(-np.inf))     # one ulp below: the later index wins
+    assert om.argmax(z) == 100000
