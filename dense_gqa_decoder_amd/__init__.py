@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     GQA_T, GqaError, ModelDesc, ModelInfo, lib, lib_path, load,
     gqa_model_create, gqa_model_destroy, gqa_model_get_info, gqa_session_create, gqa_session_destroy,
     gqa_session_reset, gqa_session_position, gqa_session_eval_prefill, gqa_session_eval_decode,
+    gqa_session_eval_decode_static,
     gqa_session_eval_batch, gqa_session_eval_n, gqa_session_eval_scored, gqa_session_truncate,
     gqa_session_create_pooled, gqa_session_publish, gqa_session_reused,
     gqa_model_check_device_error, gqa_model_profile, gqa_model_profile_read, GQA_PROF,

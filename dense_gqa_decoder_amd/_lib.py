@@ -77,6 +77,7 @@ _SIGS = {
     "gqa_session_truncate": (I32, [P, I32]),
     "gqa_session_eval_decode": (I32, [P, P, I32, P, P, P]),
     "gqa_session_eval_batch": (I32, [P, I32, P, I32, P, P, P]),
+    "gqa_session_eval_decode_static": (I32, [P, P, I32, P, P, P]),
     "gqa_model_check_device_error": (I32, [P, P]),
     "gqa_model_profile": (I32, [P, I32]),
     "gqa_model_profile_read": (I32, [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
@@ -209,6 +210,10 @@ def gqa_session_truncate(session, pos) -> None:
 
 def gqa_session_eval_decode(session, id_ptr, id_on_device, logits_ptr, argmax_ptr, stream) -> None:
     _check(lib().gqa_session_eval_decode(session, id_ptr, id_on_device, logits_ptr, argmax_ptr, stream))
+
+
+def gqa_session_eval_decode_static(session, id_ptr, id_on_device, logits_ptr, argmax_ptr, stream) -> None:
+    _check(lib().gqa_session_eval_decode_static(session, id_ptr, id_on_device, logits_ptr, argmax_ptr, stream))
 
 
 def gqa_session_eval_batch(sessions_ptr, B, ids_ptr, ids_on_device, logits_ptr, argmax_ptr, stream) -> None:

@@ -201,6 +201,17 @@ class Session:
             h = np.asarray([token], dtype=np.int32)
             L.gqa_session_eval_decode(self.handle, h.ctypes.data, 0, _ptr(logits), _ptr(argmax), _stream(stream))
 
+    def decode_static(self, token, logits, argmax=None, stream=None):
+        """decode() through gqa_session_eval_decode_static: the call's scratch is the library's
+        static device array, nothing is allocated."""
+        if hasattr(token, "data_ptr"):
+            L.gqa_session_eval_decode_static(self.handle, token.data_ptr(), 1, _ptr(logits), _ptr(argmax),
+                                             _stream(stream))
+        else:
+            h = np.asarray([token], dtype=np.int32)
+            L.gqa_session_eval_decode_static(self.handle, h.ctypes.data, 0, _ptr(logits), _ptr(argmax),
+                                             _stream(stream))
+
     def read_kv(self, layer, pos0, n):
         k = np.empty((n, 8, 128), dtype=np.uint16)
         v = np.empty((n, 8, 128), dtype=np.uint16)

@@ -10,10 +10,13 @@
 namespace gqa {
 
 // x[t][:] = fp32(E[ids[t]][:]). Out-of-range ids (possible only for device-resident ids)
-// poison the row with NaN and set the model's error word.
+// poison the row with NaN and set the model's error word. Workgroup 0 also clears `zero`
+// (nzero ints, e.g. the decode attention's arrival counters of a static scratch).
 __global__ void embed_kernel(const uint16_t* __restrict__ E, const int32_t* __restrict__ ids, int H, int vocab,
-                             float* __restrict__ x, int32_t* __restrict__ err) {
+                             float* __restrict__ x, int32_t* __restrict__ err, int32_t* __restrict__ zero, int nzero) {
   int t = blockIdx.x;
+  if (t == 0)
+    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
   int id = ids[t];
   float* xr = x + (int64_t)t * H;
   if (id < 0 || id >= vocab) {
@@ -291,8 +294,9 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float2* __restrict__
 }
 
 hipError_t launch_embed(const uint16_t* E, const int32_t* ids, int T, int H, int vocab, float* x, int32_t* err,
-                        hipStream_t st) {
-  hipLaunchKernelGGL(embed_kernel, dim3(T), dim3(256), 0, st, E, ids, H, vocab, x, err);
+                        hipStream_t st, int32_t* zero, int nzero) {
+  if (nzero < 0 || (nzero > 0 && !zero)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(embed_kernel, dim3(T), dim3(256), 0, st, E, ids, H, vocab, x, err, zero, nzero);
   return hipGetLastError();
 }
 

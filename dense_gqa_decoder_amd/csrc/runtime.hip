@@ -33,7 +33,7 @@ hipError_t launch_prefill_copy_q8(const int8_t* q, const f16* d, f16* dst, int64
 hipError_t launch_prefill_copy_affine4(const uint8_t* q4, const f16* d, const f16* bias, f16* dst, int64_t rows,
                                        int64_t cols, hipStream_t st);
 hipError_t launch_embed(const uint16_t* E, const int32_t* ids, int T, int H, int vocab, float* x, int32_t* err,
-                        hipStream_t st);
+                        hipStream_t st, int32_t* zero = nullptr, int nzero = 0);
 hipError_t launch_rmsnorm(float* x, int ldx, const float* part, int nsplit, int part_stride_split, int part_ld,
                           float part_scale, const uint16_t* w, int H, float eps, float out_scale, f16* yhi, f16* ylo,
                           int ldy, int rows, hipStream_t st);
@@ -233,6 +233,101 @@ uint64_t tensor_key(uint64_t seed, int L, int kind, int layer) {
     tid = 1 + 11 * layer + (kind - GQA_T_ATTN_NORM);
   return splitmix(seed, (uint64_t)tid);
 }
+
+// Per-call scratch of a decode: the residual stream (two buffers for the split-K path), the
+// projection outputs or split partials, the operand rows, the attention chunk partials and
+// arrival counters, the sum-of-squares partials and the argmax candidates. The model's own
+// buffers by default; gqa_session_eval_decode_static carves them from a static device array.
+// `zero` (nzero ints, or null) is cleared by the first kernel of the call.
+struct DecodeScratch {
+  float *x = nullptr, *x2 = nullptr, *part = nullptr, *part2 = nullptr, *ss = nullptr, *apart = nullptr;
+  int32_t* counters = nullptr;
+  f16 *oh = nullptr, *ol = nullptr, *mh = nullptr, *ml = nullptr, *xh = nullptr, *xl = nullptr;
+  float2* cand = nullptr;
+  int64_t pstride = 0;     // stride of split-K partial ranges (floats)
+  int32_t* zero = nullptr;
+  int nzero = 0;
+};
+
+DecodeScratch model_scratch(gqa_model* m) {
+  DecodeScratch sc;
+  sc.x = m->x;
+  sc.x2 = m->x2;
+  sc.part = m->part;
+  sc.part2 = m->part2;
+  sc.ss = m->ss;
+  sc.apart = m->apart;
+  sc.counters = m->counters;
+  sc.oh = m->oh;
+  sc.ol = m->ol;
+  sc.mh = m->mh;
+  sc.ml = m->ml;
+  sc.xh = m->xh;
+  sc.xl = m->xl;
+  sc.cand = m->cand;
+  sc.pstride = m->part_floats / 8;
+  return sc;
+}
+
+// ---- allocation-free decode (gqa_session_eval_decode_static)
+// The per-call decode scratch of one row lives in this file-scope device array, one copy per
+// device, held until the process ends. Host code never uses the name `scratch` as an address
+// (on the host it is only a stand-in): the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept in g_scratch_base.
+constexpr size_t kStaticScratchBytes = (size_t)2 << 20;   // 2 MiB
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_base[kMaxDevices] = {};
+
+int static_scratch_base(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(GQA_E_INVALID, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_base[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(GQA_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_base[dev] = p;
+  }
+  *out = g_scratch_base[dev];
+  return GQA_OK;
+}
+
+// Lay one row's decode scratch out from `base` (256-byte aligned pieces) and return the bytes
+// it spans; with base == nullptr only the size is computed. Whole-K matvec path only (no split
+// partials, no second residual buffer); the attention partials of row 0 and its eight arrival
+// counters, which the call's embedding launch clears.
+size_t carve_static_scratch(const gqa_model* m, void* base, DecodeScratch* sc) {
+  const gqa_model_desc& d = m->d;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = base ? (void*)((char*)base + off) : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  *sc = DecodeScratch{};
+  sc->x = (float*)take(4 * (size_t)d.hidden);
+  sc->part = (float*)take(4 * (size_t)m->QKV);
+  sc->ss = (float*)take(4 * 2 * 8 * 32);
+  sc->apart = (float*)take(4 * (size_t)(attn_decode_part_floats(d.n_q_heads) / kMaxBatch));
+  sc->counters = (int32_t*)take(4 * kKvHeads);
+  sc->oh = (f16*)take(2 * (size_t)m->QD);
+  sc->ol = (f16*)take(2 * (size_t)m->QD);
+  sc->mh = (f16*)take(2 * (size_t)d.ffn);
+  sc->ml = (f16*)take(2 * (size_t)d.ffn);
+  sc->xh = (f16*)take(2 * (size_t)d.hidden);
+  sc->xl = (f16*)take(2 * (size_t)d.hidden);
+  sc->cand = (float2*)take(sizeof(float2) * (size_t)(d.vocab / 16));
+  sc->pstride = m->QKV;
+  sc->zero = sc->counters;
+  sc->nzero = kKvHeads;
+  return off;
+}
+
+int eval_rows(gqa_session* const* ss, int32_t B, const int32_t* ids, int32_t ids_on_device, float* logits,
+              int32_t* argmax, const DecodeScratch* scr, hipStream_t st);
 
 }  // namespace
 
@@ -765,6 +860,7 @@ struct ProfScope {
     if (e_ != hipSuccess) return fail(GQA_E_HIP, "launch failed at %s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
 
+
 // Decode / batched decode over B rows; ids already on the device. Per layer: q|k|v matvec (its
 // prologue adds the previous down projection to the residual stream and multiplies by the
 // norm weight), fused attention (1/rms scale, q/k norm, RoPE, KV write, attention, chunk
@@ -773,8 +869,8 @@ struct ProfScope {
 // between two buffers so a prologue can write the updated stream while other workgroups still
 // read the previous one. With B > 4 the prologue work runs in rows_kernel with the same
 // arithmetic.
-int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t* ids_dev, float* logits,
-               int32_t* argmax, hipStream_t st) {
+int run_decode(gqa_model* m, const DecodeScratch& sc, const Rows& rows, int B, int max_ctx, const int32_t* ids_dev,
+               float* logits, int32_t* argmax, hipStream_t st) {
   const gqa_model_desc& d = m->d;
   const int H = d.hidden, F = d.ffn, V = d.vocab, NQ = d.n_q_heads, QD = m->QD, QKV = m->QKV;
   const float eps = d.rms_eps;
@@ -782,14 +878,14 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
   auto kv_k = [m](const LayerW& w) { return w.kq8.kq ? m->kwin : w.kpool; };
   auto kv_v = [m](const LayerW& w) { return w.kq8.kq ? m->vwin : w.vpool; };
   const bool fused = B <= 4;
-  const int64_t pstride = m->part_floats / 8;
-  float* xa = m->x;
-  float* xb = m->x2;
-  float* P0 = m->part;
-  float* P1 = m->part2;
-  float* ss_qkv = m->ss;
-  float* ss_gu = m->ss + 8 * 32;
-  LAUNCH(launch_embed(m->embed, ids_dev, B, H, V, xa, m->err, st));
+  const int64_t pstride = sc.pstride;
+  float* xa = sc.x;
+  float* xb = sc.x2;
+  float* P0 = sc.part;
+  float* P1 = sc.part2;
+  float* ss_qkv = sc.ss;
+  float* ss_gu = sc.ss + 8 * 32;
+  LAUNCH(launch_embed(m->embed, ids_dev, B, H, V, xa, m->err, st, sc.zero, sc.nzero));
 
   auto resid_src = [&](float* res, float* res_out, const float* part, int nsplit, float pscale, const uint16_t* w,
                        float* ss_out) {
@@ -842,34 +938,34 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
       LAUNCH(launch_gemv_full(XF_NORM, EPI_STORE, m->s_qkv, q, st));
       if (w.kq8.kq) LAUNCH(launch_kv_q8_window(rows, B, max_ctx - 1, w.kq8, m->kwin, m->vwin, st));
       LAUNCH(launch_attn_decode(P0, 1, pstride, QKV, NQ, ss_qkv, m->s_qkv, H, w.q_norm, w.k_norm, eps, m->rcos,
-                                m->rsin, rows, B, max_ctx, kv_k(w), kv_v(w), w.kq8, m->apart, m->counters, kAttnOutScale,
-                                m->oh, m->ol, QD, st));
+                                m->rsin, rows, B, max_ctx, kv_k(w), kv_v(w), w.kq8, sc.apart, sc.counters, kAttnOutScale,
+                                sc.oh, sc.ol, QD, st));
       FullArgs o = fa();
       o.W = w.wo; o.Wq = w.qo; o.Wd = w.so; o.Wb = w.bo; o.K = QD; o.N = H;
-      o.xhi = m->oh; o.xlo = m->ol; o.ldx = QD; o.y = xa; o.ldy = H; o.yscale = 1.f / kAttnOutScale;
+      o.xhi = sc.oh; o.xlo = sc.ol; o.ldx = QD; o.y = xa; o.ldy = H; o.yscale = 1.f / kAttnOutScale;
       LAUNCH(launch_gemv_full(XF_RAW, EPI_ADD, m->s_o, o, st));
       FullArgs g = fa();
       g.W = w.wgu; g.Wq = w.qgu; g.Wd = w.sgu; g.Wb = w.bgu; g.K = H; g.N = 2 * F;
-      g.xres = xa; g.nw = w.ffn_norm; g.ss_out = ss_gu; g.mhi = m->mh; g.mlo = m->ml; g.ldm = F;
+      g.xres = xa; g.nw = w.ffn_norm; g.ss_out = ss_gu; g.mhi = sc.mh; g.mlo = sc.ml; g.ldm = F;
       {
         ProfScope ps(m, GQA_PROF_DECODE_GATEUP, st);
         LAUNCH(launch_gemv_full(XF_NORM, EPI_SWIGLU, m->s_gu, g, st));
       }
       FullArgs dn = fa();
       dn.W = w.wd; dn.Wq = w.qd; dn.Wd = w.sd; dn.Wb = w.bd; dn.K = F; dn.N = H;
-      dn.xhi = m->mh; dn.xlo = m->ml; dn.ldx = F; dn.y = xa; dn.ldy = H; dn.yscale = 1.f;
+      dn.xhi = sc.mh; dn.xlo = sc.ml; dn.ldx = F; dn.y = xa; dn.ldy = H; dn.yscale = 1.f;
       LAUNCH(launch_gemv_full(XF_RAW, EPI_ADD, m->s_d, dn, st));
     }
-    LAUNCH(launch_final_norm(resid_src(xa, nullptr, nullptr, 0, 1.f, m->final_norm, nullptr), B, m->xh, m->xl, H,
+    LAUNCH(launch_final_norm(resid_src(xa, nullptr, nullptr, 0, 1.f, m->final_norm, nullptr), B, sc.xh, sc.xl, H,
                              st));
     FullArgs lm = fa();
-    lm.W = m->lm_head; lm.K = H; lm.N = V; lm.xhi = m->xh; lm.xlo = m->xl; lm.ldx = H; lm.y = logits; lm.ldy = V;
-    lm.cand = argmax ? m->cand : nullptr;
+    lm.W = m->lm_head; lm.K = H; lm.N = V; lm.xhi = sc.xh; lm.xlo = sc.xl; lm.ldx = H; lm.y = logits; lm.ldy = V;
+    lm.cand = argmax ? sc.cand : nullptr;
     {
       ProfScope ps(m, GQA_PROF_DECODE_LMHEAD, st);
       LAUNCH(launch_gemv_full(XF_RAW, EPI_STORE, 1, lm, st));
     }
-    if (argmax) LAUNCH(launch_argmax(m->cand, V / 16, B, argmax, st));
+    if (argmax) LAUNCH(launch_argmax(sc.cand, V / 16, B, argmax, st));
     return GQA_OK;
   }
 
@@ -878,19 +974,19 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
   for (int l = 0; l < d.n_layers; ++l) {
     const LayerW& w = m->L[l];
     LAUNCH(gemv_built(w.wqkv, w.qqkv, w.sqkv, w.bqkv, H, QKV, resid_src(xa, xb, prev, prev_split, 1.f, w.attn_norm, ss_qkv),
-                      m->s_qkv, P0, QKV, m->xh, m->xl));
+                      m->s_qkv, P0, QKV, sc.xh, sc.xl));
     std::swap(xa, xb);
     if (w.kq8.kq) LAUNCH(launch_kv_q8_window(rows, B, max_ctx - 1, w.kq8, m->kwin, m->vwin, st));
     LAUNCH(launch_attn_decode(P0, m->s_qkv, pstride, QKV, NQ, ss_qkv, m->s_qkv, H, w.q_norm, w.k_norm, eps, m->rcos,
-                              m->rsin, rows, B, max_ctx, kv_k(w), kv_v(w), w.kq8, m->apart, m->counters, kAttnOutScale,
-                              m->oh, m->ol, QD, st));
-    LAUNCH(launch_gemv(w.wo, w.qo, w.so, w.bo, QD, H, raw_src(m->oh, m->ol, QD), B, m->s_o, P1, pstride, H, nullptr,
+                              m->rsin, rows, B, max_ctx, kv_k(w), kv_v(w), w.kq8, sc.apart, sc.counters, kAttnOutScale,
+                              sc.oh, sc.ol, QD, st));
+    LAUNCH(launch_gemv(w.wo, w.qo, w.so, w.bo, QD, H, raw_src(sc.oh, sc.ol, QD), B, m->s_o, P1, pstride, H, nullptr,
                        st));
     {
       ProfScope ps(m, GQA_PROF_DECODE_GATEUP, st);
       LAUNCH(gemv_built(w.wgu, w.qgu, w.sgu, w.bgu, H, 2 * F,
                         resid_src(xa, xb, P1, m->s_o, 1.f / kAttnOutScale, w.ffn_norm, ss_gu), m->s_gu, P0, 2 * F,
-                        m->xh, m->xl));
+                        sc.xh, sc.xl));
     }
     std::swap(xa, xb);
     XSrc sw{};
@@ -903,18 +999,18 @@ int run_decode(gqa_model* m, const Rows& rows, int B, int max_ctx, const int32_t
     sw.ss_n = m->s_gu;
     sw.H = H;
     sw.eps = eps;
-    LAUNCH(gemv_built(w.wd, w.qd, w.sd, w.bd, F, H, sw, m->s_d, P1, H, m->mh, m->ml));
+    LAUNCH(gemv_built(w.wd, w.qd, w.sd, w.bd, F, H, sw, m->s_d, P1, H, sc.mh, sc.ml));
     prev = P1;
     prev_split = m->s_d;
   }
-  LAUNCH(launch_final_norm(resid_src(xa, nullptr, prev, prev_split, 1.f, m->final_norm, nullptr), B, m->xh, m->xl, H,
+  LAUNCH(launch_final_norm(resid_src(xa, nullptr, prev, prev_split, 1.f, m->final_norm, nullptr), B, sc.xh, sc.xl, H,
                            st));
   {
     ProfScope ps(m, GQA_PROF_DECODE_LMHEAD, st);
-    LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, nullptr, H, V, raw_src(m->xh, m->xl, H), B, 1, logits, pstride, V,
-                       argmax ? m->cand : nullptr, st));
+    LAUNCH(launch_gemv(m->lm_head, nullptr, nullptr, nullptr, H, V, raw_src(sc.xh, sc.xl, H), B, 1, logits, pstride, V,
+                       argmax ? sc.cand : nullptr, st));
   }
-  if (argmax) LAUNCH(launch_argmax(m->cand, V / 16, B, argmax, st));
+  if (argmax) LAUNCH(launch_argmax(sc.cand, V / 16, B, argmax, st));
   return GQA_OK;
 }
 
@@ -1186,6 +1282,43 @@ int gqa_session_truncate(gqa_session* s, int32_t pos) {
 int gqa_session_eval_batch(gqa_session* const* ss, int32_t B, const int32_t* ids, int32_t ids_on_device,
                            float* logits, int32_t* argmax, hipStream_t st) {
   g_err.clear();
+  return eval_rows(ss, B, ids, ids_on_device, logits, argmax, nullptr, st);
+}
+
+int gqa_session_eval_decode_static(gqa_session* s, const int32_t* id, int32_t id_on_device, float* logits,
+                                   int32_t* argmax, hipStream_t st) {
+  g_err.clear();
+  if (!s || !id || !logits) return fail(GQA_E_INVALID, "null argument");
+  gqa_model* m = s->m;
+  const gqa_model_desc& d = m->d;
+  if (d.kv_quant != GQA_KV_BF16)
+    return fail(GQA_E_INVALID, "the static-scratch decode does not support a Q8_0 KV cache (its read window is model memory)");
+  if (!gemv_full_fits(std::max(std::max(d.hidden, m->QD), d.ffn), 1))
+    return fail(GQA_E_INVALID, "the static-scratch decode needs the whole-K matvec path (hidden, attention width and "
+                               "ffn <= %d)", 16380);
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev != m->dev) return fail(GQA_E_INVALID, "current device %d is not the model's device %d", dev, m->dev);
+  DecodeScratch sc;
+  const size_t need = carve_static_scratch(m, nullptr, &sc);
+  if (need > kStaticScratchBytes)
+    return fail(GQA_E_INVALID, "this model's decode needs %zu bytes of scratch; the static scratch holds %zu", need,
+                kStaticScratchBytes);
+  void* base = nullptr;
+  int rc = static_scratch_base(dev, &base);
+  if (rc) return rc;
+  carve_static_scratch(m, base, &sc);
+  return eval_rows(&s, 1, id, id_on_device, logits, argmax, &sc, st);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Rows of one batched (or single) decode: checks, id upload, KV block mapping, then run_decode
+// over the model's scratch or the given one.
+int eval_rows(gqa_session* const* ss, int32_t B, const int32_t* ids, int32_t ids_on_device, float* logits,
+              int32_t* argmax, const DecodeScratch* scr, hipStream_t st) {
   if (!ss || !ids || !logits) return fail(GQA_E_INVALID, "null argument");
   if (B < 1 || B > kMaxBatch) return fail(GQA_E_INVALID, "B = %d outside [1, %d]", B, kMaxBatch);
   gqa_model* m = ss[0] ? ss[0]->m : nullptr;
@@ -1215,11 +1348,15 @@ int gqa_session_eval_batch(gqa_session* const* ss, int32_t B, const int32_t* ids
     int rc = prepare_write(ss[b], ss[b]->pos, ss[b]->pos + 1, ids_on_device ? nullptr : ids + b, st);
     if (rc) return rc;
   }
-  int rc = run_decode(m, rows, B, max_ctx, ids_dev, logits, argmax, st);
+  int rc = run_decode(m, scr ? *scr : model_scratch(m), rows, B, max_ctx, ids_dev, logits, argmax, st);
   if (rc) return rc;
   for (int b = 0; b < B; ++b) ss[b]->pos++;
   return GQA_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int gqa_session_eval_decode(gqa_session* s, const int32_t* id, int32_t id_on_device, float* logits, int32_t* argmax,
                             hipStream_t st) {

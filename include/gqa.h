@@ -245,6 +245,24 @@ int gqa_session_eval_decode(gqa_session* session, const int32_t* id, int32_t id_
 int gqa_session_eval_batch(gqa_session* const* sessions, int32_t B, const int32_t* ids, int32_t ids_on_device,
                            float* logits, int32_t* argmax, hipStream_t stream);
 
+/* Allocation-free single-row decode, for callers that cannot allocate device memory during a
+ * call: code recorded under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments, arithmetic, kernels and results (bit for bit) as
+ * gqa_session_eval_decode, but the call's scratch -- residual stream, projection outputs,
+ * operand rows, attention chunk partials and arrival counters, sums of squares, argmax
+ * candidates -- lives in a static device array of the library (2 MiB per device, held by each
+ * device the library runs on until the process ends) instead of the model's buffers. The call
+ * allocates and frees nothing. Limits: the model's decode must fit the whole-K matvec path
+ * (hidden, attention width and ffn <= 16380) and its row scratch must fit 2 MiB (the Qwen3-8B
+ * shape needs about 1.3 MiB; the size grows with vocab / 2 bytes and n_q_heads x 33 KiB), and
+ * the KV cache must be BF16; otherwise GQA_E_INVALID with the needed size, before any work is
+ * enqueued. The current device must be the model's (GQA_E_INVALID otherwise). Every call on a
+ * device shares that device's array, which keeps the last call's contents (the arrival
+ * counters that must start at zero are cleared by the call itself): calls that overlap on one
+ * device -- on different streams, or from different models -- race and must not be made. */
+int gqa_session_eval_decode_static(gqa_session* session, const int32_t* id, int32_t id_on_device, float* logits,
+                                   int32_t* argmax, hipStream_t stream);
+
 /* Synchronise `stream`, then return GQA_E_RANGE (and clear the flag) if a device-resident
  * token id was out of range since the last check, else GQA_OK. */
 int gqa_model_check_device_error(gqa_model* model, hipStream_t stream);
