@@ -391,8 +391,15 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
 constexpr int kDecodeWaves = 4;
 constexpr int kBatchChunksPerWorkgroup = 4;
 
+#ifndef GQA_DECODE_TARGET_CHUNKS
+#define GQA_DECODE_TARGET_CHUNKS 32
+#endif
+// Chunk length of a row's context: the smallest multiple of 64 positions that cuts it into at
+// most GQA_DECODE_TARGET_CHUNKS chunks (<= kDecodeMaxChunks). A function of the row's own
+// context only, so a row's partials and merge do not depend on the batch.
 __host__ __device__ __forceinline__ int decode_chunk_len(int ctx) {
-  return 64 * ((ctx + 64 * kDecodeMaxChunks - 1) / (64 * kDecodeMaxChunks));
+  static_assert(GQA_DECODE_TARGET_CHUNKS >= 1 && GQA_DECODE_TARGET_CHUNKS <= kDecodeMaxChunks, "chunk count");
+  return 64 * ((ctx + 64 * GQA_DECODE_TARGET_CHUNKS - 1) / (64 * GQA_DECODE_TARGET_CHUNKS));
 }
 
 // Device-scope (sc1) accesses: coherent across the XCDs' L2 caches without an L2 writeback or
@@ -410,14 +417,14 @@ __device__ __forceinline__ float2 load_dev2(const float* p) {
 // w_c l_c with w_c = 2^(m_c - max m). One wave; lane t owns dims 2t, 2t + 1. The result is
 // written as the FP16 hi/lo operand of the o projection, times out_scale. DEV: the partials
 // were written by other workgroups of the same launch (device-scope loads).
-template <bool DEV>
-__device__ __forceinline__ void merge_head(const float* pp, int nchunk, int lane, float out_scale, f16* ohi,
-                                           f16* olo) {
+template <bool DEV, int NC>
+__device__ __forceinline__ void merge_head_n(const float* pp, int nchunk, int lane, float out_scale, f16* ohi,
+                                             f16* olo) {
   auto ld2 = [](const float* p) { return DEV ? load_dev2(p) : *(const float2*)p; };
   const float2 ml = ld2(pp + (int64_t)min(lane, nchunk - 1) * kPartStride);
-  float2 ov[kDecodeMaxChunks];
+  float2 ov[NC];
 #pragma unroll
-  for (int cc = 0; cc < kDecodeMaxChunks; ++cc)
+  for (int cc = 0; cc < NC; ++cc)
     ov[cc] = ld2(pp + (int64_t)min(cc, nchunk - 1) * kPartStride + 4 + 2 * lane);
   const float mv = lane < nchunk ? ml.x : -INFINITY;
   const float M = wave_max(mv);
@@ -428,7 +435,7 @@ __device__ __forceinline__ void merge_head(const float* pp, int nchunk, int lane
   // leaves them unchanged. No branch per chunk, so the compiler cannot sink each load next to
   // its use (which serialised the loads).
 #pragma unroll
-  for (int cc = 0; cc < kDecodeMaxChunks; ++cc) {       // chunk cc's weight and sum, read as scalars
+  for (int cc = 0; cc < NC; ++cc) {                      // chunk cc's weight and sum, read as scalars
     const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), cc));
     L = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.y), cc)), w, L);
     o0 = fmaf(ov[cc].x, w, o0);
@@ -442,6 +449,18 @@ __device__ __forceinline__ void merge_head(const float* pp, int nchunk, int lane
   *(f16x2*)(olo + 2 * lane) = f16x2{l0, l1};
 }
 
+// merge_head_n over the slots a context can use: NC = 32 when it has at most 32 chunks (half the
+// partial loads), else all 64. The slots past nchunk enter with weight 0 and add exact zeros, so
+// both give the same bits.
+template <bool DEV>
+__device__ __forceinline__ void merge_head(const float* pp, int nchunk, int lane, float out_scale, f16* ohi,
+                                           f16* olo) {
+  if (nchunk <= 32)
+    merge_head_n<DEV, 32>(pp, nchunk, lane, out_scale, ohi, olo);
+  else
+    merge_head_n<DEV, kDecodeMaxChunks>(pp, nchunk, lane, out_scale, ohi, olo);
+}
+
 template <int G, bool FUSED>
 __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_kernel(
     const float* __restrict__ qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* __restrict__ ss,
@@ -453,7 +472,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
   constexpr int NE = (G + 2) * kHeadDim;                  // q heads, then k and v of the new position
   __shared__ float sraw[NE];                              // projection sums (times 1/rms)
   __shared__ float sq[NE];                                // normed + rotated q (scaled), k; v
-  __shared__ float wm[NW][G], wl[NW][G], ww[NW][G], sML[G][2];
+  __shared__ float wm[NW][G], wl[NW][G];
   __shared__ float wo[NW][G][kHeadDim];
   __shared__ __attribute__((aligned(16))) uint16_t vlds[NW][2][16 * kHeadDim];   // V planes, two steps
   __shared__ int s_last;
@@ -717,40 +736,33 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
         for (int r = 0; r < G; ++r) wo[wave][r][16 * n + lane] = O[n][r];
     }
     __syncthreads();
-    // per head: the max over the wave states, the state weights 2^(m_w - max) and the weighted sum,
-    // computed once (thread hh), in wave order
-    if (tid < G) {
-      const int hh = tid;
+    // per (head, dim): the max over the wave states, the state weights 2^(m_w - max), the
+    // weighted sums, in wave order; each thread forms its head's max and weights itself, so one
+    // barrier publishes the wave states and no second pass is needed
+    for (int idx = tid; idx < G * kHeadDim; idx += 64 * kDecodeWaves) {
+      const int hh = idx / kHeadDim, d = idx % kHeadDim;
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][hh]);
-      float L = 0.f;
+      float wt[NW], L = 0.f, Ov = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float wt = wm[w][hh] == -INFINITY ? 0.f : exp2f(wm[w][hh] - M);
-        ww[w][hh] = wt;
-        L = fmaf(wl[w][hh], wt, L);
+        wt[w] = wm[w][hh] == -INFINITY ? 0.f : exp2f(wm[w][hh] - M);
+        L = fmaf(wl[w][hh], wt[w], L);
       }
-      sML[hh][0] = M;
-      sML[hh][1] = L;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < G * kHeadDim; idx += 64 * kDecodeWaves) {
-      const int hh = idx / kHeadDim, d = idx % kHeadDim;
-      float Ov = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) Ov = fmaf(wo[w][hh][d], ww[w][hh], Ov);
+      for (int w = 0; w < NW; ++w) Ov = fmaf(wo[w][hh][d], wt[w], Ov);
       float* pp = part + (((int64_t)b * nq + kvh * G + hh) * kDecodeMaxChunks + cc) * kPartStride;
       if (FUSED) {                          // read by another workgroup of this launch
         if (d == 0) {
-          store_dev(pp, sML[hh][0]);
-          store_dev(pp + 1, sML[hh][1]);
+          store_dev(pp, M);
+          store_dev(pp + 1, L);
         }
         store_dev(pp + 4 + d, Ov);
       } else {                              // read by attn_merge_kernel after this launch
         if (d == 0) {
-          pp[0] = sML[hh][0];
-          pp[1] = sML[hh][1];
+          pp[0] = M;
+          pp[1] = L;
         }
         pp[4 + d] = Ov;
       }
@@ -759,7 +771,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
     for (int n = 0; n < 8; ++n) O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run = -INFINITY;
     l_run = 0.f;
-    __syncthreads();                      // the merge arrays are reused by the next chunk
+    if (cc + 1 < c1) __syncthreads();     // the wave-state arrays are reused by the next chunk
   };
 
   // The workgroup's steps (chunk, 64-position step) in order, double-buffered (K in registers, V
