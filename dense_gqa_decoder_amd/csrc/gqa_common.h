@@ -195,6 +195,26 @@ __device__ __forceinline__ int q8kv_code(float x, float d) {
 __device__ __forceinline__ uint16_t q8kv_read_bf16(f16 scale, int code) {
   return f32_to_bf16_rne((float)scale * (float)code);
 }
+// Eight Q8_0 KV codes of one 32-value block (two dwords, code j in byte j) -> the eight BF16
+// values attention reads, bf16(fp32(scale) * code) each (q8kv_read_bf16), packed in pairs. The
+// product is exact in FP32 (11 + 7 significant bits); v_cvt_pk_bf16_f32 rounds each to nearest
+// even, as f32_to_bf16_rne does, two per instruction.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 q8kv_bf16x8(uint2 codes, f16 scale) {
+  const float s = (float)scale;
+  const uint32_t x[2] = {codes.x, codes.y};
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t word = x[i >> 1];
+    const int sh = 16 * (i & 1);
+    const float c0 = (float)(int8_t)((word >> sh) & 0xFFu), c1 = (float)(int8_t)((word >> (sh + 8)) & 0xFFu);
+    const f32x2v p = {s * c0, s * c1};
+    w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2v));
+  }
+  return uint4{w[0], w[1], w[2], w[3]};
+}
 
 // FP32 -> FP16 conversions of MFMA operands go through explicit instructions, never through a
 // plain cast: the compiler is free to lower a cast to different instructions in different

@@ -461,8 +461,19 @@ __device__ __forceinline__ void merge_head(const float* pp, int nchunk, int lane
     merge_head_n<DEV, kDecodeMaxChunks>(pp, nchunk, lane, out_scale, ohi, olo);
 }
 
-template <int G, bool FUSED>
-__global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_kernel(
+// K/V of one wave's 16 keys of a 64-position step, in flight: BF16 K rows in registers (the V
+// planes travel by direct-to-LDS copies), or with a Q8_0 cache the K and V codes and their block
+// scales in registers, widened to the same BF16 values when the step is computed.
+struct DecStage {
+  uint4 kr[4];      // K rows: the MFMA A operand (BF16), one uint4 per 32-dim step
+  uint2 kc[4];      // Q8_0: K codes of the same elements
+  uint2 ksc;        // Q8_0: the key's four block scales
+  uint4 vc[2];      // Q8_0: V codes of one key, 32 dims
+  uint16_t vsc;     // Q8_0: their block scale
+};
+
+template <int G, bool FUSED, bool KQ8>
+__global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : (KQ8 ? 2 : 3)) void attn_decode_kernel(
     const float* __restrict__ qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* __restrict__ ss,
     int ss_n, int H, const uint16_t* __restrict__ wqn, const uint16_t* __restrict__ wkn, float eps,
     const float* __restrict__ rcos, const float* __restrict__ rsin, Rows rows, int cpw, uint16_t* __restrict__ kpool,
@@ -499,18 +510,31 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
   //   V: four 1 KiB direct-to-LDS copies into 16-dim planes (16 keys x 32 bytes each); copy j
   //      fills planes 2 j, 2 j + 1, lane l bringing key (l % 32) / 2, half l % 2 of the plane.
   auto phys_of = [&](int cc, int it) { return table[min(cc * CH + it * 64 + wave * 16, p_end_of(cc) - 1) >> 5]; };
-  auto issue = [&](int phys, uint4 (&kr)[4], int buf) {
+  //   Q8_0 cache: K as above but the codes (8 bytes per lane and 32-dim step) and the key's four
+  //   block scales; V: lane l brings the 32 codes of key l / 4, dims 32 (l % 4) .. + 31, and their
+  //   scale, widened into the same LDS planes when the step is computed.
+  auto issue = [&](int phys, DecStage& sg, int buf) {
     const int64_t rows = (int64_t)phys * kBlockElems + ((int64_t)kvh * kBlock + ((wave * 16) & 31)) * kHeadDim;
+    if constexpr (KQ8) {
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) kr[s4] = *(const uint4*)(kpool + rows + hq * kHeadDim + 32 * s4 + 8 * g4);
-    const int vrow = (lane & 31) >> 1, vhalf = lane & 1;
+      for (int s4 = 0; s4 < 4; ++s4) sg.kc[s4] = *(const uint2*)(kq8.kq + rows + hq * kHeadDim + 32 * s4 + 8 * g4);
+      sg.ksc = *(const uint2*)(kq8.ks + ((rows + hq * kHeadDim) >> 5));
+      const int64_t vo = rows + (lane >> 2) * kHeadDim + 32 * (lane & 3);
+      sg.vc[0] = *(const uint4*)(kq8.vq + vo);
+      sg.vc[1] = *(const uint4*)(kq8.vq + vo + 16);
+      sg.vsc = __builtin_bit_cast(uint16_t, kq8.vs[vo >> 5]);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int plane = 2 * j + (lane >> 5);
-      lds_dma16(vpool + rows + vrow * kHeadDim + 16 * plane + 8 * vhalf, &vlds[wave][buf][j * 512]);
+      for (int s4 = 0; s4 < 4; ++s4) sg.kr[s4] = *(const uint4*)(kpool + rows + hq * kHeadDim + 32 * s4 + 8 * g4);
+      const int vrow = (lane & 31) >> 1, vhalf = lane & 1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int plane = 2 * j + (lane >> 5);
+        lds_dma16(vpool + rows + vrow * kHeadDim + 16 * plane + 8 * vhalf, &vlds[wave][buf][j * 512]);
+      }
     }
   };
-  uint4 kA[4], kB[4];
+  DecStage kA, kB;
   // Issue order matters (vector loads complete in order): the block-table entry, the RoPE and
   // norm constants, the projection partials, then the first K/V, so q is built while the K/V
   // are in flight.
@@ -645,9 +669,26 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
   };
-  auto compute = [&](int cc, int it, uint4 (&kr)[4], int buf) {
+  auto compute = [&](int cc, int it, DecStage& sg, int buf) {
     const int p0 = cc * CH + it * 64 + wave * 16, p_end = p_end_of(cc);
     uint16_t* vl = vlds[wave][buf];
+    uint4 (&kr)[4] = sg.kr;
+    if constexpr (KQ8) {                                  // widen the step's codes (before the new row's overrides)
+      const f16 ksc[4] = {__builtin_bit_cast(f16, (uint16_t)(sg.ksc.x & 0xFFFFu)),
+                          __builtin_bit_cast(f16, (uint16_t)(sg.ksc.x >> 16)),
+                          __builtin_bit_cast(f16, (uint16_t)(sg.ksc.y & 0xFFFFu)),
+                          __builtin_bit_cast(f16, (uint16_t)(sg.ksc.y >> 16))};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) kr[s4] = q8kv_bf16x8(sg.kc[s4], ksc[s4]);
+      const f16 vsc = __builtin_bit_cast(f16, sg.vsc);
+      const int kk = lane >> 2, qd = lane & 3;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {                       // dims 32 qd + 16 h .. + 15: plane 2 qd + h
+        uint16_t* dst = vl + (2 * qd + h) * 256 + kk * 16;
+        *(uint4*)dst = q8kv_bf16x8(uint2{sg.vc[h].x, sg.vc[h].y}, vsc);
+        *(uint4*)(dst + 8) = q8kv_bf16x8(uint2{sg.vc[h].z, sg.vc[h].w}, vsc);
+      }
+    }
     if (owner && p0 + hq == pos) {                        // the new position: K from LDS, not the pool
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
@@ -786,8 +827,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : 3) void attn_decode_
     }
   };
   advance(lc, lit);                                      // step (c0, 0) was issued into kA, buffer 0
-  auto run = [&](uint4 (&kr)[4], int buf) {
-    compute(cc, cit, kr, buf);
+  auto run = [&](DecStage& sg, int buf) {
+    compute(cc, cit, sg, buf);
     if (cit + 1 == niter_of(cc)) finish(cc);
     advance(cc, cit);
   };
@@ -914,7 +955,15 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
   const int cpw = fused ? 1 : kBatchChunksPerWorkgroup;
   dim3 grid((chunks + cpw - 1) / cpw, kKvHeads, B);
 #define DEC_LAUNCH(GG, FU)                                                                                         \
-  hipLaunchKernelGGL((attn_decode_kernel<GG, FU>), grid, dim3(64 * kDecodeWaves), 0, st, qkvp, nsplit, pstride, QKV, \
+  do {                                                                                                             \
+    if (kq8.kq) {                                                                                                  \
+      DEC_LAUNCH_Q(GG, FU, true);                                                                                  \
+    } else {                                                                                                       \
+      DEC_LAUNCH_Q(GG, FU, false);                                                                                 \
+    }                                                                                                              \
+  } while (0)
+#define DEC_LAUNCH_Q(GG, FU, Q)                                                                                    \
+  hipLaunchKernelGGL((attn_decode_kernel<GG, FU, Q>), grid, dim3(64 * kDecodeWaves), 0, st, qkvp, nsplit, pstride, QKV, \
                      nq, ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, cpw, kpool, vpool, kq8, part, counters, out_scale, \
                      ohi, olo, ldo)
   if (G != 4 && G != 2) return hipErrorInvalidValue;
@@ -933,6 +982,7 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
     }
   }
 #undef DEC_LAUNCH
+#undef DEC_LAUNCH_Q
   return hipGetLastError();
 }
 

@@ -874,9 +874,9 @@ int run_decode(gqa_model* m, const DecodeScratch& sc, const Rows& rows, int B, i
   const gqa_model_desc& d = m->d;
   const int H = d.hidden, F = d.ffn, V = d.vocab, NQ = d.n_q_heads, QD = m->QD, QKV = m->QKV;
   const float eps = d.rms_eps;
-  // the K/V attention reads: the BF16 cache, or the read window of a Q8_0 cache
-  auto kv_k = [m](const LayerW& w) { return w.kq8.kq ? m->kwin : w.kpool; };
-  auto kv_v = [m](const LayerW& w) { return w.kq8.kq ? m->vwin : w.vpool; };
+  // the decode attention reads the BF16 cache, or a Q8_0 cache's codes and scales directly (w.kq8)
+  auto kv_k = [](const LayerW& w) { return w.kpool; };
+  auto kv_v = [](const LayerW& w) { return w.vpool; };
   const bool fused = B <= 4;
   const int64_t pstride = sc.pstride;
   float* xa = sc.x;
@@ -936,7 +936,6 @@ int run_decode(gqa_model* m, const DecodeScratch& sc, const Rows& rows, int B, i
       q.W = w.wqkv; q.Wq = w.qqkv; q.Wd = w.sqkv; q.Wb = w.bqkv; q.K = H; q.N = QKV;
       q.xres = xa; q.nw = w.attn_norm; q.ss_out = ss_qkv; q.y = P0; q.ldy = QKV;
       LAUNCH(launch_gemv_full(XF_NORM, EPI_STORE, m->s_qkv, q, st));
-      if (w.kq8.kq) LAUNCH(launch_kv_q8_window(rows, B, max_ctx - 1, w.kq8, m->kwin, m->vwin, st));
       LAUNCH(launch_attn_decode(P0, 1, pstride, QKV, NQ, ss_qkv, m->s_qkv, H, w.q_norm, w.k_norm, eps, m->rcos,
                                 m->rsin, rows, B, max_ctx, kv_k(w), kv_v(w), w.kq8, sc.apart, sc.counters, kAttnOutScale,
                                 sc.oh, sc.ol, QD, st));
@@ -976,7 +975,6 @@ int run_decode(gqa_model* m, const DecodeScratch& sc, const Rows& rows, int B, i
     LAUNCH(gemv_built(w.wqkv, w.qqkv, w.sqkv, w.bqkv, H, QKV, resid_src(xa, xb, prev, prev_split, 1.f, w.attn_norm, ss_qkv),
                       m->s_qkv, P0, QKV, sc.xh, sc.xl));
     std::swap(xa, xb);
-    if (w.kq8.kq) LAUNCH(launch_kv_q8_window(rows, B, max_ctx - 1, w.kq8, m->kwin, m->vwin, st));
     LAUNCH(launch_attn_decode(P0, m->s_qkv, pstride, QKV, NQ, ss_qkv, m->s_qkv, H, w.q_norm, w.k_norm, eps, m->rcos,
                               m->rsin, rows, B, max_ctx, kv_k(w), kv_v(w), w.kq8, sc.apart, sc.counters, kAttnOutScale,
                               sc.oh, sc.ol, QD, st));
@@ -1291,8 +1289,6 @@ int gqa_session_eval_decode_static(gqa_session* s, const int32_t* id, int32_t id
   if (!s || !id || !logits) return fail(GQA_E_INVALID, "null argument");
   gqa_model* m = s->m;
   const gqa_model_desc& d = m->d;
-  if (d.kv_quant != GQA_KV_BF16)
-    return fail(GQA_E_INVALID, "the static-scratch decode does not support a Q8_0 KV cache (its read window is model memory)");
   if (!gemv_full_fits(std::max(std::max(d.hidden, m->QD), d.ffn), 1))
     return fail(GQA_E_INVALID, "the static-scratch decode needs the whole-K matvec path (hidden, attention width and "
                                "ffn <= %d)", 16380);

@@ -89,8 +89,10 @@ typedef struct {
                                as four Q8_0 blocks of 32 (int8 codes, fp16 scale = fp16(max|x|/127),
                                codes round(x / (max|x|/127)) half away from zero, the Q8_0 weight
                                rule): 136 bytes instead of 256. Attention reads
-                               bf16(scale * code); the model also holds one layer's BF16 read
-                               window, rebuilt from the codes before each layer's attention */
+                               bf16(scale * code): decode attention widens the codes as it
+                               loads them; the model also holds one layer's BF16 read window,
+                               rebuilt from the codes of the earlier positions before a layer's
+                               attention in a prefill round that starts past position 0 */
 } gqa_model_desc;
 
 #define GQA_PREFILL_SPLIT 0
@@ -254,9 +256,9 @@ int gqa_session_eval_batch(gqa_session* const* sessions, int32_t B, const int32_
  * device the library runs on until the process ends) instead of the model's buffers. The call
  * allocates and frees nothing. Limits: the model's decode must fit the whole-K matvec path
  * (hidden, attention width and ffn <= 16380) and its row scratch must fit 2 MiB (the Qwen3-8B
- * shape needs about 1.3 MiB; the size grows with vocab / 2 bytes and n_q_heads x 33 KiB), and
- * the KV cache must be BF16; otherwise GQA_E_INVALID with the needed size, before any work is
- * enqueued. The current device must be the model's (GQA_E_INVALID otherwise). Every call on a
+ * shape needs about 1.3 MiB; the size grows with vocab / 2 bytes and n_q_heads x 33 KiB);
+ * otherwise GQA_E_INVALID with the needed size, before any work is enqueued. BF16 and Q8_0 KV
+ * caches are both supported. The current device must be the model's (GQA_E_INVALID otherwise). Every call on a
  * device shares that device's array, which keeps the last call's contents (the arrival
  * counters that must start at zero are cleared by the call itself): calls that overlap on one
  * device -- on different streams, or from different models -- race and must not be made. */

@@ -126,6 +126,34 @@ def test_kv_q8_codes_match_oracle(g):
     m.close()
 
 
+def test_kv_q8_quantiser_byte_exact_on_device_inputs(g):
+    """The device's Q8_0 KV quantiser (prefill K/V write) against the oracle's quantiser
+    (oracle.quantize_q8_0, the Q8_0 weight rule of Kipp Model Support, "Quantization (Q8_0)") on
+    the very same FP32 inputs: V rows are stored without normalisation, so after a one-round prefill
+    (40 rows, the GEMM path) the round's FP32 q|k|v projection left in the model's scratch holds
+    exactly what the last layer's V quantiser read. Every code and every fp16 scale bit must match,
+    with no tolerance. Two prompts: random ids, and one repeated id (identical rows, scales from
+    equal maxima)."""
+    shape = synth.TINY
+    T = 40
+    QD, QKV = shape.q_dim, shape.q_dim + 2 * shape.kv_dim
+    for prompt in (synth.token_ids(19, T), np.full(T, 4242, dtype=np.int32)):
+        m = g.Model.from_shape(shape, seed=1001, kv_pool_blocks=4, max_positions=64, kv_quant="q8_0")
+        s = g.Session(m, 64, block_ids=[3, 1])
+        lg = torch.empty(shape.vocab, device="cuda")
+        s.prefill(prompt, lg)
+        torch.cuda.synchronize()
+        qkv = m.read_scratch("qkv", 0, T * QKV).reshape(T, QKV)
+        v = np.ascontiguousarray(qkv[:, QD + shape.kv_dim:QD + 2 * shape.kv_dim], dtype=np.float32)
+        want_s, want_c = quantize_q8_0(v.reshape(-1, 128))
+        kc, ks, vc, vs = s.read_kv_q8(shape.n_layers - 1, 0, T)
+        assert np.array_equal(vs, np.asarray(want_s).reshape(T, 8, 4).view(np.uint16))
+        assert np.array_equal(vc, np.asarray(want_c).reshape(T, 8, 128))
+        say("V quantiser byte-exact over", T * 8 * 128, "codes and", T * 8 * 4, "scales")
+        s.close()
+        m.close()
+
+
 def test_tiny_kv_q8_parity(g):
     """Tiny decoder with the Q8_0 cache: the 16-token prompt and 16 greedy steps, then a 100-token
     prompt in ragged rounds of 48 (each later round reads the earlier ones through the window)."""
