@@ -106,6 +106,34 @@ def measured_traffic():
     return t.get("traffic_bytes_per_launch")
 
 
+def blas_ceiling(reps=10):
+    """Context for the prefill roofline: the vendor BLAS (torch FP16 and BF16 matmul, i.e.
+    hipBLASLt) on the 4B prefill projection shapes at 2,048 tokens with random operands, as a
+    measured ceiling for one FP16 matrix-core pass on this part. Not part of the product path."""
+    import torch
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for dt in (torch.float16, torch.bfloat16):
+        for nm, N, K in (("q|k|v", 6144, 2560), ("o", 2560, 4096), ("gate|up", 19456, 2560), ("down", 2560, 9728)):
+            x = (torch.rand(2048, K, device="cuda", generator=g) * 6 - 3).to(dt)
+            w = ((torch.rand(N, K, device="cuda", generator=g) * 2 - 1) * 0.02).to(dt).t()
+            for _ in range(3):
+                x @ w
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                x @ w
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            tf = 2.0 * 2048 * N * K / (us * 1e-6) / 1e12
+            out[f"{str(dt).split('.')[-1]} {nm}"] = {"us": round(us, 1), "tflops": round(tf, 1),
+                                                     "frac_of_2.5pf": round(tf / 2500, 4)}
+    print(json.dumps({"blas_ceiling": "torch matmul (hipBLASLt), 2048 x K x N, random operands", "shapes": out}),
+          flush=True)
+
+
 def pmc_workload(n_decode):
     """The benchmark's model, prompt and decode loop without torch, for rocprofv3 --pmc passes:
     device buffers come from hipMalloc through the HIP runtime the library is linked against, and
@@ -336,7 +364,12 @@ def main():
     ap.add_argument("--pmc-batch", type=int, default=0, metavar="N",
                     help="run the 8B batched workload (32 sessions, N batched steps) without torch, for "
                          "rocprofv3 --pmc passes (no timing output)")
+    ap.add_argument("--blas-ceiling", action="store_true",
+                    help="time the vendor BLAS on the 4B prefill GEMM shapes (context for the prefill roofline) and exit")
     args = ap.parse_args()
+    if args.blas_ceiling:
+        blas_ceiling()
+        return
     if args.pmc_workload:
         pmc_workload(args.pmc_workload)
         return
