@@ -944,8 +944,15 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
                               uint16_t* vpool, const KvQ8& kq8, float* part, int* counters, float out_scale, f16* ohi,
                               f16* olo, int ldo, hipStream_t st) {
   if (nsplit < 1 || nsplit > 8 || B < 1 || B > kMaxBatch || max_ctx < 1) return hipErrorInvalidValue;
-  const int CH = decode_chunk_len(max_ctx);
-  const int chunks = (max_ctx + CH - 1) / CH;          // rows with shorter contexts exit early
+  // the grid covers the largest chunk count of any row: the count is not monotonic in the
+  // context (the chunk length grows in steps), so a shorter row can need more chunks than the
+  // longest one; workgroups past a row's own count exit early
+  int chunks = 1;
+  for (int b = 0; b < B; ++b) {
+    const int ctx = rows.pos[b] + 1, ch = decode_chunk_len(ctx);
+    if (ctx > max_ctx) return hipErrorInvalidValue;
+    chunks = std::max(chunks, (ctx + ch - 1) / ch);
+  }
   const int G = nq / kKvHeads;
   // up to four rows: the last workgroup of a (row, KV head) merges; more rows: a merge kernel
   const bool fused = B <= 4;

@@ -242,6 +242,41 @@ def test_batched_equals_isolated_bitwise(g, nseq):
         o.close()
 
 
+@pytest.mark.parametrize("lens", [(8193, 4096), (8193, 4096, 3000, 100, 4000)])
+def test_batched_rows_needing_more_chunks_than_the_longest(g, lens):
+    """Regression: a decode row's context is cut into chunks whose length grows in steps, so the
+    chunk count is not monotonic in the context (8,193 positions give 26 chunks of 320, 4,096
+    give 32 of 128). The attention grid must cover the largest count of any row, not the count of
+    the longest row. Tiny shape, fused (2 rows) and row-kernel (5 rows) paths: every batched row
+    equals its twin stepped alone, bit for bit, for 3 steps."""
+    shape = synth.TINY
+    nb = sum(synth.blocks_for(n + 4) for n in lens)
+    m = g.Model.from_shape(shape, seed=1001, kv_pool_blocks=2 * nb + 8, max_positions=8256)
+    lg = torch.empty(shape.vocab, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    A, Bs = [], []
+    for i, n in enumerate(lens):
+        p = synth.token_ids(300 + i, n - 1)                  # decode runs at context n
+        a, b = g.Session(m, n + 4), g.Session(m, n + 4)
+        a.prefill(p, lg)
+        b.prefill(p, lg)
+        A.append(a)
+        Bs.append(b)
+    blg = torch.empty(len(lens), shape.vocab, device="cuda")
+    bam = torch.empty(len(lens), dtype=torch.int32, device="cuda")
+    for step in range(3):
+        ids = [(4099 * step + 13 * i + 5) % shape.vocab for i in range(len(lens))]
+        m.eval_batch(A, ids, blg, bam)
+        torch.cuda.synchronize()
+        for i, sb in enumerate(Bs):
+            sb.decode(ids[i], lg, am)
+            torch.cuda.synchronize()
+            assert torch.equal(lg.view(torch.int32), blg[i].view(torch.int32)), (lens, step, i)
+            assert int(am.item()) == int(bam[i].item())
+    for o in A + Bs + [m]:
+        o.close()
+
+
 def test_device_ids_and_errors(g):
     shape = synth.reduced(synth.TINY, n_layers=1)
     m = g.Model.from_shape(shape, seed=3, kv_pool_blocks=4, max_positions=40)
