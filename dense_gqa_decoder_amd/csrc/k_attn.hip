@@ -33,6 +33,8 @@
 // attn_decode_kernel.
 #include "gqa_common.h"
 
+#include <algorithm>
+
 namespace gqa {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -389,7 +391,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
 //  3. The last workgroup of a (row, KV head) to finish combines the chunk partials of its heads in
 //     chunk order (merge_head).
 constexpr int kDecodeWaves = 4;
-constexpr int kBatchChunksPerWorkgroup = 4;
+#ifndef GQA_BATCH_CHUNKS_PER_WG
+#define GQA_BATCH_CHUNKS_PER_WG 3
+#endif
+constexpr int kBatchChunksPerWorkgroup = GQA_BATCH_CHUNKS_PER_WG;
 
 #ifndef GQA_DECODE_TARGET_CHUNKS
 #define GQA_DECODE_TARGET_CHUNKS 32
@@ -472,11 +477,19 @@ struct DecStage {
   uint16_t vsc;     // Q8_0: their block scale
 };
 
+// Dispatch order of a batch's rows: grid slice z serves row b[z]. Workgroups are dispatched in
+// index order, so the launcher puts the rows with the longest workgroups first and the short ones
+// fill the tail. Which row a workgroup serves does not change what it computes.
+struct RowOrder {
+  uint8_t b[kMaxBatch];
+};
+static_assert(kMaxBatch <= 256, "row indices fit a byte");
+
 template <int G, bool FUSED, bool KQ8>
 __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : (KQ8 ? 2 : 3)) void attn_decode_kernel(
     const float* __restrict__ qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* __restrict__ ss,
     int ss_n, int H, const uint16_t* __restrict__ wqn, const uint16_t* __restrict__ wkn, float eps,
-    const float* __restrict__ rcos, const float* __restrict__ rsin, Rows rows, int cpw, uint16_t* __restrict__ kpool,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, Rows rows, RowOrder order, int cpw, uint16_t* __restrict__ kpool,
     uint16_t* __restrict__ vpool, KvQ8 kq8, float* part, int* __restrict__ counters, float out_scale, f16* __restrict__ ohi,
     f16* __restrict__ olo, int ldo) {
   constexpr int NW = kDecodeWaves;                        // softmax states per workgroup (one per wave)
@@ -487,7 +500,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : (KQ8 ? 2 : 3)) void 
   __shared__ float wo[NW][G][kHeadDim];
   __shared__ __attribute__((aligned(16))) uint16_t vlds[NW][2][16 * kHeadDim];   // V planes, two steps
   __shared__ int s_last;
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int kvh = blockIdx.y, b = order.b[blockIdx.z];
   const int pos = rows.pos[b], ctx = pos + 1;
   const int CH = decode_chunk_len(ctx);
   const int nchunk = (ctx + CH - 1) / CH;
@@ -961,6 +974,18 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
   // across its chunks); the chunks and their partials are the same either way
   const int cpw = fused ? 1 : kBatchChunksPerWorkgroup;
   dim3 grid((chunks + cpw - 1) / cpw, kKvHeads, B);
+  // rows by decreasing workgroup length (positions one workgroup walks), then by decreasing
+  // context, then by index
+  RowOrder order;
+  int wl[kMaxBatch];
+  for (int b = 0; b < B; ++b) {
+    const int ctx = rows.pos[b] + 1, ch = decode_chunk_len(ctx);
+    wl[b] = std::min(ctx, cpw * ch);
+    order.b[b] = (uint8_t)b;
+  }
+  std::stable_sort(order.b, order.b + B, [&](uint8_t x, uint8_t y) {
+    return wl[x] != wl[y] ? wl[x] > wl[y] : rows.pos[x] > rows.pos[y];
+  });
 #define DEC_LAUNCH(GG, FU)                                                                                         \
   do {                                                                                                             \
     if (kq8.kq) {                                                                                                  \
@@ -971,7 +996,7 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
   } while (0)
 #define DEC_LAUNCH_Q(GG, FU, Q)                                                                                    \
   hipLaunchKernelGGL((attn_decode_kernel<GG, FU, Q>), grid, dim3(64 * kDecodeWaves), 0, st, qkvp, nsplit, pstride, QKV, \
-                     nq, ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, cpw, kpool, vpool, kq8, part, counters, out_scale, \
+                     nq, ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, order, cpw, kpool, vpool, kq8, part, counters, out_scale, \
                      ohi, olo, ldo)
   if (G != 4 && G != 2) return hipErrorInvalidValue;
   if (fused) {
