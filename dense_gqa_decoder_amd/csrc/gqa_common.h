@@ -266,7 +266,9 @@ typedef __bf16 bf16v8 __attribute__((ext_vector_type(8)));
 // every LDS read. Being invisible to the compiler, the copies are also not covered by the waits
 // it places before a barrier: a barrier that publishes them must follow vm_wait_all().
 __device__ __forceinline__ void lds_dma16(const void* src, const void* lds_dst) {
-  const uint32_t la = (uint32_t)(uintptr_t)lds_dst;
+  // the destination is the same for the whole wave; readfirstlane keeps it in a scalar register
+  // also where the copy sits under a lane condition
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
   // one wait state between the M0 write and the load that reads it
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la), "v"(src)
                : "memory", "m0");

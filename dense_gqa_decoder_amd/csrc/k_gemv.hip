@@ -302,8 +302,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* _
 }
 
 // B > 4 token rows (X_RAW operands in global memory). The operand rows of the workgroup's K
-// range pass through LDS 256 K-elements at a time: per stage each staged row is one 1 KiB
-// direct-to-LDS copy (hi then lo half), double-buffered, shared by the eight waves (eight 16-row
+// range pass through LDS kRowsStageK K-elements at a time: per stage each staged row is one
+// wave-wide direct-to-LDS copy (hi then lo half), double-buffered, shared by the eight waves (eight 16-row
 // bands) of the workgroup, so the activations cross the L2-to-CU path once per workgroup instead
 // of once per wave. Each wave streams its band's weights one stage ahead in registers and runs
 // the same MFMA chain per (band, K range) as gemv_kernel, so the partials are bit-identical to
@@ -311,7 +311,11 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* _
 // the range are skipped in compute), so a wave issues exactly the same number per stage and one
 // vmcnt wait covers a stage's operand copies and the weights of the stage before.
 constexpr int kRowsWaves = 8;
-constexpr int kRowsStageK = 256;
+#ifndef GQA_ROWS_STAGE_K
+#define GQA_ROWS_STAGE_K 128
+#endif
+constexpr int kRowsStageK = GQA_ROWS_STAGE_K;   // 128: 34 KB of staged rows for 32 tokens, four workgroups per CU
+static_assert(kRowsStageK % 128 == 0 && kRowsStageK <= 256, "whole groups of four K-steps, one copy per row");
 constexpr int kRowsPitch = 2 * kRowsStageK + 8;   // f16 per staged row: hi | lo | 16 bytes pad
 
 template <int N>
@@ -367,15 +371,20 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows_kernel(const uint16
       }
     }
   };
-  // stage t's operand rows into buffer t & 1: lanes 0-31 copy the hi pieces, 32-63 the lo pieces
+  // stage t's operand rows into buffer t & 1, one wave-wide copy per row: lane l brings 16 bytes
+  // to byte 16 l of the row's slot, lanes [0, P) the hi piece and [P, 2 P) the lo piece with
+  // P = kRowsStageK / 8; lanes past 2 P (a stage shorter than 256) copy nothing, which leaves the
+  // number of copies a wave issues per stage unchanged
+  constexpr int P8 = kRowsStageK / 8;
+  static_assert(2 * P8 <= 64 && 16 * 2 * P8 <= 2 * kRowsPitch, "one copy per staged row");
   auto issue_x = [&](int t) {
-    const int hl = lane >> 5;
-    const int kk = min(k0 + t * kRowsStageK + (lane & 31) * 8, ke - 8);
+    const int hl = lane >= P8;
+    const int kk = min(k0 + t * kRowsStageK + (lane % P8) * 8, ke - 8);
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int row = wave * RPW + i;
       const f16* src = (hl ? xs.lo : xs.hi) + (int64_t)min(row, B - 1) * xs.ld + kk;
-      lds_dma16(src, sx + (t & 1) * BUF + row * kRowsPitch);
+      if (2 * P8 == 64 || lane < 2 * P8) lds_dma16(src, sx + (t & 1) * BUF + row * kRowsPitch);
     }
   };
 
