@@ -485,26 +485,75 @@ struct RowOrder {
 };
 static_assert(kMaxBatch <= 256, "row indices fit a byte");
 
+// Shared memory of one decode-attention workgroup.
+template <int G>
+struct AttnSmem {
+  float sraw[(G + 2) * kHeadDim];                         // projection sums (times 1/rms)
+  float sq[(G + 2) * kHeadDim];                           // normed + rotated q (scaled), k; v
+  float wm[kDecodeWaves][G], wl[kDecodeWaves][G];
+  float wo[kDecodeWaves][G][kHeadDim];
+  __attribute__((aligned(16))) uint16_t vlds[kDecodeWaves][2][16 * kHeadDim];   // V planes, two steps
+  int s_last;
+};
+
+// The arguments of a decode-attention launch.
+struct AttnArgs {
+  const float* qkvp;
+  int nsplit;
+  int64_t pstride;
+  int QKV, nq;
+  const float* ss;
+  int ss_n, H;
+  const uint16_t *wqn, *wkn;
+  float eps;
+  const float *rcos, *rsin;
+  Rows rows;
+  RowOrder order;
+  int cpw;
+  uint16_t *kpool, *vpool;
+  KvQ8 kq8;
+  float* part;
+  int* counters;
+  float out_scale;
+  f16 *ohi, *olo;
+  int ldo;
+};
+
+// One workgroup of the decode attention: chunk group bx, KV head kvh, grid row slot zs.
 template <int G, bool FUSED, bool KQ8>
-__global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : (KQ8 ? 2 : 3)) void attn_decode_kernel(
-    const float* __restrict__ qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* __restrict__ ss,
-    int ss_n, int H, const uint16_t* __restrict__ wqn, const uint16_t* __restrict__ wkn, float eps,
-    const float* __restrict__ rcos, const float* __restrict__ rsin, Rows rows, RowOrder order, int cpw, uint16_t* __restrict__ kpool,
-    uint16_t* __restrict__ vpool, KvQ8 kq8, float* part, int* __restrict__ counters, float out_scale, f16* __restrict__ ohi,
-    f16* __restrict__ olo, int ldo) {
+__device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kvh, int zs, const AttnArgs& A) {
   constexpr int NW = kDecodeWaves;                        // softmax states per workgroup (one per wave)
   constexpr int NE = (G + 2) * kHeadDim;                  // q heads, then k and v of the new position
-  __shared__ float sraw[NE];                              // projection sums (times 1/rms)
-  __shared__ float sq[NE];                                // normed + rotated q (scaled), k; v
-  __shared__ float wm[NW][G], wl[NW][G];
-  __shared__ float wo[NW][G][kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint16_t vlds[NW][2][16 * kHeadDim];   // V planes, two steps
-  __shared__ int s_last;
-  const int kvh = blockIdx.y, b = order.b[blockIdx.z];
+  const float* __restrict__ qkvp = A.qkvp;
+  int nsplit = A.nsplit;
+  const int64_t pstride = A.pstride;
+  const int QKV = A.QKV, nq = A.nq, ss_n = A.ss_n, H = A.H, cpw = A.cpw, ldo = A.ldo;
+  const float* __restrict__ ss = A.ss;
+  const uint16_t* __restrict__ wqn = A.wqn;
+  const uint16_t* __restrict__ wkn = A.wkn;
+  const float eps = A.eps, out_scale = A.out_scale;
+  const float* __restrict__ rcos = A.rcos;
+  const float* __restrict__ rsin = A.rsin;
+  const Rows& rows = A.rows;
+  uint16_t* __restrict__ kpool = A.kpool;
+  uint16_t* __restrict__ vpool = A.vpool;
+  const KvQ8& kq8 = A.kq8;
+  float* part = A.part;
+  int* __restrict__ counters = A.counters;
+  f16* __restrict__ ohi = A.ohi;
+  f16* __restrict__ olo = A.olo;
+  float (&sraw)[NE] = sm.sraw;
+  float (&sq)[NE] = sm.sq;
+  float (&wm)[NW][G] = sm.wm;
+  float (&wl)[NW][G] = sm.wl;
+  float (&wo)[NW][G][kHeadDim] = sm.wo;
+  uint16_t (&vlds)[NW][2][16 * kHeadDim] = sm.vlds;
+  int& s_last = sm.s_last;
+  const int b = A.order.b[zs];
   const int pos = rows.pos[b], ctx = pos + 1;
   const int CH = decode_chunk_len(ctx);
   const int nchunk = (ctx + CH - 1) / CH;
-  const int c0 = blockIdx.x * cpw;                        // this workgroup's chunks [c0, c1)
+  const int c0 = bx * cpw;                                // this workgroup's chunks [c0, c1)
   if (c0 >= nchunk) return;
   const int c1 = min(c0 + cpw, nchunk);
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -890,6 +939,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : (KQ8 ? 2 : 3)) void 
   if (tid == 0) counters[b * kKvHeads + kvh] = 0;
 }
 
+template <int G, bool FUSED, bool KQ8>
+__global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : (KQ8 ? 2 : 3)) void attn_decode_kernel(AttnArgs A) {
+  __shared__ AttnSmem<G> sm;
+  attn_decode_body<G, FUSED, KQ8>(sm, blockIdx.x, blockIdx.y, blockIdx.z, A);
+}
+
 // Chunk merge as a kernel of its own, for large batches: grid (KV head, row), one wave per query
 // head of the group. The kernel boundary orders it after every chunk partial, so no workgroup
 // of the attention kernel needs a device-scope fence (with thousands of workgroups those
@@ -986,6 +1041,8 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
   std::stable_sort(order.b, order.b + B, [&](uint8_t x, uint8_t y) {
     return wl[x] != wl[y] ? wl[x] > wl[y] : rows.pos[x] > rows.pos[y];
   });
+  const AttnArgs A{qkvp, nsplit, pstride, QKV, nq, ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, order, cpw,
+                   kpool, vpool, kq8, part, counters, out_scale, ohi, olo, ldo};
 #define DEC_LAUNCH(GG, FU)                                                                                         \
   do {                                                                                                             \
     if (kq8.kq) {                                                                                                  \
@@ -994,10 +1051,8 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
       DEC_LAUNCH_Q(GG, FU, false);                                                                                 \
     }                                                                                                              \
   } while (0)
-#define DEC_LAUNCH_Q(GG, FU, Q)                                                                                    \
-  hipLaunchKernelGGL((attn_decode_kernel<GG, FU, Q>), grid, dim3(64 * kDecodeWaves), 0, st, qkvp, nsplit, pstride, QKV, \
-                     nq, ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, order, cpw, kpool, vpool, kq8, part, counters, out_scale, \
-                     ohi, olo, ldo)
+#define DEC_LAUNCH_Q(GG, FU, Q) \
+  hipLaunchKernelGGL((attn_decode_kernel<GG, FU, Q>), grid, dim3(64 * kDecodeWaves), 0, st, A)
   if (G != 4 && G != 2) return hipErrorInvalidValue;
   if (fused) {
     if (G == 4) DEC_LAUNCH(4, true);
