@@ -100,12 +100,17 @@ struct PrefillLds {
 // writes, per query row t and head h, the partial (m, l, o[128]) of its keys at
 // part[((t * nq + h) * kDecodeMaxChunks + c) * kPartStride] (the decode chunk-partial layout; m in
 // log2 units, o relative to m), merged afterwards by attn_merge_rows_kernel.
-template <int G, bool PSPLIT>
+// KQ8: the cache is Q8_0 (kq8); a copy's 8 codes and their block scale go through registers and
+// are widened to the values attention reads, bf16(fp32(scale) * code), into the same LDS slots
+// the BF16 cache's direct copies fill. They are loaded where the copies are issued and written
+// before the barrier that publishes the tile.
+template <int G, bool PSPLIT, bool KQ8>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restrict__ q, int nq, int T, int pos0,
                                                            const int32_t* __restrict__ table,
                                                            const uint16_t* kpool, const uint16_t* vpool,
                                                            float out_scale, f16* __restrict__ ohi,
-                                                           f16* __restrict__ olo, int ldo, float* __restrict__ part) {
+                                                           f16* __restrict__ olo, int ldo, float* __restrict__ part,
+                                                           KvQ8 kq8) {
   using L = PrefillLds<G>;
   constexpr int NS = L::NS, KT = L::KT, TILE = L::TILE, KPLANE = L::KPLANE, VPLANE = L::VPLANE;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[L::BYTES / 2];
@@ -120,8 +125,6 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
   const int hf = lane >> 5, c32 = lane & 31;
   const float qscale = kLog2e * 0.08838834764831845f;
   const int64_t blk_elems = (int64_t)kKvHeads * kBlock * kHeadDim;
-  const uint16_t* kbase = kpool + (int64_t)kvh * kBlock * kHeadDim;
-  const uint16_t* vbase = vpool + (int64_t)kvh * kBlock * kHeadDim;
 
   // Staging: wave w copies the 1 KiB segments w + 8 i (i < NS) of each tile. A K segment is 32
   // rows (one pool block) of plane (w + 8 i) / NS, rows 32 (w % NS) ..; lane l brings row l / 2,
@@ -159,33 +162,68 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
     // P(t) V(t)), so the K stream runs one tile ahead of the V stream; tile u of a stream sits
     // in buffer u & 1. Iteration t issues the copies of K(t + 2) and V(t + 1) into the buffers
     // that iteration t - 1 finished with; they land while it computes.
+    // Q8_0: one tile of each stream in registers between issue and land
+    uint2 kc[NS], vc[NS];
+    uint16_t ksc[NS], vsc[NS];
     auto issue_k = [&](int u) {
       const int ph = tbl[min(u * KT + krg * 32, kend - 1) >> 5];
       const int key = min(u * KT + krg * 32 + (lane >> 1), kend - 1);   // rows past the last query: a valid row
-      const uint16_t* src = kbase + (int64_t)ph * blk_elems + (key & 31) * kHeadDim + kchunk;
+      const int64_t e0 = (int64_t)ph * blk_elems + ((int64_t)kvh * kBlock + (key & 31)) * kHeadDim + kchunk;
       uint16_t* dst = lds + (u & 1) * TILE;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int sg = wave + 8 * i;
-        lds_dma16(src + 16 * (sg / NS), dst + sg * 512);
+        const int64_t e = e0 + 16 * (sg / NS);
+        if constexpr (KQ8) {
+          kc[i] = *(const uint2*)(kq8.kq + e);
+          ksc[i] = __builtin_bit_cast(uint16_t, kq8.ks[e >> 5]);
+        } else {
+          lds_dma16(kpool + e, dst + sg * 512);
+        }
       }
     };
     auto issue_v = [&](int u) {
       const int ph = tbl[min(u * KT + vrg * 16, kend - 1) >> 5];
       const int key = min(u * KT + vrg * 16 + (lane >> 2), kend - 1);
-      const uint16_t* src = vbase + (int64_t)ph * blk_elems + (key & 31) * kHeadDim + (lane & 3) * 8;
+      const int64_t e0 = (int64_t)ph * blk_elems + ((int64_t)kvh * kBlock + (key & 31)) * kHeadDim + (lane & 3) * 8;
       uint16_t* dst = lds + (2 + (u & 1)) * TILE;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int sg = wave + 8 * i;
-        lds_dma16(src + 32 * (sg / (2 * NS)), dst + sg * 512);
+        const int64_t e = e0 + 32 * (sg / (2 * NS));
+        if constexpr (KQ8) {
+          vc[i] = *(const uint2*)(kq8.vq + e);
+          vsc[i] = __builtin_bit_cast(uint16_t, kq8.vs[e >> 5]);
+        } else {
+          lds_dma16(vpool + e, dst + sg * 512);
+        }
       }
     };
-    // first copies, then the Q loads (their latencies overlap)
+    auto land_k = [&](int u) {
+      uint16_t* dst = lds + (u & 1) * TILE;
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        *(uint4*)(dst + (wave + 8 * i) * 512 + 8 * lane) = q8kv_bf16x8(kc[i], __builtin_bit_cast(f16, ksc[i]));
+    };
+    auto land_v = [&](int u) {
+      uint16_t* dst = lds + (2 + (u & 1)) * TILE;
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        *(uint4*)(dst + (wave + 8 * i) * 512 + 8 * lane) = q8kv_bf16x8(vc[i], __builtin_bit_cast(f16, vsc[i]));
+    };
+    // first copies, then the Q loads (their latencies overlap); Q8_0: K(tb) lands before K(tb + 1)
+    // reuses the registers
     if (tb < ntile) {
       issue_k(tb);
       issue_v(tb);
-      if (tb + 1 < ntile) issue_k(tb + 1);
+      if constexpr (KQ8) {
+        land_k(tb);
+        land_v(tb);
+      }
+      if (tb + 1 < ntile) {
+        issue_k(tb + 1);
+        if constexpr (KQ8) land_k(tb + 1);
+      }
     }
 
     // Q^T operand: lane holds query c32, dims 16 st + 8 hf .. +7, pre-scaled, as BF16 hi/lo
@@ -233,6 +271,12 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
     __syncthreads();
     f32x16 sc = scores(tb);
     for (int t = tb; t < ntile; ++t) {
+      if constexpr (KQ8) {             // the tiles loaded during iteration t - 1
+        if (t > tb) {
+          if (t + 1 < ntile) land_k(t + 1);
+          land_v(t);
+        }
+      }
       vm_wait_all();                   // this wave's copies of K(t + 1) and V(t)
       __syncthreads();                 // ... and every wave's; the buffers of K(t), V(t - 1) are free
       if (t + 2 < ntile) issue_k(t + 2);
@@ -976,8 +1020,8 @@ __global__ __launch_bounds__(64 * G) void attn_merge_rows_kernel(const float* __
 // round of at most 32 rows over a long context splits the keys over several workgroups per KV
 // head (a single query tile would otherwise run on eight workgroups) and merges them after.
 hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const int32_t* table, const uint16_t* kpool,
-                               const uint16_t* vpool, float out_scale, f16* ohi, f16* olo, int ldo, float* part,
-                               hipStream_t st) {
+                               const uint16_t* vpool, const KvQ8& kq8, float out_scale, f16* ohi, f16* olo, int ldo,
+                               float* part, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if ((pos0 + T + 31) / 32 > PrefillLds<4>::MAX_BLOCKS) return hipErrorInvalidValue;   // context too long
   const int G = nq / kKvHeads;
@@ -989,12 +1033,18 @@ hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const in
   const int csplit = (part && T <= 32) ? std::min(kDecodeMaxChunks, std::max(1, (ntile * kt + 255) / 256)) : 1;
   float* const pp = csplit > 1 ? part : nullptr;
   const dim3 grid(pairs * kKvHeads, csplit);
-  if (G == 4)
-    GQA_LAUNCH((attn_prefill_kernel<4, true>), grid, dim3(512), 0, st, q, nq, T, pos0, table, kpool, vpool, out_scale,
-               ohi, olo, ldo, pp);
-  else
-    GQA_LAUNCH((attn_prefill_kernel<2, true>), grid, dim3(512), 0, st, q, nq, T, pos0, table, kpool, vpool, out_scale,
-               ohi, olo, ldo, pp);
+  if (!kq8.kq && (!kpool || !vpool)) return hipErrorInvalidValue;
+#define PF_LAUNCH(GG, Q) \
+  GQA_LAUNCH((attn_prefill_kernel<GG, true, Q>), grid, dim3(512), 0, st, q, nq, T, pos0, table, kpool, vpool, out_scale, \
+             ohi, olo, ldo, pp, kq8)
+  if (G == 4) {
+    if (kq8.kq) PF_LAUNCH(4, true);
+    else PF_LAUNCH(4, false);
+  } else {
+    if (kq8.kq) PF_LAUNCH(2, true);
+    else PF_LAUNCH(2, false);
+  }
+#undef PF_LAUNCH
   if (pp) {
     if (G == 4)
       hipLaunchKernelGGL(attn_merge_rows_kernel<4>, dim3(kKvHeads, T), dim3(256), 0, st, pp, nq, csplit, out_scale, ohi,

@@ -175,11 +175,9 @@ __global__ __launch_bounds__(256) void qk_rope_kv_kernel(const float* __restrict
     int kvh = isk ? h - nq : h - nq - kKvHeads;
     int phys = table[pos >> 5];
     const int64_t off = (((int64_t)phys * kKvHeads + kvh) * kBlock + (pos & 31)) * kHeadDim;
-    uint16_t* dst = (isk ? kpool : vpool) + off;
     if (kq8.kq) {
       // Q8_0 row: lane l holds dims l (block l / 32) and l + 64 (block 2 + l / 32); the block
-      // maxima are taken over each half of the wave. The codes and scales go to the Q8_0 pool, the
-      // values attention reads to the BF16 pool (the layer's read window).
+      // maxima are taken over each half of the wave. Attention reads the codes and scales.
       float ma = fabsf(a), mb = fabsf(b);
 #pragma unroll
       for (int m = 16; m >= 1; m >>= 1) {
@@ -197,52 +195,12 @@ __global__ __launch_bounds__(256) void qk_rope_kv_kernel(const float* __restrict
         sc[l >> 5] = sa;
         sc[2 + (l >> 5)] = sb;
       }
-      dst[l] = q8kv_read_bf16(sa, ca);
-      dst[l + 64] = q8kv_read_bf16(sb, cb);
     } else {
+      uint16_t* dst = (isk ? kpool : vpool) + off;
       dst[l] = f32_to_bf16_rne(a);
       dst[l + 64] = f32_to_bf16_rne(b);
     }
   }
-}
-
-// Read window of a Q8_0 KV cache: the values attention reads, bf16(fp32(scale) * code), of
-// positions [0, rows.pos[b]) of each row b, written to a BF16 pool at the offsets the codes have
-// in the Q8_0 pool (whole 32-position blocks, through the row's block table). grid
-// (ceil(max_n / 32) * 8, B): one workgroup per (block, KV head), 256 threads; a thread converts
-// 16 codes, which share one scale.
-__global__ __launch_bounds__(256) void kv_q8_window_kernel(Rows rows, KvQ8 kq8, uint16_t* __restrict__ kwin,
-                                                          uint16_t* __restrict__ vwin) {
-  const int j = blockIdx.x / kKvHeads, kvh = blockIdx.x % kKvHeads, b = blockIdx.y;
-  if (j * kBlock >= rows.pos[b]) return;
-  const int64_t base = ((int64_t)rows.table[b][j] * kKvHeads + kvh) * kBlock * kHeadDim;
-  constexpr int kChunks = kBlock * kHeadDim / 16;
-  for (int c = threadIdx.x; c < 2 * kChunks; c += 256) {
-    const bool isv = c >= kChunks;
-    const int64_t off = base + (int64_t)(c - (isv ? kChunks : 0)) * 16;
-    const uint4 q = *(const uint4*)((isv ? kq8.vq : kq8.kq) + off);
-    const f16 sc = (isv ? kq8.vs : kq8.ks)[off >> 5];
-    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-    uint32_t w[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {            // codes 2e, 2e + 1: bytes 2 (e % 2), + 1 of word e / 2
-      const int c0 = (int8_t)((qw[e / 2] >> (16 * (e % 2))) & 0xFFu);
-      const int c1 = (int8_t)((qw[e / 2] >> (16 * (e % 2) + 8)) & 0xFFu);
-      w[e] = (uint32_t)q8kv_read_bf16(sc, c0) | ((uint32_t)q8kv_read_bf16(sc, c1) << 16);
-    }
-    uint16_t* dst = (isv ? vwin : kwin) + off;
-    *(uint4*)dst = uint4{w[0], w[1], w[2], w[3]};
-    *(uint4*)(dst + 8) = uint4{w[4], w[5], w[6], w[7]};
-  }
-}
-
-hipError_t launch_kv_q8_window(const Rows& rows, int B, int max_n, const KvQ8& kq8, uint16_t* kwin, uint16_t* vwin,
-                               hipStream_t st) {
-  if (B < 1 || B > kMaxBatch || !kq8.kq) return hipErrorInvalidValue;
-  if (max_n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kv_q8_window_kernel, dim3((max_n + kBlock - 1) / kBlock * kKvHeads, B), dim3(256), 0, st, rows,
-                     kq8, kwin, vwin);
-  return hipGetLastError();
 }
 
 // argmax of each token row from the lm_head matvec's per-tile candidates cand[b][t] =

@@ -41,8 +41,6 @@ hipError_t launch_qk_rope_kv(bool decode, const float* qkv, int nsplit, int part
                              const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
                              const float* rsin, int pos0, const int32_t* table0, const Rows& rows, uint16_t* kpool,
                              uint16_t* vpool, const KvQ8& kq8, float* qout, int nrows, hipStream_t st);
-hipError_t launch_kv_q8_window(const Rows& rows, int B, int max_n, const KvQ8& kq8, uint16_t* kwin, uint16_t* vwin,
-                               hipStream_t st);
 hipError_t launch_argmax(const float2* cand, int ntiles, int B, int32_t* out, hipStream_t st);
 hipError_t launch_argmax_rows(const float* logits, int V, int64_t ld, int rows, int32_t* out, hipStream_t st);
 hipError_t launch_score(const float* logits, int V, const int32_t* targets, int B, float* out, hipStream_t st);
@@ -62,8 +60,8 @@ bool gemv_full_fits(int K, int B);
 hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStream_t st);
 hipError_t launch_final_norm(const XSrc& xs, int B, f16* yhi, f16* ylo, int ldy, hipStream_t st);
 hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const int32_t* table, const uint16_t* kpool,
-                               const uint16_t* vpool, float out_scale, f16* ohi, f16* olo, int ldo, float* part,
-                               hipStream_t st);
+                               const uint16_t* vpool, const KvQ8& kq8, float out_scale, f16* ohi, f16* olo, int ldo,
+                               float* part, hipStream_t st);
 hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, int QKV, int nq, const float* ss,
                               int ss_n, int H, const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
                               const float* rsin, const Rows& rows, int B, int max_ctx, uint16_t* kpool,
@@ -144,7 +142,6 @@ struct gqa_model {
         *apart = nullptr;
   float* ppart = nullptr;       // prefill: K-range partials of the o and down projections [<= 4 R][H]
   int32_t* counters = nullptr;  // decode attention: finished chunks per (row, KV head)
-  uint16_t *kwin = nullptr, *vwin = nullptr;   // Q8_0 KV cache: the BF16 read window of one layer
   float* ss = nullptr;          // decode: sum-of-squares partials [2][8][32] (q|k|v input, gate|up input)
   float2* cand = nullptr;   // lm_head argmax candidates [32][vocab / 16]
   float* slog = nullptr;    // logits of up to kScoreRows rows being scored [kScoreRows][vocab]
@@ -468,10 +465,6 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
       ALLOC(w.vpool, pool_elems, &m->kv_bytes);
     }
   }
-  if (d.kv_quant == GQA_KV_Q8_0) {           // one layer's BF16 read window
-    ALLOC(m->kwin, pool_elems, &m->kv_bytes);
-    ALLOC(m->vwin, pool_elems, &m->kv_bytes);
-  }
   const int rows = std::max(m->R, kMaxBatch);
   int64_t* sb = &m->scratch_bytes;
   ALLOC(m->x, (int64_t)rows * H, sb);
@@ -586,10 +579,6 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
       chk(hipMemsetAsync(w.kpool, 0, pool_elems * 2, st));
       chk(hipMemsetAsync(w.vpool, 0, pool_elems * 2, st));
     }
-  }
-  if (d.kv_quant == GQA_KV_Q8_0) {
-    chk(hipMemsetAsync(m->kwin, 0, pool_elems * 2, st));
-    chk(hipMemsetAsync(m->vwin, 0, pool_elems * 2, st));
   }
   chk(hipMemsetAsync(m->err, 0, 4, st));
   chk(hipMemsetAsync(m->counters, 0, sizeof(int32_t) * kMaxBatch * kKvHeads, st));
@@ -1041,8 +1030,9 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
   const int H = d.hidden, F = d.ffn, V = d.vocab, NQ = d.n_q_heads, QD = m->QD, QKV = m->QKV;
   const float eps = d.rms_eps;
   Rows none{};
-  auto kv_k = [m](const LayerW& w) { return w.kq8.kq ? m->kwin : w.kpool; };
-  auto kv_v = [m](const LayerW& w) { return w.kq8.kq ? m->vwin : w.vpool; };
+  // a Q8_0 cache has no BF16 pools: K/V are written and read as codes and scales (w.kq8)
+  auto kv_k = [](const LayerW& w) { return w.kpool; };
+  auto kv_v = [](const LayerW& w) { return w.vpool; };
   const bool split = d.prefill_operands == GQA_PREFILL_SPLIT;
   // the GEMM reads Q8_0 quants directly if so configured; otherwise every scheme uses the FP16
   // prefill copies
@@ -1071,12 +1061,6 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
     for (int l = 0; l < d.n_layers; ++l) {
       const LayerW& w = m->L[l];
       const bool last = l + 1 == d.n_layers;
-      if (w.kq8.kq && pos0 > 0) {             // Q8_0 cache: the earlier positions into the read window
-        Rows win{};
-        win.pos[0] = pos0;
-        win.table[0] = s->d_table;
-        LAUNCH(launch_kv_q8_window(win, 1, pos0, w.kq8, m->kwin, m->vwin, st));
-      }
       if (mv) {
         int rc = matvec(w.wqkv, w.qqkv, w.sqkv, w.bqkv, H, QKV, m->xh, m->xl, H, T, m->s_qkv, m->part);
         if (rc) return rc;
@@ -1093,7 +1077,7 @@ int run_prefill(gqa_session* s, const int32_t* ids_dev, int n, int out, float* l
       const int rows = one ? 1 : T, r0 = one ? T - 1 : 0;
       {
         ProfScope ps(m, last ? kProfNever : GQA_PROF_PREFILL_ATTN, st);
-        LAUNCH(launch_attn_prefill(m->q + (int64_t)r0 * QD, NQ, rows, pos0 + r0, s->d_table, kv_k(w), kv_v(w),
+        LAUNCH(launch_attn_prefill(m->q + (int64_t)r0 * QD, NQ, rows, pos0 + r0, s->d_table, kv_k(w), kv_v(w), w.kq8,
                                    kAttnOutScale, m->oh, m->ol, QD, m->apart, st));
       }
       float* pp = mv ? m->part2 : m->ppart;     // o and down partials

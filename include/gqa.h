@@ -89,10 +89,8 @@ typedef struct {
                                as four Q8_0 blocks of 32 (int8 codes, fp16 scale = fp16(max|x|/127),
                                codes round(x / (max|x|/127)) half away from zero, the Q8_0 weight
                                rule): 136 bytes instead of 256. Attention reads
-                               bf16(scale * code): decode attention widens the codes as it
-                               loads them; the model also holds one layer's BF16 read window,
-                               rebuilt from the codes of the earlier positions before a layer's
-                               attention in a prefill round that starts past position 0 */
+                               bf16(scale * code): the decode and prefill attention kernels widen
+                               the codes as they load them; no BF16 copy is kept */
 } gqa_model_desc;
 
 #define GQA_PREFILL_SPLIT 0
@@ -105,8 +103,8 @@ typedef struct {
   int32_t round_tokens;       /* prefill round width in use */
   int32_t cu_count;           /* compute units of the device */
   int64_t weight_bytes;       /* device bytes of all weights (Q8_0: quants + scales) */
-  int64_t kv_pool_bytes;      /* device bytes of the K and V pools (with a Q8_0 cache: codes, scales
-                                 and the one-layer BF16 read window) */
+  int64_t kv_pool_bytes;      /* device bytes of the K and V pools (with a Q8_0 cache: codes and
+                                 scales) */
   int64_t scratch_bytes;      /* device bytes of per-model activation scratch */
   int64_t prefill_copy_bytes; /* device bytes of the FP16 copies prefill GEMMs read: projections
                                  (BF16, or dequantised Q8_0 / AFFINE4) and the padded lm_head */

@@ -64,15 +64,15 @@ def check(name, got, ref):
 
 
 def test_kv_q8_pool_bytes(g):
-    """Per position and KV head 2 x (128 codes + 4 fp16 scales) = 272 bytes instead of 512, plus one
-    layer's BF16 read window."""
+    """Per position and KV head 2 x (128 codes + 4 fp16 scales) = 272 bytes instead of 512 (1.88x);
+    no BF16 copy of any layer is kept."""
     shape = synth.TINY
     nb = 8
     mq = g.Model.from_shape(shape, seed=1001, kv_pool_blocks=nb, max_positions=64, kv_quant="q8_0")
     mb = g.Model.from_shape(shape, seed=1001, kv_pool_blocks=nb, max_positions=64)
     per = nb * 8 * 32
     assert mb.info().kv_pool_bytes == shape.n_layers * per * 512
-    assert mq.info().kv_pool_bytes == shape.n_layers * per * 272 + per * 512
+    assert mq.info().kv_pool_bytes == shape.n_layers * per * 272
     mq.close()
     mb.close()
 
@@ -156,7 +156,7 @@ def test_kv_q8_quantiser_byte_exact_on_device_inputs(g):
 
 def test_tiny_kv_q8_parity(g):
     """Tiny decoder with the Q8_0 cache: the 16-token prompt and 16 greedy steps, then a 100-token
-    prompt in ragged rounds of 48 (each later round reads the earlier ones through the window)."""
+    prompt in ragged rounds of 48 (each later round's attention reads the earlier rounds' codes)."""
     wl = synth.WORKLOADS["tiny"]
     shape = wl.shape
     prompt = synth.token_ids(wl.ids_seed, wl.prompt)
