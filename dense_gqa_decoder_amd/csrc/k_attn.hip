@@ -434,7 +434,11 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
 //     for that position.
 //  3. The last workgroup of a (row, KV head) to finish combines the chunk partials of its heads in
 //     chunk order (merge_head).
-constexpr int kDecodeWaves = 4;
+#ifndef GQA_DECODE_WAVES
+#define GQA_DECODE_WAVES 4
+#endif
+constexpr int kDecodeWaves = GQA_DECODE_WAVES;
+constexpr int kDecodeStep = 16 * kDecodeWaves;          // positions per step: 16 keys per wave
 #ifndef GQA_BATCH_CHUNKS_PER_WG
 #define GQA_BATCH_CHUNKS_PER_WG 3
 #endif
@@ -443,12 +447,12 @@ constexpr int kBatchChunksPerWorkgroup = GQA_BATCH_CHUNKS_PER_WG;
 #ifndef GQA_DECODE_TARGET_CHUNKS
 #define GQA_DECODE_TARGET_CHUNKS 32
 #endif
-// Chunk length of a row's context: the smallest multiple of 64 positions that cuts it into at
-// most GQA_DECODE_TARGET_CHUNKS chunks (<= kDecodeMaxChunks). A function of the row's own
-// context only, so a row's partials and merge do not depend on the batch.
+// Chunk length of a row's context: the smallest multiple of a step (kDecodeStep positions) that
+// cuts it into at most GQA_DECODE_TARGET_CHUNKS chunks (<= kDecodeMaxChunks). A function of the
+// row's own context only, so a row's partials and merge do not depend on the batch.
 __host__ __device__ __forceinline__ int decode_chunk_len(int ctx) {
   static_assert(GQA_DECODE_TARGET_CHUNKS >= 1 && GQA_DECODE_TARGET_CHUNKS <= kDecodeMaxChunks, "chunk count");
-  return 64 * ((ctx + 64 * GQA_DECODE_TARGET_CHUNKS - 1) / (64 * GQA_DECODE_TARGET_CHUNKS));
+  return kDecodeStep * ((ctx + kDecodeStep * GQA_DECODE_TARGET_CHUNKS - 1) / (kDecodeStep * GQA_DECODE_TARGET_CHUNKS));
 }
 
 // Device-scope (sc1) accesses: coherent across the XCDs' L2 caches without an L2 writeback or
@@ -604,7 +608,7 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
   const int hq = lane & 15, g4 = lane >> 4;
   const bool owner = c1 == nchunk;                        // the last chunk holds the new position
   auto p_end_of = [&](int cc) { return min(cc * CH + CH, ctx); };
-  auto niter_of = [&](int cc) { return (p_end_of(cc) - cc * CH + 63) / 64; };
+  auto niter_of = [&](int cc) { return (p_end_of(cc) - cc * CH + kDecodeStep - 1) / kDecodeStep; };
   const int32_t* table = rows.table[b];
   constexpr int64_t kBlockElems = (int64_t)kKvHeads * kBlock * kHeadDim;
 
@@ -615,7 +619,7 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
   //   K: lane l loads key l % 16, dims 32 s + 8 (l / 16) .. + 7 for s = 0..3 (the A operand rows).
   //   V: four 1 KiB direct-to-LDS copies into 16-dim planes (16 keys x 32 bytes each); copy j
   //      fills planes 2 j, 2 j + 1, lane l bringing key (l % 32) / 2, half l % 2 of the plane.
-  auto phys_of = [&](int cc, int it) { return table[min(cc * CH + it * 64 + wave * 16, p_end_of(cc) - 1) >> 5]; };
+  auto phys_of = [&](int cc, int it) { return table[min(cc * CH + it * kDecodeStep + wave * 16, p_end_of(cc) - 1) >> 5]; };
   //   Q8_0 cache: K as above but the codes (8 bytes per lane and 32-dim step) and the key's four
   //   block scales; V: lane l brings the 32 codes of key l / 4, dims 32 (l % 4) .. + 31, and their
   //   scale, widened into the same LDS planes when the step is computed.
@@ -776,7 +780,7 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
   };
   auto compute = [&](int cc, int it, DecStage& sg, int buf) {
-    const int p0 = cc * CH + it * 64 + wave * 16, p_end = p_end_of(cc);
+    const int p0 = cc * CH + it * kDecodeStep + wave * 16, p_end = p_end_of(cc);
     uint16_t* vl = vlds[wave][buf];
     uint4 (&kr)[4] = sg.kr;
     if constexpr (KQ8) {                                  // widen the step's codes (before the new row's overrides)
