@@ -1,4 +1,4 @@
-// GQA attention over the paged BF16 KV cache.
+// GQA attention over the paged KV cache (BF16, or Q8_0 codes read as bf16(scale * code)).
 //
 // Kipp Roadmap, status v0.0.3/v0.0.4: flash-attention prefill for GQA (kipp_flash_gqa_prefill);
 // status v0.0.2: K/V live in 32-position blocks addressed through a per-session block table.
@@ -14,7 +14,9 @@
 // queries of head h and, of every staged tile of 32 * 8/g keys, the 32-key subtile s, with its
 // own online-softmax state; the split states are merged in LDS at the end of the query tile.
 //  - K and V tiles go from the pool to LDS by direct-to-LDS loads (no register staging), double
-//    buffered; the block ids of the keys are staged in LDS once per workgroup. K runs one tile
+//    buffered; the block ids of the keys are staged in LDS once per workgroup. With a Q8_0 cache
+//    each copy's codes and block scale pass through registers and are widened into the same
+//    LDS slots. K runs one tile
 //    ahead of V, so each iteration issues the score MFMAs of the next subtile in the same
 //    straight-line block as the softmax and P V products of the current one.
 //  - S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K is the exact BF16 A operand (one 16-byte LDS
@@ -29,8 +31,8 @@
 //  - The running max is kept lazily: the accumulator and sum are rescaled only when a new score
 //    exceeds the reference max by more than 2^8, so p = 2^(s - m) stays below 256.
 //
-// Decode: split-context attention in FP32 on the vector ALUs, then a chunk merge; see
-// attn_decode_kernel.
+// Decode: split-context attention on the matrix cores into chunk partials, then a chunk merge in
+// chunk order; see attn_decode_kernel.
 #include "gqa_common.h"
 
 #include <algorithm>
@@ -418,13 +420,15 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const float* __restri
   }
 }
 
-// Decode attention (split context), grid (chunk, KV head, row), four waves per workgroup.
-// A row's context [0, pos] is cut into chunks of decode_chunk_len(ctx) positions (a multiple of
-// 64 chosen from the row's own context length only, so a row gets the same chunks whether it is
-// evaluated alone or in a batch). A workgroup walks its chunk 64 positions at a time, wave w
-// taking 16 consecutive keys on the matrix cores (section 3 below); each wave keeps its own
-// online-softmax state (max, sum, value sum) for the g query heads of the KV head, and the four
-// states are merged in LDS, in wave order, into one chunk partial (max, sum, o[128]) per head.
+// Decode attention (split context), grid (chunk group, KV head, row), kDecodeWaves (four) waves
+// per workgroup. A row's context [0, pos] is cut into chunks of decode_chunk_len(ctx) positions
+// (a multiple of the 64-position step chosen from the row's own context length only, so a row
+// gets the same chunks whether it is evaluated alone or in a batch). A workgroup walks its chunk
+// one step at a time, wave w taking 16 consecutive keys on the matrix cores (section 3 below);
+// each wave keeps its own online-softmax state (max, sum, value sum) for the g query heads of the
+// KV head, and the wave states are merged in LDS, in wave order, into one chunk partial (max,
+// sum, o[128]) per head. A Q8_0 cache is read as codes and block scales, widened to
+// bf16(scale * code) as a step is computed.
 //  1. q for the g query heads: the fixed-order sum of the q|k|v projection's split partials,
 //     times the row's 1/rms (recomputed from the sum-of-squares partials the projection's
 //     prologue wrote), per-head RMSNorm, rotate-half RoPE at the row's position, built once
