@@ -134,11 +134,13 @@ def blas_ceiling(reps=10):
           flush=True)
 
 
-def pmc_workload(n_decode):
+def pmc_workload(n_decode, chained=False):
     """The benchmark's model, prompt and decode loop without torch, for rocprofv3 --pmc passes:
     device buffers come from hipMalloc through the HIP runtime the library is linked against, and
     a 256 MiB device-to-device copy of known size follows, whose FETCH_SIZE / WRITE_SIZE readings
-    calibrate the byte counters. Prints the copy size and exits."""
+    calibrate the byte counters. The decode steps run with the gate/up matvec's event timing on,
+    as in bench.py's roofline leg (the per-layer launches unchained, so the counted kernel is the
+    one the events time), or chained as in the timed steps. Prints the copy size and exits."""
     import ctypes
     import dense_gqa_decoder_amd as g
     import synth
@@ -166,8 +168,11 @@ def pmc_workload(n_decode):
     s = g.Session(m, nb * 32, block_ids=table)
     lg, am = DevBuf(wl.shape.vocab * 4), DevBuf(4)
     s.prefill(synth.token_ids(wl.ids_seed, wl.prompt), lg, am, NullStream)
+    if not chained:
+        m.profile("decode_gateup")
     for _ in range(n_decode):
         s.decode(am, lg, am, NullStream)
+    m.profile("none")
     size = 256 << 20
     src, dst = DevBuf(size), DevBuf(size)
     if hip.hipMemset(ctypes.c_void_p(src.p), 1, ctypes.c_size_t(size)) != 0 or \
@@ -176,8 +181,8 @@ def pmc_workload(n_decode):
         raise RuntimeError("calibration copy failed")
     s.close()
     m.close()
-    print(json.dumps({"pmc_workload": wl.shape.name, "decode_steps": n_decode, "calibration_copy_bytes": size}),
-          flush=True)
+    print(json.dumps({"pmc_workload": wl.shape.name, "decode_steps": n_decode, "decode_chained": chained,
+                      "calibration_copy_bytes": size}), flush=True)
 
 
 def pmc_batch_workload(n_steps):
@@ -361,6 +366,9 @@ def main():
     ap.add_argument("--pmc-workload", type=int, default=0, metavar="N",
                     help="run the 4B prompt + N decode steps and a known-size copy without torch, "
                          "for rocprofv3 --pmc passes (no timing output)")
+    ap.add_argument("--pmc-chained", action="store_true",
+                    help="with --pmc-workload: decode chained as in the timed steps (default: unchained, as in "
+                         "the roofline leg)")
     ap.add_argument("--pmc-batch", type=int, default=0, metavar="N",
                     help="run the 8B batched workload (32 sessions, N batched steps) without torch, for "
                          "rocprofv3 --pmc passes (no timing output)")
@@ -371,7 +379,7 @@ def main():
         blas_ceiling()
         return
     if args.pmc_workload:
-        pmc_workload(args.pmc_workload)
+        pmc_workload(args.pmc_workload, args.pmc_chained)
         return
     if args.pmc_batch:
         pmc_batch_workload(args.pmc_batch)
@@ -444,7 +452,9 @@ def main():
     flops, dec_bytes, w_bytes = algorithmic(shape, wl.prompt, wl.decode, wl.scheme, wl.kv_quant)
 
     # dominant kernel (decode gate/up matvec): HIP events around each of its launches in one
-    # more step identical to the timed ones
+    # more step identical to the timed ones, except that while the gate/up class is recorded the
+    # library issues the decode's per-layer launches unchained (a chained launch starts before its
+    # predecessor ends and waits, so its events would include the wait)
     kernels = {}
     for cls in ("decode_gateup", "prefill_gateup", "prefill_attn"):
         m.profile(cls)

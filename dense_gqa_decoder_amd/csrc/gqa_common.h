@@ -20,16 +20,20 @@ struct LaunchEvents {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 extern thread_local LaunchEvents g_launch_events;
-#define GQA_LAUNCH(kernel, grid, block, shm, st, ...)                                                         \
+// GQA_LAUNCH_F passes dispatch flags (hipExtAnyOrderLaunch for the chained decode launches).
+#define GQA_LAUNCH_F(kernel, grid, block, shm, st, flags, ...)                                                \
   do {                                                                                                      \
     if (::gqa::g_launch_events.start) {                                                                     \
       const ::gqa::LaunchEvents ev_ = ::gqa::g_launch_events;                                               \
       ::gqa::g_launch_events = ::gqa::LaunchEvents{};                                                       \
-      hipExtLaunchKernelGGL(kernel, grid, block, shm, st, ev_.start, ev_.stop, 0, __VA_ARGS__);            \
+      hipExtLaunchKernelGGL(kernel, grid, block, shm, st, ev_.start, ev_.stop, flags, __VA_ARGS__);        \
+    } else if (flags) {                                                                                     \
+      hipExtLaunchKernelGGL(kernel, grid, block, shm, st, nullptr, nullptr, flags, __VA_ARGS__);           \
     } else {                                                                                                \
       hipLaunchKernelGGL(kernel, grid, block, shm, st, __VA_ARGS__);                                        \
     }                                                                                                       \
   } while (0)
+#define GQA_LAUNCH(kernel, grid, block, shm, st, ...) GQA_LAUNCH_F(kernel, grid, block, shm, st, 0u, __VA_ARGS__)
 
 
 constexpr int kHeadDim = 128;
@@ -91,6 +95,115 @@ struct XSrc {
 
 enum FullMode : int { XF_RAW = 0, XF_NORM = 1 };
 
+// ---- Dependent decode launches without a queue barrier
+// The per-layer launches of a decode of a few rows go out with hipExtAnyOrderLaunch: the queue
+// then neither holds a launch until its predecessor has finished nor writes back and
+// invalidates the L2 caches between the two, which saves most of the fixed cost of a dependent
+// launch. Each launch orders itself against its predecessors instead:
+//  * a producer writes what later launches of the chain read with device-scope stores (through
+//    the non-coherent per-XCD L2 to memory); at its end every wave waits until its stores have
+//    completed, then one thread adds 1 to arrival counter (workgroup index) % kChainLanes;
+//  * a consumer first issues the loads that do not depend on its predecessors (weights, block
+//    table, constants), then one wave polls the counters until each has reached the target the
+//    host passed (the arrivals of every earlier launch of the chain), and then reads the
+//    predecessors' outputs with device-scope loads.
+// A wait is bounded: after kChainSpinMax polls (about 0.1 s) the workgroup sets kErrChainWait in
+// the model's error word and goes on, and every later wait that sees the flag gives up at once
+// (wrong results, reported by gqa_model_check_device_error; no hang). The counters are cleared
+// by the first (ordered) launch of each call.
+constexpr int kChainLanes = 16;
+constexpr int kChainStride = 64;          // ints between counters: one 256-byte line each
+constexpr int kChainInts = kChainLanes * kChainStride;
+constexpr int kChainSpinMax = 1 << 16;
+constexpr int32_t kErrChainWait = 2;
+struct Chain {
+  int32_t* cnt = nullptr;                 // arrival counters, or null: not chained
+  int32_t* err = nullptr;                 // error word
+  int wait = 0;                           // 1: wait for target[] first (any-order launch)
+  int32_t target[kChainLanes] = {};
+};
+
+// Device-scope (sc1) accesses of the chained buffers.
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev8(const void* p) {
+  return __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint4 ld_dev16(const void* p) {
+  const uint64_t a = ld_dev8(p), b = ld_dev8((const char*)p + 8);
+  return uint4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+}
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev8(void* p, uint64_t v) {
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev16(void* p, uint4 v) {
+  st_dev8(p, (uint64_t)v.x | ((uint64_t)v.y << 32));
+  st_dev8((char*)p + 8, (uint64_t)v.z | ((uint64_t)v.w << 32));
+}
+
+// Wait until every counter has reached its target (all threads of the workgroup call this).
+__device__ __forceinline__ void chain_wait(const Chain& c) {
+  if (!c.wait) return;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    // lanes 0..15 poll the counters, lane 16 the error word
+    const int32_t want = lane < kChainLanes ? c.target[lane] : 0;
+    const int32_t* at = lane < kChainLanes ? c.cnt + lane * kChainStride : c.err;
+    for (int spin = 0;; ++spin) {
+      const int32_t v = __hip_atomic_load(at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__all(lane >= kChainLanes || v >= want)) break;
+      if (__any(lane >= kChainLanes && (v & kErrChainWait))) break;   // an earlier wait gave up
+      if (spin >= kChainSpinMax) {
+        if (lane == 0) __hip_atomic_fetch_or(c.err, kErrChainWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+// Count this workgroup in once all of its stores have completed (all threads call this).
+__device__ __forceinline__ void chain_signal(const Chain& c) {
+  if (!c.cnt) return;
+  __builtin_amdgcn_s_waitcnt(0);          // vmcnt = lgkmcnt = 0: this wave's stores are done
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    __hip_atomic_fetch_add(c.cnt + (wg % kChainLanes) * kChainStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Host side: the targets of the next launch of a chain, and the arrivals of each launch.
+struct ChainTrack {
+  int32_t* cnt = nullptr;
+  int32_t* err = nullptr;
+  int32_t arrived[kChainLanes] = {};
+  int launches = 0;
+  // Arguments of the next launch: the first one is an ordinary launch (the queue holds it until
+  // the call's earlier, unchained work has finished) that only signals; the others go out
+  // any-order and wait. (An ordinary launch in the middle of a chain would cost more than the
+  // chain saves: the queue would hold it until all any-order launches before it had finished.)
+  Chain next() const {
+    Chain c;
+    if (!cnt) return c;
+    c.cnt = cnt;
+    c.err = err;
+    c.wait = launches > 0;
+    for (int i = 0; i < kChainLanes; ++i) c.target[i] = arrived[i];
+    return c;
+  }
+  void launched(int nwg) {
+    if (!cnt) return;
+    for (int i = 0; i < kChainLanes; ++i) arrived[i] += nwg / kChainLanes + (i < nwg % kChainLanes ? 1 : 0);
+    ++launches;
+  }
+};
+
 // Arguments of the whole-K decode matvec (k_gemv_full.hip).
 struct FullArgs {
   const uint16_t* W;
@@ -112,6 +225,7 @@ struct FullArgs {
   f16* mlo;
   int ldm;
   float2* cand;            // EPI_STORE: argmax candidates [B][N / 16] or null
+  Chain chain;             // chained decode launch (or none)
 };
 
 // Sum-of-squares partials: ss[range][row], kMaxBatch rows per range.
@@ -120,6 +234,16 @@ __device__ __forceinline__ float inv_rms_from_ss(const float* ss, int n, int row
   float v[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) v[r] = ss[min(r, n - 1) * 32 + row];   // unconditional, no branches
+  float t = 0.f;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) t += r < n ? v[r] : 0.f;
+  return 1.0f / sqrtf(t / (float)H + eps);
+}
+// The same from device-scope loads (partials written by a chained predecessor).
+__device__ __forceinline__ float inv_rms_from_ss_dev(const float* ss, int n, int row, int H, float eps) {
+  float v[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) v[r] = ld_dev(ss + min(r, n - 1) * 32 + row);
   float t = 0.f;
 #pragma unroll
   for (int r = 0; r < 8; ++r) t += r < n ? v[r] : 0.f;

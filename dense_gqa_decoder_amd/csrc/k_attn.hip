@@ -474,7 +474,7 @@ __device__ __forceinline__ float2 load_dev2(const float* p) {
 // w_c l_c with w_c = 2^(m_c - max m). One wave; lane t owns dims 2t, 2t + 1. The result is
 // written as the FP16 hi/lo operand of the o projection, times out_scale. DEV: the partials
 // were written by other workgroups of the same launch (device-scope loads).
-template <bool DEV, int NC>
+template <bool DEV, int NC, bool STDEV = false>
 __device__ __forceinline__ void merge_head_n(const float* pp, int nchunk, int lane, float out_scale, f16* ohi,
                                              f16* olo) {
   auto ld2 = [](const float* p) { return DEV ? load_dev2(p) : *(const float2*)p; };
@@ -502,20 +502,27 @@ __device__ __forceinline__ void merge_head_n(const float* pp, int nchunk, int la
   f16 h0, l0, h1, l1;
   split_f16(o0 * inv, h0, l0);
   split_f16(o1 * inv, h1, l1);
-  *(f16x2*)(ohi + 2 * lane) = f16x2{h0, h1};
-  *(f16x2*)(olo + 2 * lane) = f16x2{l0, l1};
+  if constexpr (STDEV) {                                  // read by the next launch of a chain
+    __hip_atomic_store((uint32_t*)(ohi + 2 * lane), __builtin_bit_cast(uint32_t, f16x2{h0, h1}), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store((uint32_t*)(olo + 2 * lane), __builtin_bit_cast(uint32_t, f16x2{l0, l1}), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *(f16x2*)(ohi + 2 * lane) = f16x2{h0, h1};
+    *(f16x2*)(olo + 2 * lane) = f16x2{l0, l1};
+  }
 }
 
 // merge_head_n over the slots a context can use: NC = 32 when it has at most 32 chunks (half the
 // partial loads), else all 64. The slots past nchunk enter with weight 0 and add exact zeros, so
 // both give the same bits.
-template <bool DEV>
+template <bool DEV, bool STDEV = false>
 __device__ __forceinline__ void merge_head(const float* pp, int nchunk, int lane, float out_scale, f16* ohi,
                                            f16* olo) {
   if (nchunk <= 32)
-    merge_head_n<DEV, 32>(pp, nchunk, lane, out_scale, ohi, olo);
+    merge_head_n<DEV, 32, STDEV>(pp, nchunk, lane, out_scale, ohi, olo);
   else
-    merge_head_n<DEV, kDecodeMaxChunks>(pp, nchunk, lane, out_scale, ohi, olo);
+    merge_head_n<DEV, kDecodeMaxChunks, STDEV>(pp, nchunk, lane, out_scale, ohi, olo);
 }
 
 // K/V of one wave's 16 keys of a 64-position step, in flight: BF16 K rows in registers (the V
@@ -569,10 +576,13 @@ struct AttnArgs {
   float out_scale;
   f16 *ohi, *olo;
   int ldo;
+  Chain chain;                                            // a launch of a decode chain (or none)
 };
 
 // One workgroup of the decode attention: chunk group bx, KV head kvh, grid row slot zs.
-template <int G, bool FUSED, bool KQ8>
+// CHAIN: a launch of a decode chain (gqa_common.h): issues its first K/V, waits for its
+// predecessors, reads the projection device-scope and writes the merged rows device-scope.
+template <int G, bool FUSED, bool KQ8, bool CHAIN>
 __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kvh, int zs, const AttnArgs& A) {
   constexpr int NW = kDecodeWaves;                        // softmax states per workgroup (one per wave)
   constexpr int NE = (G + 2) * kHeadDim;                  // q heads, then k and v of the new position
@@ -665,6 +675,10 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
     const int nel = owner ? NE : G * kHeadDim;
     constexpr int NI = (NE + 64 * kDecodeWaves - 1) / (64 * kDecodeWaves);
     float t[NI][8];
+    if constexpr (CHAIN) {                               // one projection range (nsplit == 1)
+      issue(phys0, kA, 0);
+      chain_wait(A.chain);
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {                       // every load first
       const int e = i * 64 * kDecodeWaves + tid;
@@ -672,10 +686,15 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
                                         : (e < (G + 1) * kHeadDim ? nq + kvh : nq + kKvHeads + kvh);
       const float* p = qrow + (e < nel ? hrow * kHeadDim + (e % kHeadDim) : 0);
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) t[i][s2] = p[(int64_t)min(s2, nsplit - 1) * pstride];   // unconditional
+      for (int s2 = 0; s2 < 8; ++s2) {
+        if constexpr (CHAIN)
+          t[i][s2] = s2 == 0 ? ld_dev(p) : 0.f;
+        else
+          t[i][s2] = p[(int64_t)min(s2, nsplit - 1) * pstride];   // unconditional
+      }
     }
-    issue(phys0, kA, 0);
-    const float cin = inv_rms_from_ss(ss, ss_n, b, H, eps);
+    if constexpr (!CHAIN) issue(phys0, kA, 0);
+    const float cin = CHAIN ? inv_rms_from_ss_dev(ss, ss_n, b, H, eps) : inv_rms_from_ss(ss, ss_n, b, H, eps);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int e = i * 64 * kDecodeWaves + tid;
@@ -985,16 +1004,24 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
   if (!s_last) return;
   if (wave < G) {
     const int h = kvh * G + wave;
-    merge_head<true>(part + ((int64_t)b * nq + h) * kDecodeMaxChunks * kPartStride, nchunk, lane, out_scale,
+    merge_head<true, CHAIN>(part + ((int64_t)b * nq + h) * kDecodeMaxChunks * kPartStride, nchunk, lane, out_scale,
                      ohi + (int64_t)b * ldo + h * kHeadDim, olo + (int64_t)b * ldo + h * kHeadDim);
   }
-  if (tid == 0) counters[b * kKvHeads + kvh] = 0;
+  // in a chain the count goes back to zero with a device-scope store, which the arrivals of a
+  // later any-order launch cannot overtake through a cache writeback
+  if (tid == 0) {
+    if constexpr (CHAIN)
+      __hip_atomic_store(&counters[b * kKvHeads + kvh], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      counters[b * kKvHeads + kvh] = 0;
+  }
 }
 
-template <int G, bool FUSED, bool KQ8>
+template <int G, bool FUSED, bool KQ8, bool CHAIN>
 __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : (KQ8 ? 2 : 3)) void attn_decode_kernel(AttnArgs A) {
   __shared__ AttnSmem<G> sm;
-  attn_decode_body<G, FUSED, KQ8>(sm, blockIdx.x, blockIdx.y, blockIdx.z, A);
+  attn_decode_body<G, FUSED, KQ8, CHAIN>(sm, blockIdx.x, blockIdx.y, blockIdx.z, A);
+  if constexpr (CHAIN) chain_signal(A.chain);
 }
 
 // Chunk merge as a kernel of its own, for large batches: grid (KV head, row), one wave per query
@@ -1068,8 +1095,10 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
                               int ss_n, int H, const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
                               const float* rsin, const Rows& rows, int B, int max_ctx, uint16_t* kpool,
                               uint16_t* vpool, const KvQ8& kq8, float* part, int* counters, float out_scale, f16* ohi,
-                              f16* olo, int ldo, hipStream_t st) {
+                              f16* olo, int ldo, hipStream_t st, const Chain& chain, int* nwg) {
   if (nsplit < 1 || nsplit > 8 || B < 1 || B > kMaxBatch || max_ctx < 1) return hipErrorInvalidValue;
+  const bool ch = chain.cnt != nullptr;                   // chained: fused path, one projection range
+  if (ch && (B > 4 || nsplit != 1 || (chain.wait && !chain.err))) return hipErrorInvalidValue;
   // the grid covers the largest chunk count of any row: the count is not monotonic in the
   // context (the chunk length grows in steps), so a shorter row can need more chunks than the
   // longest one; workgroups past a row's own count exit early
@@ -1100,7 +1129,9 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
     return wl[x] != wl[y] ? wl[x] > wl[y] : rows.pos[x] > rows.pos[y];
   });
   const AttnArgs A{qkvp, nsplit, pstride, QKV, nq, ss, ss_n, H, wqn, wkn, eps, rcos, rsin, rows, order, cpw,
-                   kpool, vpool, kq8, part, counters, out_scale, ohi, olo, ldo};
+                   kpool, vpool, kq8, part, counters, out_scale, ohi, olo, ldo, chain};
+  const unsigned flags = chain.wait ? hipExtAnyOrderLaunch : 0u;
+  if (nwg) *nwg = (int)(grid.x * grid.y * grid.z);
 #define DEC_LAUNCH(GG, FU)                                                                                         \
   do {                                                                                                             \
     if (kq8.kq) {                                                                                                  \
@@ -1109,8 +1140,13 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
       DEC_LAUNCH_Q(GG, FU, false);                                                                                 \
     }                                                                                                              \
   } while (0)
-#define DEC_LAUNCH_Q(GG, FU, Q) \
-  hipLaunchKernelGGL((attn_decode_kernel<GG, FU, Q>), grid, dim3(64 * kDecodeWaves), 0, st, A)
+#define DEC_LAUNCH_Q(GG, FU, Q)                                                                               \
+  do {                                                                                                        \
+    if (FU && ch)                                                                                             \
+      GQA_LAUNCH_F((attn_decode_kernel<GG, FU, Q, FU>), grid, dim3(64 * kDecodeWaves), 0, st, flags, A);      \
+    else                                                                                                      \
+      hipLaunchKernelGGL((attn_decode_kernel<GG, FU, Q, false>), grid, dim3(64 * kDecodeWaves), 0, st, A);    \
+  } while (0)
   if (G != 4 && G != 2) return hipErrorInvalidValue;
   if (fused) {
     if (G == 4) DEC_LAUNCH(4, true);

@@ -34,7 +34,11 @@ constexpr int kFullMaxB = 4;
 constexpr int kUQkv = 3, kUGu = 3, kUOd = 6, kUQkvQ = 4, kUGuQ = 4, kUOdQ = 8, kULm = 8;
 constexpr int kFullMaxLds = 64 * 1024;   // operand rows (hi + lo) in LDS
 
-template <int QM, int NWB, int NBW, int U, int MODE, int EPI, int MAXB>
+// CH: membership of a decode chain (gqa_common.h). 0: none. 1: an any-order launch that waits
+// for its predecessors before reading the operand rows and reads them device-scope. 2: an
+// ordered launch (the queue has finished its predecessors), plain loads. 1 and 2 write what
+// later launches read device-scope and count themselves in at the end.
+template <int QM, int NWB, int NBW, int U, int MODE, int EPI, int MAXB, int CH>
 __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
   constexpr int NT = 64 * NWB * NBW;
   constexpr int S = NWB;
@@ -74,6 +78,8 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
   Buf b0, b1;
   fetch(b0, s0);
   fetch(b1, s0 + U);
+  const int n = band * 16 + g4 * 4;                   // epilogue: rows n .. n + 3 of token row r16
+  const bool yown = kp == 0 && r16 < B;
 
   // Q8_0 / AFFINE4: the scales (and biases) of the workgroup's bands, staged in LDS once, in their
   // memory order [band][K-step][16 rows] after the operand rows, so the weight stream issues one
@@ -89,6 +95,17 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
       if (QM == WM_A4) *(uint4*)(sbs + bb * KS * 16 + c * 8) = *(const uint4*)(a.Wb + src);
     }
   }
+  if constexpr (CH == 1) chain_wait(a.chain);
+  // EPI_ADD: the residual rows this lane updates, loaded now rather than after the stream (this
+  // workgroup is the only writer of its band)
+  float4 yold = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (EPI == EPI_ADD && yown) {
+    const float* src = a.y + (int64_t)r16 * a.ldy + n;
+    if constexpr (CH == 1)
+      yold = __builtin_bit_cast(float4, ld_dev16(src));
+    else
+      yold = *(const float4*)src;
+  }
 
   // ---- operand rows into LDS: [0][b][k] = hi, [1][b][k] = lo
   const int BK = B * K;
@@ -100,7 +117,11 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
     for (int i = 0; i < CMAX; ++i) {
       const int c = min(tid + i * NT, npiece - 1);
       const int hl = c >= BK / 8, rem = c - hl * (BK / 8), b = rem / (K / 8), q = rem - b * (K / 8);
-      v[i] = *(const uint4*)((hl ? a.xlo : a.xhi) + (int64_t)b * a.ldx + q * 8);
+      const f16* src = (hl ? a.xlo : a.xhi) + (int64_t)b * a.ldx + q * 8;
+      if constexpr (CH == 1)
+        v[i] = ld_dev16(src);
+      else
+        v[i] = *(const uint4*)src;
     }
 #pragma unroll
     for (int i = 0; i < CMAX; ++i) *(uint4*)(sx + (int64_t)min(tid + i * NT, npiece) * 8) = v[i];
@@ -119,7 +140,13 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
         const int r = p * G + g, off = min(t + 256 * j, klen - 1);
         wv[p][j] = bf16_bits_to_f32(a.nw[r * klen + off]);
 #pragma unroll
-        for (int b = 0; b < MAXB; ++b) xv[b][p][j] = a.xres[(int64_t)min(b, B - 1) * K + r * klen + off];
+        for (int b = 0; b < MAXB; ++b) {
+          const float* src = a.xres + (int64_t)min(b, B - 1) * K + r * klen + off;
+          if constexpr (CH == 1)
+            xv[b][p][j] = ld_dev(src);
+          else
+            xv[b][p][j] = *src;
+        }
       }
 #pragma unroll
     for (int b = 0; b < MAXB; ++b) {
@@ -152,7 +179,12 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
       float tot = 0.f;
       for (int r = 0; r < S && b < B; ++r) {
         const float sr = __fadd_rn(__fadd_rn(__fadd_rn(sred[b][r][0], sred[b][r][1]), sred[b][r][2]), sred[b][r][3]);
-        if (blockIdx.x == 0 && a.ss_out) a.ss_out[r * 32 + b] = sr;
+        if (blockIdx.x == 0 && a.ss_out) {
+          if constexpr (CH != 0)
+            st_dev(a.ss_out + r * 32 + b, sr);
+          else
+            a.ss_out[r * 32 + b] = sr;
+        }
         tot += sr;
       }
       sinv[b] = 1.0f / sqrtf(tot / (float)K + a.eps);
@@ -212,7 +244,10 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
   // acc[r] of lane (r16, g4) = row 16 band + 4 g4 + r of token row r16
   if constexpr (EPI == EPI_SWIGLU) {
     static_assert(NBW == 2, "gate and up bands");
-    if (wave != 0) return;
+    if (wave != 0) {
+      if constexpr (CH != 0) chain_signal(a.chain);
+      return;
+    }
     f32x4 gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NWB; ++w) {
@@ -236,12 +271,23 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
         hv[r] = h;
         lv[r] = l;
       }
-      *(f16x4*)(a.mhi + (int64_t)r16 * a.ldm + f) = hv;
-      *(f16x4*)(a.mlo + (int64_t)r16 * a.ldm + f) = lv;
+      f16* dh = a.mhi + (int64_t)r16 * a.ldm + f;
+      f16* dl = a.mlo + (int64_t)r16 * a.ldm + f;
+      if constexpr (CH != 0) {
+        st_dev8(dh, __builtin_bit_cast(uint64_t, hv));
+        st_dev8(dl, __builtin_bit_cast(uint64_t, lv));
+      } else {
+        *(f16x4*)dh = hv;
+        *(f16x4*)dl = lv;
+      }
     }
+    if constexpr (CH != 0) chain_signal(a.chain);
     return;
   }
-  if (kp != 0) return;
+  if (kp != 0) {
+    if constexpr (CH != 0) chain_signal(a.chain);
+    return;
+  }
   f32x4 tsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int w = 0; w < NWB; ++w) {
@@ -249,16 +295,18 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) tsum[r] += o[r];
   }
-  const int n = band * 16 + g4 * 4;
   if (r16 < B) {
     float* dst = a.y + (int64_t)r16 * a.ldy + n;
-    if (EPI == EPI_ADD) {
-      const float4 o = *(const float4*)dst;
-      *(float4*)dst = make_float4(__fadd_rn(o.x, __fmul_rn(tsum[0], a.yscale)), __fadd_rn(o.y, __fmul_rn(tsum[1], a.yscale)),
-                                  __fadd_rn(o.z, __fmul_rn(tsum[2], a.yscale)), __fadd_rn(o.w, __fmul_rn(tsum[3], a.yscale)));
-    } else {
-      *(float4*)dst = make_float4(tsum[0], tsum[1], tsum[2], tsum[3]);
-    }
+    const float4 o = yold;
+    const float4 out =
+        EPI == EPI_ADD
+            ? make_float4(__fadd_rn(o.x, __fmul_rn(tsum[0], a.yscale)), __fadd_rn(o.y, __fmul_rn(tsum[1], a.yscale)),
+                          __fadd_rn(o.z, __fmul_rn(tsum[2], a.yscale)), __fadd_rn(o.w, __fmul_rn(tsum[3], a.yscale)))
+            : make_float4(tsum[0], tsum[1], tsum[2], tsum[3]);
+    if constexpr (CH != 0)
+      st_dev16(dst, __builtin_bit_cast(uint4, out));
+    else
+      *(float4*)dst = out;
   }
   if (EPI == EPI_STORE && a.cand) {
     // argmax candidate of the band's 16 rows for token row r16: (value, index), lowest index on ties
@@ -281,6 +329,7 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
     }
     if (g4 == 0 && r16 < B) a.cand[(int64_t)r16 * (a.N / 16) + band] = make_float2(bv, __int_as_float(bi));
   }
+  if constexpr (CH != 0) chain_signal(a.chain);
 }
 
 // Whether the whole-K path can take B rows of a K-wide operand.
@@ -288,20 +337,46 @@ bool gemv_full_fits(int K, int B) { return B >= 1 && B <= kFullMaxB && (size_t)4
 
 // S = waves per band = K ranges; EPI_SWIGLU takes band pairs (gate, up). Requires
 // K % (32 * S) == 0, N % (16 * bands per workgroup) == 0, and for XF_NORM K <= 4096.
-hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStream_t st) {
+// A launch of a decode chain (a.chain.cnt set) runs the CH kernels, any-order when it waits;
+// *nwg (if not null) receives the number of workgroups launched.
+hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStream_t st, int* nwg) {
   if (!gemv_full_fits(a.K, a.B) || a.K % (32 * S) != 0 || a.N % 16 != 0) return hipErrorInvalidValue;
   if (mode == XF_NORM && (a.K > 4096 || !a.xres || !a.nw)) return hipErrorInvalidValue;
+  const int chm = !a.chain.cnt ? 0 : a.chain.wait ? 1 : 2;
+  if (chm && (a.cand || (a.chain.wait && !a.chain.err))) return hipErrorInvalidValue;
   const int qm = a.Wb ? WM_A4 : a.Wq ? WM_Q8 : WM_BF16;
   const size_t shm = (size_t)4 * a.B * a.K + 16;
+  const unsigned flags = a.chain.wait ? hipExtAnyOrderLaunch : 0u;
+#define FULL_CH(Q, NWB, NBW, U, MO, EP, MB)                                                                   \
+  do {                                                                                                        \
+    if (chm == 1)                                                                                             \
+      GQA_LAUNCH_F((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, MB, 1>), dim3(a.N / 16 / NBW),                   \
+                   dim3(64 * NWB * NBW), shm_, st, flags, a);                                                  \
+    else if (chm == 2)                                                                                        \
+      GQA_LAUNCH((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, MB, 2>), dim3(a.N / 16 / NBW),                     \
+                 dim3(64 * NWB * NBW), shm_, st, a);                                                           \
+    else                                                                                                      \
+      GQA_LAUNCH((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, MB, 0>), dim3(a.N / 16 / NBW),                     \
+                 dim3(64 * NWB * NBW), shm_, st, a);                                                           \
+  } while (0)
 #define FULL(Q, NWB, NBW, U, MO, EP)                                                                          \
   do {                                                                                                        \
     const size_t shm_ = shm + (Q == WM_BF16 ? 0 : (size_t)NBW * (a.K / 32) * 32 * (Q == WM_A4 ? 2 : 1));    \
+    if (nwg) *nwg = a.N / 16 / NBW;                                                                           \
     if (a.B == 1 && (size_t)4 * a.K + 16 <= kFullMaxLds / 4)                                                  \
-      GQA_LAUNCH((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, 1>), dim3(a.N / 16 / NBW),                         \
-                 dim3(64 * NWB * NBW), shm_, st, a);                                                           \
+      FULL_CH(Q, NWB, NBW, U, MO, EP, 1);                                                                     \
     else                                                                                                      \
-      GQA_LAUNCH((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, kFullMaxB>), dim3(a.N / 16 / NBW),                 \
-                 dim3(64 * NWB * NBW), shm_, st, a);                                                           \
+      FULL_CH(Q, NWB, NBW, U, MO, EP, kFullMaxB);                                                             \
+  } while (0)
+#define FULL_NC(NWB, NBW)                                                                                     \
+  do {                                                                                                        \
+    if (nwg) *nwg = a.N / 16 / NBW;                                                                           \
+    if (a.B == 1 && (size_t)4 * a.K + 16 <= kFullMaxLds / 4)                                                  \
+      GQA_LAUNCH((gemv_full_kernel<WM_BF16, NWB, NBW, kULm, XF_RAW, EPI_STORE, 1, 0>), dim3(a.N / 16 / NBW), \
+                 dim3(64 * NWB * NBW), shm, st, a);                                                            \
+    else                                                                                                      \
+      GQA_LAUNCH((gemv_full_kernel<WM_BF16, NWB, NBW, kULm, XF_RAW, EPI_STORE, kFullMaxB, 0>),            \
+                 dim3(a.N / 16 / NBW), dim3(64 * NWB * NBW), shm, st, a);                                      \
   } while (0)
 #define BY_QM(NWB, NBW, UB, UQ, MO, EP)    \
   do {                                     \
@@ -326,15 +401,18 @@ hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStre
     }
   } else if (S == 1) {
     if (mode != XF_RAW || epi != EPI_STORE || qm != WM_BF16) return hipErrorInvalidValue;
+    if (chm) return hipErrorInvalidValue;                // the lm_head is not part of a chain
     if (a.N % 64 == 0)
-      FULL(WM_BF16, 1, 4, kULm, XF_RAW, EPI_STORE);
+      FULL_NC(1, 4);
     else
-      FULL(WM_BF16, 1, 1, kULm, XF_RAW, EPI_STORE);
+      FULL_NC(1, 1);
   } else {
     return hipErrorInvalidValue;
   }
 #undef BY_QM
 #undef FULL
+#undef FULL_CH
+#undef FULL_NC
   return hipGetLastError();
 }
 

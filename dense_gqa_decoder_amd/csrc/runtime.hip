@@ -57,7 +57,7 @@ hipError_t launch_gemv(const uint16_t* W, const int8_t* Wq, const f16* Wd, const
                        bool staged = false);
 hipError_t launch_rows(const XSrc& xs, int K, int nsplit, int B, f16* yhi, f16* ylo, int ldy, hipStream_t st);
 bool gemv_full_fits(int K, int B);
-hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStream_t st);
+hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStream_t st, int* nwg = nullptr);
 hipError_t launch_final_norm(const XSrc& xs, int B, f16* yhi, f16* ylo, int ldy, hipStream_t st);
 hipError_t launch_attn_prefill(const float* q, int nq, int T, int pos0, const int32_t* table, const uint16_t* kpool,
                                const uint16_t* vpool, const KvQ8& kq8, float out_scale, f16* ohi, f16* olo, int ldo,
@@ -66,13 +66,19 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
                               int ss_n, int H, const uint16_t* wqn, const uint16_t* wkn, float eps, const float* rcos,
                               const float* rsin, const Rows& rows, int B, int max_ctx, uint16_t* kpool,
                               uint16_t* vpool, const KvQ8& kq8, float* part, int* counters, float out_scale, f16* ohi,
-                              f16* olo,
-                              int ldo, hipStream_t st);
+                              f16* olo, int ldo, hipStream_t st, const Chain& chain = Chain{}, int* nwg = nullptr);
 int64_t attn_decode_part_floats(int nq);
 }  // namespace gqa
 
 namespace gqa {
 thread_local LaunchEvents g_launch_events;
+
+// The whole-K decode path's per-layer launches go out as one chain of any-order launches
+// (gqa_common.h); 0 launches them as ordinary dependent launches (same kernels, same results).
+#ifndef GQA_DECODE_CHAIN
+#define GQA_DECODE_CHAIN 1
+#endif
+constexpr bool kDecodeChain = GQA_DECODE_CHAIN != 0;
 }
 
 using namespace gqa;
@@ -142,6 +148,7 @@ struct gqa_model {
         *apart = nullptr;
   float* ppart = nullptr;       // prefill: K-range partials of the o and down projections [<= 4 R][H]
   int32_t* counters = nullptr;  // decode attention: finished chunks per (row, KV head)
+  int32_t* chain = nullptr;     // decode: arrival counters of the chained launches (kChainInts)
   float* ss = nullptr;          // decode: sum-of-squares partials [2][8][32] (q|k|v input, gate|up input)
   float2* cand = nullptr;   // lm_head argmax candidates [32][vocab / 16]
   float* slog = nullptr;    // logits of up to kScoreRows rows being scored [kScoreRows][vocab]
@@ -233,12 +240,14 @@ uint64_t tensor_key(uint64_t seed, int L, int kind, int layer) {
 
 // Per-call scratch of a decode: the residual stream (two buffers for the split-K path), the
 // projection outputs or split partials, the operand rows, the attention chunk partials and
-// arrival counters, the sum-of-squares partials and the argmax candidates. The model's own
-// buffers by default; gqa_session_eval_decode_static carves them from a static device array.
-// `zero` (nzero ints, or null) is cleared by the first kernel of the call.
+// arrival counters, the sum-of-squares partials, the argmax candidates and the arrival counters
+// of the chained launches. The model's own buffers by default; gqa_session_eval_decode_static
+// carves them from a static device array. `zero` (nzero ints, or null) is cleared by the first
+// kernel of the call.
 struct DecodeScratch {
   float *x = nullptr, *x2 = nullptr, *part = nullptr, *part2 = nullptr, *ss = nullptr, *apart = nullptr;
   int32_t* counters = nullptr;
+  int32_t* chain = nullptr;
   f16 *oh = nullptr, *ol = nullptr, *mh = nullptr, *ml = nullptr, *xh = nullptr, *xl = nullptr;
   float2* cand = nullptr;
   int64_t pstride = 0;     // stride of split-K partial ranges (floats)
@@ -255,6 +264,9 @@ DecodeScratch model_scratch(gqa_model* m) {
   sc.ss = m->ss;
   sc.apart = m->apart;
   sc.counters = m->counters;
+  sc.chain = m->chain;
+  sc.zero = m->chain;
+  sc.nzero = kChainInts;
   sc.oh = m->oh;
   sc.ol = m->ol;
   sc.mh = m->mh;
@@ -295,7 +307,7 @@ int static_scratch_base(int dev, void** out) {
 // Lay one row's decode scratch out from `base` (256-byte aligned pieces) and return the bytes
 // it spans; with base == nullptr only the size is computed. Whole-K matvec path only (no split
 // partials, no second residual buffer); the attention partials of row 0 and its eight arrival
-// counters, which the call's embedding launch clears.
+// counters, then the chain's arrival counters, which the call's embedding launch clears.
 size_t carve_static_scratch(const gqa_model* m, void* base, DecodeScratch* sc) {
   const gqa_model_desc& d = m->d;
   size_t off = 0;
@@ -309,7 +321,8 @@ size_t carve_static_scratch(const gqa_model* m, void* base, DecodeScratch* sc) {
   sc->part = (float*)take(4 * (size_t)m->QKV);
   sc->ss = (float*)take(4 * 2 * 8 * 32);
   sc->apart = (float*)take(4 * (size_t)(attn_decode_part_floats(d.n_q_heads) / kMaxBatch));
-  sc->counters = (int32_t*)take(4 * kKvHeads);
+  sc->counters = (int32_t*)take(4 * kKvHeads);       // 256 bytes, then the chain counters
+  sc->chain = (int32_t*)take(4 * kChainInts);
   sc->oh = (f16*)take(2 * (size_t)m->QD);
   sc->ol = (f16*)take(2 * (size_t)m->QD);
   sc->mh = (f16*)take(2 * (size_t)d.ffn);
@@ -319,7 +332,7 @@ size_t carve_static_scratch(const gqa_model* m, void* base, DecodeScratch* sc) {
   sc->cand = (float2*)take(sizeof(float2) * (size_t)(d.vocab / 16));
   sc->pstride = m->QKV;
   sc->zero = sc->counters;
-  sc->nzero = kKvHeads;
+  sc->nzero = 64 + kChainInts;
   return off;
 }
 
@@ -483,6 +496,7 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   ALLOC(m->apart, attn_decode_part_floats(NQ), sb);
   ALLOC(m->ppart, (int64_t)4 * m->R * H, sb);
   ALLOC(m->counters, kMaxBatch * kKvHeads, sb);
+  ALLOC(m->chain, kChainInts, sb);
   ALLOC(m->ss, 2 * 8 * 32, sb);
   ALLOC(m->ids_dev, std::max(d.max_positions, kMaxBatch), sb);
   ALLOC(m->cand, (int64_t)kMaxBatch * (V / 16), sb);
@@ -582,6 +596,7 @@ int gqa_model_create(const gqa_model_desc* desc, uint64_t seed, gqa_model** out)
   }
   chk(hipMemsetAsync(m->err, 0, 4, st));
   chk(hipMemsetAsync(m->counters, 0, sizeof(int32_t) * kMaxBatch * kKvHeads, st));
+  chk(hipMemsetAsync(m->chain, 0, sizeof(int32_t) * kChainInts, st));
   chk(hipDeviceSynchronize());
   if (tmp) (void)hipFree(tmp);
   if (ge != hipSuccess) {
@@ -919,30 +934,50 @@ int run_decode(gqa_model* m, const DecodeScratch& sc, const Rows& rows, int B, i
       a.eps = eps;
       return a;
     };
+    // The layers' launches form one chain (any-order launches that order themselves through
+    // arrival counters, cleared by the embedding launch above); the final norm after it is an
+    // ordinary launch, which the queue holds until every launch before it has finished. While
+    // the decode gate/up matvec is being timed the chain is off: a chained launch starts before
+    // its predecessor ends and waits, so its events would not bracket its own execution.
+    ChainTrack ct;
+    if (kDecodeChain && m->prof_cls != GQA_PROF_DECODE_GATEUP) {
+      ct.cnt = sc.chain;
+      ct.err = m->err;
+    }
+    int nwg = 0;
     for (int l = 0; l < d.n_layers; ++l) {
       const LayerW& w = m->L[l];
       FullArgs q = fa();
       q.W = w.wqkv; q.Wq = w.qqkv; q.Wd = w.sqkv; q.Wb = w.bqkv; q.K = H; q.N = QKV;
       q.xres = xa; q.nw = w.attn_norm; q.ss_out = ss_qkv; q.y = P0; q.ldy = QKV;
-      LAUNCH(launch_gemv_full(XF_NORM, EPI_STORE, m->s_qkv, q, st));
+      q.chain = ct.next();
+      LAUNCH(launch_gemv_full(XF_NORM, EPI_STORE, m->s_qkv, q, st, &nwg));
+      ct.launched(nwg);
       LAUNCH(launch_attn_decode(P0, 1, pstride, QKV, NQ, ss_qkv, m->s_qkv, H, w.q_norm, w.k_norm, eps, m->rcos,
                                 m->rsin, rows, B, max_ctx, kv_k(w), kv_v(w), w.kq8, sc.apart, sc.counters, kAttnOutScale,
-                                sc.oh, sc.ol, QD, st));
+                                sc.oh, sc.ol, QD, st, ct.next(), &nwg));
+      ct.launched(nwg);
       FullArgs o = fa();
       o.W = w.wo; o.Wq = w.qo; o.Wd = w.so; o.Wb = w.bo; o.K = QD; o.N = H;
       o.xhi = sc.oh; o.xlo = sc.ol; o.ldx = QD; o.y = xa; o.ldy = H; o.yscale = 1.f / kAttnOutScale;
-      LAUNCH(launch_gemv_full(XF_RAW, EPI_ADD, m->s_o, o, st));
+      o.chain = ct.next();
+      LAUNCH(launch_gemv_full(XF_RAW, EPI_ADD, m->s_o, o, st, &nwg));
+      ct.launched(nwg);
       FullArgs g = fa();
       g.W = w.wgu; g.Wq = w.qgu; g.Wd = w.sgu; g.Wb = w.bgu; g.K = H; g.N = 2 * F;
       g.xres = xa; g.nw = w.ffn_norm; g.ss_out = ss_gu; g.mhi = sc.mh; g.mlo = sc.ml; g.ldm = F;
+      g.chain = ct.next();
       {
         ProfScope ps(m, GQA_PROF_DECODE_GATEUP, st);
-        LAUNCH(launch_gemv_full(XF_NORM, EPI_SWIGLU, m->s_gu, g, st));
+        LAUNCH(launch_gemv_full(XF_NORM, EPI_SWIGLU, m->s_gu, g, st, &nwg));
       }
+      ct.launched(nwg);
       FullArgs dn = fa();
       dn.W = w.wd; dn.Wq = w.qd; dn.Wd = w.sd; dn.Wb = w.bd; dn.K = F; dn.N = H;
       dn.xhi = sc.mh; dn.xlo = sc.ml; dn.ldx = F; dn.y = xa; dn.ldy = H; dn.yscale = 1.f;
-      LAUNCH(launch_gemv_full(XF_RAW, EPI_ADD, m->s_d, dn, st));
+      dn.chain = ct.next();
+      LAUNCH(launch_gemv_full(XF_RAW, EPI_ADD, m->s_d, dn, st, &nwg));
+      ct.launched(nwg);
     }
     LAUNCH(launch_final_norm(resid_src(xa, nullptr, nullptr, 0, 1.f, m->final_norm, nullptr), B, sc.xh, sc.xl, H,
                              st));
@@ -1375,6 +1410,8 @@ int gqa_model_check_device_error(gqa_model* m, hipStream_t st) {
   HIP_TRY(hipMemcpy(&v, m->err, 4, hipMemcpyDeviceToHost));
   if (v) {
     HIP_TRY(hipMemset(m->err, 0, 4));
+    if (v & kErrChainWait)
+      return fail(GQA_E_HIP, "a chained decode launch gave up waiting for its predecessor (results invalid)");
     return fail(GQA_E_RANGE, "a device-resident token id was outside [0, %d)", m->d.vocab);
   }
   return GQA_OK;

@@ -264,7 +264,10 @@ int gqa_session_eval_decode_static(gqa_session* session, const int32_t* id, int3
                                    int32_t* argmax, hipStream_t stream);
 
 /* Synchronise `stream`, then return GQA_E_RANGE (and clear the flag) if a device-resident
- * token id was out of range since the last check, else GQA_OK. */
+ * token id was out of range since the last check; GQA_E_HIP (and clear it) if a decode
+ * launch gave up waiting for the launch before it (the decode of at most four rows orders its
+ * per-layer launches through device counters with a bounded wait; the results of that call
+ * are invalid); else GQA_OK. */
 int gqa_model_check_device_error(gqa_model* model, hipStream_t stream);
 
 /* Kernel timing with HIP events on the caller's stream, for roofline reports: while a class is
@@ -272,7 +275,10 @@ int gqa_model_check_device_error(gqa_model* model, hipStream_t stream);
  * gqa_model_profile(model, cls) starts a new recording (cls = GQA_PROF_NONE stops);
  * gqa_model_profile_read synchronises the device and returns the launch count and the summed
  * event time in milliseconds of the current recording. At most 65,536 launches are recorded;
- * later ones are counted in *dropped. */
+ * later ones are counted in *dropped. While GQA_PROF_DECODE_GATEUP is selected, decode calls
+ * issue their per-layer launches as ordinary dependent launches (not the any-order chain they
+ * use otherwise, whose launches start early and wait), so each event pair brackets the
+ * kernel's own execution; the results are the same bits. */
 #define GQA_PROF_NONE 0
 #define GQA_PROF_DECODE_GATEUP 1   /* decode gate/up matvec with SwiGLU (HBM bound) */
 #define GQA_PROF_PREFILL_GATEUP 2  /* prefill gate/up GEMM with SwiGLU (matrix-core bound) */
