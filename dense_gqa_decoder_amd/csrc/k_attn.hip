@@ -763,8 +763,11 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = f32_to_bf16_rne(src[e]);
     const int64_t off = (int64_t)table[pos >> 5] * kBlockElems + ((int64_t)kvh * kBlock + (pos & 31)) * kHeadDim + d0;
-    *(uint4*)((kv ? vpool : kpool) + off) =
-        uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    const uint4 row8 = uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    if constexpr (CHAIN)                                  // no dirty L2 lines from a chained launch
+      st_dev16((kv ? vpool : kpool) + off, row8);
+    else
+      *(uint4*)((kv ? vpool : kpool) + off) = row8;
   }
   // 3. attention over the chunk on the matrix cores; wave w takes keys 16 w .. 16 w + 15 of every
   //    64-position step and keeps its own online-softmax state per head.

@@ -33,6 +33,15 @@ constexpr int kFullMaxB = 4;
 // faster than 4 and 8, which the quantised formats keep (their smaller steps gain from depth).
 constexpr int kUQkv = 3, kUGu = 3, kUOd = 6, kUQkvQ = 4, kUGuQ = 4, kUOdQ = 8, kULm = 8;
 constexpr int kFullMaxLds = 64 * 1024;   // operand rows (hi + lo) in LDS
+// Gate/up of BF16 weights as mixed bands: workgroup m takes rows 8 (m % 2) .. + 7 of the gate
+// band 2 (m / 2) and of the up band after it (the same eight features) as the 16 rows of its
+// matrix-core tiles, so the SwiGLU pairs meet in one wave and the grid has one workgroup per
+// eight features (1,216 of four waves for the 4B shape, 4.75 per CU) instead of one per sixteen
+// (608 of eight waves: two or three per CU, and the CUs with three set the kernel's end).
+constexpr int EPI_SWIGLU_MIX = 3;
+#ifndef GQA_GATEUP_MIXED
+#define GQA_GATEUP_MIXED 1
+#endif
 
 // CH: membership of a decode chain (gqa_common.h). 0: none. 1: an any-order launch that waits
 // for its predecessors before reading the operand rows and reads them device-scope. 2: an
@@ -53,8 +62,16 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
   const int s0 = kp * (KS / S), s1 = s0 + KS / S;
   const int r16 = lane & 15, g4 = lane >> 4;
 
-  // weight stream of this wave: band `band`, K-steps [s0, s1)
-  const int64_t chunk0 = (int64_t)band * KS;
+  // weight stream of this wave: band `band`, K-steps [s0, s1); lane l loads tile row l % 16,
+  // K-elements 8 (l / 16) .. + 7 (the tile-major layout), or for a mixed band that row of the
+  // gate (l % 16 < 8) or up band
+  static_assert(EPI != EPI_SWIGLU_MIX || (QM == WM_BF16 && NBW == 1), "mixed bands: BF16, one per workgroup");
+  int64_t chunk0 = (int64_t)band * KS;
+  int loff = lane * 8;
+  if constexpr (EPI == EPI_SWIGLU_MIX) {
+    chunk0 = (int64_t)(2 * (blockIdx.x >> 1) + (r16 >> 3)) * KS;
+    loff = 8 * (16 * g4 + 8 * (blockIdx.x & 1) + (r16 & 7));
+  }
   struct Buf {
     uint4 w[U];
     uint2 q[U];
@@ -71,7 +88,7 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
       } else if (QM == WM_A4) {
         f.q4[u] = *(const uint32_t*)(a.Wq + ch * 256 + lane * 4);
       } else {
-        f.w[u] = *(const uint4*)(a.W + ch * 512 + lane * 8);
+        f.w[u] = *(const uint4*)(a.W + ch * 512 + loff);
       }
     }
   };
@@ -242,6 +259,49 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
   red[bw][kp][lane] = acc;
   __syncthreads();
   // acc[r] of lane (r16, g4) = row 16 band + 4 g4 + r of token row r16
+  if constexpr (EPI == EPI_SWIGLU_MIX) {
+    // lanes g4 = 0, 1 hold gate rows 4 g4 + r (features 16 (m / 2) + 8 (m % 2) + 4 g4 + r), lanes
+    // g4 + 2 the up rows of the same features
+    if (wave != 0) {
+      if constexpr (CH != 0) chain_signal(a.chain);
+      return;
+    }
+    f32x4 tsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NWB; ++w) {
+      const f32x4 o = red[0][w][lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tsum[r] += o[r];
+    }
+    float us[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) us[r] = __shfl_xor(tsum[r], 32, 64);
+    if (g4 < 2 && r16 < B) {
+      const float c = sinv[r16];
+      const int f = (blockIdx.x >> 1) * 16 + (blockIdx.x & 1) * 8 + g4 * 4;
+      f16x4 hv, lv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gg = __fmul_rn(tsum[r], c), uu = __fmul_rn(us[r], c);
+        const float m = __fmul_rn(__fdiv_rn(gg, 1.0f + expf(-gg)), uu);
+        f16 h, l;
+        split_f16(m, h, l);
+        hv[r] = h;
+        lv[r] = l;
+      }
+      f16* dh = a.mhi + (int64_t)r16 * a.ldm + f;
+      f16* dl = a.mlo + (int64_t)r16 * a.ldm + f;
+      if constexpr (CH != 0) {
+        st_dev8(dh, __builtin_bit_cast(uint64_t, hv));
+        st_dev8(dl, __builtin_bit_cast(uint64_t, lv));
+      } else {
+        *(f16x4*)dh = hv;
+        *(f16x4*)dl = lv;
+      }
+    }
+    if constexpr (CH != 0) chain_signal(a.chain);
+    return;
+  }
   if constexpr (EPI == EPI_SWIGLU) {
     static_assert(NBW == 2, "gate and up bands");
     if (wave != 0) {
@@ -389,7 +449,10 @@ hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStre
   } while (0)
   if (epi == EPI_SWIGLU) {
     if (mode != XF_NORM || S != 4 || a.N % 32 != 0) return hipErrorInvalidValue;
-    BY_QM(4, 2, kUGu, kUGuQ, XF_NORM, EPI_SWIGLU);
+    if (qm == WM_BF16 && GQA_GATEUP_MIXED)
+      FULL(WM_BF16, 4, 1, kUGu, XF_NORM, EPI_SWIGLU_MIX);
+    else
+      BY_QM(4, 2, kUGu, kUGuQ, XF_NORM, EPI_SWIGLU);
   } else if (S == 8) {
     if (mode == XF_NORM) {
       if (epi != EPI_STORE) return hipErrorInvalidValue;
