@@ -80,6 +80,7 @@ _SIGS = {
     "gqa_session_eval_decode_static": (I32, [P, P, I32, P, P, P]),
     "gqa_model_check_device_error": (I32, [P, P]),
     "gqa_model_profile": (I32, [P, I32]),
+    "gqa_model_debug_chain_offset": (I32, [P, I32]),
     "gqa_model_profile_read": (I32, [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int64)]),
     "gqa_last_error": (ctypes.c_char_p, []),
@@ -225,6 +226,10 @@ def gqa_model_check_device_error(model, stream) -> None:
 
 
 GQA_PROF = {"none": 0, "decode_gateup": 1, "prefill_gateup": 2, "prefill_attn": 3, "decode_lmhead": 4, "rows_lmhead": 5}
+
+
+def gqa_model_debug_chain_offset(model, offset: int) -> None:
+    _check(lib().gqa_model_debug_chain_offset(model, offset))
 
 
 def gqa_model_profile(model, kernel_class: int) -> None:

@@ -107,6 +107,10 @@ class Model:
         L.gqa_debug_read_rope(self.handle, n, c.ctypes.data, s.ctypes.data)
         return c, s
 
+    def debug_chain_offset(self, offset: int):
+        """Test hook: make the decode chain's waits unsatisfiable (offset > 0) or normal (0)."""
+        L.gqa_model_debug_chain_offset(self.handle, offset)
+
     def profile(self, kernel_class: str):
         L.gqa_model_profile(self.handle, L.GQA_PROF[kernel_class])
 

@@ -184,6 +184,7 @@ struct ChainTrack {
   int32_t* err = nullptr;
   int32_t arrived[kChainLanes] = {};
   int launches = 0;
+  int32_t offset = 0;                     // added to every target (a test of the bounded wait)
   // Arguments of the next launch: the first one is an ordinary launch (the queue holds it until
   // the call's earlier, unchained work has finished) that only signals; the others go out
   // any-order and wait. (An ordinary launch in the middle of a chain would cost more than the
@@ -194,7 +195,7 @@ struct ChainTrack {
     c.cnt = cnt;
     c.err = err;
     c.wait = launches > 0;
-    for (int i = 0; i < kChainLanes; ++i) c.target[i] = arrived[i];
+    for (int i = 0; i < kChainLanes; ++i) c.target[i] = arrived[i] + offset;
     return c;
   }
   void launched(int nwg) {

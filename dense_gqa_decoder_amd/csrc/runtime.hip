@@ -166,6 +166,7 @@ struct gqa_model {
   int prof_cls = GQA_PROF_NONE;
   std::vector<hipEvent_t> prof_ev;
   int64_t prof_used = 0, prof_dropped = 0;
+  int32_t chain_offset = 0;     // gqa_model_debug_chain_offset
 };
 
 struct gqa_session {
@@ -943,6 +944,7 @@ int run_decode(gqa_model* m, const DecodeScratch& sc, const Rows& rows, int B, i
     if (kDecodeChain && m->prof_cls != GQA_PROF_DECODE_GATEUP) {
       ct.cnt = sc.chain;
       ct.err = m->err;
+      ct.offset = m->chain_offset;
     }
     int nwg = 0;
     for (int l = 0; l < d.n_layers; ++l) {
@@ -1385,6 +1387,13 @@ int gqa_model_profile(gqa_model* m, int32_t cls) {
   m->prof_cls = cls;
   m->prof_used = 0;
   m->prof_dropped = 0;
+  return GQA_OK;
+}
+
+int gqa_model_debug_chain_offset(gqa_model* m, int32_t offset) {
+  if (!m) return fail(GQA_E_INVALID, "null model");
+  if (offset < 0 || offset > (1 << 20)) return fail(GQA_E_INVALID, "chain offset %d outside [0, 2^20]", offset);
+  m->chain_offset = offset;
   return GQA_OK;
 }
 

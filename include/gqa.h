@@ -288,6 +288,15 @@ int gqa_model_check_device_error(gqa_model* model, hipStream_t stream);
 int gqa_model_profile(gqa_model* model, int32_t kernel_class);
 int gqa_model_profile_read(gqa_model* model, int64_t* launches, double* total_ms, int64_t* dropped);
 
+/* Test hook of the bounded wait in the decode chain (see gqa_model_check_device_error), not for
+ * production use. While `offset` > 0 every chained decode launch of this model waits for `offset`
+ * more arrivals per counter than any launch makes: the first waiting launch gives up after its
+ * bounded wait (about 2^16 polls) and sets the model's error word, the later ones give up at
+ * once, and the call completes with invalid results (the session's KV rows written by it are
+ * invalid too) while gqa_model_check_device_error reports GQA_E_HIP. 0 (the default) restores
+ * normal operation. GQA_E_INVALID for an offset outside [0, 2^20]. */
+int gqa_model_debug_chain_offset(gqa_model* model, int32_t offset);
+
 /* Message of the last failure on this thread ("" if none). Valid until the next call. */
 const char* gqa_last_error(void);
 
