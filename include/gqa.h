@@ -115,7 +115,9 @@ typedef struct {
   int64_t prefix_evictions;   /* cached blocks evicted to make room */
 } gqa_model_info;
 
-/* Create a model on the current HIP device with seeded synthetic weights.
+/* Create a model on the current HIP device with seeded synthetic weights (Kipp Model Support,
+ * "The registry": the dense Qwen3 decoders; the pages load checkpoints, this library generates
+ * random-init weights of the same shape).
  * Weights: the counter-based generator documented in the library source (SplitMix64 outputs
  * summed Irwin-Hall style, scaled to std 0.02, rounded to BF16), one key per tensor derived
  * from `seed`; norm weights are 1.0. For GQA_SCHEME_Q8_0 the seven projections are then
@@ -228,7 +230,9 @@ int gqa_session_eval_scored(gqa_session* session, const int32_t* ids, int32_t n,
  * next. */
 int gqa_session_truncate(gqa_session* session, int32_t pos);
 
-/* Evaluate one token at the session's position. `id` is a host pointer when id_on_device is
+/* Evaluate one token at the session's position: incremental decode over the session's KV cache
+ * (Kipp Model Support, "What the gates check": cached decode equal to recomputation without the
+ * cache, at every decode position). `id` is a host pointer when id_on_device is
  * 0 (validated: GQA_E_RANGE if outside [0, vocab)) or a device pointer when 1 (for greedy
  * loops without host round trips, e.g. the previous call's argmax buffer). A device id
  * outside [0, vocab) cannot be reported synchronously: its logits become NaN, argmax -1, and
@@ -237,7 +241,8 @@ int gqa_session_truncate(gqa_session* session, int32_t pos);
 int gqa_session_eval_decode(gqa_session* session, const int32_t* id, int32_t id_on_device, float* logits,
                             int32_t* argmax, hipStream_t stream);
 
-/* One token for each of B distinct sessions of the same model (1 <= B <= 32): row b of
+/* One token for each of B distinct sessions of the same model (1 <= B <= 32; Kipp Roadmap, status
+ * v0.0.2: batched evaluation, gated equal to isolated evaluation): row b of
  * `ids` (host or device per ids_on_device, as for eval_decode) is evaluated at sessions[b]'s
  * position. Writes logits [B][vocab] and argmax [B] (device). Row b is bit-identical to
  * gqa_session_eval_decode on sessions[b] alone. GQA_E_INVALID for duplicate sessions, mixed
