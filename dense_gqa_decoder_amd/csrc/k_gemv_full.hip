@@ -10,7 +10,8 @@
 // split-K path's consumers perform on its global partials -- so a row gives bit-identical
 // results on both paths (Kipp Roadmap, status v0.0.2: batched evaluation equals isolated).
 //
-// Operand prologues (the whole row is read by every workgroup; it is small and L2-resident):
+// Operand prologues (the whole row is read by every workgroup; it is small and L2-resident, or
+// for a launch of a decode chain read device-scope once the predecessors have counted in):
 //   XF_RAW  copy FP16 hi/lo rows from global memory.
 //   XF_NORM the RMSNorm input of a projection: x * w_norm, split hi/lo; the sum of squares of x
 //           per K range is formed with the split-K path's element-to-thread mapping and order
@@ -22,7 +23,9 @@
 //   EPI_STORE  y = sum (q|k|v, lm_head; optional argmax candidates per band)
 //   EPI_ADD    y = y + sum * yscale (residual stream update after o and down)
 //   EPI_SWIGLU bands 2j, 2j+1 are gate and up of features 16j..16j+15: m = silu(g c) * (u c),
-//              c = 1/rms of the layer input, written as FP16 hi/lo rows for the down projection.
+//              c = 1/rms of the layer input, written as FP16 hi/lo rows for the down projection
+//              (BF16 weights: as mixed bands, EPI_SWIGLU_MIX below, the same products).
+//   EPI_ADD loads its residual rows before the weight stream (its workgroup is their only writer).
 #include "gqa_common.h"
 
 namespace gqa {
