@@ -18,6 +18,9 @@ FLAGS = [
     # no implicit multiply-add contraction: every kernel rounds the same expression the same way
     # (explicit fmaf() where a fused multiply-add is intended)
     "-ffp-contract=off",
+    # leading scalar and pointer kernel arguments (up to 16) are preloaded into SGPRs by the
+    # dispatcher, so a wave's first loads need no kernel-argument load
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

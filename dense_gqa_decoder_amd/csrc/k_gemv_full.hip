@@ -50,8 +50,11 @@ constexpr int EPI_SWIGLU_MIX = 3;
 // for its predecessors before reading the operand rows and reads them device-scope. 2: an
 // ordered launch (the queue has finished its predecessors), plain loads. 1 and 2 write what
 // later launches read device-scope and count themselves in at the end.
+// wsrc (the weights: a.W, or a.Wq for the quantised formats) and kdim (a.K) lead the arguments so
+// that the dispatcher preloads them into scalar registers (-amdgpu-kernarg-preload-count): a
+// wave issues its first weight loads without waiting for a kernel-argument load.
 template <int QM, int NWB, int NBW, int U, int MODE, int EPI, int MAXB, int CH>
-__global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
+__global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(const void* __restrict__ wsrc, int kdim, FullArgs a) {
   constexpr int NT = 64 * NWB * NBW;
   constexpr int S = NWB;
   extern __shared__ f16 sx[];                         // [2][B][K] (+ one padding piece)
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bw = wave / NWB, kp = wave % NWB;
   const int band = blockIdx.x * NBW + bw;
-  const int K = a.K, B = a.B, KS = K >> 5;
+  const int K = kdim, B = a.B, KS = K >> 5;
   const int s0 = kp * (KS / S), s1 = s0 + KS / S;
   const int r16 = lane & 15, g4 = lane >> 4;
 
@@ -87,11 +90,11 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(FullArgs a) {
     for (int u = 0; u < U; ++u) {
       const int64_t ch = chunk0 + min(s + u, s1 - 1);     // unconditional: no branch between loads
       if (QM == WM_Q8) {
-        f.q[u] = *(const uint2*)(a.Wq + ch * 512 + lane * 8);
+        f.q[u] = *(const uint2*)((const int8_t*)wsrc + ch * 512 + lane * 8);
       } else if (QM == WM_A4) {
-        f.q4[u] = *(const uint32_t*)(a.Wq + ch * 256 + lane * 4);
+        f.q4[u] = *(const uint32_t*)((const int8_t*)wsrc + ch * 256 + lane * 4);
       } else {
-        f.w[u] = *(const uint4*)(a.W + ch * 512 + loff);
+        f.w[u] = *(const uint4*)((const uint16_t*)wsrc + ch * 512 + loff);
       }
     }
   };
@@ -410,17 +413,18 @@ hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStre
   const int qm = a.Wb ? WM_A4 : a.Wq ? WM_Q8 : WM_BF16;
   const size_t shm = (size_t)4 * a.B * a.K + 16;
   const unsigned flags = a.chain.wait ? hipExtAnyOrderLaunch : 0u;
+  const void* const wsrc_ = qm == WM_BF16 ? (const void*)a.W : (const void*)a.Wq;
 #define FULL_CH(Q, NWB, NBW, U, MO, EP, MB)                                                                   \
   do {                                                                                                        \
     if (chm == 1)                                                                                             \
       GQA_LAUNCH_F((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, MB, 1>), dim3(a.N / 16 / NBW),                   \
-                   dim3(64 * NWB * NBW), shm_, st, flags, a);                                                  \
+                   dim3(64 * NWB * NBW), shm_, st, flags, wsrc_, a.K, a);                                                  \
     else if (chm == 2)                                                                                        \
       GQA_LAUNCH((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, MB, 2>), dim3(a.N / 16 / NBW),                     \
-                 dim3(64 * NWB * NBW), shm_, st, a);                                                           \
+                 dim3(64 * NWB * NBW), shm_, st, wsrc_, a.K, a);                                                           \
     else                                                                                                      \
       GQA_LAUNCH((gemv_full_kernel<Q, NWB, NBW, U, MO, EP, MB, 0>), dim3(a.N / 16 / NBW),                     \
-                 dim3(64 * NWB * NBW), shm_, st, a);                                                           \
+                 dim3(64 * NWB * NBW), shm_, st, wsrc_, a.K, a);                                                           \
   } while (0)
 #define FULL(Q, NWB, NBW, U, MO, EP)                                                                          \
   do {                                                                                                        \
@@ -436,10 +440,10 @@ hipError_t launch_gemv_full(int mode, int epi, int S, const FullArgs& a, hipStre
     if (nwg) *nwg = a.N / 16 / NBW;                                                                           \
     if (a.B == 1 && (size_t)4 * a.K + 16 <= kFullMaxLds / 4)                                                  \
       GQA_LAUNCH((gemv_full_kernel<WM_BF16, NWB, NBW, kULm, XF_RAW, EPI_STORE, 1, 0>), dim3(a.N / 16 / NBW), \
-                 dim3(64 * NWB * NBW), shm, st, a);                                                            \
+                 dim3(64 * NWB * NBW), shm, st, wsrc_, a.K, a);                                                            \
     else                                                                                                      \
       GQA_LAUNCH((gemv_full_kernel<WM_BF16, NWB, NBW, kULm, XF_RAW, EPI_STORE, kFullMaxB, 0>),            \
-                 dim3(a.N / 16 / NBW), dim3(64 * NWB * NBW), shm, st, a);                                      \
+                 dim3(a.N / 16 / NBW), dim3(64 * NWB * NBW), shm, st, wsrc_, a.K, a);                                      \
   } while (0)
 #define BY_QM(NWB, NBW, UB, UQ, MO, EP)    \
   do {                                     \
