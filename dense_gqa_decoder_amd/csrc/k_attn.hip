@@ -545,13 +545,14 @@ struct RowOrder {
 static_assert(kMaxBatch <= 256, "row indices fit a byte");
 
 // Shared memory of one decode-attention workgroup.
-template <int G>
+template <int G, int NBUF>
 struct AttnSmem {
   float sraw[(G + 2) * kHeadDim];                         // projection sums (times 1/rms)
   float sq[(G + 2) * kHeadDim];                           // normed + rotated q (scaled), k; v
   float wm[kDecodeWaves][G], wl[kDecodeWaves][G];
   float wo[kDecodeWaves][G][kHeadDim];
-  __attribute__((aligned(16))) uint16_t vlds[kDecodeWaves][2][16 * kHeadDim];   // V planes, two steps
+  __attribute__((aligned(16))) uint16_t vlds[kDecodeWaves][NBUF][16 * kHeadDim];   // V planes, NBUF steps
+  int stab[64 * kDecodeWaves];                            // block-table entries of the workgroup's chunks
   int s_last;
 };
 
@@ -582,8 +583,20 @@ struct AttnArgs {
 // One workgroup of the decode attention: chunk group bx, KV head kvh, grid row slot zs.
 // CHAIN: a launch of a decode chain (gqa_common.h): issues its first K/V, waits for its
 // predecessors, reads the projection device-scope and writes the merged rows device-scope.
+// Steps in flight of a decode-attention workgroup: K/V of NBUF steps (registers and V planes)
+// are held at once, so while a step is computed the next NBUF - 1 are loading. Three for the
+// single workgroup per CU of a few-row decode (one wave per SIMD: latency is all there is to
+// hide), two for the row-batched launch (three workgroups per CU).
+#ifndef GQA_DECODE_BUFFERS_FUSED
+#define GQA_DECODE_BUFFERS_FUSED 3
+#endif
+constexpr int decode_buffers(bool fused) { return fused ? GQA_DECODE_BUFFERS_FUSED : 2; }
+
 template <int G, bool FUSED, bool KQ8, bool CHAIN>
-__device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kvh, int zs, const AttnArgs& A) {
+__device__ __forceinline__ void attn_decode_body(AttnSmem<G, decode_buffers(FUSED)>& sm, int bx, int kvh, int zs,
+                                                 const AttnArgs& A) {
+  constexpr int NBUF = decode_buffers(FUSED);
+  static_assert(NBUF == 2 || NBUF == 3, "two or three steps in flight");
   constexpr int NW = kDecodeWaves;                        // softmax states per workgroup (one per wave)
   constexpr int NE = (G + 2) * kHeadDim;                  // q heads, then k and v of the new position
   const float* __restrict__ qkvp = A.qkvp;
@@ -609,7 +622,7 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
   float (&wm)[NW][G] = sm.wm;
   float (&wl)[NW][G] = sm.wl;
   float (&wo)[NW][G][kHeadDim] = sm.wo;
-  uint16_t (&vlds)[NW][2][16 * kHeadDim] = sm.vlds;
+  uint16_t (&vlds)[NW][NBUF][16 * kHeadDim] = sm.vlds;
   int& s_last = sm.s_last;
   const int b = A.order.b[zs];
   const int pos = rows.pos[b], ctx = pos + 1;
@@ -633,7 +646,18 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
   //   K: lane l loads key l % 16, dims 32 s + 8 (l / 16) .. + 7 for s = 0..3 (the A operand rows).
   //   V: four 1 KiB direct-to-LDS copies into 16-dim planes (16 keys x 32 bytes each); copy j
   //      fills planes 2 j, 2 j + 1, lane l bringing key (l % 32) / 2, half l % 2 of the plane.
-  auto phys_of = [&](int cc, int it) { return table[min(cc * CH + it * kDecodeStep + wave * 16, p_end_of(cc) - 1) >> 5]; };
+  // The block-table entries of the workgroup's positions are staged in LDS (one per thread, loaded
+  // with the first K/V and stored before the barrier that publishes q), so a step's K/V loads do
+  // not wait for a table load; the first step reads the table directly, and so does every step
+  // of a workgroup that spans more blocks than it has threads.
+  const int blk0 = (c0 * CH) >> 5, nblk = ((min(c1 * CH, ctx) - 1) >> 5) - blk0 + 1;
+  const bool ltab = nblk <= 64 * kDecodeWaves;
+  const int tabv = ltab && tid < nblk ? table[blk0 + tid] : 0;
+  bool lready = false;                                     // set once stab is published
+  auto phys_of = [&](int cc, int it) {
+    const int bi = min(cc * CH + it * kDecodeStep + wave * 16, p_end_of(cc) - 1) >> 5;
+    return lready ? sm.stab[bi - blk0] : table[bi];
+  };
   //   Q8_0 cache: K as above but the codes (8 bytes per lane and 32-dim step) and the key's four
   //   block scales; V: lane l brings the 32 codes of key l / 4, dims 32 (l % 4) .. + 31, and their
   //   scale, widened into the same LDS planes when the step is computed.
@@ -658,7 +682,7 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
       }
     }
   };
-  DecStage kA, kB;
+  DecStage kA, kB, kC;                                   // kC: third buffer (NBUF == 3)
   // Issue order matters (vector loads complete in order): the block-table entry, the RoPE and
   // norm constants, the projection partials, then the first K/V, so q is built while the K/V
   // are in flight.
@@ -704,7 +728,9 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
       if (e < nel) sraw[e] = __fmul_rn(acc, cin);
     }
   }
+  if (ltab && tid < nblk) sm.stab[tid] = tabv;
   __syncthreads();
+  lready = ltab;
   // 2. per-head RMSNorm(128) and rotate-half RoPE at `pos`: wave w handles heads w, w + 4, ...;
   //    lane t owns dims t and t + 64 (a RoPE pair). q is pre-scaled by log2(e)/sqrt(128).
   {
@@ -951,10 +977,12 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
     if (cc + 1 < c1) __syncthreads();     // the wave-state arrays are reused by the next chunk
   };
 
-  // The workgroup's steps (chunk, 64-position step) in order, double-buffered (K in registers, V
-  // in two LDS buffers per wave) across chunk boundaries, so the next chunk's first copies are in
-  // flight during a chunk's merge; a step's copies and loads have landed once at most the next
-  // step's eight are in flight. (lc, lit): next step to issue; (cc, cit): next step to compute.
+  // The workgroup's steps (chunk, 64-position step) in order through a ring of NBUF buffers (K in
+  // registers, V planes in LDS per wave) across chunk boundaries, so the next chunk's first
+  // copies are in flight during a chunk's merge. Before a step is computed the step NBUF - 1
+  // ahead is issued into the buffer the previous step used; the step's own copies and loads
+  // have landed once at most the eight of each later issued step are in flight. (lc, lit): next
+  // step to issue; (cc, cit): next step to compute; `ahead`: issued steps not yet computed.
   int lc = c0, lit = 0, cc = c0, cit = 0;
   auto advance = [&](int& ch, int& it) {
     if (++it >= niter_of(ch)) {
@@ -963,32 +991,51 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
     }
   };
   advance(lc, lit);                                      // step (c0, 0) was issued into kA, buffer 0
+  int ahead = 1;
+  if constexpr (NBUF == 3) {
+    if (lc < c1) {                                       // step 2 of the ring, into kB
+      issue(phys_of(lc, lit), kB, 1);
+      advance(lc, lit);
+      ahead = 2;
+    }
+  }
   auto run = [&](DecStage& sg, int buf) {
     compute(cc, cit, sg, buf);
     if (cit + 1 == niter_of(cc)) finish(cc);
     advance(cc, cit);
   };
-  while (true) {
-    const bool more = lc < c1;
-    if (more) {
-      issue(phys_of(lc, lit), kB, 1);
+  // compute the step in (cur, cb) after issuing the next one into (fre, fb)
+  auto one = [&](DecStage& cur, int cb, DecStage& fre, int fb) {
+    if (lc < c1) {
+      issue(phys_of(lc, lit), fre, fb);
       advance(lc, lit);
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    } else {
-      vm_wait_all();
+      ++ahead;
     }
-    run(kA, 0);
-    if (!more) break;
-    const bool more2 = lc < c1;
-    if (more2) {
-      issue(phys_of(lc, lit), kA, 0);
-      advance(lc, lit);
+    if (ahead >= 3)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (ahead == 2)
       asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    } else {
+    else
       vm_wait_all();
+    run(cur, cb);
+    --ahead;
+  };
+  if constexpr (NBUF == 3) {
+    while (true) {
+      one(kA, 0, kC, 2);
+      if (ahead == 0) break;
+      one(kB, 1, kA, 0);
+      if (ahead == 0) break;
+      one(kC, 2, kB, 1);
+      if (ahead == 0) break;
     }
-    run(kB, 1);
-    if (!more2) break;
+  } else {
+    while (true) {
+      one(kA, 0, kB, 1);
+      if (ahead == 0) break;
+      one(kB, 1, kA, 0);
+      if (ahead == 0) break;
+    }
   }
   if (!FUSED) return;                     // attn_merge_kernel combines the partials
   // 5. the last workgroup of this (row, KV head) to finish merges the chunk partials. The
@@ -1022,7 +1069,7 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G>& sm, int bx, int kv
 
 template <int G, bool FUSED, bool KQ8, bool CHAIN>
 __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : (KQ8 ? 2 : 3)) void attn_decode_kernel(AttnArgs A) {
-  __shared__ AttnSmem<G> sm;
+  __shared__ AttnSmem<G, decode_buffers(FUSED)> sm;
   attn_decode_body<G, FUSED, KQ8, CHAIN>(sm, blockIdx.x, blockIdx.y, blockIdx.z, A);
   if constexpr (CHAIN) chain_signal(A.chain);
 }
