@@ -592,7 +592,11 @@ struct AttnArgs {
 #endif
 constexpr int decode_buffers(bool fused) { return fused ? GQA_DECODE_BUFFERS_FUSED : 2; }
 
-template <int G, bool FUSED, bool KQ8, bool CHAIN>
+// LTAB: every workgroup's block-table entries fit the LDS table (one per thread), which the
+// launcher checks; the steps then read their block ids from LDS only. (A step reading "LDS or
+// global" through one pointer becomes a generic load, which waits for every vector load in
+// flight.)
+template <int G, bool FUSED, bool KQ8, bool CHAIN, bool LTAB>
 __device__ __forceinline__ void attn_decode_body(AttnSmem<G, decode_buffers(FUSED)>& sm, int bx, int kvh, int zs,
                                                  const AttnArgs& A) {
   constexpr int NBUF = decode_buffers(FUSED);
@@ -646,17 +650,18 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G, decode_buffers(FUSE
   //   K: lane l loads key l % 16, dims 32 s + 8 (l / 16) .. + 7 for s = 0..3 (the A operand rows).
   //   V: four 1 KiB direct-to-LDS copies into 16-dim planes (16 keys x 32 bytes each); copy j
   //      fills planes 2 j, 2 j + 1, lane l bringing key (l % 32) / 2, half l % 2 of the plane.
-  // The block-table entries of the workgroup's positions are staged in LDS (one per thread, loaded
-  // with the first K/V and stored before the barrier that publishes q), so a step's K/V loads do
-  // not wait for a table load; the first step reads the table directly, and so does every step
-  // of a workgroup that spans more blocks than it has threads.
+  // The block-table entries of the workgroup's positions are staged in LDS (LTAB; one per thread,
+  // loaded with the first K/V and stored before the barrier that publishes q), so a step's K/V
+  // loads do not wait for a table load; the first step reads the table directly.
   const int blk0 = (c0 * CH) >> 5, nblk = ((min(c1 * CH, ctx) - 1) >> 5) - blk0 + 1;
-  const bool ltab = nblk <= 64 * kDecodeWaves;
-  const int tabv = ltab && tid < nblk ? table[blk0 + tid] : 0;
-  bool lready = false;                                     // set once stab is published
+  const int tabv = LTAB && tid < nblk ? table[blk0 + tid] : 0;
+  auto blk_of = [&](int cc, int it) { return min(cc * CH + it * kDecodeStep + wave * 16, p_end_of(cc) - 1) >> 5; };
+  auto phys_first = [&](int cc, int it) { return table[blk_of(cc, it)]; };
   auto phys_of = [&](int cc, int it) {
-    const int bi = min(cc * CH + it * kDecodeStep + wave * 16, p_end_of(cc) - 1) >> 5;
-    return lready ? sm.stab[bi - blk0] : table[bi];
+    if constexpr (LTAB)
+      return sm.stab[blk_of(cc, it) - blk0];
+    else
+      return table[blk_of(cc, it)];
   };
   //   Q8_0 cache: K as above but the codes (8 bytes per lane and 32-dim step) and the key's four
   //   block scales; V: lane l brings the 32 codes of key l / 4, dims 32 (l % 4) .. + 31, and their
@@ -686,7 +691,7 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G, decode_buffers(FUSE
   // Issue order matters (vector loads complete in order): the block-table entry, the RoPE and
   // norm constants, the projection partials, then the first K/V, so q is built while the K/V
   // are in flight.
-  const int phys0 = phys_of(c0, 0);
+  const int phys0 = phys_first(c0, 0);
   nsplit = max(1, min(nsplit, 8));
   const float cs = rcos[(int64_t)pos * 64 + lane], sn = rsin[(int64_t)pos * 64 + lane];
   const float wq0 = bf16_bits_to_f32(wqn[lane]), wq1 = bf16_bits_to_f32(wqn[64 + lane]);
@@ -728,9 +733,8 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G, decode_buffers(FUSE
       if (e < nel) sraw[e] = __fmul_rn(acc, cin);
     }
   }
-  if (ltab && tid < nblk) sm.stab[tid] = tabv;
+  if (LTAB && tid < nblk) sm.stab[tid] = tabv;
   __syncthreads();
-  lready = ltab;
   // 2. per-head RMSNorm(128) and rotate-half RoPE at `pos`: wave w handles heads w, w + 4, ...;
   //    lane t owns dims t and t + 64 (a RoPE pair). q is pre-scaled by log2(e)/sqrt(128).
   {
@@ -1067,10 +1071,10 @@ __device__ __forceinline__ void attn_decode_body(AttnSmem<G, decode_buffers(FUSE
   }
 }
 
-template <int G, bool FUSED, bool KQ8, bool CHAIN>
+template <int G, bool FUSED, bool KQ8, bool CHAIN, bool LTAB>
 __global__ __launch_bounds__(64 * kDecodeWaves, FUSED ? 1 : (KQ8 ? 2 : 3)) void attn_decode_kernel(AttnArgs A) {
   __shared__ AttnSmem<G, decode_buffers(FUSED)> sm;
-  attn_decode_body<G, FUSED, KQ8, CHAIN>(sm, blockIdx.x, blockIdx.y, blockIdx.z, A);
+  attn_decode_body<G, FUSED, KQ8, CHAIN, LTAB>(sm, blockIdx.x, blockIdx.y, blockIdx.z, A);
   if constexpr (CHAIN) chain_signal(A.chain);
 }
 
@@ -1166,6 +1170,11 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
   // across its chunks); the chunks and their partials are the same either way
   const int cpw = fused ? 1 : kBatchChunksPerWorkgroup;
   dim3 grid((chunks + cpw - 1) / cpw, kKvHeads, B);
+  // the LDS block table holds one entry per thread: a workgroup spans at most cpw chunks of
+  // 32-position blocks (chunk starts are block aligned)
+  bool ltab = true;
+  for (int b = 0; b < B; ++b)
+    if (cpw * decode_chunk_len(rows.pos[b] + 1) / kBlock > 64 * kDecodeWaves) ltab = false;
   // rows by decreasing workgroup length (positions one workgroup walks), then by decreasing
   // context, then by index
   RowOrder order;
@@ -1190,12 +1199,19 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
       DEC_LAUNCH_Q(GG, FU, false);                                                                                 \
     }                                                                                                              \
   } while (0)
-#define DEC_LAUNCH_Q(GG, FU, Q)                                                                               \
-  do {                                                                                                        \
-    if (FU && ch)                                                                                             \
-      GQA_LAUNCH_F((attn_decode_kernel<GG, FU, Q, FU>), grid, dim3(64 * kDecodeWaves), 0, st, flags, A);      \
-    else                                                                                                      \
-      hipLaunchKernelGGL((attn_decode_kernel<GG, FU, Q, false>), grid, dim3(64 * kDecodeWaves), 0, st, A);    \
+#define DEC_LAUNCH_Q(GG, FU, Q)          \
+  do {                                   \
+    if (ltab)                            \
+      DEC_LAUNCH_T(GG, FU, Q, true);     \
+    else                                 \
+      DEC_LAUNCH_T(GG, FU, Q, false);    \
+  } while (0)
+#define DEC_LAUNCH_T(GG, FU, Q, LT)                                                                               \
+  do {                                                                                                            \
+    if (FU && ch)                                                                                                 \
+      GQA_LAUNCH_F((attn_decode_kernel<GG, FU, Q, FU, LT>), grid, dim3(64 * kDecodeWaves), 0, st, flags, A);      \
+    else                                                                                                          \
+      hipLaunchKernelGGL((attn_decode_kernel<GG, FU, Q, false, LT>), grid, dim3(64 * kDecodeWaves), 0, st, A);    \
   } while (0)
   if (G != 4 && G != 2) return hipErrorInvalidValue;
   if (fused) {
@@ -1214,6 +1230,7 @@ hipError_t launch_attn_decode(const float* qkvp, int nsplit, int64_t pstride, in
   }
 #undef DEC_LAUNCH
 #undef DEC_LAUNCH_Q
+#undef DEC_LAUNCH_T
   return hipGetLastError();
 }
 
