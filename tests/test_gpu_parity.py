@@ -242,6 +242,41 @@ def test_batched_equals_isolated_bitwise(g, nseq):
         o.close()
 
 
+def test_batched_rows_past_the_lds_block_table(g):
+    """The decode attention stages each workgroup's block-table entries in LDS (one per thread,
+    256) when every workgroup of the launch fits; a row-batched launch walks three chunks per
+    workgroup, so past 86,016 positions it reads the table from global memory instead. Such a
+    launch (tiny shape, 5 rows, two of them at 86,105 positions) must equal each row stepped
+    alone -- a one-row launch, which stages its table in LDS -- bit for bit, for 2 steps."""
+    shape = synth.TINY
+    lens = (86105, 3000, 86105, 100, 4000)
+    nb = sum(synth.blocks_for(n + 4) for n in lens)
+    m = g.Model.from_shape(shape, seed=1001, kv_pool_blocks=2 * nb + 8, max_positions=86112)
+    lg = torch.empty(shape.vocab, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    A, Bs = [], []
+    for i, n in enumerate(lens):
+        p = synth.token_ids(400 + i, n - 1)                  # decode runs at context n
+        a, b = g.Session(m, n + 4), g.Session(m, n + 4)
+        a.prefill(p, lg)
+        b.prefill(p, lg)
+        A.append(a)
+        Bs.append(b)
+    blg = torch.empty(len(lens), shape.vocab, device="cuda")
+    bam = torch.empty(len(lens), dtype=torch.int32, device="cuda")
+    for step in range(2):
+        ids = [(4099 * step + 17 * i + 3) % shape.vocab for i in range(len(lens))]
+        m.eval_batch(A, ids, blg, bam)
+        torch.cuda.synchronize()
+        for i, sb in enumerate(Bs):
+            sb.decode(ids[i], lg, am)
+            torch.cuda.synchronize()
+            assert torch.equal(lg.view(torch.int32), blg[i].view(torch.int32)), (step, i)
+            assert int(am.item()) == int(bam[i].item())
+    for o in A + Bs + [m]:
+        o.close()
+
+
 @pytest.mark.parametrize("lens", [(8193, 4096), (8193, 4096, 3000, 100, 4000)])
 def test_batched_rows_needing_more_chunks_than_the_longest(g, lens):
     """Regression: a decode row's context is cut into chunks whose length grows in steps, so the
