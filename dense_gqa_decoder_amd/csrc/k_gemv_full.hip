@@ -61,7 +61,8 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(const void* _
   __shared__ f32x4 red[NBW][NWB][64];
   __shared__ float sred[kFullMaxB][8][4];
   __shared__ float sinv[kFullMaxB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar, so the K-range bounds and every test on them are uniform branches
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bw = wave / NWB, kp = wave % NWB;
   const int band = blockIdx.x * NBW + bw;
   const int K = kdim, B = a.B, KS = K >> 5;
@@ -216,9 +217,12 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(const void* _
   }
 
   // ---- stream the weights
+  // token columns r16 >= B: their products are computed and never stored (every store, candidate and
+  // shuffle below is per column and gated on r16 < B). The BF16 stream gives them zero operands by
+  // masked LDS reads (only the token lanes read); the quantised streams, which issue more per step,
+  // let them read row 0 unmasked, which spares the exec-mask branches and measured faster there.
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const bool xvalid = r16 < B;
-  const f16* xh = sx + (int64_t)(xvalid ? r16 : 0) * K + g4 * 8;
+  const f16* xh = sx + (int64_t)(r16 < B ? r16 : 0) * K + g4 * 8;
   const f16* xl = xh + BK;
   auto compute = [&](const Buf& f, int s) {
     if constexpr (QM == WM_BF16) {
@@ -226,8 +230,8 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(const void* _
       for (int u = 0; u < U; ++u) {
         if (s + u < s1) {
           const int kk = (s + u) * 32;
-          const f16x8 bh = xvalid ? *(const f16x8*)(xh + kk) : f16x8{};
-          const f16x8 bl = xvalid ? *(const f16x8*)(xl + kk) : f16x8{};
+          const f16x8 bh = r16 < B ? *(const f16x8*)(xh + kk) : f16x8{};
+          const f16x8 bl = r16 < B ? *(const f16x8*)(xl + kk) : f16x8{};
           const f16x8 w = bf16x8_to_f16x8(f.w[u]);
           acc = mfma16(w, bh, acc);
           acc = mfma16(w, bl, acc);
@@ -240,8 +244,8 @@ __global__ __launch_bounds__(64 * NWB * NBW) void gemv_full_kernel(const void* _
       for (int u = 0; u < U; ++u) {
         if (s + u < s1) {
           const int kk = (s + u) * 32;
-          const f16x8 bh = xvalid ? *(const f16x8*)(xh + kk) : f16x8{};
-          const f16x8 bl = xvalid ? *(const f16x8*)(xl + kk) : f16x8{};
+          const f16x8 bh = *(const f16x8*)(xh + kk);
+          const f16x8 bl = *(const f16x8*)(xl + kk);
           qstep_products<QM>(qwiden<QM>(f.q[u], f.q4[u]), bh, bl, p[u], xs[u]);
         }
       }
